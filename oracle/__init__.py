@@ -1,0 +1,45 @@
+"""Oracle: plain, slow, fp64 CPU implementations of the packed varlen KDA path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links
+this package. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use it. It shares no code with the HIP
+library under ``packed_varlen_gated_amd/`` and imports nothing from it.
+
+Sources (the pages; cited by title and section):
+
+* RFC-0025 "Support attention varlen and align loss" (wiki-b2l, rfc/0025),
+  Design section 1 "segment_ids -> cu_seqlens conversion" and section 3
+  "ShortConvolution segment boundary mask".
+* RFC-0026 "Ling3 KDA varlen support" (wiki-b2l, rfc/0026), Background
+  "KDA state leakage problem" (the recurrence) and section 3.1.1 "API
+  contract" (reset semantics).
+* "Drill: Sequence Packing from scratch" (ac.fzhiy.net), section "The math"
+  (cu_seqlens, doc(s), block-diagonal mask).
+
+Functions and their pin status (every function is pinned; see tests/):
+
+==================================  =========================================
+``segment_ids_to_cu_seqlens``       pinned: printed examples, page algorithm
+                                    on its own domain, construction from
+                                    document lengths, hand-derived deviations
+``token_segment``                   pinned: brute force of the doc(s) definition
+``short_conv_segmask``              pinned: numpy.convolve per channel, single
+                                    tap closed form, hand-computed fixture
+``chunk_kda_varlen``                pinned: unrolled closed form, g=0 masked
+                                    matmul, geometric series, single-token
+                                    segments, gate injection, invariants
+==================================  =========================================
+"""
+
+from .cu_seqlens import segment_ids_to_cu_seqlens, token_segment, FLAG_OVERFLOW, FLAG_LEADING_PAD
+from .short_conv import short_conv_segmask
+from .kda import chunk_kda_varlen
+
+__all__ = [
+    "segment_ids_to_cu_seqlens",
+    "token_segment",
+    "short_conv_segmask",
+    "chunk_kda_varlen",
+    "FLAG_OVERFLOW",
+    "FLAG_LEADING_PAD",
+]

@@ -1,0 +1,70 @@
+"""Oracle for the packed (varlen) gated linear-attention recurrence of KDA.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+RFC-0026, Background ("KDA state leakage problem"), gives the state update
+
+    S'_t = S_{t-1} * exp(g_t)
+    S_t  = S'_t + beta_t * k_t (outer) v_t
+
+and section 3.1.1 ("API contract") says the state is cleared where the segment
+changes. Readings (listed in the design doc): g_t has one entry per key channel, so
+exp(g_t) scales the key (row) axis of the [Dk, Dv] state, i.e.
+S_t = diag(exp g_t) S_{t-1} + beta_t k_t v_t^T; the readout is taken after the
+update, o_t = scale * S_t^T q_t; segments come from cu_seqlens (FLA
+convention, segment i = [cu[i], cu[i+1])); zero-length (phantom) segments
+have a zero final state; positions at or beyond cu[max_segs] get o = 0;
+cu_seqlens = None means one segment [0, N).
+
+The chunked GPU method reaches this result up to rounding order, so the
+oracle is the plain definition: the token-by-token recurrence in float64.
+"""
+
+import numpy as np
+
+
+def _as_thd(a, name, ndim):
+    a = np.asarray(a, dtype=np.float64)
+    if a.ndim == ndim + 1 and a.shape[0] == 1:
+        a = a[0]
+    if a.ndim != ndim:
+        raise ValueError(f"{name} has shape {a.shape}")
+    return a
+
+
+def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0):
+    """Return ``(o [N, H, Dv], final_state [max_segs, H, Dk, Dv])`` in float64.
+
+    q, k, g: [N, H, Dk] (a leading unit batch axis is accepted);
+    v: [N, H, Dv]; beta: [N, H]; cu_seqlens: int [max_segs + 1] or None.
+    """
+    q = _as_thd(q, "q", 3)
+    k = _as_thd(k, "k", 3)
+    v = _as_thd(v, "v", 3)
+    g = _as_thd(g, "g", 3)
+    beta = _as_thd(beta, "beta", 2)
+    N, H, Dk = q.shape
+    Dv = v.shape[2]
+    if cu_seqlens is None:
+        cu = np.array([0, N], dtype=np.int64)
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+    max_segs = cu.shape[0] - 1
+    if cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] > N:
+        raise ValueError("malformed cu_seqlens")
+
+    o = np.zeros((N, H, Dv), dtype=np.float64)
+    final_state = np.zeros((max_segs, H, Dk, Dv), dtype=np.float64)
+    for i in range(max_segs):
+        start, end = int(cu[i]), int(cu[i + 1])
+        if end <= start:
+            continue  # phantom segment: state stays zero
+        S = np.zeros((H, Dk, Dv), dtype=np.float64)  # reset at the boundary
+        for t in range(start, end):
+            decay = np.exp(g[t])[:, :, None]                       # [H, Dk, 1]
+            update = beta[t][:, None, None] * k[t][:, :, None] * v[t][:, None, :]
+            S = decay * S + update
+            # o_t[h, e] = sum_d S[h, d, e] * q_t[h, d]
+            o[t] = scale * np.einsum("hde,hd->he", S, q[t])
+        final_state[i] = S
+    return o, final_state

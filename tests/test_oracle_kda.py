@@ -1,0 +1,200 @@
+"""Pins for the oracle's packed KDA recurrence.
+
+None of these re-types the oracle's update rule: each compares it with an
+independent statement of the same result (unrolled closed form, a masked
+matrix product, a geometric series, single-token algebra, gate injection) or
+checks an invariant the pages require (reset, isolation, phantoms).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _rand_inputs(rng, N, H, Dk, Dv, gmax=0.5, gpos=False):
+    q = rng.standard_normal((N, H, Dk))
+    k = rng.standard_normal((N, H, Dk))
+    v = rng.standard_normal((N, H, Dv))
+    g = -rng.uniform(0.0, gmax, (N, H, Dk))
+    if gpos:
+        g = rng.uniform(-gmax, gmax, (N, H, Dk))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((N, H))))
+    return q, k, v, g, beta
+
+
+def _closed_form(q, k, v, g, beta, cu, scale):
+    """Unrolled recurrence: with b the in-segment inclusive cumsum of g,
+    o_t = scale * sum_{s<=t} beta_s (sum_i q_t[i] k_s[i] e^{b_t[i]-b_s[i]}) v_s and
+    S_end = sum_s diag(e^{b_end - b_s}) beta_s k_s v_s^T."""
+    N, H, Dk = q.shape
+    Dv = v.shape[2]
+    M = len(cu) - 1
+    o = np.zeros((N, H, Dv))
+    fs = np.zeros((M, H, Dk, Dv))
+    for i in range(M):
+        a, e = cu[i], cu[i + 1]
+        if e <= a:
+            continue
+        for h in range(H):
+            b = np.cumsum(g[a:e, h, :], axis=0)          # b[t - a] = sum_{u=a..t} g_u
+            for t in range(a, e):
+                acc = np.zeros(Dv)
+                for s in range(a, t + 1):
+                    w = sum(q[t, h, d] * k[s, h, d] * math.exp(b[t - a, d] - b[s - a, d]) for d in range(Dk))
+                    acc += beta[s, h] * w * v[s, h, :]
+                o[t, h] = scale * acc
+            for s in range(a, e):
+                fs[i, h] += np.outer(np.exp(b[e - 1 - a] - b[s - a]) * beta[s, h] * k[s, h], v[s, h])
+    return o, fs
+
+
+@pytest.mark.parametrize("gpos", [False, True])
+def test_unrolled_closed_form(gpos):
+    rng = np.random.default_rng(1)
+    N, H, Dk, Dv = 40, 2, 3, 2       # Dk != Dv catches a transposed state
+    q, k, v, g, beta = _rand_inputs(rng, N, H, Dk, Dv, gpos=gpos)
+    cu = np.array([0, 7, 7, 19, 20, 33, 33])      # phantom slots, tail [33, 40) uncovered
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, cu, scale=0.75)
+    o2, fs2 = _closed_form(q, k, v, g, beta, cu, 0.75)
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(fs, fs2, rtol=1e-12, atol=1e-13)
+    assert np.all(o[33:] == 0)
+
+
+def test_zero_gate_is_block_diagonal_masked_matmul():
+    # g = 0, beta = 1: o = (M * Q K^T) V with M the block-diagonal causal mask
+    # of "Drill: Sequence Packing", The math.
+    rng = np.random.default_rng(2)
+    N, H, Dk, Dv = 50, 3, 5, 4
+    q, k, v, _, _ = _rand_inputs(rng, N, H, Dk, Dv)
+    g = np.zeros((N, H, Dk))
+    beta = np.ones((N, H))
+    cu = np.array([0, 11, 12, 30, 45, 45])
+    o, _ = oracle.chunk_kda_varlen(q, k, v, g, beta, cu)
+    doc = np.full(N, -1)
+    for i in range(len(cu) - 1):
+        doc[cu[i]:cu[i + 1]] = i
+    s = np.arange(N)
+    M = (doc[:, None] == doc[None, :]) & (doc[:, None] >= 0) & (s[:, None] >= s[None, :])
+    for h in range(H):
+        ref = (M * (q[:, h] @ k[:, h].T)) @ v[:, h]
+        np.testing.assert_allclose(o[:, h], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_geometric_series():
+    # Dk = Dv = 1 with constant g, k, v, beta: S_t = beta k v (1 - e^{g(t+1)}) / (1 - e^g).
+    L, gval, kv, bval, qv = 57, -0.137, (0.8, -1.3), 0.6, 0.9
+    q = np.full((L, 1, 1), qv)
+    k = np.full((L, 1, 1), kv[0])
+    v = np.full((L, 1, 1), kv[1])
+    g = np.full((L, 1, 1), gval)
+    beta = np.full((L, 1), bval)
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, None)
+    t = np.arange(L)
+    S = bval * kv[0] * kv[1] * (1 - np.exp(gval * (t + 1))) / (1 - np.exp(gval))
+    np.testing.assert_allclose(o[:, 0, 0], qv * S, rtol=1e-12)
+    np.testing.assert_allclose(fs[0, 0, 0, 0], S[-1], rtol=1e-12)
+
+
+def test_single_token_segments():
+    # segment_ids [1, 2, 3, 4] (RFC-0025 Design section 1, fourth example):
+    # every segment is one token, so o_t = beta_t (q_t . k_t) v_t, S = beta k v^T.
+    seg = np.array([[1, 2, 3, 4]], dtype=np.int32)
+    cu, _, _ = oracle.segment_ids_to_cu_seqlens(seg, 4)
+    rng = np.random.default_rng(3)
+    q, k, v, g, beta = _rand_inputs(rng, 4, 2, 3, 5)
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, cu)
+    for t in range(4):
+        for h in range(2):
+            np.testing.assert_allclose(o[t, h], beta[t, h] * np.dot(q[t, h], k[t, h]) * v[t, h], rtol=1e-13)
+            np.testing.assert_allclose(fs[t, h], beta[t, h] * np.outer(k[t, h], v[t, h]), rtol=1e-13)
+
+
+def test_gate_injection_equivalence():
+    # RFC-0026 Alternatives, gate injection: one continuous segment with
+    # g = -inf at every document's first token gives the segmented result.
+    rng = np.random.default_rng(4)
+    N, H, Dk, Dv = 60, 2, 4, 3
+    q, k, v, g, beta = _rand_inputs(rng, N, H, Dk, Dv)
+    cu = np.array([0, 9, 25, 26, 60])
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, cu)
+    g2 = g.copy()
+    for i in range(1, len(cu) - 1):
+        g2[cu[i]] = -np.inf
+    o2, fs2 = oracle.chunk_kda_varlen(q, k, v, g2, beta, None)
+    assert np.array_equal(o, o2)
+    assert np.array_equal(fs[-1], fs2[0])
+
+
+def test_first_token_gate_has_no_effect():
+    rng = np.random.default_rng(5)
+    N, H, Dk, Dv = 30, 2, 3, 3
+    q, k, v, g, beta = _rand_inputs(rng, N, H, Dk, Dv)
+    cu = np.array([0, 4, 17, 30])
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, cu)
+    g2 = g.copy()
+    g2[cu[:-1]] = rng.uniform(-3, 3, g2[cu[:-1]].shape)
+    o2, fs2 = oracle.chunk_kda_varlen(q, k, v, g2, beta, cu)
+    assert np.array_equal(o, o2) and np.array_equal(fs, fs2)
+
+
+def test_packed_equals_each_document_alone_and_no_leakage():
+    # RFC-0026 Tests: packed output equals running each document on its own
+    # from a zero state; perturbing one document changes no other.
+    rng = np.random.default_rng(6)
+    N, H, Dk, Dv = 64, 2, 4, 4
+    q, k, v, g, beta = _rand_inputs(rng, N, H, Dk, Dv)
+    cu = np.array([0, 13, 40, 41, 64, 64])
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, cu)
+    for i in range(len(cu) - 1):
+        a, e = cu[i], cu[i + 1]
+        if e <= a:
+            assert np.all(fs[i] == 0)
+            continue
+        oi, fsi = oracle.chunk_kda_varlen(q[a:e], k[a:e], v[a:e], g[a:e], beta[a:e], None)
+        assert np.array_equal(o[a:e], oi) and np.array_equal(fs[i], fsi[0])
+    # leakage: perturb document 1 only
+    q2, v2, g2 = q.copy(), v.copy(), g.copy()
+    q2[13:40] += 1.0
+    v2[13:40] *= -2.0
+    g2[13:40] -= 0.3
+    o2, fs2 = oracle.chunk_kda_varlen(q2, k, v2, g2, beta, cu)
+    other = np.r_[0:13, 40:64]
+    assert np.array_equal(o[other], o2[other])
+    assert np.array_equal(fs[[0, 2, 3]], fs2[[0, 2, 3]])
+    assert not np.allclose(o[13:40], o2[13:40])
+
+
+def test_linearity_and_phantoms():
+    rng = np.random.default_rng(8)
+    N, H, Dk, Dv = 33, 2, 3, 4
+    q, k, v, g, beta = _rand_inputs(rng, N, H, Dk, Dv)
+    cu = np.array([0, 10, 10, 10, 30])
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, cu)
+    assert np.all(fs[1] == 0) and np.all(fs[2] == 0)
+    assert np.all(o[30:] == 0)
+    o2, _ = oracle.chunk_kda_varlen(q, k, 2.0 * v, g, beta, cu)
+    assert np.array_equal(o2, 2.0 * o)
+    q3 = rng.standard_normal(q.shape)
+    o3, _ = oracle.chunk_kda_varlen(q3, k, v, g, beta, cu)
+    o4, _ = oracle.chunk_kda_varlen(q + q3, k, v, g, beta, cu)
+    np.testing.assert_allclose(o4, o + o3, rtol=1e-12, atol=1e-12)
+
+
+def test_decay_acts_on_key_axis():
+    # One key channel with a strong decay and one without: only the state row
+    # of the decaying key channel fades (the gate has Dk entries).
+    L = 5
+    q = np.zeros((L, 1, 2)); q[-1, 0] = [1.0, 0.0]
+    k = np.zeros((L, 1, 2)); k[0, 0] = [1.0, 1.0]
+    v = np.zeros((L, 1, 3)); v[0, 0] = [1.0, 2.0, 3.0]
+    g = np.zeros((L, 1, 2)); g[:, 0, 0] = math.log(0.5)
+    beta = np.ones((L, 1))
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, None)
+    # row 0 decays by 0.5 per step after the first token, row 1 keeps its value
+    np.testing.assert_allclose(fs[0, 0, 0], 0.5 ** (L - 1) * np.array([1.0, 2.0, 3.0]), rtol=1e-14)
+    np.testing.assert_allclose(fs[0, 0, 1], np.array([1.0, 2.0, 3.0]), rtol=1e-14)
+    np.testing.assert_allclose(o[-1, 0], 0.5 ** (L - 1) * np.array([1.0, 2.0, 3.0]), rtol=1e-14)
