@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed varlen KDA forward on one MI355X.
+
+A step is one pass of the whole path over one synthetic packed batch:
+segment_ids -> cu_seqlens (pkv_segment_ids_to_cu_seqlens), the masked short
+conv when the workload has one, and chunk_kda_varlen. Inputs are resident in
+HBM before the timed region. Prints ONE JSON line on stdout.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Modes used for profiling (no JSON line): --mode kernel (only chunk_kda_varlen,
+for rocprofv3 counters) and --mode copy (a plain device copy of known size,
+the calibration of the HBM byte counters).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed tokens/sec for chunk_kda_varlen fwd at H=32,D=128; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+DOMINANT_KERNEL = "chunk_kda_varlen"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="flat_microbatch")
+    p.add_argument("--final-state", choices=["auto", "on", "off"], default="auto")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=0,
+                   help="oracle sample size in tokens (0: sized for ~15 s of CPU work)")
+    p.add_argument("--mode", choices=["bench", "kernel", "copy"], default="bench")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    """Hash of the sources of the dominant kernel (ties a counter summary to its code)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "packed_varlen_gated_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.startswith("kda") or f == "common.h":
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(cfg, cu, final_state):
+    """Bytes the dominant kernel must move at least once: q, k, g, v, beta read
+    and o written for tokens inside segments; o written for uncovered tokens;
+    cu_seqlens read; final states written when requested."""
+    E = 4 if cfg.dtype == "f32" else 2
+    N, H = cfg.B * cfg.T, cfg.H
+    covered = int(cu[-1])
+    per_tok_head = E * (3 * cfg.Dk + 2 * cfg.Dv + 1)
+    total = covered * H * per_tok_head + (N - covered) * H * E * cfg.Dv + 4 * len(cu)
+    if final_state:
+        total += 4 * (len(cu) - 1) * H * cfg.Dk * cfg.Dv
+    return total
+
+
+def algorithmic_flops(cfg, cu):
+    """Chunked method (C = 64): 2*Dk*Dv each for Q.S and K^T V, and the causal
+    halves of the intra-chunk Q K^T and A V, per token and head."""
+    covered = int(cu[-1])
+    C = 64
+    return covered * cfg.H * (4 * cfg.Dk * cfg.Dv + C * (cfg.Dk + cfg.Dv))
+
+
+def read_traffic(workload):
+    """Measured HBM bytes per launch from the committed counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{DOMINANT_KERNEL}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(wl, cu, sample_tokens):
+    """The oracle, as it stands, on the first `sample_tokens` tokens of the
+    workload (segments clipped there), all heads, split by head over a process
+    pool. Returns a dict for the JSON line."""
+    import multiprocessing as mp
+    import numpy as np
+    from concurrent.futures import ProcessPoolExecutor
+
+    cfg = wl.cfg
+    ncores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, ncores, cfg.H))
+    S = min(sample_tokens, wl.N)
+    cu_s = np.minimum(cu, S)
+    arrs = [t[:S].double().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]
+    groups = np.array_split(np.arange(cfg.H), workers)
+    jobs = [tuple(a[:, gidx] for a in arrs) + (cu_s,) for gidx in groups]
+    ctx = mp.get_context("spawn")  # workers never touch the GPU
+    os.environ["OMP_NUM_THREADS"] = "1"
+    with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(_oracle_job, jobs))
+        dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"first {S} of {wl.N} tokens ({cfg.name}), all {cfg.H} heads, "
+                      f"fp64 token recurrence, {workers} processes split by head, {dt:.1f} s"}
+
+
+def _oracle_job(args):
+    import oracle
+    q, k, v, g, beta, cu = args
+    oracle.chunk_kda_varlen(q, k, v, g, beta, cu)
+    return True
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log("bench.py runs on one GPU only: this build has no multi-GPU path "
+            "(the sharding design is described in DESIGN.md). Use --gpus 1.")
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads
+    import packed_varlen_gated_amd as pkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    if args.mode == "copy":
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 copies of {nbytes} bytes")
+        return
+
+    t0 = time.perf_counter()
+    wl = workloads.make_workload(args.workload)
+    cfg = wl.cfg
+    log(f"workload {cfg.name}: {cfg.description}; generated in {time.perf_counter() - t0:.1f} s")
+    final_state = cfg.final_state if args.final_state == "auto" else args.final_state == "on"
+    N, H = wl.N, cfg.H
+    seg = torch.from_numpy(wl.segment_ids).to(dev)
+    q = wl.q.reshape(1, N, H, cfg.Dk).to(dev)
+    k = wl.k.reshape(1, N, H, cfg.Dk).to(dev)
+    v = wl.v.reshape(1, N, H, cfg.Dv).to(dev)
+    g = wl.g.reshape(1, N, H, cfg.Dk).to(dev)
+    beta = wl.beta.reshape(1, N, H).to(dev)
+    conv_x = wl.conv_x.to(dev) if wl.conv_x is not None else None
+    conv_w = wl.conv_w.to(dev) if wl.conv_w is not None else None
+
+    # Outputs allocated once, outside the timed region.
+    o = torch.empty(1, N, H, cfg.Dv, dtype=q.dtype, device=dev)
+    conv_y = torch.empty_like(conv_x) if conv_x is not None else None
+    ws_bytes = pkv.chunk_kda_varlen_workspace_size(N, H, cfg.Dk, cfg.Dv, cfg.max_segs, q.dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    res = pkv.segment_ids_to_cu_seqlens(seg, cfg.max_segs)
+    cu_host = res.cu_seqlens.cpu().numpy()
+    n_segs = int(res.n_segs.item())
+
+    if args.mode == "kernel":
+        for _ in range(args.warmup + args.steps):
+            pkv.chunk_kda_varlen(q, k, v, g, beta, res.cu_seqlens, output_final_state=final_state,
+                                 flags=flags, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"kernel mode: {args.warmup + args.steps} launches of {DOMINANT_KERNEL}")
+        return
+
+    def step(ev=None):
+        r = pkv.segment_ids_to_cu_seqlens(seg, cfg.max_segs)
+        if conv_x is not None:
+            pkv.short_conv_segmask(conv_x, conv_w, seg, out=conv_y)
+        if ev is not None:
+            ev[0].record()
+        out = pkv.chunk_kda_varlen(q, k, v, g, beta, r.cu_seqlens, output_final_state=final_state,
+                                   flags=flags, out=o, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        return out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(flags.item()) != 0:
+        log(f"warning: flags = {int(flags.item())}")
+    ms = (t1 - t0) * 1000.0 / args.steps
+    kc_ms = [a.elapsed_time(b) for a, b in events]
+    kc_avg_s = sum(kc_ms) / len(kc_ms) / 1000.0
+    value = N / (ms / 1000.0)
+
+    alg_bytes = algorithmic_bytes(cfg, cu_host, final_state)
+    achieved = alg_bytes / kc_avg_s / 1e9
+    flops = algorithmic_flops(cfg, cu_host)
+    mfma_frac = flops / kc_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    traffic = read_traffic(cfg.name)
+    log(f"step {ms:.3f} ms; {DOMINANT_KERNEL} {kc_avg_s * 1e6:.1f} us avg "
+        f"(min {min(kc_ms) * 1e3:.1f} max {max(kc_ms) * 1e3:.1f}); {achieved:.0f} GB/s "
+        f"= {achieved / HBM_PEAK_GBS:.3f} of HBM peak; MFMA {mfma_frac:.4f} of bf16 peak; "
+        f"n_segs {n_segs}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample_tokens or (2048 if cfg.Dk * cfg.Dv >= 128 * 128 else 8192)
+        log(f"cpu baseline: oracle on {sample} tokens ...")
+        cpu = cpu_baseline(wl, cu_host, sample)
+        log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "N": N, "H": H, "Dk": cfg.Dk,
+                   "Dv": cfg.Dv, "max_segs": cfg.max_segs, "n_segs": n_segs,
+                   "output_final_state": final_state, "short_conv": conv_x is not None,
+                   "step": "segment_ids_to_cu_seqlens" + (" + short_conv_segmask" if conv_x is not None else "")
+                           + " + chunk_kda_varlen"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": DOMINANT_KERNEL, "kernel_avg_us": kc_avg_s * 1e6,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "mfma_frac_bf16": mfma_frac},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

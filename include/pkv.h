@@ -1,0 +1,166 @@
+/*
+ * pkv.h - C ABI of libpkv: packed (varlen) gated linear attention (KDA) forward
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, following the problem statement of the pages:
+ *
+ *   pkv_segment_ids_to_cu_seqlens  segment ids [B, T] -> cu_seqlens [max_segs + 1]
+ *       RFC-0025 "Support attention varlen and align loss", Design section 1
+ *       (segment_ids -> cu_seqlens conversion); row-start rule from RFC-0026
+ *       "Ling3 KDA varlen support", section 3.1.1 (API contract); doc(s) from
+ *       "Drill: Sequence Packing from scratch", section "The math".
+ *   pkv_short_conv_segmask         causal depthwise conv masked at segment changes
+ *       RFC-0025, Design section 3 (ShortConvolution segment boundary mask).
+ *   pkv_chunk_kda_varlen           S_t = diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,
+ *                                  o_t = scale * S_t^T q_t, S reset per segment
+ *       RFC-0026, Background (KDA state leakage problem) and section 3.1.1;
+ *       RFC-0025, Design sections 2 (batch flatten) and 4 (kernel wrappers).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer (HIP device memory or memory the
+ *     GPU can address). Scalars are passed by value.
+ *   - The caller allocates and owns every buffer, including the workspace. The
+ *     library allocates nothing, keeps no state between calls and never
+ *     synchronizes: work is enqueued on `stream` (a hipStream_t; NULL means the
+ *     default stream) and results are valid once that stream has been
+ *     synchronized by the caller.
+ *   - Layouts are dense row-major with the last index contiguous.
+ *   - Problems visible from the host (null pointers, bad sizes, unsupported
+ *     shapes or dtypes, too small a workspace) return an error code
+ *     synchronously, before anything is enqueued. Data-dependent conditions are
+ *     reported through a device `flags` word (PKV_FLAG_*), the counterpart of
+ *     the page's debug-callback warning: they never abort.
+ *   - A failure of the HIP runtime to launch returns PKV_ERR_HIP.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_BF16 = 0, /* bfloat16 tensors, fp32 arithmetic inside */
+    PKV_F32 = 1   /* float32 tensors, fp32 arithmetic inside */
+} pkv_dtype;
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARGUMENT = 1, /* null pointer, size out of range, aliasing */
+    PKV_ERR_UNSUPPORTED = 2,      /* head dim, conv width or dtype not built */
+    PKV_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    PKV_ERR_HIP = 4               /* the HIP runtime refused a launch */
+} pkv_status;
+
+/* Bits of the device flags word. */
+#define PKV_FLAG_OVERFLOW 1        /* more segments than max_segs: the last slot
+                                      ends at B*T and merges the rest (leakage) */
+#define PKV_FLAG_LEADING_PAD 2     /* padding before the first real token; it
+                                      falls into segment 0 because cu[0] = 0 */
+#define PKV_FLAG_BAD_CU_SEQLENS 4  /* chunk_kda_varlen saw cu[0] != 0, a
+                                      decreasing pair or cu[i] > N; the outputs
+                                      of the offending segments are undefined */
+
+/*
+ * segment_ids -> cu_seqlens (FLA convention, fixed length max_segs + 1).
+ *
+ * segment_ids  int32 [B, T]: per row, 1-based increasing document ids; 0 is
+ *              padding. The batch is treated as flattened to [B*T].
+ * A boundary is a real (non-zero) token that starts a row or whose id differs
+ * from the previous position. Segment i (0-based) starts at the (i+1)-th
+ * boundary and ends where the next one starts, so padding between documents
+ * joins the preceding segment; the last real segment ends one past the last
+ * non-zero position. Slots beyond the number of segments are zero-length
+ * (phantoms repeat the last end). If there are more segments than max_segs,
+ * slot max_segs-1 ends at B*T and PKV_FLAG_OVERFLOW is set.
+ *
+ * Outputs (device, written in full by the call):
+ *   cu_seqlens  int32 [max_segs + 1], cu_seqlens[0] = 0.
+ *   token_seg   int32 [B*T] or NULL: doc(p) = i with cu[i] <= p < cu[i+1],
+ *               -1 for p >= cu[max_segs].
+ *   n_segs      int32 [1] or NULL: number of boundaries (may exceed max_segs).
+ *   flags       int32 [1] or NULL: overwritten with PKV_FLAG_OVERFLOW |
+ *               PKV_FLAG_LEADING_PAD as they apply.
+ * Errors: PKV_ERR_INVALID_ARGUMENT if segment_ids or cu_seqlens is NULL,
+ * B < 1, T < 1, B*T > INT32_MAX or max_segs < 1 or max_segs >= INT32_MAX.
+ */
+pkv_status pkv_segment_ids_to_cu_seqlens(const int32_t* segment_ids, int64_t B, int64_t T,
+                                         int32_t max_segs, int32_t* cu_seqlens,
+                                         int32_t* token_seg, int32_t* n_segs, int32_t* flags,
+                                         void* stream);
+
+/*
+ * Segment-masked short causal depthwise convolution.
+ *
+ * y[b,t,f] = sum_{k<Kc} w[f,k] * x[b,t-k,f] * [t-k >= 0] * [seg[b,t-k] == seg[b,t]]
+ *
+ * x            [B, T, F] in `dtype`.
+ * w            float32 [F, Kc]; w[f, 0] weights the current token (the page's
+ *              kernel[k] for channel f).
+ * segment_ids  int32 [B, T] or NULL (NULL: plain causal conv, no mask).
+ * y            [B, T, F] in `dtype`, must not overlap x. Accumulation is fp32
+ *              with one rounding to `dtype`. No bias, no activation.
+ * Errors: PKV_ERR_INVALID_ARGUMENT for NULL x/w/y, x == y, B, T or F < 1 or
+ * B*T*F > INT64 range of the kernel (2^62); PKV_ERR_UNSUPPORTED for Kc outside
+ * [1, 8] or an unknown dtype.
+ */
+pkv_status pkv_short_conv_segmask(const void* x, const float* w, const int32_t* segment_ids,
+                                  void* y, int64_t B, int64_t T, int64_t F, int32_t Kc,
+                                  int32_t dtype, void* stream);
+
+/*
+ * Bytes of device workspace pkv_chunk_kda_varlen needs for these sizes
+ * (0 means no workspace is needed and NULL may be passed).
+ */
+size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+                                           int32_t max_segs, int32_t dtype);
+
+/*
+ * Packed gated linear-attention recurrence with per-segment reset.
+ *
+ * For every segment i = [cu[i], cu[i+1]) and head h, from S = 0:
+ *   S_t = diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T      (S is [Dk, Dv], fp32)
+ *   o_t = scale * S_t^T q_t                              (readout after the update)
+ * final_state[i, h] = S after the segment's last token (0 for empty slots).
+ * Positions p >= cu[max_segs] get o = 0.
+ *
+ * q, k, g     [1, N, H, Dk] in `dtype` (the batch flattened to one row, B*T = N).
+ * v           [1, N, H, Dv] in `dtype`.
+ * beta        [1, N, H] in `dtype`.
+ * cu_seqlens  int32 [max_segs + 1] or NULL. NULL means one segment [0, N) and
+ *             max_segs is taken as 1. Expected: cu[0] = 0, non-decreasing,
+ *             cu[max_segs] <= N; a violation sets PKV_FLAG_BAD_CU_SEQLENS.
+ * o           [1, N, H, Dv] in `dtype`; must not overlap the inputs.
+ * final_state float32 [max_segs, H, Dk, Dv] or NULL (not written).
+ * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in.
+ * workspace   device buffer of at least pkv_chunk_kda_varlen_workspace_size()
+ *             bytes (NULL allowed when that size is 0); contents are scratch.
+ * Supported: Dk, Dv in {32, 64, 128}. Inputs with large positive g or with
+ * 16 * max|g| beyond ~60 within a segment may lose accuracy (the chunked
+ * factorisation bounds exponents per 16-token sub-chunk).
+ * Errors: PKV_ERR_INVALID_ARGUMENT for NULL tensors, N < 1, N > INT32_MAX,
+ * H < 1, max_segs < 1 (with cu_seqlens) or o aliasing an input;
+ * PKV_ERR_UNSUPPORTED for other Dk/Dv or dtype; PKV_ERR_WORKSPACE if the
+ * workspace is too small.
+ */
+pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
+                                int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                int32_t dtype, void* o, float* final_state, int32_t* flags,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* pkv_status_string(int32_t status);
+
+/* ABI version of this header (bumped on any signature change). */
+#define PKV_ABI_VERSION 1
+int32_t pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

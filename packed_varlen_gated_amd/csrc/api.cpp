@@ -1,0 +1,113 @@
+// libpkv C ABI: argument validation and dispatch. Every check here runs before
+// any HIP call, so invalid arguments are reported synchronously and nothing is
+// enqueued. See include/pkv.h for the contract of each entry point.
+
+#include "pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int64_t kInt32Max = 2147483647;
+
+bool supported_head_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
+bool known_dtype(int32_t dt) { return dt == PKV_BF16 || dt == PKV_F32; }
+int64_t elem_size(int32_t dt) { return dt == PKV_BF16 ? 2 : 4; }
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + b_bytes && pb < pa + a_bytes;
+}
+
+pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int32_t status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARGUMENT: return "PKV_ERR_INVALID_ARGUMENT";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+  }
+  return "PKV_ERR_UNKNOWN";
+}
+
+pkv_status pkv_segment_ids_to_cu_seqlens(const int32_t* segment_ids, int64_t B, int64_t T,
+                                         int32_t max_segs, int32_t* cu_seqlens,
+                                         int32_t* token_seg, int32_t* n_segs, int32_t* flags,
+                                         void* stream) {
+  if (segment_ids == nullptr || cu_seqlens == nullptr) return PKV_ERR_INVALID_ARGUMENT;
+  if (B < 1 || T < 1 || B > kInt32Max || T > kInt32Max || B * T > kInt32Max)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (max_segs < 1 || max_segs >= kInt32Max) return PKV_ERR_INVALID_ARGUMENT;
+  return from_hip(pkv::launch_cu_seqlens(segment_ids, B * T, T, max_segs, cu_seqlens, token_seg,
+                                         n_segs, flags, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_short_conv_segmask(const void* x, const float* w, const int32_t* segment_ids,
+                                  void* y, int64_t B, int64_t T, int64_t F, int32_t Kc,
+                                  int32_t dtype, void* stream) {
+  if (x == nullptr || w == nullptr || y == nullptr) return PKV_ERR_INVALID_ARGUMENT;
+  if (B < 1 || T < 1 || F < 1) return PKV_ERR_INVALID_ARGUMENT;
+  if (B > 65535 || T > (int64_t(1) << 36) || F > (int64_t(1) << 36) || B * T > (int64_t(1) << 40) ||
+      (B * T) > (int64_t(1) << 62) / F)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(dtype) || Kc < 1 || Kc > 8) return PKV_ERR_UNSUPPORTED;
+  const int64_t bytes = B * T * F * elem_size(dtype);
+  if (overlaps(x, bytes, y, bytes)) return PKV_ERR_INVALID_ARGUMENT;
+  if ((T + 31) / 32 > 65535 || ((F + 255) / 256) > kInt32Max) return PKV_ERR_INVALID_ARGUMENT;
+  return from_hip(pkv::launch_short_conv(x, w, segment_ids, y, B, T, F, Kc, dtype,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+                                           int32_t max_segs, int32_t dtype) {
+  (void)N;
+  (void)H;
+  (void)Dk;
+  (void)Dv;
+  (void)max_segs;
+  (void)dtype;
+  return 0;
+}
+
+pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
+                                int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                int32_t dtype, void* o, float* final_state, int32_t* flags,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
+      o == nullptr)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (N < 1 || N > kInt32Max || H < 1 || H > 65536) return PKV_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr) {
+    max_segs = 1;
+  } else if (max_segs < 1 || max_segs >= kInt32Max) {
+    return PKV_ERR_INVALID_ARGUMENT;
+  }
+  if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv))
+    return PKV_ERR_UNSUPPORTED;
+  if (int64_t(max_segs) * H + 64 > kInt32Max) return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t es = elem_size(dtype);
+  const int64_t o_bytes = N * H * Dv * es;
+  if (overlaps(o, o_bytes, q, N * H * Dk * es) || overlaps(o, o_bytes, k, N * H * Dk * es) ||
+      overlaps(o, o_bytes, v, N * H * Dv * es) || overlaps(o, o_bytes, g, N * H * Dk * es) ||
+      overlaps(o, o_bytes, beta, N * H * es))
+    return PKV_ERR_INVALID_ARGUMENT;
+  const size_t need = pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  return from_hip(pkv::launch_kda_serial(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
+                                         scale, dtype, o, final_state, flags,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

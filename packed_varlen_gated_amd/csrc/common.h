@@ -1,0 +1,40 @@
+// Shared device helpers and launcher declarations for libpkv (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }  // RNE
+
+// Flags word bits (mirrors include/pkv.h).
+constexpr int32_t kFlagOverflow = 1;
+constexpr int32_t kFlagLeadingPad = 2;
+constexpr int32_t kFlagBadCuSeqlens = 4;
+
+// Launchers (host side). Each returns the HIP error of its launch(es).
+hipError_t launch_cu_seqlens(const int32_t* seg, int64_t N, int64_t T, int32_t max_segs,
+                             int32_t* cu, int32_t* token_seg, int32_t* n_segs, int32_t* flags,
+                             hipStream_t stream);
+
+hipError_t launch_short_conv(const void* x, const float* w, const int32_t* seg, void* y,
+                             int64_t B, int64_t T, int64_t F, int32_t Kc, int32_t dtype,
+                             hipStream_t stream);
+
+hipError_t launch_kda_serial(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
+                             int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
+                             void* o, float* final_state, int32_t* flags, hipStream_t stream);
+
+}  // namespace pkv

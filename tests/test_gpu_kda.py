@@ -1,0 +1,211 @@
+"""GPU parity of pkv_chunk_kda_varlen against the fp64 oracle, plus the
+invariants the pages require (reset, isolation, determinism)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import (check_close, device, f64, kda_inputs_to_device, oracle_segment_head)
+
+pytestmark = pytest.mark.gpu
+
+
+def _pkv():
+    import packed_varlen_gated_amd as pkv
+    return pkv
+
+
+def _cu(wl):
+    cu, _, _ = oracle.segment_ids_to_cu_seqlens(wl.segment_ids, wl.cfg.max_segs)
+    return cu
+
+
+def _run_wl(wl, final_state=True, cu=None):
+    pkv = _pkv()
+    q, k, v, g, beta = kda_inputs_to_device(wl)
+    cu = _cu(wl) if cu is None else cu
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    flags = torch.zeros(1, dtype=torch.int32, device=device())
+    o, fs = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, output_final_state=final_state, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    return o[0], fs, cu
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_midpad"])
+def test_tiny_full_oracle(name):
+    wl = workloads.make_workload(name)
+    o, fs, cu = _run_wl(wl)
+    ro, rfs = oracle.chunk_kda_varlen(f64(wl.q), f64(wl.k), f64(wl.v), f64(wl.g), f64(wl.beta), cu)
+    check_close(f64(o), ro, "f32", "o")
+    check_close(f64(fs), rfs, "f32", "final_state")
+    assert np.all(f64(o)[cu[-1]:] == 0)
+
+
+def test_ling3_tiny_sample_full_oracle():
+    wl = workloads.make_workload("ling3_tiny_sample", conv=False)
+    o, fs, cu = _run_wl(wl)
+    ro, rfs = oracle.chunk_kda_varlen(f64(wl.q), f64(wl.k), f64(wl.v), f64(wl.g), f64(wl.beta), cu)
+    check_close(f64(o), ro, "bf16", "o")
+    check_close(f64(fs), rfs, "bf16", "final_state")
+    for i in range(len(cu) - 1):
+        if cu[i + 1] > cu[i]:
+            check_close(f64(o)[cu[i]:cu[i + 1]], ro[cu[i]:cu[i + 1]], "bf16", f"o segment {i}")
+
+
+def _sampled(wl, o, fs, cu, segs, heads):
+    dt = wl.cfg.dtype
+    got, ref, gfs, rfs = [], [], [], []
+    for i in segs:
+        a, e = int(cu[i]), int(cu[i + 1])
+        for h in heads:
+            print(f"  oracle segment {i} [{a},{e}) head {h}", flush=True)
+            ro, rf = oracle_segment_head(wl, a, e, h)
+            go = f64(o[a:e, h])
+            check_close(go, ro, dt, f"o segment {i} head {h}")
+            got.append(go.ravel()); ref.append(ro.ravel())
+            if fs is not None:
+                gf = f64(fs[i, h])
+                check_close(gf, rf, dt, f"state segment {i} head {h}")
+                gfs.append(gf.ravel()); rfs.append(rf.ravel())
+    check_close(np.concatenate(got), np.concatenate(ref), dt, "o sampled")
+    if gfs:
+        check_close(np.concatenate(gfs), np.concatenate(rfs), dt, "states sampled")
+
+
+@pytest.mark.parametrize("name", ["flat_microbatch", "many_short_docs", "long_context"])
+def test_full_size_sampled(name):
+    wl = workloads.make_workload(name)
+    o, fs, cu = _run_wl(wl, final_state=True)
+    lens = np.diff(cu)
+    real = [i for i in range(len(lens)) if lens[i] > 0]
+    order = sorted(real, key=lambda i: lens[i])
+    rng = np.random.default_rng(99)
+    pick = sorted(set([order[0], order[-1], order[len(order) // 2]] +
+                      [int(x) for x in rng.choice(real, size=min(3, len(real)), replace=False)]))
+    heads = sorted(set([0, wl.cfg.H - 1, int(rng.integers(0, wl.cfg.H))]))
+    if name == "long_context":
+        heads = [0, wl.cfg.H - 1]
+    _sampled(wl, o, fs, cu, pick, heads)
+    # uncovered tail and phantom slots
+    assert torch.count_nonzero(o[int(cu[-1]):]).item() == 0
+    for i in range(len(lens)):
+        if lens[i] == 0:
+            assert torch.count_nonzero(fs[i]).item() == 0
+
+
+def _small_case(rng, N, H, Dk, Dv, dtype, cu):
+    q = rng.standard_normal((N, H, Dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((N, H, Dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((N, H, Dv))
+    g = -rng.uniform(0.01, 0.3, (N, H, Dk))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((N, H))))
+    ts = [torch.from_numpy(a).to(dtype) for a in (q, k, v, g, beta)]
+    return ts
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("Dk,Dv", [(32, 32), (64, 64), (128, 128), (32, 128), (128, 64), (64, 32)])
+def test_small_shapes(dtype, Dk, Dv):
+    pkv = _pkv()
+    rng = np.random.default_rng(Dk * 7 + Dv)
+    H = 3
+    lens = [1, 63, 64, 65, 2, 127, 128, 129, 16, 17, 200]
+    cu = np.concatenate([[0], np.cumsum(lens), [sum(lens)] * 2])      # two phantom slots
+    N = sum(lens) + 37                                                 # uncovered tail
+    ts = _small_case(rng, N, H, Dk, Dv, dtype, cu)
+    q, k, v, g, beta = [t.to(device()) for t in ts]
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    o, fs = pkv.chunk_kda_varlen(q[None], k[None], v[None], g[None], beta[None], cud, scale=0.5)
+    torch.cuda.synchronize()
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], cu, scale=0.5)
+    dt = "f32" if dtype == torch.float32 else "bf16"
+    check_close(f64(o[0]), ro, dt, "o")
+    check_close(f64(fs), rfs, dt, "final_state")
+    for i in range(len(cu) - 1):
+        if cu[i + 1] > cu[i]:
+            check_close(f64(o[0])[cu[i]:cu[i + 1]], ro[cu[i]:cu[i + 1]], dt, f"segment {i}")
+    assert torch.count_nonzero(o[0, cu[-1]:]).item() == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_no_cu_seqlens_is_one_segment(dtype):
+    pkv = _pkv()
+    rng = np.random.default_rng(5)
+    N, H, D = 301, 2, 64
+    ts = _small_case(rng, N, H, D, D, dtype, None)
+    q, k, v, g, beta = [t.to(device())[None] for t in ts]
+    o, fs = pkv.chunk_kda_varlen(q, k, v, g, beta, None)
+    torch.cuda.synchronize()
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], None)
+    dt = "f32" if dtype == torch.float32 else "bf16"
+    check_close(f64(o[0]), ro, dt, "o")
+    check_close(f64(fs), rfs, dt, "state")
+
+
+def test_leakage_row_independence_determinism():
+    pkv = _pkv()
+    wl = workloads.make_workload("many_short_docs")
+    q, k, v, g, beta = kda_inputs_to_device(wl)
+    cu = _cu(wl)
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    o1, f1 = pkv.chunk_kda_varlen(q, k, v, g, beta, cud)
+    o2, f2 = pkv.chunk_kda_varlen(q, k, v, g, beta, cud)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2), "not deterministic"
+    # perturb document 5 only: every other document is bit-identical
+    a, e = int(cu[5]), int(cu[6])
+    v2, q2, g2 = v.clone(), q.clone(), g.clone()
+    v2[0, a:e] *= -3
+    q2[0, a:e] += 1
+    g2[0, a:e] -= 0.5
+    o3, f3 = pkv.chunk_kda_varlen(q2, k, v2, g2, beta, cud)
+    torch.cuda.synchronize()
+    keep = torch.ones(wl.N, dtype=torch.bool, device=device())
+    keep[a:e] = False
+    assert torch.equal(o1[0, keep], o3[0, keep])
+    assert torch.equal(torch.cat([f1[:5], f1[6:]]), torch.cat([f3[:5], f3[6:]]))
+    assert not torch.equal(o1[0, a:e], o3[0, a:e])
+    # row independence: change the segment ids of row 3 only; rows 0..2 keep their bits
+    seg = wl.segment_ids.copy()
+    seg[3] = np.where(seg[3] > 0, (seg[3] + 1) // 2, 0)     # merge pairs of documents in row 3
+    cu_b = torch.from_numpy(oracle.segment_ids_to_cu_seqlens(seg, wl.cfg.max_segs)[0].astype(np.int32)).to(device())
+    o4, _ = pkv.chunk_kda_varlen(q, k, v, g, beta, cu_b)
+    torch.cuda.synchronize()
+    T = wl.cfg.T
+    assert torch.equal(o1[0, :3 * T], o4[0, :3 * T])
+    assert not torch.equal(o1[0, 3 * T:], o4[0, 3 * T:])
+
+
+def test_packed_equals_each_document_alone():
+    pkv = _pkv()
+    wl = workloads.make_workload("ling3_tiny_sample", conv=False)
+    q, k, v, g, beta = kda_inputs_to_device(wl)
+    cu = _cu(wl)
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    o, fs = pkv.chunk_kda_varlen(q, k, v, g, beta, cud)
+    for i in range(len(cu) - 1):
+        a, e = int(cu[i]), int(cu[i + 1])
+        if e <= a:
+            continue
+        oi, fi = pkv.chunk_kda_varlen(q[:, a:e].contiguous(), k[:, a:e].contiguous(), v[:, a:e].contiguous(),
+                                      g[:, a:e].contiguous(), beta[:, a:e].contiguous(), None)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, a:e], oi), f"segment {i}"
+        assert torch.equal(fs[i], fi[0]), f"segment {i}"
+
+
+def test_bad_cu_seqlens_sets_flag():
+    pkv = _pkv()
+    rng = np.random.default_rng(1)
+    N, H, D = 200, 2, 32
+    ts = _small_case(rng, N, H, D, D, torch.float32, None)
+    q, k, v, g, beta = [t.to(device())[None] for t in ts]
+    for bad in ([0, 50, 40, 120], [3, 50, 90, 120], [0, 50, 90, 250]):
+        cud = torch.tensor(bad, dtype=torch.int32, device=device())
+        flags = torch.zeros(1, dtype=torch.int32, device=device())
+        pkv.chunk_kda_varlen(q, k, v, g, beta, cud, flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) & pkv.FLAG_BAD_CU_SEQLENS, bad
