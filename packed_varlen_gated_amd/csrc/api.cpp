@@ -105,6 +105,10 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
     return PKV_ERR_INVALID_ARGUMENT;
   const size_t need = pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  if (pkv::kda_chunk_supported(Dk, Dv, dtype))
+    return from_hip(pkv::launch_kda_chunk(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
+                                          scale, o, final_state, flags,
+                                          static_cast<hipStream_t>(stream)));
   return from_hip(pkv::launch_kda_serial(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
                                          scale, dtype, o, final_state, flags,
                                          static_cast<hipStream_t>(stream)));

@@ -37,4 +37,11 @@ hipError_t launch_kda_serial(const void* q, const void* k, const void* v, const 
                              int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
                              void* o, float* final_state, int32_t* flags, hipStream_t stream);
 
+bool kda_chunk_supported(int32_t Dk, int32_t Dv, int32_t dtype);
+
+hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
+                            int32_t H, int32_t Dk, int32_t Dv, float scale, void* o,
+                            float* final_state, int32_t* flags, hipStream_t stream);
+
 }  // namespace pkv
