@@ -94,10 +94,11 @@ def read_traffic(workload):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(wl, cu, sample_tokens):
-    """The oracle, as it stands, on the first `sample_tokens` tokens of the
-    workload (segments clipped there), all heads, split by head over a process
-    pool. Returns a dict for the JSON line."""
+def cpu_baseline(wl, cu, sample_tokens, target_s=15.0):
+    """The oracle, as it stands, on the first S tokens of the workload
+    (segments clipped there), all heads, split by head over a process pool.
+    S = sample_tokens if given, else sized from a short timed prefix so the
+    measured run takes about target_s seconds. Returns a dict for the JSON line."""
     import multiprocessing as mp
     import numpy as np
     from concurrent.futures import ProcessPoolExecutor
@@ -105,27 +106,44 @@ def cpu_baseline(wl, cu, sample_tokens):
     cfg = wl.cfg
     ncores = len(os.sched_getaffinity(0))
     workers = max(1, min(16, ncores, cfg.H))
-    S = min(sample_tokens, wl.N)
-    cu_s = np.minimum(cu, S)
-    arrs = [t[:S].double().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]
     groups = np.array_split(np.arange(cfg.H), workers)
-    jobs = [tuple(a[:, gidx] for a in arrs) + (cu_s,) for gidx in groups]
+
+    def jobs(S):
+        cu_s = np.minimum(cu, S)
+        arrs = [t[:S].float().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]  # exact for bf16
+        return [tuple(a[:, gidx] for a in arrs) + (cu_s,) for gidx in groups]
+
     ctx = mp.get_context("spawn")  # workers never touch the GPU
     os.environ["OMP_NUM_THREADS"] = "1"
     with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
-        t0 = time.perf_counter()
-        list(ex.map(_oracle_job, jobs))
-        dt = time.perf_counter() - t0
+        list(ex.map(_warm, range(workers)))  # spawn and import outside the timed runs
+        if sample_tokens:
+            S = min(sample_tokens, wl.N)
+        else:
+            S0 = min(512, wl.N)
+            rate = S0 / max(ex.map(_oracle_job, jobs(S0)))
+            S = int(min(wl.N, max(S0, rate * target_s)) // 64 * 64) or S0
+        dt = max(ex.map(_oracle_job, jobs(S)))  # workers run in parallel: the slowest one
     return {"value": S / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"first {S} of {wl.N} tokens ({cfg.name}), all {cfg.H} heads, "
-                      f"fp64 token recurrence, {workers} processes split by head, {dt:.1f} s"}
+                      f"fp64 token recurrence, {workers} processes split by head, {dt:.1f} s "
+                      f"(slowest process, compute only)"}
+
+
+def _warm(_):
+    import oracle  # noqa: F401
+    return True
 
 
 def _oracle_job(args):
+    """Runs the oracle on one head group; returns its own run time (the data
+    transfer and the fp64 conversion are not timed)."""
+    import numpy as np
     import oracle
-    q, k, v, g, beta, cu = args
-    oracle.chunk_kda_varlen(q, k, v, g, beta, cu)
-    return True
+    q, k, v, g, beta = (a.astype(np.float64) for a in args[:5])
+    t0 = time.perf_counter()
+    oracle.chunk_kda_varlen(q, k, v, g, beta, args[5])
+    return time.perf_counter() - t0
 
 
 def main():
@@ -228,9 +246,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample_tokens or (2048 if cfg.Dk * cfg.Dv >= 128 * 128 else 8192)
-        log(f"cpu baseline: oracle on {sample} tokens ...")
-        cpu = cpu_baseline(wl, cu_host, sample)
+        log("cpu baseline: timing the oracle ...")
+        cpu = cpu_baseline(wl, cu_host, args.cpu_sample_tokens)
         log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
 
     line = {

@@ -3,12 +3,12 @@
 // Computes what RFC-0026 "Ling3 KDA varlen support" defines in its Background
 // section (KDA state leakage problem) with the reset of section 3.1.1:
 //   S_t = diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,  o_t = scale * S_t^T q_t,
-// S = 0 at every segment start; segments from cu_seqlens (RFC-0025 Design
-// sections 1 and 2). The page's own kernels (a TPU Pallas chunk_kda with
-// _align_seqs, chunk_local_cumsum_vector and kda_fwd_intra stages) are prior
-// art; this kernel keeps the chunked idea but aligns chunks to segment starts
-// by index arithmetic, so no chunk straddles a document and no padded copy of
-// the sequence is ever built.
+// S = 0 at every segment start; segments come from cu_seqlens (RFC-0025
+// Design sections 1 and 2). The page's own kernels (a TPU Pallas chunk_kda
+// with _align_seqs, chunk_local_cumsum_vector and kda_fwd_intra stages) are
+// prior art; this kernel keeps the chunked idea but aligns chunks to segment
+// starts by index arithmetic, so no chunk straddles a document and no padded
+// copy of the sequence is ever built.
 //
 // Math per 64-token chunk (b_r = in-chunk inclusive cumsum of g, base 2):
 //   o_r    = S_prev^T (q_r 2^{b_r})  +  sum_{s<=r} A[r,s] v_s
@@ -22,20 +22,21 @@
 // it). Per element only 2^{c} and 2^{T - c} are evaluated (c = in-sub-chunk
 // cumsum); every other factor is per channel.
 //
-// Work-group: Dv/16 waves (8 at Dv = 128, two per SIMD) per (segment, head).
-// Wave e owns the fp32 state columns [16e, 16e + 16) in registers.
-//  1. prep: wave w takes sub-chunk w%4 and a share of the channels; lane =
-//     4 tokens x CPL channels (8-byte buffer loads; rows past the chunk end
-//     read 0 through the buffer range check). In-lane prefix + DPP quad scan
-//     give c; sub-chunk totals go to LDS.                              barrier
-//     Per-channel factors (one lane of each quad per channel, DPP broadcast),
-//     then bf16 operands to LDS: Q^ = q 2^b, the query versions of the ten A
-//     blocks, KE, Kbar^T = (beta k 2^{b_C - b})^T, V^T. The next chunk's
-//     loads are issued here.                                            barrier
-//  2. the ten A blocks (plus two zero blocks) on MFMA, masked and
-//     beta-scaled, to LDS.                                              barrier
-//  3. o^T = S^T Q^^T + V^T A^T for the wave's 16 columns, stored;
-//     S = diag(2^{b_C}) S + Kbar^T V.                                   barrier
+// Work-group per (segment, head): Dk/16 producer waves and 4 consumer waves,
+// software-pipelined over chunks (two barriers per chunk):
+//   first half  P: chunk c: gate cumsums and factors; Q^ = q 2^b and
+//                  Kbar^T = (beta k 2^{b_C - b})^T to the LDS buffers of c's
+//                  parity, the query versions of the ten A blocks and KE.
+//               C: chunk c-1: o^T = S^T Q^^T + V^T A^T for its Dv/4 columns,
+//                  stored; S = diag(2^{b_C}) S + Kbar^T V.
+//   second half P: V^T and 2^{b_C} of chunk c.
+//               C: the A blocks of chunk c (MFMA), masked, beta-scaled, to LDS.
+// Raw inputs of chunk c+1 are prefetched into registers during chunk c. Each
+// single-buffered LDS tile is written in one half and read in the other; Q^
+// and Kbar^T, read a step later, are double-buffered. A producer lane holds 4
+// consecutive tokens x 4 channels, so the cumsum is an in-lane prefix, a DPP
+// quad scan (the 16 tokens of a sub-chunk) and DPP row shifts (the four
+// sub-chunks), with no cross-wave exchange.
 // MFMA v_mfma_f32_16x16x32_bf16: A operand lane l holds row l%16 and eight
 // contraction slots of lane group l/16, B likewise for column l%16; the 16x16
 // fp32 result has column l%16 and rows 4(l/16)+i. The contraction index may be
@@ -71,26 +72,26 @@ __device__ __forceinline__ void block_of(int b, int& w, int& j) {
 
 template <int DK, int DV>
 struct Cfg {
-  static constexpr int NW = DV / 16;      // waves
-  static constexpr int NT = NW * 64;      // threads (= 4 * DV, the launch bound)
-  static constexpr int HALVES = NW / 4;   // channel shares per sub-chunk in the prep
-  static constexpr int CPL = DK / HALVES / 16;  // prep channels per lane
-  static constexpr int VPL = DV / HALVES / 16;  // staged v channels per lane
-  static constexpr int DT = DK / 16;      // 16-row state tiles
-  static constexpr int KS = DK / 32;      // contraction steps over Dk
-  static constexpr int KP = DK + 8;       // token-major LDS rows (bf16 elements)
-  static constexpr int TP = kC + 8;       // transposed / A rows (bf16 elements)
-  static constexpr int off_qh = 0;
-  static constexpr int off_qv = off_qh + kC * KP * 2;
+  static constexpr int NP = DK / 16;     // producer waves (16 channels each)
+  static constexpr int NT = 64 * (NP + 4);  // threads: producers + 4 consumers
+  static constexpr int PCPL = 4;         // producer channels per lane (4 tokens each)
+  static constexpr int PVPL = DV / NP / 4;  // producer v channels per lane
+  static constexpr int EW = DV / 4;      // consumer state / output columns
+  static constexpr int ET = EW / 16;     // 16-column tiles per consumer
+  static constexpr int DT = DK / 16;     // 16-row state tiles
+  static constexpr int KS = DK / 32;     // contraction steps over Dk
+  static constexpr int KP = DK + 8;      // token-major LDS rows (bf16 elements)
+  static constexpr int TP = kC + 8;      // transposed / A rows (bf16 elements)
+  static constexpr int off_qh = 0;                           // two buffers
+  static constexpr int off_qv = off_qh + 2 * kC * KP * 2;
   static constexpr int off_ke = off_qv + 10 * 16 * KP * 2;
-  static constexpr int off_kbT = off_ke + kC * KP * 2;
-  static constexpr int off_vT = off_kbT + DK * TP * 2;
+  static constexpr int off_kbT = off_ke + kC * KP * 2;        // two buffers
+  static constexpr int off_vT = off_kbT + 2 * DK * TP * 2;
   static constexpr int off_a = off_vT + DV * TP * 2;
-  static constexpr int off_T = off_a + kC * TP * 2;      // float [4][DK]
-  static constexpr int off_decay = off_T + 4 * DK * 4;   // float [DK]
+  static constexpr int off_decay = off_a + kC * TP * 2;  // float [DK]
   static constexpr int off_beta = off_decay + DK * 4;    // float [kC]
   static constexpr int bytes = off_beta + kC * 4;
-  static_assert(CPL >= 2 && CPL <= 8 && VPL >= 2 && VPL <= 8, "prep layout");
+  static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
 template <int n>
@@ -104,32 +105,37 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Quad-permute DPP move (lane i of each quad receives lane SEL[i]).
+// DPP move; lanes whose source lies outside the row read 0.
 template <int CTRL>
-__device__ __forceinline__ float qperm(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
+constexpr int kQuadPrev1 = 0x90;  // quad_perm [0,0,1,2]
+constexpr int kQuadPrev2 = 0x40;  // quad_perm [0,0,0,1]
+constexpr int kRowShr4 = 0x114;   // row_shr:4
+constexpr int kRowShr8 = 0x118;   // row_shr:8
+constexpr int kRowShl4 = 0x104;   // row_shl:4
+constexpr int kRowShl8 = 0x108;   // row_shl:8
+constexpr int kRowShl12 = 0x10C;  // row_shl:12
 template <int L>
 __device__ __forceinline__ float qbcast(float x) {
-  return qperm<L | (L << 2) | (L << 4) | (L << 6)>(x);
+  return dpp<L | (L << 2) | (L << 4) | (L << 6)>(x);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufFlags);
 }
 
-// n bf16 values from a raw buffer (n in {2, 4, 8}); out-of-range reads give 0.
+// n bf16 values from a raw buffer (n in {4, 8}); out-of-range reads give 0.
 template <int n>
 __device__ __forceinline__ BfPack<n> bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   BfPack<n> p;
-  if constexpr (n == 2) {
-    const int x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-    __builtin_memcpy(&p, &x, 4);
-  } else if constexpr (n == 4) {
+  if constexpr (n == 4) {
     typedef int v2 __attribute__((ext_vector_type(2)));
     const v2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     __builtin_memcpy(&p, &x, 8);
   } else {
+    static_assert(n == 8, "load width");
     typedef int v4 __attribute__((ext_vector_type(4)));
     const v4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     __builtin_memcpy(&p, &x, 16);
@@ -137,40 +143,85 @@ __device__ __forceinline__ BfPack<n> bload(__amdgpu_buffer_rsrc_t r, uint32_t of
   return p;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Two floats -> one register of two bf16 (round to nearest even), a single
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// Four floats -> four bf16 at an 8-byte aligned address.
+__device__ __forceinline__ void st4(bf16* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pk2(a, b), pk2(c, d)};
+}
+__device__ __forceinline__ void st4(bf16* dst, const float* x) { st4(dst, x[0], x[1], x[2], x[3]); }
+
+// Raw producer inputs of one chunk: 4 tokens x PCPL channels of q, k, g and
+// PVPL channels of v as packed bf16 pairs, and beta. They stay packed until used, so the prefetch of
+// the next chunk is never waited for early.
+template <int PCPL, int PVPL>
+struct Raw {
+  uint32_t g[4][PCPL / 2], q[4][PCPL / 2], k[4][PCPL / 2];
+  uint32_t v[4][PVPL / 2];
+  uint32_t b[4];
+};
+
+// bf16 element c of a packed pair array, as fp32 (exact).
 template <int n>
-__device__ __forceinline__ void lds_put(bf16* dst, const float* x) {
-  BfPack<n> p;
+__device__ __forceinline__ float bf(const uint32_t (&w)[n], int c) {
+  const uint32_t x = w[c >> 1];
+  return __uint_as_float((c & 1) ? (x & 0xFFFF0000u) : (x << 16));
+}
+
+// 2n packed bf16 values (n in {2, 4}) from a raw buffer; out-of-range reads give 0.
+template <int n>
+__device__ __forceinline__ void wload(uint32_t (&w)[n], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (n == 1) {
+    w[0] = uint32_t(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  } else if constexpr (n == 2) {
+    typedef int v2 __attribute__((ext_vector_type(2)));
+    const v2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = uint32_t(x[0]);
+    w[1] = uint32_t(x[1]);
+  } else {
+    static_assert(n == 4, "load width");  // n in {1, 2, 4}
+    typedef int v4 __attribute__((ext_vector_type(4)));
+    const v4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 #pragma unroll
-  for (int c = 0; c < n; ++c) p.v[c] = from_f32<bf16>(x[c]);
-  *reinterpret_cast<BfPack<n>*>(dst) = p;
+    for (int i = 0; i < 4; ++i) w[i] = uint32_t(x[i]);
+  }
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(4 * DV, 1) void kda_chunk_kernel(
+__global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
     int32_t max_segs, int64_t N, int32_t H, float scale, bf16* __restrict__ o,
     float* __restrict__ final_state, int32_t* __restrict__ flags) {
   using C = Cfg<DK, DV>;
-  constexpr int NT = C::NT, CPL = C::CPL, VPL = C::VPL, DT = C::DT, KS = C::KS;
+  constexpr int NP = C::NP, NT = C::NT;
+  constexpr int PCPL = C::PCPL, PVPL = C::PVPL, ET = C::ET, DT = C::DT, KS = C::KS;
   constexpr int KP = C::KP, TP = C::TP;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16* s_qh = reinterpret_cast<bf16*>(smem + C::off_qh);
+  bf16* s_qh0 = reinterpret_cast<bf16*>(smem + C::off_qh);     // Q^ of even / odd chunks
+  bf16* s_qh1 = s_qh0 + kC * KP;
   bf16* s_qv = reinterpret_cast<bf16*>(smem + C::off_qv);
   bf16* s_ke = reinterpret_cast<bf16*>(smem + C::off_ke);
-  bf16* s_kbT = reinterpret_cast<bf16*>(smem + C::off_kbT);
+  bf16* s_kbT0 = reinterpret_cast<bf16*>(smem + C::off_kbT);   // Kbar^T of even / odd chunks
+  bf16* s_kbT1 = s_kbT0 + DK * TP;
   bf16* s_vT = reinterpret_cast<bf16*>(smem + C::off_vT);
   bf16* s_a = reinterpret_cast<bf16*>(smem + C::off_a);
-  float* s_T = reinterpret_cast<float*>(smem + C::off_T);
   float* s_decay = reinterpret_cast<float*>(smem + C::off_decay);
   float* s_beta = reinterpret_cast<float*>(smem + C::off_beta);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int gq = lane >> 4;
-  const int lr = lane & 15;
+  const bool producer = w < NP;
   const int64_t seg_blocks = int64_t(max_segs) * H;
 
   if (int64_t(blockIdx.x) >= seg_blocks) {
@@ -198,264 +249,347 @@ __global__ __launch_bounds__(4 * DV, 1) void kda_chunk_kernel(
     }
   }
   const int nchunks = int((end - start + kC - 1) / kC);
-
-  // Prep coordinates: sub-chunk sc, channel share; lane = (channel group cg, token quad tq).
-  const int sc = w & 3;
-  const int share = w >> 2;
-  const int cg = lane >> 2;
-  const int tq = lane & 3;
-  const int ch0 = share * (DK / C::HALVES) + cg * CPL;   // first prep channel of the lane
-  const int vch0 = share * (DV / C::HALVES) + cg * VPL;  // first staged v channel
-  const int tok0 = 16 * sc + 4 * tq;                     // first token (in chunk) of the lane
-  const uint32_t rowK = uint32_t(H) * DK * 2;            // bytes between tokens (q, k, g)
+  const uint32_t rowK = uint32_t(H) * DK * 2;  // bytes between tokens (q, k, g)
   const uint32_t rowV = uint32_t(H) * DV * 2;
   const uint32_t rowB = uint32_t(H) * 2;
-  // State / output coordinates: 16 columns per wave.
-  const int e0 = 16 * w;
+  auto chunk_len = [&](int c) {
+    const int64_t rem = end - (start + int64_t(c) * kC);
+    return int(rem < kC ? rem : kC);
+  };
 
-  f32x4 S[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) S[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---------------------------------------------------------------- roles
+  // Producer lane: 4 tokens [4tq, 4tq+4) of the chunk, PCPL channels.
+  const int tq = lane & 15;            // token group; sub-chunk = tq >> 2
+  const int qp = lane & 3;             // position in the quad (one sub-chunk)
+  const int sw = tq >> 2;              // producer's sub-chunk
+  const int cg = lane >> 4;            // channel group within the producer's share
+  const int ch0 = w * (DK / NP) + cg * PCPL;
+  const int vch0 = w * (DV / NP) + cg * PVPL;
+  const int tok0 = 4 * tq;
+  // Consumer lane (MFMA layout).
+  const int gq = lane >> 4;
+  const int lr = lane & 15;
+  const int ci = w - NP;               // consumer index 0..3
+  const int e0 = ci * C::EW;
 
-  BfPack<CPL> xg[4], xq[4], xk[4];
-  BfPack<VPL> xv[4];
-  float xb[4];
-
-  auto load_chunk = [&](int64_t p0, int Lc) {
+  // Loads are unconditional so the wait counts stay exact: a chunk index past
+  // the segment gets an empty buffer (every read returns 0, no memory access).
+  auto load_raw = [&](Raw<PCPL, PVPL>& R, int c) {
+    const bool live = c < nchunks;
+    const int64_t p0 = start + int64_t(live ? c : 0) * kC;
+    const int Lc = live ? chunk_len(c) : 1;
     const int64_t tokbase = p0 * H + h;
-    const uint32_t nK = uint32_t(Lc - 1) * rowK + DK * 2;
-    const uint32_t nV = uint32_t(Lc - 1) * rowV + DV * 2;
-    const uint32_t nB = uint32_t(Lc - 1) * rowB + 2;
+    const uint32_t nK = live ? uint32_t(Lc - 1) * rowK + DK * 2 : 0u;
+    const uint32_t nB = live ? uint32_t(Lc - 1) * rowB + 2 : 0u;
+    const uint32_t nV = live ? uint32_t(Lc - 1) * rowV + DV * 2 : 0u;
     const auto rq = rsrc(q + tokbase * DK, nK), rk = rsrc(k + tokbase * DK, nK);
     const auto rg = rsrc(g + tokbase * DK, nK), rv = rsrc(v + tokbase * DV, nV);
     const auto rb = rsrc(beta + tokbase, nB);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t t = uint32_t(tok0 + i);
-      xg[i] = bload<CPL>(rg, t * rowK + ch0 * 2);
-      xq[i] = bload<CPL>(rq, t * rowK + ch0 * 2);
-      xk[i] = bload<CPL>(rk, t * rowK + ch0 * 2);
-      xv[i] = bload<VPL>(rv, t * rowV + vch0 * 2);
-      const unsigned short bb = __builtin_amdgcn_raw_buffer_load_b16(rb, t * rowB, 0, 0);
-      xb[i] = __uint_as_float(uint32_t(bb) << 16);
+      wload(R.g[i], rg, t * rowK + ch0 * 2);
+      wload(R.q[i], rq, t * rowK + ch0 * 2);
+      wload(R.k[i], rk, t * rowK + ch0 * 2);
+      wload(R.v[i], rv, t * rowV + vch0 * 2);
+      R.b[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, t * rowB, 0, 0);
+    }
+  };
+  // ---- producer, first half: everything up to the A-block operands.
+  // Q^ and Kbar^T go to the LDS buffer of this chunk's parity; dec_out is
+  // carried to the second half. The lane's channels are processed four at a
+  // time (one per quad lane for the per-channel factors).
+  auto produce_a = [&](Raw<PCPL, PVPL>& R, bf16* s_qh, bf16* s_kbT, float* dec_out) {
+    const int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
+#pragma unroll
+    for (int hh = 0; hh < PCPL / 4; ++hh) {
+      float cs[4][4], Tw[4], fx[6];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int cc = 4 * hh + c4;
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          run = fmaf(bf(R.g[i], cc), kLog2e, run);
+          cs[i][c4] = run;
+        }
+        // prefix over the quad (the four token groups of one sub-chunk)
+        const float a1 = dpp<kQuadPrev1>(run);
+        const float s1 = run + (qp >= 1 ? a1 : 0.f);
+        const float a2 = dpp<kQuadPrev2>(s1);
+        const float inc = s1 + (qp >= 2 ? a2 : 0.f);
+        const float excl = inc - run;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs[i][c4] += excl;
+        const float T = qbcast<3>(inc);
+        // prefix over the four sub-chunks of the row (row shifts by 4 and 8 lanes)
+        const float T1 = dpp<kRowShr4>(T);     // previous sub-chunk's total (0 for sub-chunk 0)
+        const float T2 = dpp<kRowShr8>(T);     // total two sub-chunks back
+        const float y = T + T1;
+        const float z = y + dpp<kRowShr8>(y);  // rho_{w+1}
+        const float bC = z + dpp<kRowShl4>(T) + dpp<kRowShl8>(T) + dpp<kRowShl12>(T);  // b_C
+        Tw[c4] = T;
+        // exponents of the per-channel factors of channel cc, kept by quad lane c4
+        if (qp == c4) {
+          fx[0] = z - T;        // rho_w
+          fx[1] = bC - z;       // b_C - rho_{w+1}
+          fx[2] = -T;
+          fx[3] = T1;
+          fx[4] = T1 + T2;
+          fx[5] = bC;
+        }
+      }
+      float fm[5];
+#pragma unroll
+      for (int j = 0; j < 5; ++j) fm[j] = ex2(fx[j]);
+      dec_out[hh] = ex2(fx[5]);  // 2^{b_C} of channel 4hh + qp
+      // f[j][c4]: factor j of channel 4hh + c4, broadcast from quad lane c4
+      float f[5][4];
+#pragma unroll
+      for (int j = 0; j < 5; ++j) {
+        f[j][0] = qbcast<0>(fm[j]);
+        f[j][1] = qbcast<1>(fm[j]);
+        f[j][2] = qbcast<2>(fm[j]);
+        f[j][3] = qbcast<3>(fm[j]);
+      }
+      // f[0] = 2^{rho_w} (Q^ = Q~ f0); f[1] = 2^{b_C - rho_{w+1}} (Kbar = beta KE f1);
+      // f[2] = 2^{-T_w} (diagonal version); f[3] = 2^{T_{w-1}} (block (w, w-2));
+      // f[4] = 2^{T_{w-1} + T_{w-2}} (block (3, 0)).
+      float kb[4][4];  // [channel][token] for the transposed store
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = tok0 + i;
+        float qt[4], ke[4], t0[4];
+        const int chh = ch0 + 4 * hh;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int cc = 4 * hh + c4;
+          qt[c4] = bf(R.q[i], cc) * ex2(cs[i][c4]);
+          ke[c4] = bf(R.k[i], cc) * ex2(Tw[c4] - cs[i][c4]);
+          t0[c4] = qt[c4] * f[0][c4];
+          kb[c4][i] = ke[c4] * (__uint_as_float(R.b[i] << 16) * f[1][c4]);
+        }
+        st4(s_qh + tok * KP + chh, t0);
+        st4(s_ke + tok * KP + chh, ke);
+        bf16* qv = s_qv + (tok & 15) * KP + chh;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) t0[c4] = qt[c4] * f[2][c4];
+        st4(qv + (vbase + sw) * 16 * KP, t0);
+        if (sw >= 1) st4(qv + (vbase + sw - 1) * 16 * KP, qt);
+        if (sw >= 2) {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) t0[c4] = qt[c4] * f[3][c4];
+          st4(qv + (vbase + sw - 2) * 16 * KP, t0);
+        }
+        if (sw == 3) {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) t0[c4] = qt[c4] * f[4][c4];
+          st4(qv + (vbase + 0) * 16 * KP, t0);
+        }
+      }
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+        st4(s_kbT + (ch0 + 4 * hh + c4) * TP + tok0, kb[c4]);
+    }
+    if (w == 0 && cg == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_beta[tok0 + i] = __uint_as_float(R.b[i] << 16);
     }
   };
 
-  if (nchunks > 0) load_chunk(start, int((end - start) < kC ? (end - start) : kC));
+  // ---- producer, second half: V^T and 2^{b_C} of the chunk.
+  auto produce_b = [&](const float* dec_out, const uint32_t (&V)[4][PVPL / 2]) {
+    // V^T: channel pair (2j, 2j+1) of tokens tok0..tok0+3 -> two 8-byte rows.
+    static_assert(PVPL % 2 == 0, "v channels come in pairs");
+#pragma unroll
+    for (int j = 0; j < PVPL / 2; ++j) {
+      const uint32_t lo01 = __builtin_amdgcn_perm(V[1][j], V[0][j], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(V[3][j], V[2][j], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(V[1][j], V[0][j], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(V[3][j], V[2][j], 0x07060302u);
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u2*>(s_vT + (vch0 + 2 * j) * TP + tok0) = u2{lo01, lo23};
+      *reinterpret_cast<u2*>(s_vT + (vch0 + 2 * j + 1) * TP + tok0) = u2{hi01, hi23};
+    }
+    if (sw == 0) {
+#pragma unroll
+      for (int hh = 0; hh < PCPL / 4; ++hh) s_decay[ch0 + 4 * hh + qp] = dec_out[hh];
+    }
+  };
 
-  for (int c = 0; c < nchunks; ++c) {
+  // ---- consumer, first half: outputs and state update of chunk c.
+  // Operands are fetched in batches and the MFMAs ordered so that consecutive
+  // ones are independent (four row tiles x ET column tiles per step).
+  auto consume_state = [&](f32x4 (&S)[DT][ET], int c) {
     const int64_t p0 = start + int64_t(c) * kC;
-    const int Lc = int((end - p0) < kC ? (end - p0) : kC);
-
-    // ---- 1a. in-sub-chunk cumsum of the gates (base 2); sub-chunk totals.
-    float cs[4][CPL], Tw[CPL];
+    const int Lc = chunk_len(c);
+    const bf16* s_qh = (c & 1) ? s_qh1 : s_qh0;
+    const bf16* s_kbT = (c & 1) ? s_kbT1 : s_kbT0;
+    f32x4 acc[4][ET];
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) {
-      float run = 0.f;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        run = fmaf(to_f32(xg[i].v[cc]), kLog2e, run);
-        cs[i][cc] = run;
+      for (int et = 0; et < ET; ++et) acc[t][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // o^T += S^T Q^^T, contraction over Dk in steps of 32
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      bf16x8 bq[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16* row = s_qh + (16 * t + lr) * KP + 32 * u + 4 * gq;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
+        bq[t] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      // exclusive prefix over the quad's token groups, then the sub-chunk total
-      const float p1 = qperm<0x90>(run);  // quad lanes [0,0,1,2]
-      const float s1 = run + (tq >= 1 ? p1 : 0.f);
-      const float p2 = qperm<0x40>(s1);   // quad lanes [0,0,0,1]
-      const float inc = s1 + (tq >= 2 ? p2 : 0.f);
-      const float excl = inc - run;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cs[i][cc] += excl;
-      Tw[cc] = qbcast<3>(inc);
-    }
-    if (tq == 0) {
+      for (int et = 0; et < ET; ++et) {
+        const f32x4 x = S[2 * u][et], y = S[2 * u + 1][et];
+        const bf16x8 sop = __builtin_bit_cast(
+            bf16x8, u32x4{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(y[0], y[1]), pk2(y[2], y[3])});
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) s_T[sc * DK + ch0 + cc] = Tw[cc];
+        for (int t = 0; t < 4; ++t) acc[t][et] = mfma(sop, bq[t], acc[t][et]);
+      }
     }
-    if (share == 0 && cg == 0) {
+    // o^T += V^T A^T, contraction over tokens in steps of 32 (causal: rows >= 32 only for the second)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_beta[tok0 + i] = xb[i];
+    for (int m2 = 0; m2 < 2; ++m2) {
+      bf16x8 va[ET], aa[4];
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+        va[et] = *reinterpret_cast<const bf16x8*>(s_vT + (e0 + 16 * et + lr) * TP + 32 * m2 + 8 * gq);
+#pragma unroll
+      for (int t = 2 * m2; t < 4; ++t)
+        aa[t] = *reinterpret_cast<const bf16x8*>(s_a + (16 * t + lr) * TP + 32 * m2 + 8 * gq);
+#pragma unroll
+      for (int t = 2 * m2; t < 4; ++t)
+#pragma unroll
+        for (int et = 0; et < ET; ++et) acc[t][et] = mfma(va[et], aa[t], acc[t][et]);
     }
-    __syncthreads();
+    const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
+    typedef int v2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const f32x4 x = acc[t][et];
+        const v2 bits = {int(pk2(x[0] * scale, x[1] * scale)), int(pk2(x[2] * scale, x[3] * scale))};
+        // rows past the chunk end fall outside the buffer range and are dropped
+        __builtin_amdgcn_raw_buffer_store_b64(bits, ro,
+                                              uint32_t(16 * t + lr) * rowV + (e0 + 16 * et + 4 * gq) * 2, 0, 0);
+      }
+    // S = diag(2^{b_C}) S + Kbar^T V
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(s_decay + 16 * dt + 4 * gq);
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[dt][et][i] *= dec[i];
+    }
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      bf16x8 vb[ET], kb[DT];
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+        vb[et] = *reinterpret_cast<const bf16x8*>(s_vT + (e0 + 16 * et + lr) * TP + 32 * m2 + 8 * gq);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        kb[dt] = *reinterpret_cast<const bf16x8*>(s_kbT + (16 * dt + lr) * TP + 32 * m2 + 8 * gq);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int et = 0; et < ET; ++et) S[dt][et] = mfma(kb[dt], vb[et], S[dt][et]);
+    }
+  };
 
-    // ---- 1b. per-channel factors: lane tq computes channels cc = tq (mod 4).
-    constexpr int FM = (CPL + 3) / 4;
-    float fQh_m[FM], fKb_m[FM], fd_m[FM], fo0_m[FM], fo1_m[FM];
+  // ---- consumer, second half: the A blocks of the chunk just prepared
+  // (three jobs per consumer, their MFMAs interleaved).
+  auto consume_a = [&]() {
+    int bw[3], bj[3];
 #pragma unroll
-    for (int m = 0; m < FM; ++m) {
-      const int cc = 4 * m + tq;
-      const int ch = ch0 + (cc < CPL ? cc : 0);
-      float rho[5];
-      rho[0] = 0.f;
+    for (int jb = 0; jb < 3; ++jb) block_of(ci + 4 * jb, bw[jb], bj[jb]);
+    const bool third = ci + 8 < 10;  // jobs 10 and 11 only zero their block
+    f32x4 acc[3];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rho[j + 1] = rho[j] + s_T[j * DK + ch];
-      float rw = rho[0], rw1 = rho[1];
+    for (int jb = 0; jb < 3; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 1; j < 4; ++j)
-        if (j == sc) {
-          rw = rho[j];
-          rw1 = rho[j + 1];
+    for (int u = 0; u < KS; ++u) {
+      const int col = 32 * u + 8 * gq;
+      bf16x8 aop[3], bop[3];
+#pragma unroll
+      for (int jb = 0; jb < 3; ++jb) {
+        if (jb < 2 || third) {
+          aop[jb] = *reinterpret_cast<const bf16x8*>(s_ke + (16 * bj[jb] + lr) * KP + col);
+          bop[jb] = *reinterpret_cast<const bf16x8*>(s_qv + ((ci + 4 * jb) * 16 + lr) * KP + col);
         }
-      fQh_m[m] = ex2(rw);
-      fKb_m[m] = ex2(rho[4] - rw1);
-      fd_m[m] = ex2(rw - rw1);
-      fo0_m[m] = ex2(rw - rho[1]);  // query factor of block (sc, 0) when sc >= 2
-      fo1_m[m] = ex2(rw - rho[2]);  // query factor of block (3, 1)
-      if (sc == 0 && cc < CPL) s_decay[ch] = ex2(rho[4]);
-    }
-    float fQh[CPL], fKb[CPL], fd[CPL], fo0[CPL], fo1[CPL];
-#pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) {
-      const int m = cc / 4;
-      switch (cc % 4) {
-        case 0: fQh[cc] = qbcast<0>(fQh_m[m]); fKb[cc] = qbcast<0>(fKb_m[m]); fd[cc] = qbcast<0>(fd_m[m]);
-                fo0[cc] = qbcast<0>(fo0_m[m]); fo1[cc] = qbcast<0>(fo1_m[m]); break;
-        case 1: fQh[cc] = qbcast<1>(fQh_m[m]); fKb[cc] = qbcast<1>(fKb_m[m]); fd[cc] = qbcast<1>(fd_m[m]);
-                fo0[cc] = qbcast<1>(fo0_m[m]); fo1[cc] = qbcast<1>(fo1_m[m]); break;
-        case 2: fQh[cc] = qbcast<2>(fQh_m[m]); fKb[cc] = qbcast<2>(fKb_m[m]); fd[cc] = qbcast<2>(fd_m[m]);
-                fo0[cc] = qbcast<2>(fo0_m[m]); fo1[cc] = qbcast<2>(fo1_m[m]); break;
-        default: fQh[cc] = qbcast<3>(fQh_m[m]); fKb[cc] = qbcast<3>(fKb_m[m]); fd[cc] = qbcast<3>(fd_m[m]);
-                 fo0[cc] = qbcast<3>(fo0_m[m]); fo1[cc] = qbcast<3>(fo1_m[m]); break;
       }
-    }
-
-    // ---- 1c. bf16 operands.
-    const int vbase = (sc * (sc + 1)) / 2;  // LDS slot of block (sc, 0)
-    float kb4[CPL][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = tok0 + i;
-      const float bt = xb[i];
-      float qt[CPL], tmp[CPL], ke[CPL];
-#pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) {
-        qt[cc] = to_f32(xq[i].v[cc]) * ex2(cs[i][cc]);
-        ke[cc] = to_f32(xk[i].v[cc]) * ex2(Tw[cc] - cs[i][cc]);
-        kb4[cc][i] = ke[cc] * (bt * fKb[cc]);
-        tmp[cc] = qt[cc] * fQh[cc];
-      }
-      lds_put<CPL>(s_qh + tok * KP + ch0, tmp);
-      lds_put<CPL>(s_ke + tok * KP + ch0, ke);
-      bf16* qv = s_qv + (4 * tq + i) * KP + ch0;
-      // block (sc, sc): diagonal factor
-#pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) tmp[cc] = qt[cc] * fd[cc];
-      lds_put<CPL>(qv + (vbase + sc) * 16 * KP, tmp);
-      if (sc >= 1) lds_put<CPL>(qv + (vbase + sc - 1) * 16 * KP, qt);  // block (sc, sc-1)
-      if (sc >= 2) {
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) tmp[cc] = qt[cc] * fo0[cc];
-        lds_put<CPL>(qv + (vbase + 0) * 16 * KP, tmp);                  // block (sc, 0)
-      }
-      if (sc == 3) {
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) tmp[cc] = qt[cc] * fo1[cc];
-        lds_put<CPL>(qv + (vbase + 1) * 16 * KP, tmp);                  // block (3, 1)
-      }
+      for (int jb = 0; jb < 3; ++jb)
+        if (jb < 2 || third) acc[jb] = mfma(aop[jb], bop[jb], acc[jb]);
     }
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) lds_put<4>(s_kbT + (ch0 + cc) * TP + tok0, kb4[cc]);
-#pragma unroll
-    for (int cc = 0; cc < VPL; ++cc) {
-      BfPack<4> p;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p.v[i] = xv[i].v[cc];
-      *reinterpret_cast<BfPack<4>*>(s_vT + (vch0 + cc) * TP + tok0) = p;
-    }
-    // Raw registers consumed: fetch the next chunk while this one computes.
-    if (c + 1 < nchunks) {
-      const int64_t p1 = p0 + kC;
-      load_chunk(p1, int((end - p1) < kC ? (end - p1) : kC));
-    }
-    __syncthreads();
-
-    // ---- 2. A blocks (s in sub-chunk j, r in sub-chunk bw) -> A[r][s] in LDS.
-#pragma unroll
-    for (int job = w; job < 12; job += C::NW) {
-      int bw, bj;
-      block_of(job, bw, bj);
-      bf16x4 out;
-      if (job < 10) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < KS; ++u) {
-          const int col = 32 * u + 8 * gq;
-          const bf16x8 aop = *reinterpret_cast<const bf16x8*>(s_ke + (16 * bj + lr) * KP + col);
-          const bf16x8 bop = *reinterpret_cast<const bf16x8*>(s_qv + (job * 16 + lr) * KP + col);
-          acc = mfma(aop, bop, acc);
-        }
+    for (int jb = 0; jb < 3; ++jb) {
+      float out[4] = {0.f, 0.f, 0.f, 0.f};
+      if (jb < 2 || third) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int sl = 4 * gq + i;
-          const bool keep = (bj < bw) || (sl <= lr);
-          out[i] = from_f32<bf16>(keep ? acc[i] * s_beta[16 * bj + sl] : 0.f);
+          const bool keep = (bj[jb] < bw[jb]) || (sl <= lr);
+          out[i] = keep ? acc[jb][i] * s_beta[16 * bj[jb] + sl] : 0.f;
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = from_f32<bf16>(0.f);
       }
-      *reinterpret_cast<bf16x4*>(s_a + (16 * bw + lr) * TP + 16 * bj + 4 * gq) = out;
+      st4(s_a + (16 * bw[jb] + lr) * TP + 16 * bj[jb] + 4 * gq, out);
     }
-    __syncthreads();
+  };
 
-    // ---- 3. outputs for columns [e0, e0 + 16), then the state update.
-    {
-      bf16x8 sop[KS];
-#pragma unroll
-      for (int u = 0; u < KS; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sop[u][i] = from_f32<bf16>(S[2 * u][i]);
-          sop[u][4 + i] = from_f32<bf16>(S[2 * u + 1][i]);
-        }
-      const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
-      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(s_vT + (e0 + lr) * TP + 8 * gq);
-      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(s_vT + (e0 + lr) * TP + 32 + 8 * gq);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (16 * t < Lc) {
-          const int rrow = 16 * t + lr;
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int u = 0; u < KS; ++u) {
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(s_qh + rrow * KP + 32 * u + 4 * gq);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(s_qh + rrow * KP + 32 * u + 16 + 4 * gq);
-            const bf16x8 bop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc = mfma(sop[u], bop, acc);
-          }
-          acc = mfma(v0, *reinterpret_cast<const bf16x8*>(s_a + rrow * TP + 8 * gq), acc);
-          if (t >= 2) acc = mfma(v1, *reinterpret_cast<const bf16x8*>(s_a + rrow * TP + 32 + 8 * gq), acc);
-          typedef int v2 __attribute__((ext_vector_type(2)));
-          bf16x4 out;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) out[i] = from_f32<bf16>(acc[i] * scale);
-          v2 bits;
-          __builtin_memcpy(&bits, &out, 8);
-          __builtin_amdgcn_raw_buffer_store_b64(bits, ro, uint32_t(rrow) * rowV + (e0 + 4 * gq) * 2, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 dec = *reinterpret_cast<const f32x4*>(s_decay + 16 * dt + 4 * gq);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[dt][i] *= dec[i];
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s_kbT + (16 * dt + lr) * TP + 8 * gq);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s_kbT + (16 * dt + lr) * TP + 32 + 8 * gq);
-        S[dt] = mfma(a0, v0, S[dt]);
-        S[dt] = mfma(a1, v1, S[dt]);
-      }
+  // ---------------------------------------------------------------- pipeline
+  // Producers and consumers run separate loops with the same barrier sequence
+  // (two per step), so neither role keeps the other's registers live.
+  if (producer) {
+    Raw<PCPL, PVPL> cur, nxt;
+    float dec_out[PCPL / 4];
+    load_raw(cur, 0);
+    for (int s = 0; s <= nchunks; s += 2) {
+      // even chunk s: LDS buffers 0; odd chunk s + 1: buffers 1
+      load_raw(nxt, s + 1);
+      if (s < nchunks) produce_a(cur, s_qh0, s_kbT0, dec_out);
+      __syncthreads();
+      if (s < nchunks) produce_b(dec_out, cur.v);
+      __syncthreads();
+      if (s + 1 > nchunks) break;
+      load_raw(cur, s + 2);
+      if (s + 1 < nchunks) produce_a(nxt, s_qh1, s_kbT1, dec_out);
+      __syncthreads();
+      if (s + 1 < nchunks) produce_b(dec_out, nxt.v);
+      __syncthreads();
     }
-    __syncthreads();
-  }
-
-  if (final_state != nullptr) {
-    float* fs = final_state + (int64_t(slot) * H + h) * DK * DV;
+  } else {
+    f32x4 S[DT][ET];  // state rows [0, DK), columns [e0, e0 + EW)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + lr] = S[dt][i];
+      for (int et = 0; et < ET; ++et) S[dt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s <= nchunks; s += 2) {
+      if (s >= 1) consume_state(S, s - 1);
+      __syncthreads();
+      if (s < nchunks) consume_a();
+      __syncthreads();
+      if (s + 1 > nchunks) break;
+      consume_state(S, s);
+      __syncthreads();
+      if (s + 1 < nchunks) consume_a();
+      __syncthreads();
+    }
+    if (final_state != nullptr) {
+      float* fs = final_state + (int64_t(slot) * H + h) * DK * DV;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int et = 0; et < ET; ++et)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + 16 * et + lr] = S[dt][et][i];
+    }
   }
 }
 
