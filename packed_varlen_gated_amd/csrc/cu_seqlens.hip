@@ -9,13 +9,21 @@
 // segment); the last real segment ends one past the last non-zero position.
 // doc(p) follows "Drill: Sequence Packing from scratch", section "The math".
 //
-// One work-group of 1024 threads walks the flattened buffer in tiles of 8192
-// positions (8 consecutive positions per thread). Pass 1 counts boundaries and
-// finds the last real token; pass 2 re-reads the (now L2-resident) ids, runs a
-// block-wide exclusive scan of the per-thread boundary counts (wave shuffles +
-// one LDS exchange per tile) and scatters. The ids of one 8B*T buffer are at
-// most a few hundred KiB, so one CU finishes in a few microseconds and no
-// cross-work-group synchronisation or scratch memory is needed.
+// One work-group of 1024 threads. The buffer is cut into groups of 4
+// consecutive positions and tiles of 16384 groups (65536 positions):
+//   0. only when token_seg is requested over more than one tile: the last
+//      non-zero position, by a backward sweep (one step covers 4096
+//      positions; packed batches end in at most a short pad);
+//   A. each thread loads groups tid, tid + 1024, ... (16-byte coalesced
+//      loads, all in flight at once), writes each group's 4 boundary bits to
+//      LDS and tracks the last non-zero position;
+//   B. each thread takes 16 consecutive groups from LDS, a block-wide scan
+//      of their boundary counts gives every boundary its rank k, and the
+//      k-th boundary scatters its position into cu[k-1];
+//   C. only when token_seg is requested: every position's segment index,
+//      from the per-group ranks left in LDS, with coalesced 16-byte stores.
+// The ids are read from HBM once; the bitmask and ranks of a tile take 48 KiB
+// of LDS. No cross-work-group synchronisation or scratch memory is needed.
 
 #include "common.h"
 
@@ -24,98 +32,133 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kPerThread = 8;
-constexpr int64_t kTile = int64_t(kThreads) * kPerThread;
+constexpr int kGroupsPerThread = 16;
+constexpr int kTileGroups = kThreads * kGroupsPerThread;  // 16384
+constexpr int64_t kTilePos = 4 * int64_t(kTileGroups);    // 65536
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, 64);
+    const int y = __shfl_up(x, d, 64);
     if (lane >= d) x += y;
   }
-  return x;
-}
-
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
   return x;
 }
 
 __device__ __forceinline__ int64_t wave_max64(int64_t x) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
-    int64_t y = __shfl_xor(x, d, 64);
+    const int64_t y = __shfl_xor(x, d, 64);
     x = y > x ? y : x;
   }
   return x;
 }
 
-// Boundary bits of positions p0 .. p0+7 (bit j for p0 + j), positions >= N are 0.
-__device__ __forceinline__ unsigned boundary_bits(const int32_t* __restrict__ seg, int64_t p0,
-                                                  int64_t N, int64_t T, int64_t* last_nz) {
-  unsigned bits = 0;
-  int prev = (p0 > 0 && p0 < N) ? seg[p0 - 1] : 0;
-  int64_t row_pos = p0 % T;
+// Four ids at p .. p+3; positions >= N read as 0. kVec: seg is 16-byte aligned.
+template <bool kVec>
+__device__ __forceinline__ i32x4 load4(const int32_t* __restrict__ seg, int64_t p, int64_t N) {
+  if (kVec && p + 4 <= N) return *reinterpret_cast<const i32x4*>(seg + p);
+  i32x4 x = {0, 0, 0, 0};
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t p = p0 + j;
-    if (p < N) {
-      const int s = seg[p];
-      if (s != 0) {
-        *last_nz = p;
-        if (row_pos == 0 || s != prev) bits |= 1u << j;
-      }
-      prev = s;
-    }
-    row_pos = (row_pos + 1 == T) ? 0 : row_pos + 1;
-  }
-  return bits;
+  for (int i = 0; i < 4; ++i)
+    if (p + i < N) x[i] = seg[p + i];
+  return x;
 }
 
+template <bool kVec>
 __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
     const int32_t* __restrict__ seg, int64_t N, int64_t T, int32_t max_segs,
     int32_t* __restrict__ cu, int32_t* __restrict__ token_seg, int32_t* __restrict__ n_segs_out,
     int32_t* __restrict__ flags_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_bits[kTileGroups];   // boundary bits per group
+  __shared__ __attribute__((aligned(16))) uint16_t s_rank[kTileGroups];  // boundaries before the group (in tile)
   __shared__ int s_wsum[kWaves];
   __shared__ int64_t s_wmax[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
 
-  // Pass 1: number of boundaries and last real token.
-  int cnt = 0;
-  int64_t last = -1;
-  for (int64_t base = 0; base < N; base += kTile) {
-    const int64_t p0 = base + int64_t(tid) * kPerThread;
-    cnt += __popc(boundary_bits(seg, p0, N, T, &last));
-  }
-  cnt = wave_sum(cnt);
-  last = wave_max64(last);
-  if (lane == 0) {
-    s_wsum[wid] = cnt;
-    s_wmax[wid] = last;
-  }
-  __syncthreads();
-  int n = 0;
-  int64_t last_all = -1;
+  // 0. Last non-zero position (-1 if none), needed before the first tile's
+  // token indices only when there are several tiles.
+  int64_t last_nz = -1;
+  const bool sweep = token_seg != nullptr && N > kTilePos;
+  for (int64_t hi = sweep ? N : 0; hi > 0; hi -= 4 * kThreads) {
+    const int64_t lo = hi - 4 * kThreads;
+    const int64_t p = lo + 4 * int64_t(tid);
+    int64_t m = -1;
+    if (p + 3 >= 0) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    n += s_wsum[w];
-    last_all = s_wmax[w] > last_all ? s_wmax[w] : last_all;
+      for (int i = 0; i < 4; ++i)
+        if (p + i >= 0 && p + i < hi && seg[p + i] != 0) m = p + i;
+    }
+    m = wave_max64(m);
+    if (lane == 0) s_wmax[wid] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) last_nz = s_wmax[w] > last_nz ? s_wmax[w] : last_nz;
+    __syncthreads();
+    if (last_nz >= 0) break;  // uniform: every thread read the same values
   }
-  __syncthreads();
-  const int64_t e_last = last_all + 1;
-  const int lim = n < max_segs ? n : max_segs;
-  const int64_t cu_last = n > max_segs ? N : e_last;
 
-  // Pass 2: scan and scatter.
-  int running = 0;
-  for (int64_t base = 0; base < N; base += kTile) {
-    const int64_t p0 = base + int64_t(tid) * kPerThread;
-    int64_t dummy = -1;
-    const unsigned bits = boundary_bits(seg, p0, N, T, &dummy);
-    const int c = __popc(bits);
+  // Row position of a thread's first group in a tile, advanced by 4096 per group step.
+  const uint32_t T32 = uint32_t(T);
+  const uint32_t step = uint32_t(4 * kThreads) % T32;
+  int running = 0;  // boundaries before the tile
+  for (int64_t base = 0; base < N; base += kTilePos) {
+    // A. boundary bits of each group
+    uint32_t rp = uint32_t((base + 4 * int64_t(tid)) % T);
+    i32x4 xs[kGroupsPerThread];
+    int prevs[kGroupsPerThread];
+#pragma unroll
+    for (int j = 0; j < kGroupsPerThread; ++j) {
+      const int64_t p = base + 4 * int64_t(tid + kThreads * j);
+      xs[j] = i32x4{0, 0, 0, 0};
+      prevs[j] = 0;
+      if (p < N) {
+        xs[j] = load4<kVec>(seg, p, N);
+        prevs[j] = p > 0 ? seg[p - 1] : 0;
+      }
+    }
+    int64_t tile_nz = -1;
+#pragma unroll
+    for (int j = 0; j < kGroupsPerThread; ++j) {
+      const int m = tid + kThreads * j;
+      const int64_t p = base + 4 * int64_t(m);
+      unsigned bits = 0;
+      if (p < N) {
+        const i32x4 x = xs[j];
+        int prev = prevs[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // r = row position of p + i, plus T when it wrapped; r <= T + 2, so
+          // it is a multiple of T only as 0 or T, or 2T, 3T when T <= 2
+          const uint32_t r = rp + uint32_t(i);
+          const bool row_start = r == 0 || r == T32 || (T32 <= 2 && (r == 2 * T32 || r == 3 * T32));
+          if (p + i < N && x[i] != 0) {
+            tile_nz = p + i;
+            if (row_start || x[i] != prev) bits |= 1u << i;
+          }
+          prev = x[i];
+        }
+      }
+      s_bits[m] = uint8_t(bits);
+      rp += step;
+      if (rp >= T32) rp -= T32;
+    }
+    tile_nz = wave_max64(tile_nz);
+    if (lane == 0) s_wmax[wid] = tile_nz;
+    __syncthreads();
+    if (!sweep) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) last_nz = s_wmax[w] > last_nz ? s_wmax[w] : last_nz;
+    }
+
+    // B. ranks and scatter: thread tid owns groups [16 tid, 16 tid + 16)
+    const uint4 w4 = *reinterpret_cast<const uint4*>(s_bits + kGroupsPerThread * tid);
+    const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+    const int c = __popc(wd[0]) + __popc(wd[1]) + __popc(wd[2]) + __popc(wd[3]);
     const int incl = wave_incl_scan(c, lane);
     if (lane == 63) s_wsum[wid] = incl;
     __syncthreads();
@@ -126,30 +169,75 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
       wave_off += (w < wid) ? s : 0;
       tile_total += s;
     }
-    int kth = running + wave_off + incl - c;  // boundaries before p0
+    const int excl = wave_off + incl - c;  // boundaries in the tile before this thread's groups
+    if (token_seg != nullptr) {
+      // ranks of groups 2i, 2i + 1 packed in one word (each < 4 * kTileGroups = 65536)
+      uint32_t rk[kGroupsPerThread / 2];
+      uint32_t r = uint32_t(excl);
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int64_t p = p0 + j;
-      if (p < N) {
-        if ((bits >> j) & 1u) {
+      for (int gi = 0; gi < kGroupsPerThread; ++gi) {
+        if (gi & 1) rk[gi >> 1] |= r << 16;
+        else rk[gi >> 1] = r;
+        r += __popc((wd[gi >> 2] >> (8 * (gi & 3))) & 0xFu);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(s_rank + kGroupsPerThread * tid);
+      dst[0] = uint4{rk[0], rk[1], rk[2], rk[3]};
+      dst[1] = uint4{rk[4], rk[5], rk[6], rk[7]};
+    }
+    if (c != 0) {
+      int kth = running + excl;
+      const int64_t p0 = base + 4 * int64_t(kGroupsPerThread) * tid;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        uint32_t word = wd[qd];  // byte b holds the bits of group 4 qd + b
+        while (word != 0) {
+          const int bit = __builtin_ctz(word);
+          word &= word - 1;
           ++kth;
           // The kth boundary starts segment kth-1, which is where slot kth-2 ends.
-          if (kth >= 2 && kth <= lim) cu[kth - 1] = static_cast<int32_t>(p);
+          if (kth >= 2 && kth <= max_segs)
+            cu[kth - 1] = int32_t(p0 + 4 * (4 * qd + (bit >> 3)) + (bit & 7));
         }
-        if (token_seg != nullptr) {
-          int idx = -1;
-          if (p < cu_last) {
-            idx = (kth < max_segs ? kth : max_segs) - 1;
-            idx = idx < 0 ? 0 : idx;  // padding in front of the first boundary joins segment 0
-          }
-          token_seg[p] = idx;
+      }
+    }
+    __syncthreads();
+
+    // C. token -> segment index. Positions after the last real token belong to
+    // no segment, unless the segments overflowed (then to the merged last slot);
+    // a tile holding such positions has every boundary at or before them.
+    if (token_seg != nullptr) {
+      const int n_upto = running + tile_total;
+      const int tail_idx = n_upto > max_segs ? max_segs - 1 : -1;
+#pragma unroll 4
+      for (int j = 0; j < kGroupsPerThread; ++j) {
+        const int m = tid + kThreads * j;
+        const int64_t p = base + 4 * int64_t(m);
+        if (p >= N) break;
+        const unsigned bits = s_bits[m];
+        int kth = running + int(s_rank[m]);
+        i32x4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kth += (bits >> i) & 1u;
+          int idx = (kth < max_segs ? kth : max_segs) - 1;
+          idx = idx < 0 ? 0 : idx;  // padding in front of the first boundary joins segment 0
+          out[i] = p + i <= last_nz ? idx : tail_idx;
+        }
+        if (kVec && p + 4 <= N) {
+          *reinterpret_cast<i32x4*>(token_seg + p) = out;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (p + i < N) token_seg[p + i] = out[i];
         }
       }
     }
     running += tile_total;
-    __syncthreads();
+    __syncthreads();  // the next tile overwrites s_bits and s_rank
   }
 
+  const int n = running;
+  const int64_t e_last = last_nz + 1;
   // Slots past the scattered starts: last real end, or N for the merged slot.
   if (n > max_segs) {
     if (tid == 0) cu[max_segs] = static_cast<int32_t>(N);
@@ -174,8 +262,14 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
 hipError_t launch_cu_seqlens(const int32_t* seg, int64_t N, int64_t T, int32_t max_segs,
                              int32_t* cu, int32_t* token_seg, int32_t* n_segs, int32_t* flags,
                              hipStream_t stream) {
-  hipLaunchKernelGGL(cu_seqlens_kernel, dim3(1), dim3(kThreads), 0, stream, seg, N, T, max_segs,
-                     cu, token_seg, n_segs, flags);
+  const bool vec = (reinterpret_cast<uintptr_t>(seg) % 16 == 0) &&
+                   (token_seg == nullptr || reinterpret_cast<uintptr_t>(token_seg) % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL(cu_seqlens_kernel<true>, dim3(1), dim3(kThreads), 0, stream, seg, N, T,
+                       max_segs, cu, token_seg, n_segs, flags);
+  else
+    hipLaunchKernelGGL(cu_seqlens_kernel<false>, dim3(1), dim3(kThreads), 0, stream, seg, N, T,
+                       max_segs, cu, token_seg, n_segs, flags);
   return hipGetLastError();
 }
 

@@ -74,3 +74,53 @@ def test_row_start_collision_and_overflow_flags():
     _check(seg, 8)
     _check(seg, 2)
     _check(np.array([[0, 0, 3, 3, 0, 4]], dtype=np.int32), 4)
+
+
+@pytest.mark.parametrize("N", [65535, 65536, 65537, 2 * 65536 + 5, 3 * 65536 - 1])
+def test_large_tile_edges(N):
+    rng = np.random.default_rng(N + 1)
+    seg = workloads.random_segment_ids(rng, 1, N, 900, pad_prob=0.5, mid_pad=True)
+    _check(seg, 1024)
+    _check(seg, 40)    # overflow
+
+
+def test_long_trailing_and_leading_pad():
+    # last real token in the first tile, then more than a tile of padding
+    seg = np.zeros((1, 3 * 65536 + 7), dtype=np.int32)
+    seg[0, 5:1000] = 1
+    seg[0, 1000:40000] = 2
+    _check(seg, 4)
+    _check(seg, 1)   # overflow: the trailing pad joins the merged slot
+    # real tokens only near the end: the backward sweep stops after one step
+    seg2 = np.zeros((1, 2 * 65536 + 3), dtype=np.int32)
+    seg2[0, -50:-20] = 7
+    _check(seg2, 4)
+    # real tokens only at the start: the backward sweep walks the whole pad
+    seg3 = np.zeros((2, 70001), dtype=np.int32)
+    seg3[0, :3] = 9
+    _check(seg3, 4)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5])
+def test_short_rows(T):
+    rng = np.random.default_rng(T)
+    seg = workloads.random_segment_ids(rng, 4099, T, 5, pad_prob=0.3, mid_pad=True)
+    _check(seg, 8192)
+    _check(seg, 100)
+
+
+def test_unaligned_input():
+    """segment_ids at a 4-byte (not 16-byte) aligned address: the scalar-load path."""
+    import packed_varlen_gated_amd as pkv
+    rng = np.random.default_rng(11)
+    B, T = 3, 30001
+    seg_np = workloads.random_segment_ids(rng, B, T, 60, pad_prob=0.3, mid_pad=True)
+    buf = torch.zeros(B * T + 1, dtype=torch.int32, device="cuda")
+    buf[1:] = torch.from_numpy(seg_np.reshape(-1)).cuda()
+    seg = buf[1:].view(B, T)
+    assert seg.data_ptr() % 16 != 0
+    r = pkv.segment_ids_to_cu_seqlens(seg, 256, with_token_seg=True)
+    rcu, rn, rflags = oracle.segment_ids_to_cu_seqlens(seg_np, 256)
+    assert r.cu_seqlens.cpu().numpy().tolist() == rcu.tolist()
+    assert int(r.n_segs.item()) == rn and int(r.flags.item()) == rflags
+    assert r.token_seg.cpu().numpy().tolist() == oracle.token_segment(rcu, B * T).tolist()
