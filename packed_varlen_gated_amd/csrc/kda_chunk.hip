@@ -22,21 +22,25 @@
 // it). Per element only 2^{c} and 2^{T - c} are evaluated (c = in-sub-chunk
 // cumsum); every other factor is per channel.
 //
-// Work-group per (segment, head): Dk/16 producer waves and 4 consumer waves,
-// software-pipelined over chunks (two barriers per chunk):
-//   first half  P: chunk c: gate cumsums and factors; Q^ = q 2^b and
-//                  Kbar^T = (beta k 2^{b_C - b})^T to the LDS buffers of c's
-//                  parity, the query versions of the ten A blocks and KE.
+// Work-group per (segment, head): 4·Dk/64 producer waves and 4 consumer
+// waves, software-pipelined over chunks (two barriers per chunk step):
+//   first half  P: chunk c: per-channel factors from the sub-chunk totals,
+//                  Q^ = q 2^b and Kbar^T = (beta k 2^{b_C - b})^T to the LDS
+//                  buffers of c's parity, the query versions of the ten A
+//                  blocks, KE, and 2^{b_C}.
 //               C: chunk c-1: o^T = S^T Q^^T + V^T A^T for its Dv/4 columns,
 //                  stored; S = diag(2^{b_C}) S + Kbar^T V.
-//   second half P: V^T and 2^{b_C} of chunk c.
+//   second half P: V^T of chunk c; the in-sub-chunk cumulative gates of chunk
+//                  c+1 and their sub-chunk totals (to LDS).
 //               C: the A blocks of chunk c (MFMA), masked, beta-scaled, to LDS.
-// Raw inputs of chunk c+1 are prefetched into registers during chunk c. Each
-// single-buffered LDS tile is written in one half and read in the other; Q^
-// and Kbar^T, read a step later, are double-buffered. A producer lane holds 4
-// consecutive tokens x 4 channels, so the cumsum is an in-lane prefix, a DPP
-// quad scan (the 16 tokens of a sub-chunk) and DPP row shifts (the four
-// sub-chunks), with no cross-wave exchange.
+// A producer wave owns one 16-token sub-chunk and 64 key channels, so each of
+// its loads covers four tokens x one whole 128-byte line; a lane holds 4
+// consecutive tokens x 4 channels, so the in-sub-chunk cumsum is an in-lane
+// prefix plus a DPP quad scan. The sub-chunk totals go through a small LDS
+// table, and the sub-chunk index is uniform per wave (no divergent stores).
+// Raw inputs of chunk c+1 are loaded at the start of step c. Each
+// single-buffered LDS tile is written in one half and read in the other; Q^,
+// Kbar^T and 2^{b_C}, read a step later, are double-buffered.
 // MFMA v_mfma_f32_16x16x32_bf16: A operand lane l holds row l%16 and eight
 // contraction slots of lane group l/16, B likewise for column l%16; the 16x16
 // fp32 result has column l%16 and rows 4(l/16)+i. The contraction index may be
@@ -72,26 +76,34 @@ __device__ __forceinline__ void block_of(int b, int& w, int& j) {
 
 template <int DK, int DV>
 struct Cfg {
-  static constexpr int NP = DK / 16;     // producer waves (16 channels each)
+  static constexpr int NP = 4 * (DK / 64);  // producer waves: 4 sub-chunks x Dk/64 channel halves
   static constexpr int NT = 64 * (NP + 4);  // threads: producers + 4 consumers
-  static constexpr int PCPL = 4;         // producer channels per lane (4 tokens each)
-  static constexpr int PVPL = DV / NP / 4;  // producer v channels per lane
+  static constexpr int PCPL = 4;            // producer k channels per lane (4 tokens each)
+  static constexpr int PVPL = 4 * DV / DK;  // producer v channels per lane
   static constexpr int EW = DV / 4;      // consumer state / output columns
   static constexpr int ET = EW / 16;     // 16-column tiles per consumer
   static constexpr int DT = DK / 16;     // 16-row state tiles
   static constexpr int KS = DK / 32;     // contraction steps over Dk
   static constexpr int KP = DK + 8;      // token-major LDS rows (bf16 elements)
   static constexpr int TP = kC + 8;      // transposed / A rows (bf16 elements)
-  static constexpr int off_qh = 0;                           // two buffers
-  static constexpr int off_qv = off_qh + 2 * kC * KP * 2;
-  static constexpr int off_ke = off_qv + 10 * 16 * KP * 2;
-  static constexpr int off_kbT = off_ke + kC * KP * 2;        // two buffers
-  static constexpr int off_vT = off_kbT + 2 * DK * TP * 2;
-  static constexpr int off_a = off_vT + DV * TP * 2;
-  static constexpr int off_decay = off_a + kC * TP * 2;  // float [DK]
-  static constexpr int off_beta = off_decay + DK * 4;    // float [kC]
-  static constexpr int bytes = off_beta + kC * 4;
+  // Small tables first: ds_read/ds_write immediates reach 64 KiB, so tiles
+  // read at many row offsets sit low where one base register serves them.
+  static constexpr int off_decay = 0;                        // float [2][DK]
+  static constexpr int off_beta = off_decay + 2 * DK * 4;    // float [kC]
+  static constexpr int off_T = off_beta + kC * 4;            // float [DK][4] sub-chunk totals
+  static constexpr int off_a = off_T + DK * 4 * 4;           // A, bf16 [kC][TP]
+  static constexpr int off_vT = off_a + kC * TP * 2;         // V^T, bf16 [DV][TP]
+  static constexpr int off_kbT = off_vT + DV * TP * 2;       // Kbar^T, bf16 [2][DK][TP]
+  static constexpr int off_qh = off_kbT + 2 * DK * TP * 2;   // Q^, bf16 [2][kC][KP]
+  static constexpr int off_ke = off_qh + 2 * kC * KP * 2;    // KE, bf16 [kC][KP]
+  static constexpr int off_qv = off_ke + kC * KP * 2;        // query versions, bf16 [10][16][KP]
+  static constexpr int bytes = off_qv + 10 * 16 * KP * 2;
   static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
 };
 
 template <int n>
@@ -112,15 +124,6 @@ __device__ __forceinline__ float dpp(float x) {
 }
 constexpr int kQuadPrev1 = 0x90;  // quad_perm [0,0,1,2]
 constexpr int kQuadPrev2 = 0x40;  // quad_perm [0,0,0,1]
-constexpr int kRowShr4 = 0x114;   // row_shr:4
-constexpr int kRowShr8 = 0x118;   // row_shr:8
-constexpr int kRowShl4 = 0x104;   // row_shl:4
-constexpr int kRowShl8 = 0x108;   // row_shl:8
-constexpr int kRowShl12 = 0x10C;  // row_shl:12
-template <int L>
-__device__ __forceinline__ float qbcast(float x) {
-  return dpp<L | (L << 2) | (L << 4) | (L << 6)>(x);
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufFlags);
@@ -196,7 +199,7 @@ __device__ __forceinline__ void wload(uint32_t (&w)[n], __amdgpu_buffer_rsrc_t r
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
+__global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
     int32_t max_segs, int64_t N, int32_t H, float scale, bf16* __restrict__ o,
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
   bf16* s_a = reinterpret_cast<bf16*>(smem + C::off_a);
   float* s_decay = reinterpret_cast<float*>(smem + C::off_decay);
   float* s_beta = reinterpret_cast<float*>(smem + C::off_beta);
+  float* s_T = reinterpret_cast<float*>(smem + C::off_T);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -258,14 +262,15 @@ __global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
   };
 
   // ---------------------------------------------------------------- roles
-  // Producer lane: 4 tokens [4tq, 4tq+4) of the chunk, PCPL channels.
-  const int tq = lane & 15;            // token group; sub-chunk = tq >> 2
-  const int qp = lane & 3;             // position in the quad (one sub-chunk)
-  const int sw = tq >> 2;              // producer's sub-chunk
-  const int cg = lane >> 4;            // channel group within the producer's share
-  const int ch0 = w * (DK / NP) + cg * PCPL;
-  const int vch0 = w * (DV / NP) + cg * PVPL;
-  const int tok0 = 4 * tq;
+  // Producer wave: sub-chunk sw, key channels [64 kh, 64 kh + 64). Lane: 4
+  // tokens [tok0, tok0 + 4) (quad position tq), 4 channels from ch0.
+  const int sw = w & 3;
+  const int kh = w >> 2;
+  const int tq = lane & 3;
+  const int cg = lane >> 2;
+  const int ch0 = 64 * kh + PCPL * cg;
+  const int vch0 = kh * (64 * DV / DK) + PVPL * cg;
+  const int tok0 = 16 * sw + 4 * tq;
   // Consumer lane (MFMA layout).
   const int gq = lane >> 4;
   const int lr = lane & 15;
@@ -274,132 +279,160 @@ __global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
 
   // Loads are unconditional so the wait counts stay exact: a chunk index past
   // the segment gets an empty buffer (every read returns 0, no memory access).
-  auto load_raw = [&](Raw<PCPL, PVPL>& R, int c) {
+  // Each part of the raw inputs is refilled right after its last use: q, k,
+  // beta of chunk c+1 after the factors of chunk c, v of chunk c+1 after V^T
+  // of chunk c, g of chunk c+2 after the scan of chunk c+1.
+  struct Src {
+    int64_t tokbase;
+    uint32_t nK, nV, nB;
+  };
+  auto src_of = [&](int c) {
     const bool live = c < nchunks;
     const int64_t p0 = start + int64_t(live ? c : 0) * kC;
     const int Lc = live ? chunk_len(c) : 1;
-    const int64_t tokbase = p0 * H + h;
-    const uint32_t nK = live ? uint32_t(Lc - 1) * rowK + DK * 2 : 0u;
-    const uint32_t nB = live ? uint32_t(Lc - 1) * rowB + 2 : 0u;
-    const uint32_t nV = live ? uint32_t(Lc - 1) * rowV + DV * 2 : 0u;
-    const auto rq = rsrc(q + tokbase * DK, nK), rk = rsrc(k + tokbase * DK, nK);
-    const auto rg = rsrc(g + tokbase * DK, nK), rv = rsrc(v + tokbase * DV, nV);
-    const auto rb = rsrc(beta + tokbase, nB);
+    Src r;
+    r.tokbase = p0 * H + h;
+    r.nK = live ? uint32_t(Lc - 1) * rowK + DK * 2 : 0u;
+    r.nV = live ? uint32_t(Lc - 1) * rowV + DV * 2 : 0u;
+    r.nB = live ? uint32_t(Lc - 1) * rowB + 2 : 0u;
+    return r;
+  };
+  auto load_g = [&](Raw<PCPL, PVPL>& R, int c) {
+    const Src r = src_of(c);
+    const auto rg = rsrc(g + r.tokbase * DK, r.nK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wload(R.g[i], rg, uint32_t(tok0 + i) * rowK + ch0 * 2);
+  };
+  auto load_qkb = [&](Raw<PCPL, PVPL>& R, int c) {
+    const Src r = src_of(c);
+    const auto rq = rsrc(q + r.tokbase * DK, r.nK), rk = rsrc(k + r.tokbase * DK, r.nK);
+    const auto rb = rsrc(beta + r.tokbase, r.nB);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t t = uint32_t(tok0 + i);
-      wload(R.g[i], rg, t * rowK + ch0 * 2);
       wload(R.q[i], rq, t * rowK + ch0 * 2);
       wload(R.k[i], rk, t * rowK + ch0 * 2);
-      wload(R.v[i], rv, t * rowV + vch0 * 2);
       R.b[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, t * rowB, 0, 0);
     }
   };
-  // ---- producer, first half: everything up to the A-block operands.
-  // Q^ and Kbar^T go to the LDS buffer of this chunk's parity; dec_out is
-  // carried to the second half. The lane's channels are processed four at a
-  // time (one per quad lane for the per-channel factors).
-  auto produce_a = [&](Raw<PCPL, PVPL>& R, bf16* s_qh, bf16* s_kbT, float* dec_out) {
-    const int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
+  auto load_v = [&](Raw<PCPL, PVPL>& R, int c) {
+    const Src r = src_of(c);
+    const auto rv = rsrc(v + r.tokbase * DV, r.nV);
 #pragma unroll
-    for (int hh = 0; hh < PCPL / 4; ++hh) {
-      float cs[4][4], Tw[4], fx[6];
+    for (int i = 0; i < 4; ++i) wload(R.v[i], rv, uint32_t(tok0 + i) * rowV + vch0 * 2);
+  };
+  // ---- producer, second half: in-sub-chunk cumulative gates (base 2) of a
+  // chunk. cs[i][c] is the inclusive cumsum at token tok0 + i, channel ch0 + c,
+  // from the start of the sub-chunk; the sub-chunk totals go to s_T.
+  auto scan = [&](const Raw<PCPL, PVPL>& R, float (&cs)[4][PCPL]) {
+    float tot[PCPL];
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int cc = 4 * hh + c4;
-        float run = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          run = fmaf(bf(R.g[i], cc), kLog2e, run);
-          cs[i][c4] = run;
-        }
-        // prefix over the quad (the four token groups of one sub-chunk)
-        const float a1 = dpp<kQuadPrev1>(run);
-        const float s1 = run + (qp >= 1 ? a1 : 0.f);
-        const float a2 = dpp<kQuadPrev2>(s1);
-        const float inc = s1 + (qp >= 2 ? a2 : 0.f);
-        const float excl = inc - run;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cs[i][c4] += excl;
-        const float T = qbcast<3>(inc);
-        // prefix over the four sub-chunks of the row (row shifts by 4 and 8 lanes)
-        const float T1 = dpp<kRowShr4>(T);     // previous sub-chunk's total (0 for sub-chunk 0)
-        const float T2 = dpp<kRowShr8>(T);     // total two sub-chunks back
-        const float y = T + T1;
-        const float z = y + dpp<kRowShr8>(y);  // rho_{w+1}
-        const float bC = z + dpp<kRowShl4>(T) + dpp<kRowShl8>(T) + dpp<kRowShl12>(T);  // b_C
-        Tw[c4] = T;
-        // exponents of the per-channel factors of channel cc, kept by quad lane c4
-        if (qp == c4) {
-          fx[0] = z - T;        // rho_w
-          fx[1] = bC - z;       // b_C - rho_{w+1}
-          fx[2] = -T;
-          fx[3] = T1;
-          fx[4] = T1 + T2;
-          fx[5] = bC;
-        }
-      }
-      float fm[5];
-#pragma unroll
-      for (int j = 0; j < 5; ++j) fm[j] = ex2(fx[j]);
-      dec_out[hh] = ex2(fx[5]);  // 2^{b_C} of channel 4hh + qp
-      // f[j][c4]: factor j of channel 4hh + c4, broadcast from quad lane c4
-      float f[5][4];
-#pragma unroll
-      for (int j = 0; j < 5; ++j) {
-        f[j][0] = qbcast<0>(fm[j]);
-        f[j][1] = qbcast<1>(fm[j]);
-        f[j][2] = qbcast<2>(fm[j]);
-        f[j][3] = qbcast<3>(fm[j]);
-      }
-      // f[0] = 2^{rho_w} (Q^ = Q~ f0); f[1] = 2^{b_C - rho_{w+1}} (Kbar = beta KE f1);
-      // f[2] = 2^{-T_w} (diagonal version); f[3] = 2^{T_{w-1}} (block (w, w-2));
-      // f[4] = 2^{T_{w-1} + T_{w-2}} (block (3, 0)).
-      float kb[4][4];  // [channel][token] for the transposed store
+    for (int c = 0; c < PCPL; ++c) {
+      float run = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = tok0 + i;
-        float qt[4], ke[4], t0[4];
-        const int chh = ch0 + 4 * hh;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const int cc = 4 * hh + c4;
-          qt[c4] = bf(R.q[i], cc) * ex2(cs[i][c4]);
-          ke[c4] = bf(R.k[i], cc) * ex2(Tw[c4] - cs[i][c4]);
-          t0[c4] = qt[c4] * f[0][c4];
-          kb[c4][i] = ke[c4] * (__uint_as_float(R.b[i] << 16) * f[1][c4]);
-        }
-        st4(s_qh + tok * KP + chh, t0);
-        st4(s_ke + tok * KP + chh, ke);
-        bf16* qv = s_qv + (tok & 15) * KP + chh;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) t0[c4] = qt[c4] * f[2][c4];
-        st4(qv + (vbase + sw) * 16 * KP, t0);
-        if (sw >= 1) st4(qv + (vbase + sw - 1) * 16 * KP, qt);
-        if (sw >= 2) {
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) t0[c4] = qt[c4] * f[3][c4];
-          st4(qv + (vbase + sw - 2) * 16 * KP, t0);
-        }
-        if (sw == 3) {
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) t0[c4] = qt[c4] * f[4][c4];
-          st4(qv + (vbase + 0) * 16 * KP, t0);
-        }
+        run = fmaf(bf(R.g[i], c), kLog2e, run);
+        cs[i][c] = run;
       }
+      // prefix over the quad (the four token groups of the sub-chunk)
+      const float a1 = dpp<kQuadPrev1>(run);
+      const float s1 = run + (tq >= 1 ? a1 : 0.f);
+      const float a2 = dpp<kQuadPrev2>(s1);
+      const float inc = s1 + (tq >= 2 ? a2 : 0.f);
+      const float excl = inc - run;
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4)
-        st4(s_kbT + (ch0 + 4 * hh + c4) * TP + tok0, kb[c4]);
+      for (int i = 0; i < 4; ++i) cs[i][c] += excl;
+      tot[c] = inc;  // quad lane 3 holds the sub-chunk total
     }
-    if (w == 0 && cg == 0) {
+    if (tq == 3) {
+#pragma unroll
+      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c) * 4 + sw] = tot[c];
+    }
+  };
+
+  // ---- producer, first half: factors and MFMA operands of one chunk.
+  // With T_j the sub-chunk totals of a channel, rho_w = T_0 + .. + T_{w-1}:
+  // f0 = 2^{rho_w} (Q^ = Q~ f0), f1 = 2^{T_{w+1} + .. + T_3} (Kbar = beta KE f1),
+  // f2 = 2^{-T_w} (diagonal version), f3 = 2^{T_{w-1}} (block (w, w-2)),
+  // f4 = 2^{T_{w-1} + T_{w-2}} (block (3, 0)); decay = 2^{T_0 + .. + T_3}.
+  // The sub-chunk index is a compile-time constant inside (one instance per
+  // sub-chunk), so every choice below is resolved without branches.
+  auto produce_a_sw = [&](auto swc, const Raw<PCPL, PVPL>& R, const float (&cs)[4][PCPL],
+                          bf16* s_qh, bf16* s_kbT, float* s_dec) {
+    constexpr int sw = decltype(swc)::value;
+    constexpr int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
+    float Tw[PCPL], f[5][PCPL], dec[PCPL];
+#pragma unroll
+    for (int c = 0; c < PCPL; ++c) {
+      const f32x4 Tj = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c) * 4);
+      const float T = Tj[sw];
+      const float Tm1 = sw >= 1 ? Tj[sw >= 1 ? sw - 1 : 0] : 0.f;
+      const float Tm2 = sw >= 2 ? Tj[sw >= 2 ? sw - 2 : 0] : 0.f;
+      const float rho = sw == 0 ? 0.f : sw == 1 ? Tj[0] : sw == 2 ? Tj[0] + Tj[1] : (Tj[0] + Tj[1]) + Tj[2];
+      const float after = sw == 3 ? 0.f : sw == 2 ? Tj[3] : sw == 1 ? Tj[2] + Tj[3] : Tj[1] + (Tj[2] + Tj[3]);
+      Tw[c] = T;
+      f[0][c] = ex2(rho);
+      f[1][c] = ex2(after);
+      f[2][c] = ex2(-T);
+      f[3][c] = ex2(Tm1);
+      f[4][c] = ex2(Tm1 + Tm2);
+      dec[c] = ex2((Tj[0] + Tj[1]) + (Tj[2] + Tj[3]));
+    }
+    if (sw == 0 && tq == 0)
+      *reinterpret_cast<f32x4*>(s_dec + ch0) = f32x4{dec[0], dec[1], dec[2], dec[3]};
+    (void)dec;
+    float kb[PCPL][4];  // [channel][token] for the transposed store
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok0 + i;
+      const float bt = __uint_as_float(R.b[i] << 16);
+      float qt[PCPL], ke[PCPL], t0[PCPL];
+#pragma unroll
+      for (int c = 0; c < PCPL; ++c) {
+        qt[c] = bf(R.q[i], c) * ex2(cs[i][c]);
+        ke[c] = bf(R.k[i], c) * ex2(Tw[c] - cs[i][c]);
+        t0[c] = qt[c] * f[0][c];
+        kb[c][i] = ke[c] * (bt * f[1][c]);
+      }
+      st4(s_qh + tok * KP + ch0, t0);
+      st4(s_ke + tok * KP + ch0, ke);
+      bf16* qv = s_qv + (tok & 15) * KP + ch0;  // row of the token in each version slot
+#pragma unroll
+      for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[2][c];
+      st4(qv + (vbase + sw) * 16 * KP, t0);
+      if constexpr (sw >= 1) st4(qv + (vbase + sw - 1) * 16 * KP, qt);
+      if constexpr (sw >= 2) {
+#pragma unroll
+        for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[3][c];
+        st4(qv + (vbase + sw - 2) * 16 * KP, t0);
+      }
+      if constexpr (sw == 3) {
+#pragma unroll
+        for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[4][c];
+        st4(qv + (vbase + 0) * 16 * KP, t0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < PCPL; ++c) st4(s_kbT + (ch0 + c) * TP + tok0, kb[c]);
+    if (kh == 0 && cg == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_beta[tok0 + i] = __uint_as_float(R.b[i] << 16);
     }
   };
 
-  // ---- producer, second half: V^T and 2^{b_C} of the chunk.
-  auto produce_b = [&](const float* dec_out, const uint32_t (&V)[4][PVPL / 2]) {
-    // V^T: channel pair (2j, 2j+1) of tokens tok0..tok0+3 -> two 8-byte rows.
+  auto produce_a = [&](const Raw<PCPL, PVPL>& R, const float (&cs)[4][PCPL], bf16* s_qh,
+                       bf16* s_kbT, float* s_dec) {
+    switch (sw) {
+      case 0: produce_a_sw(IntC<0>{}, R, cs, s_qh, s_kbT, s_dec); break;
+      case 1: produce_a_sw(IntC<1>{}, R, cs, s_qh, s_kbT, s_dec); break;
+      case 2: produce_a_sw(IntC<2>{}, R, cs, s_qh, s_kbT, s_dec); break;
+      default: produce_a_sw(IntC<3>{}, R, cs, s_qh, s_kbT, s_dec); break;
+    }
+  };
+
+  // ---- producer, second half: V^T of the chunk (channel pair (2j, 2j+1) of
+  // tokens tok0 .. tok0+3 -> two 8-byte rows).
+  auto produce_b = [&](const uint32_t (&V)[4][PVPL / 2]) {
     static_assert(PVPL % 2 == 0, "v channels come in pairs");
 #pragma unroll
     for (int j = 0; j < PVPL / 2; ++j) {
@@ -407,24 +440,18 @@ __global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
       const uint32_t lo23 = __builtin_amdgcn_perm(V[3][j], V[2][j], 0x05040100u);
       const uint32_t hi01 = __builtin_amdgcn_perm(V[1][j], V[0][j], 0x07060302u);
       const uint32_t hi23 = __builtin_amdgcn_perm(V[3][j], V[2][j], 0x07060302u);
-      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-      *reinterpret_cast<u2*>(s_vT + (vch0 + 2 * j) * TP + tok0) = u2{lo01, lo23};
-      *reinterpret_cast<u2*>(s_vT + (vch0 + 2 * j + 1) * TP + tok0) = u2{hi01, hi23};
-    }
-    if (sw == 0) {
-#pragma unroll
-      for (int hh = 0; hh < PCPL / 4; ++hh) s_decay[ch0 + 4 * hh + qp] = dec_out[hh];
+      *reinterpret_cast<u32x2*>(s_vT + (vch0 + 2 * j) * TP + tok0) = u32x2{lo01, lo23};
+      *reinterpret_cast<u32x2*>(s_vT + (vch0 + 2 * j + 1) * TP + tok0) = u32x2{hi01, hi23};
     }
   };
 
   // ---- consumer, first half: outputs and state update of chunk c.
   // Operands are fetched in batches and the MFMAs ordered so that consecutive
   // ones are independent (four row tiles x ET column tiles per step).
-  auto consume_state = [&](f32x4 (&S)[DT][ET], int c) {
+  auto consume_state = [&](f32x4 (&S)[DT][ET], int c, const bf16* s_qh, const bf16* s_kbT,
+                           const float* s_dec) {
     const int64_t p0 = start + int64_t(c) * kC;
     const int Lc = chunk_len(c);
-    const bf16* s_qh = (c & 1) ? s_qh1 : s_qh0;
-    const bf16* s_kbT = (c & 1) ? s_kbT1 : s_kbT0;
     f32x4 acc[4][ET];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -480,7 +507,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
     // S = diag(2^{b_C}) S + Kbar^T V
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const f32x4 dec = *reinterpret_cast<const f32x4*>(s_decay + 16 * dt + 4 * gq);
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(s_dec + 16 * dt + 4 * gq);
 #pragma unroll
       for (int et = 0; et < ET; ++et)
 #pragma unroll
@@ -546,21 +573,32 @@ __global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
   // Producers and consumers run separate loops with the same barrier sequence
   // (two per step), so neither role keeps the other's registers live.
   if (producer) {
-    Raw<PCPL, PVPL> cur, nxt;
-    float dec_out[PCPL / 4];
-    load_raw(cur, 0);
+    Raw<PCPL, PVPL> R;
+    float cs[4][PCPL];
+    load_g(R, 0);
+    load_qkb(R, 0);
+    load_v(R, 0);
+    scan(R, cs);
+    load_g(R, 1);
+    __syncthreads();
     for (int s = 0; s <= nchunks; s += 2) {
       // even chunk s: LDS buffers 0; odd chunk s + 1: buffers 1
-      load_raw(nxt, s + 1);
-      if (s < nchunks) produce_a(cur, s_qh0, s_kbT0, dec_out);
+      if (s < nchunks) produce_a(R, cs, s_qh0, s_kbT0, s_decay);
+      load_qkb(R, s + 1);
       __syncthreads();
-      if (s < nchunks) produce_b(dec_out, cur.v);
+      if (s < nchunks) produce_b(R.v);
+      load_v(R, s + 1);
+      if (s + 1 < nchunks) scan(R, cs);
+      load_g(R, s + 2);
       __syncthreads();
       if (s + 1 > nchunks) break;
-      load_raw(cur, s + 2);
-      if (s + 1 < nchunks) produce_a(nxt, s_qh1, s_kbT1, dec_out);
+      if (s + 1 < nchunks) produce_a(R, cs, s_qh1, s_kbT1, s_decay + DK);
+      load_qkb(R, s + 2);
       __syncthreads();
-      if (s + 1 < nchunks) produce_b(dec_out, nxt.v);
+      if (s + 1 < nchunks) produce_b(R.v);
+      load_v(R, s + 2);
+      if (s + 2 < nchunks) scan(R, cs);
+      load_g(R, s + 3);
       __syncthreads();
     }
   } else {
@@ -569,13 +607,14 @@ __global__ __launch_bounds__(64 * (DK / 16 + 4), 1) void kda_chunk_kernel(
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int et = 0; et < ET; ++et) S[dt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // the producers' first scan
     for (int s = 0; s <= nchunks; s += 2) {
-      if (s >= 1) consume_state(S, s - 1);
+      if (s >= 1) consume_state(S, s - 1, s_qh1, s_kbT1, s_decay + DK);
       __syncthreads();
       if (s < nchunks) consume_a();
       __syncthreads();
       if (s + 1 > nchunks) break;
-      consume_state(S, s);
+      consume_state(S, s, s_qh0, s_kbT0, s_decay);
       __syncthreads();
       if (s + 1 < nchunks) consume_a();
       __syncthreads();
