@@ -113,7 +113,9 @@ pkv_status pkv_short_conv_segmask(const void* x, const float* w, const int32_t* 
 
 /*
  * Bytes of device workspace pkv_chunk_kda_varlen needs for these sizes
- * (0 means no workspace is needed and NULL may be passed).
+ * (0 means no workspace is needed and NULL may be passed). With bf16 and
+ * Dk, Dv in {64, 128} and 2 <= max_segs <= 2048 it holds the order in which
+ * the segment slots are processed (longest first), one int32 per slot.
  */
 size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,
                                            int32_t max_segs, int32_t dtype);
@@ -137,7 +139,9 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
  * final_state float32 [max_segs, H, Dk, Dv] or NULL (not written).
  * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in.
  * workspace   device buffer of at least pkv_chunk_kda_varlen_workspace_size()
- *             bytes (NULL allowed when that size is 0); contents are scratch.
+ *             bytes, 4-byte aligned (NULL allowed when that size is 0);
+ *             contents are scratch, overwritten by every call, so calls that
+ *             share a workspace must be ordered on one stream.
  * Supported: Dk, Dv in {32, 64, 128}. Inputs with large positive g or with
  * 16 * max|g| beyond ~60 within a segment may lose accuracy (the chunked
  * factorisation bounds exponents per 16-token sub-chunk).

@@ -73,11 +73,7 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
                                            int32_t max_segs, int32_t dtype) {
   (void)N;
   (void)H;
-  (void)Dk;
-  (void)Dv;
-  (void)max_segs;
-  (void)dtype;
-  return 0;
+  return pkv::kda_chunk_workspace_bytes(Dk, Dv, dtype, max_segs);
 }
 
 pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
@@ -107,7 +103,7 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   if (pkv::kda_chunk_supported(Dk, Dv, dtype))
     return from_hip(pkv::launch_kda_chunk(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
-                                          scale, o, final_state, flags,
+                                          scale, o, final_state, flags, workspace,
                                           static_cast<hipStream_t>(stream)));
   return from_hip(pkv::launch_kda_serial(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
                                          scale, dtype, o, final_state, flags,

@@ -89,13 +89,13 @@ struct Cfg {
   // Small tables first: ds_read/ds_write immediates reach 64 KiB, so tiles
   // read at many row offsets sit low where one base register serves them.
   static constexpr int off_decay = 0;                        // float [2][DK]
-  static constexpr int off_beta = off_decay + 2 * DK * 4;    // float [kC]
-  static constexpr int off_T = off_beta + kC * 4;            // float [DK][4] sub-chunk totals
+  static constexpr int off_beta = off_decay + 2 * DK * 4;    // float [2][kC]
+  static constexpr int off_T = off_beta + 2 * kC * 4;        // float [DK][4] sub-chunk totals
   static constexpr int off_a = off_T + DK * 4 * 4;           // A, bf16 [kC][TP]
   static constexpr int off_vT = off_a + kC * TP * 2;         // V^T, bf16 [DV][TP]
   static constexpr int off_kbT = off_vT + DV * TP * 2;       // Kbar^T, bf16 [2][DK][TP]
-  static constexpr int off_qh = off_kbT + 2 * DK * TP * 2;   // Q^, bf16 [2][kC][KP]
-  static constexpr int off_ke = off_qh + 2 * kC * KP * 2;    // KE, bf16 [kC][KP]
+  static constexpr int off_qh = off_kbT + 2 * DK * TP * 2;   // Q^, bf16 [kC][KP]
+  static constexpr int off_ke = off_qh + kC * KP * 2;        // KE, bf16 [kC][KP]
   static constexpr int off_qv = off_ke + kC * KP * 2;        // query versions, bf16 [10][16][KP]
   static constexpr int bytes = off_qv + 10 * 16 * KP * 2;
   static_assert(bytes <= 160 * 1024, "LDS budget");
@@ -150,6 +150,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Two floats -> one register of two bf16 (round to nearest even), a single
 // v_cvt_pk_bf16_f32.
@@ -163,13 +164,12 @@ __device__ __forceinline__ void st4(bf16* dst, float a, float b, float c, float 
 __device__ __forceinline__ void st4(bf16* dst, const float* x) { st4(dst, x[0], x[1], x[2], x[3]); }
 
 // Raw producer inputs of one chunk: 4 tokens x PCPL channels of q, k, g and
-// PVPL channels of v as packed bf16 pairs, and beta. They stay packed until used, so the prefetch of
-// the next chunk is never waited for early.
+// PVPL channels of v as packed bf16 pairs. They stay packed until used, so a
+// load is never waited for before its first use.
 template <int PCPL, int PVPL>
 struct Raw {
   uint32_t g[4][PCPL / 2], q[4][PCPL / 2], k[4][PCPL / 2];
   uint32_t v[4][PVPL / 2];
-  uint32_t b[4];
 };
 
 // bf16 element c of a packed pair array, as fp32 (exact).
@@ -202,25 +202,30 @@ template <int DK, int DV>
 __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
-    int32_t max_segs, int64_t N, int32_t H, float scale, bf16* __restrict__ o,
-    float* __restrict__ final_state, int32_t* __restrict__ flags) {
+    const int32_t* __restrict__ order, int32_t max_segs, int64_t N, int32_t H, float scale,
+    bf16* __restrict__ o, float* __restrict__ final_state, int32_t* __restrict__ flags,
+    int32_t lds_zero) {
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
   constexpr int PCPL = C::PCPL, PVPL = C::PVPL, ET = C::ET, DT = C::DT, KS = C::KS;
   constexpr int KP = C::KP, TP = C::TP;
 
+  // Tile bases are made opaque to the compiler (lds_zero is 0 at run time):
+  // an LDS access then takes one base register per tile and lane pattern plus
+  // a 16-bit immediate, instead of folding tile offsets beyond 64 KiB into
+  // per-access address registers.
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16* s_qh0 = reinterpret_cast<bf16*>(smem + C::off_qh);     // Q^ of even / odd chunks
-  bf16* s_qh1 = s_qh0 + kC * KP;
-  bf16* s_qv = reinterpret_cast<bf16*>(smem + C::off_qv);
-  bf16* s_ke = reinterpret_cast<bf16*>(smem + C::off_ke);
-  bf16* s_kbT0 = reinterpret_cast<bf16*>(smem + C::off_kbT);   // Kbar^T of even / odd chunks
-  bf16* s_kbT1 = s_kbT0 + DK * TP;
-  bf16* s_vT = reinterpret_cast<bf16*>(smem + C::off_vT);
-  bf16* s_a = reinterpret_cast<bf16*>(smem + C::off_a);
-  float* s_decay = reinterpret_cast<float*>(smem + C::off_decay);
-  float* s_beta = reinterpret_cast<float*>(smem + C::off_beta);
-  float* s_T = reinterpret_cast<float*>(smem + C::off_T);
+  auto tile = [&](int off) { return smem + (off | lds_zero); };
+  bf16* s_qh = reinterpret_cast<bf16*>(tile(C::off_qh));
+  bf16* s_qv = reinterpret_cast<bf16*>(tile(C::off_qv));
+  bf16* s_ke = reinterpret_cast<bf16*>(tile(C::off_ke));
+  bf16* s_kbT0 = reinterpret_cast<bf16*>(tile(C::off_kbT));   // Kbar^T of even / odd chunks
+  bf16* s_kbT1 = reinterpret_cast<bf16*>(tile(C::off_kbT + DK * TP * 2));
+  bf16* s_vT = reinterpret_cast<bf16*>(tile(C::off_vT));
+  bf16* s_a = reinterpret_cast<bf16*>(tile(C::off_a));
+  float* s_decay = reinterpret_cast<float*>(tile(C::off_decay));
+  float* s_beta = reinterpret_cast<float*>(tile(C::off_beta));
+  float* s_T = reinterpret_cast<float*>(tile(C::off_T));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -240,7 +245,11 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     return;
   }
 
-  const int slot = int(blockIdx.x / H);
+  // Work-groups take (segment, head) pairs longest segment first when an
+  // order is given, so the longest chains start early and the tail of the
+  // launch holds the short ones.
+  const int rank = int(blockIdx.x / H);
+  const int slot = order != nullptr ? order[rank] : rank;
   const int h = int(blockIdx.x % H);
   int64_t start = 0, end = N;
   if (cu != nullptr) {
@@ -271,17 +280,19 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   const int ch0 = 64 * kh + PCPL * cg;
   const int vch0 = kh * (64 * DV / DK) + PVPL * cg;
   const int tok0 = 16 * sw + 4 * tq;
-  // Consumer lane (MFMA layout).
+  // MFMA lane layout (consumers, and every wave for the A blocks).
   const int gq = lane >> 4;
   const int lr = lane & 15;
+  constexpr int NW = NT / 64;  // waves per work-group
   const int ci = w - NP;               // consumer index 0..3
   const int e0 = ci * C::EW;
 
   // Loads are unconditional so the wait counts stay exact: a chunk index past
   // the segment gets an empty buffer (every read returns 0, no memory access).
-  // Each part of the raw inputs is refilled right after its last use: q, k,
-  // beta of chunk c+1 after the factors of chunk c, v of chunk c+1 after V^T
-  // of chunk c, g of chunk c+2 after the scan of chunk c+1.
+  // Each part of the raw inputs is refilled right after its last use: q, k
+  // of chunk c+1 after the MFMA operands of chunk c, v of chunk c+1 after V^T
+  // of chunk c, g of chunk c+2 after the scan of chunk c+1. beta goes through
+  // LDS (double-buffered by chunk parity): wave 0 loads it a step ahead.
   struct Src {
     int64_t tokbase;
     uint32_t nK, nV, nB;
@@ -303,17 +314,21 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wload(R.g[i], rg, uint32_t(tok0 + i) * rowK + ch0 * 2);
   };
-  auto load_qkb = [&](Raw<PCPL, PVPL>& R, int c) {
+  auto load_qk = [&](Raw<PCPL, PVPL>& R, int c) {
     const Src r = src_of(c);
     const auto rq = rsrc(q + r.tokbase * DK, r.nK), rk = rsrc(k + r.tokbase * DK, r.nK);
-    const auto rb = rsrc(beta + r.tokbase, r.nB);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t t = uint32_t(tok0 + i);
       wload(R.q[i], rq, t * rowK + ch0 * 2);
       wload(R.k[i], rk, t * rowK + ch0 * 2);
-      R.b[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, t * rowB, 0, 0);
     }
+  };
+  // beta of a whole chunk, token = lane (one wave loads it for everyone)
+  auto load_beta = [&](int c) {
+    const Src r = src_of(c);
+    return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rsrc(beta + r.tokbase, r.nB),
+                                                         uint32_t(lane) * rowB, 0, 0));
   };
   auto load_v = [&](Raw<PCPL, PVPL>& R, int c) {
     const Src r = src_of(c);
@@ -358,7 +373,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   // The sub-chunk index is a compile-time constant inside (one instance per
   // sub-chunk), so every choice below is resolved without branches.
   auto produce_a_sw = [&](auto swc, const Raw<PCPL, PVPL>& R, const float (&cs)[4][PCPL],
-                          bf16* s_qh, bf16* s_kbT, float* s_dec) {
+                          bf16* s_qh, bf16* s_kbT, float* s_dec, const float* s_bet) {
     constexpr int sw = decltype(swc)::value;
     constexpr int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
     float Tw[PCPL], f[5][PCPL], dec[PCPL];
@@ -382,10 +397,11 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
       *reinterpret_cast<f32x4*>(s_dec + ch0) = f32x4{dec[0], dec[1], dec[2], dec[3]};
     (void)dec;
     float kb[PCPL][4];  // [channel][token] for the transposed store
+    const f32x4 bt4 = *reinterpret_cast<const f32x4*>(s_bet + tok0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = tok0 + i;
-      const float bt = __uint_as_float(R.b[i] << 16);
+      const float bt = bt4[i];
       float qt[PCPL], ke[PCPL], t0[PCPL];
 #pragma unroll
       for (int c = 0; c < PCPL; ++c) {
@@ -414,19 +430,15 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     }
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) st4(s_kbT + (ch0 + c) * TP + tok0, kb[c]);
-    if (kh == 0 && cg == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_beta[tok0 + i] = __uint_as_float(R.b[i] << 16);
-    }
   };
 
   auto produce_a = [&](const Raw<PCPL, PVPL>& R, const float (&cs)[4][PCPL], bf16* s_qh,
-                       bf16* s_kbT, float* s_dec) {
+                       bf16* s_kbT, float* s_dec, const float* s_bet) {
     switch (sw) {
-      case 0: produce_a_sw(IntC<0>{}, R, cs, s_qh, s_kbT, s_dec); break;
-      case 1: produce_a_sw(IntC<1>{}, R, cs, s_qh, s_kbT, s_dec); break;
-      case 2: produce_a_sw(IntC<2>{}, R, cs, s_qh, s_kbT, s_dec); break;
-      default: produce_a_sw(IntC<3>{}, R, cs, s_qh, s_kbT, s_dec); break;
+      case 0: produce_a_sw(IntC<0>{}, R, cs, s_qh, s_kbT, s_dec, s_bet); break;
+      case 1: produce_a_sw(IntC<1>{}, R, cs, s_qh, s_kbT, s_dec, s_bet); break;
+      case 2: produce_a_sw(IntC<2>{}, R, cs, s_qh, s_kbT, s_dec, s_bet); break;
+      default: produce_a_sw(IntC<3>{}, R, cs, s_qh, s_kbT, s_dec, s_bet); break;
     }
   };
 
@@ -445,19 +457,14 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     }
   };
 
-  // ---- consumer, first half: outputs and state update of chunk c.
-  // Operands are fetched in batches and the MFMAs ordered so that consecutive
-  // ones are independent (four row tiles x ET column tiles per step).
-  auto consume_state = [&](f32x4 (&S)[DT][ET], int c, const bf16* s_qh, const bf16* s_kbT,
-                           const float* s_dec) {
-    const int64_t p0 = start + int64_t(c) * kC;
-    const int Lc = chunk_len(c);
-    f32x4 acc[4][ET];
+  // ---- consumer, second half of step c: o^T = S^T Q^^T for chunk c (S holds
+  // the state after chunk c-1 by then); kept in registers until the first
+  // half of step c+1 adds V^T A^T. Contraction over Dk in steps of 32.
+  auto consume_inter = [&](const f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int et = 0; et < ET; ++et) acc[t][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // o^T += S^T Q^^T, contraction over Dk in steps of 32
 #pragma unroll
     for (int u = 0; u < KS; ++u) {
       bf16x8 bq[4];
@@ -477,13 +484,23 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
         for (int t = 0; t < 4; ++t) acc[t][et] = mfma(sop, bq[t], acc[t][et]);
       }
     }
-    // o^T += V^T A^T, contraction over tokens in steps of 32 (causal: rows >= 32 only for the second)
+  };
+
+  // ---- consumer, first half of step c+1: o of chunk c = acc + V^T A^T
+  // (contraction over tokens in steps of 32; causal: the second step only
+  // for rows >= 32), scaled and stored; then S = diag(2^{b_C}) S + Kbar^T V.
+  auto consume_finish = [&](f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET], int c, const bf16* s_kbT,
+                            const float* s_dec) {
+    const int64_t p0 = start + int64_t(c) * kC;
+    const int Lc = chunk_len(c);
+    auto vT_op = [&](int m2, int et) {
+      return *reinterpret_cast<const bf16x8*>(s_vT + (e0 + 16 * et + lr) * TP + 32 * m2 + 8 * gq);
+    };
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
       bf16x8 va[ET], aa[4];
 #pragma unroll
-      for (int et = 0; et < ET; ++et)
-        va[et] = *reinterpret_cast<const bf16x8*>(s_vT + (e0 + 16 * et + lr) * TP + 32 * m2 + 8 * gq);
+      for (int et = 0; et < ET; ++et) va[et] = vT_op(m2, et);
 #pragma unroll
       for (int t = 2 * m2; t < 4; ++t)
         aa[t] = *reinterpret_cast<const bf16x8*>(s_a + (16 * t + lr) * TP + 32 * m2 + 8 * gq);
@@ -492,6 +509,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
 #pragma unroll
         for (int et = 0; et < ET; ++et) acc[t][et] = mfma(va[et], aa[t], acc[t][et]);
     }
+    // acc[t][et] holds o of token 16t + lr, channels e0 + 16et + 4gq .. +3
     const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
     typedef int v2 __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -504,7 +522,6 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
         __builtin_amdgcn_raw_buffer_store_b64(bits, ro,
                                               uint32_t(16 * t + lr) * rowV + (e0 + 16 * et + 4 * gq) * 2, 0, 0);
       }
-    // S = diag(2^{b_C}) S + Kbar^T V
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const f32x4 dec = *reinterpret_cast<const f32x4*>(s_dec + 16 * dt + 4 * gq);
@@ -515,57 +532,51 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     }
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
-      bf16x8 vb[ET], kb[DT];
+      bf16x8 vb[ET];
 #pragma unroll
-      for (int et = 0; et < ET; ++et)
-        vb[et] = *reinterpret_cast<const bf16x8*>(s_vT + (e0 + 16 * et + lr) * TP + 32 * m2 + 8 * gq);
+      for (int et = 0; et < ET; ++et) vb[et] = vT_op(m2, et);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        kb[dt] = *reinterpret_cast<const bf16x8*>(s_kbT + (16 * dt + lr) * TP + 32 * m2 + 8 * gq);
+      for (int d0 = 0; d0 < DT; d0 += 4) {
+        bf16x8 kb[4];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt)
+          kb[dt] = *reinterpret_cast<const bf16x8*>(s_kbT + (16 * (d0 + dt) + lr) * TP + 32 * m2 + 8 * gq);
 #pragma unroll
-        for (int et = 0; et < ET; ++et) S[dt][et] = mfma(kb[dt], vb[et], S[dt][et]);
+        for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt)
+#pragma unroll
+          for (int et = 0; et < ET; ++et) S[d0 + dt][et] = mfma(kb[dt], vb[et], S[d0 + dt][et]);
+      }
     }
   };
 
-  // ---- consumer, second half: the A blocks of the chunk just prepared
-  // (three jobs per consumer, their MFMAs interleaved).
-  auto consume_a = [&]() {
-    int bw[3], bj[3];
+  // ---- every wave, second half: the A blocks of the chunk just prepared.
+  // Jobs 0..9 are the blocks (w, j <= w), jobs 10 and 11 zero the blocks
+  // (0, 1) and (2, 3) that the A.V product reads through its 32-wide steps;
+  // wave w takes jobs w, w + NW, ... Zero jobs run on a valid slot and their
+  // result is replaced, so no job branches.
+  auto a_blocks = [&](const float* s_bet) {
+    for (int job = w; job < 12; job += NW) {
+      int bw, bj;
+      block_of(job, bw, bj);
+      const bool real = job < 10;
+      const int slot = real ? job : 0;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jb = 0; jb < 3; ++jb) block_of(ci + 4 * jb, bw[jb], bj[jb]);
-    const bool third = ci + 8 < 10;  // jobs 10 and 11 only zero their block
-    f32x4 acc[3];
-#pragma unroll
-    for (int jb = 0; jb < 3; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      const int col = 32 * u + 8 * gq;
-      bf16x8 aop[3], bop[3];
-#pragma unroll
-      for (int jb = 0; jb < 3; ++jb) {
-        if (jb < 2 || third) {
-          aop[jb] = *reinterpret_cast<const bf16x8*>(s_ke + (16 * bj[jb] + lr) * KP + col);
-          bop[jb] = *reinterpret_cast<const bf16x8*>(s_qv + ((ci + 4 * jb) * 16 + lr) * KP + col);
-        }
+      for (int u = 0; u < KS; ++u) {
+        const int col = 32 * u + 8 * gq;
+        const bf16x8 aop = *reinterpret_cast<const bf16x8*>(s_ke + (16 * bj + lr) * KP + col);
+        const bf16x8 bop = *reinterpret_cast<const bf16x8*>(s_qv + (slot * 16 + lr) * KP + col);
+        acc = mfma(aop, bop, acc);
       }
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(s_bet + 16 * bj + 4 * gq);
+      float out[4];
 #pragma unroll
-      for (int jb = 0; jb < 3; ++jb)
-        if (jb < 2 || third) acc[jb] = mfma(aop[jb], bop[jb], acc[jb]);
-    }
-#pragma unroll
-    for (int jb = 0; jb < 3; ++jb) {
-      float out[4] = {0.f, 0.f, 0.f, 0.f};
-      if (jb < 2 || third) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sl = 4 * gq + i;
-          const bool keep = (bj[jb] < bw[jb]) || (sl <= lr);
-          out[i] = keep ? acc[jb][i] * s_beta[16 * bj[jb] + sl] : 0.f;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * gq + i;
+        const bool keep = real && ((bj < bw) || (sl <= lr));
+        out[i] = keep ? acc[i] * bt[i] : 0.f;
       }
-      st4(s_a + (16 * bw[jb] + lr) * TP + 16 * bj[jb] + 4 * gq, out);
+      st4(s_a + (16 * bw + lr) * TP + 16 * bj + 4 * gq, out);
     }
   };
 
@@ -575,28 +586,41 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   if (producer) {
     Raw<PCPL, PVPL> R;
     float cs[4][PCPL];
+    const bool beta_wave = w == 0;
+    uint32_t bnext = 0, bnext2 = 0;  // raw beta of the next chunks (wave 0)
     load_g(R, 0);
-    load_qkb(R, 0);
+    load_qk(R, 0);
     load_v(R, 0);
+    if (beta_wave) {
+      const uint32_t b0 = load_beta(0);
+      bnext = load_beta(1);
+      s_beta[lane] = __uint_as_float(b0 << 16);
+    }
     scan(R, cs);
     load_g(R, 1);
     __syncthreads();
     for (int s = 0; s <= nchunks; s += 2) {
       // even chunk s: LDS buffers 0; odd chunk s + 1: buffers 1
-      if (s < nchunks) produce_a(R, cs, s_qh0, s_kbT0, s_decay);
-      load_qkb(R, s + 1);
+      if (s < nchunks) produce_a(R, cs, s_qh, s_kbT0, s_decay, s_beta);
+      load_qk(R, s + 1);
+      if (beta_wave) bnext2 = load_beta(s + 2);
       __syncthreads();
+      if (s < nchunks) a_blocks(s_beta);
       if (s < nchunks) produce_b(R.v);
       load_v(R, s + 1);
+      if (beta_wave) s_beta[kC + lane] = __uint_as_float(bnext << 16);
       if (s + 1 < nchunks) scan(R, cs);
       load_g(R, s + 2);
       __syncthreads();
       if (s + 1 > nchunks) break;
-      if (s + 1 < nchunks) produce_a(R, cs, s_qh1, s_kbT1, s_decay + DK);
-      load_qkb(R, s + 2);
+      if (s + 1 < nchunks) produce_a(R, cs, s_qh, s_kbT1, s_decay + DK, s_beta + kC);
+      load_qk(R, s + 2);
+      if (beta_wave) bnext = load_beta(s + 3);
       __syncthreads();
+      if (s + 1 < nchunks) a_blocks(s_beta + kC);
       if (s + 1 < nchunks) produce_b(R.v);
       load_v(R, s + 2);
+      if (beta_wave) s_beta[lane] = __uint_as_float(bnext2 << 16);
       if (s + 2 < nchunks) scan(R, cs);
       load_g(R, s + 3);
       __syncthreads();
@@ -607,16 +631,23 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int et = 0; et < ET; ++et) S[dt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[4][ET];  // o^T of the chunk in flight, between its two halves
     __syncthreads();  // the producers' first scan
     for (int s = 0; s <= nchunks; s += 2) {
-      if (s >= 1) consume_state(S, s - 1, s_qh1, s_kbT1, s_decay + DK);
+      if (s >= 1) consume_finish(S, acc, s - 1, s_kbT1, s_decay + DK);
       __syncthreads();
-      if (s < nchunks) consume_a();
+      if (s < nchunks) {
+        a_blocks(s_beta);
+        consume_inter(S, acc);
+      }
       __syncthreads();
       if (s + 1 > nchunks) break;
-      consume_state(S, s, s_qh0, s_kbT0, s_decay);
+      consume_finish(S, acc, s, s_kbT0, s_decay);
       __syncthreads();
-      if (s + 1 < nchunks) consume_a();
+      if (s + 1 < nchunks) {
+        a_blocks(s_beta + kC);
+        consume_inter(S, acc);
+      }
       __syncthreads();
     }
     if (final_state != nullptr) {
@@ -632,11 +663,37 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   }
 }
 
+// Segment slots sorted by chunk count, longest first (ties: lower slot first):
+// order[rank] = slot. One work-group; each thread ranks its slots against all
+// others (chunk counts staged in LDS, read as broadcasts).
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderMaxSegs = 2048;
+
+__global__ __launch_bounds__(kOrderThreads) void kda_order_kernel(const int32_t* __restrict__ cu,
+                                                                  int32_t max_segs,
+                                                                  int32_t* __restrict__ order) {
+  __shared__ int32_t s_nch[kOrderMaxSegs];
+  for (int i = threadIdx.x; i < max_segs; i += kOrderThreads) {
+    const int64_t len = int64_t(cu[i + 1]) - int64_t(cu[i]);  // malformed: flagged by the main kernel
+    s_nch[i] = len > 0 ? int32_t((len + kC - 1) / kC) : 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < max_segs; i += kOrderThreads) {
+    const int mine = s_nch[i];
+    int rank = 0;
+    for (int j = 0; j < max_segs; ++j) {
+      const int other = s_nch[j];
+      rank += (other > mine) || (other == mine && j < i);
+    }
+    order[rank] = i;
+  }
+}
+
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                        int32_t H, float scale, void* o, float* fs, int32_t* flags,
-                       hipStream_t s) {
+                       int32_t* order, hipStream_t s) {
   using C = Cfg<DK, DV>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -645,12 +702,17 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  if (order != nullptr) {
+    hipLaunchKernelGGL(kda_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, cu, max_segs, order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t blocks = int64_t(max_segs) * H + kTailBlocks;
   hipLaunchKernelGGL((kda_chunk_kernel<DK, DV>), dim3(unsigned(blocks)), dim3(C::NT), C::bytes, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(g),
-                     static_cast<const bf16*>(beta), cu, max_segs, N, H, scale,
-                     static_cast<bf16*>(o), fs, flags);
+                     static_cast<const bf16*>(beta), cu, order, max_segs, N, H, scale,
+                     static_cast<bf16*>(o), fs, flags, 0);
   return hipGetLastError();
 }
 
@@ -660,18 +722,26 @@ bool kda_chunk_supported(int32_t Dk, int32_t Dv, int32_t dtype) {
   return dtype == 0 && (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
 }
 
+size_t kda_chunk_workspace_bytes(int32_t Dk, int32_t Dv, int32_t dtype, int32_t max_segs) {
+  if (!kda_chunk_supported(Dk, Dv, dtype) || max_segs < 2 || max_segs > kOrderMaxSegs) return 0;
+  return (size_t(max_segs) * 4 + 255) / 256 * 256;
+}
+
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                             int32_t H, int32_t Dk, int32_t Dv, float scale, void* o,
-                            float* final_state, int32_t* flags, hipStream_t stream) {
+                            float* final_state, int32_t* flags, void* workspace,
+                            hipStream_t stream) {
+  int32_t* order = (cu != nullptr && kda_chunk_workspace_bytes(Dk, Dv, 0, max_segs) > 0)
+                       ? static_cast<int32_t*>(workspace) : nullptr;
   if (Dk == 128 && Dv == 128)
-    return launch_dims<128, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, stream);
+    return launch_dims<128, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, order, stream);
   if (Dk == 64 && Dv == 64)
-    return launch_dims<64, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, stream);
+    return launch_dims<64, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, order, stream);
   if (Dk == 128 && Dv == 64)
-    return launch_dims<128, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, stream);
+    return launch_dims<128, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, order, stream);
   if (Dk == 64 && Dv == 128)
-    return launch_dims<64, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, stream);
+    return launch_dims<64, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, order, stream);
   return hipErrorInvalidValue;
 }
 

@@ -97,3 +97,16 @@ def test_workspace_query_is_host_only(lib):
     for N, H, D in [(512, 2, 32), (65536, 32, 128), (131072, 32, 128)]:
         ws = lib.pkv_chunk_kda_varlen_workspace_size(N, H, D, D, 256, 0)
         assert ws >= 0
+
+
+def test_workspace_size_and_check(lib):
+    """The chunk path (bf16, Dk/Dv in {64, 128}) keeps a longest-first order of
+    the segment slots (int32 per slot) in the workspace; other paths need none."""
+    size = lib.pkv_chunk_kda_varlen_workspace_size
+    assert size(65536, 32, 128, 128, 256, 0) >= 256 * 4
+    assert size(65536, 32, 128, 128, 1, 0) == 0          # one segment: nothing to order
+    assert size(512, 2, 32, 32, 16, 1) == 0              # fp32 token-serial path
+    assert size(512, 2, 32, 32, 16, 0) == 0              # Dk = 32: token-serial path
+    # a valid call without the workspace is refused before any launch
+    assert lib.pkv_chunk_kda_varlen(*_kda_args(max_segs=4)) == 3
+    assert lib.pkv_chunk_kda_varlen(*_kda_args(ws=P, ws_bytes=8)) == 3

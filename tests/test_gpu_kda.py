@@ -209,3 +209,33 @@ def test_bad_cu_seqlens_sets_flag():
         pkv.chunk_kda_varlen(q, k, v, g, beta, cud, flags=flags)
         torch.cuda.synchronize()
         assert int(flags.item()) & pkv.FLAG_BAD_CU_SEQLENS, bad
+
+
+@pytest.mark.parametrize("n_slots", [37, 2100])
+def test_slot_order_ties_phantoms_and_unordered_path(n_slots):
+    """Longest-first processing order (up to 2048 slots) and the plain slot
+    order above it give the oracle's per-segment results: lengths with ties,
+    empty slots between real ones, and phantom slots at the end."""
+    pkv = _pkv()
+    rng = np.random.default_rng(n_slots)
+    H, D = 2, 64
+    lens = [int(x) for x in rng.choice([0, 1, 64, 65, 130, 130, 7, 64, 0, 300], size=30)]
+    real = np.concatenate([[0], np.cumsum(lens)])
+    cu = np.concatenate([real, [real[-1]] * (n_slots + 1 - len(real))])
+    N = int(real[-1]) + 5
+    ts = _small_case(rng, N, H, D, D, torch.bfloat16, cu)
+    q, k, v, g, beta = [t.to(device()) for t in ts]
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    print(f"slots {n_slots}: workspace {pkv.chunk_kda_varlen_workspace_size(N, H, D, D, n_slots, torch.bfloat16)} bytes",
+          flush=True)
+    o, fs = pkv.chunk_kda_varlen(q[None], k[None], v[None], g[None], beta[None], cud)
+    torch.cuda.synchronize()
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], cu)
+    check_close(f64(o[0]), ro, "bf16", "o")
+    for i in range(len(cu) - 1):
+        if cu[i + 1] > cu[i]:
+            check_close(f64(o[0])[cu[i]:cu[i + 1]], ro[cu[i]:cu[i + 1]], "bf16", f"segment {i}")
+            check_close(f64(fs[i]), rfs[i], "bf16", f"state {i}")
+        else:
+            assert torch.count_nonzero(fs[i]).item() == 0
+    assert torch.count_nonzero(o[0, cu[-1]:]).item() == 0
