@@ -286,6 +286,12 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   constexpr int NW = NT / 64;  // waves per work-group
   const int ci = w - NP;               // consumer index 0..3
   const int e0 = ci * C::EW;
+  // Row rho of 16-column tile et of a consumer's state / output holds channel
+  // e0 + ecol(et, rho); the map puts each lane's 4 x ET output values of a
+  // token next to each other (one vector store per token tile). The labels
+  // are only a permutation of the consumer's columns: S, V^T and o use the
+  // same one.
+  auto ecol = [&](int et, int rho) { return 4 * ET * (rho >> 2) + 4 * et + (rho & 3); };
 
   // Loads are unconditional so the wait counts stay exact: a chunk index past
   // the segment gets an empty buffer (every read returns 0, no memory access).
@@ -494,7 +500,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     const int64_t p0 = start + int64_t(c) * kC;
     const int Lc = chunk_len(c);
     auto vT_op = [&](int m2, int et) {
-      return *reinterpret_cast<const bf16x8*>(s_vT + (e0 + 16 * et + lr) * TP + 32 * m2 + 8 * gq);
+      return *reinterpret_cast<const bf16x8*>(s_vT + (e0 + ecol(et, lr)) * TP + 32 * m2 + 8 * gq);
     };
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
@@ -509,19 +515,27 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
 #pragma unroll
         for (int et = 0; et < ET; ++et) acc[t][et] = mfma(va[et], aa[t], acc[t][et]);
     }
-    // acc[t][et] holds o of token 16t + lr, channels e0 + 16et + 4gq .. +3
+    // acc[t][et][i] holds o of token 16t + lr, channel e0 + 4 ET gq + 4 et + i
     const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
-    typedef int v2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      uint32_t w2[2 * ET];
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
         const f32x4 x = acc[t][et];
-        const v2 bits = {int(pk2(x[0] * scale, x[1] * scale)), int(pk2(x[2] * scale, x[3] * scale))};
-        // rows past the chunk end fall outside the buffer range and are dropped
-        __builtin_amdgcn_raw_buffer_store_b64(bits, ro,
-                                              uint32_t(16 * t + lr) * rowV + (e0 + 16 * et + 4 * gq) * 2, 0, 0);
+        w2[2 * et] = pk2(x[0] * scale, x[1] * scale);
+        w2[2 * et + 1] = pk2(x[2] * scale, x[3] * scale);
       }
+      // rows past the chunk end fall outside the buffer range and are dropped
+      const uint32_t off = uint32_t(16 * t + lr) * rowV + (e0 + 4 * ET * gq) * 2;
+      if constexpr (ET == 2) {
+        __builtin_amdgcn_raw_buffer_store_b128(v4i{int(w2[0]), int(w2[1]), int(w2[2]), int(w2[3])}, ro,
+                                               off, 0, 0);
+      } else {
+        typedef int v2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(v2{int(w2[0]), int(w2[1])}, ro, off, 0, 0);
+      }
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const f32x4 dec = *reinterpret_cast<const f32x4*>(s_dec + 16 * dt + 4 * gq);
@@ -658,7 +672,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
         for (int et = 0; et < ET; ++et)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + 16 * et + lr] = S[dt][et][i];
+            fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + ecol(et, lr)] = S[dt][et][i];
     }
   }
 }
