@@ -76,25 +76,26 @@ __device__ __forceinline__ void block_of(int b, int& w, int& j) {
 
 template <int DK, int DV>
 struct Cfg {
-  static constexpr int NP = 4 * (DK / 64);  // producer waves: 4 sub-chunks x Dk/64 channel halves
+  static constexpr int NP = 4;              // producer waves: one per 16-token sub-chunk
   static constexpr int NT = 64 * (NP + 4);  // threads: producers + 4 consumers
-  static constexpr int PCPL = 4;            // producer k channels per lane (4 tokens each)
-  static constexpr int PVPL = 4 * DV / DK;  // producer v channels per lane
-  static constexpr int EW = DV / 4;      // consumer state / output columns
-  static constexpr int ET = EW / 16;     // 16-column tiles per consumer
-  static constexpr int DT = DK / 16;     // 16-row state tiles
-  static constexpr int KS = DK / 32;     // contraction steps over Dk
-  static constexpr int KP = DK + 8;      // token-major LDS rows (bf16 elements)
-  static constexpr int TP = kC + 8;      // transposed / A rows (bf16 elements)
-  // Small tables first: ds_read/ds_write immediates reach 64 KiB, so tiles
-  // read at many row offsets sit low where one base register serves them.
+  static constexpr int PCPL = DK / 16;      // producer k channels per lane (4 tokens each)
+  static constexpr int PVPL = DV / 16;      // producer v channels per lane
+  static constexpr int EW = DV / 4;         // consumer state / output columns
+  static constexpr int ET = EW / 16;        // 16-column tiles per consumer
+  static constexpr int DT = DK / 16;        // 16-row state tiles
+  static constexpr int KS = DK / 32;        // contraction steps over Dk
+  static constexpr int KP = DK + 8;         // Q^, KE, query versions: token-major rows (bf16)
+  static constexpr int RP = DK + 16;        // Kbar: token-major rows, read transposed
+  static constexpr int VP = DV + 16;        // V: token-major rows, read transposed
+  static constexpr int TP = kC + 8;         // A rows (bf16)
+  // Small tables first: ds_read/ds_write immediates reach 64 KiB.
   static constexpr int off_decay = 0;                        // float [2][DK]
   static constexpr int off_beta = off_decay + 2 * DK * 4;    // float [2][kC]
   static constexpr int off_T = off_beta + 2 * kC * 4;        // float [DK][4] sub-chunk totals
   static constexpr int off_a = off_T + DK * 4 * 4;           // A, bf16 [kC][TP]
-  static constexpr int off_vT = off_a + kC * TP * 2;         // V^T, bf16 [DV][TP]
-  static constexpr int off_kbT = off_vT + DV * TP * 2;       // Kbar^T, bf16 [2][DK][TP]
-  static constexpr int off_qh = off_kbT + 2 * DK * TP * 2;   // Q^, bf16 [kC][KP]
+  static constexpr int off_v = off_a + kC * TP * 2;          // V, bf16 [kC][VP]
+  static constexpr int off_kb = off_v + kC * VP * 2;         // Kbar, bf16 [2][kC][RP]
+  static constexpr int off_qh = off_kb + 2 * kC * RP * 2;    // Q^, bf16 [kC][KP]
   static constexpr int off_ke = off_qh + kC * KP * 2;        // KE, bf16 [kC][KP]
   static constexpr int off_qv = off_ke + kC * KP * 2;        // query versions, bf16 [10][16][KP]
   static constexpr int bytes = off_qv + 10 * 16 * KP * 2;
@@ -162,14 +163,46 @@ __device__ __forceinline__ void st4(bf16* dst, float a, float b, float c, float 
   *reinterpret_cast<u32x2*>(dst) = u32x2{pk2(a, b), pk2(c, d)};
 }
 __device__ __forceinline__ void st4(bf16* dst, const float* x) { st4(dst, x[0], x[1], x[2], x[3]); }
+// n floats (n in {4, 8}) -> n bf16 at an 8n/4-byte aligned address, one store.
+template <int n>
+__device__ __forceinline__ void stn(bf16* dst, const float* x) {
+  if constexpr (n == 4) {
+    st4(dst, x);
+  } else {
+    static_assert(n == 8, "store width");
+    *reinterpret_cast<u32x4*>(dst) =
+        u32x4{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(x[4], x[5]), pk2(x[6], x[7])};
+  }
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane k supplies the address of 4 consecutive bf16; lane j = 4a + b receives
+// element b of the chunks supplied by lanes a, 4 + a, 8 + a, 12 + a, in that
+// order. So if lane k points at row (token) r0 + k/4, column c0 + 4 (k % 4) of
+// a token-major tile, lane j gets column c0 + j of rows r0 .. r0 + 3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 tr4(const bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 join_tr(s16x4 lo, s16x4 hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
 
 // Raw producer inputs of one chunk: 4 tokens x PCPL channels of q, k, g and
 // PVPL channels of v as packed bf16 pairs. They stay packed until used, so a
 // load is never waited for before its first use.
 template <int PCPL, int PVPL>
 struct Raw {
-  uint32_t g[4][PCPL / 2], q[4][PCPL / 2], k[4][PCPL / 2];
+  uint32_t g[4][PCPL / 2];
   uint32_t v[4][PVPL / 2];
+};
+// q and k of one chunk (two sets alternate, so they are loaded a whole chunk
+// step before use).
+template <int PCPL>
+struct RawQK {
+  uint32_t q[4][PCPL / 2], k[4][PCPL / 2];
 };
 
 // bf16 element c of a packed pair array, as fp32 (exact).
@@ -199,7 +232,7 @@ __device__ __forceinline__ void wload(uint32_t (&w)[n], __amdgpu_buffer_rsrc_t r
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
+__global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ order, int32_t max_segs, int64_t N, int32_t H, float scale,
@@ -208,7 +241,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
   constexpr int PCPL = C::PCPL, PVPL = C::PVPL, ET = C::ET, DT = C::DT, KS = C::KS;
-  constexpr int KP = C::KP, TP = C::TP;
+  constexpr int KP = C::KP, TP = C::TP, RP = C::RP, VP = C::VP;
 
   // Tile bases are made opaque to the compiler (lds_zero is 0 at run time):
   // an LDS access then takes one base register per tile and lane pattern plus
@@ -219,9 +252,9 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   bf16* s_qh = reinterpret_cast<bf16*>(tile(C::off_qh));
   bf16* s_qv = reinterpret_cast<bf16*>(tile(C::off_qv));
   bf16* s_ke = reinterpret_cast<bf16*>(tile(C::off_ke));
-  bf16* s_kbT0 = reinterpret_cast<bf16*>(tile(C::off_kbT));   // Kbar^T of even / odd chunks
-  bf16* s_kbT1 = reinterpret_cast<bf16*>(tile(C::off_kbT + DK * TP * 2));
-  bf16* s_vT = reinterpret_cast<bf16*>(tile(C::off_vT));
+  bf16* s_kb0 = reinterpret_cast<bf16*>(tile(C::off_kb));   // Kbar of even / odd chunks
+  bf16* s_kb1 = reinterpret_cast<bf16*>(tile(C::off_kb + kC * RP * 2));
+  bf16* s_v = reinterpret_cast<bf16*>(tile(C::off_v));
   bf16* s_a = reinterpret_cast<bf16*>(tile(C::off_a));
   float* s_decay = reinterpret_cast<float*>(tile(C::off_decay));
   float* s_beta = reinterpret_cast<float*>(tile(C::off_beta));
@@ -271,14 +304,14 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   };
 
   // ---------------------------------------------------------------- roles
-  // Producer wave: sub-chunk sw, key channels [64 kh, 64 kh + 64). Lane: 4
-  // tokens [tok0, tok0 + 4) (quad position tq), 4 channels from ch0.
+  // Producer wave w: sub-chunk sw = w, all channels. Lane: 4 tokens
+  // [tok0, tok0 + 4) (quad position tq), PCPL k channels from ch0 and PVPL v
+  // channels from vch0, so each load covers four tokens x whole rows.
   const int sw = w & 3;
-  const int kh = w >> 2;
   const int tq = lane & 3;
   const int cg = lane >> 2;
-  const int ch0 = 64 * kh + PCPL * cg;
-  const int vch0 = kh * (64 * DV / DK) + PVPL * cg;
+  const int ch0 = PCPL * cg;
+  const int vch0 = PVPL * cg;
   const int tok0 = 16 * sw + 4 * tq;
   // MFMA lane layout (consumers, and every wave for the A blocks).
   const int gq = lane >> 4;
@@ -295,10 +328,11 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
 
   // Loads are unconditional so the wait counts stay exact: a chunk index past
   // the segment gets an empty buffer (every read returns 0, no memory access).
-  // Each part of the raw inputs is refilled right after its last use: q, k
-  // of chunk c+1 after the MFMA operands of chunk c, v of chunk c+1 after V^T
-  // of chunk c, g of chunk c+2 after the scan of chunk c+1. beta goes through
-  // LDS (double-buffered by chunk parity): wave 0 loads it a step ahead.
+  // Every raw input is loaded a whole chunk step before its use: q, k of chunk
+  // c+1 at the start of step c (two register sets alternate), v of chunk c+1
+  // right after V^T of chunk c, g of chunk c+2 after the scan of chunk c+1.
+  // beta goes through LDS (double-buffered by chunk parity): wave 0 loads it a
+  // step ahead.
   struct Src {
     int64_t tokbase;
     uint32_t nK, nV, nB;
@@ -320,7 +354,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wload(R.g[i], rg, uint32_t(tok0 + i) * rowK + ch0 * 2);
   };
-  auto load_qk = [&](Raw<PCPL, PVPL>& R, int c) {
+  auto load_qk = [&](RawQK<PCPL>& R, int c) {
     const Src r = src_of(c);
     const auto rq = rsrc(q + r.tokbase * DK, r.nK), rk = rsrc(k + r.tokbase * DK, r.nK);
 #pragma unroll
@@ -378,8 +412,8 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   // f4 = 2^{T_{w-1} + T_{w-2}} (block (3, 0)); decay = 2^{T_0 + .. + T_3}.
   // The sub-chunk index is a compile-time constant inside (one instance per
   // sub-chunk), so every choice below is resolved without branches.
-  auto produce_a_sw = [&](auto swc, const Raw<PCPL, PVPL>& R, const float (&cs)[4][PCPL],
-                          bf16* s_qh, bf16* s_kbT, float* s_dec, const float* s_bet) {
+  auto produce_a_sw = [&](auto swc, const RawQK<PCPL>& R, const float (&cs)[4][PCPL],
+                          bf16* s_qh, bf16* s_kb, float* s_dec, const float* s_bet) {
     constexpr int sw = decltype(swc)::value;
     constexpr int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
     float Tw[PCPL], f[5][PCPL], dec[PCPL];
@@ -399,67 +433,65 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
       f[4][c] = ex2(Tm1 + Tm2);
       dec[c] = ex2((Tj[0] + Tj[1]) + (Tj[2] + Tj[3]));
     }
-    if (sw == 0 && tq == 0)
-      *reinterpret_cast<f32x4*>(s_dec + ch0) = f32x4{dec[0], dec[1], dec[2], dec[3]};
-    (void)dec;
-    float kb[PCPL][4];  // [channel][token] for the transposed store
+    if (sw == 0 && tq == 0) {
+#pragma unroll
+      for (int c = 0; c < PCPL; c += 4)
+        *reinterpret_cast<f32x4*>(s_dec + ch0 + c) = f32x4{dec[c], dec[c + 1], dec[c + 2], dec[c + 3]};
+    }
     const f32x4 bt4 = *reinterpret_cast<const f32x4*>(s_bet + tok0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = tok0 + i;
       const float bt = bt4[i];
-      float qt[PCPL], ke[PCPL], t0[PCPL];
+      float qt[PCPL], ke[PCPL], t0[PCPL], kb[PCPL];
 #pragma unroll
       for (int c = 0; c < PCPL; ++c) {
         qt[c] = bf(R.q[i], c) * ex2(cs[i][c]);
         ke[c] = bf(R.k[i], c) * ex2(Tw[c] - cs[i][c]);
         t0[c] = qt[c] * f[0][c];
-        kb[c][i] = ke[c] * (bt * f[1][c]);
+        kb[c] = ke[c] * (bt * f[1][c]);
       }
-      st4(s_qh + tok * KP + ch0, t0);
-      st4(s_ke + tok * KP + ch0, ke);
+      stn<PCPL>(s_qh + tok * KP + ch0, t0);
+      stn<PCPL>(s_ke + tok * KP + ch0, ke);
+      stn<PCPL>(s_kb + tok * RP + ch0, kb);
       bf16* qv = s_qv + (tok & 15) * KP + ch0;  // row of the token in each version slot
 #pragma unroll
       for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[2][c];
-      st4(qv + (vbase + sw) * 16 * KP, t0);
-      if constexpr (sw >= 1) st4(qv + (vbase + sw - 1) * 16 * KP, qt);
+      stn<PCPL>(qv + (vbase + sw) * 16 * KP, t0);
+      if constexpr (sw >= 1) stn<PCPL>(qv + (vbase + sw - 1) * 16 * KP, qt);
       if constexpr (sw >= 2) {
 #pragma unroll
         for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[3][c];
-        st4(qv + (vbase + sw - 2) * 16 * KP, t0);
+        stn<PCPL>(qv + (vbase + sw - 2) * 16 * KP, t0);
       }
       if constexpr (sw == 3) {
 #pragma unroll
         for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[4][c];
-        st4(qv + (vbase + 0) * 16 * KP, t0);
+        stn<PCPL>(qv + (vbase + 0) * 16 * KP, t0);
       }
     }
-#pragma unroll
-    for (int c = 0; c < PCPL; ++c) st4(s_kbT + (ch0 + c) * TP + tok0, kb[c]);
   };
 
-  auto produce_a = [&](const Raw<PCPL, PVPL>& R, const float (&cs)[4][PCPL], bf16* s_qh,
-                       bf16* s_kbT, float* s_dec, const float* s_bet) {
+  auto produce_a = [&](const RawQK<PCPL>& R, const float (&cs)[4][PCPL], bf16* s_qh,
+                       bf16* s_kb, float* s_dec, const float* s_bet) {
     switch (sw) {
-      case 0: produce_a_sw(IntC<0>{}, R, cs, s_qh, s_kbT, s_dec, s_bet); break;
-      case 1: produce_a_sw(IntC<1>{}, R, cs, s_qh, s_kbT, s_dec, s_bet); break;
-      case 2: produce_a_sw(IntC<2>{}, R, cs, s_qh, s_kbT, s_dec, s_bet); break;
-      default: produce_a_sw(IntC<3>{}, R, cs, s_qh, s_kbT, s_dec, s_bet); break;
+      case 0: produce_a_sw(IntC<0>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
+      case 1: produce_a_sw(IntC<1>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
+      case 2: produce_a_sw(IntC<2>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
+      default: produce_a_sw(IntC<3>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
     }
   };
 
-  // ---- producer, second half: V^T of the chunk (channel pair (2j, 2j+1) of
-  // tokens tok0 .. tok0+3 -> two 8-byte rows).
+  // ---- producer, second half: V of the chunk, token-major (the consumers
+  // read it transposed).
   auto produce_b = [&](const uint32_t (&V)[4][PVPL / 2]) {
-    static_assert(PVPL % 2 == 0, "v channels come in pairs");
 #pragma unroll
-    for (int j = 0; j < PVPL / 2; ++j) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(V[1][j], V[0][j], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(V[3][j], V[2][j], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(V[1][j], V[0][j], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(V[3][j], V[2][j], 0x07060302u);
-      *reinterpret_cast<u32x2*>(s_vT + (vch0 + 2 * j) * TP + tok0) = u32x2{lo01, lo23};
-      *reinterpret_cast<u32x2*>(s_vT + (vch0 + 2 * j + 1) * TP + tok0) = u32x2{hi01, hi23};
+    for (int i = 0; i < 4; ++i) {
+      bf16* dst = s_v + (tok0 + i) * VP + vch0;
+      if constexpr (PVPL == 8)
+        *reinterpret_cast<u32x4*>(dst) = u32x4{V[i][0], V[i][1], V[i][2], V[i][3]};
+      else
+        *reinterpret_cast<u32x2*>(dst) = u32x2{V[i][0], V[i][1]};
     }
   };
 
@@ -495,12 +527,21 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   // ---- consumer, first half of step c+1: o of chunk c = acc + V^T A^T
   // (contraction over tokens in steps of 32; causal: the second step only
   // for rows >= 32), scaled and stored; then S = diag(2^{b_C}) S + Kbar^T V.
-  auto consume_finish = [&](f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET], int c, const bf16* s_kbT,
+  auto consume_finish = [&](f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET], int c, const bf16* s_kb,
                             const float* s_dec) {
     const int64_t p0 = start + int64_t(c) * kC;
     const int Lc = chunk_len(c);
-    auto vT_op = [&](int m2, int et) {
-      return *reinterpret_cast<const bf16x8*>(s_vT + (e0 + ecol(et, lr)) * TP + 32 * m2 + 8 * gq);
+    // Operands whose contraction runs over the tokens 32 m2 + 8 gq + 0..7 of
+    // the chunk, read transposed from token-major tiles: lane lr gets column
+    // c0(lr / 4 ...) as set by the supplying lanes (see tr4).
+    const int trow = 8 * gq + (lr >> 2);  // token supplied by this lane, + 32 m2 (+ 4)
+    auto vT_op = [&](int m2, int et) {    // V^T rows e0 + ecol(et, lr)
+      const bf16* p = s_v + (32 * m2 + trow) * VP + e0 + 4 * ET * (lr & 3) + 4 * et;
+      return join_tr(tr4(p), tr4(p + 4 * VP));
+    };
+    auto kbT_op = [&](int m2, int dt) {   // Kbar^T rows 16 dt + lr
+      const bf16* p = s_kb + (32 * m2 + trow) * RP + 16 * dt + 4 * (lr & 3);
+      return join_tr(tr4(p), tr4(p + 4 * RP));
     };
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
@@ -553,8 +594,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
       for (int d0 = 0; d0 < DT; d0 += 4) {
         bf16x8 kb[4];
 #pragma unroll
-        for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt)
-          kb[dt] = *reinterpret_cast<const bf16x8*>(s_kbT + (16 * (d0 + dt) + lr) * TP + 32 * m2 + 8 * gq);
+        for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt) kb[dt] = kbT_op(m2, d0 + dt);
 #pragma unroll
         for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt)
 #pragma unroll
@@ -599,11 +639,12 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
   // (two per step), so neither role keeps the other's registers live.
   if (producer) {
     Raw<PCPL, PVPL> R;
+    RawQK<PCPL> QA, QB;  // q, k of even / odd chunks
     float cs[4][PCPL];
     const bool beta_wave = w == 0;
     uint32_t bnext = 0, bnext2 = 0;  // raw beta of the next chunks (wave 0)
     load_g(R, 0);
-    load_qk(R, 0);
+    load_qk(QA, 0);
     load_v(R, 0);
     if (beta_wave) {
       const uint32_t b0 = load_beta(0);
@@ -615,8 +656,8 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     __syncthreads();
     for (int s = 0; s <= nchunks; s += 2) {
       // even chunk s: LDS buffers 0; odd chunk s + 1: buffers 1
-      if (s < nchunks) produce_a(R, cs, s_qh, s_kbT0, s_decay, s_beta);
-      load_qk(R, s + 1);
+      load_qk(QB, s + 1);
+      if (s < nchunks) produce_a(QA, cs, s_qh, s_kb0, s_decay, s_beta);
       if (beta_wave) bnext2 = load_beta(s + 2);
       __syncthreads();
       if (s < nchunks) a_blocks(s_beta);
@@ -627,8 +668,8 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
       load_g(R, s + 2);
       __syncthreads();
       if (s + 1 > nchunks) break;
-      if (s + 1 < nchunks) produce_a(R, cs, s_qh, s_kbT1, s_decay + DK, s_beta + kC);
-      load_qk(R, s + 2);
+      load_qk(QA, s + 2);
+      if (s + 1 < nchunks) produce_a(QB, cs, s_qh, s_kb1, s_decay + DK, s_beta + kC);
       if (beta_wave) bnext = load_beta(s + 3);
       __syncthreads();
       if (s + 1 < nchunks) a_blocks(s_beta + kC);
@@ -648,7 +689,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
     f32x4 acc[4][ET];  // o^T of the chunk in flight, between its two halves
     __syncthreads();  // the producers' first scan
     for (int s = 0; s <= nchunks; s += 2) {
-      if (s >= 1) consume_finish(S, acc, s - 1, s_kbT1, s_decay + DK);
+      if (s >= 1) consume_finish(S, acc, s - 1, s_kb1, s_decay + DK);
       __syncthreads();
       if (s < nchunks) {
         a_blocks(s_beta);
@@ -656,7 +697,7 @@ __global__ __launch_bounds__(64 * (4 * (DK / 64) + 4), 1) void kda_chunk_kernel(
       }
       __syncthreads();
       if (s + 1 > nchunks) break;
-      consume_finish(S, acc, s, s_kbT0, s_decay);
+      consume_finish(S, acc, s, s_kb0, s_decay);
       __syncthreads();
       if (s + 1 < nchunks) {
         a_blocks(s_beta + kC);
