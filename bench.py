@@ -37,8 +37,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="flat_microbatch")
     p.add_argument("--final-state", choices=["auto", "on", "off"], default="auto")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -527,10 +527,8 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   // ---- consumer, first half of step c+1: o of chunk c = acc + V^T A^T
   // (contraction over tokens in steps of 32; causal: the second step only
   // for rows >= 32), scaled and stored; then S = diag(2^{b_C}) S + Kbar^T V.
-  auto consume_finish = [&](f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET], int c, const bf16* s_kb,
-                            const float* s_dec) {
-    const int64_t p0 = start + int64_t(c) * kC;
-    const int Lc = chunk_len(c);
+  auto consume_finish = [&](f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET], uint32_t (&opk)[4][2 * ET],
+                            const bf16* s_kb, const float* s_dec) {
     // Operands whose contraction runs over the tokens 32 m2 + 8 gq + 0..7 of
     // the chunk, read transposed from token-major tiles: lane lr gets column
     // c0(lr / 4 ...) as set by the supplying lanes (see tr4).
@@ -556,27 +554,16 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
 #pragma unroll
         for (int et = 0; et < ET; ++et) acc[t][et] = mfma(va[et], aa[t], acc[t][et]);
     }
-    // acc[t][et][i] holds o of token 16t + lr, channel e0 + 4 ET gq + 4 et + i
-    const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
+    // acc[t][et][i] holds o of token 16t + lr, channel e0 + 4 ET gq + 4 et + i;
+    // packed here, stored at the start of the next half (store_out)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t w2[2 * ET];
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
         const f32x4 x = acc[t][et];
-        w2[2 * et] = pk2(x[0] * scale, x[1] * scale);
-        w2[2 * et + 1] = pk2(x[2] * scale, x[3] * scale);
+        opk[t][2 * et] = pk2(x[0] * scale, x[1] * scale);
+        opk[t][2 * et + 1] = pk2(x[2] * scale, x[3] * scale);
       }
-      // rows past the chunk end fall outside the buffer range and are dropped
-      const uint32_t off = uint32_t(16 * t + lr) * rowV + (e0 + 4 * ET * gq) * 2;
-      if constexpr (ET == 2) {
-        __builtin_amdgcn_raw_buffer_store_b128(v4i{int(w2[0]), int(w2[1]), int(w2[2]), int(w2[3])}, ro,
-                                               off, 0, 0);
-      } else {
-        typedef int v2 __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(v2{int(w2[0]), int(w2[1])}, ro, off, 0, 0);
-      }
-    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const f32x4 dec = *reinterpret_cast<const f32x4*>(s_dec + 16 * dt + 4 * gq);
@@ -599,6 +586,27 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt)
 #pragma unroll
           for (int et = 0; et < ET; ++et) S[d0 + dt][et] = mfma(kb[dt], vb[et], S[d0 + dt][et]);
+      }
+    }
+  };
+
+  // ---- consumer, second half of step c+1: the outputs of chunk c packed in
+  // the first half. Issuing the stores here keeps them off the first half,
+  // where the producers' loads fill the vector memory queue.
+  auto store_out = [&](const uint32_t (&opk)[4][2 * ET], int c) {
+    const int64_t p0 = start + int64_t(c) * kC;
+    const int Lc = chunk_len(c);
+    const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // rows past the chunk end fall outside the buffer range and are dropped
+      const uint32_t off = uint32_t(16 * t + lr) * rowV + (e0 + 4 * ET * gq) * 2;
+      if constexpr (ET == 2) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v4i{int(opk[t][0]), int(opk[t][1]), int(opk[t][2]), int(opk[t][3])}, ro, off, 0, 0);
+      } else {
+        typedef int v2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(v2{int(opk[t][0]), int(opk[t][1])}, ro, off, 0, 0);
       }
     }
   };
@@ -687,18 +695,21 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
 #pragma unroll
       for (int et = 0; et < ET; ++et) S[dt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 acc[4][ET];  // o^T of the chunk in flight, between its two halves
+    uint32_t opk[4][2 * ET];  // packed outputs of the chunk finished in this step
     __syncthreads();  // the producers' first scan
     for (int s = 0; s <= nchunks; s += 2) {
-      if (s >= 1) consume_finish(S, acc, s - 1, s_kb1, s_decay + DK);
+      if (s >= 1) consume_finish(S, acc, opk, s_kb1, s_decay + DK);
       __syncthreads();
+      if (s >= 1) store_out(opk, s - 1);
       if (s < nchunks) {
         a_blocks(s_beta);
         consume_inter(S, acc);
       }
       __syncthreads();
       if (s + 1 > nchunks) break;
-      consume_finish(S, acc, s, s_kb0, s_decay);
+      consume_finish(S, acc, opk, s_kb0, s_decay);
       __syncthreads();
+      store_out(opk, s);
       if (s + 1 < nchunks) {
         a_blocks(s_beta + kC);
         consume_inter(S, acc);
