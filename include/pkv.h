@@ -113,9 +113,13 @@ pkv_status pkv_short_conv_segmask(const void* x, const float* w, const int32_t* 
 
 /*
  * Bytes of device workspace pkv_chunk_kda_varlen needs for these sizes
- * (0 means no workspace is needed and NULL may be passed). With bf16 and
- * Dk, Dv in {64, 128} and 2 <= max_segs <= 2048 it holds the order in which
- * the segment slots are processed (longest first), one int32 per slot.
+ * (0 means no workspace is needed and NULL may be passed). Host-only: no HIP
+ * call. With bf16 and Dk, Dv in {64, 128} it holds the call's work plan: the
+ * (segment, chunk range) runs in the order they are processed, longest first,
+ * and, for segments long enough to be cut into several runs so that one
+ * document does not set the length of the whole launch, the state and the
+ * per-channel decay product of every run but the last (fp32, at most
+ * 1024 + H run-heads in all, i.e. about 64 MiB at Dk = Dv = 128).
  */
 size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,
                                            int32_t max_segs, int32_t dtype);
@@ -139,16 +143,18 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
  * final_state float32 [max_segs, H, Dk, Dv] or NULL (not written).
  * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in.
  * workspace   device buffer of at least pkv_chunk_kda_varlen_workspace_size()
- *             bytes, 4-byte aligned (NULL allowed when that size is 0);
+ *             bytes, 16-byte aligned (NULL allowed when that size is 0);
  *             contents are scratch, overwritten by every call, so calls that
- *             share a workspace must be ordered on one stream.
+ *             share a workspace must be ordered on one stream. After the
+ *             call its int32 words 0 and 1 hold the number of runs and of
+ *             runs whose state was saved for the next piece (diagnostics).
  * Supported: Dk, Dv in {32, 64, 128}. Inputs with large positive g or with
  * 16 * max|g| beyond ~60 within a segment may lose accuracy (the chunked
  * factorisation bounds exponents per 16-token sub-chunk).
  * Errors: PKV_ERR_INVALID_ARGUMENT for NULL tensors, N < 1, N > INT32_MAX,
- * H < 1, max_segs < 1 (with cu_seqlens) or o aliasing an input;
- * PKV_ERR_UNSUPPORTED for other Dk/Dv or dtype; PKV_ERR_WORKSPACE if the
- * workspace is too small.
+ * H < 1, max_segs < 1 (with cu_seqlens), max_segs * H > 2^22 or o aliasing
+ * an input; PKV_ERR_UNSUPPORTED for other Dk/Dv or dtype; PKV_ERR_WORKSPACE
+ * if the workspace is too small or not 16-byte aligned.
  */
 pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta, const int32_t* cu_seqlens, int32_t max_segs,

@@ -71,9 +71,7 @@ pkv_status pkv_short_conv_segmask(const void* x, const float* w, const int32_t* 
 
 size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,
                                            int32_t max_segs, int32_t dtype) {
-  (void)N;
-  (void)H;
-  return pkv::kda_chunk_workspace_bytes(Dk, Dv, dtype, max_segs);
+  return pkv::kda_chunk_workspace_bytes(N, H, Dk, Dv, dtype, max_segs);
 }
 
 pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
@@ -92,7 +90,7 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
   }
   if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv))
     return PKV_ERR_UNSUPPORTED;
-  if (int64_t(max_segs) * H + 64 > kInt32Max) return PKV_ERR_INVALID_ARGUMENT;
+  if (int64_t(max_segs) * H > (int64_t(1) << 22)) return PKV_ERR_INVALID_ARGUMENT;
   const int64_t es = elem_size(dtype);
   const int64_t o_bytes = N * H * Dv * es;
   if (overlaps(o, o_bytes, q, N * H * Dk * es) || overlaps(o, o_bytes, k, N * H * Dk * es) ||
@@ -100,7 +98,9 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
       overlaps(o, o_bytes, beta, N * H * es))
     return PKV_ERR_INVALID_ARGUMENT;
   const size_t need = pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
+    return PKV_ERR_WORKSPACE;
   if (pkv::kda_chunk_supported(Dk, Dv, dtype))
     return from_hip(pkv::launch_kda_chunk(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
                                           scale, o, final_state, flags, workspace,

@@ -39,9 +39,11 @@ hipError_t launch_kda_serial(const void* q, const void* k, const void* v, const 
 
 bool kda_chunk_supported(int32_t Dk, int32_t Dv, int32_t dtype);
 
-// Workspace of the chunk path: the longest-first order of the segment slots
-// (0 when the path is not used or no ordering is done).
-size_t kda_chunk_workspace_bytes(int32_t Dk, int32_t Dv, int32_t dtype, int32_t max_segs);
+// Workspace of the chunk path (0 when the path is not used): the work plan
+// (runs, longest first) and the states and decay products of the pieces of
+// cut segments.
+size_t kda_chunk_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                                 int32_t max_segs);
 
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,

@@ -62,6 +62,15 @@ constexpr int kTailBlocks = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
+// Work plan (built on the device by kda_plan_kernel; see there).
+constexpr int kPlanThreads = 1024;
+constexpr int kHistBins = 2048;   // run-length bins of the longest-first order
+constexpr int kMinRun = 32;       // chunks: no run is cut shorter, no shorter segment is cut
+constexpr int kRunDiv = 4;        // cut runs are at most 1/kRunDiv of the per-CU share
+constexpr int kMaxRuns = 16;      // runs per segment
+constexpr int kShareCUs = 256;    // compute units the per-CU share is counted over
+constexpr int kPlanHeader = 64;   // int32 words before the run table
+
 // A blocks (row sub-chunk w, column sub-chunk j), j <= w, in this order; the
 // query version of block b lives in LDS slot b. Jobs 10 and 11 zero the blocks
 // (0, 1) and (2, 3), which the A.V product reads through its 32-wide steps.
@@ -231,12 +240,18 @@ __device__ __forceinline__ void wload(uint32_t (&w)[n], __amdgpu_buffer_rsrc_t r
   }
 }
 
-template <int DK, int DV>
+// kState = false: the forward pass of one run (a whole segment, or a piece of
+// a long one that starts from the state composed of the earlier pieces'
+// results). kState = true: the state pass of a run that is not its segment's
+// last: S from zero over the run and the product of its decays, both to the
+// workspace (no outputs).
+template <int DK, int DV, bool kState>
 __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ order, int32_t max_segs, int64_t N, int32_t H, float scale,
-    bf16* __restrict__ o, float* __restrict__ final_state, int32_t* __restrict__ flags,
+    const int32_t* __restrict__ plan, int32_t runs_max, int32_t max_segs, int64_t N,
+    int32_t H, float scale, bf16* __restrict__ o, float* __restrict__ final_state,
+    int32_t* __restrict__ flags, float* __restrict__ run_states, float* __restrict__ run_decays,
     int32_t lds_zero) {
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
@@ -264,35 +279,61 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = w < NP;
-  const int64_t seg_blocks = int64_t(max_segs) * H;
 
-  if (int64_t(blockIdx.x) >= seg_blocks) {
-    // Positions not covered by any segment get o = 0.
+  // Work-group blockIdx / H takes the run of that rank in the plan (longest
+  // first, so the longest chains start early and the launch ends on short
+  // ones); head h = blockIdx % H. In the forward pass, blocks past the
+  // runs_max * H run blocks zero the outputs of positions outside every
+  // segment.
+  const int64_t run_blocks = int64_t(runs_max) * H;
+  if (!kState && int64_t(blockIdx.x) >= run_blocks) {
     int64_t cu_last = cu ? int64_t(cu[max_segs]) : N;
     cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
     const int64_t total = (N - cu_last) * H * DV;
     const int64_t base = cu_last * H * DV;
-    for (int64_t i = (int64_t(blockIdx.x) - seg_blocks) * NT + tid; i < total;
+    for (int64_t i = (int64_t(blockIdx.x) - run_blocks) * NT + tid; i < total;
          i += int64_t(kTailBlocks) * NT)
       o[base + i] = from_f32<bf16>(0.f);
     return;
   }
-
-  // Work-groups take (segment, head) pairs longest segment first when an
-  // order is given, so the longest chains start early and the tail of the
-  // launch holds the short ones.
   const int rank = int(blockIdx.x / H);
-  const int slot = order != nullptr ? order[rank] : rank;
   const int h = int(blockIdx.x % H);
+  int slot, c0, c1, run_idx = 0, sbase;
+  bool last = false;
+  if constexpr (kState) {
+    if (rank >= plan[1]) return;
+    const int32_t* e = plan + kPlanHeader + 8 * runs_max + 4 * rank;
+    slot = e[0];
+    c0 = e[1];
+    c1 = e[2];
+    sbase = e[3];  // the state slot this run writes
+  } else {
+    if (rank >= plan[0]) return;
+    const int32_t* e = plan + kPlanHeader + 8 * rank;
+    slot = e[0];
+    c0 = e[1];
+    c1 = e[2];
+    run_idx = e[3];  // runs of the segment before this one
+    sbase = e[4];    // their state slots: sbase .. sbase + run_idx - 1
+    last = e[5] != 0;
+  }
   int64_t start = 0, end = N;
   if (cu != nullptr) {
     start = cu[slot];
     end = cu[slot + 1];
     const bool bad = start < 0 || end < start || end > N || (slot == 0 && start != 0);
     if (bad) {
-      if (tid == 0 && flags != nullptr) atomicOr(flags, kFlagBadCuSeqlens);
+      if (!kState && tid == 0 && flags != nullptr) atomicOr(flags, kFlagBadCuSeqlens);
       return;
     }
+  }
+  // the run: chunks [c0, c1) of the segment, which are aligned to its start
+  {
+    const int64_t seg_start = start;
+    start = seg_start + int64_t(c0) * kC;
+    const int64_t run_end = seg_start + int64_t(c1) * kC;
+    end = end < run_end ? end : run_end;
+    if (end < start) end = start;
   }
   const int nchunks = int((end - start + kC - 1) / kC);
   const uint32_t rowK = uint32_t(H) * DK * 2;  // bytes between tokens (q, k, g)
@@ -360,7 +401,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t t = uint32_t(tok0 + i);
-      wload(R.q[i], rq, t * rowK + ch0 * 2);
+      if constexpr (!kState) wload(R.q[i], rq, t * rowK + ch0 * 2);
       wload(R.k[i], rk, t * rowK + ch0 * 2);
     }
   };
@@ -472,8 +513,46 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     }
   };
 
+  // State pass: only Kbar and the decay.
+  auto produce_kb_sw = [&](auto swc, const RawQK<PCPL>& R, const float (&cs)[4][PCPL],
+                           bf16* s_kb, float* s_dec, const float* s_bet) {
+    constexpr int sw = decltype(swc)::value;
+    float Tw[PCPL], f1[PCPL], dec[PCPL];
+#pragma unroll
+    for (int c = 0; c < PCPL; ++c) {
+      const f32x4 Tj = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c) * 4);
+      const float after = sw == 3 ? 0.f : sw == 2 ? Tj[3] : sw == 1 ? Tj[2] + Tj[3] : Tj[1] + (Tj[2] + Tj[3]);
+      Tw[c] = Tj[sw];
+      f1[c] = ex2(after);
+      dec[c] = ex2((Tj[0] + Tj[1]) + (Tj[2] + Tj[3]));
+    }
+    if (sw == 0 && tq == 0) {
+#pragma unroll
+      for (int c = 0; c < PCPL; c += 4)
+        *reinterpret_cast<f32x4*>(s_dec + ch0 + c) = f32x4{dec[c], dec[c + 1], dec[c + 2], dec[c + 3]};
+    }
+    const f32x4 bt4 = *reinterpret_cast<const f32x4*>(s_bet + tok0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float kb[PCPL];
+#pragma unroll
+      for (int c = 0; c < PCPL; ++c)
+        kb[c] = bf(R.k[i], c) * ex2(Tw[c] - cs[i][c]) * (bt4[i] * f1[c]);
+      stn<PCPL>(s_kb + (tok0 + i) * RP + ch0, kb);
+    }
+  };
+
   auto produce_a = [&](const RawQK<PCPL>& R, const float (&cs)[4][PCPL], bf16* s_qh,
                        bf16* s_kb, float* s_dec, const float* s_bet) {
+    if constexpr (kState) {
+      switch (sw) {
+        case 0: produce_kb_sw(IntC<0>{}, R, cs, s_kb, s_dec, s_bet); break;
+        case 1: produce_kb_sw(IntC<1>{}, R, cs, s_kb, s_dec, s_bet); break;
+        case 2: produce_kb_sw(IntC<2>{}, R, cs, s_kb, s_dec, s_bet); break;
+        default: produce_kb_sw(IntC<3>{}, R, cs, s_kb, s_dec, s_bet); break;
+      }
+      return;
+    }
     switch (sw) {
       case 0: produce_a_sw(IntC<0>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
       case 1: produce_a_sw(IntC<1>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
@@ -527,20 +606,50 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   // ---- consumer, first half of step c+1: o of chunk c = acc + V^T A^T
   // (contraction over tokens in steps of 32; causal: the second step only
   // for rows >= 32), scaled and stored; then S = diag(2^{b_C}) S + Kbar^T V.
+  // Operands whose contraction runs over the tokens 32 m2 + 8 gq + 0..7 of
+  // the chunk, read transposed from token-major tiles: lane lr gets column
+  // c0(lr / 4 ...) as set by the supplying lanes (see tr4).
+  const int trow = 8 * gq + (lr >> 2);  // token supplied by this lane, + 32 m2 (+ 4)
+  auto vT_op = [&](int m2, int et) {    // V^T rows e0 + ecol(et, lr)
+    const bf16* p = s_v + (32 * m2 + trow) * VP + e0 + 4 * ET * (lr & 3) + 4 * et;
+    return join_tr(tr4(p), tr4(p + 4 * VP));
+  };
+  auto kbT_op = [&](const bf16* s_kb, int m2, int dt) {  // Kbar^T rows 16 dt + lr
+    const bf16* p = s_kb + (32 * m2 + trow) * RP + 16 * dt + 4 * (lr & 3);
+    return join_tr(tr4(p), tr4(p + 4 * RP));
+  };
+  // S = diag(2^{b_C}) S + Kbar^T V (the decay also multiplies into Dacc when
+  // given: the state pass keeps the run's product of decays).
+  auto state_update = [&](f32x4 (&S)[DT][ET], f32x4* Dacc, const bf16* s_kb, const float* s_dec) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(s_dec + 16 * dt + 4 * gq);
+      if (Dacc != nullptr) Dacc[dt] *= dec;
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[dt][et][i] *= dec[i];
+    }
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      bf16x8 vb[ET];
+#pragma unroll
+      for (int et = 0; et < ET; ++et) vb[et] = vT_op(m2, et);
+#pragma unroll
+      for (int d0 = 0; d0 < DT; d0 += 4) {
+        bf16x8 kb[4];
+#pragma unroll
+        for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt) kb[dt] = kbT_op(s_kb, m2, d0 + dt);
+#pragma unroll
+        for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt)
+#pragma unroll
+          for (int et = 0; et < ET; ++et) S[d0 + dt][et] = mfma(kb[dt], vb[et], S[d0 + dt][et]);
+      }
+    }
+  };
+
   auto consume_finish = [&](f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET], uint32_t (&opk)[4][2 * ET],
                             const bf16* s_kb, const float* s_dec) {
-    // Operands whose contraction runs over the tokens 32 m2 + 8 gq + 0..7 of
-    // the chunk, read transposed from token-major tiles: lane lr gets column
-    // c0(lr / 4 ...) as set by the supplying lanes (see tr4).
-    const int trow = 8 * gq + (lr >> 2);  // token supplied by this lane, + 32 m2 (+ 4)
-    auto vT_op = [&](int m2, int et) {    // V^T rows e0 + ecol(et, lr)
-      const bf16* p = s_v + (32 * m2 + trow) * VP + e0 + 4 * ET * (lr & 3) + 4 * et;
-      return join_tr(tr4(p), tr4(p + 4 * VP));
-    };
-    auto kbT_op = [&](int m2, int dt) {   // Kbar^T rows 16 dt + lr
-      const bf16* p = s_kb + (32 * m2 + trow) * RP + 16 * dt + 4 * (lr & 3);
-      return join_tr(tr4(p), tr4(p + 4 * RP));
-    };
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
       bf16x8 va[ET], aa[4];
@@ -564,30 +673,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         opk[t][2 * et] = pk2(x[0] * scale, x[1] * scale);
         opk[t][2 * et + 1] = pk2(x[2] * scale, x[3] * scale);
       }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f32x4 dec = *reinterpret_cast<const f32x4*>(s_dec + 16 * dt + 4 * gq);
-#pragma unroll
-      for (int et = 0; et < ET; ++et)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[dt][et][i] *= dec[i];
-    }
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      bf16x8 vb[ET];
-#pragma unroll
-      for (int et = 0; et < ET; ++et) vb[et] = vT_op(m2, et);
-#pragma unroll
-      for (int d0 = 0; d0 < DT; d0 += 4) {
-        bf16x8 kb[4];
-#pragma unroll
-        for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt) kb[dt] = kbT_op(m2, d0 + dt);
-#pragma unroll
-        for (int dt = 0; dt < 4 && d0 + dt < DT; ++dt)
-#pragma unroll
-          for (int et = 0; et < ET; ++et) S[d0 + dt][et] = mfma(kb[dt], vb[et], S[d0 + dt][et]);
-      }
-    }
+    state_update(S, nullptr, s_kb, s_dec);
   };
 
   // ---- consumer, second half of step c+1: the outputs of chunk c packed in
@@ -668,7 +754,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
       if (s < nchunks) produce_a(QA, cs, s_qh, s_kb0, s_decay, s_beta);
       if (beta_wave) bnext2 = load_beta(s + 2);
       __syncthreads();
-      if (s < nchunks) a_blocks(s_beta);
+      if (!kState && s < nchunks) a_blocks(s_beta);
       if (s < nchunks) produce_b(R.v);
       load_v(R, s + 1);
       if (beta_wave) s_beta[kC + lane] = __uint_as_float(bnext << 16);
@@ -680,7 +766,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
       if (s + 1 < nchunks) produce_a(QB, cs, s_qh, s_kb1, s_decay + DK, s_beta + kC);
       if (beta_wave) bnext = load_beta(s + 3);
       __syncthreads();
-      if (s + 1 < nchunks) a_blocks(s_beta + kC);
+      if (!kState && s + 1 < nchunks) a_blocks(s_beta + kC);
       if (s + 1 < nchunks) produce_b(R.v);
       load_v(R, s + 2);
       if (beta_wave) s_beta[lane] = __uint_as_float(bnext2 << 16);
@@ -689,96 +775,307 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
       __syncthreads();
     }
   } else {
+    // Run states and decays in the workspace: slot j, head h holds S as the
+    // consumers keep it (consumer ci, tile (dt, et), lane: one f32x4 each)
+    // and 2^{sum of the run's log2 gates} per key channel.
+    auto state_at = [&](int j, int dt, int et) {
+      return reinterpret_cast<f32x4*>(run_states) +
+             (((int64_t(j) * H + h) * 4 + ci) * DT * ET + dt * ET + et) * 64 + lane;
+    };
+    auto decay_at = [&](int j, int dt) {
+      return reinterpret_cast<f32x4*>(run_decays + (int64_t(j) * H + h) * DK + 16 * dt + 4 * gq);
+    };
     f32x4 S[DT][ET];  // state rows [0, DK), columns [e0, e0 + EW)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int et = 0; et < ET; ++et) S[dt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 acc[4][ET];  // o^T of the chunk in flight, between its two halves
-    uint32_t opk[4][2 * ET];  // packed outputs of the chunk finished in this step
-    __syncthreads();  // the producers' first scan
-    for (int s = 0; s <= nchunks; s += 2) {
-      if (s >= 1) consume_finish(S, acc, opk, s_kb1, s_decay + DK);
-      __syncthreads();
-      if (s >= 1) store_out(opk, s - 1);
-      if (s < nchunks) {
-        a_blocks(s_beta);
-        consume_inter(S, acc);
+    if constexpr (kState) {
+      f32x4 Dacc[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) Dacc[dt] = f32x4{1.f, 1.f, 1.f, 1.f};
+      __syncthreads();  // the producers' first scan
+      for (int s = 0; s <= nchunks; s += 2) {
+        if (s >= 1) state_update(S, Dacc, s_kb1, s_decay + DK);
+        __syncthreads();
+        __syncthreads();
+        if (s + 1 > nchunks) break;
+        state_update(S, Dacc, s_kb0, s_decay);
+        __syncthreads();
+        __syncthreads();
       }
-      __syncthreads();
-      if (s + 1 > nchunks) break;
-      consume_finish(S, acc, opk, s_kb0, s_decay);
-      __syncthreads();
-      store_out(opk, s);
-      if (s + 1 < nchunks) {
-        a_blocks(s_beta + kC);
-        consume_inter(S, acc);
-      }
-      __syncthreads();
-    }
-    if (final_state != nullptr) {
-      float* fs = final_state + (int64_t(slot) * H + h) * DK * DV;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int et = 0; et < ET; ++et)
+        for (int et = 0; et < ET; ++et) *state_at(sbase, dt, et) = S[dt][et];
+      if (ci == 0 && lr == 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + ecol(et, lr)] = S[dt][et][i];
+        for (int dt = 0; dt < DT; ++dt) *decay_at(sbase, dt) = Dacc[dt];
+      }
+    } else {
+      // A piece of a cut segment starts from the state of the pieces before
+      // it: S = D_j S + L_j over them in order (D_j, L_j: piece j's decay
+      // product and its state from zero).
+      for (int j = 0; j < run_idx; ++j) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4 d = *decay_at(sbase + j, dt);
+#pragma unroll
+          for (int et = 0; et < ET; ++et) S[dt][et] = S[dt][et] * d + *state_at(sbase + j, dt, et);
+        }
+      }
+      f32x4 acc[4][ET];  // o^T of the chunk in flight, between its two halves
+      uint32_t opk[4][2 * ET];  // packed outputs of the chunk finished in this step
+      __syncthreads();  // the producers' first scan
+      for (int s = 0; s <= nchunks; s += 2) {
+        if (s >= 1) consume_finish(S, acc, opk, s_kb1, s_decay + DK);
+        __syncthreads();
+        if (s >= 1) store_out(opk, s - 1);
+        if (s < nchunks) {
+          a_blocks(s_beta);
+          consume_inter(S, acc);
+        }
+        __syncthreads();
+        if (s + 1 > nchunks) break;
+        consume_finish(S, acc, opk, s_kb0, s_decay);
+        __syncthreads();
+        store_out(opk, s);
+        if (s + 1 < nchunks) {
+          a_blocks(s_beta + kC);
+          consume_inter(S, acc);
+        }
+        __syncthreads();
+      }
+      if (final_state != nullptr && last) {
+        float* fs = final_state + (int64_t(slot) * H + h) * DK * DV;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int et = 0; et < ET; ++et)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + ecol(et, lr)] = S[dt][et][i];
+      }
     }
   }
 }
 
-// Segment slots sorted by chunk count, longest first (ties: lower slot first):
-// order[rank] = slot. One work-group; each thread ranks its slots against all
-// others (chunk counts staged in LDS, read as broadcasts).
-constexpr int kOrderThreads = 1024;
-constexpr int kOrderMaxSegs = 2048;
+// ---------------------------------------------------------------- work plan
+// One work-group builds the launch's work list from cu_seqlens:
+// 1. the chunk total over the well-formed segments gives the per-CU share
+//    avg = ceil(total H / kShareCUs) in chunk steps;
+// 2. a segment longer than max(avg, kMinRun) chunks is cut into m nearly equal
+//    runs of at most max(kMinRun, ceil(avg / kRunDiv)) chunks (m <= kMaxRuns);
+//    every other segment, empty ones included, is one run;
+// 3. runs are ranked longest first through a histogram of run lengths (ties in
+//    any order: results do not depend on the order), and so are the runs that
+//    are not last in their segment, which the state pass takes.
+// The state slots of a segment's first m - 1 runs are consecutive from sbase
+// (exclusive prefix of m - 1 over the segments, computed tile by tile).
+__device__ __forceinline__ int plan_runs(int64_t n, int64_t thr, int64_t R) {
+  if (n <= thr) return 1;
+  const int64_t Ri = R > (n + kMaxRuns - 1) / kMaxRuns ? R : (n + kMaxRuns - 1) / kMaxRuns;
+  return int((n + Ri - 1) / Ri);
+}
+// chunks of run j of a segment of n chunks cut into m runs
+__device__ __forceinline__ int run_len(int64_t n, int m, int j) {
+  return int((n * (j + 1)) / m - (n * j) / m);
+}
+__device__ __forceinline__ int len_bin(int len) { return len < kHistBins - 1 ? len : kHistBins - 1; }
 
-__global__ __launch_bounds__(kOrderThreads) void kda_order_kernel(const int32_t* __restrict__ cu,
-                                                                  int32_t max_segs,
-                                                                  int32_t* __restrict__ order) {
-  __shared__ int32_t s_nch[kOrderMaxSegs];
-  for (int i = threadIdx.x; i < max_segs; i += kOrderThreads) {
-    const int64_t len = int64_t(cu[i + 1]) - int64_t(cu[i]);  // malformed: flagged by the main kernel
-    s_nch[i] = len > 0 ? int32_t((len + kC - 1) / kC) : 0;
+// Exclusive prefix over the work-group (kPlanThreads threads); *total gets the sum.
+__device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) s_tmp[wv] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int i = 0; i < kPlanThreads / 64; ++i) {
+    const int t = s_tmp[i];
+    before += i < wv ? t : 0;
+    all += t;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < max_segs; i += kOrderThreads) {
-    const int mine = s_nch[i];
-    int rank = 0;
-    for (int j = 0; j < max_segs; ++j) {
-      const int other = s_nch[j];
-      rank += (other > mine) || (other == mine && j < i);
+  *total = all;
+  return before + inc - x;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* __restrict__ cu,
+                                                                int32_t max_segs, int64_t N,
+                                                                int32_t H, int32_t states_max,
+                                                                int32_t runs_max,
+                                                                int32_t* __restrict__ plan) {
+  __shared__ int s_hr[kHistBins];  // main runs per length bin, then next free rank
+  __shared__ int s_hs[kHistBins];  // state runs likewise
+  __shared__ int s_tmp[kPlanThreads / 64];
+  __shared__ unsigned long long s_total;
+  const int tid = threadIdx.x;
+  const int64_t states_word_off = kPlanHeader + 8 * int64_t(runs_max);
+  for (int i = tid; i < kHistBins; i += kPlanThreads) s_hr[i] = s_hs[i] = 0;
+  if (tid == 0) s_total = 0;
+  __syncthreads();
+  // chunks of segment i (malformed ones count 0: the main kernel flags them)
+  auto chunks = [&](int i) -> int64_t {
+    if (cu == nullptr) return (N + kC - 1) / kC;
+    const int64_t a = cu[i], e = cu[i + 1];
+    const bool bad = a < 0 || e < a || e > N || (i == 0 && a != 0);
+    return bad ? 0 : (e - a + kC - 1) / kC;
+  };
+  unsigned long long mine = 0;
+  for (int i = tid; i < max_segs; i += kPlanThreads) mine += uint64_t(chunks(i));
+  atomicAdd(&s_total, mine);
+  __syncthreads();
+  const int64_t total = int64_t(s_total);
+  const int64_t avg = (total * H + kShareCUs - 1) / kShareCUs;
+  const int64_t thr = avg > kMinRun ? avg : kMinRun;
+  const int64_t R = (avg + kRunDiv - 1) / kRunDiv > kMinRun ? (avg + kRunDiv - 1) / kRunDiv : kMinRun;
+
+  // Runs of each segment, with the state-slot budget enforced in slot order:
+  // a segment whose extra runs would not fit stays whole (only on malformed
+  // input; the workspace bound covers every well-formed one).
+  auto pass = [&](auto&& body) {
+    int carry = 0;
+    for (int base = 0; base < max_segs; base += kPlanThreads) {
+      const int i = base + tid;
+      const int64_t n = i < max_segs ? chunks(i) : 0;
+      int m = i < max_segs ? plan_runs(n, thr, R) : 0;
+      int tile_total;
+      int sb = carry + block_exclusive_scan(m > 0 ? m - 1 : 0, s_tmp, &tile_total);
+      if (m > 1 && sb + m - 1 > states_max) m = 1;
+      // a clamped segment's slots stay unused; later segments keep theirs
+      if (i < max_segs) body(i, n, m, sb);
+      carry = carry + tile_total < (1 << 29) ? carry + tile_total : (1 << 29);
     }
-    order[rank] = i;
+  };
+  pass([&](int, int64_t n, int m, int) {
+    for (int j = 0; j < m; ++j) {
+      const int b = len_bin(run_len(n, m, j));
+      atomicAdd(&s_hr[b], 1);
+      if (j + 1 < m) atomicAdd(&s_hs[b], 1);
+    }
+  });
+  __syncthreads();
+  // bins to first ranks, longest first (suffix sums), one thread per bin group
+  constexpr int kPer = kHistBins / kPlanThreads;
+  int cr[kPer], cs[kPer], sr = 0, ss = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int b = kHistBins - 1 - (tid * kPer + u);
+    cr[u] = s_hr[b];
+    cs[u] = s_hs[b];
+    sr += cr[u];
+    ss += cs[u];
   }
+  int tr, ts;
+  int er = block_exclusive_scan(sr, s_tmp, &tr);
+  int es = block_exclusive_scan(ss, s_tmp, &ts);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int b = kHistBins - 1 - (tid * kPer + u);
+    s_hr[b] = er;
+    s_hs[b] = es;
+    er += cr[u];
+    es += cs[u];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    plan[0] = tr;  // runs
+    plan[1] = ts;  // state runs
+  }
+  pass([&](int i, int64_t n, int m, int sb) {
+    int c0 = 0;
+    for (int j = 0; j < m; ++j) {
+      const int len = run_len(n, m, j);
+      const int b = len_bin(len);
+      const int rank = atomicAdd(&s_hr[b], 1);
+      int32_t* e = plan + kPlanHeader + 8 * rank;
+      e[0] = i;
+      e[1] = c0;
+      e[2] = c0 + len;
+      e[3] = j;
+      e[4] = sb;
+      e[5] = j + 1 == m;
+      if (j + 1 < m) {
+        const int sr2 = atomicAdd(&s_hs[b], 1);
+        int32_t* f = plan + states_word_off + 4 * sr2;
+        f[0] = i;
+        f[1] = c0;
+        f[2] = c0 + len;
+        f[3] = sb + j;
+      }
+      c0 += len;
+    }
+  });
+}
+
+struct PlanLayout {
+  int64_t runs_max, states_max;
+  size_t states_word_off;  // int32 words from the workspace start
+  size_t off_L, off_D, bytes;
+};
+
+PlanLayout plan_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs) {
+  PlanLayout p;
+  const int64_t chunk_ub = (N + int64_t(kC - 1) * max_segs) / kC;
+  const int64_t by_min = chunk_ub / kMinRun;
+  const int64_t by_share = int64_t(kShareCUs) * kRunDiv / H;
+  p.states_max = by_min < by_share ? by_min : by_share;
+  p.runs_max = int64_t(max_segs) + p.states_max;
+  p.states_word_off = size_t(kPlanHeader) + 8 * size_t(p.runs_max);
+  const size_t table = (p.states_word_off + 4 * size_t(p.states_max)) * 4;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.off_L = up(table);
+  p.off_D = p.off_L + up(size_t(p.states_max) * H * Dk * Dv * 4);
+  p.bytes = p.off_D + up(size_t(p.states_max) * H * Dk * 4);
+  return p;
 }
 
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                        int32_t H, float scale, void* o, float* fs, int32_t* flags,
-                       int32_t* order, hipStream_t s) {
+                       char* ws, hipStream_t s) {
   using C = Cfg<DK, DV>;
+  constexpr int state_bytes = C::off_qh;  // the state pass uses the small tables, V and Kbar
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::bytes);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, state_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  if (order != nullptr) {
-    hipLaunchKernelGGL(kda_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, cu, max_segs, order);
-    const hipError_t e = hipGetLastError();
+  const PlanLayout L = plan_layout(N, H, DK, DV, max_segs);
+  int32_t* plan = reinterpret_cast<int32_t*>(ws);
+  float* states = reinterpret_cast<float*>(ws + L.off_L);
+  float* decays = reinterpret_cast<float*>(ws + L.off_D);
+  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, max_segs, N, H,
+                     int32_t(L.states_max), int32_t(L.runs_max), plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const auto qp = static_cast<const bf16*>(q), kp = static_cast<const bf16*>(k);
+  const auto vp = static_cast<const bf16*>(v), gp = static_cast<const bf16*>(g);
+  const auto bp = static_cast<const bf16*>(beta);
+  if (L.states_max > 0) {
+    hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true>), dim3(unsigned(L.states_max * H)),
+                       dim3(C::NT), state_bytes, s, qp, kp, vp, gp, bp, cu, plan,
+                       int32_t(L.runs_max), max_segs, N, H, scale,
+                       static_cast<bf16*>(nullptr), static_cast<float*>(nullptr),
+                       static_cast<int32_t*>(nullptr), states, decays, 0);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t blocks = int64_t(max_segs) * H + kTailBlocks;
-  hipLaunchKernelGGL((kda_chunk_kernel<DK, DV>), dim3(unsigned(blocks)), dim3(C::NT), C::bytes, s,
-                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(g),
-                     static_cast<const bf16*>(beta), cu, order, max_segs, N, H, scale,
-                     static_cast<bf16*>(o), fs, flags, 0);
+  const int64_t blocks = L.runs_max * H + kTailBlocks;
+  hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false>), dim3(unsigned(blocks)), dim3(C::NT), C::bytes,
+                     s, qp, kp, vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H,
+                     scale, static_cast<bf16*>(o), fs, flags, states, decays, 0);
   return hipGetLastError();
 }
 
@@ -788,9 +1085,10 @@ bool kda_chunk_supported(int32_t Dk, int32_t Dv, int32_t dtype) {
   return dtype == 0 && (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
 }
 
-size_t kda_chunk_workspace_bytes(int32_t Dk, int32_t Dv, int32_t dtype, int32_t max_segs) {
-  if (!kda_chunk_supported(Dk, Dv, dtype) || max_segs < 2 || max_segs > kOrderMaxSegs) return 0;
-  return (size_t(max_segs) * 4 + 255) / 256 * 256;
+size_t kda_chunk_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                                 int32_t max_segs) {
+  if (!kda_chunk_supported(Dk, Dv, dtype) || N < 1 || H < 1 || max_segs < 1) return 0;
+  return plan_layout(N, H, Dk, Dv, max_segs).bytes;
 }
 
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
@@ -798,16 +1096,15 @@ hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const v
                             int32_t H, int32_t Dk, int32_t Dv, float scale, void* o,
                             float* final_state, int32_t* flags, void* workspace,
                             hipStream_t stream) {
-  int32_t* order = (cu != nullptr && kda_chunk_workspace_bytes(Dk, Dv, 0, max_segs) > 0)
-                       ? static_cast<int32_t*>(workspace) : nullptr;
+  char* ws = static_cast<char*>(workspace);
   if (Dk == 128 && Dv == 128)
-    return launch_dims<128, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, order, stream);
+    return launch_dims<128, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, ws, stream);
   if (Dk == 64 && Dv == 64)
-    return launch_dims<64, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, order, stream);
+    return launch_dims<64, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, ws, stream);
   if (Dk == 128 && Dv == 64)
-    return launch_dims<128, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, order, stream);
+    return launch_dims<128, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, ws, stream);
   if (Dk == 64 && Dv == 128)
-    return launch_dims<64, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, order, stream);
+    return launch_dims<64, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, ws, stream);
   return hipErrorInvalidValue;
 }
 

@@ -212,10 +212,11 @@ def test_bad_cu_seqlens_sets_flag():
 
 
 @pytest.mark.parametrize("n_slots", [37, 2100])
-def test_slot_order_ties_phantoms_and_unordered_path(n_slots):
-    """Longest-first processing order (up to 2048 slots) and the plain slot
-    order above it give the oracle's per-segment results: lengths with ties,
-    empty slots between real ones, and phantom slots at the end."""
+def test_slot_order_ties_phantoms(n_slots):
+    """The longest-first processing order gives the oracle's per-segment
+    results: lengths with ties, empty slots between real ones, and phantom
+    slots at the end (37 slots, and 2100, more than the plan's 2048 length
+    bins and two tiles of its slot scan)."""
     pkv = _pkv()
     rng = np.random.default_rng(n_slots)
     H, D = 2, 64
@@ -239,3 +240,62 @@ def test_slot_order_ties_phantoms_and_unordered_path(n_slots):
         else:
             assert torch.count_nonzero(fs[i]).item() == 0
     assert torch.count_nonzero(o[0, cu[-1]:]).item() == 0
+
+
+# Segments longer than max(per-CU share, 32 chunks) are cut into up to 16
+# nearly equal runs (each run's chunks [n j / m, n (j + 1) / m)); a run starts
+# from the state composed of the earlier runs' states and decay products.
+# Slow gates keep that carried state large, so a wrong composition shows.
+@pytest.mark.parametrize("case,H,Dk,Dv,lens,slots,runs,pieces", [
+    # 79 chunks, share 1 -> cut at 32: 3 runs
+    ("one_segment", 2, 64, 64, [5000], None, 3, 2),
+    # 47, 2, 0, 65, 33, 32, 1 chunks: 47 -> 2 runs, 65 -> 3, 33 -> 2, 32 stays whole
+    ("mixed", 2, 128, 128, [3000, 100, 0, 4100, 2112, 2048, 1], 10, 14, 4),
+    # 600 chunks: runs of at least ceil(600 / 16) = 38 -> the 16-run cap
+    ("sixteen_runs", 1, 128, 64, [64 * 600 - 17], 2, 17, 15),
+])
+def test_long_segments_cut_into_runs(case, H, Dk, Dv, lens, slots, runs, pieces):
+    pkv = _pkv()
+    rng = np.random.default_rng(len(case))
+    if slots is None:
+        cu = None
+        N = lens[0]
+    else:
+        real = np.concatenate([[0], np.cumsum(lens)])
+        cu = np.concatenate([real, [real[-1]] * (slots + 1 - len(real))])
+        N = int(real[-1]) + 3
+    q = rng.standard_normal((N, H, Dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((N, H, Dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((N, H, Dv))
+    g = -rng.uniform(0.0001, 0.003, (N, H, Dk))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((N, H))))
+    ts = [torch.from_numpy(a).to(torch.bfloat16) for a in (q, k, v, g, beta)]
+    dq, dk, dv, dg, db = [t.to(device())[None] for t in ts]
+    max_segs = 1 if cu is None else len(cu) - 1
+    ws = torch.empty(pkv.chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, torch.bfloat16),
+                     dtype=torch.uint8, device=device())
+    cud = None if cu is None else torch.from_numpy(cu.astype(np.int32)).to(device())
+    print(f"{case}: N {N} H {H} Dk {Dk} Dv {Dv} slots {max_segs} workspace {ws.numel()} bytes", flush=True)
+    o, fs = pkv.chunk_kda_varlen(dq, dk, dv, dg, db, cud, workspace=ws)
+    torch.cuda.synchronize()
+    head = ws[:8].view(torch.int32).cpu().tolist()
+    assert (head[0], head[1]) == (runs, pieces)
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], cu)
+    go = f64(o[0])
+    check_close(go, ro, "bf16", "o")
+    check_close(f64(fs), rfs, "bf16", "final states")
+    bounds = np.array([0, N]) if cu is None else cu
+    for i in range(len(bounds) - 1):
+        a, e = int(bounds[i]), int(bounds[i + 1])
+        n = (e - a + 63) // 64
+        if n <= 32:
+            continue
+        m = -(-n // max(32, -(-n // 16)))
+        for j in range(m):
+            ra, re = a + 64 * (n * j // m), min(e, a + 64 * (n * (j + 1) // m))
+            check_close(go[ra:re], ro[ra:re], "bf16", f"segment {i} run {j}")
+        # the carried state matters: the last run alone from zero is far off
+        alone, _ = oracle.chunk_kda_varlen(*[f64(t)[ra:re] for t in ts], None)
+        assert np.linalg.norm(alone - ro[ra:re]) > 0.2 * np.linalg.norm(ro[ra:re])
+    if cu is not None:
+        assert torch.count_nonzero(o[0, int(cu[-1]):]).item() == 0
