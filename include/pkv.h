@@ -140,6 +140,8 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
  *             max_segs is taken as 1. Expected: cu[0] = 0, non-decreasing,
  *             cu[max_segs] <= N; a violation sets PKV_FLAG_BAD_CU_SEQLENS.
  * o           [1, N, H, Dv] in `dtype`; must not overlap the inputs.
+ *             q, k, v, g, o and final_state must be 16-byte aligned, beta
+ *             aligned to its element size.
  * final_state float32 [max_segs, H, Dk, Dv] or NULL (not written).
  * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in.
  * workspace   device buffer of at least pkv_chunk_kda_varlen_workspace_size()
@@ -152,8 +154,8 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
  * 16 * max|g| beyond ~60 within a segment may lose accuracy (the chunked
  * factorisation bounds exponents per 16-token sub-chunk).
  * Errors: PKV_ERR_INVALID_ARGUMENT for NULL tensors, N < 1, N > INT32_MAX,
- * H < 1, max_segs < 1 (with cu_seqlens), max_segs * H > 2^22 or o aliasing
- * an input; PKV_ERR_UNSUPPORTED for other Dk/Dv or dtype; PKV_ERR_WORKSPACE
+ * H < 1, max_segs < 1 (with cu_seqlens), max_segs * H > 2^22, a misaligned
+ * tensor or o aliasing an input; PKV_ERR_UNSUPPORTED for other Dk/Dv or dtype; PKV_ERR_WORKSPACE
  * if the workspace is too small or not 16-byte aligned.
  */
 pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,

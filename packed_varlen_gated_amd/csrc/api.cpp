@@ -90,6 +90,11 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
   }
   if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv))
     return PKV_ERR_UNSUPPORTED;
+  for (const void* p : {q, k, v, g, static_cast<const void*>(o)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(beta) % elem_size(dtype) != 0 ||
+      reinterpret_cast<uintptr_t>(final_state) % 16 != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
   if (int64_t(max_segs) * H > (int64_t(1) << 22)) return PKV_ERR_INVALID_ARGUMENT;
   const int64_t es = elem_size(dtype);
   const int64_t o_bytes = N * H * Dv * es;

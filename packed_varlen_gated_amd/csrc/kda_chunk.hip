@@ -58,7 +58,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;
-constexpr int kTailBlocks = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
@@ -98,7 +97,8 @@ struct Cfg {
   static constexpr int VP = DV + 16;        // V: token-major rows, read transposed
   static constexpr int TP = kC + 8;         // A rows (bf16)
   // Small tables first: ds_read/ds_write immediates reach 64 KiB.
-  static constexpr int off_decay = 0;                        // float [2][DK]
+  static constexpr int off_item = 0;                         // int: next queue item
+  static constexpr int off_decay = 16;                       // float [2][DK]
   static constexpr int off_beta = off_decay + 2 * DK * 4;    // float [2][kC]
   static constexpr int off_T = off_beta + 2 * kC * 4;        // float [DK][4] sub-chunk totals
   static constexpr int off_a = off_T + DK * 4 * 4;           // A, bf16 [kC][TP]
@@ -249,9 +249,9 @@ template <int DK, int DV, bool kState>
 __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ plan, int32_t runs_max, int32_t max_segs, int64_t N,
+    int32_t* __restrict__ plan, int32_t runs_max, int32_t max_segs, int64_t N,
     int32_t H, float scale, bf16* __restrict__ o, float* __restrict__ final_state,
-    int32_t* __restrict__ flags, float* __restrict__ run_states, float* __restrict__ run_decays,
+    float* __restrict__ run_states, float* __restrict__ run_decays,
     int32_t lds_zero) {
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
@@ -280,62 +280,55 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = w < NP;
 
-  // Work-group blockIdx / H takes the run of that rank in the plan (longest
-  // first, so the longest chains start early and the launch ends on short
-  // ones); head h = blockIdx % H. In the forward pass, blocks past the
-  // runs_max * H run blocks zero the outputs of positions outside every
-  // segment.
-  const int64_t run_blocks = int64_t(runs_max) * H;
-  if (!kState && int64_t(blockIdx.x) >= run_blocks) {
-    int64_t cu_last = cu ? int64_t(cu[max_segs]) : N;
-    cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
-    const int64_t total = (N - cu_last) * H * DV;
-    const int64_t base = cu_last * H * DV;
-    for (int64_t i = (int64_t(blockIdx.x) - run_blocks) * NT + tid; i < total;
-         i += int64_t(kTailBlocks) * NT)
-      o[base + i] = from_f32<bf16>(0.f);
-    return;
-  }
-  const int rank = int(blockIdx.x / H);
-  const int h = int(blockIdx.x % H);
-  int slot, c0, c1, run_idx = 0, sbase;
+  // Persistent work-groups: each takes (run, head) items from the plan's
+  // queue, a counter the plan kernel resets, in the plan's order (longest
+  // run first, heads of a run together; item = rank * H + h). The next item
+  // is claimed when the current one starts, so the claim's latency hides
+  // behind the item's first loads.
+  int* s_item = reinterpret_cast<int*>(tile(C::off_item));
+  int32_t* const counter = plan + (kState ? 3 : 2);
+  const int n_items = (kState ? plan[1] : plan[0]) * H;
+  // Producers and consumers each loop over the same item sequence (with the
+  // same barriers), so neither role's loop keeps the other's registers live.
+  // The current item's run, set by begin_item in both loops:
+  int h = 0, slot = 0, run_idx = 0, sbase = 0, nchunks = 0;
   bool last = false;
-  if constexpr (kState) {
-    if (rank >= plan[1]) return;
-    const int32_t* e = plan + kPlanHeader + 8 * runs_max + 4 * rank;
-    slot = e[0];
-    c0 = e[1];
-    c1 = e[2];
-    sbase = e[3];  // the state slot this run writes
-  } else {
-    if (rank >= plan[0]) return;
-    const int32_t* e = plan + kPlanHeader + 8 * rank;
-    slot = e[0];
-    c0 = e[1];
-    c1 = e[2];
-    run_idx = e[3];  // runs of the segment before this one
-    sbase = e[4];    // their state slots: sbase .. sbase + run_idx - 1
-    last = e[5] != 0;
-  }
-  int64_t start = 0, end = N;
-  if (cu != nullptr) {
-    start = cu[slot];
-    end = cu[slot + 1];
-    const bool bad = start < 0 || end < start || end > N || (slot == 0 && start != 0);
-    if (bad) {
-      if (!kState && tid == 0 && flags != nullptr) atomicOr(flags, kFlagBadCuSeqlens);
-      return;
+  int64_t start = 0, end = 0;
+  auto begin_item = [&](int item) {
+    const int rank = item / H;
+    h = item % H;
+    int c0, c1;
+    if constexpr (kState) {
+      const int32_t* e = plan + kPlanHeader + 8 * runs_max + 4 * rank;
+      slot = e[0];
+      c0 = e[1];
+      c1 = e[2];
+      sbase = e[3];  // the state slot this run writes
+    } else {
+      const int32_t* e = plan + kPlanHeader + 8 * rank;
+      slot = e[0];
+      c0 = e[1];
+      c1 = e[2];
+      run_idx = e[3];  // runs of the segment before this one
+      sbase = e[4];    // their state slots: sbase .. sbase + run_idx - 1
+      last = e[5] != 0;
     }
-  }
-  // the run: chunks [c0, c1) of the segment, which are aligned to its start
-  {
-    const int64_t seg_start = start;
+    // the run: chunks [c0, c1) of the segment, which are aligned to its start
+    // (the plan holds well-formed, non-empty segments only)
+    int64_t seg_start = 0, seg_end = N;
+    if (cu != nullptr) {
+      seg_start = cu[slot];
+      seg_end = cu[slot + 1];
+    }
     start = seg_start + int64_t(c0) * kC;
     const int64_t run_end = seg_start + int64_t(c1) * kC;
-    end = end < run_end ? end : run_end;
+    end = seg_end < run_end ? seg_end : run_end;
     if (end < start) end = start;
-  }
-  const int nchunks = int((end - start + kC - 1) / kC);
+    nchunks = int((end - start + kC - 1) / kC);
+  };
+  if (tid == 0) *s_item = atomicAdd(counter, 1);
+  __syncthreads();
+  const int first_item = __builtin_amdgcn_readfirstlane(*s_item);
   const uint32_t rowK = uint32_t(H) * DK * 2;  // bytes between tokens (q, k, g)
   const uint32_t rowV = uint32_t(H) * DV * 2;
   const uint32_t rowB = uint32_t(H) * 2;
@@ -732,48 +725,57 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   // Producers and consumers run separate loops with the same barrier sequence
   // (two per step), so neither role keeps the other's registers live.
   if (producer) {
-    Raw<PCPL, PVPL> R;
-    RawQK<PCPL> QA, QB;  // q, k of even / odd chunks
-    float cs[4][PCPL];
-    const bool beta_wave = w == 0;
-    uint32_t bnext = 0, bnext2 = 0;  // raw beta of the next chunks (wave 0)
-    load_g(R, 0);
-    load_qk(QA, 0);
-    load_v(R, 0);
-    if (beta_wave) {
-      const uint32_t b0 = load_beta(0);
-      bnext = load_beta(1);
-      s_beta[lane] = __uint_as_float(b0 << 16);
-    }
-    scan(R, cs);
-    load_g(R, 1);
-    __syncthreads();
-    for (int s = 0; s <= nchunks; s += 2) {
-      // even chunk s: LDS buffers 0; odd chunk s + 1: buffers 1
-      load_qk(QB, s + 1);
-      if (s < nchunks) produce_a(QA, cs, s_qh, s_kb0, s_decay, s_beta);
-      if (beta_wave) bnext2 = load_beta(s + 2);
+    for (int item = first_item; item < n_items;) {
+      int next = 0;
+      if (tid == 0) next = atomicAdd(counter, 1);
+      begin_item(item);
+      Raw<PCPL, PVPL> R;
+      RawQK<PCPL> QA, QB;  // q, k of even / odd chunks
+      float cs[4][PCPL];
+      const bool beta_wave = w == 0;
+      uint32_t bnext = 0, bnext2 = 0;  // raw beta of the next chunks (wave 0)
+      load_g(R, 0);
+      load_qk(QA, 0);
+      load_v(R, 0);
+      if (beta_wave) {
+        const uint32_t b0 = load_beta(0);
+        bnext = load_beta(1);
+        s_beta[lane] = __uint_as_float(b0 << 16);
+      }
+      scan(R, cs);
+      load_g(R, 1);
       __syncthreads();
-      if (!kState && s < nchunks) a_blocks(s_beta);
-      if (s < nchunks) produce_b(R.v);
-      load_v(R, s + 1);
-      if (beta_wave) s_beta[kC + lane] = __uint_as_float(bnext << 16);
-      if (s + 1 < nchunks) scan(R, cs);
-      load_g(R, s + 2);
+      for (int s = 0; s <= nchunks; s += 2) {
+        // even chunk s: LDS buffers 0; odd chunk s + 1: buffers 1
+        load_qk(QB, s + 1);
+        if (s < nchunks) produce_a(QA, cs, s_qh, s_kb0, s_decay, s_beta);
+        if (beta_wave) bnext2 = load_beta(s + 2);
+        __syncthreads();
+        if (!kState && s < nchunks) a_blocks(s_beta);
+        if (s < nchunks) produce_b(R.v);
+        load_v(R, s + 1);
+        if (beta_wave) s_beta[kC + lane] = __uint_as_float(bnext << 16);
+        if (s + 1 < nchunks) scan(R, cs);
+        load_g(R, s + 2);
+        __syncthreads();
+        if (s + 1 > nchunks) break;
+        load_qk(QA, s + 2);
+        if (s + 1 < nchunks) produce_a(QB, cs, s_qh, s_kb1, s_decay + DK, s_beta + kC);
+        if (beta_wave) bnext = load_beta(s + 3);
+        __syncthreads();
+        if (!kState && s + 1 < nchunks) a_blocks(s_beta + kC);
+        if (s + 1 < nchunks) produce_b(R.v);
+        load_v(R, s + 2);
+        if (beta_wave) s_beta[lane] = __uint_as_float(bnext2 << 16);
+        if (s + 2 < nchunks) scan(R, cs);
+        load_g(R, s + 3);
+        __syncthreads();
+      }
+      // every thread has read this item's number before the item's first barrier
+      if (tid == 0) *s_item = next;
       __syncthreads();
-      if (s + 1 > nchunks) break;
-      load_qk(QA, s + 2);
-      if (s + 1 < nchunks) produce_a(QB, cs, s_qh, s_kb1, s_decay + DK, s_beta + kC);
-      if (beta_wave) bnext = load_beta(s + 3);
-      __syncthreads();
-      if (!kState && s + 1 < nchunks) a_blocks(s_beta + kC);
-      if (s + 1 < nchunks) produce_b(R.v);
-      load_v(R, s + 2);
-      if (beta_wave) s_beta[lane] = __uint_as_float(bnext2 << 16);
-      if (s + 2 < nchunks) scan(R, cs);
-      load_g(R, s + 3);
-      __syncthreads();
-    }
+      item = __builtin_amdgcn_readfirstlane(*s_item);
+    }  // item loop
   } else {
     // Run states and decays in the workspace: slot j, head h holds S as the
     // consumers keep it (consumer ci, tile (dt, et), lane: one f32x4 each)
@@ -785,76 +787,102 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     auto decay_at = [&](int j, int dt) {
       return reinterpret_cast<f32x4*>(run_decays + (int64_t(j) * H + h) * DK + 16 * dt + 4 * gq);
     };
-    f32x4 S[DT][ET];  // state rows [0, DK), columns [e0, e0 + EW)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int et = 0; et < ET; ++et) S[dt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (kState) {
-      f32x4 Dacc[DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) Dacc[dt] = f32x4{1.f, 1.f, 1.f, 1.f};
-      __syncthreads();  // the producers' first scan
-      for (int s = 0; s <= nchunks; s += 2) {
-        if (s >= 1) state_update(S, Dacc, s_kb1, s_decay + DK);
-        __syncthreads();
-        __syncthreads();
-        if (s + 1 > nchunks) break;
-        state_update(S, Dacc, s_kb0, s_decay);
-        __syncthreads();
-        __syncthreads();
-      }
+    for (int item = first_item; item < n_items;) {
+      begin_item(item);
+      f32x4 S[DT][ET];  // state rows [0, DK), columns [e0, e0 + EW)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int et = 0; et < ET; ++et) *state_at(sbase, dt, et) = S[dt][et];
-      if (ci == 0 && lr == 0) {
+        for (int et = 0; et < ET; ++et) S[dt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kState) {
+        f32x4 Dacc[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *decay_at(sbase, dt) = Dacc[dt];
-      }
-    } else {
-      // A piece of a cut segment starts from the state of the pieces before
-      // it: S = D_j S + L_j over them in order (D_j, L_j: piece j's decay
-      // product and its state from zero).
-      for (int j = 0; j < run_idx; ++j) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const f32x4 d = *decay_at(sbase + j, dt);
-#pragma unroll
-          for (int et = 0; et < ET; ++et) S[dt][et] = S[dt][et] * d + *state_at(sbase + j, dt, et);
+        for (int dt = 0; dt < DT; ++dt) Dacc[dt] = f32x4{1.f, 1.f, 1.f, 1.f};
+        __syncthreads();  // the producers' first scan
+        for (int s = 0; s <= nchunks; s += 2) {
+          if (s >= 1) state_update(S, Dacc, s_kb1, s_decay + DK);
+          __syncthreads();
+          __syncthreads();
+          if (s + 1 > nchunks) break;
+          state_update(S, Dacc, s_kb0, s_decay);
+          __syncthreads();
+          __syncthreads();
         }
-      }
-      f32x4 acc[4][ET];  // o^T of the chunk in flight, between its two halves
-      uint32_t opk[4][2 * ET];  // packed outputs of the chunk finished in this step
-      __syncthreads();  // the producers' first scan
-      for (int s = 0; s <= nchunks; s += 2) {
-        if (s >= 1) consume_finish(S, acc, opk, s_kb1, s_decay + DK);
-        __syncthreads();
-        if (s >= 1) store_out(opk, s - 1);
-        if (s < nchunks) {
-          a_blocks(s_beta);
-          consume_inter(S, acc);
-        }
-        __syncthreads();
-        if (s + 1 > nchunks) break;
-        consume_finish(S, acc, opk, s_kb0, s_decay);
-        __syncthreads();
-        store_out(opk, s);
-        if (s + 1 < nchunks) {
-          a_blocks(s_beta + kC);
-          consume_inter(S, acc);
-        }
-        __syncthreads();
-      }
-      if (final_state != nullptr && last) {
-        float* fs = final_state + (int64_t(slot) * H + h) * DK * DV;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int et = 0; et < ET; ++et)
+          for (int et = 0; et < ET; ++et) *state_at(sbase, dt, et) = S[dt][et];
+        if (ci == 0 && lr == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + ecol(et, lr)] = S[dt][et][i];
+          for (int dt = 0; dt < DT; ++dt) *decay_at(sbase, dt) = Dacc[dt];
+        }
+      } else {
+        // A piece of a cut segment starts from the state of the pieces before
+        // it: S = D_j S + L_j over them in order (D_j, L_j: piece j's decay
+        // product and its state from zero).
+        for (int j = 0; j < run_idx; ++j) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 d = *decay_at(sbase + j, dt);
+#pragma unroll
+            for (int et = 0; et < ET; ++et) S[dt][et] = S[dt][et] * d + *state_at(sbase + j, dt, et);
+          }
+        }
+        f32x4 acc[4][ET];  // o^T of the chunk in flight, between its two halves
+        uint32_t opk[4][2 * ET];  // packed outputs of the chunk finished in this step
+        __syncthreads();  // the producers' first scan
+        for (int s = 0; s <= nchunks; s += 2) {
+          if (s >= 1) consume_finish(S, acc, opk, s_kb1, s_decay + DK);
+          __syncthreads();
+          if (s >= 1) store_out(opk, s - 1);
+          if (s < nchunks) {
+            a_blocks(s_beta);
+            consume_inter(S, acc);
+          }
+          __syncthreads();
+          if (s + 1 > nchunks) break;
+          consume_finish(S, acc, opk, s_kb0, s_decay);
+          __syncthreads();
+          store_out(opk, s);
+          if (s + 1 < nchunks) {
+            a_blocks(s_beta + kC);
+            consume_inter(S, acc);
+          }
+          __syncthreads();
+        }
+        if (final_state != nullptr && last) {
+          float* fs = final_state + (int64_t(slot) * H + h) * DK * DV;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int et = 0; et < ET; ++et)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + ecol(et, lr)] = S[dt][et][i];
+        }
+      }
+      __syncthreads();
+      item = __builtin_amdgcn_readfirstlane(*s_item);
+    }  // item loop
+  }
+
+  if constexpr (!kState) {
+    // After the queue: o = 0 at positions outside every segment, and zero
+    // final states for empty (and malformed) slots; grid-strided, 16-byte stores.
+    const int64_t G = gridDim.x;
+    int64_t cu_last = cu ? int64_t(cu[max_segs]) : N;
+    cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
+    const int64_t n16 = (N - cu_last) * H * DV / 8;  // DV * 2 bytes is a multiple of 16
+    u32x4* o16 = reinterpret_cast<u32x4*>(o + cu_last * H * DV);
+    for (int64_t i = int64_t(blockIdx.x) * NT + tid; i < n16; i += G * NT) o16[i] = u32x4{0u, 0u, 0u, 0u};
+    if (final_state != nullptr && cu != nullptr) {
+      for (int64_t u = blockIdx.x; u < int64_t(max_segs) * H; u += G) {
+        const int i = int(u / H);
+        const int64_t a = cu[i], e = cu[i + 1];
+        const bool bad = a < 0 || e < a || e > N || (i == 0 && a != 0);
+        if (!bad && e > a) continue;
+        f32x4* f = reinterpret_cast<f32x4*>(final_state + u * DK * DV);
+        for (int j = tid; j < DK * DV / 4; j += NT) f[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
@@ -866,13 +894,15 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
 //    avg = ceil(total H / kShareCUs) in chunk steps;
 // 2. a segment longer than max(avg, kMinRun) chunks is cut into m nearly equal
 //    runs of at most max(kMinRun, ceil(avg / kRunDiv)) chunks (m <= kMaxRuns);
-//    every other segment, empty ones included, is one run;
+//    every other non-empty segment is one run; empty and malformed segments
+//    have none (malformed ones set PKV_FLAG_BAD_CU_SEQLENS here);
 // 3. runs are ranked longest first through a histogram of run lengths (ties in
 //    any order: results do not depend on the order), and so are the runs that
 //    are not last in their segment, which the state pass takes.
 // The state slots of a segment's first m - 1 runs are consecutive from sbase
 // (exclusive prefix of m - 1 over the segments, computed tile by tile).
 __device__ __forceinline__ int plan_runs(int64_t n, int64_t thr, int64_t R) {
+  if (n <= 0) return 0;
   if (n <= thr) return 1;
   const int64_t Ri = R > (n + kMaxRuns - 1) / kMaxRuns ? R : (n + kMaxRuns - 1) / kMaxRuns;
   return int((n + Ri - 1) / Ri);
@@ -909,7 +939,8 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
                                                                 int32_t max_segs, int64_t N,
                                                                 int32_t H, int32_t states_max,
                                                                 int32_t runs_max,
-                                                                int32_t* __restrict__ plan) {
+                                                                int32_t* __restrict__ plan,
+                                                                int32_t* __restrict__ flags) {
   __shared__ int s_hr[kHistBins];  // main runs per length bin, then next free rank
   __shared__ int s_hs[kHistBins];  // state runs likewise
   __shared__ int s_tmp[kPlanThreads / 64];
@@ -919,16 +950,24 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   for (int i = tid; i < kHistBins; i += kPlanThreads) s_hr[i] = s_hs[i] = 0;
   if (tid == 0) s_total = 0;
   __syncthreads();
-  // chunks of segment i (malformed ones count 0: the main kernel flags them)
+  // chunks of segment i (malformed ones count 0 and are flagged)
+  auto is_bad = [&](int i) {
+    if (cu == nullptr) return false;
+    const int64_t a = cu[i], e = cu[i + 1];
+    return a < 0 || e < a || e > N || (i == 0 && a != 0);
+  };
   auto chunks = [&](int i) -> int64_t {
     if (cu == nullptr) return (N + kC - 1) / kC;
-    const int64_t a = cu[i], e = cu[i + 1];
-    const bool bad = a < 0 || e < a || e > N || (i == 0 && a != 0);
-    return bad ? 0 : (e - a + kC - 1) / kC;
+    return is_bad(i) ? 0 : (int64_t(cu[i + 1]) - cu[i] + kC - 1) / kC;
   };
   unsigned long long mine = 0;
-  for (int i = tid; i < max_segs; i += kPlanThreads) mine += uint64_t(chunks(i));
+  bool any_bad = false;
+  for (int i = tid; i < max_segs; i += kPlanThreads) {
+    mine += uint64_t(chunks(i));
+    any_bad = any_bad || is_bad(i);
+  }
   atomicAdd(&s_total, mine);
+  if (any_bad && flags != nullptr) atomicOr(flags, kFlagBadCuSeqlens);
   __syncthreads();
   const int64_t total = int64_t(s_total);
   const int64_t avg = (total * H + kShareCUs - 1) / kShareCUs;
@@ -986,6 +1025,8 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   if (tid == 0) {
     plan[0] = tr;  // runs
     plan[1] = ts;  // state runs
+    plan[2] = 0;   // queue counters of the forward and state passes
+    plan[3] = 0;
   }
   pass([&](int i, int64_t n, int m, int sb) {
     int c0 = 0;
@@ -1035,6 +1076,19 @@ PlanLayout plan_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max
   return p;
 }
 
+// Compute units of the current device (the persistent grids' size).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
@@ -1057,25 +1111,24 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   float* states = reinterpret_cast<float*>(ws + L.off_L);
   float* decays = reinterpret_cast<float*>(ws + L.off_D);
   hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, max_segs, N, H,
-                     int32_t(L.states_max), int32_t(L.runs_max), plan);
+                     int32_t(L.states_max), int32_t(L.runs_max), plan, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const auto qp = static_cast<const bf16*>(q), kp = static_cast<const bf16*>(k);
   const auto vp = static_cast<const bf16*>(v), gp = static_cast<const bf16*>(g);
   const auto bp = static_cast<const bf16*>(beta);
+  // one work-group per CU: the LDS of either pass leaves room for one only
+  const unsigned grid = unsigned(device_cus());
   if (L.states_max > 0) {
-    hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true>), dim3(unsigned(L.states_max * H)),
-                       dim3(C::NT), state_bytes, s, qp, kp, vp, gp, bp, cu, plan,
-                       int32_t(L.runs_max), max_segs, N, H, scale,
-                       static_cast<bf16*>(nullptr), static_cast<float*>(nullptr),
-                       static_cast<int32_t*>(nullptr), states, decays, 0);
+    hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true>), dim3(grid), dim3(C::NT), state_bytes, s,
+                       qp, kp, vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale,
+                       static_cast<bf16*>(nullptr), static_cast<float*>(nullptr), states, decays, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t blocks = L.runs_max * H + kTailBlocks;
-  hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false>), dim3(unsigned(blocks)), dim3(C::NT), C::bytes,
-                     s, qp, kp, vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H,
-                     scale, static_cast<bf16*>(o), fs, flags, states, decays, 0);
+  hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false>), dim3(grid), dim3(C::NT), C::bytes, s, qp, kp,
+                     vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale,
+                     static_cast<bf16*>(o), fs, states, decays, 0);
   return hipGetLastError();
 }
 

@@ -86,6 +86,9 @@ def _kda_args(**kw):
     (dict(o=NUL), 1), (dict(N=0), 1), (dict(N=1 << 31), 1), (dict(H=0), 1), (dict(max_segs=0), 1),
     (dict(Dk=48), 2), (dict(Dv=256), 2), (dict(dtype=5), 2),
     (dict(o=ctypes.c_void_p(0x10000000 + 64)), 1),    # o overlaps q
+    (dict(o=ctypes.c_void_p(0x60000008)), 1),         # o not 16-byte aligned
+    (dict(k=ctypes.c_void_p(0x20000002)), 1),         # k not 16-byte aligned
+    (dict(beta=ctypes.c_void_p(0x50000001)), 1),      # beta not element-aligned
 ])
 def test_chunk_kda_validation(lib, kw, code):
     args = _kda_args(**kw)

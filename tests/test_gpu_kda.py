@@ -245,14 +245,16 @@ def test_slot_order_ties_phantoms(n_slots):
 # Segments longer than max(per-CU share, 32 chunks) are cut into up to 16
 # nearly equal runs (each run's chunks [n j / m, n (j + 1) / m)); a run starts
 # from the state composed of the earlier runs' states and decay products.
-# Slow gates keep that carried state large, so a wrong composition shows.
+# Empty slots get no run. Slow gates keep the carried state large, so a wrong
+# composition shows.
 @pytest.mark.parametrize("case,H,Dk,Dv,lens,slots,runs,pieces", [
     # 79 chunks, share 1 -> cut at 32: 3 runs
     ("one_segment", 2, 64, 64, [5000], None, 3, 2),
-    # 47, 2, 0, 65, 33, 32, 1 chunks: 47 -> 2 runs, 65 -> 3, 33 -> 2, 32 stays whole
-    ("mixed", 2, 128, 128, [3000, 100, 0, 4100, 2112, 2048, 1], 10, 14, 4),
+    # 47, 2, 0, 65, 33, 32, 1 chunks: 47 -> 2 runs, 65 -> 3, 33 -> 2, 32 stays
+    # whole, the empty slot and the 3 phantoms get none
+    ("mixed", 2, 128, 128, [3000, 100, 0, 4100, 2112, 2048, 1], 10, 10, 4),
     # 600 chunks: runs of at least ceil(600 / 16) = 38 -> the 16-run cap
-    ("sixteen_runs", 1, 128, 64, [64 * 600 - 17], 2, 17, 15),
+    ("sixteen_runs", 1, 128, 64, [64 * 600 - 17], 2, 16, 15),
 ])
 def test_long_segments_cut_into_runs(case, H, Dk, Dv, lens, slots, runs, pieces):
     pkv = _pkv()
