@@ -67,7 +67,7 @@ __device__ __forceinline__ i32x4 load4(const int32_t* __restrict__ seg, int64_t 
   return x;
 }
 
-template <bool kVec>
+template <bool kVec, bool kT4>
 __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
     const int32_t* __restrict__ seg, int64_t N, int64_t T, int32_t max_segs,
     int32_t* __restrict__ cu, int32_t* __restrict__ token_seg, int32_t* __restrict__ n_segs_out,
@@ -75,6 +75,7 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t s_bits[kTileGroups];   // boundary bits per group
   __shared__ __attribute__((aligned(16))) uint16_t s_rank[kTileGroups];  // boundaries before the group (in tile)
   __shared__ int s_wsum[kWaves];
+  __shared__ int s_edge[kGroupsPerThread * kWaves];  // last id of each wave's groups
   __shared__ int64_t s_wmax[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,48 +108,59 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
   const uint32_t step = uint32_t(4 * kThreads) % T32;
   int running = 0;  // boundaries before the tile
   for (int64_t base = 0; base < N; base += kTilePos) {
-    // A. boundary bits of each group
+    // A. boundary bits of each group. The id before group m is the last id
+    // of group m - 1: lane - 1's (a shuffle), for lane 0 the wave before's
+    // lane 63 (through LDS), for the tile's first group the previous tile's
+    // last position.
     uint32_t rp = uint32_t((base + 4 * int64_t(tid)) % T);
     i32x4 xs[kGroupsPerThread];
-    int prevs[kGroupsPerThread];
 #pragma unroll
     for (int j = 0; j < kGroupsPerThread; ++j) {
       const int64_t p = base + 4 * int64_t(tid + kThreads * j);
-      xs[j] = i32x4{0, 0, 0, 0};
-      prevs[j] = 0;
-      if (p < N) {
-        xs[j] = load4<kVec>(seg, p, N);
-        prevs[j] = p > 0 ? seg[p - 1] : 0;
-      }
+      xs[j] = p < N ? load4<kVec>(seg, p, N) : i32x4{0, 0, 0, 0};
     }
-    int64_t tile_nz = -1;
+    if (lane == 63) {
+#pragma unroll
+      for (int j = 0; j < kGroupsPerThread; ++j) s_edge[j * kWaves + wid] = xs[j][3];
+    }
+    const int before_tile = (tid == 0 && base > 0) ? seg[base - 1] : 0;
+    __syncthreads();
+    int tile_nz = -1;  // last non-zero position in the tile, tile-relative
 #pragma unroll
     for (int j = 0; j < kGroupsPerThread; ++j) {
       const int m = tid + kThreads * j;
-      const int64_t p = base + 4 * int64_t(m);
-      unsigned bits = 0;
-      if (p < N) {
-        const i32x4 x = xs[j];
-        int prev = prevs[j];
+      const i32x4 x = xs[j];
+      int prev = __shfl_up(x[3], 1, 64);
+      if (lane == 0)
+        prev = wid > 0 ? s_edge[j * kWaves + wid - 1]
+                       : (j > 0 ? s_edge[(j - 1) * kWaves + kWaves - 1] : before_tile);
+      unsigned bits;
+      if (kT4) {
+        // T % 4 == 0: rows start only at a group's first position
+        bits = unsigned(x[0] != 0 && (x[0] != prev || rp == 0)) |
+               (unsigned(x[1] != 0 && x[1] != x[0]) << 1) |
+               (unsigned(x[2] != 0 && x[2] != x[1]) << 2) |
+               (unsigned(x[3] != 0 && x[3] != x[2]) << 3);
+      } else {
+        bits = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // r = row position of p + i, plus T when it wrapped; r <= T + 2, so
           // it is a multiple of T only as 0 or T, or 2T, 3T when T <= 2
           const uint32_t r = rp + uint32_t(i);
           const bool row_start = r == 0 || r == T32 || (T32 <= 2 && (r == 2 * T32 || r == 3 * T32));
-          if (p + i < N && x[i] != 0) {
-            tile_nz = p + i;
-            if (row_start || x[i] != prev) bits |= 1u << i;
-          }
-          prev = x[i];
+          const int pv = i == 0 ? prev : x[i - 1];
+          if (x[i] != 0 && (row_start || x[i] != pv)) bits |= 1u << i;
         }
       }
+      const int nz = x[3] != 0 ? 3 : x[2] != 0 ? 2 : x[1] != 0 ? 1 : x[0] != 0 ? 0 : -1;
+      if (nz >= 0) tile_nz = 4 * m + nz;  // positions >= N read as 0
       s_bits[m] = uint8_t(bits);
       rp += step;
       if (rp >= T32) rp -= T32;
     }
-    tile_nz = wave_max64(tile_nz);
-    if (lane == 0) s_wmax[wid] = tile_nz;
+    const int64_t tile_last = wave_max64(tile_nz >= 0 ? base + tile_nz : int64_t(-1));
+    if (lane == 0) s_wmax[wid] = tile_last;
     __syncthreads();
     if (!sweep) {
 #pragma unroll
@@ -264,12 +276,10 @@ hipError_t launch_cu_seqlens(const int32_t* seg, int64_t N, int64_t T, int32_t m
                              hipStream_t stream) {
   const bool vec = (reinterpret_cast<uintptr_t>(seg) % 16 == 0) &&
                    (token_seg == nullptr || reinterpret_cast<uintptr_t>(token_seg) % 16 == 0);
-  if (vec)
-    hipLaunchKernelGGL(cu_seqlens_kernel<true>, dim3(1), dim3(kThreads), 0, stream, seg, N, T,
-                       max_segs, cu, token_seg, n_segs, flags);
-  else
-    hipLaunchKernelGGL(cu_seqlens_kernel<false>, dim3(1), dim3(kThreads), 0, stream, seg, N, T,
-                       max_segs, cu, token_seg, n_segs, flags);
+  auto kernel = vec ? (T % 4 == 0 ? cu_seqlens_kernel<true, true> : cu_seqlens_kernel<true, false>)
+                    : (T % 4 == 0 ? cu_seqlens_kernel<false, true> : cu_seqlens_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, dim3(1), dim3(kThreads), 0, stream, seg, N, T, max_segs, cu, token_seg,
+                     n_segs, flags);
   return hipGetLastError();
 }
 

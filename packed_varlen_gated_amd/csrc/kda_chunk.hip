@@ -62,13 +62,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
 // Work plan (built on the device by kda_plan_kernel; see there).
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kHistBins = 2048;   // run-length bins of the longest-first order
 constexpr int kMinRun = 32;       // chunks: no run is cut shorter, no shorter segment is cut
 constexpr int kRunDiv = 4;        // cut runs are at most 1/kRunDiv of the per-CU share
 constexpr int kMaxRuns = 16;      // runs per segment
 constexpr int kShareCUs = 256;    // compute units the per-CU share is counted over
 constexpr int kPlanHeader = 64;   // int32 words before the run table
+constexpr int kPlanCache = 8192;  // segment slots whose chunk counts the plan keeps in LDS
 
 // A blocks (row sub-chunk w, column sub-chunk j), j <= w, in this order; the
 // query version of block b lives in LDS slot b. Jobs 10 and 11 zero the blocks
@@ -893,25 +894,33 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
 // 1. the chunk total over the well-formed segments gives the per-CU share
 //    avg = ceil(total H / kShareCUs) in chunk steps;
 // 2. a segment longer than max(avg, kMinRun) chunks is cut into m nearly equal
-//    runs of at most max(kMinRun, ceil(avg / kRunDiv)) chunks (m <= kMaxRuns);
-//    every other non-empty segment is one run; empty and malformed segments
-//    have none (malformed ones set PKV_FLAG_BAD_CU_SEQLENS here);
+//    runs of at least max(kMinRun, ceil(avg / kRunDiv)) chunks
+//    (m <= kMaxRuns); every other non-empty segment is one run; empty and
+//    malformed segments have none (malformed ones set
+//    PKV_FLAG_BAD_CU_SEQLENS here);
 // 3. runs are ranked longest first through a histogram of run lengths (ties in
 //    any order: results do not depend on the order), and so are the runs that
 //    are not last in their segment, which the state pass takes.
 // The state slots of a segment's first m - 1 runs are consecutive from sbase
 // (exclusive prefix of m - 1 over the segments, computed tile by tile).
-__device__ __forceinline__ int plan_runs(int64_t n, int64_t thr, int64_t R) {
+// Chunk counts are below 2^26 (N <= INT32_MAX), so all per-segment arithmetic
+// is 32-bit; the work-group is small because the work is tiny and serial.
+__device__ __forceinline__ int plan_runs(int n, int thr, int R) {
   if (n <= 0) return 0;
   if (n <= thr) return 1;
-  const int64_t Ri = R > (n + kMaxRuns - 1) / kMaxRuns ? R : (n + kMaxRuns - 1) / kMaxRuns;
-  return int((n + Ri - 1) / Ri);
+  const int floor_len = (n + kMaxRuns - 1) / kMaxRuns;
+  const int Ri = R > floor_len ? R : floor_len;
+  return (n + Ri - 1) / Ri;
 }
-// chunks of run j of a segment of n chunks cut into m runs
-__device__ __forceinline__ int run_len(int64_t n, int m, int j) {
-  return int((n * (j + 1)) / m - (n * j) / m);
-}
+// chunks before run j of a segment of n chunks cut into m runs (n j < 2^30)
+__device__ __forceinline__ int run_begin(int n, int m, int j) { return int(uint32_t(n * j) / uint32_t(m)); }
 __device__ __forceinline__ int len_bin(int len) { return len < kHistBins - 1 ? len : kHistBins - 1; }
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
 
 // Exclusive prefix over the work-group (kPlanThreads threads); *total gets the sum.
 __device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
@@ -925,6 +934,7 @@ __device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
   if (lane == 63) s_tmp[wv] = inc;
   __syncthreads();
   int before = 0, all = 0;
+#pragma unroll
   for (int i = 0; i < kPlanThreads / 64; ++i) {
     const int t = s_tmp[i];
     before += i < wv ? t : 0;
@@ -936,7 +946,7 @@ __device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* __restrict__ cu,
-                                                                int32_t max_segs, int64_t N,
+                                                                int32_t max_segs, int32_t N,
                                                                 int32_t H, int32_t states_max,
                                                                 int32_t runs_max,
                                                                 int32_t* __restrict__ plan,
@@ -945,34 +955,39 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   __shared__ int s_hs[kHistBins];  // state runs likewise
   __shared__ int s_tmp[kPlanThreads / 64];
   __shared__ unsigned long long s_total;
+  __shared__ int s_n[kPlanCache];  // chunk counts, when max_segs <= kPlanCache
   const int tid = threadIdx.x;
-  const int64_t states_word_off = kPlanHeader + 8 * int64_t(runs_max);
+  const int states_word_off = kPlanHeader + 8 * runs_max;
+  const bool cached = max_segs <= kPlanCache;
   for (int i = tid; i < kHistBins; i += kPlanThreads) s_hr[i] = s_hs[i] = 0;
   if (tid == 0) s_total = 0;
   __syncthreads();
-  // chunks of segment i (malformed ones count 0 and are flagged)
-  auto is_bad = [&](int i) {
-    if (cu == nullptr) return false;
-    const int64_t a = cu[i], e = cu[i + 1];
-    return a < 0 || e < a || e > N || (i == 0 && a != 0);
+  // chunks of segment i; malformed ones count 0 and are flagged
+  auto chunks = [&](int i, bool& bad) -> int {
+    bad = false;
+    if (cu == nullptr) return int((uint32_t(N) + kC - 1) / kC);
+    const int a = cu[i], e = cu[i + 1];
+    bad = a < 0 || e < a || e > N || (i == 0 && a != 0);
+    return bad ? 0 : int((uint32_t(e - a) + kC - 1) / kC);
   };
-  auto chunks = [&](int i) -> int64_t {
-    if (cu == nullptr) return (N + kC - 1) / kC;
-    return is_bad(i) ? 0 : (int64_t(cu[i + 1]) - cu[i] + kC - 1) / kC;
-  };
-  unsigned long long mine = 0;
+  int64_t mine = 0;  // 64-bit: overlapping (malformed) slots can sum past 2^31
   bool any_bad = false;
   for (int i = tid; i < max_segs; i += kPlanThreads) {
-    mine += uint64_t(chunks(i));
-    any_bad = any_bad || is_bad(i);
+    bool bad;
+    const int n = chunks(i, bad);
+    if (cached) s_n[i] = n;
+    mine += n;
+    any_bad = any_bad || bad;
   }
-  atomicAdd(&s_total, mine);
   if (any_bad && flags != nullptr) atomicOr(flags, kFlagBadCuSeqlens);
+  mine = wave_sum64(mine);
+  if ((tid & 63) == 0) atomicAdd(&s_total, (unsigned long long)mine);
   __syncthreads();
   const int64_t total = int64_t(s_total);
-  const int64_t avg = (total * H + kShareCUs - 1) / kShareCUs;
-  const int64_t thr = avg > kMinRun ? avg : kMinRun;
-  const int64_t R = (avg + kRunDiv - 1) / kRunDiv > kMinRun ? (avg + kRunDiv - 1) / kRunDiv : kMinRun;
+  const int64_t avg64 = (total * H + kShareCUs - 1) / kShareCUs;
+  const int avg = avg64 < (1 << 30) ? int(avg64) : (1 << 30);
+  const int thr = avg > kMinRun ? avg : kMinRun;
+  const int R = (avg + kRunDiv - 1) / kRunDiv > kMinRun ? (avg + kRunDiv - 1) / kRunDiv : kMinRun;
 
   // Runs of each segment, with the state-slot budget enforced in slot order:
   // a segment whose extra runs would not fit stays whole (only on malformed
@@ -981,25 +996,28 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
     int carry = 0;
     for (int base = 0; base < max_segs; base += kPlanThreads) {
       const int i = base + tid;
-      const int64_t n = i < max_segs ? chunks(i) : 0;
-      int m = i < max_segs ? plan_runs(n, thr, R) : 0;
+      bool bad;
+      const int n = i >= max_segs ? 0 : cached ? s_n[i] : chunks(i, bad);
+      int m = plan_runs(n, thr, R);
       int tile_total;
-      int sb = carry + block_exclusive_scan(m > 0 ? m - 1 : 0, s_tmp, &tile_total);
+      const int sb = carry + block_exclusive_scan(m > 1 ? m - 1 : 0, s_tmp, &tile_total);
       if (m > 1 && sb + m - 1 > states_max) m = 1;
       // a clamped segment's slots stay unused; later segments keep theirs
-      if (i < max_segs) body(i, n, m, sb);
+      if (m > 0) body(i, n, m, sb);
       carry = carry + tile_total < (1 << 29) ? carry + tile_total : (1 << 29);
     }
   };
-  pass([&](int, int64_t n, int m, int) {
-    for (int j = 0; j < m; ++j) {
-      const int b = len_bin(run_len(n, m, j));
-      atomicAdd(&s_hr[b], 1);
-      if (j + 1 < m) atomicAdd(&s_hs[b], 1);
-    }
+  // A segment of n chunks in m runs has n % m runs of q + 1 chunks and the
+  // rest of q (q = n / m); its last run is one of the long ones iff n % m > 0.
+  pass([&](int, int n, int m, int) {
+    const int q = n / m, nl = n - q * m, last_long = nl > 0;
+    atomicAdd(&s_hr[len_bin(q + 1)], nl);
+    atomicAdd(&s_hr[len_bin(q)], m - nl);
+    atomicAdd(&s_hs[len_bin(q + 1)], nl - last_long);
+    atomicAdd(&s_hs[len_bin(q)], m - nl - 1 + last_long);
   });
   __syncthreads();
-  // bins to first ranks, longest first (suffix sums), one thread per bin group
+  // bins to first ranks, longest first (suffix sums), consecutive bins per thread
   constexpr int kPer = kHistBins / kPlanThreads;
   int cr[kPer], cs[kPer], sr = 0, ss = 0;
 #pragma unroll
@@ -1028,28 +1046,30 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
     plan[2] = 0;   // queue counters of the forward and state passes
     plan[3] = 0;
   }
-  pass([&](int i, int64_t n, int m, int sb) {
-    int c0 = 0;
+  pass([&](int i, int n, int m, int sb) {
+    // ranks for the segment's long and short runs, reserved in one go each
+    const int q = n / m, nl = n - q * m, last_long = nl > 0;
+    int rl = atomicAdd(&s_hr[len_bin(q + 1)], nl);
+    int rs = atomicAdd(&s_hr[len_bin(q)], m - nl);
+    int sl = atomicAdd(&s_hs[len_bin(q + 1)], nl - last_long);
+    int ss = atomicAdd(&s_hs[len_bin(q)], m - nl - 1 + last_long);
     for (int j = 0; j < m; ++j) {
-      const int len = run_len(n, m, j);
-      const int b = len_bin(len);
-      const int rank = atomicAdd(&s_hr[b], 1);
-      int32_t* e = plan + kPlanHeader + 8 * rank;
+      const int c0 = run_begin(n, m, j), c1 = run_begin(n, m, j + 1);
+      const bool lng = c1 - c0 > q;
+      int32_t* e = plan + kPlanHeader + 8 * (lng ? rl++ : rs++);
       e[0] = i;
       e[1] = c0;
-      e[2] = c0 + len;
+      e[2] = c1;
       e[3] = j;
       e[4] = sb;
       e[5] = j + 1 == m;
       if (j + 1 < m) {
-        const int sr2 = atomicAdd(&s_hs[b], 1);
-        int32_t* f = plan + states_word_off + 4 * sr2;
+        int32_t* f = plan + states_word_off + 4 * (lng ? sl++ : ss++);
         f[0] = i;
         f[1] = c0;
-        f[2] = c0 + len;
+        f[2] = c1;
         f[3] = sb + j;
       }
-      c0 += len;
     }
   });
 }
@@ -1110,7 +1130,7 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   int32_t* plan = reinterpret_cast<int32_t*>(ws);
   float* states = reinterpret_cast<float*>(ws + L.off_L);
   float* decays = reinterpret_cast<float*>(ws + L.off_D);
-  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, max_segs, N, H,
+  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, max_segs, int32_t(N), H,
                      int32_t(L.states_max), int32_t(L.runs_max), plan, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
