@@ -22,22 +22,23 @@
 // it). Per element only 2^{c} and 2^{T - c} are evaluated (c = in-sub-chunk
 // cumsum); every other factor is per channel.
 //
-// Work-group per (segment, head): 4·Dk/64 producer waves and 4 consumer
-// waves, software-pipelined over chunks (two barriers per chunk step):
+// A work-group runs one (run, head) item at a time: 4 producer waves and 4
+// consumer waves, software-pipelined over chunks (two barriers per chunk step):
 //   first half  P: chunk c: per-channel factors from the sub-chunk totals,
 //                  Q^ = q 2^b and Kbar^T = (beta k 2^{b_C - b})^T to the LDS
 //                  buffers of c's parity, the query versions of the ten A
 //                  blocks, KE, and 2^{b_C}.
-//               C: chunk c-1: o^T = S^T Q^^T + V^T A^T for its Dv/4 columns,
-//                  stored; S = diag(2^{b_C}) S + Kbar^T V.
-//   second half P: V^T of chunk c; the in-sub-chunk cumulative gates of chunk
-//                  c+1 and their sub-chunk totals (to LDS).
-//               C: the A blocks of chunk c (MFMA), masked, beta-scaled, to LDS.
-// A producer wave owns one 16-token sub-chunk and 64 key channels, so each of
-// its loads covers four tokens x one whole 128-byte line; a lane holds 4
-// consecutive tokens x 4 channels, so the in-sub-chunk cumsum is an in-lane
-// prefix plus a DPP quad scan. The sub-chunk totals go through a small LDS
-// table, and the sub-chunk index is uniform per wave (no divergent stores).
+//               C: chunk c-1: o^T += V^T A^T for its Dv/4 columns, packed;
+//                  S = diag(2^{b_C}) S + Kbar^T V.
+//   second half P: V of chunk c; the in-sub-chunk cumulative gates of chunk
+//                  c+1 and their sub-chunk totals (to LDS); one A block.
+//               C: the stores of chunk c-1's outputs; two A blocks of chunk c
+//                  (MFMA), masked, beta-scaled, to LDS; o^T = S^T Q^^T.
+// Producer wave w owns 16-token sub-chunk w and all Dk channels; a lane holds
+// 4 consecutive tokens x Dk/16 channels, so each load covers four tokens x
+// whole 128-byte lines and the in-sub-chunk cumsum is an in-lane prefix plus
+// a DPP quad scan. The sub-chunk totals go through a small LDS table, and the
+// sub-chunk index is uniform per wave (no divergent stores).
 // Raw inputs of chunk c+1 are loaded at the start of step c. Each
 // single-buffered LDS tile is written in one half and read in the other; Q^,
 // Kbar^T and 2^{b_C}, read a step later, are double-buffered.
@@ -351,7 +352,6 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   // MFMA lane layout (consumers, and every wave for the A blocks).
   const int gq = lane >> 4;
   const int lr = lane & 15;
-  constexpr int NW = NT / 64;  // waves per work-group
   const int ci = w - NP;               // consumer index 0..3
   const int e0 = ci * C::EW;
   // Row rho of 16-column tile et of a consumer's state / output holds channel
@@ -691,13 +691,17 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     }
   };
 
-  // ---- every wave, second half: the A blocks of the chunk just prepared.
-  // Jobs 0..9 are the blocks (w, j <= w), jobs 10 and 11 zero the blocks
-  // (0, 1) and (2, 3) that the A.V product reads through its 32-wide steps;
-  // wave w takes jobs w, w + NW, ... Zero jobs run on a valid slot and their
-  // result is replaced, so no job branches.
+  // ---- second half: the A blocks of the chunk just prepared. Jobs 0..9
+  // are the blocks (w, j <= w), jobs 10 and 11 zero the blocks (0, 1) and
+  // (2, 3) that the A.V product reads through its 32-wide steps. Consumer ci
+  // takes jobs ci and ci + 4, producer w job 8 + w: the consumers' half is the
+  // longer one. Zero jobs run on a valid slot and their result is replaced,
+  // so no job branches.
   auto a_blocks = [&](const float* s_bet) {
-    for (int job = w; job < 12; job += NW) {
+    const int j0 = producer ? 8 + w : ci;
+    const int nj = producer ? 1 : 2;
+    for (int jj = 0; jj < nj; ++jj) {
+      const int job = j0 + 4 * jj;
       int bw, bj;
       block_of(job, bw, bj);
       const bool real = job < 10;
