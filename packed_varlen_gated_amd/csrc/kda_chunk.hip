@@ -109,7 +109,11 @@ struct Cfg {
   static constexpr int off_qh = off_kb + 2 * kC * RP * 2;    // Q^, bf16 [kC][KP]
   static constexpr int off_ke = off_qh + kC * KP * 2;        // KE, bf16 [kC][KP]
   static constexpr int off_qv = off_ke + kC * KP * 2;        // query versions, bf16 [10][16][KP]
-  static constexpr int bytes = off_qv + 10 * 16 * KP * 2;
+  // Dv = 128: outputs staged through LDS, bf16 [kC][DV], 16-byte chunk c of
+  // row r at chunk c ^ (r % 16) (conflict-free both ways, no padding room)
+  static constexpr bool stage_o = DV == 128;
+  static constexpr int off_o = off_qv + 10 * 16 * KP * 2;
+  static constexpr int bytes = off_o + (stage_o ? kC * DV * 2 : 0);
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -276,6 +280,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   float* s_decay = reinterpret_cast<float*>(tile(C::off_decay));
   float* s_beta = reinterpret_cast<float*>(tile(C::off_beta));
   float* s_T = reinterpret_cast<float*>(tile(C::off_T));
+  char* s_o = tile(C::off_o);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -670,9 +675,34 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     state_update(S, nullptr, s_kb, s_dec);
   };
 
-  // ---- consumer, second half of step c+1: the outputs of chunk c packed in
-  // the first half. Issuing the stores here keeps them off the first half,
-  // where the producers' loads fill the vector memory queue.
+  // ---- Dv = 128, consumer, end of the first half of step c+1: the packed
+  // outputs of chunk c to the LDS stage (the producers store them).
+  auto stage_out = [&](const uint32_t (&opk)[4][2 * ET]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = 16 * t + lr, chunk = 4 * ci + gq;  // channels e0 + 8 gq .. + 7
+      *reinterpret_cast<u32x4*>(s_o + row * (DV * 2) + ((chunk ^ (row & 15)) << 4)) =
+          u32x4{opk[t][0], opk[t][1], opk[t][2], opk[t][3]};
+    }
+  };
+  // ---- Dv = 128, producer, second half of step c+1: chunk c's outputs from
+  // the stage, whole rows per store (producer w: the rows of sub-chunk w, 16
+  // lanes per 256-byte row); rows past the chunk end are dropped by the range.
+  auto store_rows = [&](int c) {
+    const int64_t p0 = start + int64_t(c) * kC;
+    const int Lc = chunk_len(c);
+    const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = 16 * sw + 4 * m + (lane >> 4), chunk = lane & 15;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(s_o + row * (DV * 2) + ((chunk ^ (row & 15)) << 4));
+      __builtin_amdgcn_raw_buffer_store_b128(v4i{int(x[0]), int(x[1]), int(x[2]), int(x[3])}, ro,
+                                             uint32_t(row) * rowV + (chunk << 4), 0, 0);
+    }
+  };
+  // ---- Dv = 64, consumer, second half of step c+1: the outputs of chunk c
+  // packed in the first half. Issuing the stores here keeps them off the first
+  // half, where the producers' loads fill the vector memory queue.
   auto store_out = [&](const uint32_t (&opk)[4][2 * ET], int c) {
     const int64_t p0 = start + int64_t(c) * kC;
     const int Lc = chunk_len(c);
@@ -756,6 +786,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         if (s < nchunks) produce_a(QA, cs, s_qh, s_kb0, s_decay, s_beta);
         if (beta_wave) bnext2 = load_beta(s + 2);
         __syncthreads();
+        if (!kState && C::stage_o && s >= 1) store_rows(s - 1);
         if (!kState && s < nchunks) a_blocks(s_beta);
         if (s < nchunks) produce_b(R.v);
         load_v(R, s + 1);
@@ -768,6 +799,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         if (s + 1 < nchunks) produce_a(QB, cs, s_qh, s_kb1, s_decay + DK, s_beta + kC);
         if (beta_wave) bnext = load_beta(s + 3);
         __syncthreads();
+        if (!kState && C::stage_o) store_rows(s);
         if (!kState && s + 1 < nchunks) a_blocks(s_beta + kC);
         if (s + 1 < nchunks) produce_b(R.v);
         load_v(R, s + 2);
@@ -837,9 +869,12 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         uint32_t opk[4][2 * ET];  // packed outputs of the chunk finished in this step
         __syncthreads();  // the producers' first scan
         for (int s = 0; s <= nchunks; s += 2) {
-          if (s >= 1) consume_finish(S, acc, opk, s_kb1, s_decay + DK);
+          if (s >= 1) {
+            consume_finish(S, acc, opk, s_kb1, s_decay + DK);
+            if constexpr (C::stage_o) stage_out(opk);
+          }
           __syncthreads();
-          if (s >= 1) store_out(opk, s - 1);
+          if (!C::stage_o && s >= 1) store_out(opk, s - 1);
           if (s < nchunks) {
             a_blocks(s_beta);
             consume_inter(S, acc);
@@ -847,8 +882,9 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
           __syncthreads();
           if (s + 1 > nchunks) break;
           consume_finish(S, acc, opk, s_kb0, s_decay);
+          if constexpr (C::stage_o) stage_out(opk);
           __syncthreads();
-          store_out(opk, s);
+          if constexpr (!C::stage_o) store_out(opk, s);
           if (s + 1 < nchunks) {
             a_blocks(s_beta + kC);
             consume_inter(S, acc);
