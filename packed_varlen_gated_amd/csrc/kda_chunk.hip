@@ -102,7 +102,7 @@ struct Cfg {
   static constexpr int off_item = 0;                         // int: next queue item
   static constexpr int off_decay = 16;                       // float [2][DK]
   static constexpr int off_beta = off_decay + 2 * DK * 4;    // float [2][kC]
-  static constexpr int off_T = off_beta + 2 * kC * 4;        // float [DK][4] sub-chunk totals
+  static constexpr int off_T = off_beta + 2 * kC * 4;        // float [DK][4] 2^{sub-chunk totals}
   static constexpr int off_a = off_T + DK * 4 * 4;           // A, bf16 [kC][TP]
   static constexpr int off_v = off_a + kC * TP * 2;          // V, bf16 [kC][VP]
   static constexpr int off_kb = off_v + kC * VP * 2;         // Kbar, bf16 [2][kC][RP]
@@ -140,6 +140,7 @@ __device__ __forceinline__ float dpp(float x) {
 }
 constexpr int kQuadPrev1 = 0x90;  // quad_perm [0,0,1,2]
 constexpr int kQuadPrev2 = 0x40;  // quad_perm [0,0,0,1]
+constexpr int kQuadLast = 0xFF;   // quad_perm [3,3,3,3]
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufFlags);
@@ -418,8 +419,9 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   };
   // ---- producer, second half: in-sub-chunk cumulative gates (base 2) of a
   // chunk. cs[i][c] is the inclusive cumsum at token tok0 + i, channel ch0 + c,
-  // from the start of the sub-chunk; the sub-chunk totals go to s_T.
-  auto scan = [&](const Raw<PCPL, PVPL>& R, float (&cs)[4][PCPL]) {
+  // from the start of the sub-chunk, cs[4][c] the sub-chunk total T; s_T gets
+  // 2^T of every sub-chunk (the next half's factors are products of those).
+  auto scan = [&](const Raw<PCPL, PVPL>& R, float (&cs)[5][PCPL]) {
     float tot[PCPL];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
@@ -438,40 +440,38 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) cs[i][c] += excl;
       tot[c] = inc;  // quad lane 3 holds the sub-chunk total
+      cs[4][c] = dpp<kQuadLast>(inc);
     }
     if (tq == 3) {
 #pragma unroll
-      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c) * 4 + sw] = tot[c];
+      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c) * 4 + sw] = ex2(tot[c]);
     }
   };
 
   // ---- producer, first half: factors and MFMA operands of one chunk.
-  // With T_j the sub-chunk totals of a channel, rho_w = T_0 + .. + T_{w-1}:
-  // f0 = 2^{rho_w} (Q^ = Q~ f0), f1 = 2^{T_{w+1} + .. + T_3} (Kbar = beta KE f1),
-  // f2 = 2^{-T_w} (diagonal version), f3 = 2^{T_{w-1}} (block (w, w-2)),
-  // f4 = 2^{T_{w-1} + T_{w-2}} (block (3, 0)); decay = 2^{T_0 + .. + T_3}.
-  // The sub-chunk index is a compile-time constant inside (one instance per
-  // sub-chunk), so every choice below is resolved without branches.
-  auto produce_a_sw = [&](auto swc, const RawQK<PCPL>& R, const float (&cs)[4][PCPL],
+  // With T_j the sub-chunk totals of a channel and E_j = 2^{T_j} (from s_T):
+  // f0 = 2^{T_0 + .. + T_{w-1}} (Q^ = Q~ f0), f1 = 2^{T_{w+1} + .. + T_3}
+  // (Kbar = beta KE f1), f2 = 2^{-T_w} (diagonal version), f3 = 2^{T_{w-1}}
+  // (block (w, w-2)), f4 = 2^{T_{w-1} + T_{w-2}} (block (3, 0)), decay =
+  // 2^{T_0 + .. + T_3}: products of the E_j and one reciprocal, instead of an
+  // exponential each. The sub-chunk index is a compile-time constant inside
+  // (one instance per sub-chunk), so every choice below is resolved without
+  // branches.
+  auto produce_a_sw = [&](auto swc, const RawQK<PCPL>& R, const float (&cs)[5][PCPL],
                           bf16* s_qh, bf16* s_kb, float* s_dec, const float* s_bet) {
     constexpr int sw = decltype(swc)::value;
     constexpr int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
-    float Tw[PCPL], f[5][PCPL], dec[PCPL];
+    float f[5][PCPL], dec[PCPL];
+    const float (&Tw)[PCPL] = cs[4];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
-      const f32x4 Tj = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c) * 4);
-      const float T = Tj[sw];
-      const float Tm1 = sw >= 1 ? Tj[sw >= 1 ? sw - 1 : 0] : 0.f;
-      const float Tm2 = sw >= 2 ? Tj[sw >= 2 ? sw - 2 : 0] : 0.f;
-      const float rho = sw == 0 ? 0.f : sw == 1 ? Tj[0] : sw == 2 ? Tj[0] + Tj[1] : (Tj[0] + Tj[1]) + Tj[2];
-      const float after = sw == 3 ? 0.f : sw == 2 ? Tj[3] : sw == 1 ? Tj[2] + Tj[3] : Tj[1] + (Tj[2] + Tj[3]);
-      Tw[c] = T;
-      f[0][c] = ex2(rho);
-      f[1][c] = ex2(after);
-      f[2][c] = ex2(-T);
-      f[3][c] = ex2(Tm1);
-      f[4][c] = ex2(Tm1 + Tm2);
-      dec[c] = ex2((Tj[0] + Tj[1]) + (Tj[2] + Tj[3]));
+      const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c) * 4);
+      f[0][c] = sw == 0 ? 1.f : sw == 1 ? E[0] : sw == 2 ? E[0] * E[1] : (E[0] * E[1]) * E[2];
+      f[1][c] = sw == 3 ? 1.f : sw == 2 ? E[3] : sw == 1 ? E[2] * E[3] : E[1] * (E[2] * E[3]);
+      f[2][c] = __builtin_amdgcn_rcpf(E[sw]);
+      f[3][c] = sw >= 1 ? E[sw >= 1 ? sw - 1 : 0] : 0.f;
+      f[4][c] = sw >= 2 ? E[sw >= 1 ? sw - 1 : 0] * E[sw >= 2 ? sw - 2 : 0] : 0.f;
+      dec[c] = (E[0] * E[1]) * (E[2] * E[3]);
     }
     if (sw == 0 && tq == 0) {
 #pragma unroll
@@ -513,17 +513,16 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   };
 
   // State pass: only Kbar and the decay.
-  auto produce_kb_sw = [&](auto swc, const RawQK<PCPL>& R, const float (&cs)[4][PCPL],
+  auto produce_kb_sw = [&](auto swc, const RawQK<PCPL>& R, const float (&cs)[5][PCPL],
                            bf16* s_kb, float* s_dec, const float* s_bet) {
     constexpr int sw = decltype(swc)::value;
-    float Tw[PCPL], f1[PCPL], dec[PCPL];
+    float f1[PCPL], dec[PCPL];
+    const float (&Tw)[PCPL] = cs[4];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
-      const f32x4 Tj = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c) * 4);
-      const float after = sw == 3 ? 0.f : sw == 2 ? Tj[3] : sw == 1 ? Tj[2] + Tj[3] : Tj[1] + (Tj[2] + Tj[3]);
-      Tw[c] = Tj[sw];
-      f1[c] = ex2(after);
-      dec[c] = ex2((Tj[0] + Tj[1]) + (Tj[2] + Tj[3]));
+      const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c) * 4);
+      f1[c] = sw == 3 ? 1.f : sw == 2 ? E[3] : sw == 1 ? E[2] * E[3] : E[1] * (E[2] * E[3]);
+      dec[c] = (E[0] * E[1]) * (E[2] * E[3]);
     }
     if (sw == 0 && tq == 0) {
 #pragma unroll
@@ -541,7 +540,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     }
   };
 
-  auto produce_a = [&](const RawQK<PCPL>& R, const float (&cs)[4][PCPL], bf16* s_qh,
+  auto produce_a = [&](const RawQK<PCPL>& R, const float (&cs)[5][PCPL], bf16* s_qh,
                        bf16* s_kb, float* s_dec, const float* s_bet) {
     if constexpr (kState) {
       switch (sw) {
@@ -766,7 +765,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
       begin_item(item);
       Raw<PCPL, PVPL> R;
       RawQK<PCPL> QA, QB;  // q, k of even / odd chunks
-      float cs[4][PCPL];
+      float cs[5][PCPL];
       const bool beta_wave = w == 0;
       uint32_t bnext = 0, bnext2 = 0;  // raw beta of the next chunks (wave 0)
       load_g(R, 0);
