@@ -15,6 +15,8 @@ Sources (the pages; cited by title and section):
   contract" (reset semantics).
 * "Drill: Sequence Packing from scratch" (ac.fzhiy.net), section "The math"
   (cu_seqlens, doc(s), block-diagonal mask).
+* RFC-0026, section 6 (data pipeline alignment: EOD segmentation, positions,
+  loss mask) and section 3.3 (the wrapper's ``initial_state``).
 
 Functions and their pin status (every function is pinned; see tests/):
 
@@ -27,19 +29,25 @@ Functions and their pin status (every function is pinned; see tests/):
                                     tap closed form, hand-computed fixture
 ``chunk_kda_varlen``                pinned: unrolled closed form, g=0 masked
                                     matmul, geometric series, single-token
-                                    segments, gate injection, invariants
+                                    segments, gate injection, invariants;
+                                    initial states: decayed closed form,
+                                    split-and-resume identity
+``eod_to_segment_ids``              pinned: hand-derived rows, construction
+                                    from document lengths
 ==================================  =========================================
 """
 
 from .cu_seqlens import segment_ids_to_cu_seqlens, token_segment, FLAG_OVERFLOW, FLAG_LEADING_PAD
 from .short_conv import short_conv_segmask
 from .kda import chunk_kda_varlen
+from .eod import eod_to_segment_ids
 
 __all__ = [
     "segment_ids_to_cu_seqlens",
     "token_segment",
     "short_conv_segmask",
     "chunk_kda_varlen",
+    "eod_to_segment_ids",
     "FLAG_OVERFLOW",
     "FLAG_LEADING_PAD",
 ]

@@ -8,7 +8,10 @@ RFC-0026, Background ("KDA state leakage problem"), gives the state update
     S_t  = S'_t + beta_t * k_t (outer) v_t
 
 and section 3.1.1 ("API contract") says the state is cleared where the segment
-changes. Readings (listed in the design doc): g_t has one entry per key channel, so
+changes. Section 3.3's wrapper also takes an optional ``initial_state``; with
+cu_seqlens it is read as one state per segment slot, [max_segs, H, Dk, Dv],
+from which that segment's recurrence starts instead of zero (an empty slot
+then keeps it as its final state). Readings (listed in the design doc): g_t has one entry per key channel, so
 exp(g_t) scales the key (row) axis of the [Dk, Dv] state, i.e.
 S_t = diag(exp g_t) S_{t-1} + beta_t k_t v_t^T; the readout is taken after the
 update, o_t = scale * S_t^T q_t; segments come from cu_seqlens (FLA
@@ -32,11 +35,12 @@ def _as_thd(a, name, ndim):
     return a
 
 
-def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0):
+def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None):
     """Return ``(o [N, H, Dv], final_state [max_segs, H, Dk, Dv])`` in float64.
 
     q, k, g: [N, H, Dk] (a leading unit batch axis is accepted);
-    v: [N, H, Dv]; beta: [N, H]; cu_seqlens: int [max_segs + 1] or None.
+    v: [N, H, Dv]; beta: [N, H]; cu_seqlens: int [max_segs + 1] or None;
+    initial_state: [max_segs, H, Dk, Dv] or None (zeros).
     """
     q = _as_thd(q, "q", 3)
     k = _as_thd(k, "k", 3)
@@ -53,13 +57,19 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0):
     if cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] > N:
         raise ValueError("malformed cu_seqlens")
 
+    if initial_state is not None:
+        init = np.asarray(initial_state, dtype=np.float64)
+        if init.shape != (max_segs, H, Dk, Dv):
+            raise ValueError(f"initial_state has shape {init.shape}")
     o = np.zeros((N, H, Dv), dtype=np.float64)
     final_state = np.zeros((max_segs, H, Dk, Dv), dtype=np.float64)
     for i in range(max_segs):
         start, end = int(cu[i]), int(cu[i + 1])
+        # reset at the boundary: zero, or the segment's given initial state
+        S = np.zeros((H, Dk, Dv)) if initial_state is None else init[i].copy()
         if end <= start:
-            continue  # phantom segment: state stays zero
-        S = np.zeros((H, Dk, Dv), dtype=np.float64)  # reset at the boundary
+            final_state[i] = S  # phantom segment: no token changes the state
+            continue
         for t in range(start, end):
             decay = np.exp(g[t])[:, :, None]                       # [H, Dk, 1]
             update = beta[t][:, None, None] * k[t][:, :, None] * v[t][:, None, :]

@@ -198,3 +198,44 @@ def test_decay_acts_on_key_axis():
     np.testing.assert_allclose(fs[0, 0, 0], 0.5 ** (L - 1) * np.array([1.0, 2.0, 3.0]), rtol=1e-14)
     np.testing.assert_allclose(fs[0, 0, 1], np.array([1.0, 2.0, 3.0]), rtol=1e-14)
     np.testing.assert_allclose(o[-1, 0], 0.5 ** (L - 1) * np.array([1.0, 2.0, 3.0]), rtol=1e-14)
+
+
+def test_initial_state_adds_its_decayed_readout():
+    """RFC-0026 section 3.3's initial_state (one per segment slot): the state a
+    segment starts from decays with the running product of exp(g) and is read
+    out by q, on top of the zero-start result (linearity in S0):
+    delta o_t = scale * (exp(sum_{u=a..t} g_u) * S0)^T q_t,
+    delta final = exp(sum_{u=a..e-1} g_u) * S0 (per key channel)."""
+    rng = np.random.default_rng(31)
+    N, H, Dk, Dv = 23, 2, 3, 4
+    q, k, v, g, beta = _rand_inputs(rng, N, H, Dk, Dv)
+    cu = np.array([0, 9, 9, 23])
+    S0 = rng.standard_normal((3, H, Dk, Dv))
+    scale = 0.7
+    o0, f0 = oracle.chunk_kda_varlen(q, k, v, g, beta, cu, scale)
+    o1, f1 = oracle.chunk_kda_varlen(q, k, v, g, beta, cu, scale, initial_state=S0)
+    for i in range(3):
+        a, e = cu[i], cu[i + 1]
+        G = np.cumsum(g[a:e], axis=0)                          # [L, H, Dk]
+        for t in range(a, e):
+            dS = np.exp(G[t - a])[:, :, None] * S0[i]            # [H, Dk, Dv]
+            want = scale * np.einsum("hd,hde->he", q[t], dS)
+            np.testing.assert_allclose(o1[t] - o0[t], want, rtol=1e-10, atol=1e-12)
+        decay = np.exp(G[-1]) if e > a else np.ones((H, Dk))
+        np.testing.assert_allclose(f1[i] - f0[i], decay[:, :, None] * S0[i], rtol=1e-10, atol=1e-12)
+    assert np.array_equal(f1[1], S0[1])  # the empty slot keeps its initial state
+
+
+def test_split_and_resume_equals_whole_segment():
+    """Running [a, c) as [a, b) and then [b, c) started from the first part's
+    final state gives the whole segment's outputs and final state."""
+    rng = np.random.default_rng(32)
+    N, H, Dk, Dv = 40, 2, 4, 3
+    q, k, v, g, beta = _rand_inputs(rng, N, H, Dk, Dv)
+    ow, fw = oracle.chunk_kda_varlen(q, k, v, g, beta, np.array([0, N]))
+    for b in (1, 17, 39):
+        oa, fa = oracle.chunk_kda_varlen(q[:b], k[:b], v[:b], g[:b], beta[:b], np.array([0, b]))
+        ob, fb = oracle.chunk_kda_varlen(q[b:], k[b:], v[b:], g[b:], beta[b:], np.array([0, N - b]),
+                                         initial_state=fa)
+        np.testing.assert_allclose(np.concatenate([oa, ob]), ow, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(fb, fw, rtol=1e-12, atol=1e-12)
