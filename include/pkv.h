@@ -16,6 +16,12 @@
  *       RFC-0026, Background (KDA state leakage problem) and section 3.1.1;
  *       RFC-0025, Design sections 2 (batch flatten) and 4 (kernel wrappers).
  *
+ * and the step before them in the data pipeline:
+ *
+ *   pkv_eod_to_segment_ids         EOD-separated token rows -> segment ids,
+ *                                  positions and loss segment ids
+ *       RFC-0026, section 6 (data pipeline alignment).
+ *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer (HIP device memory or memory the
  *     GPU can address). Scalars are passed by value.
@@ -93,6 +99,30 @@ pkv_status pkv_segment_ids_to_cu_seqlens(const int32_t* segment_ids, int64_t B, 
                                          void* stream);
 
 /*
+ * EOD-separated token rows -> segment ids, positions and loss segment ids
+ * (RFC-0026 "Ling3 KDA varlen support", section 6, data pipeline alignment:
+ * an EOD token keeps the id of the document it ends and a new segment starts
+ * right after it; positions restart at 0 after an EOD; EOD positions carry no
+ * loss). Every row is an independent packed sample with ids from 1:
+ *   segment_ids[b,t]      = 1 + #{u < t : tokens[b,u] == eod_id}
+ *   positions[b,t]        = t - (1 + last u < t with tokens[b,u] == eod_id),
+ *                           or t when there is none
+ *   loss_segment_ids[b,t] = 0 where tokens[b,t] == eod_id, else segment_ids[b,t]
+ * There is no padding (segment_ids is never 0), so the result feeds
+ * pkv_segment_ids_to_cu_seqlens directly.
+ *
+ * tokens            int32 [B, T] (device).
+ * segment_ids       int32 [B, T] (device), written in full.
+ * positions         int32 [B, T] or NULL.
+ * loss_segment_ids  int32 [B, T] or NULL.
+ * Errors: PKV_ERR_INVALID_ARGUMENT if tokens or segment_ids is NULL, B < 1,
+ * T < 1, B*T > INT32_MAX, or an output overlaps the tokens or another output.
+ */
+pkv_status pkv_eod_to_segment_ids(const int32_t* tokens, int64_t B, int64_t T, int32_t eod_id,
+                                  int32_t* segment_ids, int32_t* positions,
+                                  int32_t* loss_segment_ids, void* stream);
+
+/*
  * Segment-masked short causal depthwise convolution.
  *
  * y[b,t,f] = sum_{k<Kc} w[f,k] * x[b,t-k,f] * [t-k >= 0] * [seg[b,t-k] == seg[b,t]]
@@ -127,10 +157,12 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
 /*
  * Packed gated linear-attention recurrence with per-segment reset.
  *
- * For every segment i = [cu[i], cu[i+1]) and head h, from S = 0:
+ * For every segment i = [cu[i], cu[i+1]) and head h, from S = initial_state[i, h]
+ * (0 when initial_state is NULL):
  *   S_t = diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T      (S is [Dk, Dv], fp32)
  *   o_t = scale * S_t^T q_t                              (readout after the update)
- * final_state[i, h] = S after the segment's last token (0 for empty slots).
+ * final_state[i, h] = S after the segment's last token (the initial state, or 0,
+ * for empty slots).
  * Positions p >= cu[max_segs] get o = 0.
  *
  * q, k, g     [1, N, H, Dk] in `dtype` (the batch flattened to one row, B*T = N).
@@ -139,9 +171,12 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
  * cu_seqlens  int32 [max_segs + 1] or NULL. NULL means one segment [0, N) and
  *             max_segs is taken as 1. Expected: cu[0] = 0, non-decreasing,
  *             cu[max_segs] <= N; a violation sets PKV_FLAG_BAD_CU_SEQLENS.
+ * initial_state float32 [max_segs, H, Dk, Dv] or NULL (RFC-0026 section 3.3's
+ *             wrapper argument, one state per segment slot); must not overlap
+ *             final_state.
  * o           [1, N, H, Dv] in `dtype`; must not overlap the inputs.
- *             q, k, v, g, o and final_state must be 16-byte aligned, beta
- *             aligned to its element size.
+ *             q, k, v, g, o, initial_state and final_state must be 16-byte
+ *             aligned, beta aligned to its element size.
  * final_state float32 [max_segs, H, Dk, Dv] or NULL (not written).
  * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in.
  * workspace   device buffer of at least pkv_chunk_kda_varlen_workspace_size()
@@ -161,14 +196,15 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
 pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
                                 int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                int32_t dtype, void* o, float* final_state, int32_t* flags,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                int32_t dtype, const float* initial_state, void* o,
+                                float* final_state, int32_t* flags, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(int32_t status);
 
 /* ABI version of this header (bumped on any signature change). */
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 int32_t pkv_abi_version(void);
 
 #ifdef __cplusplus

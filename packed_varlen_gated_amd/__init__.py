@@ -47,12 +47,14 @@ def _load():
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     lib.pkv_segment_ids_to_cu_seqlens.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.pkv_segment_ids_to_cu_seqlens.restype = i32
+    lib.pkv_eod_to_segment_ids.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
+    lib.pkv_eod_to_segment_ids.restype = i32
     lib.pkv_short_conv_segmask.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     lib.pkv_short_conv_segmask.restype = i32
     lib.pkv_chunk_kda_varlen_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
     lib.pkv_chunk_kda_varlen_workspace_size.restype = sz
     lib.pkv_chunk_kda_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32,
-                                         vp, vp, vp, vp, sz, vp]
+                                         vp, vp, vp, vp, vp, sz, vp]
     lib.pkv_chunk_kda_varlen.restype = i32
     lib.pkv_status_string.argtypes = [i32]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -101,6 +103,12 @@ def _need(t, name, device, dtype=None, ndim=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+class EodSegments(NamedTuple):
+    segment_ids: torch.Tensor                 # int32 [B, T]
+    positions: Optional[torch.Tensor]         # int32 [B, T] or None
+    loss_segment_ids: Optional[torch.Tensor]  # int32 [B, T] or None
+
+
 class CuSeqlens(NamedTuple):
     cu_seqlens: torch.Tensor          # int32 [max_segs + 1]
     token_seg: Optional[torch.Tensor]  # int32 [B*T] or None
@@ -121,6 +129,21 @@ def segment_ids_to_cu_seqlens(segment_ids, max_segs, with_token_seg=False):
     _check(lib.pkv_segment_ids_to_cu_seqlens(_ptr(segment_ids), B, T, max_segs, _ptr(cu), _ptr(tok),
                                              _ptr(n), _ptr(flags), _stream(dev)))
     return CuSeqlens(cu, tok, n, flags)
+
+
+def eod_to_segment_ids(tokens, eod_id, with_positions=True, with_loss=True):
+    """tokens int32 [B, T] (device) -> EodSegments of int32 [B, T] device tensors
+    (positions / loss_segment_ids None when not requested). No sync."""
+    lib = _load()
+    dev = tokens.device
+    _need(tokens, "tokens", dev, torch.int32, 2)
+    B, T = tokens.shape
+    seg = torch.empty(B, T, dtype=torch.int32, device=dev)
+    pos = torch.empty(B, T, dtype=torch.int32, device=dev) if with_positions else None
+    loss = torch.empty(B, T, dtype=torch.int32, device=dev) if with_loss else None
+    _check(lib.pkv_eod_to_segment_ids(_ptr(tokens), B, T, int(eod_id), _ptr(seg), _ptr(pos), _ptr(loss),
+                                      _stream(dev)))
+    return EodSegments(seg, pos, loss)
 
 
 def short_conv_segmask(x, w, segment_ids=None, out=None):
@@ -149,11 +172,12 @@ def chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype):
 
 
 def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_state=True,
-                     flags=None, out=None, workspace=None):
+                     flags=None, out=None, workspace=None, initial_state=None):
     """Packed KDA forward.
 
     q, k, g: [1, N, H, Dk] (or [B, T, H, Dk], taken as the flattened [1, B*T, H, Dk]);
     v: [..., Dv]; beta: [1, N, H]; cu_seqlens: int32 [max_segs + 1] or None (one segment).
+    initial_state: fp32 [max_segs, H, Dk, Dv] or None (each segment starts from its slot's state).
     Returns (o [same leading shape as q, Dv], final_state fp32 [max_segs, H, Dk, Dv] or None).
     """
     lib = _load()
@@ -179,11 +203,16 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_
     fs = torch.empty(max_segs, H, Dk, Dv, dtype=torch.float32, device=dev) if output_final_state else None
     if flags is not None:
         _need(flags, "flags", dev, torch.int32, 1)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", dev, torch.float32, 4)
+        if tuple(initial_state.shape) != (max_segs, H, Dk, Dv):
+            raise ValueError(f"initial_state must be [{max_segs}, {H}, {Dk}, {Dv}]")
     need = int(lib.pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, code))
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pkv_chunk_kda_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                    max_segs, N, H, Dk, Dv, float(scale), code, _ptr(o), _ptr(fs),
+                                    max_segs, N, H, Dk, Dv, float(scale), code, _ptr(initial_state),
+                                    _ptr(o), _ptr(fs),
                                     _ptr(flags), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, fs

@@ -53,6 +53,24 @@ pkv_status pkv_segment_ids_to_cu_seqlens(const int32_t* segment_ids, int64_t B, 
                                          n_segs, flags, static_cast<hipStream_t>(stream)));
 }
 
+pkv_status pkv_eod_to_segment_ids(const int32_t* tokens, int64_t B, int64_t T, int32_t eod_id,
+                                  int32_t* segment_ids, int32_t* positions,
+                                  int32_t* loss_segment_ids, void* stream) {
+  if (tokens == nullptr || segment_ids == nullptr) return PKV_ERR_INVALID_ARGUMENT;
+  if (B < 1 || T < 1 || B > kInt32Max || T > kInt32Max || B * T > kInt32Max)
+    return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t n = B * T * 4;
+  const void* outs[3] = {segment_ids, positions, loss_segment_ids};
+  for (int i = 0; i < 3; ++i) {
+    if (outs[i] == nullptr) continue;
+    if (overlaps(outs[i], n, tokens, n)) return PKV_ERR_INVALID_ARGUMENT;
+    for (int j = 0; j < i; ++j)
+      if (outs[j] != nullptr && overlaps(outs[i], n, outs[j], n)) return PKV_ERR_INVALID_ARGUMENT;
+  }
+  return from_hip(pkv::launch_eod_segments(tokens, B, T, eod_id, segment_ids, positions,
+                                           loss_segment_ids, static_cast<hipStream_t>(stream)));
+}
+
 pkv_status pkv_short_conv_segmask(const void* x, const float* w, const int32_t* segment_ids,
                                   void* y, int64_t B, int64_t T, int64_t F, int32_t Kc,
                                   int32_t dtype, void* stream) {
@@ -77,8 +95,9 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
 pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
                                 int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                int32_t dtype, void* o, float* final_state, int32_t* flags,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                int32_t dtype, const float* initial_state, void* o,
+                                float* final_state, int32_t* flags, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
       o == nullptr)
     return PKV_ERR_INVALID_ARGUMENT;
@@ -93,7 +112,12 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
   for (const void* p : {q, k, v, g, static_cast<const void*>(o)})
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARGUMENT;
   if (reinterpret_cast<uintptr_t>(beta) % elem_size(dtype) != 0 ||
-      reinterpret_cast<uintptr_t>(final_state) % 16 != 0)
+      reinterpret_cast<uintptr_t>(final_state) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(initial_state) % 16 != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t state_bytes = int64_t(max_segs) * H * Dk * Dv * 4;
+  if (initial_state != nullptr && final_state != nullptr &&
+      overlaps(initial_state, state_bytes, final_state, state_bytes))
     return PKV_ERR_INVALID_ARGUMENT;
   if (int64_t(max_segs) * H > (int64_t(1) << 22)) return PKV_ERR_INVALID_ARGUMENT;
   const int64_t es = elem_size(dtype);
@@ -108,10 +132,10 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
     return PKV_ERR_WORKSPACE;
   if (pkv::kda_chunk_supported(Dk, Dv, dtype))
     return from_hip(pkv::launch_kda_chunk(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
-                                          scale, o, final_state, flags, workspace,
+                                          scale, initial_state, o, final_state, flags, workspace,
                                           static_cast<hipStream_t>(stream)));
   return from_hip(pkv::launch_kda_serial(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
-                                         scale, dtype, o, final_state, flags,
+                                         scale, dtype, initial_state, o, final_state, flags,
                                          static_cast<hipStream_t>(stream)));
 }
 

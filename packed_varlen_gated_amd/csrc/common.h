@@ -28,6 +28,9 @@ hipError_t launch_cu_seqlens(const int32_t* seg, int64_t N, int64_t T, int32_t m
                              int32_t* cu, int32_t* token_seg, int32_t* n_segs, int32_t* flags,
                              hipStream_t stream);
 
+hipError_t launch_eod_segments(const int32_t* tokens, int64_t B, int64_t T, int32_t eod_id,
+                               int32_t* seg, int32_t* pos, int32_t* loss, hipStream_t stream);
+
 hipError_t launch_short_conv(const void* x, const float* w, const int32_t* seg, void* y,
                              int64_t B, int64_t T, int64_t F, int32_t Kc, int32_t dtype,
                              hipStream_t stream);
@@ -35,7 +38,8 @@ hipError_t launch_short_conv(const void* x, const float* w, const int32_t* seg, 
 hipError_t launch_kda_serial(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                              int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
-                             void* o, float* final_state, int32_t* flags, hipStream_t stream);
+                             const float* initial_state, void* o, float* final_state,
+                             int32_t* flags, hipStream_t stream);
 
 bool kda_chunk_supported(int32_t Dk, int32_t Dv, int32_t dtype);
 
@@ -47,8 +51,8 @@ size_t kda_chunk_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, i
 
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
-                            int32_t H, int32_t Dk, int32_t Dv, float scale, void* o,
-                            float* final_state, int32_t* flags, void* workspace,
-                            hipStream_t stream);
+                            int32_t H, int32_t Dk, int32_t Dv, float scale,
+                            const float* initial_state, void* o, float* final_state,
+                            int32_t* flags, void* workspace, hipStream_t stream);
 
 }  // namespace pkv

@@ -257,9 +257,9 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
     int32_t* __restrict__ plan, int32_t runs_max, int32_t max_segs, int64_t N,
-    int32_t H, float scale, bf16* __restrict__ o, float* __restrict__ final_state,
-    float* __restrict__ run_states, float* __restrict__ run_decays,
-    int32_t lds_zero) {
+    int32_t H, float scale, const float* __restrict__ initial_state, bf16* __restrict__ o,
+    float* __restrict__ final_state, float* __restrict__ run_states,
+    float* __restrict__ run_decays, int32_t lds_zero) {
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
   constexpr int PCPL = C::PCPL, PVPL = C::PVPL, ET = C::ET, DT = C::DT, KS = C::KS;
@@ -853,9 +853,20 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
           for (int dt = 0; dt < DT; ++dt) *decay_at(sbase, dt) = Dacc[dt];
         }
       } else {
-        // A piece of a cut segment starts from the state of the pieces before
-        // it: S = D_j S + L_j over them in order (D_j, L_j: piece j's decay
+        // The segment starts from its initial state, when one is given; a
+        // piece of a cut segment then folds in the pieces before it:
+        // S = D_j S + L_j over them in order (D_j, L_j: piece j's decay
         // product and its state from zero).
+        if (initial_state != nullptr) {
+          const float* s0 = initial_state + (int64_t(slot) * H + h) * DK * DV;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int et = 0; et < ET; ++et)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                S[dt][et][i] = s0[int64_t(16 * dt + 4 * gq + i) * DV + e0 + ecol(et, lr)];
+        }
         for (int j = 0; j < run_idx; ++j) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
@@ -907,8 +918,9 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   }
 
   if constexpr (!kState) {
-    // After the queue: o = 0 at positions outside every segment, and zero
-    // final states for empty (and malformed) slots; grid-strided, 16-byte stores.
+    // After the queue: o = 0 at positions outside every segment, and the final
+    // states of empty (and malformed) slots: their initial states, or zero;
+    // grid-strided, 16-byte accesses.
     const int64_t G = gridDim.x;
     int64_t cu_last = cu ? int64_t(cu[max_segs]) : N;
     cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
@@ -922,7 +934,9 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         const bool bad = a < 0 || e < a || e > N || (i == 0 && a != 0);
         if (!bad && e > a) continue;
         f32x4* f = reinterpret_cast<f32x4*>(final_state + u * DK * DV);
-        for (int j = tid; j < DK * DV / 4; j += NT) f[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4* f0 = reinterpret_cast<const f32x4*>(initial_state + u * DK * DV);
+        for (int j = tid; j < DK * DV / 4; j += NT)
+          f[j] = initial_state != nullptr ? f0[j] : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
@@ -1151,8 +1165,8 @@ int device_cus() {
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
-                       int32_t H, float scale, void* o, float* fs, int32_t* flags,
-                       char* ws, hipStream_t s) {
+                       int32_t H, float scale, const float* s0, void* o, float* fs,
+                       int32_t* flags, char* ws, hipStream_t s) {
   using C = Cfg<DK, DV>;
   constexpr int state_bytes = C::off_qh;  // the state pass uses the small tables, V and Kbar
   static bool attr_set = false;
@@ -1181,12 +1195,13 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   if (L.states_max > 0) {
     hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true>), dim3(grid), dim3(C::NT), state_bytes, s,
                        qp, kp, vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale,
-                       static_cast<bf16*>(nullptr), static_cast<float*>(nullptr), states, decays, 0);
+                       static_cast<const float*>(nullptr), static_cast<bf16*>(nullptr),
+                       static_cast<float*>(nullptr), states, decays, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false>), dim3(grid), dim3(C::NT), C::bytes, s, qp, kp,
-                     vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale,
+                     vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale, s0,
                      static_cast<bf16*>(o), fs, states, decays, 0);
   return hipGetLastError();
 }
@@ -1205,18 +1220,18 @@ size_t kda_chunk_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, i
 
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
-                            int32_t H, int32_t Dk, int32_t Dv, float scale, void* o,
-                            float* final_state, int32_t* flags, void* workspace,
-                            hipStream_t stream) {
+                            int32_t H, int32_t Dk, int32_t Dv, float scale,
+                            const float* initial_state, void* o, float* final_state,
+                            int32_t* flags, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   if (Dk == 128 && Dv == 128)
-    return launch_dims<128, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, ws, stream);
+    return launch_dims<128, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, stream);
   if (Dk == 64 && Dv == 64)
-    return launch_dims<64, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, ws, stream);
+    return launch_dims<64, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, stream);
   if (Dk == 128 && Dv == 64)
-    return launch_dims<128, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, ws, stream);
+    return launch_dims<128, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, stream);
   if (Dk == 64 && Dv == 128)
-    return launch_dims<64, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state, flags, ws, stream);
+    return launch_dims<64, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, stream);
   return hipErrorInvalidValue;
 }
 

@@ -29,8 +29,8 @@ template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, const int32_t* __restrict__ cu,
-    int32_t max_segs, int64_t N, int32_t H, float scale, T* __restrict__ o,
-    float* __restrict__ final_state, int32_t* __restrict__ flags) {
+    int32_t max_segs, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
+    T* __restrict__ o, float* __restrict__ final_state, int32_t* __restrict__ flags) {
   constexpr int RG = kThreads / DV;  // row groups
   constexpr int R = DK / RG;         // consecutive rows per thread
   static_assert(RG * DV == kThreads && R * RG == DK, "bad tile");
@@ -72,9 +72,11 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
   const int e = tid % DV;
   const int rg = tid / DV;
   const int d0 = rg * R;
+  // the segment's recurrence starts from its initial state (zero if none)
   float S[R];
+  const float* s0 = initial_state ? initial_state + (int64_t(slot) * H + h) * DK * DV : nullptr;
 #pragma unroll
-  for (int r = 0; r < R; ++r) S[r] = 0.f;
+  for (int r = 0; r < R; ++r) S[r] = s0 ? s0[int64_t(d0 + r) * DV + e] : 0.f;
 
   for (int64_t t0 = start; t0 < end; t0 += kTB) {
     const int nt = (end - t0) < kTB ? int(end - t0) : kTB;
@@ -123,13 +125,13 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
 template <typename T, int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
-                       int32_t H, float scale, void* o, float* fs, int32_t* flags,
-                       hipStream_t s) {
+                       int32_t H, float scale, const float* s0, void* o, float* fs,
+                       int32_t* flags, hipStream_t s) {
   const int64_t blocks = int64_t(max_segs) * H + kTailBlocks;
   hipLaunchKernelGGL((kda_serial_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(kThreads), 0, s,
                      static_cast<const T*>(q), static_cast<const T*>(k),
                      static_cast<const T*>(v), static_cast<const T*>(g),
-                     static_cast<const T*>(beta), cu, max_segs, N, H, scale,
+                     static_cast<const T*>(beta), cu, max_segs, N, H, scale, s0,
                      static_cast<T*>(o), fs, flags);
   return hipGetLastError();
 }
@@ -137,11 +139,12 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
 template <typename T, int DK>
 hipError_t launch_dv(int32_t Dv, const void* q, const void* k, const void* v, const void* g,
                      const void* beta, const int32_t* cu, int32_t max_segs, int64_t N, int32_t H,
-                     float scale, void* o, float* fs, int32_t* flags, hipStream_t s) {
+                     float scale, const float* s0, void* o, float* fs, int32_t* flags,
+                     hipStream_t s) {
   switch (Dv) {
-    case 32: return launch_dims<T, DK, 32>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, fs, flags, s);
-    case 64: return launch_dims<T, DK, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, fs, flags, s);
-    case 128: return launch_dims<T, DK, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, o, fs, flags, s);
+    case 32: return launch_dims<T, DK, 32>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
+    case 64: return launch_dims<T, DK, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
+    case 128: return launch_dims<T, DK, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
   }
   return hipErrorInvalidValue;
 }
@@ -149,12 +152,12 @@ hipError_t launch_dv(int32_t Dv, const void* q, const void* k, const void* v, co
 template <typename T>
 hipError_t launch_dk(int32_t Dk, int32_t Dv, const void* q, const void* k, const void* v,
                      const void* g, const void* beta, const int32_t* cu, int32_t max_segs,
-                     int64_t N, int32_t H, float scale, void* o, float* fs, int32_t* flags,
-                     hipStream_t s) {
+                     int64_t N, int32_t H, float scale, const float* s0, void* o, float* fs,
+                     int32_t* flags, hipStream_t s) {
   switch (Dk) {
-    case 32: return launch_dv<T, 32>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, o, fs, flags, s);
-    case 64: return launch_dv<T, 64>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, o, fs, flags, s);
-    case 128: return launch_dv<T, 128>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, o, fs, flags, s);
+    case 32: return launch_dv<T, 32>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
+    case 64: return launch_dv<T, 64>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
+    case 128: return launch_dv<T, 128>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
   }
   return hipErrorInvalidValue;
 }
@@ -164,12 +167,13 @@ hipError_t launch_dk(int32_t Dk, int32_t Dv, const void* q, const void* k, const
 hipError_t launch_kda_serial(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                              int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
-                             void* o, float* final_state, int32_t* flags, hipStream_t stream) {
+                             const float* initial_state, void* o, float* final_state,
+                             int32_t* flags, hipStream_t stream) {
   if (dtype == 0)
-    return launch_dk<bf16>(Dk, Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state,
-                           flags, stream);
-  return launch_dk<float>(Dk, Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, o, final_state,
-                          flags, stream);
+    return launch_dk<bf16>(Dk, Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o,
+                           final_state, flags, stream);
+  return launch_dk<float>(Dk, Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o,
+                          final_state, flags, stream);
 }
 
 }  // namespace pkv

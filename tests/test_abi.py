@@ -29,13 +29,13 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 6, names
+    assert len(names) == 7, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
     for code, name in [(0, b"PKV_OK"), (1, b"PKV_ERR_INVALID_ARGUMENT"), (2, b"PKV_ERR_UNSUPPORTED"),
                        (3, b"PKV_ERR_WORKSPACE"), (4, b"PKV_ERR_HIP"), (99, b"PKV_ERR_UNKNOWN")]:
         assert lib.pkv_status_string(code) == name
@@ -72,10 +72,23 @@ def test_short_conv_validation(lib, args, code):
     assert lib.pkv_short_conv_segmask(*args) == code
 
 
+@pytest.mark.parametrize("args,code", [
+    ((NUL, 2, 8, 0, Q, NUL, NUL, NUL), 1),                 # no tokens
+    ((P, 2, 8, 0, NUL, NUL, NUL, NUL), 1),                 # no segment_ids
+    ((P, 0, 8, 0, Q, NUL, NUL, NUL), 1),                   # B < 1
+    ((P, 2, 0, 0, Q, NUL, NUL, NUL), 1),                   # T < 1
+    ((P, 1 << 16, 1 << 16, 0, Q, NUL, NUL, NUL), 1),       # B*T > INT32_MAX
+    ((P, 2, 8, 0, P, NUL, NUL, NUL), 1),                   # segment_ids overlaps tokens
+    ((P, 2, 8, 0, Q, Q, NUL, NUL), 1),                     # positions overlaps segment_ids
+])
+def test_eod_validation(lib, args, code):
+    assert lib.pkv_eod_to_segment_ids(*args) == code
+
+
 def _kda_args(**kw):
     base = dict(q=ctypes.c_void_p(0x10000000), k=ctypes.c_void_p(0x20000000), v=ctypes.c_void_p(0x30000000),
                 g=ctypes.c_void_p(0x40000000), beta=ctypes.c_void_p(0x50000000), cu=P, max_segs=4, N=256,
-                H=2, Dk=64, Dv=64, scale=1.0, dtype=0, o=ctypes.c_void_p(0x60000000), fs=NUL, flags=NUL,
+                H=2, Dk=64, Dv=64, scale=1.0, dtype=0, s0=NUL, o=ctypes.c_void_p(0x60000000), fs=NUL, flags=NUL,
                 ws=NUL, ws_bytes=0, stream=NUL)
     base.update(kw)
     return tuple(base.values())
@@ -89,6 +102,8 @@ def _kda_args(**kw):
     (dict(o=ctypes.c_void_p(0x60000008)), 1),         # o not 16-byte aligned
     (dict(k=ctypes.c_void_p(0x20000002)), 1),         # k not 16-byte aligned
     (dict(beta=ctypes.c_void_p(0x50000001)), 1),      # beta not element-aligned
+    (dict(s0=ctypes.c_void_p(0x70000004)), 1),        # initial_state not 16-byte aligned
+    (dict(s0=ctypes.c_void_p(0x70000000), fs=ctypes.c_void_p(0x70000000 + 4096)), 1),  # initial overlaps final
 ])
 def test_chunk_kda_validation(lib, kw, code):
     args = _kda_args(**kw)

@@ -301,3 +301,59 @@ def test_long_segments_cut_into_runs(case, H, Dk, Dv, lens, slots, runs, pieces)
         assert np.linalg.norm(alone - ro[ra:re]) > 0.2 * np.linalg.norm(ro[ra:re])
     if cu is not None:
         assert torch.count_nonzero(o[0, int(cu[-1]):]).item() == 0
+
+
+# RFC-0026 section 3.3's initial_state, one per segment slot: every segment
+# starts from its slot's state; empty slots keep it as their final state.
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("Dk,Dv", [(32, 32), (64, 64), (128, 128), (64, 128), (128, 64)])
+def test_initial_state(dtype, Dk, Dv):
+    pkv = _pkv()
+    rng = np.random.default_rng(Dk * 7 + Dv)
+    lens = [70, 0, 1, 200, 64]
+    real = np.concatenate([[0], np.cumsum(lens)])
+    cu = np.concatenate([real, [real[-1]] * 2])  # two phantom slots
+    N, H = int(real[-1]) + 9, 2
+    ts = _small_case(rng, N, H, Dk, Dv, dtype, cu)
+    S0 = rng.standard_normal((len(cu) - 1, H, Dk, Dv)) * 0.5
+    q, k, v, g, beta = [t.to(device())[None] for t in ts]
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    s0 = torch.from_numpy(S0).to(torch.float32).to(device())
+    print(f"initial_state dtype {dtype} Dk {Dk} Dv {Dv}", flush=True)
+    o, fs = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, initial_state=s0, scale=0.8)
+    torch.cuda.synchronize()
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], cu, scale=0.8, initial_state=S0)
+    dt = "f32" if dtype == torch.float32 else "bf16"
+    check_close(f64(o[0]), ro, dt, "o")
+    for i in range(len(cu) - 1):
+        check_close(f64(fs[i]), rfs[i], dt, f"state {i}")
+    assert torch.equal(fs[1], s0[1]) and torch.equal(fs[-1], s0[-1])  # empty slots keep it
+    assert torch.count_nonzero(o[0, int(cu[-1]):]).item() == 0
+
+
+def test_initial_state_with_cut_segments():
+    """A long segment cut into runs: the first run starts from the initial
+    state and the later ones fold it in through the composition."""
+    pkv = _pkv()
+    rng = np.random.default_rng(77)
+    N, H, D = 5000, 2, 64
+    q = rng.standard_normal((N, H, D)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((N, H, D)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((N, H, D))
+    g = -rng.uniform(0.00001, 0.0005, (N, H, D))  # slow: the initial state lasts the whole segment
+    beta = 1 / (1 + np.exp(-rng.standard_normal((N, H))))
+    ts = [torch.from_numpy(a).to(torch.bfloat16) for a in (q, k, v, g, beta)]
+    S0 = rng.standard_normal((1, H, D, D)) * 2.0
+    dq, dk, dv, dg, db = [t.to(device())[None] for t in ts]
+    ws = torch.empty(pkv.chunk_kda_varlen_workspace_size(N, H, D, D, 1, torch.bfloat16),
+                     dtype=torch.uint8, device=device())
+    o, fs = pkv.chunk_kda_varlen(dq, dk, dv, dg, db, None, workspace=ws,
+                                 initial_state=torch.from_numpy(S0).float().to(device()))
+    torch.cuda.synchronize()
+    assert ws[:8].view(torch.int32).cpu().tolist()[1] == 2  # 79 chunks: three runs, two saved pieces
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], None, initial_state=S0)
+    check_close(f64(o[0]), ro, "bf16", "o")
+    check_close(f64(fs), rfs, "bf16", "final state")
+    # the initial state matters for the last run's outputs (chunks 53..78)
+    r0, _ = oracle.chunk_kda_varlen(*[f64(t) for t in ts], None)
+    assert np.linalg.norm(ro[3400:] - r0[3400:]) > 0.2 * np.linalg.norm(ro[3400:])
