@@ -16,7 +16,8 @@ Sources (the pages; cited by title and section):
 * "Drill: Sequence Packing from scratch" (ac.fzhiy.net), section "The math"
   (cu_seqlens, doc(s), block-diagonal mask).
 * RFC-0026, section 6 (data pipeline alignment: EOD segmentation, positions,
-  loss mask) and section 3.3 (the wrapper's ``initial_state``).
+  loss mask), section 3.3 (the wrapper's ``initial_state``) and section 3.1.1's
+  [B, T] ``segment_ids`` contract (reset where the id changes or a row starts).
 
 Functions and their pin status (every function is pinned; see tests/):
 
@@ -32,6 +33,9 @@ Functions and their pin status (every function is pinned; see tests/):
                                     segments, gate injection, invariants;
                                     initial states: decayed closed form,
                                     split-and-resume identity
+``chunk_kda_segment_ids``           pinned: gate injection (g = -inf at each
+                                    segment start, RFC-0026 Alternatives),
+                                    hand-derived two-row case, padding runs
 ``eod_to_segment_ids``              pinned: hand-derived rows, construction
                                     from document lengths
 ==================================  =========================================
@@ -39,7 +43,7 @@ Functions and their pin status (every function is pinned; see tests/):
 
 from .cu_seqlens import segment_ids_to_cu_seqlens, token_segment, FLAG_OVERFLOW, FLAG_LEADING_PAD
 from .short_conv import short_conv_segmask
-from .kda import chunk_kda_varlen
+from .kda import chunk_kda_varlen, chunk_kda_segment_ids
 from .eod import eod_to_segment_ids
 
 __all__ = [
@@ -47,6 +51,7 @@ __all__ = [
     "token_segment",
     "short_conv_segmask",
     "chunk_kda_varlen",
+    "chunk_kda_segment_ids",
     "eod_to_segment_ids",
     "FLAG_OVERFLOW",
     "FLAG_LEADING_PAD",

@@ -78,3 +78,38 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state
             o[t] = scale * np.einsum("hde,hd->he", S, q[t])
         final_state[i] = S
     return o, final_state
+
+
+def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, initial_state=None):
+    """The [B, T] segment_ids contract of RFC-0026 section 3.1.1, row by row.
+
+    q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H]; segment_ids: int
+    [B, T]; initial_state: [B, H, Dk, Dv] or None. The state is cleared where
+    segment_ids[b, t] != segment_ids[b, t - 1] and at t = 0 of every row (rows
+    never share state); id 0 (padding) is an id like any other. The first
+    segment of row b starts from initial_state[b] (section 3.3's per-row
+    shape), later ones from zero. Returns (o [B, T, H, Dv], final_state
+    [B, H, Dk, Dv]): the state after each row's last position.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    seg = np.asarray(segment_ids)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    if seg.shape != (B, T):
+        raise ValueError(f"segment_ids has shape {seg.shape}")
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    final_state = np.zeros((B, H, Dk, Dv), dtype=np.float64)
+    for b in range(B):
+        S = np.zeros((H, Dk, Dv)) if initial_state is None else np.array(initial_state[b], dtype=np.float64)
+        for t in range(T):
+            if t > 0 and seg[b, t] != seg[b, t - 1]:
+                S = np.zeros((H, Dk, Dv))  # a new segment: the state is cleared
+            decay = np.exp(g[b, t])[:, :, None]
+            S = decay * S + beta[b, t][:, None, None] * k[b, t][:, :, None] * v[b, t][:, None, :]
+            o[b, t] = scale * np.einsum("hde,hd->he", S, q[b, t])
+        final_state[b] = S
+    return o, final_state

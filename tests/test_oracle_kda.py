@@ -239,3 +239,40 @@ def test_split_and_resume_equals_whole_segment():
                                          initial_state=fa)
         np.testing.assert_allclose(np.concatenate([oa, ob]), ow, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(fb, fw, rtol=1e-12, atol=1e-12)
+
+
+def test_segment_ids_contract_is_gate_injection_per_row():
+    """RFC-0026 section 3.1.1's [B, T] contract (clear the state where the id
+    changes and at every row start; id 0 is an id like any other) equals, row
+    by row, one continuous run with g = -inf at each segment start (RFC-0026
+    Alternatives, gate injection); the first segment keeps the row's initial
+    state and the row's final state is the last segment's."""
+    rng = np.random.default_rng(41)
+    B, T, H, Dk, Dv = 3, 40, 2, 3, 4
+    q, k, v, g, beta = [a.reshape((B, T) + a.shape[1:]) for a in _rand_inputs(rng, B * T, H, Dk, Dv)]
+    seg = np.array([[1] * 10 + [2] * 5 + [0] * 3 + [3] * 22,
+                    [0] * 4 + [1] * 36,
+                    [5] * 40])
+    S0 = rng.standard_normal((B, H, Dk, Dv))
+    o, fs = oracle.chunk_kda_segment_ids(q, k, v, g, beta, seg, scale=0.9, initial_state=S0)
+    for b in range(B):
+        g2 = g[b].copy()
+        for t in range(1, T):
+            if seg[b, t] != seg[b, t - 1]:
+                g2[t] = -np.inf
+        o2, f2 = oracle.chunk_kda_varlen(q[b], k[b], v[b], g2, beta[b], None, scale=0.9,
+                                         initial_state=S0[b:b + 1])
+        assert np.array_equal(o[b], o2)
+        assert np.array_equal(fs[b], f2[0])
+
+
+def test_segment_ids_contract_hand_case():
+    """Dk = Dv = 1, q = k = v = beta = 1, g = 0: the state counts the tokens of
+    the current segment (plus the row's initial state in its first segment)."""
+    seg = np.array([[1, 1, 2, 2, 2], [0, 0, 3, 3, 0]])
+    one = np.ones((2, 5, 1, 1))
+    o, fs = oracle.chunk_kda_segment_ids(one, one, one, np.zeros((2, 5, 1, 1)), np.ones((2, 5, 1)), seg,
+                                         initial_state=np.array([[[[5.0]]], [[[0.0]]]]))
+    assert o[0, :, 0, 0].tolist() == [6, 7, 1, 2, 3]
+    assert o[1, :, 0, 0].tolist() == [1, 2, 1, 2, 1]
+    assert fs[:, 0, 0, 0].tolist() == [3, 1]
