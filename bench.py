@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="oracle sample size in tokens (0: sized for ~15 s of CPU work)")
     p.add_argument("--mode", choices=["bench", "kernel", "copy"], default="bench")
+    p.add_argument("--entry", choices=["cu_seqlens", "segment_ids"], default="cu_seqlens",
+                   help="segment_ids: the step is one pkv_chunk_kda_segment_ids call on the [B, T] ids "
+                        "(no conversion, no phantom slots) instead of the conversion + chunk_kda_varlen")
     return p.parse_args()
 
 
@@ -204,7 +207,24 @@ def main():
         log(f"kernel mode: {args.warmup + args.steps} launches of {DOMINANT_KERNEL}")
         return
 
+    if args.entry == "segment_ids":
+        B, T = cfg.B, cfg.T
+        qb, kb, gb = (t.view(B, T, H, cfg.Dk) for t in (q, k, g))
+        vb, ob, betab = v.view(B, T, H, cfg.Dv), o.view(B, T, H, cfg.Dv), beta.view(B, T, H)
+        ws_ids = torch.empty(pkv.chunk_kda_segment_ids_workspace_size(B, T, H, cfg.Dk, cfg.Dv, q.dtype),
+                             dtype=torch.uint8, device=dev)
+
     def step(ev=None):
+        if args.entry == "segment_ids":
+            if conv_x is not None:
+                pkv.short_conv_segmask(conv_x, conv_w, seg, out=conv_y)
+            if ev is not None:
+                ev[0].record()
+            out = pkv.chunk_kda_segment_ids(qb, kb, vb, gb, betab, seg, output_final_state=final_state,
+                                            flags=flags, out=ob, workspace=ws_ids)
+            if ev is not None:
+                ev[1].record()
+            return out
         r = pkv.segment_ids_to_cu_seqlens(seg, cfg.max_segs)
         if conv_x is not None:
             pkv.short_conv_segmask(conv_x, conv_w, seg, out=conv_y)
@@ -238,7 +258,7 @@ def main():
     achieved = alg_bytes / kc_avg_s / 1e9
     flops = algorithmic_flops(cfg, cu_host)
     mfma_frac = flops / kc_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS
-    traffic = read_traffic(cfg.name)
+    traffic = read_traffic(cfg.name) if args.entry == "cu_seqlens" else None
     log(f"step {ms:.3f} ms; {DOMINANT_KERNEL} {kc_avg_s * 1e6:.1f} us avg "
         f"(min {min(kc_ms) * 1e3:.1f} max {max(kc_ms) * 1e3:.1f}); {achieved:.0f} GB/s "
         f"= {achieved / HBM_PEAK_GBS:.3f} of HBM peak; MFMA {mfma_frac:.4f} of bf16 peak; "
@@ -266,12 +286,14 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "N": N, "H": H, "Dk": cfg.Dk,
                    "Dv": cfg.Dv, "max_segs": cfg.max_segs, "n_segs": n_segs,
                    "output_final_state": final_state, "short_conv": conv_x is not None,
-                   "step": "segment_ids_to_cu_seqlens" + (" + short_conv_segmask" if conv_x is not None else "")
-                           + " + chunk_kda_varlen"},
+                   "step": ("chunk_kda_segment_ids" if args.entry == "segment_ids" else
+                            "segment_ids_to_cu_seqlens" + (" + short_conv_segmask" if conv_x is not None else "")
+                            + " + chunk_kda_varlen")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": DOMINANT_KERNEL, "kernel_avg_us": kc_avg_s * 1e6,
+                     "kernel": DOMINANT_KERNEL if args.entry == "cu_seqlens" else "chunk_kda_segment_ids",
+                     "kernel_avg_us": kc_avg_s * 1e6,
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "mfma_frac_bf16": mfma_frac},
         "cpu_baseline": cpu,

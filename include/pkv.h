@@ -22,6 +22,11 @@
  *                                  positions and loss segment ids
  *       RFC-0026, section 6 (data pipeline alignment).
  *
+ * and the kernel contract that takes segment ids directly:
+ *
+ *   pkv_chunk_kda_segment_ids      the recurrence with [B, T] segment_ids
+ *       RFC-0026, section 3.1.1 (kernel contract) and Alternatives (Alt1).
+ *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer (HIP device memory or memory the
  *     GPU can address). Scalars are passed by value.
@@ -199,6 +204,36 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
                                 int32_t dtype, const float* initial_state, void* o,
                                 float* final_state, int32_t* flags, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Packed KDA straight from [B, T] segment ids (RFC-0026 section 3.1.1's
+ * kernel contract), with no cu_seqlens round trip and no phantom slots.
+ *
+ * For every row b and head h the recurrence of pkv_chunk_kda_varlen runs over
+ * the row, and the state is cleared at t = 0 and wherever
+ * segment_ids[b, t] != segment_ids[b, t-1] (id 0, padding, is an id like any
+ * other: a run of padding is a segment of its own). The row's first segment
+ * starts from initial_state[b, h] (0 when initial_state is NULL);
+ * final_state[b, h] is the state after the row's last position (section 3.3's
+ * per-row shapes). Rows never share state.
+ *
+ * q, k, g     [B, T, H, Dk]; v [B, T, H, Dv]; beta [B, T, H]; o [B, T, H, Dv]
+ *             (one dtype); segment_ids int32 [B, T].
+ * initial_state, final_state  float32 [B, H, Dk, Dv] or NULL; must not overlap.
+ * workspace   at least pkv_chunk_kda_segment_ids_workspace_size() bytes,
+ *             16-byte aligned; scratch, as for pkv_chunk_kda_varlen (the
+ *             segment starts found in the ids are kept there).
+ * Errors: as pkv_chunk_kda_varlen, with B*T in place of N (B*T must not
+ * exceed INT32_MAX - 8192) and no max_segs.
+ */
+size_t pkv_chunk_kda_segment_ids_workspace_size(int64_t B, int64_t T, int32_t H, int32_t Dk,
+                                                int32_t Dv, int32_t dtype);
+pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v, const void* g,
+                                     const void* beta, const int32_t* segment_ids, int64_t B,
+                                     int64_t T, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                     int32_t dtype, const float* initial_state, void* o,
+                                     float* final_state, int32_t* flags, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(int32_t status);

@@ -56,6 +56,11 @@ def _load():
     lib.pkv_chunk_kda_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32,
                                          vp, vp, vp, vp, vp, sz, vp]
     lib.pkv_chunk_kda_varlen.restype = i32
+    lib.pkv_chunk_kda_segment_ids_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32]
+    lib.pkv_chunk_kda_segment_ids_workspace_size.restype = sz
+    lib.pkv_chunk_kda_segment_ids.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, i32,
+                                              vp, vp, vp, vp, vp, sz, vp]
+    lib.pkv_chunk_kda_segment_ids.restype = i32
     lib.pkv_status_string.argtypes = [i32]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -215,4 +220,48 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_
                                     max_segs, N, H, Dk, Dv, float(scale), code, _ptr(initial_state),
                                     _ptr(o), _ptr(fs),
                                     _ptr(flags), _ptr(workspace), ws_bytes, _stream(dev)))
+    return o, fs
+
+
+def chunk_kda_segment_ids_workspace_size(B, T, H, Dk, Dv, dtype):
+    return int(_load().pkv_chunk_kda_segment_ids_workspace_size(B, T, H, Dk, Dv, _dtype_code(dtype)))
+
+
+def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, output_final_state=True,
+                          initial_state=None, flags=None, out=None, workspace=None):
+    """Packed KDA from [B, T] segment ids (reset where the id changes and at each row start).
+
+    q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H]; segment_ids: int32 [B, T];
+    initial_state: fp32 [B, H, Dk, Dv] or None (the first segment of each row starts from it).
+    Returns (o [B, T, H, Dv], final_state fp32 [B, H, Dk, Dv] (the state after each row) or None).
+    """
+    lib = _load()
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    for name, t, nd in (("q", q, 4), ("k", k, 4), ("v", v, 4), ("g", g, 4), ("beta", beta, 3)):
+        _need(t, name, dev, dt, nd)
+    _need(segment_ids, "segment_ids", dev, torch.int32, 2)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    if tuple(k.shape) != tuple(q.shape) or tuple(g.shape) != tuple(q.shape):
+        raise ValueError("q, k and g must have the same shape")
+    if tuple(v.shape[:3]) != (B, T, H) or tuple(beta.shape) != (B, T, H) or tuple(segment_ids.shape) != (B, T):
+        raise ValueError("v must be [B, T, H, Dv], beta [B, T, H] and segment_ids [B, T]")
+    o = torch.empty(B, T, H, Dv, dtype=dt, device=dev) if out is None else out
+    _need(o, "out", dev, dt, 4)
+    fs = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev) if output_final_state else None
+    if initial_state is not None:
+        _need(initial_state, "initial_state", dev, torch.float32, 4)
+        if tuple(initial_state.shape) != (B, H, Dk, Dv):
+            raise ValueError(f"initial_state must be [{B}, {H}, {Dk}, {Dv}]")
+    if flags is not None:
+        _need(flags, "flags", dev, torch.int32, 1)
+    need = int(lib.pkv_chunk_kda_segment_ids_workspace_size(B, T, H, Dk, Dv, code))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_chunk_kda_segment_ids(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(segment_ids),
+                                         B, T, H, Dk, Dv, float(scale), code, _ptr(initial_state), _ptr(o),
+                                         _ptr(fs), _ptr(flags), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, fs

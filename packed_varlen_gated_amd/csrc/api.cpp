@@ -139,4 +139,55 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t pkv_chunk_kda_segment_ids_workspace_size(int64_t B, int64_t T, int32_t H, int32_t Dk,
+                                                int32_t Dv, int32_t dtype) {
+  if (B < 1 || T < 1 || B * T > kInt32Max) return 0;
+  return pkv::kda_chunk_ids_workspace_bytes(B * T, H, Dk, Dv, dtype);
+}
+
+pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v, const void* g,
+                                     const void* beta, const int32_t* segment_ids, int64_t B,
+                                     int64_t T, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                     int32_t dtype, const float* initial_state, void* o,
+                                     float* final_state, int32_t* flags, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
+      o == nullptr || segment_ids == nullptr)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (B < 1 || T < 1 || B > kInt32Max || T > kInt32Max || B * T > kInt32Max - 8192 || H < 1 ||
+      H > 65536)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv))
+    return PKV_ERR_UNSUPPORTED;
+  if (B * H > (int64_t(1) << 22)) return PKV_ERR_INVALID_ARGUMENT;
+  for (const void* p : {q, k, v, g, static_cast<const void*>(o)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(beta) % elem_size(dtype) != 0 ||
+      reinterpret_cast<uintptr_t>(final_state) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(initial_state) % 16 != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t N = B * T;
+  const int64_t es = elem_size(dtype);
+  const int64_t o_bytes = N * H * Dv * es;
+  if (overlaps(o, o_bytes, q, N * H * Dk * es) || overlaps(o, o_bytes, k, N * H * Dk * es) ||
+      overlaps(o, o_bytes, v, N * H * Dv * es) || overlaps(o, o_bytes, g, N * H * Dk * es) ||
+      overlaps(o, o_bytes, beta, N * H * es) || overlaps(o, o_bytes, segment_ids, N * 4))
+    return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t state_bytes = B * H * Dk * Dv * 4;
+  if (initial_state != nullptr && final_state != nullptr &&
+      overlaps(initial_state, state_bytes, final_state, state_bytes))
+    return PKV_ERR_INVALID_ARGUMENT;
+  const size_t need = pkv_chunk_kda_segment_ids_workspace_size(B, T, H, Dk, Dv, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
+    return PKV_ERR_WORKSPACE;
+  if (pkv::kda_chunk_supported(Dk, Dv, dtype))
+    return from_hip(pkv::launch_kda_chunk_ids(q, k, v, g, beta, segment_ids, B, T, H, Dk, Dv,
+                                              scale, initial_state, o, final_state, flags,
+                                              workspace, static_cast<hipStream_t>(stream)));
+  return from_hip(pkv::launch_kda_serial_ids(q, k, v, g, beta, segment_ids, B, T, H, Dk, Dv,
+                                             scale, dtype, initial_state, o, final_state,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -28,6 +28,11 @@ hipError_t launch_cu_seqlens(const int32_t* seg, int64_t N, int64_t T, int32_t m
                              int32_t* cu, int32_t* token_seg, int32_t* n_segs, int32_t* flags,
                              hipStream_t stream);
 
+// The [B, T] contract's segment starts (every id change and row start):
+// bounds[0..n] with bounds[n] = N, n to *n_segs.
+hipError_t launch_segment_bounds(const int32_t* seg, int64_t N, int64_t T, int32_t* bounds,
+                                 int32_t* n_segs, hipStream_t stream);
+
 hipError_t launch_eod_segments(const int32_t* tokens, int64_t B, int64_t T, int32_t eod_id,
                                int32_t* seg, int32_t* pos, int32_t* loss, hipStream_t stream);
 
@@ -48,6 +53,20 @@ bool kda_chunk_supported(int32_t Dk, int32_t Dv, int32_t dtype);
 // cut segments.
 size_t kda_chunk_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
                                  int32_t max_segs);
+
+// [B, T] segment_ids entry (RFC-0026 section 3.1.1) on the chunk path.
+size_t kda_chunk_ids_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype);
+hipError_t launch_kda_chunk_ids(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta, const int32_t* seg, int64_t B, int64_t T,
+                                int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                const float* initial_state, void* o, float* final_state,
+                                int32_t* flags, void* workspace, hipStream_t stream);
+// ... and on the token-serial path (one work-group per (row, head)).
+hipError_t launch_kda_serial_ids(const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, const int32_t* seg, int64_t B, int64_t T,
+                                 int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
+                                 const float* initial_state, void* o, float* final_state,
+                                 hipStream_t stream);
 
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,

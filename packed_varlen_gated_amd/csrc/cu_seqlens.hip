@@ -67,7 +67,11 @@ __device__ __forceinline__ i32x4 load4(const int32_t* __restrict__ seg, int64_t 
   return x;
 }
 
-template <bool kVec, bool kT4>
+// kIds: the [B, T] kernel contract of RFC-0026 section 3.1.1 instead of the
+// conversion's: every id change and every row start is a boundary (id 0 is an
+// id like any other), and the last segment ends at N; cu then holds exactly
+// n + 1 entries (cu[n] = N; no phantoms, no flags, no token map).
+template <bool kVec, bool kT4, bool kIds>
 __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
     const int32_t* __restrict__ seg, int64_t N, int64_t T, int32_t max_segs,
     int32_t* __restrict__ cu, int32_t* __restrict__ token_seg, int32_t* __restrict__ n_segs_out,
@@ -135,7 +139,18 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
         prev = wid > 0 ? s_edge[j * kWaves + wid - 1]
                        : (j > 0 ? s_edge[(j - 1) * kWaves + kWaves - 1] : before_tile);
       unsigned bits;
-      if (kT4) {
+      if (kIds) {
+        bits = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t r = rp + uint32_t(i);
+          const bool row_start = kT4 ? (i == 0 && rp == 0)
+                                     : (r == 0 || r == T32 || (T32 <= 2 && (r == 2 * T32 || r == 3 * T32)));
+          const int pv = i == 0 ? prev : x[i - 1];
+          const int64_t pos = base + 4 * int64_t(m) + i;
+          if (pos < N && (row_start || x[i] != pv)) bits |= 1u << i;
+        }
+      } else if (kT4) {
         // T % 4 == 0: rows start only at a group's first position
         bits = unsigned(x[0] != 0 && (x[0] != prev || rp == 0)) |
                (unsigned(x[1] != 0 && x[1] != x[0]) << 1) |
@@ -249,6 +264,14 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
   }
 
   const int n = running;
+  if (kIds) {
+    if (tid == 0) {
+      cu[0] = 0;
+      cu[n] = static_cast<int32_t>(N);
+      if (n_segs_out != nullptr) *n_segs_out = n;
+    }
+    return;
+  }
   const int64_t e_last = last_nz + 1;
   // Slots past the scattered starts: last real end, or N for the merged slot.
   if (n > max_segs) {
@@ -276,10 +299,20 @@ hipError_t launch_cu_seqlens(const int32_t* seg, int64_t N, int64_t T, int32_t m
                              hipStream_t stream) {
   const bool vec = (reinterpret_cast<uintptr_t>(seg) % 16 == 0) &&
                    (token_seg == nullptr || reinterpret_cast<uintptr_t>(token_seg) % 16 == 0);
-  auto kernel = vec ? (T % 4 == 0 ? cu_seqlens_kernel<true, true> : cu_seqlens_kernel<true, false>)
-                    : (T % 4 == 0 ? cu_seqlens_kernel<false, true> : cu_seqlens_kernel<false, false>);
+  auto kernel = vec ? (T % 4 == 0 ? cu_seqlens_kernel<true, true, false> : cu_seqlens_kernel<true, false, false>)
+                    : (T % 4 == 0 ? cu_seqlens_kernel<false, true, false> : cu_seqlens_kernel<false, false, false>);
   hipLaunchKernelGGL(kernel, dim3(1), dim3(kThreads), 0, stream, seg, N, T, max_segs, cu, token_seg,
                      n_segs, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_bounds(const int32_t* seg, int64_t N, int64_t T, int32_t* bounds,
+                                 int32_t* n_segs, hipStream_t stream) {
+  const bool vec = reinterpret_cast<uintptr_t>(seg) % 16 == 0;
+  auto kernel = vec ? (T % 4 == 0 ? cu_seqlens_kernel<true, true, true> : cu_seqlens_kernel<true, false, true>)
+                    : (T % 4 == 0 ? cu_seqlens_kernel<false, true, true> : cu_seqlens_kernel<false, false, true>);
+  hipLaunchKernelGGL(kernel, dim3(1), dim3(kThreads), 0, stream, seg, N, T, int32_t(N), bounds,
+                     static_cast<int32_t*>(nullptr), n_segs, static_cast<int32_t*>(nullptr));
   return hipGetLastError();
 }
 

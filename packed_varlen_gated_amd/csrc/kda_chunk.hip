@@ -259,7 +259,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     int32_t* __restrict__ plan, int32_t runs_max, int32_t max_segs, int64_t N,
     int32_t H, float scale, const float* __restrict__ initial_state, bf16* __restrict__ o,
     float* __restrict__ final_state, float* __restrict__ run_states,
-    float* __restrict__ run_decays, int32_t lds_zero) {
+    float* __restrict__ run_decays, int64_t row_len, int32_t lds_zero) {
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
   constexpr int PCPL = C::PCPL, PVPL = C::PVPL, ET = C::ET, DT = C::DT, KS = C::KS;
@@ -857,8 +857,17 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         // piece of a cut segment then folds in the pieces before it:
         // S = D_j S + L_j over them in order (D_j, L_j: piece j's decay
         // product and its state from zero).
-        if (initial_state != nullptr) {
-          const float* s0 = initial_state + (int64_t(slot) * H + h) * DK * DV;
+        // Slot-indexed states; with row_len > 0 (segments from a [B, T] id
+        // scan) they are row-indexed: a row's first segment starts from its
+        // row's state and its last one writes the row's final state.
+        int64_t init_idx = slot, fin_idx = slot;
+        if (row_len > 0) {
+          const int64_t a = cu[slot], e = cu[slot + 1];
+          init_idx = a % row_len == 0 ? a / row_len : -1;
+          fin_idx = e % row_len == 0 ? e / row_len - 1 : -1;
+        }
+        if (initial_state != nullptr && init_idx >= 0) {
+          const float* s0 = initial_state + (init_idx * H + h) * DK * DV;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -901,8 +910,8 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
           }
           __syncthreads();
         }
-        if (final_state != nullptr && last) {
-          float* fs = final_state + (int64_t(slot) * H + h) * DK * DV;
+        if (final_state != nullptr && last && fin_idx >= 0) {
+          float* fs = final_state + (fin_idx * H + h) * DK * DV;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -922,7 +931,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     // states of empty (and malformed) slots: their initial states, or zero;
     // grid-strided, 16-byte accesses.
     const int64_t G = gridDim.x;
-    int64_t cu_last = cu ? int64_t(cu[max_segs]) : N;
+    int64_t cu_last = (cu && row_len == 0) ? int64_t(cu[max_segs]) : N;
     cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
     const int64_t n16 = (N - cu_last) * H * DV / 8;  // DV * 2 bytes is a multiple of 16
     u32x4* o16 = reinterpret_cast<u32x4*>(o + cu_last * H * DV);
@@ -999,7 +1008,8 @@ __device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* __restrict__ cu,
-                                                                int32_t max_segs, int32_t N,
+                                                                const int32_t* __restrict__ n_dev,
+                                                                int32_t max_segs_arg, int32_t N,
                                                                 int32_t H, int32_t states_max,
                                                                 int32_t runs_max,
                                                                 int32_t* __restrict__ plan,
@@ -1010,6 +1020,8 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   __shared__ unsigned long long s_total;
   __shared__ int s_n[kPlanCache];  // chunk counts, when max_segs <= kPlanCache
   const int tid = threadIdx.x;
+  // segment slots: the caller's count, or the one a boundary scan left on the device
+  const int max_segs = n_dev != nullptr ? *n_dev : max_segs_arg;
   const int states_word_off = kPlanHeader + 8 * runs_max;
   const bool cached = max_segs <= kPlanCache;
   for (int i = tid; i < kHistBins; i += kPlanThreads) s_hr[i] = s_hs[i] = 0;
@@ -1162,11 +1174,16 @@ int device_cus() {
   return cus[dev];
 }
 
+// The plan, the state pass and the forward pass over segments given by cu
+// (max_segs slots), or, with n_dev, by the first *n_dev + 1 entries of cu that
+// a boundary scan wrote (layout_segs bounds their number; row_len > 0 then
+// maps segments to rows for the initial and final states).
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
-                       const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
-                       int32_t H, float scale, const float* s0, void* o, float* fs,
-                       int32_t* flags, char* ws, hipStream_t s) {
+                       const void* beta, const int32_t* cu, const int32_t* n_dev,
+                       int32_t layout_segs, int32_t max_segs, int64_t N, int32_t H, float scale,
+                       const float* s0, void* o, float* fs, int32_t* flags, char* ws,
+                       int64_t row_len, hipStream_t s) {
   using C = Cfg<DK, DV>;
   constexpr int state_bytes = C::off_qh;  // the state pass uses the small tables, V and Kbar
   static bool attr_set = false;
@@ -1179,12 +1196,12 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const PlanLayout L = plan_layout(N, H, DK, DV, max_segs);
+  const PlanLayout L = plan_layout(N, H, DK, DV, layout_segs);
   int32_t* plan = reinterpret_cast<int32_t*>(ws);
   float* states = reinterpret_cast<float*>(ws + L.off_L);
   float* decays = reinterpret_cast<float*>(ws + L.off_D);
-  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, max_segs, int32_t(N), H,
-                     int32_t(L.states_max), int32_t(L.runs_max), plan, flags);
+  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, n_dev, max_segs,
+                     int32_t(N), H, int32_t(L.states_max), int32_t(L.runs_max), plan, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const auto qp = static_cast<const bf16*>(q), kp = static_cast<const bf16*>(k);
@@ -1196,13 +1213,13 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
     hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true>), dim3(grid), dim3(C::NT), state_bytes, s,
                        qp, kp, vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale,
                        static_cast<const float*>(nullptr), static_cast<bf16*>(nullptr),
-                       static_cast<float*>(nullptr), states, decays, 0);
+                       static_cast<float*>(nullptr), states, decays, row_len, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false>), dim3(grid), dim3(C::NT), C::bytes, s, qp, kp,
                      vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale, s0,
-                     static_cast<bf16*>(o), fs, states, decays, 0);
+                     static_cast<bf16*>(o), fs, states, decays, row_len, 0);
   return hipGetLastError();
 }
 
@@ -1218,6 +1235,40 @@ size_t kda_chunk_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, i
   return plan_layout(N, H, Dk, Dv, max_segs).bytes;
 }
 
+// [B, T] ids path: the segment count word and bounds (N + 1 int32) first,
+// then the plan's layout for at most N segments.
+size_t ids_bounds_bytes(int64_t N) { return (size_t(N) * 4 + 4 + 256 + 255) / 256 * 256; }
+
+size_t kda_chunk_ids_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype) {
+  if (!kda_chunk_supported(Dk, Dv, dtype) || N < 1 || H < 1) return 0;
+  return ids_bounds_bytes(N) + plan_layout(N, H, Dk, Dv, int32_t(N)).bytes;
+}
+
+hipError_t launch_kda_chunk_ids(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta, const int32_t* seg, int64_t B, int64_t T,
+                                int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                const float* initial_state, void* o, float* final_state,
+                                int32_t* flags, void* workspace, hipStream_t stream) {
+  const int64_t N = B * T;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* n_dev = reinterpret_cast<int32_t*>(ws);
+  int32_t* bounds = reinterpret_cast<int32_t*>(ws + 256);
+  char* wp = ws + ids_bounds_bytes(N);
+  // segment starts of the [B, T] contract, found by the conversion's scan
+  const hipError_t e = launch_segment_bounds(seg, N, T, bounds, n_dev, stream);
+  if (e != hipSuccess) return e;
+  const int32_t S = int32_t(N);
+  if (Dk == 128 && Dv == 128)
+    return launch_dims<128, 128>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, stream);
+  if (Dk == 64 && Dv == 64)
+    return launch_dims<64, 64>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, stream);
+  if (Dk == 128 && Dv == 64)
+    return launch_dims<128, 64>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, stream);
+  if (Dk == 64 && Dv == 128)
+    return launch_dims<64, 128>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                             int32_t H, int32_t Dk, int32_t Dv, float scale,
@@ -1225,13 +1276,13 @@ hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const v
                             int32_t* flags, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   if (Dk == 128 && Dv == 128)
-    return launch_dims<128, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, stream);
+    return launch_dims<128, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, stream);
   if (Dk == 64 && Dv == 64)
-    return launch_dims<64, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, stream);
+    return launch_dims<64, 64>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, stream);
   if (Dk == 128 && Dv == 64)
-    return launch_dims<128, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, stream);
+    return launch_dims<128, 64>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, stream);
   if (Dk == 64 && Dv == 128)
-    return launch_dims<64, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, stream);
+    return launch_dims<64, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, stream);
   return hipErrorInvalidValue;
 }
 

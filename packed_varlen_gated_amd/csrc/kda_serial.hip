@@ -15,6 +15,11 @@
 // the chunked MFMA kernel.
 //
 // Extra work-groups past max_segs*H zero o for positions >= cu[max_segs].
+//
+// With seg_ids (the [B, T] contract of RFC-0026 section 3.1.1) a work-group
+// takes one (row, head) instead of a slot: the state is cleared where the id
+// changes, by a zero decay for that token (as gate injection does), and the
+// initial and final states are the row's.
 
 #include "common.h"
 
@@ -30,7 +35,8 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, const int32_t* __restrict__ cu,
     int32_t max_segs, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
-    T* __restrict__ o, float* __restrict__ final_state, int32_t* __restrict__ flags) {
+    T* __restrict__ o, float* __restrict__ final_state, int32_t* __restrict__ flags,
+    const int32_t* __restrict__ seg_ids, int64_t row_len) {
   constexpr int RG = kThreads / DV;  // row groups
   constexpr int R = DK / RG;         // consecutive rows per thread
   static_assert(RG * DV == kThreads && R * RG == DK, "bad tile");
@@ -39,6 +45,7 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
   __shared__ float s_a[kTB][DK];
   __shared__ float s_v[kTB][DV];
   __shared__ float s_b[kTB];
+  __shared__ int s_rst[kTB];
   __shared__ float s_part[kTB][RG][DV];
 
   const int tid = threadIdx.x;
@@ -59,7 +66,10 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
   const int slot = int(blockIdx.x / H);
   const int h = int(blockIdx.x % H);
   int64_t start = 0, end = N;
-  if (cu != nullptr) {
+  if (seg_ids != nullptr) {
+    start = int64_t(slot) * row_len;
+    end = start + row_len;
+  } else if (cu != nullptr) {
     start = cu[slot];
     end = cu[slot + 1];
     const bool bad = start < 0 || end < start || end > N || (slot == 0 && start != 0);
@@ -92,15 +102,20 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
       const int tt = i / DV, ee = i % DV;
       s_v[tt][ee] = to_f32(v[((t0 + tt) * H + h) * DV + ee]);
     }
-    if (tid < nt) s_b[tid] = to_f32(beta[(t0 + tid) * H + h]);
+    if (tid < nt) {
+      s_b[tid] = to_f32(beta[(t0 + tid) * H + h]);
+      const int64_t t = t0 + tid;
+      s_rst[tid] = seg_ids != nullptr && t > start && seg_ids[t] != seg_ids[t - 1];
+    }
     __syncthreads();
     for (int tt = 0; tt < nt; ++tt) {
       const float bv = s_b[tt] * s_v[tt][e];
+      const bool rst = s_rst[tt] != 0;  // a new segment: nothing carries over
       float acc = 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int d = d0 + r;
-        S[r] = fmaf(s_a[tt][d], S[r], s_k[tt][d] * bv);
+        S[r] = fmaf(rst ? 0.f : s_a[tt][d], S[r], s_k[tt][d] * bv);
         acc = fmaf(S[r], s_q[tt][d], acc);
       }
       s_part[tt][rg][e] = acc;
@@ -126,13 +141,13 @@ template <typename T, int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                        int32_t H, float scale, const float* s0, void* o, float* fs,
-                       int32_t* flags, hipStream_t s) {
+                       int32_t* flags, const int32_t* seg_ids, int64_t row_len, hipStream_t s) {
   const int64_t blocks = int64_t(max_segs) * H + kTailBlocks;
   hipLaunchKernelGGL((kda_serial_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(kThreads), 0, s,
                      static_cast<const T*>(q), static_cast<const T*>(k),
                      static_cast<const T*>(v), static_cast<const T*>(g),
                      static_cast<const T*>(beta), cu, max_segs, N, H, scale, s0,
-                     static_cast<T*>(o), fs, flags);
+                     static_cast<T*>(o), fs, flags, seg_ids, row_len);
   return hipGetLastError();
 }
 
@@ -140,11 +155,11 @@ template <typename T, int DK>
 hipError_t launch_dv(int32_t Dv, const void* q, const void* k, const void* v, const void* g,
                      const void* beta, const int32_t* cu, int32_t max_segs, int64_t N, int32_t H,
                      float scale, const float* s0, void* o, float* fs, int32_t* flags,
-                     hipStream_t s) {
+                     const int32_t* seg_ids, int64_t row_len, hipStream_t s) {
   switch (Dv) {
-    case 32: return launch_dims<T, DK, 32>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
-    case 64: return launch_dims<T, DK, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
-    case 128: return launch_dims<T, DK, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
+    case 32: return launch_dims<T, DK, 32>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
+    case 64: return launch_dims<T, DK, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
+    case 128: return launch_dims<T, DK, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
   }
   return hipErrorInvalidValue;
 }
@@ -153,11 +168,11 @@ template <typename T>
 hipError_t launch_dk(int32_t Dk, int32_t Dv, const void* q, const void* k, const void* v,
                      const void* g, const void* beta, const int32_t* cu, int32_t max_segs,
                      int64_t N, int32_t H, float scale, const float* s0, void* o, float* fs,
-                     int32_t* flags, hipStream_t s) {
+                     int32_t* flags, const int32_t* seg_ids, int64_t row_len, hipStream_t s) {
   switch (Dk) {
-    case 32: return launch_dv<T, 32>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
-    case 64: return launch_dv<T, 64>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
-    case 128: return launch_dv<T, 128>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, s);
+    case 32: return launch_dv<T, 32>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
+    case 64: return launch_dv<T, 64>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
+    case 128: return launch_dv<T, 128>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
   }
   return hipErrorInvalidValue;
 }
@@ -171,9 +186,23 @@ hipError_t launch_kda_serial(const void* q, const void* k, const void* v, const 
                              int32_t* flags, hipStream_t stream) {
   if (dtype == 0)
     return launch_dk<bf16>(Dk, Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o,
-                           final_state, flags, stream);
+                           final_state, flags, nullptr, 0, stream);
   return launch_dk<float>(Dk, Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o,
-                          final_state, flags, stream);
+                          final_state, flags, nullptr, 0, stream);
+}
+
+hipError_t launch_kda_serial_ids(const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, const int32_t* seg, int64_t B, int64_t T,
+                                 int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
+                                 const float* initial_state, void* o, float* final_state,
+                                 hipStream_t stream) {
+  // one "slot" per row; no cu_seqlens, so the tail blocks find nothing to zero
+  const int32_t rows = int32_t(B);
+  if (dtype == 0)
+    return launch_dk<bf16>(Dk, Dv, q, k, v, g, beta, nullptr, rows, B * T, H, scale, initial_state,
+                           o, final_state, nullptr, seg, T, stream);
+  return launch_dk<float>(Dk, Dv, q, k, v, g, beta, nullptr, rows, B * T, H, scale, initial_state,
+                          o, final_state, nullptr, seg, T, stream);
 }
 
 }  // namespace pkv

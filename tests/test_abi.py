@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -145,3 +145,35 @@ def test_workspace_size_and_check(lib):
     assert lib.pkv_chunk_kda_varlen(*_kda_args(ws=ctypes.c_void_p(0x1004), ws_bytes=need)) == 3
     # too many (segment, head) pairs for one launch
     assert lib.pkv_chunk_kda_varlen(*_kda_args(max_segs=1 << 21, H=4)) == 1
+
+
+def _ids_args(**kw):
+    base = dict(q=ctypes.c_void_p(0x10000000), k=ctypes.c_void_p(0x20000000), v=ctypes.c_void_p(0x30000000),
+                g=ctypes.c_void_p(0x40000000), beta=ctypes.c_void_p(0x50000000), seg=ctypes.c_void_p(0x58000000),
+                B=2, T=128, H=2, Dk=64, Dv=64, scale=1.0, dtype=0, s0=NUL, o=ctypes.c_void_p(0x60000000),
+                fs=NUL, flags=NUL, ws=NUL, ws_bytes=0, stream=NUL)
+    base.update(kw)
+    return tuple(base.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NUL), 1), (dict(seg=NUL), 1), (dict(o=NUL), 1), (dict(B=0), 1), (dict(T=0), 1),
+    (dict(B=1 << 16, T=1 << 15), 1),                                   # B*T too large
+    (dict(Dk=48), 2), (dict(dtype=5), 2),
+    (dict(o=ctypes.c_void_p(0x58000000)), 1),                          # o overlaps segment_ids
+    (dict(s0=ctypes.c_void_p(0x70000000), fs=ctypes.c_void_p(0x70000000)), 1),  # initial == final
+    (dict(), 3),                                                       # no workspace
+])
+def test_segment_ids_entry_validation(lib, kw, code):
+    assert lib.pkv_chunk_kda_segment_ids(*_ids_args(**kw)) == code
+
+
+def test_segment_ids_workspace_size(lib):
+    """Bounds of at most B*T segments (one int32 each, after a 256-byte count
+    word) and the chunk path's plan for that many slots; 0 off the chunk path."""
+    size = lib.pkv_chunk_kda_segment_ids_workspace_size
+    plan = lib.pkv_chunk_kda_varlen_workspace_size
+    for B, T, H, D in [(8, 8192, 32, 128), (1, 300, 2, 64), (3, 1000, 4, 64)]:
+        N = B * T
+        assert size(B, T, H, D, D, 0) == (N * 4 + 4 + 256 + 255) // 256 * 256 + plan(N, H, D, D, N, 0)
+    assert size(2, 64, 2, 32, 32, 0) == 0 and size(2, 64, 2, 64, 64, 1) == 0
