@@ -33,6 +33,9 @@ Functions and their pin status (every function is pinned; see tests/):
                                     segments, gate injection, invariants;
                                     initial states: decayed closed form,
                                     split-and-resume identity
+``chunk_kda_varlen_backward``       pinned: central finite differences of a
+                                    random linear loss for every input
+                                    (q, k, v, g, beta, initial state)
 ``chunk_kda_segment_ids``           pinned: gate injection (g = -inf at each
                                     segment start, RFC-0026 Alternatives),
                                     hand-derived two-row case, padding runs
@@ -43,7 +46,7 @@ Functions and their pin status (every function is pinned; see tests/):
 
 from .cu_seqlens import segment_ids_to_cu_seqlens, token_segment, FLAG_OVERFLOW, FLAG_LEADING_PAD
 from .short_conv import short_conv_segmask
-from .kda import chunk_kda_varlen, chunk_kda_segment_ids
+from .kda import chunk_kda_varlen, chunk_kda_segment_ids, chunk_kda_varlen_backward
 from .eod import eod_to_segment_ids
 
 __all__ = [
@@ -52,6 +55,7 @@ __all__ = [
     "short_conv_segmask",
     "chunk_kda_varlen",
     "chunk_kda_segment_ids",
+    "chunk_kda_varlen_backward",
     "eod_to_segment_ids",
     "FLAG_OVERFLOW",
     "FLAG_LEADING_PAD",

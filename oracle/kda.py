@@ -113,3 +113,60 @@ def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, initial_stat
             o[b, t] = scale * np.einsum("hde,hd->he", S, q[b, t])
         final_state[b] = S
     return o, final_state
+
+
+def chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_seqlens=None, scale=1.0,
+                              initial_state=None, dfinal_state=None):
+    """Reverse mode of ``chunk_kda_varlen`` (the recurrence above), in float64.
+
+    do: [N, H, Dv], the gradient of the loss with respect to o; dfinal_state:
+    [max_segs, H, Dk, Dv] or None, with respect to the final states. Returns
+    (dq, dk, dv, dg, dbeta, dinitial_state) shaped like q, k, v, g, beta and
+    [max_segs, H, Dk, Dv] (zeros when there is no initial state). Positions
+    outside every segment get zero gradients.
+
+    Written from the forward step, S_t = exp(g_t) * S_{t-1} + beta_t k_t v_t^T
+    (rows scaled by exp(g_t)) and o_t = scale * S_t^T q_t, by the chain rule
+    taken backwards through the segment, with every S_t kept:
+      dS_t   = dS (from t + 1) + scale * q_t do_t^T
+      dq_t   = scale * S_t do_t
+      dk_t   = beta_t * dS_t v_t,   dv_t = beta_t * dS_t^T k_t,
+      dbeta_t = k_t^T dS_t v_t,     dg_t = sum_e dS_t * (exp(g_t) * S_{t-1})
+      dS (for t - 1) = exp(g_t) * dS_t.
+    """
+    q = _as_thd(q, "q", 3)
+    k = _as_thd(k, "k", 3)
+    v = _as_thd(v, "v", 3)
+    g = _as_thd(g, "g", 3)
+    beta = _as_thd(beta, "beta", 2)
+    do = _as_thd(do, "do", 3)
+    N, H, Dk = q.shape
+    Dv = v.shape[2]
+    cu = np.array([0, N], dtype=np.int64) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    max_segs = cu.shape[0] - 1
+    dq, dk, dv, dg = (np.zeros_like(a) for a in (q, k, v, g))
+    dbeta = np.zeros_like(beta)
+    dinit = np.zeros((max_segs, H, Dk, Dv))
+    for i in range(max_segs):
+        start, end = int(cu[i]), int(cu[i + 1])
+        S0 = np.zeros((H, Dk, Dv)) if initial_state is None else np.array(initial_state[i], dtype=np.float64)
+        dS = np.zeros((H, Dk, Dv)) if dfinal_state is None else np.array(dfinal_state[i], dtype=np.float64)
+        if end <= start:
+            dinit[i] = dS  # an empty segment passes its initial state through
+            continue
+        states = [S0]  # states[j] = S after token start + j - 1
+        for t in range(start, end):
+            S = np.exp(g[t])[:, :, None] * states[-1] + beta[t][:, None, None] * k[t][:, :, None] * v[t][:, None, :]
+            states.append(S)
+        for t in range(end - 1, start - 1, -1):
+            S_t, S_prev = states[t - start + 1], states[t - start]
+            dS = dS + scale * q[t][:, :, None] * do[t][:, None, :]
+            dq[t] = scale * np.einsum("hde,he->hd", S_t, do[t])
+            u = np.einsum("hde,he->hd", dS, v[t])                 # dS_t v_t
+            dk[t] = beta[t][:, None] * u
+            dv[t] = beta[t][:, None] * np.einsum("hde,hd->he", dS, k[t])
+            dbeta[t] = np.einsum("hd,hd->h", k[t], u)
+            dg[t] = np.einsum("hde,hde->hd", dS, np.exp(g[t])[:, :, None] * S_prev)
+            dS = np.exp(g[t])[:, :, None] * dS
+        dinit[i] = dS
+    return dq, dk, dv, dg, dbeta, dinit
