@@ -27,6 +27,13 @@
  *   pkv_chunk_kda_segment_ids      the recurrence with [B, T] segment_ids
  *       RFC-0026, section 3.1.1 (kernel contract) and Alternatives (Alt1).
  *
+ * and the training step's reverse pass of the recurrence:
+ *
+ *   pkv_chunk_kda_varlen_backward  gradients of pkv_chunk_kda_varlen's outputs
+ *       with respect to q, k, v, g, beta and the initial states
+ *       RFC-0026, Background (the recurrence, differentiated) and section 3.3
+ *       (the initial/final state arguments the wrapper carries).
+ *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer (HIP device memory or memory the
  *     GPU can address). Scalars are passed by value.
@@ -235,11 +242,52 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
                                      float* final_state, int32_t* flags, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/*
+ * Reverse pass of pkv_chunk_kda_varlen: given do = dL/do and (optionally)
+ * dfinal_state = dL/dfinal_state, the gradients of L with respect to every
+ * input of the forward call on the same q, k, v, g, beta, cu_seqlens and
+ * initial_state. Per segment and head, with S_t the forward states:
+ *   dS (after the last token) = dfinal_state (0 when NULL)
+ *   dS_t   = exp(g_{t+1}) * dS_{t+1} + scale * q_t do_t^T   (rows scaled)
+ *   dq_t   = scale * S_t do_t          dk_t = beta_t * dS_t v_t
+ *   dv_t   = beta_t * dS_t^T k_t       dbeta_t = k_t . (dS_t v_t)
+ *   dg_t   = sum over the segment's u >= t of (q_u * dq_u - k_u * dk_u)
+ *            + sum_e dfinal_state[:, e] * S_last[:, e]   (elementwise in Dk)
+ *   d_initial_state = exp(g_first) * dS_first (dfinal_state for empty slots).
+ * Positions p >= cu[max_segs] get zero gradients.
+ *
+ * q, k, g, v, beta, cu_seqlens, max_segs, N, H, Dk, Dv, scale, dtype and
+ *             initial_state: exactly as passed to pkv_chunk_kda_varlen.
+ * do          [1, N, H, Dv] in `dtype`.
+ * dfinal_state float32 [max_segs, H, Dk, Dv] or NULL (zero cotangent).
+ * dq, dk, dg  [1, N, H, Dk] in `dtype`; dv [1, N, H, Dv]; dbeta [1, N, H]:
+ *             outputs, all written, none overlapping an input or each other.
+ * d_initial_state float32 [max_segs, H, Dk, Dv] or NULL (not written).
+ * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in (the
+ *             gradients of an invalid slot are then left unwritten).
+ * The reverse pass recomputes the states (nothing is saved by the forward
+ * call) and needs no workspace: between its two sweeps the dg and dk buffers
+ * hold fp32 intermediates. Alignment rules as for the forward call; the
+ * arithmetic is fp32 (bf16 tensors are read exactly and each result is
+ * rounded once).
+ * Supported: Dk, Dv in {32, 64, 128}. Errors: as pkv_chunk_kda_varlen (there
+ * is no workspace), with PKV_ERR_INVALID_ARGUMENT also for a NULL do or
+ * gradient output, or outputs that overlap an input or one another.
+ */
+pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const void* v,
+                                         const void* g, const void* beta,
+                                         const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
+                                         int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                         int32_t dtype, const float* initial_state,
+                                         const void* do_, const float* dfinal_state, void* dq,
+                                         void* dk, void* dv, void* dg, void* dbeta,
+                                         float* d_initial_state, int32_t* flags, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(int32_t status);
 
 /* ABI version of this header (bumped on any signature change). */
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 int32_t pkv_abi_version(void);
 
 #ifdef __cplusplus

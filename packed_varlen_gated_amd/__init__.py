@@ -11,6 +11,8 @@ Entry points (names follow RFC-0025 / RFC-0026):
 * ``segment_ids_to_cu_seqlens(segment_ids, max_segs)``
 * ``short_conv_segmask(x, w, segment_ids=None)``
 * ``chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_state=True)``
+* ``chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_seqlens=None, scale=1.0, ...)``
+* ``eod_to_segment_ids(tokens, eod_id)`` and ``chunk_kda_segment_ids(q, k, v, g, beta, segment_ids)``
 """
 
 import ctypes
@@ -61,6 +63,10 @@ def _load():
     lib.pkv_chunk_kda_segment_ids.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, i32,
                                               vp, vp, vp, vp, vp, sz, vp]
     lib.pkv_chunk_kda_segment_ids.restype = i32
+    lib.pkv_chunk_kda_varlen_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                                  f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  vp, vp]
+    lib.pkv_chunk_kda_varlen_backward.restype = i32
     lib.pkv_status_string.argtypes = [i32]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -265,3 +271,60 @@ def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, output_final
                                          B, T, H, Dk, Dv, float(scale), code, _ptr(initial_state), _ptr(o),
                                          _ptr(fs), _ptr(flags), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, fs
+
+
+class KdaGrads(NamedTuple):
+    dq: torch.Tensor                         # like q
+    dk: torch.Tensor                         # like k
+    dv: torch.Tensor                         # like v
+    dg: torch.Tensor                         # like g
+    dbeta: torch.Tensor                      # like beta
+    d_initial_state: Optional[torch.Tensor]  # fp32 [max_segs, H, Dk, Dv] or None
+
+
+def chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_seqlens=None, scale=1.0, initial_state=None,
+                              dfinal_state=None, output_d_initial_state=None, flags=None):
+    """Reverse pass of ``chunk_kda_varlen`` on the same inputs.
+
+    do: dL/do, shaped like the forward output; dfinal_state: fp32 [max_segs, H, Dk, Dv] or None
+    (dL/dfinal_state). Returns KdaGrads; d_initial_state is returned when
+    ``output_d_initial_state`` is true (default: when initial_state is given).
+    """
+    lib = _load()
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    for name, t, nd in (("q", q, 4), ("k", k, 4), ("v", v, 4), ("g", g, 4), ("beta", beta, 3),
+                        ("do", do, 4)):
+        _need(t, name, dev, dt, nd)
+    Bq, Tq, H, Dk = q.shape
+    N = Bq * Tq
+    Dv = v.shape[3]
+    if tuple(k.shape) != tuple(q.shape) or tuple(g.shape) != tuple(q.shape):
+        raise ValueError("q, k and g must have the same shape")
+    if tuple(v.shape) != (Bq, Tq, H, Dv) or tuple(do.shape) != (Bq, Tq, H, Dv) or \
+            tuple(beta.shape) != (Bq, Tq, H):
+        raise ValueError("v and do must be [.., N, H, Dv] and beta [.., N, H]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dev, torch.int32, 1)
+        max_segs = cu_seqlens.shape[0] - 1
+    else:
+        max_segs = 1
+    for name, t in (("initial_state", initial_state), ("dfinal_state", dfinal_state)):
+        if t is not None:
+            _need(t, name, dev, torch.float32, 4)
+            if tuple(t.shape) != (max_segs, H, Dk, Dv):
+                raise ValueError(f"{name} must be [{max_segs}, {H}, {Dk}, {Dv}]")
+    if flags is not None:
+        _need(flags, "flags", dev, torch.int32, 1)
+    if output_d_initial_state is None:
+        output_d_initial_state = initial_state is not None
+    dq, dk, dg = (torch.empty_like(q) for _ in range(3))
+    dv = torch.empty_like(v)
+    dbeta = torch.empty_like(beta)
+    dinit = torch.empty(max_segs, H, Dk, Dv, dtype=torch.float32, device=dev) if output_d_initial_state else None
+    _check(lib.pkv_chunk_kda_varlen_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), max_segs, N, H, Dk, Dv,
+        float(scale), code, _ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dinit), _ptr(flags), _stream(dev)))
+    return KdaGrads(dq, dk, dv, dg, dbeta, dinit)

@@ -139,6 +139,61 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
                                          static_cast<hipStream_t>(stream)));
 }
 
+pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const void* v,
+                                         const void* g, const void* beta,
+                                         const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
+                                         int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                         int32_t dtype, const float* initial_state,
+                                         const void* do_, const float* dfinal_state, void* dq,
+                                         void* dk, void* dv, void* dg, void* dbeta,
+                                         float* d_initial_state, int32_t* flags, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
+      do_ == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || dg == nullptr ||
+      dbeta == nullptr)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (N < 1 || N > kInt32Max || H < 1 || H > 65536) return PKV_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr) {
+    max_segs = 1;
+  } else if (max_segs < 1 || max_segs >= kInt32Max) {
+    return PKV_ERR_INVALID_ARGUMENT;
+  }
+  if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv))
+    return PKV_ERR_UNSUPPORTED;
+  if (int64_t(max_segs) * H > (int64_t(1) << 22)) return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t es = elem_size(dtype);
+  for (const void* p : {q, k, v, g, do_, static_cast<const void*>(dq),
+                        static_cast<const void*>(dk), static_cast<const void*>(dv),
+                        static_cast<const void*>(dg)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(beta) % es != 0 || reinterpret_cast<uintptr_t>(dbeta) % es != 0 ||
+      reinterpret_cast<uintptr_t>(initial_state) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(dfinal_state) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(d_initial_state) % 16 != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t kb = N * H * Dk * es, vb = N * H * Dv * es, bb = N * H * es;
+  const int64_t sb = int64_t(max_segs) * H * Dk * Dv * 4;
+  const int64_t cb = cu_seqlens ? (int64_t(max_segs) + 1) * 4 : 0;
+  const void* ins[8] = {q, k, v, g, beta, do_, initial_state, dfinal_state};
+  const int64_t in_bytes[8] = {kb, kb, vb, kb, bb, vb, sb, sb};
+  const void* outs[6] = {dq, dk, dv, dg, dbeta, d_initial_state};
+  const int64_t out_bytes[6] = {kb, kb, vb, kb, bb, sb};
+  for (int i = 0; i < 6; ++i) {
+    if (outs[i] == nullptr) continue;
+    for (int j = 0; j < 8; ++j)
+      if (ins[j] != nullptr && overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
+        return PKV_ERR_INVALID_ARGUMENT;
+    if (cu_seqlens != nullptr && overlaps(outs[i], out_bytes[i], cu_seqlens, cb))
+      return PKV_ERR_INVALID_ARGUMENT;
+    for (int j = 0; j < i; ++j)
+      if (outs[j] != nullptr && overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
+        return PKV_ERR_INVALID_ARGUMENT;
+  }
+  return from_hip(pkv::launch_kda_backward(q, k, v, g, beta, do_, cu_seqlens, max_segs, N, H, Dk,
+                                           Dv, scale, dtype, initial_state, dfinal_state, dq, dk,
+                                           dv, dg, dbeta, d_initial_state, flags,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t pkv_chunk_kda_segment_ids_workspace_size(int64_t B, int64_t T, int32_t H, int32_t Dk,
                                                 int32_t Dv, int32_t dtype) {
   if (B < 1 || T < 1 || B * T > kInt32Max) return 0;

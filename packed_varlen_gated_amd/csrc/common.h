@@ -74,4 +74,13 @@ hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const v
                             const float* initial_state, void* o, float* final_state,
                             int32_t* flags, void* workspace, hipStream_t stream);
 
+// Reverse pass of the recurrence (token-serial; no workspace).
+hipError_t launch_kda_backward(const void* q, const void* k, const void* v, const void* g,
+                               const void* beta, const void* dout, const int32_t* cu,
+                               int32_t max_segs, int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+                               float scale, int32_t dtype, const float* initial_state,
+                               const float* dfinal_state, void* dq, void* dk, void* dv, void* dg,
+                               void* dbeta, float* dinitial_state, int32_t* flags,
+                               hipStream_t stream);
+
 }  // namespace pkv

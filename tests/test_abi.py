@@ -29,13 +29,13 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
     for code, name in [(0, b"PKV_OK"), (1, b"PKV_ERR_INVALID_ARGUMENT"), (2, b"PKV_ERR_UNSUPPORTED"),
                        (3, b"PKV_ERR_WORKSPACE"), (4, b"PKV_ERR_HIP"), (99, b"PKV_ERR_UNKNOWN")]:
         assert lib.pkv_status_string(code) == name
@@ -177,3 +177,30 @@ def test_segment_ids_workspace_size(lib):
         N = B * T
         assert size(B, T, H, D, D, 0) == (N * 4 + 4 + 256 + 255) // 256 * 256 + plan(N, H, D, D, N, 0)
     assert size(2, 64, 2, 32, 32, 0) == 0 and size(2, 64, 2, 64, 64, 1) == 0
+
+
+def _bwd_args(**kw):
+    A = lambda a: ctypes.c_void_p(a)
+    base = dict(q=A(0x10000000), k=A(0x20000000), v=A(0x30000000), g=A(0x40000000), beta=A(0x50000000),
+                cu=P, max_segs=4, N=256, H=2, Dk=64, Dv=64, scale=1.0, dtype=0, s0=NUL, do=A(0x58000000),
+                dF=NUL, dq=A(0x60000000), dk=A(0x68000000), dv=A(0x70000000), dg=A(0x78000000),
+                dbeta=A(0x7c000000), dinit=NUL, flags=NUL, stream=NUL)
+    base.update(kw)
+    return tuple(base.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=NUL), 1), (dict(dq=NUL), 1), (dict(dk=NUL), 1), (dict(dv=NUL), 1), (dict(dg=NUL), 1),
+    (dict(dbeta=NUL), 1), (dict(q=NUL), 1), (dict(N=0), 1), (dict(H=0), 1), (dict(max_segs=0), 1),
+    (dict(Dk=48), 2), (dict(Dv=16), 2), (dict(dtype=7), 2),
+    (dict(dq=ctypes.c_void_p(0x10000000 + 256)), 1),     # dq overlaps q
+    (dict(dg=ctypes.c_void_p(0x58000000)), 1),           # dg overlaps do
+    (dict(dk=ctypes.c_void_p(0x60000000 + 512)), 1),     # dk overlaps dq
+    (dict(dbeta=ctypes.c_void_p(0x7c000001)), 1),        # dbeta not element-aligned
+    (dict(dv=ctypes.c_void_p(0x70000008)), 1),           # dv not 16-byte aligned
+    (dict(dinit=ctypes.c_void_p(0x7e000000), dF=ctypes.c_void_p(0x7e000000)), 1),  # d initial == dfinal
+    (dict(dinit=ctypes.c_void_p(0x7e000000), s0=ctypes.c_void_p(0x7e000000 + 4096)), 1),
+    (dict(max_segs=1 << 21, H=4), 1),
+])
+def test_backward_entry_validation(lib, kw, code):
+    assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args(**kw)) == code
