@@ -52,12 +52,12 @@ def parse():
 
 
 def kernel_source_hash():
-    """Hash of the sources of the dominant kernel (ties a counter summary to its code)."""
+    """Hash of the sources the dominant kernel is built from (ties a counter
+    summary to its code): kda_chunk.hip and the common header."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "packed_varlen_gated_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.startswith("kda") or f == "common.h":
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in ("common.h", "kda_chunk.hip"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
