@@ -10,7 +10,9 @@ HBM before the timed region. Prints ONE JSON line on stdout.
 
 Modes used for profiling (no JSON line): --mode kernel (only chunk_kda_varlen,
 for rocprofv3 counters) and --mode copy (a plain device copy of known size,
-the calibration of the HBM byte counters).
+the calibration of the HBM byte counters). --mode backward times the reverse
+pass (chunk_kda_varlen_backward) on the same workload and prints its own JSON
+line (not the headline metric).
 """
 
 import argparse
@@ -44,7 +46,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="oracle sample size in tokens (0: sized for ~15 s of CPU work)")
-    p.add_argument("--mode", choices=["bench", "kernel", "copy"], default="bench")
+    p.add_argument("--mode", choices=["bench", "kernel", "copy", "backward"], default="bench")
     p.add_argument("--entry", choices=["cu_seqlens", "segment_ids"], default="cu_seqlens",
                    help="segment_ids: the step is one pkv_chunk_kda_segment_ids call on the [B, T] ids "
                         "(no conversion, no phantom slots) instead of the conversion + chunk_kda_varlen")
@@ -73,6 +75,17 @@ def algorithmic_bytes(cfg, cu, final_state):
     if final_state:
         total += 4 * (len(cu) - 1) * H * cfg.Dk * cfg.Dv
     return total
+
+
+def backward_bytes(cfg, cu):
+    """Bytes the reverse pass must move at least once: q, k, g, v, beta and do
+    read, dq, dk, dg, dv and dbeta written, for every position (uncovered ones
+    get zero gradients, written), and cu_seqlens read."""
+    E = 4 if cfg.dtype == "f32" else 2
+    N, H = cfg.B * cfg.T, cfg.H
+    covered = int(cu[-1])
+    per_tok_head = E * (6 * cfg.Dk + 3 * cfg.Dv + 2)
+    return covered * H * per_tok_head + (N - covered) * H * E * (3 * cfg.Dk + cfg.Dv + 1) + 4 * len(cu)
 
 
 def algorithmic_flops(cfg, cu):
@@ -205,6 +218,45 @@ def main():
                                  flags=flags, out=o, workspace=ws)
         torch.cuda.synchronize()
         log(f"kernel mode: {args.warmup + args.steps} launches of {DOMINANT_KERNEL}")
+        return
+
+    if args.mode == "backward":
+        gen = torch.Generator(device=dev).manual_seed(2024)
+        do = torch.randn(1, N, H, cfg.Dv, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
+        bws = torch.empty(max(pkv.chunk_kda_varlen_backward_workspace_size(N, H, cfg.Dk, cfg.Dv, cfg.max_segs,
+                                                                          q.dtype), 1),
+                          dtype=torch.uint8, device=dev)
+        cu_dev = res.cu_seqlens
+        for _ in range(args.warmup):
+            pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_dev, flags=flags, workspace=bws)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for a_ev, b_ev in evs:
+            a_ev.record()
+            pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_dev, flags=flags, workspace=bws)
+            b_ev.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = (t1 - t0) * 1000.0 / args.steps
+        call_s = sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1000.0
+        bb = backward_bytes(cfg, cu_host)
+        achieved = bb / call_s / 1e9
+        log(f"backward: {call_s * 1e3:.3f} ms per call; {achieved:.0f} GB/s = "
+            f"{achieved / HBM_PEAK_GBS:.3f} of HBM peak; flags {int(flags.item())}")
+        print(json.dumps({
+            "metric": "packed tokens/sec for chunk_kda_varlen bwd at H=32,D=128",
+            "value": N / call_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+            "config": {"workload": cfg.name, "N": N, "H": H, "Dk": cfg.Dk, "Dv": cfg.Dv,
+                       "max_segs": cfg.max_segs, "n_segs": n_segs, "step": "chunk_kda_varlen_backward"},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "chunk_kda_varlen_backward", "kernel_avg_us": call_s * 1e6,
+                         "algorithmic_bytes_per_launch": bb},
+            "cpu_baseline": None}), flush=True)
         return
 
     if args.entry == "segment_ids":

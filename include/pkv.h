@@ -266,14 +266,25 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
  * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in (the
  *             gradients of an invalid slot are then left unwritten).
  * The reverse pass recomputes the states (nothing is saved by the forward
- * call) and needs no workspace: between its two sweeps the dg and dk buffers
- * hold fp32 intermediates. Alignment rules as for the forward call; the
- * arithmetic is fp32 (bf16 tensors are read exactly and each result is
- * rounded once).
- * Supported: Dk, Dv in {32, 64, 128}. Errors: as pkv_chunk_kda_varlen (there
- * is no workspace), with PKV_ERR_INVALID_ARGUMENT also for a NULL do or
- * gradient output, or outputs that overlap an input or one another.
+ * call). For bf16 with Dk, Dv in {64, 128} it is chunked: the workspace holds
+ * a chunk table and the bf16 state and adjoint state (dL/dS from everything
+ * after it) at every 64-token chunk boundary, written and read within the
+ * call (scratch: calls sharing a workspace must be ordered on one stream); its
+ * size, pkv_chunk_kda_varlen_backward_workspace_size(), is
+ * 256 * ceil(4 (max_segs + 1) / 256) + 4 (ceil(N / 64) + max_segs) H Dk Dv
+ * bytes. Every other shape runs token-serially and needs no workspace (size
+ * 0, NULL allowed): between its two sweeps the dg and dk buffers hold fp32
+ * intermediates. Alignment rules as for the forward call, and the workspace
+ * must be 256-byte aligned. The arithmetic is fp32 (bf16 tensors are read
+ * exactly; the chunked path rounds MFMA operands and the saved states to
+ * bf16, like the forward's chunked path).
+ * Supported: Dk, Dv in {32, 64, 128}. Errors: as pkv_chunk_kda_varlen, with
+ * PKV_ERR_INVALID_ARGUMENT also for a NULL do or gradient output, or outputs
+ * (or the workspace) that overlap an input or one another; PKV_ERR_WORKSPACE
+ * when the workspace is needed and missing, too small or misaligned.
  */
+size_t pkv_chunk_kda_varlen_backward_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+                                                    int32_t max_segs, int32_t dtype);
 pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const void* v,
                                          const void* g, const void* beta,
                                          const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
@@ -281,7 +292,8 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
                                          int32_t dtype, const float* initial_state,
                                          const void* do_, const float* dfinal_state, void* dq,
                                          void* dk, void* dv, void* dg, void* dbeta,
-                                         float* d_initial_state, int32_t* flags, void* stream);
+                                         float* d_initial_state, int32_t* flags, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(int32_t status);

@@ -65,8 +65,10 @@ def _load():
     lib.pkv_chunk_kda_segment_ids.restype = i32
     lib.pkv_chunk_kda_varlen_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                                   f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                                  vp, vp]
+                                                  vp, vp, sz, vp]
     lib.pkv_chunk_kda_varlen_backward.restype = i32
+    lib.pkv_chunk_kda_varlen_backward_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    lib.pkv_chunk_kda_varlen_backward_workspace_size.restype = sz
     lib.pkv_status_string.argtypes = [i32]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -282,13 +284,20 @@ class KdaGrads(NamedTuple):
     d_initial_state: Optional[torch.Tensor]  # fp32 [max_segs, H, Dk, Dv] or None
 
 
+def chunk_kda_varlen_backward_workspace_size(N, H, Dk, Dv, max_segs, dtype):
+    return int(_load().pkv_chunk_kda_varlen_backward_workspace_size(N, H, Dk, Dv, max_segs,
+                                                                    _dtype_code(dtype)))
+
+
 def chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_seqlens=None, scale=1.0, initial_state=None,
-                              dfinal_state=None, output_d_initial_state=None, flags=None):
+                              dfinal_state=None, output_d_initial_state=None, flags=None,
+                              workspace=None):
     """Reverse pass of ``chunk_kda_varlen`` on the same inputs.
 
     do: dL/do, shaped like the forward output; dfinal_state: fp32 [max_segs, H, Dk, Dv] or None
     (dL/dfinal_state). Returns KdaGrads; d_initial_state is returned when
-    ``output_d_initial_state`` is true (default: when initial_state is given).
+    ``output_d_initial_state`` is true (default: when initial_state is given). The chunked path
+    (bf16, Dk and Dv in {64, 128}) needs a workspace (allocated here when not given).
     """
     lib = _load()
     dev = q.device
@@ -323,8 +332,13 @@ def chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_seqlens=None, scale=1.0, 
     dv = torch.empty_like(v)
     dbeta = torch.empty_like(beta)
     dinit = torch.empty(max_segs, H, Dk, Dv, dtype=torch.float32, device=dev) if output_d_initial_state else None
+    need = int(lib.pkv_chunk_kda_varlen_backward_workspace_size(N, H, Dk, Dv, max_segs, code))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pkv_chunk_kda_varlen_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), max_segs, N, H, Dk, Dv,
         float(scale), code, _ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dinit), _ptr(flags), _stream(dev)))
+        _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dinit), _ptr(flags), _ptr(workspace), ws_bytes,
+        _stream(dev)))
     return KdaGrads(dq, dk, dv, dg, dbeta, dinit)

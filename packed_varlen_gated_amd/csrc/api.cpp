@@ -146,7 +146,8 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
                                          int32_t dtype, const float* initial_state,
                                          const void* do_, const float* dfinal_state, void* dq,
                                          void* dk, void* dv, void* dg, void* dbeta,
-                                         float* d_initial_state, int32_t* flags, void* stream) {
+                                         float* d_initial_state, int32_t* flags, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
       do_ == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || dg == nullptr ||
       dbeta == nullptr)
@@ -188,10 +189,31 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
       if (outs[j] != nullptr && overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
         return PKV_ERR_INVALID_ARGUMENT;
   }
+  const size_t need = pkv::kda_chunk_bwd_workspace_bytes(N, H, Dk, Dv, dtype, max_segs);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need ||
+        reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return PKV_ERR_WORKSPACE;
+    for (int i = 0; i < 8; ++i)
+      if (ins[i] != nullptr && overlaps(workspace, int64_t(need), ins[i], in_bytes[i]))
+        return PKV_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < 6; ++i)
+      if (outs[i] != nullptr && overlaps(workspace, int64_t(need), outs[i], out_bytes[i]))
+        return PKV_ERR_INVALID_ARGUMENT;
+    return from_hip(pkv::launch_kda_chunk_backward(
+        q, k, v, g, beta, do_, cu_seqlens, max_segs, N, H, Dk, Dv, scale, initial_state,
+        dfinal_state, dq, dk, dv, dg, dbeta, d_initial_state, flags, workspace,
+        static_cast<hipStream_t>(stream)));
+  }
   return from_hip(pkv::launch_kda_backward(q, k, v, g, beta, do_, cu_seqlens, max_segs, N, H, Dk,
                                            Dv, scale, dtype, initial_state, dfinal_state, dq, dk,
                                            dv, dg, dbeta, d_initial_state, flags,
                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_chunk_kda_varlen_backward_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+                                                    int32_t max_segs, int32_t dtype) {
+  return pkv::kda_chunk_bwd_workspace_bytes(N, H, Dk, Dv, dtype, max_segs);
 }
 
 size_t pkv_chunk_kda_segment_ids_workspace_size(int64_t B, int64_t T, int32_t H, int32_t Dk,

@@ -74,7 +74,21 @@ hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const v
                             const float* initial_state, void* o, float* final_state,
                             int32_t* flags, void* workspace, hipStream_t stream);
 
-// Reverse pass of the recurrence (token-serial; no workspace).
+// Reverse pass of the recurrence, chunked on MFMA (bf16, Dk and Dv in {64, 128}):
+// the work plan and the bf16 states S and Lambda of every chunk in the workspace.
+bool kda_chunk_bwd_supported(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                             int32_t max_segs);
+size_t kda_chunk_bwd_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                                     int32_t max_segs);
+hipError_t launch_kda_chunk_backward(const void* q, const void* k, const void* v, const void* g,
+                                     const void* beta, const void* dout, const int32_t* cu,
+                                     int32_t max_segs, int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+                                     float scale, const float* initial_state,
+                                     const float* dfinal_state, void* dq, void* dk, void* dv,
+                                     void* dg, void* dbeta, float* dinitial_state, int32_t* flags,
+                                     void* workspace, hipStream_t stream);
+
+// Reverse pass of the recurrence, token-serial (every other shape; no workspace).
 hipError_t launch_kda_backward(const void* q, const void* k, const void* v, const void* g,
                                const void* beta, const void* dout, const int32_t* cu,
                                int32_t max_segs, int64_t N, int32_t H, int32_t Dk, int32_t Dv,

@@ -1,0 +1,734 @@
+// Chunked reverse pass of the packed KDA recurrence (bf16 tensors, Dk, Dv in
+// {64, 128}), on MFMA.
+//
+// RFC-0026 "Ling3 KDA varlen support", Background: S_t = diag(exp g_t) S_{t-1}
+// + beta_t k_t v_t^T, o_t = scale * S_t^T q_t, S reset at every segment start
+// (section 3.1.1) or started from the slot's initial state (section 3.3). With
+// Lambda the adjoint of a state from everything after it, the gradients follow
+// from the same chunked form the forward pass uses. Chunks are 64 tokens
+// aligned to segment starts, split into four 16-token sub-chunks.
+//
+// Three launches:
+//   plan   one work-group: chunk count per segment slot and its prefix sums
+//          (global chunk index of each segment's first chunk).
+//   state  one work-group per (slot, head) and role, the two roles in one grid:
+//          forward, S before every chunk (bf16 in the workspace);
+//          adjoint, Lambda after every chunk, walking the chunks backwards
+//          (Lambda after the last one = dL/dfinal_state), then
+//          d initial state = Lambda before the first chunk.
+//            S   <- 2^{B} S + sum_t kbar_t v_t^T,     kbar_t = beta_t k_t 2^{B - b_t}
+//            Lam <- 2^{B} Lam + sum_t q'_t do_t^T,    q'_t = scale q_t 2^{b_t}
+//          (b_t the log2 cumulative gate from the chunk start, B its last
+//          value; rows scaled per key channel.)
+//   chunk  one work-group per (chunk, head), independent of the others: from
+//          S_c and Lambda_c it walks the sub-chunks backwards. For sub-chunk i
+//          with within-sub-chunk cumulative c_t (log2) and total T_i, S_i the
+//          state before it (formed directly from S_c) and Lambda_i the adjoint
+//          after it (carried):
+//            Qh_t = scale q_t 2^{c_t}, Kt_s = beta_s k_s 2^{-c_s},
+//            A = (Qh Kt^T) masked t >= s, dA = (dO V^T) masked t >= s,
+//            dq_t  = scale 2^{c_t} (S_i do_t + sum_s dA_ts Kt_s)
+//            u_s   = 2^{-c_s} (2^{T_i} Lambda_i v_s + sum_t dA_ts Qh_t)
+//            dk_s  = beta_s u_s,  dbeta_s = k_s . u_s
+//            dv_s  = (Kt_s 2^{T_i})^T Lambda_i + sum_t A_ts do_t
+//            Lambda_{i-1} = 2^{T_i} Lambda_i + sum_t Qh_t do_t^T.
+//          dg_t is the sum over u >= t in the chunk of (q_u dq_u - k_u dk_u)
+//          plus G_c = sum_e Lambda_c * S_end (S_end the state after the
+//          chunk): the gate gradient at the chunk's first following token,
+//          which stands for all later tokens and the final-state cotangent.
+//
+// MFMA operand conventions (v_mfma_f32_16x16x16_bf16 and _16x16x32_bf16):
+// operand lane l has row (A) or column (B) l%16 and contraction slots of lane
+// group l/16; a 16x16 fp32 result has column l%16 and rows 4(l/16)+j. So a
+// result X serves directly as the B operand of X or the A operand of X^T,
+// and tiles of two adjacent result blocks feed a 16x16x32 product whose other
+// operand is read with the same contraction-index permutation. Lambda is kept
+// in two orientations (key channels per lane for the products contracting
+// over Dv, value channels per lane for those over Dk); the second one starts
+// from a product with the identity. A 16x16x16 product never accumulates
+// straight onto a 16x16x32 result: its own accumulator is added afterwards
+// (taking the first as its C operand gave wrong rows).
+
+#include "common.h"
+
+namespace pkv {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 64;
+constexpr int kThreads = 256;
+constexpr int kPlanThreads = 1024;
+constexpr int kTailBlocks = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32(s16x8 a, s16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf2f(short x) { return __uint_as_float(uint32_t(uint16_t(x)) << 16); }
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ s16x4 pack4(float a, float b, float c, float d) {
+  return __builtin_bit_cast(s16x4, u32x2{pk2(a, b), pk2(c, d)});
+}
+__device__ __forceinline__ s16x4 pack4(f32x4 x) { return pack4(x[0], x[1], x[2], x[3]); }
+__device__ __forceinline__ s16x8 join(s16x4 lo, s16x4 hi) {
+  return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ f32x4 unpack4(s16x4 x) {
+  return f32x4{bf2f(x[0]), bf2f(x[1]), bf2f(x[2]), bf2f(x[3])};
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within a group of 16 lanes, when
+// lane k points at row r0 + k/4, column c0 + 4 (k % 4) of a row-major bf16
+// tile, lane j receives column c0 + j of rows r0 .. r0 + 3.
+__device__ __forceinline__ s16x4 tr4(const bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+// The operand (column c0 + l%16, rows r0 + 4(l/16) .. +3) of a tile with row
+// stride rs: the pointer each lane supplies.
+__device__ __forceinline__ const bf16* tr_ptr(const bf16* tile, int rs, int r0, int c0, int lane) {
+  const int n = lane & 15, g4 = lane >> 4;
+  return tile + (r0 + 4 * g4 + (n >> 2)) * rs + c0 + 4 * (n & 3);
+}
+__device__ __forceinline__ s16x4 ld4(const bf16* p) { return *reinterpret_cast<const s16x4*>(p); }
+__device__ __forceinline__ s16x8 ld8(const bf16* p) { return *reinterpret_cast<const s16x8*>(p); }
+
+// cu_seqlens entry i; a NULL cu_seqlens is the single segment [0, N).
+__device__ __forceinline__ int64_t cu_at(const int32_t* cu, int i, int64_t N) {
+  return cu != nullptr ? int64_t(cu[i]) : (i == 0 ? 0 : N);
+}
+
+__device__ __forceinline__ bool bad_segment(int64_t start, int64_t end, int64_t N, int slot) {
+  return start < 0 || end < start || end > N || (slot == 0 && start != 0);
+}
+
+// ---------------------------------------------------------------- plan
+// base[i] = global index of slot i's first chunk, base[max_segs] = total, all
+// capped at max_chunks (reached only when cu_seqlens is invalid, which sets
+// the flag; valid slots tile [0, cu[max_segs]) and need at most max_chunks).
+__global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(const int32_t* __restrict__ cu,
+                                                                    int32_t max_segs, int64_t N,
+                                                                    int32_t max_chunks,
+                                                                    int32_t* __restrict__ base,
+                                                                    int32_t* __restrict__ flags) {
+  __shared__ int64_t s_scan[kPlanThreads];
+  const int tid = threadIdx.x;
+  int64_t running = 0;
+  for (int tile0 = 0; tile0 < max_segs; tile0 += kPlanThreads) {
+    const int slot = tile0 + tid;
+    int64_t n = 0;
+    if (slot < max_segs) {
+      const int64_t start = cu_at(cu, slot, N), end = cu_at(cu, slot + 1, N);
+      if (bad_segment(start, end, N, slot)) {
+        if (flags != nullptr) atomicOr(flags, kFlagBadCuSeqlens);
+      } else {
+        n = (end - start + kC - 1) / kC;
+      }
+    }
+    s_scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+      const int64_t x = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += x;
+      __syncthreads();
+    }
+    if (slot < max_segs) {
+      const int64_t b = running + s_scan[tid] - n;
+      base[slot] = int32_t(b < max_chunks ? b : max_chunks);
+    }
+    running += s_scan[kPlanThreads - 1];
+    __syncthreads();
+  }
+  if (tid == 0) base[max_segs] = int32_t(running < max_chunks ? running : max_chunks);
+}
+
+// ---------------------------------------------------------------- state pass
+template <int DK, int DV>
+struct StCfg {
+  static constexpr int RX = DK + 8, RY = DV + 8;
+  static constexpr int o_x = 0;                        // bf16 [64][RX]: g, then kbar or q'
+  static constexpr int o_k = o_x + kC * RX * 2;        // bf16 [64][RX]: k or q
+  static constexpr int o_y = o_k + kC * RX * 2;        // bf16 [64][RY]: v or do
+  static constexpr int o_beta = o_y + kC * RY * 2;     // fp32 [64]
+  static constexpr int o_dec = o_beta + kC * 4;        // fp32 [DK]: 2^B
+  static constexpr int bytes = o_dec + DK * 4;
+};
+
+// Rows [a, a + L) of a [N, H, D] bf16 tensor (head h) into a [64][rs] LDS tile
+// with 16-byte loads; rows past L are zero.
+template <int D>
+__device__ __forceinline__ void stage_rows(bf16* tile, int rs, const bf16* __restrict__ src,
+                                          int64_t a, int L, int32_t H, int h, int tid) {
+  for (int i = tid; i < kC * (D / 8); i += kThreads) {
+    const int t = i / (D / 8), c8 = (i % (D / 8)) * 8;
+    s16x8 x = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (t < L) x = *reinterpret_cast<const s16x8*>(src + ((a + t) * H + h) * D + c8);
+    *reinterpret_cast<s16x8*>(tile + t * rs + c8) = x;
+  }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads, 2) void kda_bwd_state_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ base, int32_t max_segs,
+    int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
+    const float* __restrict__ dfinal, bf16* __restrict__ Sws, bf16* __restrict__ Lws,
+    float* __restrict__ dinit) {
+  using C = StCfg<DK, DV>;
+  constexpr int EB = DV / 16, DBW = DK / 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* s_x = reinterpret_cast<bf16*>(smem + C::o_x);
+  bf16* s_k = reinterpret_cast<bf16*>(smem + C::o_k);
+  bf16* s_y = reinterpret_cast<bf16*>(smem + C::o_y);
+  float* s_beta = reinterpret_cast<float*>(smem + C::o_beta);
+  float* s_dec = reinterpret_cast<float*>(smem + C::o_dec);
+
+  const int64_t pairs = int64_t(max_segs) * H;
+  const bool adjoint = int64_t(blockIdx.x) >= pairs;
+  const int64_t idx = adjoint ? int64_t(blockIdx.x) - pairs : int64_t(blockIdx.x);
+  const int slot = int(idx / H), h = int(idx % H);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
+  const int cbase = base[slot];
+  const int nch = base[slot + 1] - cbase;
+  const int64_t start = nch > 0 ? cu_at(cu, slot, N) : 0;
+  const int64_t end = nch > 0 ? cu_at(cu, slot + 1, N) : 0;
+  const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
+
+  // X^T tiles: rows e = 16E + 4g4 + j, column d = 16 (w DBW + dd) + n.
+  f32x4 X[EB][DBW];
+  const float* src = adjoint ? dfinal : initial_state;
+#pragma unroll
+  for (int dd = 0; dd < DBW; ++dd) {
+    const int d = 16 * (w * DBW + dd) + n;
+#pragma unroll
+    for (int E = 0; E < EB; ++E)
+      X[E][dd] = src ? *reinterpret_cast<const f32x4*>(src + sh + int64_t(d) * DV + 16 * E + 4 * g4)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto store_state = [&](bf16* ws, int gc) {
+    const int64_t off = (int64_t(gc) * H + h) * DK * DV;
+#pragma unroll
+    for (int dd = 0; dd < DBW; ++dd) {
+      const int d = 16 * (w * DBW + dd) + n;
+#pragma unroll
+      for (int E = 0; E < EB; ++E)
+        *reinterpret_cast<s16x4*>(ws + off + int64_t(d) * DV + 16 * E + 4 * g4) = pack4(X[E][dd]);
+    }
+  };
+  auto update = [&]() {
+#pragma unroll
+    for (int dd = 0; dd < DBW; ++dd) {
+      const float dec = s_dec[16 * (w * DBW + dd) + n];
+#pragma unroll
+      for (int E = 0; E < EB; ++E) X[E][dd] *= dec;
+    }
+#pragma unroll
+    for (int kb = 0; kb < kC / 16; ++kb) {
+      s16x4 xb[DBW];
+#pragma unroll
+      for (int dd = 0; dd < DBW; ++dd) xb[dd] = tr4(tr_ptr(s_x, C::RX, 16 * kb, 16 * (w * DBW + dd), lane));
+#pragma unroll
+      for (int E = 0; E < EB; ++E) {
+        const s16x4 ya = tr4(tr_ptr(s_y, C::RY, 16 * kb, 16 * E, lane));
+#pragma unroll
+        for (int dd = 0; dd < DBW; ++dd) X[E][dd] = mfma16(ya, xb[dd], X[E][dd]);
+      }
+    }
+  };
+  if (!adjoint) {
+    for (int c = 0; c < nch; ++c) {
+      store_state(Sws, cbase + c);
+      if (c == nch - 1) break;
+      const int64_t a = start + int64_t(kC) * c;
+      const int L = int(end - a < kC ? end - a : kC);
+      __syncthreads();
+      stage_rows<DK>(s_x, C::RX, g, a, L, H, h, tid);
+      stage_rows<DK>(s_k, C::RX, k, a, L, H, h, tid);
+      stage_rows<DV>(s_y, C::RY, v, a, L, H, h, tid);
+      if (tid < kC) s_beta[tid] = tid < L ? to_f32(beta[(a + tid) * H + h]) : 0.f;
+      __syncthreads();
+      if (tid < DK) {
+        // kbar_t = beta_t k_t 2^{B - b_t}, written over g
+        const int d = tid;
+        float B = 0.f;
+#pragma unroll 16
+        for (int t = 0; t < kC; ++t) B += to_f32(s_x[t * C::RX + d]) * kLog2e;
+        float b = 0.f;
+#pragma unroll 16
+        for (int t = 0; t < kC; ++t) {
+          b += to_f32(s_x[t * C::RX + d]) * kLog2e;
+          s_x[t * C::RX + d] = bf16(s_beta[t] * to_f32(s_k[t * C::RX + d]) * ex2(B - b));
+        }
+        s_dec[d] = ex2(B);
+      }
+      __syncthreads();
+      update();
+    }
+  } else {
+    for (int c = nch - 1; c >= 0; --c) {
+      store_state(Lws, cbase + c);
+      const int64_t a = start + int64_t(kC) * c;
+      const int L = int(end - a < kC ? end - a : kC);
+      __syncthreads();
+      stage_rows<DK>(s_x, C::RX, g, a, L, H, h, tid);
+      stage_rows<DK>(s_k, C::RX, q, a, L, H, h, tid);
+      stage_rows<DV>(s_y, C::RY, dout, a, L, H, h, tid);
+      __syncthreads();
+      if (tid < DK) {
+        // q'_t = scale q_t 2^{b_t}, written over g
+        const int d = tid;
+        float b = 0.f;
+#pragma unroll 16
+        for (int t = 0; t < kC; ++t) {
+          b += to_f32(s_x[t * C::RX + d]) * kLog2e;
+          s_x[t * C::RX + d] = bf16(scale * to_f32(s_k[t * C::RX + d]) * ex2(b));
+        }
+        s_dec[d] = ex2(b);
+      }
+      __syncthreads();
+      update();
+    }
+    if (dinit != nullptr) {
+#pragma unroll
+      for (int dd = 0; dd < DBW; ++dd) {
+        const int d = 16 * (w * DBW + dd) + n;
+#pragma unroll
+        for (int E = 0; E < EB; ++E)
+          *reinterpret_cast<f32x4*>(dinit + sh + int64_t(d) * DV + 16 * E + 4 * g4) = X[E][dd];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- chunk pass
+template <int DK, int DV>
+struct ChCfg {
+  static constexpr int RK = DK + 8, RV = DV + 8, ES = kC + 4;
+  static constexpr int o_q = 0;                         // bf16 [64][RK] raw q
+  static constexpr int o_k = o_q + kC * RK * 2;         // raw k
+  static constexpr int o_qh = o_k + kC * RK * 2;        // Qh = scale q 2^{c}
+  static constexpr int o_kt = o_qh + kC * RK * 2;       // Kt = beta k 2^{-c}
+  static constexpr int o_v = o_kt + kC * RK * 2;        // bf16 [64][RV]
+  static constexpr int o_do = o_v + kC * RV * 2;
+  static constexpr int o_E = o_do + kC * RV * 2;        // fp32 [DK][ES]: 2^{c_t}, channel-major
+  static constexpr int o_T = o_E + DK * ES * 4;         // fp32 [4][DK]: sub-chunk totals (log2)
+  static constexpr int o_db = o_T + 4 * DK * 4;         // fp32 [4 sub-chunks][4 waves][16]
+  static constexpr int o_beta = o_db + 4 * 4 * 16 * 4;  // fp32 [64]
+  static constexpr int bytes = o_beta + kC * 4;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ base, int32_t max_segs,
+    int32_t max_chunks, int64_t N, int32_t H, float scale, const bf16* __restrict__ Sws,
+    const bf16* __restrict__ Lws, bf16* __restrict__ dq, bf16* __restrict__ dk,
+    bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta) {
+  using C = ChCfg<DK, DV>;
+  constexpr int DB = DK / 16, EB = DV / 16, DBW = DB / 4, EBW = EB / 4;
+  constexpr int RK = C::RK, RV = C::RV, ES = C::ES;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* s_q = reinterpret_cast<bf16*>(smem + C::o_q);
+  bf16* s_k = reinterpret_cast<bf16*>(smem + C::o_k);
+  bf16* s_qh = reinterpret_cast<bf16*>(smem + C::o_qh);
+  bf16* s_kt = reinterpret_cast<bf16*>(smem + C::o_kt);
+  bf16* s_v = reinterpret_cast<bf16*>(smem + C::o_v);
+  bf16* s_do = reinterpret_cast<bf16*>(smem + C::o_do);
+  float* s_E = reinterpret_cast<float*>(smem + C::o_E);
+  float* s_T = reinterpret_cast<float*>(smem + C::o_T);
+  float* s_db = reinterpret_cast<float*>(smem + C::o_db);
+  float* s_beta = reinterpret_cast<float*>(smem + C::o_beta);
+
+  const int tid = threadIdx.x;
+  const int64_t chunk_blocks = int64_t(max_chunks) * H;
+  if (int64_t(blockIdx.x) >= chunk_blocks) {
+    // positions not covered by any segment get zero gradients
+    int64_t cu_last = cu_at(cu, max_segs, N);
+    cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
+    const int64_t stride = int64_t(kTailBlocks) * kThreads;
+    const int64_t first = (int64_t(blockIdx.x) - chunk_blocks) * kThreads + tid;
+    const bf16 z = bf16(0.f);
+    for (int64_t i = first; i < (N - cu_last) * H * DK; i += stride) {
+      dq[cu_last * H * DK + i] = z;
+      dk[cu_last * H * DK + i] = z;
+      dg[cu_last * H * DK + i] = z;
+    }
+    for (int64_t i = first; i < (N - cu_last) * H * DV; i += stride) dv[cu_last * H * DV + i] = z;
+    for (int64_t i = first; i < (N - cu_last) * H; i += stride) dbeta[cu_last * H + i] = z;
+    return;
+  }
+  const int gc = int(blockIdx.x / H), h = int(blockIdx.x % H);
+  if (gc >= base[max_segs]) return;
+  // slot: the last i with base[i] <= gc (empty slots share their base with the next)
+  int lo = 0, hi = max_segs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= gc) lo = mid; else hi = mid - 1;
+  }
+  const int slot = lo;
+  const int64_t a = cu_at(cu, slot, N) + int64_t(kC) * (gc - base[slot]);
+  const int64_t seg_end = cu_at(cu, slot + 1, N);
+  const int L = int(seg_end - a < kC ? seg_end - a : kC);
+  const int nsub = (L + 15) >> 4;
+
+  // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads
+  stage_rows<DK>(s_q, RK, q, a, L, H, h, tid);
+  stage_rows<DK>(s_k, RK, k, a, L, H, h, tid);
+  stage_rows<DK>(s_qh, RK, g, a, L, H, h, tid);
+  stage_rows<DV>(s_v, RV, v, a, L, H, h, tid);
+  stage_rows<DV>(s_do, RV, dout, a, L, H, h, tid);
+  if (tid < kC) s_beta[tid] = tid < L ? to_f32(beta[(a + tid) * H + h]) : 0.f;
+  __syncthreads();
+  // per (sub-chunk, channel): 2^{c_t}, Qh over g, Kt, and the sub-chunk total
+  for (int p = tid; p < 4 * DK; p += kThreads) {
+    const int j = p / DK, d = p % DK;
+    float c = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = 16 * j + u;
+      c += to_f32(s_qh[t * RK + d]) * kLog2e;
+      const float e = ex2(c);
+      s_E[d * ES + t] = e;
+      s_qh[t * RK + d] = bf16(scale * to_f32(s_q[t * RK + d]) * e);
+      s_kt[t * RK + d] = bf16(s_beta[t] * to_f32(s_k[t * RK + d]) * ex2(-c));
+    }
+    s_T[j * DK + d] = c;
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
+  const int64_t soff = (int64_t(gc) * H + h) * DK * DV;
+
+  // Lambda in the two orientations: L1[E][dd] (rows e, column d = 16 (w DBW + dd) + n)
+  // and L2[D][ee] (rows d = 16 D + 4 g4 + j, column e = 16 (w EBW + ee) + n).
+  f32x4 L1[EB][DBW], L2[DB][EBW];
+#pragma unroll
+  for (int dd = 0; dd < DBW; ++dd) {
+    const int d = 16 * (w * DBW + dd) + n;
+#pragma unroll
+    for (int E = 0; E < EB; ++E) L1[E][dd] = unpack4(ld4(Lws + soff + int64_t(d) * DV + 16 * E + 4 * g4));
+  }
+  {
+    s16x4 eye;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eye[j] = (4 * g4 + j == n) ? short(0x3F80) : short(0);
+#pragma unroll
+    for (int D = 0; D < DB; ++D)
+#pragma unroll
+      for (int ee = 0; ee < EBW; ++ee) {
+        const s16x4 av = ld4(Lws + soff + int64_t(16 * D + n) * DV + 16 * (w * EBW + ee) + 4 * g4);
+        L2[D][ee] = mfma16(av, eye, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+  }
+
+  // S^T before sub-chunk i, columns of this wave: 2^{sum_{j<i} T_j} S_c^T plus the
+  // sub-chunks before i, each with Kt scaled by 2^{sum_{j<=j'<i} T_j'}.
+  f32x4 S[EB][DBW];
+  auto state_at = [&](int i) {
+#pragma unroll
+    for (int dd = 0; dd < DBW; ++dd) {
+      const int d = 16 * (w * DBW + dd) + n;
+      float bs = 0.f;
+      for (int j = 0; j < i; ++j) bs += s_T[j * DK + d];
+      const float f = ex2(bs);
+#pragma unroll
+      for (int E = 0; E < EB; ++E)
+        S[E][dd] = f * unpack4(ld4(Sws + soff + int64_t(d) * DV + 16 * E + 4 * g4));
+    }
+    for (int j = 0; j < i; ++j) {
+      s16x4 kb[DBW];
+#pragma unroll
+      for (int dd = 0; dd < DBW; ++dd) {
+        const int d = 16 * (w * DBW + dd) + n;
+        float ps = 0.f;
+        for (int jj = j; jj < i; ++jj) ps += s_T[jj * DK + d];
+        kb[dd] = pack4(ex2(ps) * unpack4(tr4(tr_ptr(s_kt, RK, 16 * j, 16 * (w * DBW + dd), lane))));
+      }
+#pragma unroll
+      for (int E = 0; E < EB; ++E) {
+        const s16x4 va = tr4(tr_ptr(s_v, RV, 16 * j, 16 * E, lane));
+#pragma unroll
+        for (int dd = 0; dd < DBW; ++dd) S[E][dd] = mfma16(va, kb[dd], S[E][dd]);
+      }
+    }
+  };
+
+  // G_c = sum_e Lambda_c * S_end, per key channel: the running gate gradient
+  float r[DBW];
+  state_at(nsub);
+#pragma unroll
+  for (int dd = 0; dd < DBW; ++dd) {
+    float p = 0.f;
+#pragma unroll
+    for (int E = 0; E < EB; ++E)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p = fmaf(L1[E][dd][j], S[E][dd][j], p);
+    p += __shfl_xor(p, 16, 64);
+    p += __shfl_xor(p, 32, 64);
+    r[dd] = p;
+  }
+
+  for (int i = nsub - 1; i >= 0; --i) {
+    state_at(i);
+    const int t0 = 16 * i;
+    // A, dA (rows t, column s) and dA^T (rows s, column t) of the sub-chunk
+    f32x4 Ac = {0.f, 0.f, 0.f, 0.f}, dA = Ac, dAT = Ac;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const s16x8 qa = ld8(s_qh + (t0 + n) * RK + 32 * kb + 8 * g4);
+      const s16x8 kt = ld8(s_kt + (t0 + n) * RK + 32 * kb + 8 * g4);
+      Ac = mfma32(qa, kt, Ac);
+    }
+#pragma unroll
+    for (int kb = 0; kb < DV / 32; ++kb) {
+      const s16x8 oa = ld8(s_do + (t0 + n) * RV + 32 * kb + 8 * g4);
+      const s16x8 va = ld8(s_v + (t0 + n) * RV + 32 * kb + 8 * g4);
+      dA = mfma32(oa, va, dA);
+      dAT = mfma32(va, oa, dAT);
+    }
+    f32x4 Am, dAm, dATm;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool lower = 4 * g4 + j >= n;  // row index >= column index
+      Am[j] = lower ? Ac[j] : 0.f;
+      dAm[j] = lower ? dA[j] : 0.f;
+      dATm[j] = (4 * g4 + j <= n) ? dAT[j] : 0.f;
+    }
+    const s16x4 opAT = pack4(Am);    // A-operand of A^T (rows s, slots t)
+    const s16x4 opdA = pack4(dATm);  // A-operand of dA (rows t, slots s)
+    const s16x4 opdAT = pack4(dAm);  // A-operand of dA^T (rows s, slots t)
+
+    float db[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dd = 0; dd < DBW; ++dd) {
+      const int Dblk = w * DBW + dd;
+      const int d = 16 * Dblk + n;
+      // dq: dO S_i^T + dA Kt, then scale 2^{c_t}
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int P = 0; P < EB / 2; ++P) {
+        const s16x8 oa = join(ld4(s_do + (t0 + n) * RV + 32 * P + 4 * g4),
+                              ld4(s_do + (t0 + n) * RV + 32 * P + 16 + 4 * g4));
+        const s16x8 sb = join(pack4(S[2 * P][dd]), pack4(S[2 * P + 1][dd]));
+        acc = mfma32(oa, sb, acc);
+      }
+      acc += mfma16(opdA, tr4(tr_ptr(s_kt, RK, t0, 16 * Dblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 Et = *reinterpret_cast<const f32x4*>(s_E + d * ES + t0 + 4 * g4);
+      const f32x4 qv = unpack4(tr4(tr_ptr(s_q, RK, t0, 16 * Dblk, lane)));
+      const f32x4 kv = unpack4(tr4(tr_ptr(s_k, RK, t0, 16 * Dblk, lane)));
+      float x[4], dqv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dqv[j] = scale * Et[j] * acc[j];
+        x[j] = qv[j] * dqv[j];
+      }
+      // u: 2^{T_i} Lambda_i v + dA^T Qh, then 2^{-c_s}
+      const float fT = ex2(s_T[i * DK + d]);
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int P = 0; P < EB / 2; ++P) {
+        const s16x8 va = join(ld4(s_v + (t0 + n) * RV + 32 * P + 4 * g4),
+                              ld4(s_v + (t0 + n) * RV + 32 * P + 16 + 4 * g4));
+        const s16x8 lb = join(pack4(fT * L1[2 * P][dd]), pack4(fT * L1[2 * P + 1][dd]));
+        acc = mfma32(va, lb, acc);
+      }
+      acc += mfma16(opdAT, tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
+      float dkv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + 4 * g4 + j;
+        const float u = acc[j] * __builtin_amdgcn_rcpf(Et[j]);
+        dkv[j] = s_beta[t] * u;
+        x[j] -= kv[j] * dkv[j];
+        db[j] = fmaf(kv[j], u, db[j]);
+      }
+      // dg: suffix sum over the sub-chunk's tokens, plus everything after it
+      float suf[4];
+      suf[3] = x[3];
+      suf[2] = x[2] + suf[3];
+      suf[1] = x[1] + suf[2];
+      suf[0] = x[0] + suf[1];
+      const float tg0 = __shfl(suf[0], n, 64), tg1 = __shfl(suf[0], n + 16, 64);
+      const float tg2 = __shfl(suf[0], n + 32, 64), tg3 = __shfl(suf[0], n + 48, 64);
+      const float after = (g4 < 1 ? tg1 : 0.f) + (g4 < 2 ? tg2 : 0.f) + (g4 < 3 ? tg3 : 0.f) + r[dd];
+      r[dd] += (tg0 + tg1) + (tg2 + tg3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + 4 * g4 + j;
+        if (t < L) {
+          const int64_t off = ((a + t) * H + h) * DK + d;
+          dq[off] = bf16(dqv[j]);
+          dk[off] = bf16(dkv[j]);
+          dg[off] = bf16(suf[j] + after);
+        }
+      }
+    }
+    // dbeta partials: over this lane's channels, then the 16 lanes of a row group
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float p = db[j];
+      p += __shfl_xor(p, 1, 64);
+      p += __shfl_xor(p, 2, 64);
+      p += __shfl_xor(p, 4, 64);
+      p += __shfl_xor(p, 8, 64);
+      if (n == 0) s_db[(i * 4 + w) * 16 + 4 * g4 + j] = p;
+    }
+
+    // dv: (Kt 2^{T_i}) Lambda_i + A^T dO, columns e of this wave
+#pragma unroll
+    for (int ee = 0; ee < EBW; ++ee) {
+      const int Eblk = w * EBW + ee;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int P = 0; P < DB / 2; ++P) {
+        const int d0 = 32 * P + 4 * g4, d1 = 32 * P + 16 + 4 * g4;
+        const f32x4 k0 = unpack4(ld4(s_kt + (t0 + n) * RK + d0));
+        const f32x4 k1 = unpack4(ld4(s_kt + (t0 + n) * RK + d1));
+        const f32x4 T0 = *reinterpret_cast<const f32x4*>(s_T + i * DK + d0);
+        const f32x4 T1 = *reinterpret_cast<const f32x4*>(s_T + i * DK + d1);
+        const s16x8 ka = join(pack4(k0[0] * ex2(T0[0]), k0[1] * ex2(T0[1]), k0[2] * ex2(T0[2]), k0[3] * ex2(T0[3])),
+                              pack4(k1[0] * ex2(T1[0]), k1[1] * ex2(T1[1]), k1[2] * ex2(T1[2]), k1[3] * ex2(T1[3])));
+        const s16x8 lb = join(pack4(L2[2 * P][ee]), pack4(L2[2 * P + 1][ee]));
+        acc = mfma32(ka, lb, acc);
+      }
+      acc += mfma16(opAT, tr4(tr_ptr(s_do, RV, t0, 16 * Eblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + 4 * g4 + j;
+        if (t < L) dv[((a + t) * H + h) * DV + 16 * Eblk + n] = bf16(acc[j]);
+      }
+    }
+
+    // Lambda before sub-chunk i: 2^{T_i} Lambda_i + Qh^T dO (every register index static)
+    if (i > 0) {
+#pragma unroll
+      for (int dd = 0; dd < DBW; ++dd) {
+        const int Dblk = w * DBW + dd;
+        const float fT = ex2(s_T[i * DK + 16 * Dblk + n]);
+        const s16x4 qb = tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane));
+#pragma unroll
+        for (int E = 0; E < EB; ++E)
+          L1[E][dd] = mfma16(tr4(tr_ptr(s_do, RV, t0, 16 * E, lane)), qb, fT * L1[E][dd]);
+      }
+#pragma unroll
+      for (int ee = 0; ee < EBW; ++ee) {
+        const s16x4 ob = tr4(tr_ptr(s_do, RV, t0, 16 * (w * EBW + ee), lane));
+#pragma unroll
+        for (int D = 0; D < DB; ++D) {
+          const f32x4 Tr = *reinterpret_cast<const f32x4*>(s_T + i * DK + 16 * D + 4 * g4);
+          const f32x4 fr = {ex2(Tr[0]), ex2(Tr[1]), ex2(Tr[2]), ex2(Tr[3])};
+          L2[D][ee] = mfma16(tr4(tr_ptr(s_qh, RK, t0, 16 * D, lane)), ob, fr * L2[D][ee]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < L) {
+    const int i = tid >> 4, s = tid & 15;
+    const float* p = s_db + i * 64 + s;
+    dbeta[(a + tid) * H + h] = bf16((p[0] + p[16]) + (p[32] + p[48]));
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                       const void* dout, const int32_t* cu, int32_t max_segs, int64_t N, int32_t H,
+                       float scale, const float* s0, const float* dF, void* dq, void* dk, void* dv,
+                       void* dg, void* db, float* dinit, int32_t* flags, void* ws,
+                       hipStream_t stream) {
+  using SC = StCfg<DK, DV>;
+  using CC = ChCfg<DK, DV>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_bwd_state_kernel<DK, DV>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SC::bytes);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_bwd_chunk_kernel<DK, DV>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, CC::bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t max_chunks = (N + kC - 1) / kC + max_segs;
+  const size_t plan_bytes = ((size_t(max_segs) + 1) * 4 + 255) / 256 * 256;
+  const size_t state_bytes = size_t(max_chunks) * H * DK * DV * 2;
+  int32_t* base = static_cast<int32_t*>(ws);
+  bf16* Sws = reinterpret_cast<bf16*>(static_cast<char*>(ws) + plan_bytes);
+  bf16* Lws = reinterpret_cast<bf16*>(static_cast<char*>(ws) + plan_bytes + state_bytes);
+  const bf16* qb = static_cast<const bf16*>(q);
+  const bf16* kb = static_cast<const bf16*>(k);
+  const bf16* vb = static_cast<const bf16*>(v);
+  const bf16* gb = static_cast<const bf16*>(g);
+  const bf16* bb = static_cast<const bf16*>(beta);
+  const bf16* ob = static_cast<const bf16*>(dout);
+  hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, max_segs, N,
+                     int32_t(max_chunks), base, flags);
+  hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV>), dim3(unsigned(2 * int64_t(max_segs) * H)),
+                     dim3(kThreads), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
+                     N, H, scale, s0, dF, Sws, Lws, dinit);
+  hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(max_chunks * H + kTailBlocks)),
+                     dim3(kThreads), CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
+                     int32_t(max_chunks), N, H, scale, Sws, Lws, static_cast<bf16*>(dq),
+                     static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
+                     static_cast<bf16*>(db));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool kda_chunk_bwd_supported(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                             int32_t max_segs) {
+  if (dtype != 0 || !(Dk == 64 || Dk == 128) || !(Dv == 64 || Dv == 128)) return false;
+  if (N < 1 || H < 1 || max_segs < 1) return false;
+  const int64_t max_chunks = (N + kC - 1) / kC + max_segs;
+  return max_chunks * H + kTailBlocks < (int64_t(1) << 31) && max_chunks < (int64_t(1) << 31);
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                                     int32_t max_segs) {
+  if (!kda_chunk_bwd_supported(N, H, Dk, Dv, dtype, max_segs)) return 0;
+  const int64_t max_chunks = (N + kC - 1) / kC + max_segs;
+  const size_t plan_bytes = ((size_t(max_segs) + 1) * 4 + 255) / 256 * 256;
+  return plan_bytes + 2 * size_t(max_chunks) * H * Dk * Dv * 2;
+}
+
+hipError_t launch_kda_chunk_backward(const void* q, const void* k, const void* v, const void* g,
+                                     const void* beta, const void* dout, const int32_t* cu,
+                                     int32_t max_segs, int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+                                     float scale, const float* initial_state,
+                                     const float* dfinal_state, void* dq, void* dk, void* dv,
+                                     void* dg, void* dbeta, float* dinitial_state, int32_t* flags,
+                                     void* workspace, hipStream_t stream) {
+#define PKV_BWD_LAUNCH(DK_, DV_)                                                                  \
+  if (Dk == DK_ && Dv == DV_)                                                                     \
+    return launch_dims<DK_, DV_>(q, k, v, g, beta, dout, cu, max_segs, N, H, scale, initial_state, \
+                                 dfinal_state, dq, dk, dv, dg, dbeta, dinitial_state, flags,       \
+                                 workspace, stream);
+  PKV_BWD_LAUNCH(64, 64)
+  PKV_BWD_LAUNCH(64, 128)
+  PKV_BWD_LAUNCH(128, 64)
+  PKV_BWD_LAUNCH(128, 128)
+#undef PKV_BWD_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -184,7 +184,7 @@ def _bwd_args(**kw):
     base = dict(q=A(0x10000000), k=A(0x20000000), v=A(0x30000000), g=A(0x40000000), beta=A(0x50000000),
                 cu=P, max_segs=4, N=256, H=2, Dk=64, Dv=64, scale=1.0, dtype=0, s0=NUL, do=A(0x58000000),
                 dF=NUL, dq=A(0x60000000), dk=A(0x68000000), dv=A(0x70000000), dg=A(0x78000000),
-                dbeta=A(0x7c000000), dinit=NUL, flags=NUL, stream=NUL)
+                dbeta=A(0x7c000000), dinit=NUL, flags=NUL, ws=NUL, ws_bytes=0, stream=NUL)
     base.update(kw)
     return tuple(base.values())
 
@@ -204,3 +204,22 @@ def _bwd_args(**kw):
 ])
 def test_backward_entry_validation(lib, kw, code):
     assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args(**kw)) == code
+
+
+def test_backward_workspace(lib):
+    """The chunked reverse pass (bf16, Dk and Dv in {64, 128}) keeps a chunk
+    table (max_segs + 1 int32, padded to 256 bytes) and two bf16 states of
+    Dk x Dv per (chunk, head), chunks = ceil(N / 64) + max_segs; other shapes
+    need none."""
+    size = lib.pkv_chunk_kda_varlen_backward_workspace_size
+    for N, H, Dk, Dv, S in [(65536, 32, 128, 128, 256), (256, 2, 64, 64, 4), (1000, 3, 64, 128, 7),
+                            (131072, 32, 128, 64, 8)]:
+        table = ((S + 1) * 4 + 255) // 256 * 256
+        assert size(N, H, Dk, Dv, S, 0) == table + 2 * ((N + 63) // 64 + S) * H * Dk * Dv * 2
+    assert size(256, 2, 32, 32, 4, 0) == 0 and size(256, 2, 64, 64, 4, 1) == 0
+    need = size(256, 2, 64, 64, 4, 0)
+    assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args()) == 3                       # missing
+    assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args(ws=P, ws_bytes=need - 1)) == 3
+    assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args(ws=ctypes.c_void_p(0x1080), ws_bytes=need)) == 3
+    # a workspace over an input
+    assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args(ws=ctypes.c_void_p(0x10000000), ws_bytes=need)) == 1
