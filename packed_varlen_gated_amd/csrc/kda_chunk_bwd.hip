@@ -161,23 +161,31 @@ __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(const int32_
 }
 
 // ---------------------------------------------------------------- state pass
+// One wave per 16 key channels (as in the chunk pass); the gate scan of a
+// chunk is split over four quarters of 16 tokens per channel; the raw inputs
+// of the next chunk are loaded into registers while the current one is
+// scanned and applied.
 template <int DK, int DV>
 struct StCfg {
+  static constexpr int NW = DK / 16, NT = 64 * NW;
   static constexpr int RX = DK + 8, RY = DV + 8;
   static constexpr int o_x = 0;                        // bf16 [64][RX]: g, then kbar or q'
   static constexpr int o_k = o_x + kC * RX * 2;        // bf16 [64][RX]: k or q
   static constexpr int o_y = o_k + kC * RX * 2;        // bf16 [64][RY]: v or do
   static constexpr int o_beta = o_y + kC * RY * 2;     // fp32 [64]
-  static constexpr int o_dec = o_beta + kC * 4;        // fp32 [DK]: 2^B
+  static constexpr int o_part = o_beta + kC * 4;       // fp32 [4][DK]: quarter sums of the gate
+  static constexpr int o_dec = o_part + 4 * DK * 4;    // fp32 [DK]: 2^B
   static constexpr int bytes = o_dec + DK * 4;
+  static constexpr int NX = kC * DK / 8 / NT;          // 16-byte pieces per thread, Dk-wide tile
+  static constexpr int NY = kC * DV / 8 / NT;          // ... Dv-wide tile
 };
 
 // Rows [a, a + L) of a [N, H, D] bf16 tensor (head h) into a [64][rs] LDS tile
 // with 16-byte loads; rows past L are zero.
-template <int D>
+template <int D, int NT = kThreads>
 __device__ __forceinline__ void stage_rows(bf16* tile, int rs, const bf16* __restrict__ src,
                                           int64_t a, int L, int32_t H, int h, int tid) {
-  for (int i = tid; i < kC * (D / 8); i += kThreads) {
+  for (int i = tid; i < kC * (D / 8); i += NT) {
     const int t = i / (D / 8), c8 = (i % (D / 8)) * 8;
     s16x8 x = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     if (t < L) x = *reinterpret_cast<const s16x8*>(src + ((a + t) * H + h) * D + c8);
@@ -186,7 +194,7 @@ __device__ __forceinline__ void stage_rows(bf16* tile, int rs, const bf16* __res
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads, 2) void kda_bwd_state_kernel(
+__global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 16) threads
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base, int32_t max_segs,
@@ -194,12 +202,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_state_kernel(
     const float* __restrict__ dfinal, bf16* __restrict__ Sws, bf16* __restrict__ Lws,
     float* __restrict__ dinit) {
   using C = StCfg<DK, DV>;
-  constexpr int EB = DV / 16, DBW = DK / 64;
+  constexpr int EB = DV / 16, NT = C::NT, NX = C::NX, NY = C::NY;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* s_x = reinterpret_cast<bf16*>(smem + C::o_x);
   bf16* s_k = reinterpret_cast<bf16*>(smem + C::o_k);
   bf16* s_y = reinterpret_cast<bf16*>(smem + C::o_y);
   float* s_beta = reinterpret_cast<float*>(smem + C::o_beta);
+  float* s_part = reinterpret_cast<float*>(smem + C::o_part);
   float* s_dec = reinterpret_cast<float*>(smem + C::o_dec);
 
   const int64_t pairs = int64_t(max_segs) * H;
@@ -212,116 +221,131 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_state_kernel(
   const int64_t start = nch > 0 ? cu_at(cu, slot, N) : 0;
   const int64_t end = nch > 0 ? cu_at(cu, slot + 1, N) : 0;
   const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
+  const int d_own = 16 * w + n;  // key channel of this lane's X tiles
 
-  // X^T tiles: rows e = 16E + 4g4 + j, column d = 16 (w DBW + dd) + n.
-  f32x4 X[EB][DBW];
+  // X^T tiles: rows e = 16E + 4g4 + j, column d_own.
+  f32x4 X[EB];
   const float* src = adjoint ? dfinal : initial_state;
 #pragma unroll
-  for (int dd = 0; dd < DBW; ++dd) {
-    const int d = 16 * (w * DBW + dd) + n;
+  for (int E = 0; E < EB; ++E)
+    X[E] = src ? *reinterpret_cast<const f32x4*>(src + sh + int64_t(d_own) * DV + 16 * E + 4 * g4)
+               : f32x4{0.f, 0.f, 0.f, 0.f};
+  auto store_state = [&](bf16* ws, int gc) {
+    const int64_t off = (int64_t(gc) * H + h) * DK * DV + int64_t(d_own) * DV + 4 * g4;
+#pragma unroll
+    for (int E = 0; E < EB; ++E) *reinterpret_cast<s16x4*>(ws + off + 16 * E) = pack4(X[E]);
+  };
+
+  // raw inputs of one chunk: g, k (or q), v (or do), beta, as 16-byte pieces
+  const bf16* srcK = adjoint ? q : k;
+  const bf16* srcY = adjoint ? dout : v;
+  s16x8 px[NX], pk[NX], py[NY];
+  float pb = 0.f;
+  auto fetch = [&](int c) {
+    const int64_t a = start + int64_t(kC) * c;
+    const int L = int(end - a < kC ? end - a : kC);
+#pragma unroll
+    for (int r = 0; r < NX; ++r) {
+      const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+      const int64_t off = ((a + t) * H + h) * DK + c8;
+      px[r] = t < L ? *reinterpret_cast<const s16x8*>(g + off) : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      pk[r] = t < L ? *reinterpret_cast<const s16x8*>(srcK + off) : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < NY; ++r) {
+      const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+      py[r] = t < L ? *reinterpret_cast<const s16x8*>(srcY + ((a + t) * H + h) * DV + c8)
+                    : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    pb = (!adjoint && tid < L) ? to_f32(beta[(a + tid) * H + h]) : 0.f;
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int r = 0; r < NX; ++r) {
+      const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+      *reinterpret_cast<s16x8*>(s_x + t * C::RX + c8) = px[r];
+      *reinterpret_cast<s16x8*>(s_k + t * C::RX + c8) = pk[r];
+    }
+#pragma unroll
+    for (int r = 0; r < NY; ++r) {
+      const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+      *reinterpret_cast<s16x8*>(s_y + t * C::RY + c8) = py[r];
+    }
+    if (tid < kC) s_beta[tid] = pb;
+  };
+
+  // forward role: S before chunks 0 .. nch-1 (the last chunk's update is not needed);
+  // adjoint role: Lambda after chunks nch-1 .. 0, each update applied
+  const int napply = adjoint ? nch : nch - 1;
+  auto chunk_of = [&](int it) { return adjoint ? nch - 1 - it : it; };
+  if (napply > 0) {
+    fetch(chunk_of(0));
+    put();
+    if (napply > 1) fetch(chunk_of(1));
+  }
+  for (int it = 0; it < nch; ++it) {
+    const int c = chunk_of(it);
+    store_state(adjoint ? Lws : Sws, cbase + c);
+    if (it >= napply) break;
+    __syncthreads();
+    {
+      // quarter p4 of the tokens of channel d: local log2 cumulative gate
+      const int p4 = tid / DK, d = tid % DK;
+      float lb[16], acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        acc += to_f32(s_x[(16 * p4 + u) * C::RX + d]) * kLog2e;
+        lb[u] = acc;
+      }
+      s_part[p4 * DK + d] = acc;
+      __syncthreads();
+      float off = 0.f, B = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const float x = s_part[pp * DK + d];
+        off += pp < p4 ? x : 0.f;
+        B += x;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int t = 16 * p4 + u;
+        const float kq = to_f32(s_k[t * C::RX + d]);
+        // forward: kbar = beta k 2^{B - b_t}; adjoint: q' = scale q 2^{b_t}
+        s_x[t * C::RX + d] = adjoint ? bf16(scale * kq * ex2(off + lb[u]))
+                                     : bf16(s_beta[t] * kq * ex2(B - (off + lb[u])));
+      }
+      if (p4 == 0) s_dec[d] = ex2(B);
+    }
+    __syncthreads();
+    {
+      const float dec = s_dec[d_own];
+#pragma unroll
+      for (int E = 0; E < EB; ++E) X[E] *= dec;
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        const s16x4 xb = tr4(tr_ptr(s_x, C::RX, 16 * kb, 16 * w, lane));
+#pragma unroll
+        for (int E = 0; E < EB; ++E) X[E] = mfma16(tr4(tr_ptr(s_y, C::RY, 16 * kb, 16 * E, lane)), xb, X[E]);
+      }
+    }
+    __syncthreads();
+    if (it + 1 < napply) {
+      put();
+      if (it + 2 < napply) fetch(chunk_of(it + 2));
+    }
+  }
+  if (adjoint && dinit != nullptr) {
 #pragma unroll
     for (int E = 0; E < EB; ++E)
-      X[E][dd] = src ? *reinterpret_cast<const f32x4*>(src + sh + int64_t(d) * DV + 16 * E + 4 * g4)
-                     : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  auto store_state = [&](bf16* ws, int gc) {
-    const int64_t off = (int64_t(gc) * H + h) * DK * DV;
-#pragma unroll
-    for (int dd = 0; dd < DBW; ++dd) {
-      const int d = 16 * (w * DBW + dd) + n;
-#pragma unroll
-      for (int E = 0; E < EB; ++E)
-        *reinterpret_cast<s16x4*>(ws + off + int64_t(d) * DV + 16 * E + 4 * g4) = pack4(X[E][dd]);
-    }
-  };
-  auto update = [&]() {
-#pragma unroll
-    for (int dd = 0; dd < DBW; ++dd) {
-      const float dec = s_dec[16 * (w * DBW + dd) + n];
-#pragma unroll
-      for (int E = 0; E < EB; ++E) X[E][dd] *= dec;
-    }
-#pragma unroll
-    for (int kb = 0; kb < kC / 16; ++kb) {
-      s16x4 xb[DBW];
-#pragma unroll
-      for (int dd = 0; dd < DBW; ++dd) xb[dd] = tr4(tr_ptr(s_x, C::RX, 16 * kb, 16 * (w * DBW + dd), lane));
-#pragma unroll
-      for (int E = 0; E < EB; ++E) {
-        const s16x4 ya = tr4(tr_ptr(s_y, C::RY, 16 * kb, 16 * E, lane));
-#pragma unroll
-        for (int dd = 0; dd < DBW; ++dd) X[E][dd] = mfma16(ya, xb[dd], X[E][dd]);
-      }
-    }
-  };
-  if (!adjoint) {
-    for (int c = 0; c < nch; ++c) {
-      store_state(Sws, cbase + c);
-      if (c == nch - 1) break;
-      const int64_t a = start + int64_t(kC) * c;
-      const int L = int(end - a < kC ? end - a : kC);
-      __syncthreads();
-      stage_rows<DK>(s_x, C::RX, g, a, L, H, h, tid);
-      stage_rows<DK>(s_k, C::RX, k, a, L, H, h, tid);
-      stage_rows<DV>(s_y, C::RY, v, a, L, H, h, tid);
-      if (tid < kC) s_beta[tid] = tid < L ? to_f32(beta[(a + tid) * H + h]) : 0.f;
-      __syncthreads();
-      if (tid < DK) {
-        // kbar_t = beta_t k_t 2^{B - b_t}, written over g
-        const int d = tid;
-        float B = 0.f;
-#pragma unroll 16
-        for (int t = 0; t < kC; ++t) B += to_f32(s_x[t * C::RX + d]) * kLog2e;
-        float b = 0.f;
-#pragma unroll 16
-        for (int t = 0; t < kC; ++t) {
-          b += to_f32(s_x[t * C::RX + d]) * kLog2e;
-          s_x[t * C::RX + d] = bf16(s_beta[t] * to_f32(s_k[t * C::RX + d]) * ex2(B - b));
-        }
-        s_dec[d] = ex2(B);
-      }
-      __syncthreads();
-      update();
-    }
-  } else {
-    for (int c = nch - 1; c >= 0; --c) {
-      store_state(Lws, cbase + c);
-      const int64_t a = start + int64_t(kC) * c;
-      const int L = int(end - a < kC ? end - a : kC);
-      __syncthreads();
-      stage_rows<DK>(s_x, C::RX, g, a, L, H, h, tid);
-      stage_rows<DK>(s_k, C::RX, q, a, L, H, h, tid);
-      stage_rows<DV>(s_y, C::RY, dout, a, L, H, h, tid);
-      __syncthreads();
-      if (tid < DK) {
-        // q'_t = scale q_t 2^{b_t}, written over g
-        const int d = tid;
-        float b = 0.f;
-#pragma unroll 16
-        for (int t = 0; t < kC; ++t) {
-          b += to_f32(s_x[t * C::RX + d]) * kLog2e;
-          s_x[t * C::RX + d] = bf16(scale * to_f32(s_k[t * C::RX + d]) * ex2(b));
-        }
-        s_dec[d] = ex2(b);
-      }
-      __syncthreads();
-      update();
-    }
-    if (dinit != nullptr) {
-#pragma unroll
-      for (int dd = 0; dd < DBW; ++dd) {
-        const int d = 16 * (w * DBW + dd) + n;
-#pragma unroll
-        for (int E = 0; E < EB; ++E)
-          *reinterpret_cast<f32x4*>(dinit + sh + int64_t(d) * DV + 16 * E + 4 * g4) = X[E][dd];
-      }
-    }
+      *reinterpret_cast<f32x4*>(dinit + sh + int64_t(d_own) * DV + 16 * E + 4 * g4) = X[E];
   }
 }
 
 // ---------------------------------------------------------------- chunk pass
 template <int DK, int DV>
 struct ChCfg {
+  // one wave per 16 key channels: 8 waves at Dk = 128, 4 at Dk = 64
+  static constexpr int NW = DK / 16, NT = 64 * NW;
   static constexpr int RK = DK + 8, RV = DV + 8, ES = kC + 4;
   static constexpr int o_q = 0;                         // bf16 [64][RK] raw q
   static constexpr int o_k = o_q + kC * RK * 2;         // raw k
@@ -331,13 +355,15 @@ struct ChCfg {
   static constexpr int o_do = o_v + kC * RV * 2;
   static constexpr int o_E = o_do + kC * RV * 2;        // fp32 [DK][ES]: 2^{c_t}, channel-major
   static constexpr int o_T = o_E + DK * ES * 4;         // fp32 [4][DK]: sub-chunk totals (log2)
-  static constexpr int o_db = o_T + 4 * DK * 4;         // fp32 [4 sub-chunks][4 waves][16]
-  static constexpr int o_beta = o_db + 4 * 4 * 16 * 4;  // fp32 [64]
+  static constexpr int o_fT = o_T + 4 * DK * 4;        // fp32 [4][DK]: 2^{T_i}
+  static constexpr int o_fP = o_fT + 4 * DK * 4;       // fp32 [10][DK]: 2^{T_j + .. + T_{i-1}}, j < i <= 4
+  static constexpr int o_db = o_fP + 10 * DK * 4;       // fp32 [4 sub-chunks][NW waves][16]
+  static constexpr int o_beta = o_db + 4 * NW * 16 * 4; // fp32 [64]
   static constexpr int bytes = o_beta + kC * 4;
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
+__global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 16) threads
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base, int32_t max_segs,
@@ -345,7 +371,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     const bf16* __restrict__ Lws, bf16* __restrict__ dq, bf16* __restrict__ dk,
     bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta) {
   using C = ChCfg<DK, DV>;
-  constexpr int DB = DK / 16, EB = DV / 16, DBW = DB / 4, EBW = EB / 4;
+  constexpr int NW = C::NW, NT = C::NT;
+  // key block w per wave; value blocks split over the waves (at Dv < Dk only the
+  // first Dv / 16 waves take one)
+  constexpr int DB = DK / 16, EB = DV / 16, DBW = 1, EBW = EB >= NW ? EB / NW : 1;
   constexpr int RK = C::RK, RV = C::RV, ES = C::ES;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* s_q = reinterpret_cast<bf16*>(smem + C::o_q);
@@ -358,6 +387,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
   float* s_T = reinterpret_cast<float*>(smem + C::o_T);
   float* s_db = reinterpret_cast<float*>(smem + C::o_db);
   float* s_beta = reinterpret_cast<float*>(smem + C::o_beta);
+  float* s_fT = reinterpret_cast<float*>(smem + C::o_fT);
+  float* s_fP = reinterpret_cast<float*>(smem + C::o_fP);
+  // row of 2^{T_j + .. + T_{i-1}} in s_fP
+  auto pidx = [](int j, int i) { return i * (i - 1) / 2 + j; };
 
   const int tid = threadIdx.x;
   const int64_t chunk_blocks = int64_t(max_chunks) * H;
@@ -365,8 +398,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     // positions not covered by any segment get zero gradients
     int64_t cu_last = cu_at(cu, max_segs, N);
     cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
-    const int64_t stride = int64_t(kTailBlocks) * kThreads;
-    const int64_t first = (int64_t(blockIdx.x) - chunk_blocks) * kThreads + tid;
+    const int64_t stride = int64_t(kTailBlocks) * NT;
+    const int64_t first = (int64_t(blockIdx.x) - chunk_blocks) * NT + tid;
     const bf16 z = bf16(0.f);
     for (int64_t i = first; i < (N - cu_last) * H * DK; i += stride) {
       dq[cu_last * H * DK + i] = z;
@@ -392,15 +425,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
   const int nsub = (L + 15) >> 4;
 
   // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads
-  stage_rows<DK>(s_q, RK, q, a, L, H, h, tid);
-  stage_rows<DK>(s_k, RK, k, a, L, H, h, tid);
-  stage_rows<DK>(s_qh, RK, g, a, L, H, h, tid);
-  stage_rows<DV>(s_v, RV, v, a, L, H, h, tid);
-  stage_rows<DV>(s_do, RV, dout, a, L, H, h, tid);
+  stage_rows<DK, NT>(s_q, RK, q, a, L, H, h, tid);
+  stage_rows<DK, NT>(s_k, RK, k, a, L, H, h, tid);
+  stage_rows<DK, NT>(s_qh, RK, g, a, L, H, h, tid);
+  stage_rows<DV, NT>(s_v, RV, v, a, L, H, h, tid);
+  stage_rows<DV, NT>(s_do, RV, dout, a, L, H, h, tid);
   if (tid < kC) s_beta[tid] = tid < L ? to_f32(beta[(a + tid) * H + h]) : 0.f;
   __syncthreads();
   // per (sub-chunk, channel): 2^{c_t}, Qh over g, Kt, and the sub-chunk total
-  for (int p = tid; p < 4 * DK; p += kThreads) {
+  for (int p = tid; p < 4 * DK; p += NT) {
     const int j = p / DK, d = p % DK;
     float c = 0.f;
 #pragma unroll
@@ -415,9 +448,31 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     s_T[j * DK + d] = c;
   }
   __syncthreads();
+  // decay factors of whole sub-chunks, once per chunk
+  if (tid < DK) {
+    const int d = tid;
+    float T[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      T[j] = s_T[j * DK + d];
+      s_fT[j * DK + d] = ex2(T[j]);
+    }
+#pragma unroll
+    for (int i = 1; i <= 4; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = i - 1; j >= 0; --j) {
+        acc += T[j];
+        s_fP[pidx(j, i) * DK + d] = ex2(acc);
+      }
+    }
+  }
+  __syncthreads();
 
   const int lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
   const int64_t soff = (int64_t(gc) * H + h) * DK * DV;
+  const bool ev_active = EB >= NW || w < EB;  // wave-uniform
+  auto eblk = [&](int ee) { return EB >= NW ? w * EBW + ee : w; };
 
   // Lambda in the two orientations: L1[E][dd] (rows e, column d = 16 (w DBW + dd) + n)
   // and L2[D][ee] (rows d = 16 D + 4 g4 + j, column e = 16 (w EBW + ee) + n).
@@ -436,33 +491,35 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
     for (int D = 0; D < DB; ++D)
 #pragma unroll
       for (int ee = 0; ee < EBW; ++ee) {
-        const s16x4 av = ld4(Lws + soff + int64_t(16 * D + n) * DV + 16 * (w * EBW + ee) + 4 * g4);
+        const s16x4 av = ev_active ? ld4(Lws + soff + int64_t(16 * D + n) * DV + 16 * eblk(ee) + 4 * g4)
+                                   : s16x4{0, 0, 0, 0};
         L2[D][ee] = mfma16(av, eye, f32x4{0.f, 0.f, 0.f, 0.f});
       }
   }
 
   // S^T before sub-chunk i, columns of this wave: 2^{sum_{j<i} T_j} S_c^T plus the
   // sub-chunks before i, each with Kt scaled by 2^{sum_{j<=j'<i} T_j'}.
+  s16x4 Sc[EB][DBW];
+#pragma unroll
+  for (int dd = 0; dd < DBW; ++dd)
+#pragma unroll
+    for (int E = 0; E < EB; ++E)
+      Sc[E][dd] = ld4(Sws + soff + int64_t(16 * (w * DBW + dd) + n) * DV + 16 * E + 4 * g4);
   f32x4 S[EB][DBW];
   auto state_at = [&](int i) {
 #pragma unroll
     for (int dd = 0; dd < DBW; ++dd) {
       const int d = 16 * (w * DBW + dd) + n;
-      float bs = 0.f;
-      for (int j = 0; j < i; ++j) bs += s_T[j * DK + d];
-      const float f = ex2(bs);
+      const float f = i > 0 ? s_fP[pidx(0, i) * DK + d] : 1.f;
 #pragma unroll
-      for (int E = 0; E < EB; ++E)
-        S[E][dd] = f * unpack4(ld4(Sws + soff + int64_t(d) * DV + 16 * E + 4 * g4));
+      for (int E = 0; E < EB; ++E) S[E][dd] = f * unpack4(Sc[E][dd]);
     }
     for (int j = 0; j < i; ++j) {
       s16x4 kb[DBW];
 #pragma unroll
       for (int dd = 0; dd < DBW; ++dd) {
         const int d = 16 * (w * DBW + dd) + n;
-        float ps = 0.f;
-        for (int jj = j; jj < i; ++jj) ps += s_T[jj * DK + d];
-        kb[dd] = pack4(ex2(ps) * unpack4(tr4(tr_ptr(s_kt, RK, 16 * j, 16 * (w * DBW + dd), lane))));
+        kb[dd] = pack4(s_fP[pidx(j, i) * DK + d] * unpack4(tr4(tr_ptr(s_kt, RK, 16 * j, 16 * (w * DBW + dd), lane))));
       }
 #pragma unroll
       for (int E = 0; E < EB; ++E) {
@@ -543,7 +600,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
         x[j] = qv[j] * dqv[j];
       }
       // u: 2^{T_i} Lambda_i v + dA^T Qh, then 2^{-c_s}
-      const float fT = ex2(s_T[i * DK + d]);
+      const float fT = s_fT[i * DK + d];
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int P = 0; P < EB / 2; ++P) {
@@ -591,23 +648,23 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
       p += __shfl_xor(p, 2, 64);
       p += __shfl_xor(p, 4, 64);
       p += __shfl_xor(p, 8, 64);
-      if (n == 0) s_db[(i * 4 + w) * 16 + 4 * g4 + j] = p;
+      if (n == 0) s_db[(i * NW + w) * 16 + 4 * g4 + j] = p;
     }
 
     // dv: (Kt 2^{T_i}) Lambda_i + A^T dO, columns e of this wave
 #pragma unroll
     for (int ee = 0; ee < EBW; ++ee) {
-      const int Eblk = w * EBW + ee;
+      if (!ev_active) break;
+      const int Eblk = eblk(ee);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int P = 0; P < DB / 2; ++P) {
         const int d0 = 32 * P + 4 * g4, d1 = 32 * P + 16 + 4 * g4;
         const f32x4 k0 = unpack4(ld4(s_kt + (t0 + n) * RK + d0));
         const f32x4 k1 = unpack4(ld4(s_kt + (t0 + n) * RK + d1));
-        const f32x4 T0 = *reinterpret_cast<const f32x4*>(s_T + i * DK + d0);
-        const f32x4 T1 = *reinterpret_cast<const f32x4*>(s_T + i * DK + d1);
-        const s16x8 ka = join(pack4(k0[0] * ex2(T0[0]), k0[1] * ex2(T0[1]), k0[2] * ex2(T0[2]), k0[3] * ex2(T0[3])),
-                              pack4(k1[0] * ex2(T1[0]), k1[1] * ex2(T1[1]), k1[2] * ex2(T1[2]), k1[3] * ex2(T1[3])));
+        const f32x4 F0 = *reinterpret_cast<const f32x4*>(s_fT + i * DK + d0);
+        const f32x4 F1 = *reinterpret_cast<const f32x4*>(s_fT + i * DK + d1);
+        const s16x8 ka = join(pack4(k0 * F0), pack4(k1 * F1));
         const s16x8 lb = join(pack4(L2[2 * P][ee]), pack4(L2[2 * P + 1][ee]));
         acc = mfma32(ka, lb, acc);
       }
@@ -624,7 +681,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
 #pragma unroll
       for (int dd = 0; dd < DBW; ++dd) {
         const int Dblk = w * DBW + dd;
-        const float fT = ex2(s_T[i * DK + 16 * Dblk + n]);
+        const float fT = s_fT[i * DK + 16 * Dblk + n];
         const s16x4 qb = tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane));
 #pragma unroll
         for (int E = 0; E < EB; ++E)
@@ -632,11 +689,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
       }
 #pragma unroll
       for (int ee = 0; ee < EBW; ++ee) {
-        const s16x4 ob = tr4(tr_ptr(s_do, RV, t0, 16 * (w * EBW + ee), lane));
+        if (!ev_active) break;
+        const s16x4 ob = tr4(tr_ptr(s_do, RV, t0, 16 * eblk(ee), lane));
 #pragma unroll
         for (int D = 0; D < DB; ++D) {
-          const f32x4 Tr = *reinterpret_cast<const f32x4*>(s_T + i * DK + 16 * D + 4 * g4);
-          const f32x4 fr = {ex2(Tr[0]), ex2(Tr[1]), ex2(Tr[2]), ex2(Tr[3])};
+          const f32x4 fr = *reinterpret_cast<const f32x4*>(s_fT + i * DK + 16 * D + 4 * g4);
           L2[D][ee] = mfma16(tr4(tr_ptr(s_qh, RK, t0, 16 * D, lane)), ob, fr * L2[D][ee]);
         }
       }
@@ -645,8 +702,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(
   __syncthreads();
   if (tid < L) {
     const int i = tid >> 4, s = tid & 15;
-    const float* p = s_db + i * 64 + s;
-    dbeta[(a + tid) * H + h] = bf16((p[0] + p[16]) + (p[32] + p[48]));
+    float sum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) sum += s_db[(i * NW + ww) * 16 + s];
+    dbeta[(a + tid) * H + h] = bf16(sum);
   }
 }
 
@@ -683,10 +742,10 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, max_segs, N,
                      int32_t(max_chunks), base, flags);
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV>), dim3(unsigned(2 * int64_t(max_segs) * H)),
-                     dim3(kThreads), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
+                     dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
                      N, H, scale, s0, dF, Sws, Lws, dinit);
   hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(max_chunks * H + kTailBlocks)),
-                     dim3(kThreads), CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
+                     dim3(CC::NT), CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
                      int32_t(max_chunks), N, H, scale, Sws, Lws, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
                      static_cast<bf16*>(db));
