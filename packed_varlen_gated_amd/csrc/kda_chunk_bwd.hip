@@ -180,19 +180,6 @@ struct StCfg {
   static constexpr int NY = kC * DV / 8 / NT;          // ... Dv-wide tile
 };
 
-// Rows [a, a + L) of a [N, H, D] bf16 tensor (head h) into a [64][rs] LDS tile
-// with 16-byte loads; rows past L are zero.
-template <int D, int NT = kThreads>
-__device__ __forceinline__ void stage_rows(bf16* tile, int rs, const bf16* __restrict__ src,
-                                          int64_t a, int L, int32_t H, int h, int tid) {
-  for (int i = tid; i < kC * (D / 8); i += NT) {
-    const int t = i / (D / 8), c8 = (i % (D / 8)) * 8;
-    s16x8 x = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (t < L) x = *reinterpret_cast<const s16x8*>(src + ((a + t) * H + h) * D + c8);
-    *reinterpret_cast<s16x8*>(tile + t * rs + c8) = x;
-  }
-}
-
 template <int DK, int DV>
 __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 16) threads
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -223,6 +210,19 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
   const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
   const int d_own = 16 * w + n;  // key channel of this lane's X tiles
 
+  if (nch == 0) {
+    // empty (or malformed) slot: its d initial state is the final-state cotangent
+    if (adjoint && dinit != nullptr) {
+#pragma unroll
+      for (int E = 0; E < EB; ++E) {
+        const int64_t off = sh + int64_t(d_own) * DV + 16 * E + 4 * g4;
+        *reinterpret_cast<f32x4*>(dinit + off) =
+            dfinal ? *reinterpret_cast<const f32x4*>(dfinal + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
+
   // X^T tiles: rows e = 16E + 4g4 + j, column d_own.
   f32x4 X[EB];
   const float* src = adjoint ? dfinal : initial_state;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
   const bf16* srcK = adjoint ? q : k;
   const bf16* srcY = adjoint ? dout : v;
   s16x8 px[NX], pk[NX], py[NY];
-  float pb = 0.f;
+  bf16 pb = bf16(0.f);  // converted when stored, so the load is not waited for early
   auto fetch = [&](int c) {
     const int64_t a = start + int64_t(kC) * c;
     const int L = int(end - a < kC ? end - a : kC);
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
       py[r] = t < L ? *reinterpret_cast<const s16x8*>(srcY + ((a + t) * H + h) * DV + c8)
                     : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    pb = (!adjoint && tid < L) ? to_f32(beta[(a + tid) * H + h]) : 0.f;
+    pb = (!adjoint && tid < L) ? beta[(a + tid) * H + h] : bf16(0.f);
   };
   auto put = [&]() {
 #pragma unroll
@@ -271,22 +271,14 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
       const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
       *reinterpret_cast<s16x8*>(s_y + t * C::RY + c8) = py[r];
     }
-    if (tid < kC) s_beta[tid] = pb;
+    if (tid < kC) s_beta[tid] = to_f32(pb);
   };
 
   // forward role: S before chunks 0 .. nch-1 (the last chunk's update is not needed);
   // adjoint role: Lambda after chunks nch-1 .. 0, each update applied
   const int napply = adjoint ? nch : nch - 1;
   auto chunk_of = [&](int it) { return adjoint ? nch - 1 - it : it; };
-  if (napply > 0) {
-    fetch(chunk_of(0));
-    put();
-    if (napply > 1) fetch(chunk_of(1));
-  }
-  for (int it = 0; it < nch; ++it) {
-    const int c = chunk_of(it);
-    store_state(adjoint ? Lws : Sws, cbase + c);
-    if (it >= napply) break;
+  auto step = [&]() {  // the chunk whose inputs are in LDS: scan, then update X
     __syncthreads();
     {
       // quarter p4 of the tokens of channel d: local log2 cumulative gate
@@ -317,22 +309,36 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
       if (p4 == 0) s_dec[d] = ex2(B);
     }
     __syncthreads();
-    {
-      const float dec = s_dec[d_own];
+    const float dec = s_dec[d_own];
 #pragma unroll
-      for (int E = 0; E < EB; ++E) X[E] *= dec;
+    for (int E = 0; E < EB; ++E) X[E] *= dec;
 #pragma unroll
-      for (int kb = 0; kb < kC / 16; ++kb) {
-        const s16x4 xb = tr4(tr_ptr(s_x, C::RX, 16 * kb, 16 * w, lane));
+    for (int kb = 0; kb < kC / 16; ++kb) {
+      const s16x4 xb = tr4(tr_ptr(s_x, C::RX, 16 * kb, 16 * w, lane));
 #pragma unroll
-        for (int E = 0; E < EB; ++E) X[E] = mfma16(tr4(tr_ptr(s_y, C::RY, 16 * kb, 16 * E, lane)), xb, X[E]);
-      }
+      for (int E = 0; E < EB; ++E) X[E] = mfma16(tr4(tr_ptr(s_y, C::RY, 16 * kb, 16 * E, lane)), xb, X[E]);
     }
     __syncthreads();
-    if (it + 1 < napply) {
-      put();
-      if (it + 2 < napply) fetch(chunk_of(it + 2));
-    }
+  };
+  // Branch-free main loop (one vector-memory counter covers loads and stores, so a
+  // conditional store or load here would make the wait for the prefetched inputs wait
+  // for the stores too): the prefetch index is clamped, and the last step is peeled.
+  bf16* ws_out = adjoint ? Lws : Sws;
+  if (napply > 0) {
+    fetch(chunk_of(0));
+    put();
+    fetch(chunk_of(napply > 1 ? 1 : 0));
+  }
+  store_state(ws_out, cbase + chunk_of(0));
+  for (int it = 0; it < napply - 1; ++it) {
+    step();
+    put();
+    fetch(chunk_of(it + 2 < napply ? it + 2 : napply - 1));
+    store_state(ws_out, cbase + chunk_of(it + 1));
+  }
+  if (napply > 0) {
+    step();
+    if (napply < nch) store_state(ws_out, cbase + chunk_of(napply));
   }
   if (adjoint && dinit != nullptr) {
 #pragma unroll
@@ -424,13 +430,43 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
   const int L = int(seg_end - a < kC ? seg_end - a : kC);
   const int nsub = (L + 15) >> 4;
 
-  // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads
-  stage_rows<DK, NT>(s_q, RK, q, a, L, H, h, tid);
-  stage_rows<DK, NT>(s_k, RK, k, a, L, H, h, tid);
-  stage_rows<DK, NT>(s_qh, RK, g, a, L, H, h, tid);
-  stage_rows<DV, NT>(s_v, RV, v, a, L, H, h, tid);
-  stage_rows<DV, NT>(s_do, RV, dout, a, L, H, h, tid);
-  if (tid < kC) s_beta[tid] = tid < L ? to_f32(beta[(a + tid) * H + h]) : 0.f;
+  // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads, all
+  // issued before the first LDS store
+  {
+    constexpr int NX = kC * DK / 8 / NT, NY = kC * DV / 8 / NT;
+    const s16x8 z8 = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    s16x8 xq[NX], xk[NX], xg[NX], xv[NY], xd[NY];
+#pragma unroll
+    for (int r = 0; r < NX; ++r) {
+      const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+      const int64_t off = ((a + t) * H + h) * DK + c8;
+      xq[r] = t < L ? *reinterpret_cast<const s16x8*>(q + off) : z8;
+      xk[r] = t < L ? *reinterpret_cast<const s16x8*>(k + off) : z8;
+      xg[r] = t < L ? *reinterpret_cast<const s16x8*>(g + off) : z8;
+    }
+#pragma unroll
+    for (int r = 0; r < NY; ++r) {
+      const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+      const int64_t off = ((a + t) * H + h) * DV + c8;
+      xv[r] = t < L ? *reinterpret_cast<const s16x8*>(v + off) : z8;
+      xd[r] = t < L ? *reinterpret_cast<const s16x8*>(dout + off) : z8;
+    }
+    const bf16 xb = tid < L ? beta[(a + tid) * H + h] : bf16(0.f);
+#pragma unroll
+    for (int r = 0; r < NX; ++r) {
+      const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+      *reinterpret_cast<s16x8*>(s_q + t * RK + c8) = xq[r];
+      *reinterpret_cast<s16x8*>(s_k + t * RK + c8) = xk[r];
+      *reinterpret_cast<s16x8*>(s_qh + t * RK + c8) = xg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < NY; ++r) {
+      const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+      *reinterpret_cast<s16x8*>(s_v + t * RV + c8) = xv[r];
+      *reinterpret_cast<s16x8*>(s_do + t * RV + c8) = xd[r];
+    }
+    if (tid < kC) s_beta[tid] = to_f32(xb);
+  }
   __syncthreads();
   // per (sub-chunk, channel): 2^{c_t}, Qh over g, Kt, and the sub-chunk total
   for (int p = tid; p < 4 * DK; p += NT) {
@@ -483,10 +519,11 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
 #pragma unroll
     for (int E = 0; E < EB; ++E) L1[E][dd] = unpack4(ld4(Lws + soff + int64_t(d) * DV + 16 * E + 4 * g4));
   }
-  {
-    s16x4 eye;
+  // identity 16x16 operand (either side)
+  s16x4 eye;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) eye[j] = (4 * g4 + j == n) ? short(0x3F80) : short(0);
+  for (int j = 0; j < 4; ++j) eye[j] = (4 * g4 + j == n) ? short(0x3F80) : short(0);
+  {
 #pragma unroll
     for (int D = 0; D < DB; ++D)
 #pragma unroll
@@ -511,8 +548,9 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
     for (int dd = 0; dd < DBW; ++dd) {
       const int d = 16 * (w * DBW + dd) + n;
       const float f = i > 0 ? s_fP[pidx(0, i) * DK + d] : 1.f;
+      // S_c^T unpacked by a product with the identity, then scaled
 #pragma unroll
-      for (int E = 0; E < EB; ++E) S[E][dd] = f * unpack4(Sc[E][dd]);
+      for (int E = 0; E < EB; ++E) S[E][dd] = f * mfma16(eye, Sc[E][dd], f32x4{0.f, 0.f, 0.f, 0.f});
     }
     for (int j = 0; j < i; ++j) {
       s16x4 kb[DBW];
@@ -575,6 +613,23 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
     const s16x4 opdA = pack4(dATm);  // A-operand of dA (rows t, slots s)
     const s16x4 opdAT = pack4(dAm);  // A-operand of dA^T (rows s, slots t)
 
+    // 2^{T_i} Lambda_i in both orientations: used by u and dv, and the update
+    // to Lambda before sub-chunk i accumulates onto it
+#pragma unroll
+    for (int dd = 0; dd < DBW; ++dd) {
+      const float fT = s_fT[i * DK + 16 * (w * DBW + dd) + n];
+#pragma unroll
+      for (int E = 0; E < EB; ++E) L1[E][dd] *= fT;
+    }
+    if (ev_active) {
+#pragma unroll
+      for (int D = 0; D < DB; ++D) {
+        const f32x4 fr = *reinterpret_cast<const f32x4*>(s_fT + i * DK + 16 * D + 4 * g4);
+#pragma unroll
+        for (int ee = 0; ee < EBW; ++ee) L2[D][ee] *= fr;
+      }
+    }
+
     float db[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dd = 0; dd < DBW; ++dd) {
@@ -599,14 +654,13 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
         dqv[j] = scale * Et[j] * acc[j];
         x[j] = qv[j] * dqv[j];
       }
-      // u: 2^{T_i} Lambda_i v + dA^T Qh, then 2^{-c_s}
-      const float fT = s_fT[i * DK + d];
+      // u: (2^{T_i} Lambda_i) v + dA^T Qh, then 2^{-c_s}
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int P = 0; P < EB / 2; ++P) {
         const s16x8 va = join(ld4(s_v + (t0 + n) * RV + 32 * P + 4 * g4),
                               ld4(s_v + (t0 + n) * RV + 32 * P + 16 + 4 * g4));
-        const s16x8 lb = join(pack4(fT * L1[2 * P][dd]), pack4(fT * L1[2 * P + 1][dd]));
+        const s16x8 lb = join(pack4(L1[2 * P][dd]), pack4(L1[2 * P + 1][dd]));
         acc = mfma32(va, lb, acc);
       }
       acc += mfma16(opdAT, tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
@@ -651,7 +705,7 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
       if (n == 0) s_db[(i * NW + w) * 16 + 4 * g4 + j] = p;
     }
 
-    // dv: (Kt 2^{T_i}) Lambda_i + A^T dO, columns e of this wave
+    // dv: Kt (2^{T_i} Lambda_i) + A^T dO, columns e of this wave
 #pragma unroll
     for (int ee = 0; ee < EBW; ++ee) {
       if (!ev_active) break;
@@ -660,11 +714,7 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
 #pragma unroll
       for (int P = 0; P < DB / 2; ++P) {
         const int d0 = 32 * P + 4 * g4, d1 = 32 * P + 16 + 4 * g4;
-        const f32x4 k0 = unpack4(ld4(s_kt + (t0 + n) * RK + d0));
-        const f32x4 k1 = unpack4(ld4(s_kt + (t0 + n) * RK + d1));
-        const f32x4 F0 = *reinterpret_cast<const f32x4*>(s_fT + i * DK + d0);
-        const f32x4 F1 = *reinterpret_cast<const f32x4*>(s_fT + i * DK + d1);
-        const s16x8 ka = join(pack4(k0 * F0), pack4(k1 * F1));
+        const s16x8 ka = join(ld4(s_kt + (t0 + n) * RK + d0), ld4(s_kt + (t0 + n) * RK + d1));
         const s16x8 lb = join(pack4(L2[2 * P][ee]), pack4(L2[2 * P + 1][ee]));
         acc = mfma32(ka, lb, acc);
       }
@@ -680,22 +730,16 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
     if (i > 0) {
 #pragma unroll
       for (int dd = 0; dd < DBW; ++dd) {
-        const int Dblk = w * DBW + dd;
-        const float fT = s_fT[i * DK + 16 * Dblk + n];
-        const s16x4 qb = tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane));
+        const s16x4 qb = tr4(tr_ptr(s_qh, RK, t0, 16 * (w * DBW + dd), lane));
 #pragma unroll
-        for (int E = 0; E < EB; ++E)
-          L1[E][dd] = mfma16(tr4(tr_ptr(s_do, RV, t0, 16 * E, lane)), qb, fT * L1[E][dd]);
+        for (int E = 0; E < EB; ++E) L1[E][dd] = mfma16(tr4(tr_ptr(s_do, RV, t0, 16 * E, lane)), qb, L1[E][dd]);
       }
 #pragma unroll
       for (int ee = 0; ee < EBW; ++ee) {
         if (!ev_active) break;
         const s16x4 ob = tr4(tr_ptr(s_do, RV, t0, 16 * eblk(ee), lane));
 #pragma unroll
-        for (int D = 0; D < DB; ++D) {
-          const f32x4 fr = *reinterpret_cast<const f32x4*>(s_fT + i * DK + 16 * D + 4 * g4);
-          L2[D][ee] = mfma16(tr4(tr_ptr(s_qh, RK, t0, 16 * D, lane)), ob, fr * L2[D][ee]);
-        }
+        for (int D = 0; D < DB; ++D) L2[D][ee] = mfma16(tr4(tr_ptr(s_qh, RK, t0, 16 * D, lane)), ob, L2[D][ee]);
       }
     }
   }
