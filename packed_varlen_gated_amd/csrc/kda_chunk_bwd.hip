@@ -110,6 +110,16 @@ __device__ __forceinline__ const bf16* tr_ptr(const bf16* tile, int rs, int r0, 
 __device__ __forceinline__ s16x4 ld4(const bf16* p) { return *reinterpret_cast<const s16x4*>(p); }
 __device__ __forceinline__ s16x8 ld8(const bf16* p) { return *reinterpret_cast<const s16x8*>(p); }
 
+// Raw buffer resource over [base, base + bytes): accesses at offsets past the end
+// are dropped (stores) or read 0 (loads).
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufFlags);
+}
+__device__ __forceinline__ void st_bf16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, bf16(x)), r, int(byte_off), 0, 0);
+}
+
 // cu_seqlens entry i; a NULL cu_seqlens is the single segment [0, N).
 __device__ __forceinline__ int64_t cu_at(const int32_t* cu, int i, int64_t N) {
   return cu != nullptr ? int64_t(cu[i]) : (i == 0 ? 0 : N);
@@ -429,6 +439,11 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
   const int64_t seg_end = cu_at(cu, slot + 1, N);
   const int L = int(seg_end - a < kC ? seg_end - a : kC);
   const int nsub = (L + 15) >> 4;
+  // gradient rows of this chunk's tokens (all heads); stores past token L are dropped
+  const auto r_dq = rsrc(dq + a * H * DK, uint32_t(L) * H * DK * 2);
+  const auto r_dk = rsrc(dk + a * H * DK, uint32_t(L) * H * DK * 2);
+  const auto r_dg = rsrc(dg + a * H * DK, uint32_t(L) * H * DK * 2);
+  const auto r_dv = rsrc(dv + a * H * DV, uint32_t(L) * H * DV * 2);
 
   // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads, all
   // issued before the first LDS store
@@ -685,13 +700,10 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
       r[dd] += (tg0 + tg1) + (tg2 + tg3);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int t = t0 + 4 * g4 + j;
-        if (t < L) {
-          const int64_t off = ((a + t) * H + h) * DK + d;
-          dq[off] = bf16(dqv[j]);
-          dk[off] = bf16(dkv[j]);
-          dg[off] = bf16(suf[j] + after);
-        }
+        const uint32_t off = ((uint32_t(t0 + 4 * g4 + j) * H + h) * DK + d) * 2;
+        st_bf16(r_dq, off, dqv[j]);
+        st_bf16(r_dk, off, dkv[j]);
+        st_bf16(r_dg, off, suf[j] + after);
       }
     }
     // dbeta partials: over this lane's channels, then the 16 lanes of a row group
@@ -720,10 +732,8 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
       }
       acc += mfma16(opAT, tr4(tr_ptr(s_do, RV, t0, 16 * Eblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t0 + 4 * g4 + j;
-        if (t < L) dv[((a + t) * H + h) * DV + 16 * Eblk + n] = bf16(acc[j]);
-      }
+      for (int j = 0; j < 4; ++j)
+        st_bf16(r_dv, ((uint32_t(t0 + 4 * g4 + j) * H + h) * DV + 16 * Eblk + n) * 2, acc[j]);
     }
 
     // Lambda before sub-chunk i: 2^{T_i} Lambda_i + Qh^T dO (every register index static)
