@@ -246,7 +246,7 @@ def main():
         log(f"backward: {call_s * 1e3:.3f} ms per call; {achieved:.0f} GB/s = "
             f"{achieved / HBM_PEAK_GBS:.3f} of HBM peak; flags {int(flags.item())}")
         print(json.dumps({
-            "metric": "packed tokens/sec for chunk_kda_varlen bwd at H=32,D=128",
+            "metric": f"packed tokens/sec for chunk_kda_varlen bwd at H={H},D={cfg.Dk}",
             "value": N / call_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",

@@ -130,17 +130,39 @@ __device__ __forceinline__ bool bad_segment(int64_t start, int64_t end, int64_t 
 }
 
 // ---------------------------------------------------------------- plan
-// base[i] = global index of slot i's first chunk, base[max_segs] = total, all
-// capped at max_chunks (reached only when cu_seqlens is invalid, which sets
-// the flag; valid slots tile [0, cu[max_segs]) and need at most max_chunks).
-__global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(const int32_t* __restrict__ cu,
-                                                                    int32_t max_segs, int64_t N,
-                                                                    int32_t max_chunks,
-                                                                    int32_t* __restrict__ base,
-                                                                    int32_t* __restrict__ flags) {
+// Exclusive scan of x over the threads of the work-group (int64), in LDS.
+__device__ __forceinline__ int64_t block_excl_scan(int64_t x, int64_t* s_scan, int64_t& total) {
+  const int tid = threadIdx.x;
+  s_scan[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int64_t y = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += y;
+    __syncthreads();
+  }
+  const int64_t incl = s_scan[tid];
+  total = s_scan[kPlanThreads - 1];
+  __syncthreads();
+  return incl - x;
+}
+
+// base[i]  = global index of slot i's first chunk (base[max_segs] = chunks);
+// pbase[i] = index of slot i's first piece: a segment of n chunks is one piece,
+//            or, when n exceeds max(per-CU share, 32), m = min(16, ceil(n / R))
+//            pieces of nearly equal length (piece j = chunks [n j / m, n (j+1) / m)),
+//            R = max(32, share / 4), so no (segment, head) chain is much longer
+//            than the share; empty slots also get one (empty) piece;
+// sbase[i] = index of slot i's first piece summary (cut segments only).
+// All are capped at their workspace bounds (reached only when cu_seqlens is
+// invalid, which sets the flag).
+__global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
+    const int32_t* __restrict__ cu, int32_t max_segs, int64_t N, int32_t H, int32_t max_chunks,
+    int32_t max_pieces, int32_t max_sums, int32_t* __restrict__ base, int32_t* __restrict__ pbase,
+    int32_t* __restrict__ sbase, int32_t* __restrict__ flags) {
   __shared__ int64_t s_scan[kPlanThreads];
   const int tid = threadIdx.x;
-  int64_t running = 0;
+  int64_t running = 0, tot;
   for (int tile0 = 0; tile0 < max_segs; tile0 += kPlanThreads) {
     const int slot = tile0 + tid;
     int64_t n = 0;
@@ -152,22 +174,49 @@ __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(const int32_
         n = (end - start + kC - 1) / kC;
       }
     }
-    s_scan[tid] = n;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-      const int64_t x = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += x;
-      __syncthreads();
-    }
-    if (slot < max_segs) {
-      const int64_t b = running + s_scan[tid] - n;
-      base[slot] = int32_t(b < max_chunks ? b : max_chunks);
-    }
-    running += s_scan[kPlanThreads - 1];
-    __syncthreads();
+    const int64_t b = running + block_excl_scan(n, s_scan, tot);
+    if (slot < max_segs) base[slot] = int32_t(b < max_chunks ? b : max_chunks);
+    running += tot;
   }
-  if (tid == 0) base[max_segs] = int32_t(running < max_chunks ? running : max_chunks);
+  const int64_t chunks = running < max_chunks ? running : max_chunks;
+  if (tid == 0) base[max_segs] = int32_t(chunks);
+  __threadfence_block();
+  __syncthreads();
+  const int64_t share = (chunks * H + 255) / 256;
+  const int64_t thr = share > 32 ? share : 32;
+  const int64_t R = (share + 3) / 4 > 32 ? (share + 3) / 4 : 32;
+  int64_t run_p = 0, run_s = 0, tot_p, tot_s;
+  for (int tile0 = 0; tile0 < max_segs; tile0 += kPlanThreads) {
+    const int slot = tile0 + tid;
+    int64_t m = 0, ms = 0;
+    if (slot < max_segs) {
+      const int64_t n = int64_t(base[slot + 1]) - base[slot];
+      m = n > thr ? ((n + R - 1) / R < 16 ? (n + R - 1) / R : 16) : 1;
+      ms = m > 1 ? m : 0;
+    }
+    const int64_t bp = run_p + block_excl_scan(m, s_scan, tot_p);
+    const int64_t bs = run_s + block_excl_scan(ms, s_scan, tot_s);
+    if (slot < max_segs) {
+      pbase[slot] = int32_t(bp < max_pieces ? bp : max_pieces);
+      sbase[slot] = int32_t(bs < max_sums ? bs : max_sums);
+    }
+    run_p += tot_p;
+    run_s += tot_s;
+  }
+  if (tid == 0) {
+    pbase[max_segs] = int32_t(run_p < max_pieces ? run_p : max_pieces);
+    sbase[max_segs] = int32_t(run_s < max_sums ? run_s : max_sums);
+  }
+}
+
+// Last index i in [0, n) with tab[i] <= x (tab non-decreasing, tab[0] <= x).
+__device__ __forceinline__ int last_le(const int32_t* tab, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 // ---------------------------------------------------------------- state pass
@@ -190,14 +239,22 @@ struct StCfg {
   static constexpr int NY = kC * DV / 8 / NT;          // ... Dv-wide tile
 };
 
-template <int DK, int DV>
+// kSum = false (walk): one work-group per (piece, head, role); the state at the
+// piece's start (S role) or the adjoint at its end (Lambda role) is composed from
+// the summaries of the other pieces, then the piece's chunks are walked and the
+// state before (S) or adjoint after (Lambda) every chunk is stored.
+// kSum = true (summary): one work-group per (summary slot, head, role) of a cut
+// segment: the piece walked from a zero state; its end state (S role: after the
+// piece; Lambda role: before it) and the product of its decays are stored.
+template <int DK, int DV, bool kSum>
 __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 16) threads
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ base, int32_t max_segs,
-    int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase, int32_t max_segs,
+    int32_t units, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
     const float* __restrict__ dfinal, bf16* __restrict__ Sws, bf16* __restrict__ Lws,
-    float* __restrict__ dinit) {
+    float* __restrict__ sumL, float* __restrict__ sumD, float* __restrict__ dinit) {
   using C = StCfg<DK, DV>;
   constexpr int EB = DV / 16, NT = C::NT, NX = C::NX, NY = C::NY;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -208,19 +265,28 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
   float* s_part = reinterpret_cast<float*>(smem + C::o_part);
   float* s_dec = reinterpret_cast<float*>(smem + C::o_dec);
 
-  const int64_t pairs = int64_t(max_segs) * H;
+  const int64_t pairs = int64_t(units) * H;
   const bool adjoint = int64_t(blockIdx.x) >= pairs;
   const int64_t idx = adjoint ? int64_t(blockIdx.x) - pairs : int64_t(blockIdx.x);
-  const int slot = int(idx / H), h = int(idx % H);
+  const int u = int(idx / H), h = int(idx % H);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
+  // the unit: a summary slot or a piece, its segment slot and piece index j of m
+  const int32_t* ubase = kSum ? sbase : pbase;
+  if (u >= ubase[max_segs]) return;
+  const int slot = last_le(ubase, max_segs, u);
+  const int j = u - ubase[slot];
+  const int m = pbase[slot + 1] - pbase[slot];
+  if (kSum && (adjoint ? j == 0 : j == m - 1)) return;  // summary not needed
   const int cbase = base[slot];
-  const int nch = base[slot + 1] - cbase;
+  const int64_t nseg = int64_t(base[slot + 1]) - cbase;
+  const int c0 = int(nseg * j / m), c1 = int(nseg * (j + 1) / m);
+  const int nch = c1 - c0;  // chunks of this piece
   const int64_t start = nch > 0 ? cu_at(cu, slot, N) : 0;
   const int64_t end = nch > 0 ? cu_at(cu, slot + 1, N) : 0;
   const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
   const int d_own = 16 * w + n;  // key channel of this lane's X tiles
 
-  if (nch == 0) {
+  if (!kSum && nch == 0) {
     // empty (or malformed) slot: its d initial state is the final-state cotangent
     if (adjoint && dinit != nullptr) {
 #pragma unroll
@@ -232,14 +298,38 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
     }
     return;
   }
+  // summary storage of slot s: L [s][role][h][Dk][Dv], D [s][role][h][Dk]
+  auto sumL_at = [&](int s_, bool adj) {
+    return sumL + ((int64_t(s_) * 2 + adj) * H + h) * DK * DV + int64_t(d_own) * DV + 4 * g4;
+  };
+  auto sumD_at = [&](int s_, bool adj) { return sumD + ((int64_t(s_) * 2 + adj) * H + h) * DK + d_own; };
 
   // X^T tiles: rows e = 16E + 4g4 + j, column d_own.
   f32x4 X[EB];
-  const float* src = adjoint ? dfinal : initial_state;
+  float Dprod = 1.f;  // product of the decays applied (summary)
+  if (kSum) {
 #pragma unroll
-  for (int E = 0; E < EB; ++E)
-    X[E] = src ? *reinterpret_cast<const f32x4*>(src + sh + int64_t(d_own) * DV + 16 * E + 4 * g4)
-               : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int E = 0; E < EB; ++E) X[E] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    const float* src = adjoint ? dfinal : initial_state;
+#pragma unroll
+    for (int E = 0; E < EB; ++E)
+      X[E] = src ? *reinterpret_cast<const f32x4*>(src + sh + int64_t(d_own) * DV + 16 * E + 4 * g4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    // compose over the other pieces: S <- D S + L over pieces 0 .. j-1 in order;
+    // Lambda <- D Lambda + L' over pieces m-1 .. j+1
+    if (m > 1) {
+      const int nj = adjoint ? m - 1 - j : j;
+      for (int t = 0; t < nj; ++t) {
+        const int jj = adjoint ? m - 1 - t : t;
+        const int s_ = sbase[slot] + jj;
+        const float dprod = *sumD_at(s_, adjoint);
+        const float* Lp = sumL_at(s_, adjoint);
+#pragma unroll
+        for (int E = 0; E < EB; ++E) X[E] = dprod * X[E] + *reinterpret_cast<const f32x4*>(Lp + 16 * E);
+      }
+    }
+  }
   auto store_state = [&](bf16* ws, int gc) {
     const int64_t off = (int64_t(gc) * H + h) * DK * DV + int64_t(d_own) * DV + 4 * g4;
 #pragma unroll
@@ -284,10 +374,10 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
     if (tid < kC) s_beta[tid] = to_f32(pb);
   };
 
-  // forward role: S before chunks 0 .. nch-1 (the last chunk's update is not needed);
-  // adjoint role: Lambda after chunks nch-1 .. 0, each update applied
-  const int napply = adjoint ? nch : nch - 1;
-  auto chunk_of = [&](int it) { return adjoint ? nch - 1 - it : it; };
+  // S role: chunks c0 .. c1-1 (a walk stores S before each and skips the last
+  // update); Lambda role: chunks c1-1 .. c0, every update applied
+  const int napply = (adjoint || kSum) ? nch : nch - 1;
+  auto chunk_of = [&](int it) { return adjoint ? c1 - 1 - it : c0 + it; };
   auto step = [&]() {  // the chunk whose inputs are in LDS: scan, then update X
     __syncthreads();
     {
@@ -320,6 +410,7 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
     }
     __syncthreads();
     const float dec = s_dec[d_own];
+    if (kSum) Dprod *= dec;
 #pragma unroll
     for (int E = 0; E < EB; ++E) X[E] *= dec;
 #pragma unroll
@@ -339,18 +430,26 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
     put();
     fetch(chunk_of(napply > 1 ? 1 : 0));
   }
-  store_state(ws_out, cbase + chunk_of(0));
+  if (!kSum) store_state(ws_out, cbase + chunk_of(0));
   for (int it = 0; it < napply - 1; ++it) {
     step();
     put();
     fetch(chunk_of(it + 2 < napply ? it + 2 : napply - 1));
-    store_state(ws_out, cbase + chunk_of(it + 1));
+    if (!kSum) store_state(ws_out, cbase + chunk_of(it + 1));
   }
   if (napply > 0) {
     step();
-    if (napply < nch) store_state(ws_out, cbase + chunk_of(napply));
+    if (!kSum && napply < nch) store_state(ws_out, cbase + chunk_of(napply));
   }
-  if (adjoint && dinit != nullptr) {
+  if (kSum) {
+    const int s_ = u;
+    float* Lp = sumL_at(s_, adjoint);
+#pragma unroll
+    for (int E = 0; E < EB; ++E) *reinterpret_cast<f32x4*>(Lp + 16 * E) = X[E];
+    if (g4 == 0) *sumD_at(s_, adjoint) = Dprod;
+    return;
+  }
+  if (adjoint && j == 0 && dinit != nullptr) {
 #pragma unroll
     for (int E = 0; E < EB; ++E)
       *reinterpret_cast<f32x4*>(dinit + sh + int64_t(d_own) * DV + 16 * E + 4 * g4) = X[E];
@@ -763,6 +862,26 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
   }
 }
 
+// Workspace layout of one call (host side).
+struct BwdLayout {
+  int64_t max_chunks, max_sums, max_pieces;
+  size_t plan_bytes, state_bytes, sumL_bytes, sumD_bytes, bytes;
+};
+BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  BwdLayout l;
+  l.max_chunks = (N + kC - 1) / kC + max_segs;
+  // pieces of cut segments: m <= n / 16 per cut segment (n > 32, pieces >= 32 chunks)
+  l.max_sums = l.max_chunks / 16 + 1;
+  l.max_pieces = max_segs + l.max_sums;
+  l.plan_bytes = up((size_t(max_segs) + 1) * 4 * 3);
+  l.state_bytes = up(size_t(l.max_chunks) * H * Dk * Dv * 2);
+  l.sumL_bytes = up(size_t(l.max_sums) * 2 * H * Dk * Dv * 4);
+  l.sumD_bytes = up(size_t(l.max_sums) * 2 * H * Dk * 4);
+  l.bytes = l.plan_bytes + 2 * l.state_bytes + l.sumL_bytes + l.sumD_bytes;
+  return l;
+}
+
 template <int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g, const void* beta,
                        const void* dout, const int32_t* cu, int32_t max_segs, int64_t N, int32_t H,
@@ -773,34 +892,44 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   using CC = ChCfg<DK, DV>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_bwd_state_kernel<DK, DV>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_bwd_state_kernel<DK, DV, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SC::bytes);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_bwd_state_kernel<DK, DV, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, SC::bytes);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_bwd_chunk_kernel<DK, DV>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, CC::bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t max_chunks = (N + kC - 1) / kC + max_segs;
-  const size_t plan_bytes = ((size_t(max_segs) + 1) * 4 + 255) / 256 * 256;
-  const size_t state_bytes = size_t(max_chunks) * H * DK * DV * 2;
-  int32_t* base = static_cast<int32_t*>(ws);
-  bf16* Sws = reinterpret_cast<bf16*>(static_cast<char*>(ws) + plan_bytes);
-  bf16* Lws = reinterpret_cast<bf16*>(static_cast<char*>(ws) + plan_bytes + state_bytes);
+  const BwdLayout l = bwd_layout(N, H, DK, DV, max_segs);
+  char* w = static_cast<char*>(ws);
+  int32_t* base = reinterpret_cast<int32_t*>(w);
+  int32_t* pbase = base + (max_segs + 1);
+  int32_t* sbase = pbase + (max_segs + 1);
+  bf16* Sws = reinterpret_cast<bf16*>(w + l.plan_bytes);
+  bf16* Lws = reinterpret_cast<bf16*>(w + l.plan_bytes + l.state_bytes);
+  float* sumL = reinterpret_cast<float*>(w + l.plan_bytes + 2 * l.state_bytes);
+  float* sumD = reinterpret_cast<float*>(w + l.plan_bytes + 2 * l.state_bytes + l.sumL_bytes);
   const bf16* qb = static_cast<const bf16*>(q);
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
   const bf16* gb = static_cast<const bf16*>(g);
   const bf16* bb = static_cast<const bf16*>(beta);
   const bf16* ob = static_cast<const bf16*>(dout);
-  hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, max_segs, N,
-                     int32_t(max_chunks), base, flags);
-  hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV>), dim3(unsigned(2 * int64_t(max_segs) * H)),
-                     dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
-                     N, H, scale, s0, dF, Sws, Lws, dinit);
-  hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(max_chunks * H + kTailBlocks)),
+  hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, max_segs, N, H,
+                     int32_t(l.max_chunks), int32_t(l.max_pieces), int32_t(l.max_sums), base, pbase,
+                     sbase, flags);
+  hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, true>), dim3(unsigned(2 * l.max_sums * H)),
+                     dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
+                     max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, Lws, sumL, sumD, dinit);
+  hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(2 * l.max_pieces * H)),
+                     dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
+                     max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, Lws, sumL, sumD, dinit);
+  hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(l.max_chunks * H + kTailBlocks)),
                      dim3(CC::NT), CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
-                     int32_t(max_chunks), N, H, scale, Sws, Lws, static_cast<bf16*>(dq),
+                     int32_t(l.max_chunks), N, H, scale, Sws, Lws, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
                      static_cast<bf16*>(db));
   return hipGetLastError();
@@ -819,9 +948,7 @@ bool kda_chunk_bwd_supported(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32
 size_t kda_chunk_bwd_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
                                      int32_t max_segs) {
   if (!kda_chunk_bwd_supported(N, H, Dk, Dv, dtype, max_segs)) return 0;
-  const int64_t max_chunks = (N + kC - 1) / kC + max_segs;
-  const size_t plan_bytes = ((size_t(max_segs) + 1) * 4 + 255) / 256 * 256;
-  return plan_bytes + 2 * size_t(max_chunks) * H * Dk * Dv * 2;
+  return bwd_layout(N, H, Dk, Dv, max_segs).bytes;
 }
 
 hipError_t launch_kda_chunk_backward(const void* q, const void* k, const void* v, const void* g,

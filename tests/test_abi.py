@@ -207,15 +207,21 @@ def test_backward_entry_validation(lib, kw, code):
 
 
 def test_backward_workspace(lib):
-    """The chunked reverse pass (bf16, Dk and Dv in {64, 128}) keeps a chunk
-    table (max_segs + 1 int32, padded to 256 bytes) and two bf16 states of
-    Dk x Dv per (chunk, head), chunks = ceil(N / 64) + max_segs; other shapes
-    need none."""
+    """The chunked reverse pass (bf16, Dk and Dv in {64, 128}) keeps three tables
+    (chunk, piece and summary offsets: 3 (max_segs + 1) int32, padded to 256
+    bytes), two bf16 states of Dk x Dv per (chunk, head), chunks =
+    ceil(N / 64) + max_segs, and for the pieces of cut segments, at most
+    chunks / 16 + 1 of them, an fp32 Dk x Dv state and Dk decay products per
+    (piece, role, head); other shapes need none."""
     size = lib.pkv_chunk_kda_varlen_backward_workspace_size
+    up = lambda x: (x + 255) // 256 * 256
     for N, H, Dk, Dv, S in [(65536, 32, 128, 128, 256), (256, 2, 64, 64, 4), (1000, 3, 64, 128, 7),
                             (131072, 32, 128, 64, 8)]:
-        table = ((S + 1) * 4 + 255) // 256 * 256
-        assert size(N, H, Dk, Dv, S, 0) == table + 2 * ((N + 63) // 64 + S) * H * Dk * Dv * 2
+        chunks = (N + 63) // 64 + S
+        sums = chunks // 16 + 1
+        expect = (up(3 * 4 * (S + 1)) + 2 * up(chunks * H * Dk * Dv * 2) + up(sums * 2 * H * Dk * Dv * 4)
+                  + up(sums * 2 * H * Dk * 4))
+        assert size(N, H, Dk, Dv, S, 0) == expect, (N, H, S)
     assert size(256, 2, 32, 32, 4, 0) == 0 and size(256, 2, 64, 64, 4, 1) == 0
     need = size(256, 2, 64, 64, 4, 0)
     assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args()) == 3                       # missing

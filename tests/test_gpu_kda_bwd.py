@@ -208,3 +208,25 @@ def test_flat_microbatch_sampled():
             f64(wl.beta[sl, hs]), f64(do[sl, hs]), None, 1.0, None, f64(dF[i:i + 1, hs]))
         for name, got, exp in zip(["dq", "dk", "dv", "dg", "dbeta"], r[:5], ref[:5]):
             check_close(f64(got[0, sl, h]), exp[:, 0], "bf16", f"segment {i} head {h} {name}")
+
+
+@pytest.mark.parametrize("lens,Dk,Dv", [((3000,), 64, 64), ((70, 5000, 33), 64, 64), ((4100,), 128, 128)])
+def test_long_segments_cut_into_pieces(lens, Dk, Dv):
+    """One head and long documents: the plan cuts every segment over 32 chunks into
+    pieces (the per-CU share is tiny), so the state kernel composes the pieces'
+    summaries; with an initial state and a final-state cotangent on every slot."""
+    print(f"  bwd cut pieces lens={lens} Dk={Dk} Dv={Dv}", flush=True)
+    rng = np.random.default_rng(sum(lens) + Dk)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N, H = int(cu[-1]), 1
+    ts = _inputs(rng, N, H, Dk, Dv, torch.bfloat16, gl=0.0005, gh=0.02)
+    S = len(lens)
+    S0 = rng.standard_normal((S, H, Dk, Dv)) * 0.3
+    dF = rng.standard_normal((S, H, Dk, Dv)) * 0.3
+    r = _run(ts, cu, Dk ** -0.5, S0, dF)
+    ref = _oracle(ts, cu, Dk ** -0.5, S0, dF)
+    _compare(r, ref, "bf16", "cut pieces")
+    for i in range(S):
+        a, e = cu[i], cu[i + 1]
+        for name, got, exp in zip(["dq", "dk", "dv", "dg"], r[:4], ref[:4]):
+            check_close(f64(got)[0, a:e], exp[a:e], "bf16", f"segment {i} {name}")
