@@ -230,3 +230,54 @@ def test_long_segments_cut_into_pieces(lens, Dk, Dv):
         a, e = cu[i], cu[i + 1]
         for name, got, exp in zip(["dq", "dk", "dv", "dg"], r[:4], ref[:4]):
             check_close(f64(got)[0, a:e], exp[a:e], "bf16", f"segment {i} {name}")
+
+
+def _full_size_sampled(name, pick, dF_scale=0.1):
+    pkv = _pkv()
+    print(f"  bwd {name}: building inputs", flush=True)
+    wl = workloads.make_workload(name, conv=False)
+    cu, _, _ = oracle.segment_ids_to_cu_seqlens(wl.segment_ids, wl.cfg.max_segs)
+    N, H, Dk, Dv = wl.N, wl.cfg.H, wl.cfg.Dk, wl.cfg.Dv
+    gen = torch.Generator().manual_seed(11)
+    do = torch.randn((N, H, Dv), generator=gen).to(torch.bfloat16)
+    S = len(cu) - 1
+    dF = torch.randn((S, H, Dk, Dv), generator=gen) * dF_scale
+    dev = device()
+    args = [t.reshape(1, N, H, -1).to(dev) for t in (wl.q, wl.k, wl.v, wl.g)]
+    beta = wl.beta.reshape(1, N, H).to(dev)
+    cud = torch.from_numpy(cu.astype(np.int32)).to(dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    print(f"  bwd {name}: launch", flush=True)
+    r = pkv.chunk_kda_varlen_backward(*args, beta, do.reshape(1, N, H, Dv).to(dev), cud,
+                                      dfinal_state=dF.to(dev), output_d_initial_state=True, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    lens = np.diff(cu)
+    for n, i in enumerate(pick(lens)):
+        a, e = int(cu[i]), int(cu[i + 1])
+        h = (7 * n + 5) % H
+        print(f"  oracle bwd {name} segment {i} [{a},{e}) head {h}", flush=True)
+        sl, hs = slice(a, e), slice(h, h + 1)
+        ref = oracle.chunk_kda_varlen_backward(
+            f64(wl.q[sl, hs]), f64(wl.k[sl, hs]), f64(wl.v[sl, hs]), f64(wl.g[sl, hs]),
+            f64(wl.beta[sl, hs]), f64(do[sl, hs]), None, 1.0, None, f64(dF[i:i + 1, hs]))
+        for nm, got, exp in zip(["dq", "dk", "dv", "dg", "dbeta"], r[:5], ref[:5]):
+            check_close(f64(got[0, sl, h]), exp[:, 0], "bf16", f"{name} segment {i} head {h} {nm}")
+        check_close(f64(r.d_initial_state[i, h]), ref[5][0, 0], "bf16", f"{name} segment {i} head {h} dS0")
+
+
+def test_many_short_docs_sampled():
+    """D = 64, hundreds of short documents, phantom slots and trailing padding."""
+    def pick(lens):
+        real = [i for i in range(len(lens)) if lens[i] > 0]
+        return sorted({min(real, key=lambda i: lens[i]), real[len(real) // 2], max(real, key=lambda i: lens[i])})
+    _full_size_sampled("many_short_docs", pick)
+
+
+def test_long_context_sampled():
+    """H = 32, six documents over 131072 tokens: the long ones are cut into pieces at
+    full size (the per-CU share is 257 chunks); the shortest and the longest."""
+    def pick(lens):
+        real = [i for i in range(len(lens)) if lens[i] > 0]
+        return sorted({min(real, key=lambda i: lens[i]), max(real, key=lambda i: lens[i])})
+    _full_size_sampled("long_context", pick, dF_scale=0.05)
