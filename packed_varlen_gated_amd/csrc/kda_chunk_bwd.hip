@@ -8,34 +8,38 @@
 // from the same chunked form the forward pass uses. Chunks are 64 tokens
 // aligned to segment starts, split into four 16-token sub-chunks.
 //
-// Three launches:
-//   plan   one work-group: chunk count per segment slot and its prefix sums
-//          (global chunk index of each segment's first chunk).
-//   state  one work-group per (slot, head) and role, the two roles in one grid:
-//          forward, S before every chunk (bf16 in the workspace);
-//          adjoint, Lambda after every chunk, walking the chunks backwards
-//          (Lambda after the last one = dL/dfinal_state), then
-//          d initial state = Lambda before the first chunk.
-//            S   <- 2^{B} S + sum_t kbar_t v_t^T,     kbar_t = beta_t k_t 2^{B - b_t}
-//            Lam <- 2^{B} Lam + sum_t q'_t do_t^T,    q'_t = scale q_t 2^{b_t}
-//          (b_t the log2 cumulative gate from the chunk start, B its last
-//          value; rows scaled per key channel.)
-//   chunk  one work-group per (chunk, head), independent of the others: from
-//          S_c and Lambda_c it walks the sub-chunks backwards. For sub-chunk i
-//          with within-sub-chunk cumulative c_t (log2) and total T_i, S_i the
-//          state before it (formed directly from S_c) and Lambda_i the adjoint
-//          after it (carried):
-//            Qh_t = scale q_t 2^{c_t}, Kt_s = beta_s k_s 2^{-c_s},
-//            A = (Qh Kt^T) masked t >= s, dA = (dO V^T) masked t >= s,
-//            dq_t  = scale 2^{c_t} (S_i do_t + sum_s dA_ts Kt_s)
-//            u_s   = 2^{-c_s} (2^{T_i} Lambda_i v_s + sum_t dA_ts Qh_t)
-//            dk_s  = beta_s u_s,  dbeta_s = k_s . u_s
-//            dv_s  = (Kt_s 2^{T_i})^T Lambda_i + sum_t A_ts do_t
-//            Lambda_{i-1} = 2^{T_i} Lambda_i + sum_t Qh_t do_t^T.
-//          dg_t is the sum over u >= t in the chunk of (q_u dq_u - k_u dk_u)
-//          plus G_c = sum_e Lambda_c * S_end (S_end the state after the
-//          chunk): the gate gradient at the chunk's first following token,
-//          which stands for all later tokens and the final-state cotangent.
+// Four launches:
+//   plan     one work-group: per segment slot its chunk count and their prefix
+//            sums (global chunk index of each segment's first chunk), and the
+//            cut of long segments into pieces (as in the forward pass).
+//   summary  per piece of a cut segment, head and role: the piece walked from a
+//            zero state; its end state and the product of its decays (fp32).
+//   walk     one work-group per (piece, head) and role, the two roles in one grid:
+//            forward, S before every chunk (bf16 in the workspace), starting
+//            from the initial state composed with the earlier pieces' summaries;
+//            adjoint, Lambda after every chunk, walking the chunks backwards from
+//            dL/dfinal_state composed with the later pieces' summaries, then
+//            d initial state = Lambda before the first chunk.
+//              S   <- 2^{B} S + sum_t kbar_t v_t^T,     kbar_t = beta_t k_t 2^{B - b_t}
+//              Lam <- 2^{B} Lam + sum_t q'_t do_t^T,    q'_t = scale q_t 2^{b_t}
+//            (b_t the log2 cumulative gate from the chunk start, B its last
+//            value; rows scaled per key channel.)
+//   chunk    one work-group per (chunk, head), independent of the others: from
+//            S_c and Lambda_c it walks the sub-chunks backwards. For sub-chunk i
+//            with within-sub-chunk cumulative c_t (log2) and total T_i, S_i the
+//            state before it (formed directly from S_c) and Lambda_i the adjoint
+//            after it (carried):
+//              Qh_t = scale q_t 2^{c_t}, Kt_s = beta_s k_s 2^{-c_s},
+//              A = (Qh Kt^T) masked t >= s, dA = (dO V^T) masked t >= s,
+//              dq_t  = scale 2^{c_t} (S_i do_t + sum_s dA_ts Kt_s)
+//              u_s   = 2^{-c_s} (2^{T_i} Lambda_i v_s + sum_t dA_ts Qh_t)
+//              dk_s  = beta_s u_s,  dbeta_s = k_s . u_s
+//              dv_s  = (Kt_s 2^{T_i})^T Lambda_i + sum_t A_ts do_t
+//              Lambda_{i-1} = 2^{T_i} Lambda_i + sum_t Qh_t do_t^T.
+//            dg_t is the sum over u >= t in the chunk of (q_u dq_u - k_u dk_u)
+//            plus G_c = sum_e Lambda_c * S_end (S_end the state after the
+//            chunk): the gate gradient at the chunk's first following token,
+//            which stands for all later tokens and the final-state cotangent.
 //
 // MFMA operand conventions (v_mfma_f32_16x16x16_bf16 and _16x16x32_bf16):
 // operand lane l has row (A) or column (B) l%16 and contraction slots of lane
@@ -61,10 +65,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;
-constexpr int kThreads = 256;
 constexpr int kPlanThreads = 1024;
 constexpr int kTailBlocks = 64;
 constexpr float kLog2e = 1.4426950408889634f;
