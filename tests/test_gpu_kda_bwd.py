@@ -281,3 +281,31 @@ def test_long_context_sampled():
         real = [i for i in range(len(lens)) if lens[i] > 0]
         return sorted({min(real, key=lambda i: lens[i]), max(real, key=lambda i: lens[i])})
     _full_size_sampled("long_context", pick, dF_scale=0.05)
+
+
+def test_bad_cu_seqlens_sets_flag_chunked():
+    """The chunked path (bf16, D = 64): a decreasing cu_seqlens entry sets the flag; the
+    plan keeps every index inside the workspace (overlapping slots only race)."""
+    print("  bwd bad cu_seqlens (chunked)", flush=True)
+    rng = np.random.default_rng(4)
+    N, H, D = 64, 2, 64
+    ts = _inputs(rng, N, H, D, D, torch.bfloat16)
+    flags = torch.zeros(1, dtype=torch.int32, device=device())
+    _run(ts, np.array([0, 40, 30, 64]), 1.0, None, None, flags=flags, want_dinit=True)
+    assert int(flags.item()) & _pkv().FLAG_BAD_CU_SEQLENS
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (128, 128)])
+def test_backward_deterministic(Dk, Dv):
+    """No atomics on the data path: two calls give the same bits."""
+    print(f"  bwd determinism Dk={Dk} Dv={Dv}", flush=True)
+    rng = np.random.default_rng(9)
+    cu = np.array(CU_RAGGED, dtype=np.int64)
+    N, H = 345, 3
+    ts = _inputs(rng, N, H, Dk, Dv, torch.bfloat16)
+    S = len(cu) - 1
+    dF = rng.standard_normal((S, H, Dk, Dv))
+    r1 = _run(ts, cu, 0.5, None, dF)
+    r2 = _run(ts, cu, 0.5, None, dF)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a.cpu(), b.cpu())
