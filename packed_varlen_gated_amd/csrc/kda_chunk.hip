@@ -34,11 +34,13 @@
 //                  c+1 and their sub-chunk totals (to LDS); one A block.
 //               C: the stores of chunk c-1's outputs; two A blocks of chunk c
 //                  (MFMA), masked, beta-scaled, to LDS; o^T = S^T Q^^T.
-// Producer wave w owns 16-token sub-chunk w and all Dk channels; a lane holds
-// 4 consecutive tokens x Dk/16 channels, so each load covers four tokens x
-// whole 128-byte lines and the in-sub-chunk cumsum is an in-lane prefix plus
-// a DPP quad scan. The sub-chunk totals go through a small LDS table, and the
-// sub-chunk index is uniform per wave (no divergent stores).
+// Producer wave w owns 16-token sub-chunk w and all Dk channels; lane
+// 16 tq + cg holds the 4 consecutive tokens 4 tq .. 4 tq + 3 x Dk/16 channels
+// of group cg, so each 16-lane row of a load or an LDS store covers one whole
+// token row (conflict-free LDS writes) and the in-sub-chunk cumsum is an
+// in-lane prefix plus a scan across the four rows (v_permlane16_swap and
+// v_permlane32_swap). The sub-chunk totals go through a small LDS table, and
+// the sub-chunk index is uniform per wave (no divergent stores).
 // Raw inputs of chunk c+1 are loaded at the start of step c. Each
 // single-buffered LDS tile is written in one half and read in the other; Q^,
 // Kbar^T and 2^{b_C}, read a step later, are double-buffered.
@@ -102,8 +104,11 @@ struct Cfg {
   static constexpr int off_item = 0;                         // int: next queue item
   static constexpr int off_decay = 16;                       // float [2][DK]
   static constexpr int off_beta = off_decay + 2 * DK * 4;    // float [2][kC]
-  static constexpr int off_T = off_beta + 2 * kC * 4;        // float [DK][4] 2^{sub-chunk totals}
-  static constexpr int off_a = off_T + DK * 4 * 4;           // A, bf16 [kC][TP]
+  // 2^{sub-chunk totals}: float [4] per channel, one empty slot after every
+  // group of DK/16 channels, so the 16 channel groups of a read fall on
+  // distinct banks
+  static constexpr int off_T = off_beta + 2 * kC * 4;
+  static constexpr int off_a = off_T + (DK + 16) * 4 * 4;    // A, bf16 [kC][TP]
   static constexpr int off_v = off_a + kC * TP * 2;          // V, bf16 [kC][VP]
   static constexpr int off_kb = off_v + kC * VP * 2;         // Kbar, bf16 [2][kC][RP]
   static constexpr int off_qh = off_kb + 2 * kC * RP * 2;    // Q^, bf16 [kC][KP]
@@ -132,15 +137,6 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// DPP move; lanes whose source lies outside the row read 0.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-constexpr int kQuadPrev1 = 0x90;  // quad_perm [0,0,1,2]
-constexpr int kQuadPrev2 = 0x40;  // quad_perm [0,0,0,1]
-constexpr int kQuadLast = 0xFF;   // quad_perm [3,3,3,3]
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufFlags);
@@ -346,12 +342,12 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   };
 
   // ---------------------------------------------------------------- roles
-  // Producer wave w: sub-chunk sw = w, all channels. Lane: 4 tokens
-  // [tok0, tok0 + 4) (quad position tq), PCPL k channels from ch0 and PVPL v
-  // channels from vch0, so each load covers four tokens x whole rows.
+  // Producer wave w: sub-chunk sw = w, all channels. Lane 16 tq + cg: 4
+  // tokens [tok0, tok0 + 4), PCPL k channels from ch0 and PVPL v channels from
+  // vch0, so each 16-lane row of a load or a store covers one token's row.
   const int sw = w & 3;
-  const int tq = lane & 3;
-  const int cg = lane >> 2;
+  const int tq = lane >> 4;
+  const int cg = lane & 15;
   const int ch0 = PCPL * cg;
   const int vch0 = PVPL * cg;
   const int tok0 = 16 * sw + 4 * tq;
@@ -431,20 +427,24 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         run = fmaf(bf(R.g[i], c), kLog2e, run);
         cs[i][c] = run;
       }
-      // prefix over the quad (the four token groups of the sub-chunk)
-      const float a1 = dpp<kQuadPrev1>(run);
-      const float s1 = run + (tq >= 1 ? a1 : 0.f);
-      const float a2 = dpp<kQuadPrev2>(s1);
-      const float inc = s1 + (tq >= 2 ? a2 : 0.f);
+      // prefix over the four token groups of the sub-chunk (the four rows of
+      // 16 lanes): row pairs through v_permlane16_swap, then the pair totals
+      // through v_permlane32_swap
+      const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(run), __float_as_uint(run), false, false);
+      const float pair = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // rows 2m and 2m + 1
+      const float s1 = (tq & 1) ? pair : run;
+      const auto pt = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+      const float lo = __uint_as_float(pt[0]), hi = __uint_as_float(pt[1]);  // rows 0-1, rows 2-3
+      const float inc = s1 + (tq >= 2 ? lo : 0.f);
       const float excl = inc - run;
 #pragma unroll
       for (int i = 0; i < 4; ++i) cs[i][c] += excl;
-      tot[c] = inc;  // quad lane 3 holds the sub-chunk total
-      cs[4][c] = dpp<kQuadLast>(inc);
+      tot[c] = lo + hi;  // the sub-chunk total, in every lane
+      cs[4][c] = tot[c];
     }
     if (tq == 3) {
 #pragma unroll
-      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c) * 4 + sw] = ex2(tot[c]);
+      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c + cg) * 4 + sw] = ex2(tot[c]);
     }
   };
 
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     const float (&Tw)[PCPL] = cs[4];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
-      const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c) * 4);
+      const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c + cg) * 4);
       f[0][c] = sw == 0 ? 1.f : sw == 1 ? E[0] : sw == 2 ? E[0] * E[1] : (E[0] * E[1]) * E[2];
       f[1][c] = sw == 3 ? 1.f : sw == 2 ? E[3] : sw == 1 ? E[2] * E[3] : E[1] * (E[2] * E[3]);
       f[2][c] = __builtin_amdgcn_rcpf(E[sw]);
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     const float (&Tw)[PCPL] = cs[4];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
-      const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c) * 4);
+      const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c + cg) * 4);
       f1[c] = sw == 3 ? 1.f : sw == 2 ? E[3] : sw == 1 ? E[2] * E[3] : E[1] * (E[2] * E[3]);
       dec[c] = (E[0] * E[1]) * (E[2] * E[3]);
     }
