@@ -31,7 +31,9 @@
 //               C: chunk c-1: o^T += V^T A^T for its Dv/4 columns, packed;
 //                  S = diag(2^{b_C}) S + Kbar^T V.
 //   second half P: V of chunk c; the in-sub-chunk cumulative gates of chunk
-//                  c+1 and their sub-chunk totals (to LDS); one A block.
+//                  c+1, their sub-chunk totals (to LDS) and the per-element
+//                  factors q 2^{c} and k 2^{T - c} of chunk c+1 (in the
+//                  registers of its q and k); one A block.
 //               C: the stores of chunk c-1's outputs; two A blocks of chunk c
 //                  (MFMA), masked, beta-scaled, to LDS; o^T = S^T Q^^T.
 // Producer wave w owns 16-token sub-chunk w and all Dk channels; lane
@@ -97,8 +99,11 @@ struct Cfg {
   static constexpr int DT = DK / 16;        // 16-row state tiles
   static constexpr int KS = DK / 32;        // contraction steps over Dk
   static constexpr int KP = DK + 8;         // Q^, KE, query versions: token-major rows (bf16)
-  static constexpr int RP = DK + 16;        // Kbar: token-major rows, read transposed
-  static constexpr int VP = DV + 16;        // V: token-major rows, read transposed
+  // Dk = Dv = 64: two work-groups per CU (LDS at most 80 KiB and at most 128
+  // VGPRs each, four waves per SIMD); every other shape: one.
+  static constexpr int WG_PER_CU = (DK == 64 && DV == 64) ? 2 : 1;
+  static constexpr int RP = DK + (WG_PER_CU == 2 ? 8 : 16);  // Kbar: token-major rows, read transposed
+  static constexpr int VP = DV + (WG_PER_CU == 2 ? 8 : 16);  // V: token-major rows, read transposed
   static constexpr int TP = kC + 8;         // A rows (bf16)
   // Small tables first: ds_read/ds_write immediates reach 64 KiB.
   static constexpr int off_item = 0;                         // int: next queue item
@@ -119,7 +124,7 @@ struct Cfg {
   static constexpr bool stage_o = DV == 128;
   static constexpr int off_o = off_qv + 10 * 16 * KP * 2;
   static constexpr int bytes = off_o + (stage_o ? kC * DV * 2 : 0);
-  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(bytes <= 160 * 1024 / WG_PER_CU, "LDS budget");
 };
 
 template <int V>
@@ -187,6 +192,17 @@ __device__ __forceinline__ void stn(bf16* dst, const float* x) {
   }
 }
 
+// n bf16 that are already packed in pairs (n in {4, 8}) -> one store.
+template <int n>
+__device__ __forceinline__ void stw(bf16* dst, const uint32_t (&w)[n / 2]) {
+  if constexpr (n == 4) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+  } else {
+    static_assert(n == 8, "store width");
+    *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane k supplies the address of 4 consecutive bf16; lane j = 4a + b receives
 // element b of the chunks supplied by lanes a, 4 + a, 8 + a, 12 + a, in that
@@ -249,7 +265,7 @@ __device__ __forceinline__ void wload(uint32_t (&w)[n], __amdgpu_buffer_rsrc_t r
 // last: S from zero over the run and the product of its decays, both to the
 // workspace (no outputs).
 template <int DK, int DV, bool kState>
-__global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
+__global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
     int32_t* __restrict__ plan, int32_t runs_max, int32_t max_segs, int64_t N,
@@ -414,11 +430,15 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     for (int i = 0; i < 4; ++i) wload(R.v[i], rv, uint32_t(tok0 + i) * rowV + vch0 * 2);
   };
   // ---- producer, second half: in-sub-chunk cumulative gates (base 2) of a
-  // chunk. cs[i][c] is the inclusive cumsum at token tok0 + i, channel ch0 + c,
-  // from the start of the sub-chunk, cs[4][c] the sub-chunk total T; s_T gets
-  // 2^T of every sub-chunk (the next half's factors are products of those).
-  auto scan = [&](const Raw<PCPL, PVPL>& R, float (&cs)[5][PCPL]) {
-    float tot[PCPL];
+  // chunk, folded into its q and k at once. With c the inclusive cumsum at a
+  // token from the start of its sub-chunk and T the sub-chunk total, the
+  // registers of q and k are overwritten in place by Q~ = q 2^{c} and
+  // KE = k 2^{T - c} (bf16, packed like the raw values), so only they, not
+  // the cumsums, stay live until the first half; s_T gets 2^T of every
+  // sub-chunk (the next half's factors are products of those). The state
+  // pass has no q and folds k only.
+  auto scan = [&](const Raw<PCPL, PVPL>& R, RawQK<PCPL>& X) {
+    float cs[4][PCPL], tot[PCPL], Tw[PCPL];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
       float run = 0.f;
@@ -440,29 +460,39 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) cs[i][c] += excl;
       tot[c] = lo + hi;  // the sub-chunk total, in every lane
-      cs[4][c] = tot[c];
+      Tw[c] = tot[c];
     }
     if (tq == 3) {
 #pragma unroll
       for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c + cg) * 4 + sw] = ex2(tot[c]);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int c = 0; c < PCPL; c += 2) {
+        if constexpr (!kState)
+          X.q[i][c >> 1] = pk2(bf(X.q[i], c) * ex2(cs[i][c]), bf(X.q[i], c + 1) * ex2(cs[i][c + 1]));
+        X.k[i][c >> 1] = pk2(bf(X.k[i], c) * ex2(Tw[c] - cs[i][c]),
+                             bf(X.k[i], c + 1) * ex2(Tw[c + 1] - cs[i][c + 1]));
+      }
+    }
   };
 
-  // ---- producer, first half: factors and MFMA operands of one chunk.
-  // With T_j the sub-chunk totals of a channel and E_j = 2^{T_j} (from s_T):
-  // f0 = 2^{T_0 + .. + T_{w-1}} (Q^ = Q~ f0), f1 = 2^{T_{w+1} + .. + T_3}
-  // (Kbar = beta KE f1), f2 = 2^{-T_w} (diagonal version), f3 = 2^{T_{w-1}}
-  // (block (w, w-2)), f4 = 2^{T_{w-1} + T_{w-2}} (block (3, 0)), decay =
-  // 2^{T_0 + .. + T_3}: products of the E_j and one reciprocal, instead of an
-  // exponential each. The sub-chunk index is a compile-time constant inside
-  // (one instance per sub-chunk), so every choice below is resolved without
-  // branches.
-  auto produce_a_sw = [&](auto swc, const RawQK<PCPL>& R, const float (&cs)[5][PCPL],
-                          bf16* s_qh, bf16* s_kb, float* s_dec, const float* s_bet) {
+  // ---- producer, first half: factors and MFMA operands of one chunk from
+  // its Q~ and KE. With T_j the sub-chunk totals of a channel and
+  // E_j = 2^{T_j} (from s_T): f0 = 2^{T_0 + .. + T_{w-1}} (Q^ = Q~ f0),
+  // f1 = 2^{T_{w+1} + .. + T_3} (Kbar = beta KE f1), f2 = 2^{-T_w} (diagonal
+  // version), f3 = 2^{T_{w-1}} (block (w, w-2)), f4 = 2^{T_{w-1} + T_{w-2}}
+  // (block (3, 0)), decay = 2^{T_0 + .. + T_3}: products of the E_j and one
+  // reciprocal. KE, the version of block (w, w-1) (Q~ itself) and, for w = 0,
+  // Q^ are stored as they are. The sub-chunk index is a compile-time constant
+  // inside (one instance per sub-chunk), so every choice below is resolved
+  // without branches.
+  auto produce_a_sw = [&](auto swc, const RawQK<PCPL>& R, bf16* s_qh, bf16* s_kb, float* s_dec,
+                          const float* s_bet) {
     constexpr int sw = decltype(swc)::value;
     constexpr int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
     float f[5][PCPL], dec[PCPL];
-    const float (&Tw)[PCPL] = cs[4];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
       const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c + cg) * 4);
@@ -483,22 +513,24 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     for (int i = 0; i < 4; ++i) {
       const int tok = tok0 + i;
       const float bt = bt4[i];
-      float qt[PCPL], ke[PCPL], t0[PCPL], kb[PCPL];
+      float qt[PCPL], t0[PCPL], kb[PCPL];
 #pragma unroll
       for (int c = 0; c < PCPL; ++c) {
-        qt[c] = bf(R.q[i], c) * ex2(cs[i][c]);
-        ke[c] = bf(R.k[i], c) * ex2(Tw[c] - cs[i][c]);
+        qt[c] = bf(R.q[i], c);
         t0[c] = qt[c] * f[0][c];
-        kb[c] = ke[c] * (bt * f[1][c]);
+        kb[c] = bf(R.k[i], c) * (bt * f[1][c]);
       }
-      stn<PCPL>(s_qh + tok * KP + ch0, t0);
-      stn<PCPL>(s_ke + tok * KP + ch0, ke);
+      if constexpr (sw == 0)
+        stw<PCPL>(s_qh + tok * KP + ch0, R.q[i]);
+      else
+        stn<PCPL>(s_qh + tok * KP + ch0, t0);
+      stw<PCPL>(s_ke + tok * KP + ch0, R.k[i]);
       stn<PCPL>(s_kb + tok * RP + ch0, kb);
       bf16* qv = s_qv + (tok & 15) * KP + ch0;  // row of the token in each version slot
 #pragma unroll
       for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[2][c];
       stn<PCPL>(qv + (vbase + sw) * 16 * KP, t0);
-      if constexpr (sw >= 1) stn<PCPL>(qv + (vbase + sw - 1) * 16 * KP, qt);
+      if constexpr (sw >= 1) stw<PCPL>(qv + (vbase + sw - 1) * 16 * KP, R.q[i]);
       if constexpr (sw >= 2) {
 #pragma unroll
         for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[3][c];
@@ -513,11 +545,10 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
   };
 
   // State pass: only Kbar and the decay.
-  auto produce_kb_sw = [&](auto swc, const RawQK<PCPL>& R, const float (&cs)[5][PCPL],
-                           bf16* s_kb, float* s_dec, const float* s_bet) {
+  auto produce_kb_sw = [&](auto swc, const RawQK<PCPL>& R, bf16* s_kb, float* s_dec,
+                           const float* s_bet) {
     constexpr int sw = decltype(swc)::value;
     float f1[PCPL], dec[PCPL];
-    const float (&Tw)[PCPL] = cs[4];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
       const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c + cg) * 4);
@@ -534,28 +565,27 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
     for (int i = 0; i < 4; ++i) {
       float kb[PCPL];
 #pragma unroll
-      for (int c = 0; c < PCPL; ++c)
-        kb[c] = bf(R.k[i], c) * ex2(Tw[c] - cs[i][c]) * (bt4[i] * f1[c]);
+      for (int c = 0; c < PCPL; ++c) kb[c] = bf(R.k[i], c) * (bt4[i] * f1[c]);
       stn<PCPL>(s_kb + (tok0 + i) * RP + ch0, kb);
     }
   };
 
-  auto produce_a = [&](const RawQK<PCPL>& R, const float (&cs)[5][PCPL], bf16* s_qh,
-                       bf16* s_kb, float* s_dec, const float* s_bet) {
+  auto produce_a = [&](const RawQK<PCPL>& R, bf16* s_qh, bf16* s_kb, float* s_dec,
+                       const float* s_bet) {
     if constexpr (kState) {
       switch (sw) {
-        case 0: produce_kb_sw(IntC<0>{}, R, cs, s_kb, s_dec, s_bet); break;
-        case 1: produce_kb_sw(IntC<1>{}, R, cs, s_kb, s_dec, s_bet); break;
-        case 2: produce_kb_sw(IntC<2>{}, R, cs, s_kb, s_dec, s_bet); break;
-        default: produce_kb_sw(IntC<3>{}, R, cs, s_kb, s_dec, s_bet); break;
+        case 0: produce_kb_sw(IntC<0>{}, R, s_kb, s_dec, s_bet); break;
+        case 1: produce_kb_sw(IntC<1>{}, R, s_kb, s_dec, s_bet); break;
+        case 2: produce_kb_sw(IntC<2>{}, R, s_kb, s_dec, s_bet); break;
+        default: produce_kb_sw(IntC<3>{}, R, s_kb, s_dec, s_bet); break;
       }
       return;
     }
     switch (sw) {
-      case 0: produce_a_sw(IntC<0>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
-      case 1: produce_a_sw(IntC<1>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
-      case 2: produce_a_sw(IntC<2>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
-      default: produce_a_sw(IntC<3>{}, R, cs, s_qh, s_kb, s_dec, s_bet); break;
+      case 0: produce_a_sw(IntC<0>{}, R, s_qh, s_kb, s_dec, s_bet); break;
+      case 1: produce_a_sw(IntC<1>{}, R, s_qh, s_kb, s_dec, s_bet); break;
+      case 2: produce_a_sw(IntC<2>{}, R, s_qh, s_kb, s_dec, s_bet); break;
+      default: produce_a_sw(IntC<3>{}, R, s_qh, s_kb, s_dec, s_bet); break;
     }
   };
 
@@ -765,7 +795,6 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
       begin_item(item);
       Raw<PCPL, PVPL> R;
       RawQK<PCPL> QA, QB;  // q, k of even / odd chunks
-      float cs[5][PCPL];
       const bool beta_wave = w == 0;
       uint32_t bnext = 0, bnext2 = 0;  // raw beta of the next chunks (wave 0)
       load_g(R, 0);
@@ -776,13 +805,13 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         bnext = load_beta(1);
         s_beta[lane] = __uint_as_float(b0 << 16);
       }
-      scan(R, cs);
+      scan(R, QA);
       load_g(R, 1);
       __syncthreads();
       for (int s = 0; s <= nchunks; s += 2) {
         // even chunk s: LDS buffers 0; odd chunk s + 1: buffers 1
         load_qk(QB, s + 1);
-        if (s < nchunks) produce_a(QA, cs, s_qh, s_kb0, s_decay, s_beta);
+        if (s < nchunks) produce_a(QA, s_qh, s_kb0, s_decay, s_beta);
         if (beta_wave) bnext2 = load_beta(s + 2);
         __syncthreads();
         if (!kState && C::stage_o && s >= 1) store_rows(s - 1);
@@ -790,12 +819,12 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         if (s < nchunks) produce_b(R.v);
         load_v(R, s + 1);
         if (beta_wave) s_beta[kC + lane] = __uint_as_float(bnext << 16);
-        if (s + 1 < nchunks) scan(R, cs);
+        if (s + 1 < nchunks) scan(R, QB);
         load_g(R, s + 2);
         __syncthreads();
         if (s + 1 > nchunks) break;
         load_qk(QA, s + 2);
-        if (s + 1 < nchunks) produce_a(QB, cs, s_qh, s_kb1, s_decay + DK, s_beta + kC);
+        if (s + 1 < nchunks) produce_a(QB, s_qh, s_kb1, s_decay + DK, s_beta + kC);
         if (beta_wave) bnext = load_beta(s + 3);
         __syncthreads();
         if (!kState && C::stage_o) store_rows(s);
@@ -803,7 +832,7 @@ __global__ __launch_bounds__(512, 1) void kda_chunk_kernel(
         if (s + 1 < nchunks) produce_b(R.v);
         load_v(R, s + 2);
         if (beta_wave) s_beta[lane] = __uint_as_float(bnext2 << 16);
-        if (s + 2 < nchunks) scan(R, cs);
+        if (s + 2 < nchunks) scan(R, QA);
         load_g(R, s + 3);
         __syncthreads();
       }
@@ -1207,8 +1236,8 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   const auto qp = static_cast<const bf16*>(q), kp = static_cast<const bf16*>(k);
   const auto vp = static_cast<const bf16*>(v), gp = static_cast<const bf16*>(g);
   const auto bp = static_cast<const bf16*>(beta);
-  // one work-group per CU: the LDS of either pass leaves room for one only
-  const unsigned grid = unsigned(device_cus());
+  // persistent grids: as many work-groups as the LDS lets each CU hold
+  const unsigned grid = unsigned(device_cus() * C::WG_PER_CU);
   if (L.states_max > 0) {
     hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true>), dim3(grid), dim3(C::NT), state_bytes, s,
                        qp, kp, vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale,
