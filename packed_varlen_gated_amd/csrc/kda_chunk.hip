@@ -33,9 +33,10 @@
 //   second half P: V of chunk c; the in-sub-chunk cumulative gates of chunk
 //                  c+1, their sub-chunk totals (to LDS) and the per-element
 //                  factors q 2^{c} and k 2^{T - c} of chunk c+1 (in the
-//                  registers of its q and k); one A block.
-//               C: the stores of chunk c-1's outputs; two A blocks of chunk c
-//                  (MFMA), masked, beta-scaled, to LDS; o^T = S^T Q^^T.
+//                  registers of its q and k).
+//               C: the stores of chunk c-1's outputs; three of the twelve A
+//                  block jobs of chunk c (MFMA), masked, beta-scaled, to LDS;
+//                  o^T = S^T Q^^T.
 // Producer wave w owns 16-token sub-chunk w and all Dk channels; lane
 // 16 tq + cg holds the 4 consecutive tokens 4 tq .. 4 tq + 3 x Dk/16 channels
 // of group cg, so each 16-lane row of a load or an LDS store covers one whole
@@ -750,17 +751,16 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     }
   };
 
-  // ---- second half: the A blocks of the chunk just prepared. Jobs 0..9
-  // are the blocks (w, j <= w), jobs 10 and 11 zero the blocks (0, 1) and
-  // (2, 3) that the A.V product reads through its 32-wide steps. Consumer ci
-  // takes jobs ci and ci + 4, producer w job 8 + w: the consumers' half is the
-  // longer one. Zero jobs run on a valid slot and their result is replaced,
-  // so no job branches.
+  // ---- consumer, second half: the A blocks of the chunk just prepared.
+  // Jobs 0..9 are the blocks (w, j <= w), jobs 10 and 11 zero the blocks
+  // (0, 1) and (2, 3) that the A.V product reads through its 32-wide steps.
+  // Consumer ci takes jobs ci, ci + 4 and ci + 8 (the producers, whose work
+  // per chunk sets the pace, take none). Zero jobs run on a valid slot and
+  // their result is replaced, so no job branches.
   auto a_blocks = [&](const float* s_bet) {
-    const int j0 = producer ? 8 + w : ci;
-    const int nj = producer ? 1 : 2;
-    for (int jj = 0; jj < nj; ++jj) {
-      const int job = j0 + 4 * jj;
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+      const int job = ci + 4 * jj;
       int bw, bj;
       block_of(job, bw, bj);
       const bool real = job < 10;
@@ -815,7 +815,6 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
         if (beta_wave) bnext2 = load_beta(s + 2);
         __syncthreads();
         if (!kState && C::stage_o && s >= 1) store_rows(s - 1);
-        if (!kState && s < nchunks) a_blocks(s_beta);
         if (s < nchunks) produce_b(R.v);
         load_v(R, s + 1);
         if (beta_wave) s_beta[kC + lane] = __uint_as_float(bnext << 16);
@@ -828,7 +827,6 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
         if (beta_wave) bnext = load_beta(s + 3);
         __syncthreads();
         if (!kState && C::stage_o) store_rows(s);
-        if (!kState && s + 1 < nchunks) a_blocks(s_beta + kC);
         if (s + 1 < nchunks) produce_b(R.v);
         load_v(R, s + 2);
         if (beta_wave) s_beta[lane] = __uint_as_float(bnext2 << 16);
