@@ -546,6 +546,14 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
   const auto r_dg = rsrc(dg + a * H * DK, uint32_t(L) * H * DK * 2);
   const auto r_dv = rsrc(dv + a * H * DV, uint32_t(L) * H * DV * 2);
 
+  const int lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
+  const int64_t soff = (int64_t(gc) * H + h) * DK * DV;
+  const bool ev_active = EB >= NW || w < EB;  // wave-uniform
+  auto eblk = [&](int ee) { return EB >= NW ? w * EBW + ee : w; };
+  // the chunk's Lambda (two orientations) and S_c from the workspace, raw bf16:
+  // issued with the input loads, so their latency overlaps the scan below
+  s16x4 L1r[EB][DBW], L2r[DB][EBW], Sc[EB][DBW];
+
   // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads, all
   // issued before the first LDS store
   {
@@ -568,6 +576,21 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
       xd[r] = t < L ? *reinterpret_cast<const s16x8*>(dout + off) : z8;
     }
     const bf16 xb = tid < L ? beta[(a + tid) * H + h] : bf16(0.f);
+#pragma unroll
+    for (int dd = 0; dd < DBW; ++dd) {
+      const int d = 16 * (w * DBW + dd) + n;
+#pragma unroll
+      for (int E = 0; E < EB; ++E) {
+        L1r[E][dd] = ld4(Lws + soff + int64_t(d) * DV + 16 * E + 4 * g4);
+        Sc[E][dd] = ld4(Sws + soff + int64_t(d) * DV + 16 * E + 4 * g4);
+      }
+    }
+#pragma unroll
+    for (int D = 0; D < DB; ++D)
+#pragma unroll
+      for (int ee = 0; ee < EBW; ++ee)
+        L2r[D][ee] = ev_active ? ld4(Lws + soff + int64_t(16 * D + n) * DV + 16 * eblk(ee) + 4 * g4)
+                               : s16x4{0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
       const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
@@ -621,11 +644,6 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
   }
   __syncthreads();
 
-  const int lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
-  const int64_t soff = (int64_t(gc) * H + h) * DK * DV;
-  const bool ev_active = EB >= NW || w < EB;  // wave-uniform
-  auto eblk = [&](int ee) { return EB >= NW ? w * EBW + ee : w; };
-
   // Lambda in the two orientations: L1[E][dd] (rows e, column d = 16 (w DBW + dd) + n)
   // and L2[D][ee] (rows d = 16 D + 4 g4 + j, column e = 16 (w EBW + ee) + n).
   f32x4 L1[EB][DBW], L2[DB][EBW];
@@ -633,7 +651,7 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
   for (int dd = 0; dd < DBW; ++dd) {
     const int d = 16 * (w * DBW + dd) + n;
 #pragma unroll
-    for (int E = 0; E < EB; ++E) L1[E][dd] = unpack4(ld4(Lws + soff + int64_t(d) * DV + 16 * E + 4 * g4));
+    for (int E = 0; E < EB; ++E) L1[E][dd] = unpack4(L1r[E][dd]);
   }
   // identity 16x16 operand (either side)
   s16x4 eye;
@@ -643,21 +661,11 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
 #pragma unroll
     for (int D = 0; D < DB; ++D)
 #pragma unroll
-      for (int ee = 0; ee < EBW; ++ee) {
-        const s16x4 av = ev_active ? ld4(Lws + soff + int64_t(16 * D + n) * DV + 16 * eblk(ee) + 4 * g4)
-                                   : s16x4{0, 0, 0, 0};
-        L2[D][ee] = mfma16(av, eye, f32x4{0.f, 0.f, 0.f, 0.f});
-      }
+      for (int ee = 0; ee < EBW; ++ee) L2[D][ee] = mfma16(L2r[D][ee], eye, f32x4{0.f, 0.f, 0.f, 0.f});
   }
 
   // S^T before sub-chunk i, columns of this wave: 2^{sum_{j<i} T_j} S_c^T plus the
   // sub-chunks before i, each with Kt scaled by 2^{sum_{j<=j'<i} T_j'}.
-  s16x4 Sc[EB][DBW];
-#pragma unroll
-  for (int dd = 0; dd < DBW; ++dd)
-#pragma unroll
-    for (int E = 0; E < EB; ++E)
-      Sc[E][dd] = ld4(Sws + soff + int64_t(16 * (w * DBW + dd) + n) * DV + 16 * E + 4 * g4);
   f32x4 S[EB][DBW];
   auto state_at = [&](int i) {
 #pragma unroll
