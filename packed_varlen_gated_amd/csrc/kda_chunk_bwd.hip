@@ -648,11 +648,9 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
   // and L2[D][ee] (rows d = 16 D + 4 g4 + j, column e = 16 (w EBW + ee) + n).
   f32x4 L1[EB][DBW], L2[DB][EBW];
 #pragma unroll
-  for (int dd = 0; dd < DBW; ++dd) {
-    const int d = 16 * (w * DBW + dd) + n;
+  for (int dd = 0; dd < DBW; ++dd)
 #pragma unroll
     for (int E = 0; E < EB; ++E) L1[E][dd] = unpack4(L1r[E][dd]);
-  }
   // identity 16x16 operand (either side)
   s16x4 eye;
 #pragma unroll
