@@ -382,9 +382,10 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 
   // Loads are unconditional so the wait counts stay exact: a chunk index past
   // the segment gets an empty buffer (every read returns 0, no memory access).
-  // Every raw input is loaded a whole chunk step before its use: q, k of chunk
-  // c+1 at the start of step c (two register sets alternate), v of chunk c+1
-  // right after V^T of chunk c, g of chunk c+2 after the scan of chunk c+1.
+  // Raw inputs are loaded ahead of their use: q, k of chunk c+1 at the start
+  // of step c (two register sets alternate; the scan of chunk c+1 in the
+  // second half of step c folds the gates into them), v of chunk c+1 right
+  // after V of chunk c went to LDS, g of chunk c+2 after the scan of chunk c+1.
   // beta goes through LDS (double-buffered by chunk parity): wave 0 loads it a
   // step ahead.
   struct Src {
