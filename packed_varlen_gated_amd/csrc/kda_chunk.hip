@@ -440,7 +440,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // sub-chunk (the next half's factors are products of those). The state
   // pass has no q and folds k only.
   auto scan = [&](const Raw<PCPL, PVPL>& R, RawQK<PCPL>& X) {
-    float cs[4][PCPL], tot[PCPL], Tw[PCPL];
+    float cs[4][PCPL], tot[PCPL];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
       float run = 0.f;
@@ -462,11 +462,10 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 #pragma unroll
       for (int i = 0; i < 4; ++i) cs[i][c] += excl;
       tot[c] = lo + hi;  // the sub-chunk total, in every lane
-      Tw[c] = tot[c];
     }
     if (tq == 3) {
 #pragma unroll
-      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c + cg) * 4 + sw] = ex2(tot[c]);
+      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c + cg) * 4 + sw] = ex2(tot[c]);  // + cg: the table's padding
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -474,8 +473,8 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       for (int c = 0; c < PCPL; c += 2) {
         if constexpr (!kState)
           X.q[i][c >> 1] = pk2(bf(X.q[i], c) * ex2(cs[i][c]), bf(X.q[i], c + 1) * ex2(cs[i][c + 1]));
-        X.k[i][c >> 1] = pk2(bf(X.k[i], c) * ex2(Tw[c] - cs[i][c]),
-                             bf(X.k[i], c + 1) * ex2(Tw[c + 1] - cs[i][c + 1]));
+        X.k[i][c >> 1] = pk2(bf(X.k[i], c) * ex2(tot[c] - cs[i][c]),
+                             bf(X.k[i], c + 1) * ex2(tot[c + 1] - cs[i][c + 1]));
       }
     }
   };
