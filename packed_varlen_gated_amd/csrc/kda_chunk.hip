@@ -70,7 +70,7 @@ constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 f
 // Work plan (built on the device by kda_plan_kernel; see there).
 constexpr int kPlanThreads = 256;
 constexpr int kHistBins = 2048;   // run-length bins of the longest-first order
-constexpr int kMinRun = 8;        // chunks: no run is cut shorter, no shorter segment is cut
+constexpr int kMinRun = 4;        // chunks: no run is cut shorter, no shorter segment is cut
 constexpr int kRunDiv = 4;        // cut runs are at most 1/kRunDiv of the per-CU share
 constexpr int kMaxRuns = 16;      // runs per segment
 constexpr int kShareCUs = 256;    // compute units the per-CU share is counted over

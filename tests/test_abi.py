@@ -121,11 +121,11 @@ def test_workspace_size_and_check(lib):
     """The chunk path (bf16, Dk/Dv in {64, 128}) keeps its work plan in the
     workspace: a run table (8 int32 per run, up to max_segs + s runs) and the
     states (Dk x Dv fp32) and decay products (Dk fp32) of s cut pieces per head,
-    s = min(chunk bound / 8, 1024 / H); other paths need none."""
+    s = min(chunk bound / 4, 1024 / H); other paths need none."""
     size = lib.pkv_chunk_kda_varlen_workspace_size
 
     def expect(N, H, Dk, Dv, S):
-        s = min((N + 63 * S) // 64 // 8, 1024 // H)
+        s = min((N + 63 * S) // 64 // 4, 1024 // H)
         up = lambda x: (x + 255) // 256 * 256
         table = (64 + 8 * (S + s) + 4 * s) * 4
         return up(table) + up(s * H * Dk * Dv * 4) + up(s * H * Dk * 4)
