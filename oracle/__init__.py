@@ -15,9 +15,11 @@ Sources (the pages; cited by title and section):
   contract" (reset semantics).
 * "Drill: Sequence Packing from scratch" (ac.fzhiy.net), section "The math"
   (cu_seqlens, doc(s), block-diagonal mask).
-* RFC-0026, section 6 (data pipeline alignment: EOD segmentation, positions,
-  loss mask), section 3.3 (the wrapper's ``initial_state``) and section 3.1.1's
-  [B, T] ``segment_ids`` contract (reset where the id changes or a row starts).
+* RFC-0025, Design section 6 (data pipeline alignment: EOD segmentation,
+  positions, loss mask).
+* RFC-0026, section 3.3 (the wrapper's ``initial_state``), section 3.1.1's
+  [B, T] ``segment_ids`` contract (reset where the id changes or a row starts)
+  and section 3.4 (padding id 0, which the kernel ignores).
 
 Functions and their pin status (every function is pinned; see tests/):
 
@@ -37,8 +39,11 @@ Functions and their pin status (every function is pinned; see tests/):
                                     random linear loss for every input
                                     (q, k, v, g, beta, initial state)
 ``chunk_kda_segment_ids``           pinned: gate injection (g = -inf at each
-                                    segment start, RFC-0026 Alternatives),
-                                    hand-derived two-row case, padding runs
+                                    segment start, RFC-0026 Alternatives) on
+                                    the row's real positions, trailing padding
+                                    cut off gives the same bits, hand-derived
+                                    four-row case (padding before, between,
+                                    after and instead of documents)
 ``eod_to_segment_ids``              pinned: hand-derived rows, construction
                                     from document lengths
 ==================================  =========================================

@@ -84,12 +84,16 @@ def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, initial_stat
     """The [B, T] segment_ids contract of RFC-0026 section 3.1.1, row by row.
 
     q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H]; segment_ids: int
-    [B, T]; initial_state: [B, H, Dk, Dv] or None. The state is cleared where
-    segment_ids[b, t] != segment_ids[b, t - 1] and at t = 0 of every row (rows
-    never share state); id 0 (padding) is an id like any other. The first
-    segment of row b starts from initial_state[b] (section 3.3's per-row
-    shape), later ones from zero. Returns (o [B, T, H, Dv], final_state
-    [B, H, Dk, Dv]): the state after each row's last position.
+    [B, T]; initial_state: [B, H, Dk, Dv] or None. Rows never share state.
+    Section 3.1.1 clears the state where segment_ids[b, t] != segment_ids[b, t - 1]
+    (t = 0 always starts a segment); section 3.4 pads with id 0, which the kernel
+    ignores. Read together: a padding position (id 0) leaves the state as it is
+    and gets o = 0; a real position whose id differs from the previous
+    position's starts a new segment from zero, except the row's first real
+    position, which starts the row's first segment from initial_state[b]
+    (section 3.3's per-row shape). Returns (o [B, T, H, Dv], final_state
+    [B, H, Dk, Dv]): the state after each row's last real position
+    (initial_state[b], or zero, for a row of padding only).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -105,9 +109,13 @@ def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, initial_stat
     final_state = np.zeros((B, H, Dk, Dv), dtype=np.float64)
     for b in range(B):
         S = np.zeros((H, Dk, Dv)) if initial_state is None else np.array(initial_state[b], dtype=np.float64)
+        seen_real = False
         for t in range(T):
-            if t > 0 and seg[b, t] != seg[b, t - 1]:
+            if seg[b, t] == 0:
+                continue  # padding: the state is untouched and o stays 0
+            if seen_real and seg[b, t] != seg[b, t - 1]:
                 S = np.zeros((H, Dk, Dv))  # a new segment: the state is cleared
+            seen_real = True
             decay = np.exp(g[b, t])[:, :, None]
             S = decay * S + beta[b, t][:, None, None] * k[b, t][:, :, None] * v[b, t][:, None, :]
             o[b, t] = scale * np.einsum("hde,hd->he", S, q[b, t])

@@ -242,40 +242,70 @@ def test_split_and_resume_equals_whole_segment():
 
 
 def test_segment_ids_contract_is_gate_injection_per_row():
-    """RFC-0026 section 3.1.1's [B, T] contract (clear the state where the id
-    changes and at every row start; id 0 is an id like any other) equals, row
-    by row, one continuous run with g = -inf at each segment start (RFC-0026
-    Alternatives, gate injection); the first segment keeps the row's initial
-    state and the row's final state is the last segment's."""
+    """RFC-0026 section 3.1.1's [B, T] contract with section 3.4's padding
+    (id 0, ignored by the kernel) equals, row by row, one continuous run over
+    the row's real positions only, with g = -inf (RFC-0026 Alternatives, gate
+    injection) at every real position whose id differs from the position
+    before it in the row, except the row's first real position; the run starts
+    from the row's initial state. Padding positions get exactly o = 0 and the
+    row's final state is the run's."""
     rng = np.random.default_rng(41)
-    B, T, H, Dk, Dv = 3, 40, 2, 3, 4
+    B, T, H, Dk, Dv = 5, 40, 2, 3, 4
     q, k, v, g, beta = [a.reshape((B, T) + a.shape[1:]) for a in _rand_inputs(rng, B * T, H, Dk, Dv)]
-    seg = np.array([[1] * 10 + [2] * 5 + [0] * 3 + [3] * 22,
-                    [0] * 4 + [1] * 36,
-                    [5] * 40])
+    seg = np.array([[1] * 10 + [2] * 5 + [0] * 3 + [3] * 22,   # padding between documents
+                    [0] * 4 + [1] * 36,                        # leading padding
+                    [5] * 40,                                  # one document
+                    [1] * 7 + [0] * 2 + [1] * 20 + [0] * 11,   # the same id on both sides of padding
+                    [0] * 40])                                 # padding only
     S0 = rng.standard_normal((B, H, Dk, Dv))
     o, fs = oracle.chunk_kda_segment_ids(q, k, v, g, beta, seg, scale=0.9, initial_state=S0)
     for b in range(B):
-        g2 = g[b].copy()
-        for t in range(1, T):
-            if seg[b, t] != seg[b, t - 1]:
-                g2[t] = -np.inf
-        o2, f2 = oracle.chunk_kda_varlen(q[b], k[b], v[b], g2, beta[b], None, scale=0.9,
-                                         initial_state=S0[b:b + 1])
-        assert np.array_equal(o[b], o2)
+        real = [t for t in range(T) if seg[b, t] != 0]
+        pad = [t for t in range(T) if seg[b, t] == 0]
+        assert np.all(o[b, pad] == 0)
+        if not real:
+            assert np.array_equal(fs[b], S0[b])
+            continue
+        g2 = g[b, real].copy()
+        for j, t in enumerate(real):
+            if j > 0 and seg[b, t] != seg[b, t - 1]:
+                g2[j] = -np.inf
+        o2, f2 = oracle.chunk_kda_varlen(q[b, real], k[b, real], v[b, real], g2, beta[b, real], None,
+                                         scale=0.9, initial_state=S0[b:b + 1])
+        assert np.array_equal(o[b, real], o2)
         assert np.array_equal(fs[b], f2[0])
+
+
+def test_segment_ids_trailing_padding_is_ignored():
+    """A row padded with zeros to a longer length (RFC-0026 section 3.4: the
+    module pads T up to a multiple of 64 with id 0) gives the unpadded row's
+    outputs and final state, and zeros at the padding."""
+    rng = np.random.default_rng(43)
+    T0, T, H, Dk, Dv = 45, 64, 2, 3, 2
+    q, k, v, g, beta = [a.reshape((1, T) + a.shape[1:]) for a in _rand_inputs(rng, T, H, Dk, Dv)]
+    seg = np.array([[1] * 20 + [2] * 25 + [0] * (T - T0)])
+    S0 = rng.standard_normal((1, H, Dk, Dv))
+    o, fs = oracle.chunk_kda_segment_ids(q, k, v, g, beta, seg, initial_state=S0)
+    o0, f0 = oracle.chunk_kda_segment_ids(q[:, :T0], k[:, :T0], v[:, :T0], g[:, :T0], beta[:, :T0],
+                                          seg[:, :T0], initial_state=S0)
+    assert np.array_equal(o[:, :T0], o0) and np.array_equal(fs, f0)
+    assert np.all(o[:, T0:] == 0)
 
 
 def test_segment_ids_contract_hand_case():
     """Dk = Dv = 1, q = k = v = beta = 1, g = 0: the state counts the tokens of
-    the current segment (plus the row's initial state in its first segment)."""
-    seg = np.array([[1, 1, 2, 2, 2], [0, 0, 3, 3, 0]])
-    one = np.ones((2, 5, 1, 1))
-    o, fs = oracle.chunk_kda_segment_ids(one, one, one, np.zeros((2, 5, 1, 1)), np.ones((2, 5, 1)), seg,
-                                         initial_state=np.array([[[[5.0]]], [[[0.0]]]]))
+    the current segment (plus the row's initial state in its first segment);
+    padding positions read 0 and change nothing."""
+    seg = np.array([[1, 1, 2, 2, 2], [0, 0, 3, 3, 0], [1, 0, 1, 1, 0], [0, 0, 0, 0, 0]])
+    one = np.ones((4, 5, 1, 1))
+    S0 = np.array([5.0, 4.0, 5.0, 7.0]).reshape(4, 1, 1, 1)
+    o, fs = oracle.chunk_kda_segment_ids(one, one, one, np.zeros((4, 5, 1, 1)), np.ones((4, 5, 1)), seg,
+                                         initial_state=S0)
     assert o[0, :, 0, 0].tolist() == [6, 7, 1, 2, 3]
-    assert o[1, :, 0, 0].tolist() == [1, 2, 1, 2, 1]
-    assert fs[:, 0, 0, 0].tolist() == [3, 1]
+    assert o[1, :, 0, 0].tolist() == [0, 0, 5, 6, 0]
+    assert o[2, :, 0, 0].tolist() == [6, 0, 1, 2, 0]
+    assert o[3, :, 0, 0].tolist() == [0, 0, 0, 0, 0]
+    assert fs[:, 0, 0, 0].tolist() == [3, 6, 2, 7]
 
 
 def test_backward_matches_finite_differences():
