@@ -20,7 +20,7 @@
  *
  *   pkv_eod_to_segment_ids         EOD-separated token rows -> segment ids,
  *                                  positions and loss segment ids
- *       RFC-0026, section 6 (data pipeline alignment).
+ *       RFC-0025, Design section 6 (data pipeline alignment).
  *
  * and the kernel contract that takes segment ids directly:
  *
@@ -112,7 +112,8 @@ pkv_status pkv_segment_ids_to_cu_seqlens(const int32_t* segment_ids, int64_t B, 
 
 /*
  * EOD-separated token rows -> segment ids, positions and loss segment ids
- * (RFC-0026 "Ling3 KDA varlen support", section 6, data pipeline alignment:
+ * (RFC-0025 "Support attention varlen and align loss", Design section 6, data
+ * pipeline alignment:
  * an EOD token keeps the id of the document it ends and a new segment starts
  * right after it; positions restart at 0 after an EOD; EOD positions carry no
  * loss). Every row is an independent packed sample with ids from 1:
@@ -159,9 +160,11 @@ pkv_status pkv_short_conv_segmask(const void* x, const float* w, const int32_t* 
  * call. With bf16 and Dk, Dv in {64, 128} it holds the call's work plan: the
  * (segment, chunk range) runs in the order they are processed, longest first,
  * and, for segments long enough to be cut into several runs so that one
- * document does not set the length of the whole launch, the state and the
- * per-channel decay product of every run but the last (fp32, at most
- * 1024 + H run-heads in all, i.e. about 64 MiB at Dk = Dv = 128).
+ * document does not set the length of the whole launch (more than 8192
+ * tokens; where a segment is cut depends on its own length only), the state
+ * and the per-channel decay product of every run but the last (fp32, about
+ * N / 4096 runs x H heads x Dk x (Dv + 1) x 4 bytes, i.e. 1/16 of one
+ * [N, H, Dk] bf16 tensor at Dv = 128).
  */
 size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,
                                            int32_t max_segs, int32_t dtype);
@@ -217,12 +220,15 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
  * kernel contract), with no cu_seqlens round trip and no phantom slots.
  *
  * For every row b and head h the recurrence of pkv_chunk_kda_varlen runs over
- * the row, and the state is cleared at t = 0 and wherever
- * segment_ids[b, t] != segment_ids[b, t-1] (id 0, padding, is an id like any
- * other: a run of padding is a segment of its own). The row's first segment
- * starts from initial_state[b, h] (0 when initial_state is NULL);
- * final_state[b, h] is the state after the row's last position (section 3.3's
- * per-row shapes). Rows never share state.
+ * the row. Id 0 is padding, which the kernel ignores (RFC-0026 section 3.4):
+ * a padding position leaves the state as it is and gets o = 0. A real
+ * position whose id differs from the previous position's
+ * (segment_ids[b, t] != segment_ids[b, t-1]) starts a new segment from zero,
+ * except the row's first real position, which starts the row's first segment
+ * from initial_state[b, h] (0 when initial_state is NULL). final_state[b, h]
+ * is the state after the row's last real position (initial_state[b, h], or 0,
+ * for a row of padding only; section 3.3's per-row shapes). Rows never share
+ * state.
  *
  * q, k, g     [B, T, H, Dk]; v [B, T, H, Dv]; beta [B, T, H]; o [B, T, H, Dv]
  *             (one dtype); segment_ids int32 [B, T].

@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-RFC-0026 "Ling3 KDA varlen support", section 6 (data pipeline alignment),
-states what the pipeline derives from a packed token row whose documents are
+RFC-0025 "Support attention varlen and align loss", Design section 6 (data
+pipeline alignment), states what the pipeline derives from a packed token row whose documents are
 separated by an EOD token:
 
 * input segmentation: an EOD token keeps the id of the document it ends, and

@@ -116,6 +116,25 @@ def _need(t, name, device, dtype=None, ndim=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(workspace, need, device):
+    """The caller's workspace (checked: a contiguous uint8 tensor on the
+    call's device holding at least `need` bytes), or a new one."""
+    if need <= 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", device, torch.uint8)
+    nbytes = workspace.numel()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, the call needs {need}")
+    return workspace, nbytes
+
+
 class EodSegments(NamedTuple):
     segment_ids: torch.Tensor                 # int32 [B, T]
     positions: Optional[torch.Tensor]         # int32 [B, T] or None
@@ -175,6 +194,7 @@ def short_conv_segmask(x, w, segment_ids=None, out=None):
             raise ValueError("segment_ids must be [B, T]")
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", dev, x.dtype, 3)
+    _need_shape(y, "out", x.shape)
     _check(lib.pkv_short_conv_segmask(_ptr(x), _ptr(w), _ptr(segment_ids), _ptr(y), B, T, F,
                                       w.shape[1], dt, _stream(dev)))
     return y
@@ -213,6 +233,7 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_
         max_segs = 1
     o = torch.empty(Bq, Tq, H, Dv, dtype=dt, device=dev) if out is None else out
     _need(o, "out", dev, dt, 4)
+    _need_shape(o, "out", (Bq, Tq, H, Dv))
     fs = torch.empty(max_segs, H, Dk, Dv, dtype=torch.float32, device=dev) if output_final_state else None
     if flags is not None:
         _need(flags, "flags", dev, torch.int32, 1)
@@ -221,9 +242,7 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_
         if tuple(initial_state.shape) != (max_segs, H, Dk, Dv):
             raise ValueError(f"initial_state must be [{max_segs}, {H}, {Dk}, {Dv}]")
     need = int(lib.pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, code))
-    if need > 0 and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     _check(lib.pkv_chunk_kda_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                     max_segs, N, H, Dk, Dv, float(scale), code, _ptr(initial_state),
                                     _ptr(o), _ptr(fs),
@@ -258,6 +277,7 @@ def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, output_final
         raise ValueError("v must be [B, T, H, Dv], beta [B, T, H] and segment_ids [B, T]")
     o = torch.empty(B, T, H, Dv, dtype=dt, device=dev) if out is None else out
     _need(o, "out", dev, dt, 4)
+    _need_shape(o, "out", (B, T, H, Dv))
     fs = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev) if output_final_state else None
     if initial_state is not None:
         _need(initial_state, "initial_state", dev, torch.float32, 4)
@@ -266,9 +286,7 @@ def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, output_final
     if flags is not None:
         _need(flags, "flags", dev, torch.int32, 1)
     need = int(lib.pkv_chunk_kda_segment_ids_workspace_size(B, T, H, Dk, Dv, code))
-    if need > 0 and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     _check(lib.pkv_chunk_kda_segment_ids(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(segment_ids),
                                          B, T, H, Dk, Dv, float(scale), code, _ptr(initial_state), _ptr(o),
                                          _ptr(fs), _ptr(flags), _ptr(workspace), ws_bytes, _stream(dev)))
@@ -333,9 +351,7 @@ def chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_seqlens=None, scale=1.0, 
     dbeta = torch.empty_like(beta)
     dinit = torch.empty(max_segs, H, Dk, Dv, dtype=torch.float32, device=dev) if output_d_initial_state else None
     need = int(lib.pkv_chunk_kda_varlen_backward_workspace_size(N, H, Dk, Dv, max_segs, code))
-    if need > 0 and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     _check(lib.pkv_chunk_kda_varlen_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), max_segs, N, H, Dk, Dv,
         float(scale), code, _ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dk),

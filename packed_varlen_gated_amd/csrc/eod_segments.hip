@@ -1,6 +1,7 @@
 // EOD-separated token rows -> segment ids, positions and loss segment ids.
 //
-// RFC-0026 "Ling3 KDA varlen support", section 6 (data pipeline alignment):
+// RFC-0025 "Support attention varlen and align loss", Design section 6 (data
+// pipeline alignment):
 // an EOD token keeps the id of the document it ends and a new segment starts
 // right after it; positions restart at 0 after an EOD; positions holding the
 // EOD carry no loss (loss id 0). Ids start at 1 in every row (each row is an

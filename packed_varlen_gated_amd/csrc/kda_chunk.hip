@@ -67,13 +67,14 @@ constexpr int kC = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
-// Work plan (built on the device by kda_plan_kernel; see there).
+// Work plan (built on the device by kda_plan_kernel; see there). How a
+// segment is cut depends on its own chunk count and these constants only, so
+// a segment's results never depend on the other segments of the launch.
 constexpr int kPlanThreads = 256;
 constexpr int kHistBins = 2048;   // run-length bins of the longest-first order
-constexpr int kMinRun = 4;        // chunks: no run is cut shorter, no shorter segment is cut
-constexpr int kRunDiv = 4;        // cut runs are at most 1/kRunDiv of the per-CU share
+constexpr int kCutMin = 128;      // chunks: segments of at most this many are never cut
+constexpr int kRunLen = 64;       // chunks: target length of the runs of a cut segment
 constexpr int kMaxRuns = 16;      // runs per segment
-constexpr int kShareCUs = 256;    // compute units the per-CU share is counted over
 constexpr int kPlanHeader = 64;   // int32 words before the run table
 constexpr int kPlanCache = 8192;  // segment slots whose chunk counts the plan keeps in LDS
 
@@ -272,7 +273,8 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     int32_t* __restrict__ plan, int32_t runs_max, int32_t max_segs, int64_t N,
     int32_t H, float scale, const float* __restrict__ initial_state, bf16* __restrict__ o,
     float* __restrict__ final_state, float* __restrict__ run_states,
-    float* __restrict__ run_decays, int64_t row_len, int32_t lds_zero) {
+    float* __restrict__ run_decays, int64_t row_len, const int32_t* __restrict__ seg_ids,
+    const int32_t* __restrict__ n_dev, int32_t lds_zero) {
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
   constexpr int PCPL = C::PCPL, PVPL = C::PVPL, ET = C::ET, DT = C::DT, KS = C::KS;
@@ -885,13 +887,20 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
         // S = D_j S + L_j over them in order (D_j, L_j: piece j's decay
         // product and its state from zero).
         // Slot-indexed states; with row_len > 0 (segments from a [B, T] id
-        // scan) they are row-indexed: a row's first segment starts from its
-        // row's state and its last one writes the row's final state.
+        // scan, padding segments have no items) they are row-indexed: a
+        // row's first real segment starts from its row's state and its last
+        // real one writes the row's final state. A real segment is the first
+        // of its row when it starts the row or follows a padding segment that
+        // does, and the last when it ends the row or precedes a padding
+        // segment that does (runs of equal ids never cross a row start).
         int64_t init_idx = slot, fin_idx = slot;
         if (row_len > 0) {
           const int64_t a = cu[slot], e = cu[slot + 1];
-          init_idx = a % row_len == 0 ? a / row_len : -1;
-          fin_idx = e % row_len == 0 ? e / row_len - 1 : -1;
+          const int64_t b = a / row_len, r0 = b * row_len, r1 = r0 + row_len;
+          const bool first = a == r0 || (cu[slot - 1] == r0 && seg_ids[r0] == 0);
+          const bool lastr = e == r1 || (cu[slot + 2] == r1 && seg_ids[e] == 0);
+          init_idx = first ? b : -1;
+          fin_idx = lastr ? b : -1;
         }
         if (initial_state != nullptr && init_idx >= 0) {
           const float* s0 = initial_state + (init_idx * H + h) * DK * DV;
@@ -963,6 +972,25 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     const int64_t n16 = (N - cu_last) * H * DV / 8;  // DV * 2 bytes is a multiple of 16
     u32x4* o16 = reinterpret_cast<u32x4*>(o + cu_last * H * DV);
     for (int64_t i = int64_t(blockIdx.x) * NT + tid; i < n16; i += G * NT) o16[i] = u32x4{0u, 0u, 0u, 0u};
+    if (row_len > 0) {
+      // [B, T] ids: padding segments output 0; a row of padding only passes
+      // its initial state (or zero) through to its final state.
+      const int n_seg = *n_dev;
+      for (int u = blockIdx.x; u < n_seg; u += G) {
+        const int64_t a = cu[u], e = cu[u + 1];
+        if (seg_ids[a] != 0) continue;
+        u32x4* oz = reinterpret_cast<u32x4*>(o + a * H * DV);
+        for (int64_t i = tid; i < (e - a) * H * DV / 8; i += NT) oz[i] = u32x4{0u, 0u, 0u, 0u};
+        if (final_state == nullptr || a % row_len != 0 || e - a != row_len) continue;
+        const int64_t b = a / row_len;
+        for (int hh = 0; hh < H; ++hh) {
+          f32x4* f = reinterpret_cast<f32x4*>(final_state + (b * H + hh) * DK * DV);
+          const f32x4* f0 = reinterpret_cast<const f32x4*>(initial_state + (b * H + hh) * DK * DV);
+          for (int j = tid; j < DK * DV / 4; j += NT)
+            f[j] = initial_state != nullptr ? f0[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
     if (final_state != nullptr && cu != nullptr) {
       for (int64_t u = blockIdx.x; u < int64_t(max_segs) * H; u += G) {
         const int i = int(u / H);
@@ -980,36 +1008,28 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 
 // ---------------------------------------------------------------- work plan
 // One work-group builds the launch's work list from cu_seqlens:
-// 1. the chunk total over the well-formed segments gives the per-CU share
-//    avg = ceil(total H / kShareCUs) in chunk steps;
-// 2. a segment longer than max(avg, kMinRun) chunks is cut into m nearly equal
-//    runs of at least max(kMinRun, ceil(avg / kRunDiv)) chunks
-//    (m <= kMaxRuns); every other non-empty segment is one run; empty and
-//    malformed segments have none (malformed ones set
-//    PKV_FLAG_BAD_CU_SEQLENS here);
-// 3. runs are ranked longest first through a histogram of run lengths (ties in
+// 1. a segment of n chunks is one run when n <= kCutMin, else it is cut into
+//    m = min(kMaxRuns, ceil(n / kRunLen)) nearly equal runs (run j = chunks
+//    [n j / m, n (j + 1) / m)): a function of n alone, so where a segment is
+//    cut (and with it the rounding of the composed states) never depends on
+//    the other segments of the launch; empty and malformed segments have no
+//    run (malformed ones set PKV_FLAG_BAD_CU_SEQLENS here);
+// 2. runs are ranked longest first through a histogram of run lengths (ties in
 //    any order: results do not depend on the order), and so are the runs that
 //    are not last in their segment, which the state pass takes.
 // The state slots of a segment's first m - 1 runs are consecutive from sbase
 // (exclusive prefix of m - 1 over the segments, computed tile by tile).
 // Chunk counts are below 2^26 (N <= INT32_MAX), so all per-segment arithmetic
 // is 32-bit; the work-group is small because the work is tiny and serial.
-__device__ __forceinline__ int plan_runs(int n, int thr, int R) {
+__device__ __forceinline__ int plan_runs(int n) {
   if (n <= 0) return 0;
-  if (n <= thr) return 1;
-  const int floor_len = (n + kMaxRuns - 1) / kMaxRuns;
-  const int Ri = R > floor_len ? R : floor_len;
-  return (n + Ri - 1) / Ri;
+  if (n <= kCutMin) return 1;
+  const int m = (n + kRunLen - 1) / kRunLen;
+  return m < kMaxRuns ? m : kMaxRuns;
 }
 // chunks before run j of a segment of n chunks cut into m runs (n j < 2^30)
 __device__ __forceinline__ int run_begin(int n, int m, int j) { return int(uint32_t(n * j) / uint32_t(m)); }
 __device__ __forceinline__ int len_bin(int len) { return len < kHistBins - 1 ? len : kHistBins - 1; }
-
-__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-  return x;
-}
 
 // Exclusive prefix over the work-group (kPlanThreads threads); *total gets the sum.
 __device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
@@ -1034,17 +1054,19 @@ __device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
   return before + inc - x;
 }
 
+// seg_ids (segments from a [B, T] id scan): a segment whose first id is 0 is
+// padding and gets no run (its tokens leave the state alone and output 0).
 __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* __restrict__ cu,
                                                                 const int32_t* __restrict__ n_dev,
+                                                                const int32_t* __restrict__ seg_ids,
                                                                 int32_t max_segs_arg, int32_t N,
-                                                                int32_t H, int32_t states_max,
+                                                                int32_t states_max,
                                                                 int32_t runs_max,
                                                                 int32_t* __restrict__ plan,
                                                                 int32_t* __restrict__ flags) {
   __shared__ int s_hr[kHistBins];  // main runs per length bin, then next free rank
   __shared__ int s_hs[kHistBins];  // state runs likewise
   __shared__ int s_tmp[kPlanThreads / 64];
-  __shared__ unsigned long long s_total;
   __shared__ int s_n[kPlanCache];  // chunk counts, when max_segs <= kPlanCache
   const int tid = threadIdx.x;
   // segment slots: the caller's count, or the one a boundary scan left on the device
@@ -1052,34 +1074,25 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   const int states_word_off = kPlanHeader + 8 * runs_max;
   const bool cached = max_segs <= kPlanCache;
   for (int i = tid; i < kHistBins; i += kPlanThreads) s_hr[i] = s_hs[i] = 0;
-  if (tid == 0) s_total = 0;
   __syncthreads();
-  // chunks of segment i; malformed ones count 0 and are flagged
+  // chunks of segment i; malformed and padding ones count 0, malformed ones are flagged
   auto chunks = [&](int i, bool& bad) -> int {
     bad = false;
     if (cu == nullptr) return int((uint32_t(N) + kC - 1) / kC);
     const int a = cu[i], e = cu[i + 1];
     bad = a < 0 || e < a || e > N || (i == 0 && a != 0);
-    return bad ? 0 : int((uint32_t(e - a) + kC - 1) / kC);
+    if (bad || e == a || (seg_ids != nullptr && seg_ids[a] == 0)) return 0;
+    return int((uint32_t(e - a) + kC - 1) / kC);
   };
-  int64_t mine = 0;  // 64-bit: overlapping (malformed) slots can sum past 2^31
   bool any_bad = false;
   for (int i = tid; i < max_segs; i += kPlanThreads) {
     bool bad;
     const int n = chunks(i, bad);
     if (cached) s_n[i] = n;
-    mine += n;
     any_bad = any_bad || bad;
   }
   if (any_bad && flags != nullptr) atomicOr(flags, kFlagBadCuSeqlens);
-  mine = wave_sum64(mine);
-  if ((tid & 63) == 0) atomicAdd(&s_total, (unsigned long long)mine);
   __syncthreads();
-  const int64_t total = int64_t(s_total);
-  const int64_t avg64 = (total * H + kShareCUs - 1) / kShareCUs;
-  const int avg = avg64 < (1 << 30) ? int(avg64) : (1 << 30);
-  const int thr = avg > kMinRun ? avg : kMinRun;
-  const int R = (avg + kRunDiv - 1) / kRunDiv > kMinRun ? (avg + kRunDiv - 1) / kRunDiv : kMinRun;
 
   // Runs of each segment, with the state-slot budget enforced in slot order:
   // a segment whose extra runs would not fit stays whole (only on malformed
@@ -1090,7 +1103,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
       const int i = base + tid;
       bool bad;
       const int n = i >= max_segs ? 0 : cached ? s_n[i] : chunks(i, bad);
-      int m = plan_runs(n, thr, R);
+      int m = plan_runs(n);
       int tile_total;
       const int sb = carry + block_exclusive_scan(m > 1 ? m - 1 : 0, s_tmp, &tile_total);
       if (m > 1 && sb + m - 1 > states_max) m = 1;
@@ -1172,12 +1185,16 @@ struct PlanLayout {
   size_t off_L, off_D, bytes;
 };
 
+// Saved pieces: a cut segment has len > kCutMin * kC tokens and n =
+// ceil(len / kC) chunks, and saves m - 1 < n / kRunLen <= (len + kC - 1) /
+// (kC kRunLen) pieces; over at most N / (kCutMin kC + 1) such segments whose
+// lengths sum to at most N, that is below the bound here (about N / 4096,
+// 1/16 of one [N, H, Dk] bf16 tensor in bytes at Dv = 128).
 PlanLayout plan_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs) {
   PlanLayout p;
-  const int64_t chunk_ub = (N + int64_t(kC - 1) * max_segs) / kC;
-  const int64_t by_min = chunk_ub / kMinRun;
-  const int64_t by_share = int64_t(kShareCUs) * kRunDiv / H;
-  p.states_max = by_min < by_share ? by_min : by_share;
+  constexpr int64_t kCutLen = int64_t(kCutMin) * kC + 1;  // shortest cut segment, tokens
+  const int64_t n_cut = N / kCutLen;
+  p.states_max = n_cut == 0 ? 0 : (N + (kC - 1) * n_cut) / (int64_t(kC) * kRunLen) + 1;
   p.runs_max = int64_t(max_segs) + p.states_max;
   p.states_word_off = size_t(kPlanHeader) + 8 * size_t(p.runs_max);
   const size_t table = (p.states_word_off + 4 * size_t(p.states_max)) * 4;
@@ -1210,7 +1227,7 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
                        const void* beta, const int32_t* cu, const int32_t* n_dev,
                        int32_t layout_segs, int32_t max_segs, int64_t N, int32_t H, float scale,
                        const float* s0, void* o, float* fs, int32_t* flags, char* ws,
-                       int64_t row_len, hipStream_t s) {
+                       int64_t row_len, const int32_t* seg_ids, hipStream_t s) {
   using C = Cfg<DK, DV>;
   constexpr int state_bytes = C::off_qh;  // the state pass uses the small tables, V and Kbar
   static bool attr_set = false;
@@ -1227,8 +1244,8 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   int32_t* plan = reinterpret_cast<int32_t*>(ws);
   float* states = reinterpret_cast<float*>(ws + L.off_L);
   float* decays = reinterpret_cast<float*>(ws + L.off_D);
-  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, n_dev, max_segs,
-                     int32_t(N), H, int32_t(L.states_max), int32_t(L.runs_max), plan, flags);
+  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, n_dev, seg_ids,
+                     max_segs, int32_t(N), int32_t(L.states_max), int32_t(L.runs_max), plan, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const auto qp = static_cast<const bf16*>(q), kp = static_cast<const bf16*>(k);
@@ -1240,13 +1257,13 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
     hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true>), dim3(grid), dim3(C::NT), state_bytes, s,
                        qp, kp, vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale,
                        static_cast<const float*>(nullptr), static_cast<bf16*>(nullptr),
-                       static_cast<float*>(nullptr), states, decays, row_len, 0);
+                       static_cast<float*>(nullptr), states, decays, row_len, seg_ids, n_dev, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false>), dim3(grid), dim3(C::NT), C::bytes, s, qp, kp,
                      vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale, s0,
-                     static_cast<bf16*>(o), fs, states, decays, row_len, 0);
+                     static_cast<bf16*>(o), fs, states, decays, row_len, seg_ids, n_dev, 0);
   return hipGetLastError();
 }
 
@@ -1286,13 +1303,13 @@ hipError_t launch_kda_chunk_ids(const void* q, const void* k, const void* v, con
   if (e != hipSuccess) return e;
   const int32_t S = int32_t(N);
   if (Dk == 128 && Dv == 128)
-    return launch_dims<128, 128>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, stream);
+    return launch_dims<128, 128>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, seg, stream);
   if (Dk == 64 && Dv == 64)
-    return launch_dims<64, 64>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, stream);
+    return launch_dims<64, 64>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, seg, stream);
   if (Dk == 128 && Dv == 64)
-    return launch_dims<128, 64>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, stream);
+    return launch_dims<128, 64>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, seg, stream);
   if (Dk == 64 && Dv == 128)
-    return launch_dims<64, 128>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, stream);
+    return launch_dims<64, 128>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, seg, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1303,13 +1320,13 @@ hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const v
                             int32_t* flags, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   if (Dk == 128 && Dv == 128)
-    return launch_dims<128, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, stream);
+    return launch_dims<128, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
   if (Dk == 64 && Dv == 64)
-    return launch_dims<64, 64>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, stream);
+    return launch_dims<64, 64>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
   if (Dk == 128 && Dv == 64)
-    return launch_dims<128, 64>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, stream);
+    return launch_dims<128, 64>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
   if (Dk == 64 && Dv == 128)
-    return launch_dims<64, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, stream);
+    return launch_dims<64, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
   return hipErrorInvalidValue;
 }
 

@@ -68,6 +68,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kC = 64;
 constexpr int kPlanThreads = 1024;
+// Long segments are cut into pieces by their own chunk count only (as in the
+// forward pass): more than kCutMin chunks -> pieces of about kPieceLen chunks,
+// at most kMaxPieces of them.
+constexpr int kCutMin = 128;
+constexpr int kPieceLen = 64;
+constexpr int kMaxPieces = 16;
 constexpr int kTailBlocks = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -151,10 +157,10 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t x, int64_t* s_scan, i
 
 // base[i]  = global index of slot i's first chunk (base[max_segs] = chunks);
 // pbase[i] = index of slot i's first piece: a segment of n chunks is one piece,
-//            or, when n exceeds max(per-CU share, 32), m = min(16, ceil(n / R))
-//            pieces of nearly equal length (piece j = chunks [n j / m, n (j+1) / m)),
-//            R = max(32, share / 4), so no (segment, head) chain is much longer
-//            than the share; empty slots also get one (empty) piece;
+//            or, when n exceeds kCutMin, m = min(kMaxPieces, ceil(n / kPieceLen))
+//            pieces of nearly equal length (piece j = chunks [n j / m, n (j+1) / m)):
+//            a function of n alone, so a segment's gradients never depend on the
+//            other segments of the launch; empty slots also get one (empty) piece;
 // sbase[i] = index of slot i's first piece summary (cut segments only).
 // All are capped at their workspace bounds (reached only when cu_seqlens is
 // invalid, which sets the flag).
@@ -184,16 +190,14 @@ __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
   if (tid == 0) base[max_segs] = int32_t(chunks);
   __threadfence_block();
   __syncthreads();
-  const int64_t share = (chunks * H + 255) / 256;
-  const int64_t thr = share > 32 ? share : 32;
-  const int64_t R = (share + 3) / 4 > 32 ? (share + 3) / 4 : 32;
   int64_t run_p = 0, run_s = 0, tot_p, tot_s;
   for (int tile0 = 0; tile0 < max_segs; tile0 += kPlanThreads) {
     const int slot = tile0 + tid;
     int64_t m = 0, ms = 0;
     if (slot < max_segs) {
       const int64_t n = int64_t(base[slot + 1]) - base[slot];
-      m = n > thr ? ((n + R - 1) / R < 16 ? (n + R - 1) / R : 16) : 1;
+      const int64_t mc = (n + kPieceLen - 1) / kPieceLen;
+      m = n > kCutMin ? (mc < kMaxPieces ? mc : kMaxPieces) : 1;
       ms = m > 1 ? m : 0;
     }
     const int64_t bp = run_p + block_excl_scan(m, s_scan, tot_p);
@@ -879,7 +883,7 @@ BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_s
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   BwdLayout l;
   l.max_chunks = (N + kC - 1) / kC + max_segs;
-  // pieces of cut segments: m <= n / 16 per cut segment (n > 32, pieces >= 32 chunks)
+  // pieces of cut segments: m <= ceil(n / kPieceLen) < n / 16 per cut segment (n > kCutMin)
   l.max_sums = l.max_chunks / 16 + 1;
   l.max_pieces = max_segs + l.max_sums;
   l.plan_bytes = up((size_t(max_segs) + 1) * 4 * 3);

@@ -17,9 +17,12 @@
 // Extra work-groups past max_segs*H zero o for positions >= cu[max_segs].
 //
 // With seg_ids (the [B, T] contract of RFC-0026 section 3.1.1) a work-group
-// takes one (row, head) instead of a slot: the state is cleared where the id
-// changes, by a zero decay for that token (as gate injection does), and the
-// initial and final states are the row's.
+// takes one (row, head) instead of a slot: padding tokens (id 0, which the
+// kernel ignores by section 3.4) leave the state alone and output 0; a real
+// token whose id differs from the previous position's clears the state, by a
+// zero decay for that token (as gate injection does), unless it is the row's
+// first real token, which continues from the row's initial state; the final
+// state is the state after the row's last real token.
 
 #include "common.h"
 
@@ -45,7 +48,8 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
   __shared__ float s_a[kTB][DK];
   __shared__ float s_v[kTB][DV];
   __shared__ float s_b[kTB];
-  __shared__ int s_rst[kTB];
+  __shared__ int s_rst[kTB];  // 1: clear the state before the token; 2: padding, skip it
+  __shared__ int64_t s_first[kThreads / 64];
   __shared__ float s_part[kTB][RG][DV];
 
   const int tid = threadIdx.x;
@@ -79,6 +83,23 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
     }
   }
 
+  // [B, T] ids: the row's first real position (end if there is none)
+  int64_t first_real = end;
+  if (seg_ids != nullptr) {
+    int64_t m = end;
+    for (int64_t t = start + tid; t < end; t += kThreads)
+      if (seg_ids[t] != 0) { m = t; break; }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const int64_t y = __shfl_xor(m, d, 64);
+      m = y < m ? y : m;
+    }
+    if ((tid & 63) == 0) s_first[tid >> 6] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) first_real = s_first[w] < first_real ? s_first[w] : first_real;
+  }
+
   const int e = tid % DV;
   const int rg = tid / DV;
   const int d0 = rg * R;
@@ -105,18 +126,25 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
     if (tid < nt) {
       s_b[tid] = to_f32(beta[(t0 + tid) * H + h]);
       const int64_t t = t0 + tid;
-      s_rst[tid] = seg_ids != nullptr && t > start && seg_ids[t] != seg_ids[t - 1];
+      int r = 0;
+      if (seg_ids != nullptr) {
+        const int id = seg_ids[t];
+        r = id == 0 ? 2 : (t > first_real && id != seg_ids[t - 1]) ? 1 : 0;
+      }
+      s_rst[tid] = r;
     }
     __syncthreads();
     for (int tt = 0; tt < nt; ++tt) {
       const float bv = s_b[tt] * s_v[tt][e];
-      const bool rst = s_rst[tt] != 0;  // a new segment: nothing carries over
+      const int rst = s_rst[tt];  // 1: a new segment, nothing carries over
       float acc = 0.f;
+      if (rst != 2) {  // uniform: one token for the whole work-group
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int d = d0 + r;
-        S[r] = fmaf(rst ? 0.f : s_a[tt][d], S[r], s_k[tt][d] * bv);
-        acc = fmaf(S[r], s_q[tt][d], acc);
+        for (int r = 0; r < R; ++r) {
+          const int d = d0 + r;
+          S[r] = fmaf(rst ? 0.f : s_a[tt][d], S[r], s_k[tt][d] * bv);
+          acc = fmaf(S[r], s_q[tt][d], acc);
+        }
       }
       s_part[tt][rg][e] = acc;
     }

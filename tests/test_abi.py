@@ -120,22 +120,27 @@ def test_workspace_query_is_host_only(lib):
 def test_workspace_size_and_check(lib):
     """The chunk path (bf16, Dk/Dv in {64, 128}) keeps its work plan in the
     workspace: a run table (8 int32 per run, up to max_segs + s runs) and the
-    states (Dk x Dv fp32) and decay products (Dk fp32) of s cut pieces per head,
-    s = min(chunk bound / 4, 1024 / H); other paths need none."""
+    states (Dk x Dv fp32) and decay products (Dk fp32) of s cut pieces per head.
+    Only segments over 8192 tokens are cut, into runs of about 64 chunks, so
+    with c = N // 8193 such segments at most, s = (N + 63 c) // 4096 + 1 (0
+    when c = 0); other paths need none."""
     size = lib.pkv_chunk_kda_varlen_workspace_size
 
     def expect(N, H, Dk, Dv, S):
-        s = min((N + 63 * S) // 64 // 4, 1024 // H)
+        c = N // 8193
+        s = 0 if c == 0 else (N + 63 * c) // 4096 + 1
         up = lambda x: (x + 255) // 256 * 256
         table = (64 + 8 * (S + s) + 4 * s) * 4
         return up(table) + up(s * H * Dk * Dv * 4) + up(s * H * Dk * 4)
 
     for N, H, Dk, Dv, S in [(65536, 32, 128, 128, 256), (131072, 32, 128, 128, 8),
                             (32768, 32, 64, 64, 1024), (65536, 32, 128, 128, 1),
-                            (100, 2, 64, 128, 3), (8192, 16, 128, 128, 128), (1 << 20, 1, 64, 64, 1)]:
+                            (100, 2, 64, 128, 3), (8192, 16, 128, 128, 128), (8193, 16, 128, 128, 128),
+                            (1 << 20, 1, 64, 64, 1)]:
         assert size(N, H, Dk, Dv, S, 0) == expect(N, H, Dk, Dv, S), (N, H, S)
-    # the cut-piece budget: at most 1024 + H run-heads of states (64 MiB at D = 128)
-    assert size(1 << 24, 32, 128, 128, 4, 0) < 65 * 2 ** 20
+    # the saved pieces take about 1/16 of one [N, H, Dk] bf16 tensor at Dv = 128
+    N = 1 << 24
+    assert size(N, 32, 128, 128, 4, 0) < N * 32 * 128 * 2 / 15
     assert size(512, 2, 32, 32, 16, 1) == 0              # fp32 token-serial path
     assert size(512, 2, 32, 32, 16, 0) == 0              # Dk = 32: token-serial path
     # no workspace, too little, or misaligned: refused before any launch

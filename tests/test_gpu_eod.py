@@ -1,5 +1,5 @@
 """GPU parity of pkv_eod_to_segment_ids against the oracle: bit-exact segment
-ids, positions and loss ids (RFC-0026, section 6)."""
+ids, positions and loss ids (RFC-0025, Design section 6)."""
 
 import numpy as np
 import pytest

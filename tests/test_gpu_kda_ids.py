@@ -1,6 +1,6 @@
 """GPU parity of pkv_chunk_kda_segment_ids (RFC-0026 section 3.1.1's [B, T]
-contract) against the oracle, and against the cu_seqlens entry on the same
-documents."""
+contract, with section 3.4's padding id 0 ignored) against the oracle, and
+against the cu_seqlens entry on the same documents."""
 
 import numpy as np
 import pytest
@@ -69,19 +69,54 @@ def test_small_shapes(dtype, Dk, Dv):
 
 
 def test_long_row_cut_into_runs_with_initial_state():
-    """A 6000-token row with two segments: the long one is cut into runs and
-    folds the row's initial state in through the composition."""
+    """A 12000-token row with two segments: the long one (172 chunks) is cut
+    into 3 runs and folds the row's initial state in through the composition."""
     rng = np.random.default_rng(3)
-    B, T, H, D = 1, 6000, 2, 64
+    B, T, H, D = 1, 12000, 2, 64
     ts = _inputs(rng, B, T, H, D, D, torch.bfloat16, gl=0.00001, gh=0.0005)
     seg = np.ones((B, T), dtype=np.int32)
-    seg[0, 5500:] = 2
+    seg[0, 11000:] = 2
     S0 = rng.standard_normal((B, H, D, D)) * 2.0
     o, fs = _run(ts, seg, S0)
     ro, rfs = oracle.chunk_kda_segment_ids(*[f64(t) for t in ts], seg, initial_state=S0)
     check_close(f64(o), ro, "bf16", "o")
     check_close(f64(fs), rfs, "bf16", "final state")
-    check_close(f64(o)[0, 4000:5500], ro[0, 4000:5500], "bf16", "last run of the first segment")
+    check_close(f64(o)[0, 7296:11000], ro[0, 7296:11000], "bf16", "last run of the first segment")
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [(torch.float32, 64, 64), (torch.bfloat16, 64, 64),
+                                         (torch.bfloat16, 128, 128), (torch.bfloat16, 128, 64)])
+def test_padding_is_ignored(dtype, Dk, Dv):
+    """RFC-0026 section 3.4: rows padded with id 0 (to a multiple of 64, as the
+    module does, at the front, everywhere, and between two runs of one id),
+    with non-zero initial states. Padding outputs are exactly 0; a row's final
+    state is the state after its last real token (a row of padding only keeps
+    its initial state bit for bit); the outputs of a padded row equal those of
+    the same row with the trailing padding cut off."""
+    rng = np.random.default_rng(Dk + Dv + (dtype == torch.float32))
+    B, T, H = 4, 640, 2
+    ts = _inputs(rng, B, T, H, Dk, Dv, dtype)
+    seg = np.zeros((B, T), dtype=np.int32)
+    seg[0, :250] = 1
+    seg[0, 250:603] = 2                     # 37 trailing padding positions
+    seg[1, 100:400] = 1                     # leading and trailing padding
+    seg[1, 400:] = 2
+    seg[3, :200] = 4
+    seg[3, 300:500] = 4                     # the same id on both sides of padding
+    S0 = rng.standard_normal((B, H, Dk, Dv)) * 0.5
+    print(f"padding dtype {dtype} Dk {Dk} Dv {Dv}", flush=True)
+    o, fs = _run(ts, seg, S0, scale=0.7)
+    ro, rfs = oracle.chunk_kda_segment_ids(*[f64(t) for t in ts], seg, scale=0.7, initial_state=S0)
+    dt = "f32" if dtype == torch.float32 else "bf16"
+    check_close(f64(o), ro, dt, "o")
+    for b in range(B):
+        check_close(f64(fs[b]), rfs[b], dt, f"final state of row {b}")
+    pad = torch.from_numpy(seg == 0).to(device())
+    assert torch.count_nonzero(o[pad]).item() == 0
+    assert torch.equal(fs[2], torch.from_numpy(S0[2]).float().to(device()))
+    # row 0 without its trailing padding: the same bits
+    o0, f0 = _run([t[:1, :603].contiguous() for t in ts], seg[:1, :603].copy(), S0[:1], scale=0.7)
+    assert torch.equal(o0[0], o[0, :603]) and torch.equal(f0[0], fs[0])
 
 
 def test_every_token_its_own_segment():

@@ -1,5 +1,6 @@
-"""Pins of the EOD -> segment ids / positions / loss ids oracle (RFC-0026,
-section 6, data pipeline alignment)."""
+"""Pins of the EOD -> segment ids / positions / loss ids oracle (RFC-0025
+"Support attention varlen and align loss", Design section 6, data pipeline
+alignment)."""
 
 import numpy as np
 import pytest
