@@ -216,6 +216,33 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_chunk_kda_varlen for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Arguments, results and errors are those of pkv_chunk_kda_varlen
+ * without the workspace: the chunk path's scratch (work plan, queue counters,
+ * states of the pieces of cut segments) lives in a fixed array of
+ * PKV_NOALLOC_SCRATCH_BYTES in the library's device memory, one copy per GPU
+ * the library runs on, held until the process ends. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up that device's copy of the array.
+ * Every call on one GPU shares the array, so calls that overlap on one GPU
+ * (other streams, other threads) race: order them. The array needs no
+ * clearing between calls (every call rewrites what it reads).
+ * Errors: as pkv_chunk_kda_varlen; PKV_ERR_WORKSPACE when
+ * pkv_chunk_kda_varlen_workspace_size() for these sizes exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES (e.g. N = 131072, H = 32, Dk = Dv = 128 fits;
+ * the limit is reached at about N = 190000 tokens for that shape);
+ * PKV_ERR_HIP if the array's address cannot be found.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+pkv_status pkv_chunk_kda_varlen_noalloc(const void* q, const void* k, const void* v,
+                                        const void* g, const void* beta,
+                                        const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
+                                        int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                        int32_t dtype, const float* initial_state, void* o,
+                                        float* final_state, int32_t* flags, void* stream);
+
+/*
  * Packed KDA straight from [B, T] segment ids (RFC-0026 section 3.1.1's
  * kernel contract), with no cu_seqlens round trip and no phantom slots.
  *
@@ -305,7 +332,7 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
 const char* pkv_status_string(int32_t status);
 
 /* ABI version of this header (bumped on any signature change). */
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 int32_t pkv_abi_version(void);
 
 #ifdef __cplusplus

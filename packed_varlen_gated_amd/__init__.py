@@ -58,6 +58,9 @@ def _load():
     lib.pkv_chunk_kda_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32,
                                          vp, vp, vp, vp, vp, sz, vp]
     lib.pkv_chunk_kda_varlen.restype = i32
+    lib.pkv_chunk_kda_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32,
+                                                 vp, vp, vp, vp, vp]
+    lib.pkv_chunk_kda_varlen_noalloc.restype = i32
     lib.pkv_chunk_kda_segment_ids_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32]
     lib.pkv_chunk_kda_segment_ids_workspace_size.restype = sz
     lib.pkv_chunk_kda_segment_ids.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, i32,

@@ -92,12 +92,16 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
   return pkv::kda_chunk_workspace_bytes(N, H, Dk, Dv, dtype, max_segs);
 }
 
-pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
-                                const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
-                                int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                int32_t dtype, const float* initial_state, void* o,
-                                float* final_state, int32_t* flags, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by pkv_chunk_kda_varlen and pkv_chunk_kda_varlen_noalloc
+// (everything but the workspace); max_segs is set to 1 when cu_seqlens is NULL.
+pkv_status check_kda_args(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const int32_t* cu_seqlens, int32_t& max_segs,
+                          int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                          const float* initial_state, const void* o, const float* final_state) {
   if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
       o == nullptr)
     return PKV_ERR_INVALID_ARGUMENT;
@@ -109,7 +113,7 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
   }
   if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv))
     return PKV_ERR_UNSUPPORTED;
-  for (const void* p : {q, k, v, g, static_cast<const void*>(o)})
+  for (const void* p : {q, k, v, g, o})
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARGUMENT;
   if (reinterpret_cast<uintptr_t>(beta) % elem_size(dtype) != 0 ||
       reinterpret_cast<uintptr_t>(final_state) % 16 != 0 ||
@@ -126,6 +130,22 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
       overlaps(o, o_bytes, v, N * H * Dv * es) || overlaps(o, o_bytes, g, N * H * Dk * es) ||
       overlaps(o, o_bytes, beta, N * H * es))
     return PKV_ERR_INVALID_ARGUMENT;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
+                                int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                int32_t dtype, const float* initial_state, void* o,
+                                float* final_state, int32_t* flags, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  const pkv_status st = check_kda_args(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv, dtype,
+                                       initial_state, o, final_state);
+  if (st != PKV_OK) return st;
   const size_t need = pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
                    reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
@@ -134,6 +154,27 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
     return from_hip(pkv::launch_kda_chunk(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
                                           scale, initial_state, o, final_state, flags, workspace,
                                           static_cast<hipStream_t>(stream)));
+  return from_hip(pkv::launch_kda_serial(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
+                                         scale, dtype, initial_state, o, final_state, flags,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_chunk_kda_varlen_noalloc(const void* q, const void* k, const void* v,
+                                        const void* g, const void* beta,
+                                        const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
+                                        int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                        int32_t dtype, const float* initial_state, void* o,
+                                        float* final_state, int32_t* flags, void* stream) {
+  const pkv_status st = check_kda_args(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv, dtype,
+                                       initial_state, o, final_state);
+  if (st != PKV_OK) return st;
+  const size_t need = pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype);
+  if (need > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_WORKSPACE;
+  static_assert(PKV_NOALLOC_SCRATCH_BYTES == pkv::kNoAllocScratchBytes, "scratch size");
+  if (pkv::kda_chunk_supported(Dk, Dv, dtype))
+    return from_hip(pkv::launch_kda_chunk_noalloc(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk,
+                                                  Dv, scale, initial_state, o, final_state, flags,
+                                                  static_cast<hipStream_t>(stream)));
   return from_hip(pkv::launch_kda_serial(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
                                          scale, dtype, initial_state, o, final_state, flags,
                                          static_cast<hipStream_t>(stream)));

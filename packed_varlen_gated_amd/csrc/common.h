@@ -74,6 +74,16 @@ hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const v
                             const float* initial_state, void* o, float* final_state,
                             int32_t* flags, void* workspace, hipStream_t stream);
 
+// The same with the workspace in the library's fixed per-GPU scratch array of
+// kNoAllocScratchBytes (for callers that cannot allocate); the caller has
+// checked that the chunk path's workspace size fits.
+constexpr size_t kNoAllocScratchBytes = size_t(96) << 20;
+hipError_t launch_kda_chunk_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                    const void* beta, const int32_t* cu, int32_t max_segs,
+                                    int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                    const float* initial_state, void* o, float* final_state,
+                                    int32_t* flags, hipStream_t stream);
+
 // Reverse pass of the recurrence, chunked on MFMA (bf16, Dk and Dv in {64, 128}):
 // the work plan and the bf16 states S and Lambda of every chunk in the workspace.
 bool kda_chunk_bwd_supported(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,

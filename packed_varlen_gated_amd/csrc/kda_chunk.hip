@@ -56,6 +56,8 @@
 
 #include "common.h"
 
+#include <mutex>
+
 namespace pkv {
 namespace {
 
@@ -1328,6 +1330,52 @@ hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const v
   if (Dk == 64 && Dv == 128)
     return launch_dims<64, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- no allocation
+// Scratch of pkv_chunk_kda_varlen_noalloc: the workspace of the chunk path
+// (work plan, queue counters, states and decay products of cut pieces) in a
+// fixed array of the library's device memory. Each GPU the library runs on
+// holds its own copy until the process ends; every call on that GPU uses it,
+// so calls that overlap on one GPU race. Nothing in it needs clearing: the
+// plan kernel writes the plan and resets the queue counters at the start of
+// every call, and each piece's state is written before it is read.
+namespace {
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// The device address of this GPU's copy of the array, looked up once per
+// device with the device current. In host code the array's name is only a
+// host-side stand-in, so kernels get this pointer, never the name.
+hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_kda_chunk_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                    const void* beta, const int32_t* cu, int32_t max_segs,
+                                    int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                    const float* initial_state, void* o, float* final_state,
+                                    int32_t* flags, hipStream_t stream) {
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_kda_chunk(q, k, v, g, beta, cu, max_segs, N, H, Dk, Dv, scale, initial_state, o,
+                          final_state, flags, ws, stream);
 }
 
 }  // namespace pkv

@@ -29,13 +29,13 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
     for code, name in [(0, b"PKV_OK"), (1, b"PKV_ERR_INVALID_ARGUMENT"), (2, b"PKV_ERR_UNSUPPORTED"),
                        (3, b"PKV_ERR_WORKSPACE"), (4, b"PKV_ERR_HIP"), (99, b"PKV_ERR_UNKNOWN")]:
         assert lib.pkv_status_string(code) == name
