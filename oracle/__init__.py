@@ -17,7 +17,9 @@ Sources (the pages; cited by title and section):
   (cu_seqlens, doc(s), block-diagonal mask).
 * RFC-0025, Design section 6 (data pipeline alignment: EOD segmentation,
   positions, loss mask).
-* RFC-0026, section 3.3 (the wrapper's ``initial_state``), section 3.1.1's
+* RFC-0026, section 3.3 (the wrapper's ``initial_state`` and
+  ``use_qk_l2norm_in_kernel``; the norm's place in the module is RFC-0025
+  Design section 5), section 3.1.1's
   [B, T] ``segment_ids`` contract (reset where the id changes or a row starts)
   and section 3.4 (padding id 0, which the kernel ignores).
 
@@ -35,6 +37,12 @@ Functions and their pin status (every function is pinned; see tests/):
                                     segments, gate injection, invariants;
                                     initial states: decayed closed form,
                                     split-and-resume identity
+``l2_normalize`` (the
+``use_qk_l2norm`` option of the
+two recurrences above)              pinned: a hand-computed single token,
+                                    invariance to positive per-(token, head)
+                                    scales of q and k, unit-norm inputs
+                                    unchanged, v not normalised
 ``chunk_kda_varlen_backward``       pinned: central finite differences of a
                                     random linear loss for every input
                                     (q, k, v, g, beta, initial state)
@@ -51,7 +59,7 @@ Functions and their pin status (every function is pinned; see tests/):
 
 from .cu_seqlens import segment_ids_to_cu_seqlens, token_segment, FLAG_OVERFLOW, FLAG_LEADING_PAD
 from .short_conv import short_conv_segmask
-from .kda import chunk_kda_varlen, chunk_kda_segment_ids, chunk_kda_varlen_backward
+from .kda import chunk_kda_varlen, chunk_kda_segment_ids, chunk_kda_varlen_backward, l2_normalize
 from .eod import eod_to_segment_ids
 
 __all__ = [
@@ -61,6 +69,7 @@ __all__ = [
     "chunk_kda_varlen",
     "chunk_kda_segment_ids",
     "chunk_kda_varlen_backward",
+    "l2_normalize",
     "eod_to_segment_ids",
     "FLAG_OVERFLOW",
     "FLAG_LEADING_PAD",

@@ -25,6 +25,21 @@ oracle is the plain definition: the token-by-token recurrence in float64.
 
 import numpy as np
 
+# Added to the squared norm so a zero row stays finite (the pages give no value).
+L2NORM_EPS = 1e-6
+
+
+def l2_normalize(x):
+    """x / sqrt(sum over the last (head) axis of x^2 + L2NORM_EPS), per row.
+
+    RFC-0026 section 3.3's kernel wrappers carry ``use_qk_l2norm_in_kernel``:
+    the L2 normalisation of q and k over the head dimension, which RFC-0025
+    Design section 5 places between the short conv and the kernel, is then done
+    by the kernel itself.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2NORM_EPS)
+
 
 def _as_thd(a, name, ndim):
     a = np.asarray(a, dtype=np.float64)
@@ -35,15 +50,19 @@ def _as_thd(a, name, ndim):
     return a
 
 
-def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None):
+def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state=None,
+                     use_qk_l2norm=False):
     """Return ``(o [N, H, Dv], final_state [max_segs, H, Dk, Dv])`` in float64.
 
     q, k, g: [N, H, Dk] (a leading unit batch axis is accepted);
     v: [N, H, Dv]; beta: [N, H]; cu_seqlens: int [max_segs + 1] or None;
-    initial_state: [max_segs, H, Dk, Dv] or None (zeros).
+    initial_state: [max_segs, H, Dk, Dv] or None (zeros); use_qk_l2norm: q and
+    k are first L2-normalised per (token, head) (``l2_normalize``).
     """
     q = _as_thd(q, "q", 3)
     k = _as_thd(k, "k", 3)
+    if use_qk_l2norm:
+        q, k = l2_normalize(q), l2_normalize(k)
     v = _as_thd(v, "v", 3)
     g = _as_thd(g, "g", 3)
     beta = _as_thd(beta, "beta", 2)
@@ -80,7 +99,8 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, initial_state
     return o, final_state
 
 
-def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, initial_state=None):
+def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, initial_state=None,
+                          use_qk_l2norm=False):
     """The [B, T] segment_ids contract of RFC-0026 section 3.1.1, row by row.
 
     q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H]; segment_ids: int
@@ -93,10 +113,13 @@ def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, initial_stat
     position, which starts the row's first segment from initial_state[b]
     (section 3.3's per-row shape). Returns (o [B, T, H, Dv], final_state
     [B, H, Dk, Dv]): the state after each row's last real position
-    (initial_state[b], or zero, for a row of padding only).
+    (initial_state[b], or zero, for a row of padding only). use_qk_l2norm: q
+    and k are first L2-normalised per (token, head) (``l2_normalize``).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
+    if use_qk_l2norm:
+        q, k = l2_normalize(q), l2_normalize(k)
     v = np.asarray(v, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     beta = np.asarray(beta, dtype=np.float64)

@@ -364,3 +364,64 @@ def test_backward_gate_gradient_identity():
         db = q[a:e] * dq[a:e] - k[a:e] * dk[a:e]
         want = np.cumsum(db[::-1], axis=0)[::-1] + np.einsum("hde,hde->hd", dF[i], fs[i])[None]
         np.testing.assert_allclose(dg[a:e], want, rtol=1e-10, atol=1e-10)
+
+
+def test_qk_l2norm_hand_case():
+    """One token, Dk = 2, Dv = 1, beta = 1, v = 1: q = (3, 4) and k = (0, 2)
+    normalise to (0.6, 0.8) and (0, 1), so S = (0, 1)^T and o = 0.8; the
+    squared norms 25 and 4 each carry eps = 1e-6."""
+    q = np.array([[[3.0, 4.0]]])
+    k = np.array([[[0.0, 2.0]]])
+    o, fs = oracle.chunk_kda_varlen(q, k, np.ones((1, 1, 1)), np.zeros((1, 1, 2)), np.ones((1, 1)), None,
+                                    use_qk_l2norm=True)
+    expect = 0.8 * 5 / math.sqrt(25 + 1e-6) * 2 / math.sqrt(4 + 1e-6)
+    assert o[0, 0, 0] == pytest.approx(expect, rel=1e-15)
+    assert fs[0, 0, :, 0] == pytest.approx([0.0, 2 / math.sqrt(4 + 1e-6)], rel=1e-15)
+
+
+def test_qk_l2norm_scale_invariance_and_unit_rows():
+    """The norm is taken per (token, head) over the head dimension: positive
+    per-(token, head) scales of q and k leave the result unchanged (to the
+    eps term); already unit-norm q and k give the plain recurrence (to the
+    same term); v is not normalised, so o scales with it."""
+    rng = np.random.default_rng(61)
+    N, H, Dk, Dv = 30, 3, 5, 4
+    q, k, v, g, beta = _rand_inputs(rng, N, H, Dk, Dv)
+    q *= 3.0
+    k *= 2.0
+    cu = np.array([0, 11, 11, 30])
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, cu, scale=0.7, use_qk_l2norm=True)
+    cq = rng.uniform(0.5, 3.0, (N, H, 1))
+    ck = rng.uniform(0.5, 3.0, (N, H, 1))
+    o2, fs2 = oracle.chunk_kda_varlen(q * cq, k * ck, v, g, beta, cu, scale=0.7, use_qk_l2norm=True)
+    # eps / |x|^2 is at most about 1e-6 here: allow 1e-5 of each tensor's largest value
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-5 * np.abs(o).max())
+    np.testing.assert_allclose(fs2, fs, rtol=0, atol=1e-5 * np.abs(fs).max())
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o3, fs3 = oracle.chunk_kda_varlen(qn, kn, v, g, beta, cu, scale=0.7)
+    np.testing.assert_allclose(o3, o, rtol=0, atol=1e-5 * np.abs(o).max())
+    np.testing.assert_allclose(fs3, fs, rtol=0, atol=1e-5 * np.abs(fs).max())
+    o4, _ = oracle.chunk_kda_varlen(q, k, 2.5 * v, g, beta, cu, scale=0.7, use_qk_l2norm=True)
+    np.testing.assert_allclose(o4, 2.5 * o, rtol=1e-12, atol=1e-12)
+    # a normalisation over the wrong axis would not be invariant to these scales
+    on, _ = oracle.chunk_kda_varlen(q, k, v, g, beta, cu, scale=0.7)
+    assert np.linalg.norm(on - o) > 0.1 * np.linalg.norm(o)
+
+
+def test_qk_l2norm_segment_ids_contract():
+    """The [B, T] contract with the option, on scaled q and k, equals the
+    contract without it on unit-norm q and k (to the eps term); padding
+    positions stay 0."""
+    rng = np.random.default_rng(62)
+    B, T, H, Dk, Dv = 2, 20, 2, 3, 2
+    q, k, v, g, beta = [a.reshape((B, T) + a.shape[1:]) for a in _rand_inputs(rng, B * T, H, Dk, Dv)]
+    seg = np.array([[1] * 8 + [0] * 2 + [2] * 10, [3] * 20])
+    q, k = 3 * q, 3 * k
+    o, fs = oracle.chunk_kda_segment_ids(4 * q, 2 * k, v, g, beta, seg, use_qk_l2norm=True)
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o2, fs2 = oracle.chunk_kda_segment_ids(qn, kn, v, g, beta, seg)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-5 * np.abs(o).max())
+    np.testing.assert_allclose(fs, fs2, rtol=0, atol=1e-5 * np.abs(fs).max())
+    assert np.all(o[:, seg[0] == 0][0] == 0)
