@@ -82,6 +82,14 @@ typedef enum {
                                       decreasing pair or cu[i] > N; the outputs
                                       of the offending segments are undefined */
 
+/* Bits of the `options` argument of the recurrence's entry points. */
+#define PKV_OPT_QK_L2NORM 1        /* RFC-0026 section 3.3's use_qk_l2norm_in_kernel:
+                                      q and k are L2-normalised per (token, head)
+                                      over Dk before the recurrence,
+                                      x / sqrt(sum_d x_d^2 + 1e-6) in fp32 (the
+                                      norm RFC-0025 Design section 5 places
+                                      between the short conv and the kernel) */
+
 /*
  * segment_ids -> cu_seqlens (FLA convention, fixed length max_segs + 1).
  *
@@ -186,6 +194,8 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
  * cu_seqlens  int32 [max_segs + 1] or NULL. NULL means one segment [0, N) and
  *             max_segs is taken as 1. Expected: cu[0] = 0, non-decreasing,
  *             cu[max_segs] <= N; a violation sets PKV_FLAG_BAD_CU_SEQLENS.
+ * options     0 or PKV_OPT_QK_L2NORM (q and k normalised inside the call; the
+ *             caller's tensors are not modified).
  * initial_state float32 [max_segs, H, Dk, Dv] or NULL (RFC-0026 section 3.3's
  *             wrapper argument, one state per segment slot); must not overlap
  *             final_state.
@@ -205,14 +215,15 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
  * factorisation bounds exponents per 16-token sub-chunk).
  * Errors: PKV_ERR_INVALID_ARGUMENT for NULL tensors, N < 1, N > INT32_MAX,
  * H < 1, max_segs < 1 (with cu_seqlens), max_segs * H > 2^22, a misaligned
- * tensor or o aliasing an input; PKV_ERR_UNSUPPORTED for other Dk/Dv or dtype; PKV_ERR_WORKSPACE
- * if the workspace is too small or not 16-byte aligned.
+ * tensor or o aliasing an input; PKV_ERR_UNSUPPORTED for other Dk/Dv, dtype or
+ * an unknown options bit; PKV_ERR_WORKSPACE if the workspace is too small or
+ * not 16-byte aligned.
  */
 pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
                                 int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                int32_t dtype, const float* initial_state, void* o,
-                                float* final_state, int32_t* flags, void* workspace,
+                                int32_t dtype, int32_t options, const float* initial_state,
+                                void* o, float* final_state, int32_t* flags, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
 /*
@@ -239,8 +250,8 @@ pkv_status pkv_chunk_kda_varlen_noalloc(const void* q, const void* k, const void
                                         const void* g, const void* beta,
                                         const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
                                         int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                        int32_t dtype, const float* initial_state, void* o,
-                                        float* final_state, int32_t* flags, void* stream);
+                                        int32_t dtype, int32_t options, const float* initial_state,
+                                        void* o, float* final_state, int32_t* flags, void* stream);
 
 /*
  * Packed KDA straight from [B, T] segment ids (RFC-0026 section 3.1.1's
@@ -258,7 +269,8 @@ pkv_status pkv_chunk_kda_varlen_noalloc(const void* q, const void* k, const void
  * state.
  *
  * q, k, g     [B, T, H, Dk]; v [B, T, H, Dv]; beta [B, T, H]; o [B, T, H, Dv]
- *             (one dtype); segment_ids int32 [B, T].
+ *             (one dtype); segment_ids int32 [B, T]; options as for
+ *             pkv_chunk_kda_varlen.
  * initial_state, final_state  float32 [B, H, Dk, Dv] or NULL; must not overlap.
  * workspace   at least pkv_chunk_kda_segment_ids_workspace_size() bytes,
  *             16-byte aligned; scratch, as for pkv_chunk_kda_varlen (the
@@ -271,8 +283,8 @@ size_t pkv_chunk_kda_segment_ids_workspace_size(int64_t B, int64_t T, int32_t H,
 pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v, const void* g,
                                      const void* beta, const int32_t* segment_ids, int64_t B,
                                      int64_t T, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                     int32_t dtype, const float* initial_state, void* o,
-                                     float* final_state, int32_t* flags, void* workspace,
+                                     int32_t dtype, int32_t options, const float* initial_state,
+                                     void* o, float* final_state, int32_t* flags, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
 /*
@@ -332,7 +344,7 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
 const char* pkv_status_string(int32_t status);
 
 /* ABI version of this header (bumped on any signature change). */
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 int32_t pkv_abi_version(void);
 
 #ifdef __cplusplus

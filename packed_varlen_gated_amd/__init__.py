@@ -29,6 +29,7 @@ PKV_F32 = 1
 FLAG_OVERFLOW = 1
 FLAG_LEADING_PAD = 2
 FLAG_BAD_CU_SEQLENS = 4
+OPT_QK_L2NORM = 1
 
 _lib = None
 
@@ -55,16 +56,16 @@ def _load():
     lib.pkv_short_conv_segmask.restype = i32
     lib.pkv_chunk_kda_varlen_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
     lib.pkv_chunk_kda_varlen_workspace_size.restype = sz
-    lib.pkv_chunk_kda_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32,
+    lib.pkv_chunk_kda_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32, i32,
                                          vp, vp, vp, vp, vp, sz, vp]
     lib.pkv_chunk_kda_varlen.restype = i32
     lib.pkv_chunk_kda_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32,
-                                                 vp, vp, vp, vp, vp]
+                                                 i32, vp, vp, vp, vp, vp]
     lib.pkv_chunk_kda_varlen_noalloc.restype = i32
     lib.pkv_chunk_kda_segment_ids_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32]
     lib.pkv_chunk_kda_segment_ids_workspace_size.restype = sz
     lib.pkv_chunk_kda_segment_ids.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, i32,
-                                              vp, vp, vp, vp, vp, sz, vp]
+                                              i32, vp, vp, vp, vp, vp, sz, vp]
     lib.pkv_chunk_kda_segment_ids.restype = i32
     lib.pkv_chunk_kda_varlen_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                                   f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -208,12 +209,14 @@ def chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype):
 
 
 def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_state=True,
-                     flags=None, out=None, workspace=None, initial_state=None):
+                     flags=None, out=None, workspace=None, initial_state=None,
+                     use_qk_l2norm_in_kernel=False):
     """Packed KDA forward.
 
     q, k, g: [1, N, H, Dk] (or [B, T, H, Dk], taken as the flattened [1, B*T, H, Dk]);
     v: [..., Dv]; beta: [1, N, H]; cu_seqlens: int32 [max_segs + 1] or None (one segment).
     initial_state: fp32 [max_segs, H, Dk, Dv] or None (each segment starts from its slot's state).
+    use_qk_l2norm_in_kernel: q and k are L2-normalised per (token, head) inside the call.
     Returns (o [same leading shape as q, Dv], final_state fp32 [max_segs, H, Dk, Dv] or None).
     """
     lib = _load()
@@ -247,7 +250,8 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_
     need = int(lib.pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, code))
     workspace, ws_bytes = _workspace(workspace, need, dev)
     _check(lib.pkv_chunk_kda_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                    max_segs, N, H, Dk, Dv, float(scale), code, _ptr(initial_state),
+                                    max_segs, N, H, Dk, Dv, float(scale), code,
+                                    OPT_QK_L2NORM if use_qk_l2norm_in_kernel else 0, _ptr(initial_state),
                                     _ptr(o), _ptr(fs),
                                     _ptr(flags), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, fs
@@ -258,7 +262,8 @@ def chunk_kda_segment_ids_workspace_size(B, T, H, Dk, Dv, dtype):
 
 
 def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, output_final_state=True,
-                          initial_state=None, flags=None, out=None, workspace=None):
+                          initial_state=None, flags=None, out=None, workspace=None,
+                          use_qk_l2norm_in_kernel=False):
     """Packed KDA from [B, T] segment ids (reset where the id changes and at each row start).
 
     q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H]; segment_ids: int32 [B, T];
@@ -291,7 +296,8 @@ def chunk_kda_segment_ids(q, k, v, g, beta, segment_ids, scale=1.0, output_final
     need = int(lib.pkv_chunk_kda_segment_ids_workspace_size(B, T, H, Dk, Dv, code))
     workspace, ws_bytes = _workspace(workspace, need, dev)
     _check(lib.pkv_chunk_kda_segment_ids(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(segment_ids),
-                                         B, T, H, Dk, Dv, float(scale), code, _ptr(initial_state), _ptr(o),
+                                         B, T, H, Dk, Dv, float(scale), code,
+                                         OPT_QK_L2NORM if use_qk_l2norm_in_kernel else 0, _ptr(initial_state), _ptr(o),
                                          _ptr(fs), _ptr(flags), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, fs
 

@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int64_t kInt32Max = 2147483647;
+constexpr int32_t kKnownOptions = PKV_OPT_QK_L2NORM;
 
 bool supported_head_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
 bool known_dtype(int32_t dt) { return dt == PKV_BF16 || dt == PKV_F32; }
@@ -101,7 +102,8 @@ namespace {
 pkv_status check_kda_args(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, const int32_t* cu_seqlens, int32_t& max_segs,
                           int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
-                          const float* initial_state, const void* o, const float* final_state) {
+                          int32_t options, const float* initial_state, const void* o,
+                          const float* final_state) {
   if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
       o == nullptr)
     return PKV_ERR_INVALID_ARGUMENT;
@@ -111,7 +113,8 @@ pkv_status check_kda_args(const void* q, const void* k, const void* v, const voi
   } else if (max_segs < 1 || max_segs >= kInt32Max) {
     return PKV_ERR_INVALID_ARGUMENT;
   }
-  if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv))
+  if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv) ||
+      (options & ~kKnownOptions) != 0)
     return PKV_ERR_UNSUPPORTED;
   for (const void* p : {q, k, v, g, o})
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARGUMENT;
@@ -140,11 +143,12 @@ extern "C" {
 pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
                                 int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                int32_t dtype, const float* initial_state, void* o,
-                                float* final_state, int32_t* flags, void* workspace,
+                                int32_t dtype, int32_t options, const float* initial_state,
+                                void* o, float* final_state, int32_t* flags, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   const pkv_status st = check_kda_args(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv, dtype,
-                                       initial_state, o, final_state);
+                                       options, initial_state, o, final_state);
+  const bool l2 = (options & PKV_OPT_QK_L2NORM) != 0;
   if (st != PKV_OK) return st;
   const size_t need = pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
@@ -152,10 +156,10 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
     return PKV_ERR_WORKSPACE;
   if (pkv::kda_chunk_supported(Dk, Dv, dtype))
     return from_hip(pkv::launch_kda_chunk(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
-                                          scale, initial_state, o, final_state, flags, workspace,
-                                          static_cast<hipStream_t>(stream)));
+                                          scale, l2, initial_state, o, final_state, flags,
+                                          workspace, static_cast<hipStream_t>(stream)));
   return from_hip(pkv::launch_kda_serial(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
-                                         scale, dtype, initial_state, o, final_state, flags,
+                                         scale, dtype, l2, initial_state, o, final_state, flags,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -163,20 +167,22 @@ pkv_status pkv_chunk_kda_varlen_noalloc(const void* q, const void* k, const void
                                         const void* g, const void* beta,
                                         const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
                                         int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                        int32_t dtype, const float* initial_state, void* o,
-                                        float* final_state, int32_t* flags, void* stream) {
+                                        int32_t dtype, int32_t options, const float* initial_state,
+                                        void* o, float* final_state, int32_t* flags,
+                                        void* stream) {
   const pkv_status st = check_kda_args(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv, dtype,
-                                       initial_state, o, final_state);
+                                       options, initial_state, o, final_state);
+  const bool l2 = (options & PKV_OPT_QK_L2NORM) != 0;
   if (st != PKV_OK) return st;
   const size_t need = pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype);
   if (need > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_WORKSPACE;
   static_assert(PKV_NOALLOC_SCRATCH_BYTES == pkv::kNoAllocScratchBytes, "scratch size");
   if (pkv::kda_chunk_supported(Dk, Dv, dtype))
     return from_hip(pkv::launch_kda_chunk_noalloc(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk,
-                                                  Dv, scale, initial_state, o, final_state, flags,
-                                                  static_cast<hipStream_t>(stream)));
+                                                  Dv, scale, l2, initial_state, o, final_state,
+                                                  flags, static_cast<hipStream_t>(stream)));
   return from_hip(pkv::launch_kda_serial(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv,
-                                         scale, dtype, initial_state, o, final_state, flags,
+                                         scale, dtype, l2, initial_state, o, final_state, flags,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -266,8 +272,8 @@ size_t pkv_chunk_kda_segment_ids_workspace_size(int64_t B, int64_t T, int32_t H,
 pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v, const void* g,
                                      const void* beta, const int32_t* segment_ids, int64_t B,
                                      int64_t T, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                     int32_t dtype, const float* initial_state, void* o,
-                                     float* final_state, int32_t* flags, void* workspace,
+                                     int32_t dtype, int32_t options, const float* initial_state,
+                                     void* o, float* final_state, int32_t* flags, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
       o == nullptr || segment_ids == nullptr)
@@ -275,8 +281,10 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
   if (B < 1 || T < 1 || B > kInt32Max || T > kInt32Max || B * T > kInt32Max - 8192 || H < 1 ||
       H > 65536)
     return PKV_ERR_INVALID_ARGUMENT;
-  if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv))
+  if (!known_dtype(dtype) || !supported_head_dim(Dk) || !supported_head_dim(Dv) ||
+      (options & ~kKnownOptions) != 0)
     return PKV_ERR_UNSUPPORTED;
+  const bool l2 = (options & PKV_OPT_QK_L2NORM) != 0;
   if (B * H > (int64_t(1) << 22)) return PKV_ERR_INVALID_ARGUMENT;
   for (const void* p : {q, k, v, g, static_cast<const void*>(o)})
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARGUMENT;
@@ -301,10 +309,10 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
     return PKV_ERR_WORKSPACE;
   if (pkv::kda_chunk_supported(Dk, Dv, dtype))
     return from_hip(pkv::launch_kda_chunk_ids(q, k, v, g, beta, segment_ids, B, T, H, Dk, Dv,
-                                              scale, initial_state, o, final_state, flags,
+                                              scale, l2, initial_state, o, final_state, flags,
                                               workspace, static_cast<hipStream_t>(stream)));
   return from_hip(pkv::launch_kda_serial_ids(q, k, v, g, beta, segment_ids, B, T, H, Dk, Dv,
-                                             scale, dtype, initial_state, o, final_state,
+                                             scale, dtype, l2, initial_state, o, final_state,
                                              static_cast<hipStream_t>(stream)));
 }
 

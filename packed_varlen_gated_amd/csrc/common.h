@@ -40,11 +40,13 @@ hipError_t launch_short_conv(const void* x, const float* w, const int32_t* seg, 
                              int64_t B, int64_t T, int64_t F, int32_t Kc, int32_t dtype,
                              hipStream_t stream);
 
+// qk_l2norm (every recurrence launcher): q and k are first L2-normalised per
+// (token, head) over Dk.
 hipError_t launch_kda_serial(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                              int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
-                             const float* initial_state, void* o, float* final_state,
-                             int32_t* flags, hipStream_t stream);
+                             bool qk_l2norm, const float* initial_state, void* o,
+                             float* final_state, int32_t* flags, hipStream_t stream);
 
 bool kda_chunk_supported(int32_t Dk, int32_t Dv, int32_t dtype);
 
@@ -58,19 +60,19 @@ size_t kda_chunk_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, i
 size_t kda_chunk_ids_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype);
 hipError_t launch_kda_chunk_ids(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta, const int32_t* seg, int64_t B, int64_t T,
-                                int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                int32_t H, int32_t Dk, int32_t Dv, float scale, bool qk_l2norm,
                                 const float* initial_state, void* o, float* final_state,
                                 int32_t* flags, void* workspace, hipStream_t stream);
 // ... and on the token-serial path (one work-group per (row, head)).
 hipError_t launch_kda_serial_ids(const void* q, const void* k, const void* v, const void* g,
                                  const void* beta, const int32_t* seg, int64_t B, int64_t T,
                                  int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
-                                 const float* initial_state, void* o, float* final_state,
-                                 hipStream_t stream);
+                                 bool qk_l2norm, const float* initial_state, void* o,
+                                 float* final_state, hipStream_t stream);
 
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
-                            int32_t H, int32_t Dk, int32_t Dv, float scale,
+                            int32_t H, int32_t Dk, int32_t Dv, float scale, bool qk_l2norm,
                             const float* initial_state, void* o, float* final_state,
                             int32_t* flags, void* workspace, hipStream_t stream);
 
@@ -81,8 +83,8 @@ constexpr size_t kNoAllocScratchBytes = size_t(96) << 20;
 hipError_t launch_kda_chunk_noalloc(const void* q, const void* k, const void* v, const void* g,
                                     const void* beta, const int32_t* cu, int32_t max_segs,
                                     int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                    const float* initial_state, void* o, float* final_state,
-                                    int32_t* flags, hipStream_t stream);
+                                    bool qk_l2norm, const float* initial_state, void* o,
+                                    float* final_state, int32_t* flags, hipStream_t stream);
 
 // Reverse pass of the recurrence, chunked on MFMA (bf16, Dk and Dv in {64, 128}):
 // the work plan and the bf16 states S and Lambda of every chunk in the workspace.

@@ -143,6 +143,26 @@ struct alignas(2 * n) BfPack {
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The value of another lane of the same 16-lane row (DPP control kCtrl).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a row, the same bits in every lane (each step adds
+// two equal partial sums in either order): quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror (lane j of an 8-lane half takes lane 7 - j),
+// row_mirror (lane j of the row takes lane 15 - j).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+// Added to a squared norm before the reciprocal square root (the q/k L2
+// normalisation option), so a zero row stays finite.
+constexpr float kL2NormEps = 1e-6f;
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -268,7 +288,8 @@ __device__ __forceinline__ void wload(uint32_t (&w)[n], __amdgpu_buffer_rsrc_t r
 // results). kState = true: the state pass of a run that is not its segment's
 // last: S from zero over the run and the product of its decays, both to the
 // workspace (no outputs).
-template <int DK, int DV, bool kState>
+// kNorm: q and k are first L2-normalised per (token, head) over Dk.
+template <int DK, int DV, bool kState, bool kNorm>
 __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -444,6 +465,22 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // sub-chunk (the next half's factors are products of those). The state
   // pass has no q and folds k only.
   auto scan = [&](const Raw<PCPL, PVPL>& R, RawQK<PCPL>& X) {
+    // kNorm: 1 / sqrt(|x|^2 + eps) of each token's q and k; the 16 lanes of a
+    // row hold the token's Dk channels, PCPL each
+    float rq[4], rk[4];
+    if constexpr (kNorm) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int c = 0; c < PCPL; ++c) {
+          if constexpr (!kState) sq = fmaf(bf(X.q[i], c), bf(X.q[i], c), sq);
+          sk = fmaf(bf(X.k[i], c), bf(X.k[i], c), sk);
+        }
+        if constexpr (!kState) rq[i] = __builtin_amdgcn_rsqf(row_sum16(sq) + kL2NormEps);
+        rk[i] = __builtin_amdgcn_rsqf(row_sum16(sk) + kL2NormEps);
+      }
+    }
     float cs[4][PCPL], tot[PCPL];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
@@ -475,10 +512,18 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int c = 0; c < PCPL; c += 2) {
-        if constexpr (!kState)
-          X.q[i][c >> 1] = pk2(bf(X.q[i], c) * ex2(cs[i][c]), bf(X.q[i], c + 1) * ex2(cs[i][c + 1]));
-        X.k[i][c >> 1] = pk2(bf(X.k[i], c) * ex2(tot[c] - cs[i][c]),
-                             bf(X.k[i], c + 1) * ex2(tot[c + 1] - cs[i][c + 1]));
+        if constexpr (kNorm) {
+          if constexpr (!kState)
+            X.q[i][c >> 1] = pk2((bf(X.q[i], c) * rq[i]) * ex2(cs[i][c]),
+                                 (bf(X.q[i], c + 1) * rq[i]) * ex2(cs[i][c + 1]));
+          X.k[i][c >> 1] = pk2((bf(X.k[i], c) * rk[i]) * ex2(tot[c] - cs[i][c]),
+                               (bf(X.k[i], c + 1) * rk[i]) * ex2(tot[c + 1] - cs[i][c + 1]));
+        } else {
+          if constexpr (!kState)
+            X.q[i][c >> 1] = pk2(bf(X.q[i], c) * ex2(cs[i][c]), bf(X.q[i], c + 1) * ex2(cs[i][c + 1]));
+          X.k[i][c >> 1] = pk2(bf(X.k[i], c) * ex2(tot[c] - cs[i][c]),
+                               bf(X.k[i], c + 1) * ex2(tot[c + 1] - cs[i][c + 1]));
+        }
       }
     }
   };
@@ -1220,53 +1265,83 @@ int device_cus() {
   return cus[dev];
 }
 
+// Arguments of one call of the chunk path.
+struct Launch {
+  const void *q, *k, *v, *g, *beta;
+  const int32_t* cu;      // segment bounds
+  const int32_t* n_dev;   // number of segments on the device (ids path) or NULL
+  int32_t layout_segs;    // bound on the number of segments (workspace layout)
+  int32_t max_segs;       // segment slots (0 on the ids path)
+  int64_t N;
+  int32_t H;
+  float scale;
+  const float* s0;
+  void* o;
+  float* fs;
+  int32_t* flags;
+  char* ws;
+  int64_t row_len;        // > 0: ids path, segments map to rows of this length
+  const int32_t* seg_ids; // ids path: the [B, T] ids
+  hipStream_t stream;
+};
+
 // The plan, the state pass and the forward pass over segments given by cu
 // (max_segs slots), or, with n_dev, by the first *n_dev + 1 entries of cu that
 // a boundary scan wrote (layout_segs bounds their number; row_len > 0 then
 // maps segments to rows for the initial and final states).
-template <int DK, int DV>
-hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
-                       const void* beta, const int32_t* cu, const int32_t* n_dev,
-                       int32_t layout_segs, int32_t max_segs, int64_t N, int32_t H, float scale,
-                       const float* s0, void* o, float* fs, int32_t* flags, char* ws,
-                       int64_t row_len, const int32_t* seg_ids, hipStream_t s) {
+template <int DK, int DV, bool kNorm>
+hipError_t launch_dims(const Launch& a) {
   using C = Cfg<DK, DV>;
   constexpr int state_bytes = C::off_qh;  // the state pass uses the small tables, V and Kbar
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, false>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, false, kNorm>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::bytes);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, true>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, true, kNorm>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, state_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const PlanLayout L = plan_layout(N, H, DK, DV, layout_segs);
-  int32_t* plan = reinterpret_cast<int32_t*>(ws);
-  float* states = reinterpret_cast<float*>(ws + L.off_L);
-  float* decays = reinterpret_cast<float*>(ws + L.off_D);
-  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, n_dev, seg_ids,
-                     max_segs, int32_t(N), int32_t(L.states_max), int32_t(L.runs_max), plan, flags);
+  const PlanLayout L = plan_layout(a.N, a.H, DK, DV, a.layout_segs);
+  int32_t* plan = reinterpret_cast<int32_t*>(a.ws);
+  float* states = reinterpret_cast<float*>(a.ws + L.off_L);
+  float* decays = reinterpret_cast<float*>(a.ws + L.off_D);
+  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, a.stream, a.cu, a.n_dev, a.seg_ids,
+                     a.max_segs, int32_t(a.N), int32_t(L.states_max), int32_t(L.runs_max), plan, a.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const auto qp = static_cast<const bf16*>(q), kp = static_cast<const bf16*>(k);
-  const auto vp = static_cast<const bf16*>(v), gp = static_cast<const bf16*>(g);
-  const auto bp = static_cast<const bf16*>(beta);
+  const auto qp = static_cast<const bf16*>(a.q), kp = static_cast<const bf16*>(a.k);
+  const auto vp = static_cast<const bf16*>(a.v), gp = static_cast<const bf16*>(a.g);
+  const auto bp = static_cast<const bf16*>(a.beta);
   // persistent grids: as many work-groups as the LDS lets each CU hold
   const unsigned grid = unsigned(device_cus() * C::WG_PER_CU);
   if (L.states_max > 0) {
-    hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true>), dim3(grid), dim3(C::NT), state_bytes, s,
-                       qp, kp, vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale,
-                       static_cast<const float*>(nullptr), static_cast<bf16*>(nullptr),
-                       static_cast<float*>(nullptr), states, decays, row_len, seg_ids, n_dev, 0);
+    hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true, kNorm>), dim3(grid), dim3(C::NT), state_bytes,
+                       a.stream, qp, kp, vp, gp, bp, a.cu, plan, int32_t(L.runs_max), a.max_segs, a.N,
+                       a.H, a.scale, static_cast<const float*>(nullptr), static_cast<bf16*>(nullptr),
+                       static_cast<float*>(nullptr), states, decays, a.row_len, a.seg_ids, a.n_dev, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false>), dim3(grid), dim3(C::NT), C::bytes, s, qp, kp,
-                     vp, gp, bp, cu, plan, int32_t(L.runs_max), max_segs, N, H, scale, s0,
-                     static_cast<bf16*>(o), fs, states, decays, row_len, seg_ids, n_dev, 0);
+  hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false, kNorm>), dim3(grid), dim3(C::NT), C::bytes,
+                     a.stream, qp, kp, vp, gp, bp, a.cu, plan, int32_t(L.runs_max), a.max_segs, a.N,
+                     a.H, a.scale, a.s0, static_cast<bf16*>(a.o), a.fs, states, decays, a.row_len,
+                     a.seg_ids, a.n_dev, 0);
   return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_norm(bool qk_l2norm, const Launch& a) {
+  return qk_l2norm ? launch_dims<DK, DV, true>(a) : launch_dims<DK, DV, false>(a);
+}
+
+hipError_t dispatch(int32_t Dk, int32_t Dv, bool qk_l2norm, const Launch& a) {
+  if (Dk == 128 && Dv == 128) return launch_norm<128, 128>(qk_l2norm, a);
+  if (Dk == 64 && Dv == 64) return launch_norm<64, 64>(qk_l2norm, a);
+  if (Dk == 128 && Dv == 64) return launch_norm<128, 64>(qk_l2norm, a);
+  if (Dk == 64 && Dv == 128) return launch_norm<64, 128>(qk_l2norm, a);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -1292,44 +1367,29 @@ size_t kda_chunk_ids_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t D
 
 hipError_t launch_kda_chunk_ids(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta, const int32_t* seg, int64_t B, int64_t T,
-                                int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                int32_t H, int32_t Dk, int32_t Dv, float scale, bool qk_l2norm,
                                 const float* initial_state, void* o, float* final_state,
                                 int32_t* flags, void* workspace, hipStream_t stream) {
   const int64_t N = B * T;
   char* ws = static_cast<char*>(workspace);
   int32_t* n_dev = reinterpret_cast<int32_t*>(ws);
   int32_t* bounds = reinterpret_cast<int32_t*>(ws + 256);
-  char* wp = ws + ids_bounds_bytes(N);
   // segment starts of the [B, T] contract, found by the conversion's scan
   const hipError_t e = launch_segment_bounds(seg, N, T, bounds, n_dev, stream);
   if (e != hipSuccess) return e;
-  const int32_t S = int32_t(N);
-  if (Dk == 128 && Dv == 128)
-    return launch_dims<128, 128>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, seg, stream);
-  if (Dk == 64 && Dv == 64)
-    return launch_dims<64, 64>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, seg, stream);
-  if (Dk == 128 && Dv == 64)
-    return launch_dims<128, 64>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, seg, stream);
-  if (Dk == 64 && Dv == 128)
-    return launch_dims<64, 128>(q, k, v, g, beta, bounds, n_dev, S, 0, N, H, scale, initial_state, o, final_state, flags, wp, T, seg, stream);
-  return hipErrorInvalidValue;
+  const Launch a{q, k, v, g, beta, bounds, n_dev, int32_t(N), 0, N, H, scale, initial_state, o,
+                 final_state, flags, ws + ids_bounds_bytes(N), T, seg, stream};
+  return dispatch(Dk, Dv, qk_l2norm, a);
 }
 
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
-                            int32_t H, int32_t Dk, int32_t Dv, float scale,
+                            int32_t H, int32_t Dk, int32_t Dv, float scale, bool qk_l2norm,
                             const float* initial_state, void* o, float* final_state,
                             int32_t* flags, void* workspace, hipStream_t stream) {
-  char* ws = static_cast<char*>(workspace);
-  if (Dk == 128 && Dv == 128)
-    return launch_dims<128, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
-  if (Dk == 64 && Dv == 64)
-    return launch_dims<64, 64>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
-  if (Dk == 128 && Dv == 64)
-    return launch_dims<128, 64>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
-  if (Dk == 64 && Dv == 128)
-    return launch_dims<64, 128>(q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o, final_state, flags, ws, 0, nullptr, stream);
-  return hipErrorInvalidValue;
+  const Launch a{q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o,
+                 final_state, flags, static_cast<char*>(workspace), 0, nullptr, stream};
+  return dispatch(Dk, Dv, qk_l2norm, a);
 }
 
 // ---------------------------------------------------------------- no allocation
@@ -1369,13 +1429,13 @@ hipError_t scratch_address(void** out) {
 hipError_t launch_kda_chunk_noalloc(const void* q, const void* k, const void* v, const void* g,
                                     const void* beta, const int32_t* cu, int32_t max_segs,
                                     int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                    const float* initial_state, void* o, float* final_state,
-                                    int32_t* flags, hipStream_t stream) {
+                                    bool qk_l2norm, const float* initial_state, void* o,
+                                    float* final_state, int32_t* flags, hipStream_t stream) {
   void* ws = nullptr;
   const hipError_t e = scratch_address(&ws);
   if (e != hipSuccess) return e;
-  return launch_kda_chunk(q, k, v, g, beta, cu, max_segs, N, H, Dk, Dv, scale, initial_state, o,
-                          final_state, flags, ws, stream);
+  return launch_kda_chunk(q, k, v, g, beta, cu, max_segs, N, H, Dk, Dv, scale, qk_l2norm,
+                          initial_state, o, final_state, flags, ws, stream);
 }
 
 }  // namespace pkv

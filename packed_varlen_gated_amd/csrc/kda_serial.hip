@@ -32,6 +32,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTB = 16;
 constexpr int kTailBlocks = 64;
+constexpr float kL2NormEps = 1e-6f;  // added to a squared norm (the q/k L2 normalisation option)
+static_assert(kThreads == 16 * kTB, "16 threads per staged token for the L2 norm");
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
     const T* __restrict__ g, const T* __restrict__ beta, const int32_t* __restrict__ cu,
     int32_t max_segs, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
     T* __restrict__ o, float* __restrict__ final_state, int32_t* __restrict__ flags,
-    const int32_t* __restrict__ seg_ids, int64_t row_len) {
+    const int32_t* __restrict__ seg_ids, int64_t row_len, bool qk_l2norm) {
   constexpr int RG = kThreads / DV;  // row groups
   constexpr int R = DK / RG;         // consecutive rows per thread
   static_assert(RG * DV == kThreads && R * RG == DK, "bad tile");
@@ -134,6 +136,32 @@ __global__ __launch_bounds__(kThreads) void kda_serial_kernel(
       s_rst[tid] = r;
     }
     __syncthreads();
+    if (qk_l2norm) {
+      // q and k of each staged token L2-normalised over Dk: 16 threads per
+      // token, each over the channels j, j + 16, ...; sums over the 16 lanes
+      // by shuffles (one 64-wide wave holds four tokens' groups)
+      const int tt = tid >> 4, j = tid & 15;
+      float sq = 0.f, sk = 0.f;
+      if (tt < nt) {
+        for (int d = j; d < DK; d += 16) {
+          sq = fmaf(s_q[tt][d], s_q[tt][d], sq);
+          sk = fmaf(s_k[tt][d], s_k[tt][d], sk);
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        sq += __shfl_xor(sq, m, 16);
+        sk += __shfl_xor(sk, m, 16);
+      }
+      if (tt < nt) {
+        const float rq = 1.f / sqrtf(sq + kL2NormEps), rk = 1.f / sqrtf(sk + kL2NormEps);
+        for (int d = j; d < DK; d += 16) {
+          s_q[tt][d] *= rq;
+          s_k[tt][d] *= rk;
+        }
+      }
+      __syncthreads();
+    }
     for (int tt = 0; tt < nt; ++tt) {
       const float bv = s_b[tt] * s_v[tt][e];
       const int rst = s_rst[tt];  // 1: a new segment, nothing carries over
@@ -169,13 +197,14 @@ template <typename T, int DK, int DV>
 hipError_t launch_dims(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                        int32_t H, float scale, const float* s0, void* o, float* fs,
-                       int32_t* flags, const int32_t* seg_ids, int64_t row_len, hipStream_t s) {
+                       int32_t* flags, const int32_t* seg_ids, int64_t row_len, bool norm,
+                       hipStream_t s) {
   const int64_t blocks = int64_t(max_segs) * H + kTailBlocks;
   hipLaunchKernelGGL((kda_serial_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(kThreads), 0, s,
                      static_cast<const T*>(q), static_cast<const T*>(k),
                      static_cast<const T*>(v), static_cast<const T*>(g),
                      static_cast<const T*>(beta), cu, max_segs, N, H, scale, s0,
-                     static_cast<T*>(o), fs, flags, seg_ids, row_len);
+                     static_cast<T*>(o), fs, flags, seg_ids, row_len, norm);
   return hipGetLastError();
 }
 
@@ -183,11 +212,11 @@ template <typename T, int DK>
 hipError_t launch_dv(int32_t Dv, const void* q, const void* k, const void* v, const void* g,
                      const void* beta, const int32_t* cu, int32_t max_segs, int64_t N, int32_t H,
                      float scale, const float* s0, void* o, float* fs, int32_t* flags,
-                     const int32_t* seg_ids, int64_t row_len, hipStream_t s) {
+                     const int32_t* seg_ids, int64_t row_len, bool norm, hipStream_t s) {
   switch (Dv) {
-    case 32: return launch_dims<T, DK, 32>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
-    case 64: return launch_dims<T, DK, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
-    case 128: return launch_dims<T, DK, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
+    case 32: return launch_dims<T, DK, 32>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, norm, s);
+    case 64: return launch_dims<T, DK, 64>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, norm, s);
+    case 128: return launch_dims<T, DK, 128>(q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, norm, s);
   }
   return hipErrorInvalidValue;
 }
@@ -196,11 +225,12 @@ template <typename T>
 hipError_t launch_dk(int32_t Dk, int32_t Dv, const void* q, const void* k, const void* v,
                      const void* g, const void* beta, const int32_t* cu, int32_t max_segs,
                      int64_t N, int32_t H, float scale, const float* s0, void* o, float* fs,
-                     int32_t* flags, const int32_t* seg_ids, int64_t row_len, hipStream_t s) {
+                     int32_t* flags, const int32_t* seg_ids, int64_t row_len, bool norm,
+                     hipStream_t s) {
   switch (Dk) {
-    case 32: return launch_dv<T, 32>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
-    case 64: return launch_dv<T, 64>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
-    case 128: return launch_dv<T, 128>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, s);
+    case 32: return launch_dv<T, 32>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, norm, s);
+    case 64: return launch_dv<T, 64>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, norm, s);
+    case 128: return launch_dv<T, 128>(Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, s0, o, fs, flags, seg_ids, row_len, norm, s);
   }
   return hipErrorInvalidValue;
 }
@@ -210,27 +240,27 @@ hipError_t launch_dk(int32_t Dk, int32_t Dv, const void* q, const void* k, const
 hipError_t launch_kda_serial(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                              int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
-                             const float* initial_state, void* o, float* final_state,
-                             int32_t* flags, hipStream_t stream) {
+                             bool qk_l2norm, const float* initial_state, void* o,
+                             float* final_state, int32_t* flags, hipStream_t stream) {
   if (dtype == 0)
     return launch_dk<bf16>(Dk, Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o,
-                           final_state, flags, nullptr, 0, stream);
+                           final_state, flags, nullptr, 0, qk_l2norm, stream);
   return launch_dk<float>(Dk, Dv, q, k, v, g, beta, cu, max_segs, N, H, scale, initial_state, o,
-                          final_state, flags, nullptr, 0, stream);
+                          final_state, flags, nullptr, 0, qk_l2norm, stream);
 }
 
 hipError_t launch_kda_serial_ids(const void* q, const void* k, const void* v, const void* g,
                                  const void* beta, const int32_t* seg, int64_t B, int64_t T,
                                  int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
-                                 const float* initial_state, void* o, float* final_state,
-                                 hipStream_t stream) {
+                                 bool qk_l2norm, const float* initial_state, void* o,
+                                 float* final_state, hipStream_t stream) {
   // one "slot" per row; no cu_seqlens, so the tail blocks find nothing to zero
   const int32_t rows = int32_t(B);
   if (dtype == 0)
     return launch_dk<bf16>(Dk, Dv, q, k, v, g, beta, nullptr, rows, B * T, H, scale, initial_state,
-                           o, final_state, nullptr, seg, T, stream);
+                           o, final_state, nullptr, seg, T, qk_l2norm, stream);
   return launch_dk<float>(Dk, Dv, q, k, v, g, beta, nullptr, rows, B * T, H, scale, initial_state,
-                          o, final_state, nullptr, seg, T, stream);
+                          o, final_state, nullptr, seg, T, qk_l2norm, stream);
 }
 
 }  // namespace pkv

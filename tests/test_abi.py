@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pkv_abi_version() == 4
+    assert lib.pkv_abi_version() == 5
     for code, name in [(0, b"PKV_OK"), (1, b"PKV_ERR_INVALID_ARGUMENT"), (2, b"PKV_ERR_UNSUPPORTED"),
                        (3, b"PKV_ERR_WORKSPACE"), (4, b"PKV_ERR_HIP"), (99, b"PKV_ERR_UNKNOWN")]:
         assert lib.pkv_status_string(code) == name
@@ -88,8 +88,8 @@ def test_eod_validation(lib, args, code):
 def _kda_args(**kw):
     base = dict(q=ctypes.c_void_p(0x10000000), k=ctypes.c_void_p(0x20000000), v=ctypes.c_void_p(0x30000000),
                 g=ctypes.c_void_p(0x40000000), beta=ctypes.c_void_p(0x50000000), cu=P, max_segs=4, N=256,
-                H=2, Dk=64, Dv=64, scale=1.0, dtype=0, s0=NUL, o=ctypes.c_void_p(0x60000000), fs=NUL, flags=NUL,
-                ws=NUL, ws_bytes=0, stream=NUL)
+                H=2, Dk=64, Dv=64, scale=1.0, dtype=0, options=0, s0=NUL, o=ctypes.c_void_p(0x60000000), fs=NUL,
+                flags=NUL, ws=NUL, ws_bytes=0, stream=NUL)
     base.update(kw)
     return tuple(base.values())
 
@@ -97,7 +97,7 @@ def _kda_args(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=NUL), 1), (dict(k=NUL), 1), (dict(v=NUL), 1), (dict(g=NUL), 1), (dict(beta=NUL), 1),
     (dict(o=NUL), 1), (dict(N=0), 1), (dict(N=1 << 31), 1), (dict(H=0), 1), (dict(max_segs=0), 1),
-    (dict(Dk=48), 2), (dict(Dv=256), 2), (dict(dtype=5), 2),
+    (dict(Dk=48), 2), (dict(Dv=256), 2), (dict(dtype=5), 2), (dict(options=2), 2), (dict(options=-1), 2),
     (dict(o=ctypes.c_void_p(0x10000000 + 64)), 1),    # o overlaps q
     (dict(o=ctypes.c_void_p(0x60000008)), 1),         # o not 16-byte aligned
     (dict(k=ctypes.c_void_p(0x20000002)), 1),         # k not 16-byte aligned
@@ -155,8 +155,8 @@ def test_workspace_size_and_check(lib):
 def _ids_args(**kw):
     base = dict(q=ctypes.c_void_p(0x10000000), k=ctypes.c_void_p(0x20000000), v=ctypes.c_void_p(0x30000000),
                 g=ctypes.c_void_p(0x40000000), beta=ctypes.c_void_p(0x50000000), seg=ctypes.c_void_p(0x58000000),
-                B=2, T=128, H=2, Dk=64, Dv=64, scale=1.0, dtype=0, s0=NUL, o=ctypes.c_void_p(0x60000000),
-                fs=NUL, flags=NUL, ws=NUL, ws_bytes=0, stream=NUL)
+                B=2, T=128, H=2, Dk=64, Dv=64, scale=1.0, dtype=0, options=0, s0=NUL,
+                o=ctypes.c_void_p(0x60000000), fs=NUL, flags=NUL, ws=NUL, ws_bytes=0, stream=NUL)
     base.update(kw)
     return tuple(base.values())
 
@@ -164,7 +164,7 @@ def _ids_args(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=NUL), 1), (dict(seg=NUL), 1), (dict(o=NUL), 1), (dict(B=0), 1), (dict(T=0), 1),
     (dict(B=1 << 16, T=1 << 15), 1),                                   # B*T too large
-    (dict(Dk=48), 2), (dict(dtype=5), 2),
+    (dict(Dk=48), 2), (dict(dtype=5), 2), (dict(options=4), 2),
     (dict(o=ctypes.c_void_p(0x58000000)), 1),                          # o overlaps segment_ids
     (dict(s0=ctypes.c_void_p(0x70000000), fs=ctypes.c_void_p(0x70000000)), 1),  # initial == final
     (dict(), 3),                                                       # no workspace

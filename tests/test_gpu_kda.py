@@ -429,3 +429,75 @@ def test_initial_state_with_cut_segments():
     # five times the bf16 tolerance, so dropping it from the composition fails above
     r0, _ = oracle.chunk_kda_varlen(*[f64(t) for t in ts], None)
     assert np.linalg.norm(ro[6016:] - r0[6016:]) > 0.1 * np.linalg.norm(ro[6016:])
+
+
+# RFC-0026 section 3.3's use_qk_l2norm_in_kernel: q and k are normalised
+# inside the call, so the inputs here are not unit-norm (random positive
+# per-(token, head) scales); the oracle normalises in fp64.
+def _unnormalised(ts, rng):
+    q, k = ts[0], ts[1]
+    N, H = q.shape[0], q.shape[1]
+    sq = torch.from_numpy(rng.uniform(0.3, 4.0, (N, H, 1))).to(q.dtype)
+    sk = torch.from_numpy(rng.uniform(0.3, 4.0, (N, H, 1))).to(k.dtype)
+    return [(q * sq).to(q.dtype), (k * sk).to(k.dtype)] + list(ts[2:])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("Dk,Dv", [(32, 32), (64, 64), (128, 128), (64, 128), (128, 64)])
+def test_qk_l2norm_small_shapes(dtype, Dk, Dv):
+    pkv = _pkv()
+    rng = np.random.default_rng(Dk * 11 + Dv)
+    H = 3
+    lens = [1, 63, 64, 65, 2, 127, 129, 16, 200]
+    cu = np.concatenate([[0], np.cumsum(lens), [sum(lens)]])
+    N = sum(lens) + 21
+    ts = _unnormalised(_small_case(rng, N, H, Dk, Dv, dtype, cu), rng)
+    q, k, v, g, beta = [t.to(device()) for t in ts]
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    print(f"qk_l2norm dtype {dtype} Dk {Dk} Dv {Dv}", flush=True)
+    o, fs = pkv.chunk_kda_varlen(q[None], k[None], v[None], g[None], beta[None], cud, scale=0.6,
+                                 use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], cu, scale=0.6, use_qk_l2norm=True)
+    dt = "f32" if dtype == torch.float32 else "bf16"
+    check_close(f64(o[0]), ro, dt, "o")
+    check_close(f64(fs), rfs, dt, "final_state")
+    for i in range(len(cu) - 1):
+        if cu[i + 1] > cu[i]:
+            check_close(f64(o[0])[cu[i]:cu[i + 1]], ro[cu[i]:cu[i + 1]], dt, f"segment {i}")
+    # the unnormalised inputs give a different result without the option
+    o2, _ = pkv.chunk_kda_varlen(q[None], k[None], v[None], g[None], beta[None], cud, scale=0.6)
+    torch.cuda.synchronize()
+    assert np.linalg.norm(f64(o2[0]) - ro) > 0.1 * np.linalg.norm(ro)
+
+
+def test_qk_l2norm_cut_segment_and_ling3_sample():
+    """The option through the state pass of a cut segment (141 chunks, 3 runs,
+    with an initial state) and on the whole Ling3-like sample."""
+    pkv = _pkv()
+    rng = np.random.default_rng(91)
+    N, H, D = 9000, 2, 128
+    ts = _unnormalised(_small_case(rng, N, H, D, D, torch.bfloat16, None), rng)
+    S0 = rng.standard_normal((1, H, D, D))
+    dq, dk, dv, dg, db = [t.to(device())[None] for t in ts]
+    ws = torch.empty(pkv.chunk_kda_varlen_workspace_size(N, H, D, D, 1, torch.bfloat16),
+                     dtype=torch.uint8, device=device())
+    o, fs = pkv.chunk_kda_varlen(dq, dk, dv, dg, db, None, workspace=ws, use_qk_l2norm_in_kernel=True,
+                                 initial_state=torch.from_numpy(S0).float().to(device()))
+    torch.cuda.synchronize()
+    assert ws[:8].view(torch.int32).cpu().tolist()[:2] == [3, 2]
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], None, initial_state=S0, use_qk_l2norm=True)
+    check_close(f64(o[0]), ro, "bf16", "o")
+    check_close(f64(fs), rfs, "bf16", "final state")
+    check_close(f64(o[0])[6016:], ro[6016:], "bf16", "last run")
+
+    wl = workloads.make_workload("ling3_tiny_sample", conv=False)
+    cu = _cu(wl)
+    ts = _unnormalised([wl.q, wl.k, wl.v, wl.g, wl.beta], rng)
+    q, k, v, g, beta = [t.to(device())[None] for t in ts]
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    o, fs = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], cu, use_qk_l2norm=True)
+    check_close(f64(o[0]), ro, "bf16", "ling3 o")
+    check_close(f64(fs), rfs, "bf16", "ling3 final states")

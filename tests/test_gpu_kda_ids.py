@@ -149,3 +149,27 @@ def test_matches_cu_seqlens_entry_on_flat_microbatch():
     o2, _ = pkv.chunk_kda_varlen(q, k, v, g, beta, cu, output_final_state=False)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [(torch.float32, 64, 32), (torch.bfloat16, 64, 64),
+                                         (torch.bfloat16, 128, 128)])
+def test_qk_l2norm(dtype, Dk, Dv):
+    """RFC-0026 section 3.3's use_qk_l2norm_in_kernel on the [B, T] entry, with
+    padding and unnormalised q and k."""
+    pkv = _pkv()
+    rng = np.random.default_rng(Dk + 5 * Dv)
+    B, T, H = 3, 500, 2
+    ts = _inputs(rng, B, T, H, Dk, Dv, dtype)
+    ts[0] = (ts[0] * torch.from_numpy(rng.uniform(0.3, 4.0, (B, T, H, 1))).to(dtype)).to(dtype)
+    ts[1] = (ts[1] * torch.from_numpy(rng.uniform(0.3, 4.0, (B, T, H, 1))).to(dtype)).to(dtype)
+    seg = _ids(rng, B, T)
+    S0 = rng.standard_normal((B, H, Dk, Dv)) * 0.5
+    q, k, v, g, beta = [t.to(device()) for t in ts]
+    o, fs = pkv.chunk_kda_segment_ids(q, k, v, g, beta, torch.from_numpy(seg).to(device()),
+                                      initial_state=torch.from_numpy(S0).float().to(device()),
+                                      use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    ro, rfs = oracle.chunk_kda_segment_ids(*[f64(t) for t in ts], seg, initial_state=S0, use_qk_l2norm=True)
+    dt = "f32" if dtype == torch.float32 else "bf16"
+    check_close(f64(o), ro, dt, "o")
+    check_close(f64(fs), rfs, dt, "final states")

@@ -48,7 +48,7 @@ def _noalloc(ts, cu):
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     st = lib.pkv_chunk_kda_varlen_noalloc(p(q), p(k), p(v), p(g), p(beta), p(cud), max_segs, N, H, D, D,
-                                          1.0, 0, None, p(o), p(fs), p(flags),
+                                          1.0, 0, 0, None, p(o), p(fs), p(flags),
                                           ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
     assert st == 0, lib.pkv_status_string(st)
     torch.cuda.synchronize()
@@ -91,7 +91,7 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
     lib = _pkv().library()
     A = lambda i: ctypes.c_void_p(i << 44)  # fake, far apart, never dereferenced
     N, H, D = 1 << 20, 32, 128
-    st = lib.pkv_chunk_kda_varlen_noalloc(A(1), A(2), A(3), A(4), A(5), None, 1, N, H, D, D, 1.0, 0, None,
-                                          A(6), None, None, None)
+    st = lib.pkv_chunk_kda_varlen_noalloc(A(1), A(2), A(3), A(4), A(5), None, 1, N, H, D, D, 1.0, 0, 0,
+                                          None, A(6), None, None, None)
     assert st == 3  # PKV_ERR_WORKSPACE, before any launch
     assert lib.pkv_chunk_kda_varlen_workspace_size(N, H, D, D, 1, 0) > (96 << 20)
