@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--workload", default="flat_microbatch")
     p.add_argument("--final-state", choices=["auto", "on", "off"], default="auto")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-legs", dest="legs", action="store_false",
+                   help="skip the extra timed legs (final states toggled, q/k L2 norm, device copy)")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="oracle sample size in tokens (0: sized for ~15 s of CPU work)")
     p.add_argument("--mode", choices=["bench", "kernel", "copy", "backward"], default="bench")
@@ -110,40 +112,69 @@ def read_traffic(workload):
     return float(m_bytes.group(1))
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu's "Model name"), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, cu, sample_tokens, target_s=15.0):
     """The oracle, as it stands, on the first S tokens of the workload
-    (segments clipped there), all heads, split by head over a process pool.
-    S = sample_tokens if given, else sized from a short timed prefix so the
-    measured run takes about target_s seconds. Returns a dict for the JSON line."""
+    (segments clipped there), every (segment, head) unit: the heads are split
+    into one group per worker process (one per available core, at most 16,
+    the GPU host's CPU share), each worker running the oracle over every
+    segment of its heads. The inputs are written once to memory-mapped files
+    before the timed run (as the GPU's inputs are resident before its timed
+    region); the timed run is the pool's wall time. S = sample_tokens if
+    given, else sized from a short timed prefix so the measured run takes
+    about target_s seconds (capped at the whole workload). Returns a dict for
+    the JSON line."""
     import multiprocessing as mp
+    import shutil
+    import tempfile
     import numpy as np
     from concurrent.futures import ProcessPoolExecutor
 
     cfg = wl.cfg
-    ncores = len(os.sched_getaffinity(0))
-    workers = max(1, min(16, ncores, cfg.H))
-    groups = np.array_split(np.arange(cfg.H), workers)
+    host_cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, host_cores, cfg.H))
+    groups = [g.tolist() for g in np.array_split(np.arange(cfg.H), workers)]
+    tmp = tempfile.mkdtemp(prefix="pkv_oracle_")
+    try:
+        paths = []
+        for name, t in zip(("q", "k", "v", "g", "beta"), (wl.q, wl.k, wl.v, wl.g, wl.beta)):
+            path = os.path.join(tmp, name + ".npy")
+            np.save(path, t.float().numpy())  # exact for bf16
+            paths.append(path)
 
-    def jobs(S):
-        cu_s = np.minimum(cu, S)
-        arrs = [t[:S].float().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]  # exact for bf16
-        return [tuple(a[:, gidx] for a in arrs) + (cu_s,) for gidx in groups]
+        def run(ex, S):
+            cu_s = np.minimum(cu, S)
+            t0 = time.perf_counter()
+            list(ex.map(_oracle_job, [(paths, hs, S, cu_s) for hs in groups]))
+            return time.perf_counter() - t0
 
-    ctx = mp.get_context("spawn")  # workers never touch the GPU
-    os.environ["OMP_NUM_THREADS"] = "1"
-    with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
-        list(ex.map(_warm, range(workers)))  # spawn and import outside the timed runs
-        if sample_tokens:
-            S = min(sample_tokens, wl.N)
-        else:
-            S0 = min(512, wl.N)
-            rate = S0 / max(ex.map(_oracle_job, jobs(S0)))
-            S = int(min(wl.N, max(S0, rate * target_s)) // 64 * 64) or S0
-        dt = max(ex.map(_oracle_job, jobs(S)))  # workers run in parallel: the slowest one
+        ctx = mp.get_context("spawn")  # workers never touch the GPU
+        os.environ["OMP_NUM_THREADS"] = "1"
+        with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
+            list(ex.map(_warm, range(workers)))  # spawn and import outside the timed runs
+            if sample_tokens:
+                S = min(sample_tokens, wl.N)
+            else:
+                S0 = min(1024, wl.N)
+                rate = S0 / run(ex, S0)
+                S = int(min(wl.N, max(S0, rate * target_s)) // 64 * 64) or S0
+            dt = run(ex, S)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
     return {"value": S / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"first {S} of {wl.N} tokens ({cfg.name}), all {cfg.H} heads, "
-                      f"fp64 token recurrence, {workers} processes split by head, {dt:.1f} s "
-                      f"(slowest process, compute only)"}
+            "host_cores": host_cores, "cpu_model": cpu_model(),
+            "sample": f"first {S} of {wl.N} tokens ({cfg.name}): every (segment, head) unit, "
+                      f"fp64 token recurrence, heads split over {workers} processes, {dt:.1f} s wall"}
 
 
 def _warm(_):
@@ -152,14 +183,40 @@ def _warm(_):
 
 
 def _oracle_job(args):
-    """Runs the oracle on one head group; returns its own run time (the data
-    transfer and the fp64 conversion are not timed)."""
+    """Runs the oracle on every (segment, head) unit of a group of heads."""
     import numpy as np
     import oracle
-    q, k, v, g, beta = (a.astype(np.float64) for a in args[:5])
-    t0 = time.perf_counter()
-    oracle.chunk_kda_varlen(q, k, v, g, beta, args[5])
-    return time.perf_counter() - t0
+    paths, heads, S, cu_s = args
+    q, k, v, g, beta = (np.load(p, mmap_mode="r")[:S, heads[0]:heads[-1] + 1].astype(np.float64)
+                        for p in paths)
+    oracle.chunk_kda_varlen(q, k, v, g, beta, cu_s)
+    return True
+
+
+def pct(xs):
+    """Average, median, p10 and p90 of a list of durations."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"avg": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90))}
+
+
+def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
+    """Measured device-to-device copy rate (bytes read + written per second)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    dt = a.elapsed_time(b) / 1000.0 / reps
+    del src, dst
+    return 2 * nbytes / dt / 1e9
 
 
 def main():
@@ -240,10 +297,13 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms = (t1 - t0) * 1000.0 / args.steps
-        call_s = sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1000.0
+        calls = [a.elapsed_time(b) / 1000.0 for a, b in evs]
+        call_s = sum(calls) / len(calls)
+        cp = pct(calls)
         bb = backward_bytes(cfg, cu_host)
         achieved = bb / call_s / 1e9
-        log(f"backward: {call_s * 1e3:.3f} ms per call; {achieved:.0f} GB/s = "
+        log(f"backward: {call_s * 1e3:.3f} ms per call (median {cp['median'] * 1e3:.3f}, p10 "
+            f"{cp['p10'] * 1e3:.3f}, p90 {cp['p90'] * 1e3:.3f}); {achieved:.0f} GB/s = "
             f"{achieved / HBM_PEAK_GBS:.3f} of HBM peak; flags {int(flags.item())}")
         print(json.dumps({
             "metric": f"packed tokens/sec for chunk_kda_varlen bwd at H={H},D={cfg.Dk}",
@@ -256,6 +316,7 @@ def main():
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "kernel": "chunk_kda_varlen_backward", "kernel_avg_us": call_s * 1e6,
                          "algorithmic_bytes_per_launch": bb},
+            "timing": {"call_us": {k2: x * 1e6 for k2, x in cp.items()}},
             "cpu_baseline": None}), flush=True)
         return
 
@@ -266,44 +327,77 @@ def main():
         ws_ids = torch.empty(pkv.chunk_kda_segment_ids_workspace_size(B, T, H, cfg.Dk, cfg.Dv, q.dtype),
                              dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
+    def step(ev=None, fstate=None, l2=False):
+        """One pass of the path; ev = (step start, call start, call end, step end) events."""
+        fst = final_state if fstate is None else fstate
+        if ev is not None:
+            ev[0].record()
         if args.entry == "segment_ids":
             if conv_x is not None:
                 pkv.short_conv_segmask(conv_x, conv_w, seg, out=conv_y)
             if ev is not None:
-                ev[0].record()
-            out = pkv.chunk_kda_segment_ids(qb, kb, vb, gb, betab, seg, output_final_state=final_state,
-                                            flags=flags, out=ob, workspace=ws_ids)
+                ev[1].record()
+            out = pkv.chunk_kda_segment_ids(qb, kb, vb, gb, betab, seg, output_final_state=fst,
+                                            flags=flags, out=ob, workspace=ws_ids, use_qk_l2norm_in_kernel=l2)
+        else:
+            r = pkv.segment_ids_to_cu_seqlens(seg, cfg.max_segs)
+            if conv_x is not None:
+                pkv.short_conv_segmask(conv_x, conv_w, seg, out=conv_y)
             if ev is not None:
                 ev[1].record()
-            return out
-        r = pkv.segment_ids_to_cu_seqlens(seg, cfg.max_segs)
-        if conv_x is not None:
-            pkv.short_conv_segmask(conv_x, conv_w, seg, out=conv_y)
+            out = pkv.chunk_kda_varlen(q, k, v, g, beta, r.cu_seqlens, output_final_state=fst,
+                                       flags=flags, out=o, workspace=ws, use_qk_l2norm_in_kernel=l2)
         if ev is not None:
-            ev[0].record()
-        out = pkv.chunk_kda_varlen(q, k, v, g, beta, r.cu_seqlens, output_final_state=final_state,
-                                   flags=flags, out=o, workspace=ws)
-        if ev is not None:
-            ev[1].record()
+            ev[2].record()
+            ev[3].record()
         return out
+
+    def timed(nsteps, **kw):
+        """nsteps steps bracketed by synchronisations: (wall ms per step, call
+        durations in s, step durations in s) from HIP events on the launch stream."""
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(nsteps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(nsteps):
+            step(evs[i], **kw)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        calls = [e[1].elapsed_time(e[2]) / 1000.0 for e in evs]
+        steps = [e[0].elapsed_time(e[3]) / 1000.0 for e in evs]
+        return (t1 - t0) * 1000.0 / nsteps, calls, steps
+
+    # Extra legs, measured before the headline steps and not part of `value`:
+    # the same workload with the final states toggled, and with q, k
+    # normalised inside the call (each after its own W warm-up steps); and a
+    # plain 1 GiB device copy, the measured bandwidth beside the published
+    # peak. They run first so the headline steps find the GPU at the clocks
+    # of sustained work (clocks rise over the first ~15 ms of work).
+    legs = {}
+    if args.legs:
+        for name, kw, with_fs in (("output_final_state_" + ("off" if final_state else "on"),
+                                   {"fstate": not final_state}, not final_state),
+                                  ("qk_l2norm", {"l2": True}, final_state)):
+            for _ in range(args.warmup):
+                step(**kw)
+            lm, lk, ls = timed(args.steps, **kw)
+            b = algorithmic_bytes(cfg, cu_host, with_fs)
+            lp = pct(lk)
+            legs[name] = {"call_us": {k2: x * 1e6 for k2, x in lp.items()}, "ms_per_step": lm,
+                          "tokens_per_s": N / (lm / 1000.0), "algorithmic_bytes": b,
+                          "hbm_frac": b / lp["avg"] / 1e9 / HBM_PEAK_GBS}
+            log(f"leg {name}: call {lp['avg'] * 1e6:.1f} us avg (median {lp['median'] * 1e6:.1f}); "
+                f"{b / lp['avg'] / 1e9 / HBM_PEAK_GBS:.3f} of HBM peak")
+        legs["copy_gbs"] = copy_bandwidth(dev)
+        log(f"device copy of 1 GiB: {legs['copy_gbs']:.0f} GB/s (read + written) against the "
+            f"{HBM_PEAK_GBS:.0f} GB/s published peak")
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    ms, kc, st = timed(args.steps)
     if int(flags.item()) != 0:
         log(f"warning: flags = {int(flags.item())}")
-    ms = (t1 - t0) * 1000.0 / args.steps
-    kc_ms = [a.elapsed_time(b) for a, b in events]
-    kc_avg_s = sum(kc_ms) / len(kc_ms) / 1000.0
+    kc_avg_s = sum(kc) / len(kc)
     value = N / (ms / 1000.0)
 
     alg_bytes = algorithmic_bytes(cfg, cu_host, final_state)
@@ -311,16 +405,21 @@ def main():
     flops = algorithmic_flops(cfg, cu_host)
     mfma_frac = flops / kc_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS
     traffic = read_traffic(cfg.name) if args.entry == "cu_seqlens" else None
-    log(f"step {ms:.3f} ms; {DOMINANT_KERNEL} {kc_avg_s * 1e6:.1f} us avg "
-        f"(min {min(kc_ms) * 1e3:.1f} max {max(kc_ms) * 1e3:.1f}); {achieved:.0f} GB/s "
+    kp, sp = pct(kc), pct(st)
+    log(f"step {ms:.3f} ms (events: median {sp['median'] * 1e3:.3f}, p10 {sp['p10'] * 1e3:.3f}, "
+        f"p90 {sp['p90'] * 1e3:.3f}); {DOMINANT_KERNEL} {kc_avg_s * 1e6:.1f} us avg, median "
+        f"{kp['median'] * 1e6:.1f}, p10 {kp['p10'] * 1e6:.1f}, p90 {kp['p90'] * 1e6:.1f} "
+        f"(min {min(kc) * 1e6:.1f} max {max(kc) * 1e6:.1f}); {achieved:.0f} GB/s "
         f"= {achieved / HBM_PEAK_GBS:.3f} of HBM peak; MFMA {mfma_frac:.4f} of bf16 peak; "
         f"n_segs {n_segs}")
+    log("calls in order (us): " + " ".join(f"{x * 1e6:.0f}" for x in kc))
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle ...")
         cpu = cpu_baseline(wl, cu_host, args.cpu_sample_tokens)
-        log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
+        log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} processes "
+            f"({cpu['host_cores']} host cores available, {cpu['cpu_model']})")
 
     line = {
         "metric": METRIC,
@@ -348,6 +447,9 @@ def main():
                      "kernel_avg_us": kc_avg_s * 1e6,
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "mfma_frac_bf16": mfma_frac},
+        "timing": {"call_us": {k2: x * 1e6 for k2, x in kp.items()},
+                   "step_ms": {k2: x * 1e3 for k2, x in sp.items()}},
+        "legs": legs or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

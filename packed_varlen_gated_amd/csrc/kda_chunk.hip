@@ -194,6 +194,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// s_waitcnt vmcnt(0): every vector memory operation of the wave has completed
+// (gfx9 encoding: vmcnt 0, expcnt 7 and lgkmcnt 15, i.e. no wait on those).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Two floats -> one register of two bf16 (round to nearest even), a single
 // v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pk2(float a, float b) {
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   int h = 0, slot = 0, run_idx = 0, sbase = 0, nchunks = 0;
   bool last = false;
   int64_t start = 0, end = 0;
-  auto begin_item = [&](int item) {
+  auto begin_item = [&](int item) __attribute__((always_inline)) {
     const int rank = item / H;
     h = item % H;
     int c0, c1;
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   const uint32_t rowK = uint32_t(H) * DK * 2;  // bytes between tokens (q, k, g)
   const uint32_t rowV = uint32_t(H) * DV * 2;
   const uint32_t rowB = uint32_t(H) * 2;
-  auto chunk_len = [&](int c) {
+  auto chunk_len = [&](int c) __attribute__((always_inline)) {
     const int64_t rem = end - (start + int64_t(c) * kC);
     return int(rem < kC ? rem : kC);
   };
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     int64_t tokbase;
     uint32_t nK, nV, nB;
   };
-  auto src_of = [&](int c) {
+  auto src_of = [&](int c) __attribute__((always_inline)) {
     const bool live = c < nchunks;
     const int64_t p0 = start + int64_t(live ? c : 0) * kC;
     const int Lc = live ? chunk_len(c) : 1;
@@ -428,13 +432,13 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     r.nB = live ? uint32_t(Lc - 1) * rowB + 2 : 0u;
     return r;
   };
-  auto load_g = [&](Raw<PCPL, PVPL>& R, int c) {
+  auto load_g = [&](Raw<PCPL, PVPL>& R, int c) __attribute__((always_inline)) {
     const Src r = src_of(c);
     const auto rg = rsrc(g + r.tokbase * DK, r.nK);
 #pragma unroll
     for (int i = 0; i < 4; ++i) wload(R.g[i], rg, uint32_t(tok0 + i) * rowK + ch0 * 2);
   };
-  auto load_qk = [&](RawQK<PCPL>& R, int c) {
+  auto load_qk = [&](RawQK<PCPL>& R, int c) __attribute__((always_inline)) {
     const Src r = src_of(c);
     const auto rq = rsrc(q + r.tokbase * DK, r.nK), rk = rsrc(k + r.tokbase * DK, r.nK);
 #pragma unroll
@@ -445,12 +449,12 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     }
   };
   // beta of a whole chunk, token = lane (one wave loads it for everyone)
-  auto load_beta = [&](int c) {
+  auto load_beta = [&](int c) __attribute__((always_inline)) {
     const Src r = src_of(c);
     return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rsrc(beta + r.tokbase, r.nB),
                                                          uint32_t(lane) * rowB, 0, 0));
   };
-  auto load_v = [&](Raw<PCPL, PVPL>& R, int c) {
+  auto load_v = [&](Raw<PCPL, PVPL>& R, int c) __attribute__((always_inline)) {
     const Src r = src_of(c);
     const auto rv = rsrc(v + r.tokbase * DV, r.nV);
 #pragma unroll
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // the cumsums, stay live until the first half; s_T gets 2^T of every
   // sub-chunk (the next half's factors are products of those). The state
   // pass has no q and folds k only.
-  auto scan = [&](const Raw<PCPL, PVPL>& R, RawQK<PCPL>& X) {
+  auto scan = [&](const Raw<PCPL, PVPL>& R, RawQK<PCPL>& X) __attribute__((always_inline)) {
     // kNorm: 1 / sqrt(|x|^2 + eps) of each token's q and k; the 16 lanes of a
     // row hold the token's Dk channels, PCPL each
     float rq[4], rk[4];
@@ -539,7 +543,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // inside (one instance per sub-chunk), so every choice below is resolved
   // without branches.
   auto produce_a_sw = [&](auto swc, const RawQK<PCPL>& R, bf16* s_qh, bf16* s_kb, float* s_dec,
-                          const float* s_bet) {
+                          const float* s_bet) __attribute__((always_inline)) {
     constexpr int sw = decltype(swc)::value;
     constexpr int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
     float f[5][PCPL], dec[PCPL];
@@ -596,7 +600,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 
   // State pass: only Kbar and the decay.
   auto produce_kb_sw = [&](auto swc, const RawQK<PCPL>& R, bf16* s_kb, float* s_dec,
-                           const float* s_bet) {
+                           const float* s_bet) __attribute__((always_inline)) {
     constexpr int sw = decltype(swc)::value;
     float f1[PCPL], dec[PCPL];
 #pragma unroll
@@ -621,7 +625,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   };
 
   auto produce_a = [&](const RawQK<PCPL>& R, bf16* s_qh, bf16* s_kb, float* s_dec,
-                       const float* s_bet) {
+                       const float* s_bet) __attribute__((always_inline)) {
     if constexpr (kState) {
       switch (sw) {
         case 0: produce_kb_sw(IntC<0>{}, R, s_kb, s_dec, s_bet); break;
@@ -641,7 +645,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 
   // ---- producer, second half: V of the chunk, token-major (the consumers
   // read it transposed).
-  auto produce_b = [&](const uint32_t (&V)[4][PVPL / 2]) {
+  auto produce_b = [&](const uint32_t (&V)[4][PVPL / 2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16* dst = s_v + (tok0 + i) * VP + vch0;
@@ -655,7 +659,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // ---- consumer, second half of step c: o^T = S^T Q^^T for chunk c (S holds
   // the state after chunk c-1 by then); kept in registers until the first
   // half of step c+1 adds V^T A^T. Contraction over Dk in steps of 32.
-  auto consume_inter = [&](const f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET]) {
+  auto consume_inter = [&](const f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -688,17 +692,17 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // the chunk, read transposed from token-major tiles: lane lr gets column
   // c0(lr / 4 ...) as set by the supplying lanes (see tr4).
   const int trow = 8 * gq + (lr >> 2);  // token supplied by this lane, + 32 m2 (+ 4)
-  auto vT_op = [&](int m2, int et) {    // V^T rows e0 + ecol(et, lr)
+  auto vT_op = [&](int m2, int et) __attribute__((always_inline)) {    // V^T rows e0 + ecol(et, lr)
     const bf16* p = s_v + (32 * m2 + trow) * VP + e0 + 4 * ET * (lr & 3) + 4 * et;
     return join_tr(tr4(p), tr4(p + 4 * VP));
   };
-  auto kbT_op = [&](const bf16* s_kb, int m2, int dt) {  // Kbar^T rows 16 dt + lr
+  auto kbT_op = [&](const bf16* s_kb, int m2, int dt) __attribute__((always_inline)) {  // Kbar^T rows 16 dt + lr
     const bf16* p = s_kb + (32 * m2 + trow) * RP + 16 * dt + 4 * (lr & 3);
     return join_tr(tr4(p), tr4(p + 4 * RP));
   };
   // S = diag(2^{b_C}) S + Kbar^T V (the decay also multiplies into Dacc when
   // given: the state pass keeps the run's product of decays).
-  auto state_update = [&](f32x4 (&S)[DT][ET], f32x4* Dacc, const bf16* s_kb, const float* s_dec) {
+  auto state_update = [&](f32x4 (&S)[DT][ET], f32x4* Dacc, const bf16* s_kb, const float* s_dec) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const f32x4 dec = *reinterpret_cast<const f32x4*>(s_dec + 16 * dt + 4 * gq);
@@ -727,7 +731,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   };
 
   auto consume_finish = [&](f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET], uint32_t (&opk)[4][2 * ET],
-                            const bf16* s_kb, const float* s_dec) {
+                            const bf16* s_kb, const float* s_dec) __attribute__((always_inline)) {
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
       bf16x8 va[ET], aa[4];
@@ -756,7 +760,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 
   // ---- Dv = 128, consumer, end of the first half of step c+1: the packed
   // outputs of chunk c to the LDS stage (the producers store them).
-  auto stage_out = [&](const uint32_t (&opk)[4][2 * ET]) {
+  auto stage_out = [&](const uint32_t (&opk)[4][2 * ET]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int row = 16 * t + lr, chunk = 4 * ci + gq;  // channels e0 + 8 gq .. + 7
@@ -767,7 +771,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // ---- Dv = 128, producer, second half of step c+1: chunk c's outputs from
   // the stage, whole rows per store (producer w: the rows of sub-chunk w, 16
   // lanes per 256-byte row); rows past the chunk end are dropped by the range.
-  auto store_rows = [&](int c) {
+  auto store_rows = [&](int c) __attribute__((always_inline)) {
     const int64_t p0 = start + int64_t(c) * kC;
     const int Lc = chunk_len(c);
     const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // ---- Dv = 64, consumer, second half of step c+1: the outputs of chunk c
   // packed in the first half. Issuing the stores here keeps them off the first
   // half, where the producers' loads fill the vector memory queue.
-  auto store_out = [&](const uint32_t (&opk)[4][2 * ET], int c) {
+  auto store_out = [&](const uint32_t (&opk)[4][2 * ET], int c) __attribute__((always_inline)) {
     const int64_t p0 = start + int64_t(c) * kC;
     const int Lc = chunk_len(c);
     const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
@@ -806,7 +810,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // Consumer ci takes jobs ci, ci + 4 and ci + 8 (the producers, whose work
   // per chunk sets the pace, take none). Zero jobs run on a valid slot and
   // their result is replaced, so no job branches.
-  auto a_blocks = [&](const float* s_bet) {
+  auto a_blocks = [&](const float* s_bet) __attribute__((always_inline)) {
 #pragma unroll
     for (int jj = 0; jj < 3; ++jj) {
       const int job = ci + 4 * jj;
@@ -857,32 +861,47 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       scan(R, QA);
       load_g(R, 1);
       __syncthreads();
-      for (int s = 0; s <= nchunks; s += 2) {
-        // even chunk s: LDS buffers 0; odd chunk s + 1: buffers 1
+      // Steps s = 0 .. nchunks (step s prepares chunk s and finishes chunk
+      // s - 1): even steps use LDS buffers 0, odd steps buffers 1; two steps
+      // per iteration (the q, k register sets alternate), the last even step
+      // peeled, so the loop exits only at its bottom. Where a step skips the
+      // use of loaded registers (an item's last chunks) it waits for its
+      // loads instead: the compiler's wait bookkeeping merges the paths of a
+      // step, and a load left pending on a rare path would otherwise make
+      // every step's first LDS reads wait for the previous step's loads.
+      auto step_even = [&](int s) __attribute__((always_inline)) {
         load_qk(QB, s + 1);
         if (s < nchunks) produce_a(QA, s_qh, s_kb0, s_decay, s_beta);
         if (beta_wave) bnext2 = load_beta(s + 2);
         __syncthreads();
         if (!kState && C::stage_o && s >= 1) store_rows(s - 1);
-        if (s < nchunks) produce_b(R.v);
+        if (s < nchunks) produce_b(R.v); else wait_vm_all();
         load_v(R, s + 1);
         if (beta_wave) s_beta[kC + lane] = __uint_as_float(bnext << 16);
-        if (s + 1 < nchunks) scan(R, QB);
+        if (s + 1 < nchunks) scan(R, QB); else wait_vm_all();
         load_g(R, s + 2);
         __syncthreads();
-        if (s + 1 > nchunks) break;
+      };
+      auto step_odd = [&](int s) __attribute__((always_inline)) {  // step s + 1
         load_qk(QA, s + 2);
         if (s + 1 < nchunks) produce_a(QB, s_qh, s_kb1, s_decay + DK, s_beta + kC);
         if (beta_wave) bnext = load_beta(s + 3);
         __syncthreads();
         if (!kState && C::stage_o) store_rows(s);
-        if (s + 1 < nchunks) produce_b(R.v);
+        if (s + 1 < nchunks) produce_b(R.v); else wait_vm_all();
         load_v(R, s + 2);
         if (beta_wave) s_beta[lane] = __uint_as_float(bnext2 << 16);
-        if (s + 2 < nchunks) scan(R, QA);
+        if (s + 2 < nchunks) scan(R, QA); else wait_vm_all();
         load_g(R, s + 3);
         __syncthreads();
+      };
+      int s = 0;
+      for (; s + 1 <= nchunks; s += 2) {
+        step_even(s);
+        step_odd(s);
       }
+      if (s <= nchunks) step_even(s);
+      wait_vm_all();
       // every thread has read this item's number before the item's first barrier
       if (tid == 0) *s_item = next;
       __syncthreads();
