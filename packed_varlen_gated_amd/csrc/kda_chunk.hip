@@ -16,18 +16,20 @@
 //   S_new  = diag(2^{b_C}) S_prev + sum_s (beta_s k_s 2^{b_C - b_s}) v_s^T
 // Stable exponents: the chunk is cut into four 16-token sub-chunks; rho_j is
 // the cumsum before sub-chunk j and T_j its total. Block (w, j) of A (rows in
-// sub-chunk w, columns in sub-chunk j <= w) pairs the key factor
-// KE_s = k_s 2^{rho_{j+1} - b_s} (<= 1) with the query factor
+// sub-chunk w, columns in sub-chunk j <= w) splits 2^{b_r - b_s} at
+// rho_{j+1}: key factor KE_s = k_s 2^{rho_{j+1} - b_s} (<= 1), query factor
 // q_r 2^{b_r - rho_{j+1}} (<= 1 off the diagonal, <= 2^{16 max|g| log2 e} on
-// it). Per element only 2^{c} and 2^{T - c} are evaluated (c = in-sub-chunk
-// cumsum); every other factor is per channel.
+// it); off the diagonal the query factor is Q~_r = q_r 2^{b_r - rho_w} times
+// 2^{rho_w - rho_{j+1}} (<= 1), which goes on either operand. Per element only
+// 2^{c} and 2^{T - c} are evaluated (c = in-sub-chunk cumsum); every other
+// factor is per channel.
 //
 // A work-group runs one (run, head) item at a time: 4 producer waves and 4
 // consumer waves, software-pipelined over chunks (two barriers per chunk step):
 //   first half  P: chunk c: per-channel factors from the sub-chunk totals,
 //                  Q^ = q 2^b and Kbar^T = (beta k 2^{b_C - b})^T to the LDS
-//                  buffers of c's parity, the query versions of the ten A
-//                  blocks, KE, and 2^{b_C}.
+//                  buffers of c's parity, the operand versions of the ten
+//                  A blocks, KE, and 2^{b_C}.
 //               C: chunk c-1: o^T += V^T A^T for its Dv/4 columns, packed;
 //                  S = diag(2^{b_C}) S + Kbar^T V.
 //   second half P: V of chunk c; the in-sub-chunk cumulative gates of chunk
@@ -80,9 +82,9 @@ constexpr int kMaxRuns = 16;      // runs per segment
 constexpr int kPlanHeader = 64;   // int32 words before the run table
 constexpr int kPlanCache = 8192;  // segment slots whose chunk counts the plan keeps in LDS
 
-// A blocks (row sub-chunk w, column sub-chunk j), j <= w, in this order; the
-// query version of block b lives in LDS slot b. Jobs 10 and 11 zero the blocks
-// (0, 1) and (2, 3), which the A.V product reads through its 32-wide steps.
+// A blocks (row sub-chunk w, column sub-chunk j), j <= w, in this order (the
+// jobs of the consumer waves). Jobs 10 and 11 zero the blocks (0, 1) and
+// (2, 3), which the A.V product reads through its 32-wide steps.
 __device__ __forceinline__ void block_of(int b, int& w, int& j) {
   if (b < 1) { w = 0; j = 0; }
   else if (b < 3) { w = 1; j = b - 1; }
@@ -122,7 +124,7 @@ struct Cfg {
   static constexpr int off_kb = off_v + kC * VP * 2;         // Kbar, bf16 [2][kC][RP]
   static constexpr int off_qh = off_kb + 2 * kC * RP * 2;    // Q^, bf16 [kC][KP]
   static constexpr int off_ke = off_qh + kC * KP * 2;        // KE, bf16 [kC][KP]
-  static constexpr int off_qv = off_ke + kC * KP * 2;        // query versions, bf16 [10][16][KP]
+  static constexpr int off_qv = off_ke + kC * KP * 2;        // A-block operand versions, bf16 [10][16][KP]
   // Dv = 128: outputs staged through LDS, bf16 [kC][DV], 16-byte chunk c of
   // row r at chunk c ^ (r % 16) (conflict-free both ways, no padding room)
   static constexpr bool stage_o = DV == 128;
@@ -535,26 +537,31 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // ---- producer, first half: factors and MFMA operands of one chunk from
   // its Q~ and KE. With T_j the sub-chunk totals of a channel and
   // E_j = 2^{T_j} (from s_T): f0 = 2^{T_0 + .. + T_{w-1}} (Q^ = Q~ f0),
-  // f1 = 2^{T_{w+1} + .. + T_3} (Kbar = beta KE f1), f2 = 2^{-T_w} (diagonal
-  // version), f3 = 2^{T_{w-1}} (block (w, w-2)), f4 = 2^{T_{w-1} + T_{w-2}}
-  // (block (3, 0)), decay = 2^{T_0 + .. + T_3}: products of the E_j and one
-  // reciprocal. KE, the version of block (w, w-1) (Q~ itself) and, for w = 0,
-  // Q^ are stored as they are. The sub-chunk index is a compile-time constant
-  // inside (one instance per sub-chunk), so every choice below is resolved
-  // without branches.
+  // f1 = 2^{T_{w+1} + .. + T_3} (Kbar = beta KE f1), f2 = 2^{-T_w} (the
+  // diagonal block's query version), decay = 2^{T_0 + .. + T_3}: products of
+  // the E_j and one reciprocal. Block (w, j < w) of A needs the factor
+  // 2^{T_{j+1} + .. + T_{w-1}} on one of its operands (none for j = w - 1);
+  // it goes where the producers' work evens out: producer 0 stores KE 2^{T_1}
+  // (block (2, 0)), producer 1 KE 2^{T_2} (block (3, 1)), producer 3 the
+  // query version Q~ 2^{T_1 + T_2} (block (3, 0)), and every other
+  // off-diagonal block pairs KE with Q~ itself. Version slots (16 rows each):
+  // 0..3 the diagonal query versions of sub-chunks 0..3, 4..6 Q~ of
+  // sub-chunks 1..3, 7 and 9 those two key versions, 8 that query version.
+  // KE, Q~ and, for w = 0, Q^ are stored as they are. The
+  // sub-chunk index is a compile-time constant inside (one instance per
+  // sub-chunk), so every choice below is resolved without branches.
   auto produce_a_sw = [&](auto swc, const RawQK<PCPL>& R, bf16* s_qh, bf16* s_kb, float* s_dec,
                           const float* s_bet) __attribute__((always_inline)) {
     constexpr int sw = decltype(swc)::value;
-    constexpr int vbase = (sw * (sw + 1)) / 2;  // LDS slot of block (sw, 0)
-    float f[5][PCPL], dec[PCPL];
+    float f[3][PCPL], gk[2][PCPL], dec[PCPL];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
       const f32x4 E = *reinterpret_cast<const f32x4*>(s_T + (ch0 + c + cg) * 4);
       f[0][c] = sw == 0 ? 1.f : sw == 1 ? E[0] : sw == 2 ? E[0] * E[1] : (E[0] * E[1]) * E[2];
       f[1][c] = sw == 3 ? 1.f : sw == 2 ? E[3] : sw == 1 ? E[2] * E[3] : E[1] * (E[2] * E[3]);
       f[2][c] = __builtin_amdgcn_rcpf(E[sw]);
-      f[3][c] = sw >= 1 ? E[sw >= 1 ? sw - 1 : 0] : 0.f;
-      f[4][c] = sw >= 2 ? E[sw >= 1 ? sw - 1 : 0] * E[sw >= 2 ? sw - 2 : 0] : 0.f;
+      gk[0][c] = sw == 0 ? E[1] : E[2];
+      gk[1][c] = E[1] * E[2];  // sub-chunk 3's query version of block (3, 0)
       dec[c] = (E[0] * E[1]) * (E[2] * E[3]);
     }
     if (sw == 0 && tq == 0) {
@@ -567,12 +574,13 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     for (int i = 0; i < 4; ++i) {
       const int tok = tok0 + i;
       const float bt = bt4[i];
-      float qt[PCPL], t0[PCPL], kb[PCPL];
+      float qt[PCPL], kt[PCPL], t0[PCPL], kb[PCPL];
 #pragma unroll
       for (int c = 0; c < PCPL; ++c) {
         qt[c] = bf(R.q[i], c);
+        kt[c] = bf(R.k[i], c);
         t0[c] = qt[c] * f[0][c];
-        kb[c] = bf(R.k[i], c) * (bt * f[1][c]);
+        kb[c] = kt[c] * (bt * f[1][c]);
       }
       if constexpr (sw == 0)
         stw<PCPL>(s_qh + tok * KP + ch0, R.q[i]);
@@ -583,17 +591,17 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       bf16* qv = s_qv + (tok & 15) * KP + ch0;  // row of the token in each version slot
 #pragma unroll
       for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[2][c];
-      stn<PCPL>(qv + (vbase + sw) * 16 * KP, t0);
-      if constexpr (sw >= 1) stw<PCPL>(qv + (vbase + sw - 1) * 16 * KP, R.q[i]);
-      if constexpr (sw >= 2) {
+      stn<PCPL>(qv + sw * 16 * KP, t0);
+      if constexpr (sw >= 1) stw<PCPL>(qv + (3 + sw) * 16 * KP, R.q[i]);
+      if constexpr (sw <= 1) {
 #pragma unroll
-        for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[3][c];
-        stn<PCPL>(qv + (vbase + sw - 2) * 16 * KP, t0);
+        for (int c = 0; c < PCPL; ++c) t0[c] = kt[c] * gk[0][c];
+        stn<PCPL>(qv + (sw == 0 ? 7 : 9) * 16 * KP, t0);
       }
       if constexpr (sw == 3) {
 #pragma unroll
-        for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * f[4][c];
-        stn<PCPL>(qv + (vbase + 0) * 16 * KP, t0);
+        for (int c = 0; c < PCPL; ++c) t0[c] = qt[c] * gk[1][c];
+        stn<PCPL>(qv + 8 * 16 * KP, t0);
       }
     }
   };
@@ -808,31 +816,78 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // Jobs 0..9 are the blocks (w, j <= w), jobs 10 and 11 zero the blocks
   // (0, 1) and (2, 3) that the A.V product reads through its 32-wide steps.
   // Consumer ci takes jobs ci, ci + 4 and ci + 8 (the producers, whose work
-  // per chunk sets the pace, take none). Zero jobs run on a valid slot and
-  // their result is replaced, so no job branches.
-  auto a_blocks = [&](const float* s_bet) __attribute__((always_inline)) {
+  // per chunk sets the pace of the first half, take none). Zero jobs run on a
+  // valid slot and their result is replaced, so no job branches.
+  // a_blocks_mma does the products of all three jobs (their LDS operand reads
+  // can all be in flight together); a_blocks_store masks, scales by beta and
+  // writes them to the A tile. Keeping every write after every read of the
+  // half lets the compiler overlap the reads: it cannot tell the A tile from
+  // the operand tiles, so a write would hold back every later read.
+  // Operand tiles (16 rows each) of the consumer's three jobs: the keys (KE
+  // rows, or a key version slot) and the queries (a version slot).
+  const bf16* a_key[3];
+  const bf16* a_qry[3];
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj) {
+    int ks = -1, qs = 0;  // key slot (-1: KE rows of block column j), query slot
+    int bw, bj;
+    block_of(ci + 4 * jj, bw, bj);
+    switch (ci + 4 * jj) {
+      case 0: qs = 0; break;            // (0, 0)
+      case 1: qs = 4; break;            // (1, 0)
+      case 2: qs = 1; break;            // (1, 1)
+      case 3: ks = 7; qs = 5; break;    // (2, 0): KE 2^{T_1}
+      case 4: qs = 5; break;            // (2, 1)
+      case 5: qs = 2; break;            // (2, 2)
+      case 6: qs = 8; break;            // (3, 0): Q~ 2^{T_1 + T_2}
+      case 7: ks = 9; qs = 6; break;    // (3, 1): KE 2^{T_2}
+      case 8: qs = 6; break;            // (3, 2)
+      case 9: qs = 3; break;            // (3, 3)
+      default: qs = 0; break;           // zero jobs: any valid tiles
+    }
+    a_key[jj] = ks < 0 ? s_ke + 16 * bj * KP : s_qv + ks * 16 * KP;
+    a_qry[jj] = s_qv + qs * 16 * KP;
+  }
+  auto a_blocks_mma = [&](f32x4 (&ab)[3]) __attribute__((always_inline)) {
+    // operands of K step u for the three jobs, read two steps ahead of their
+    // products (the schedule is pinned: left to itself, the compiler keeps
+    // one read pair in flight at a time here)
+    bf16x8 op[2][3][2];
+    auto read = [&](int u, bf16x8 (&o)[3][2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj) {
+        const int col = 32 * u + 8 * gq;
+        o[jj][0] = *reinterpret_cast<const bf16x8*>(a_key[jj] + lr * KP + col);
+        o[jj][1] = *reinterpret_cast<const bf16x8*>(a_qry[jj] + lr * KP + col);
+      }
+    };
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) ab[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    read(0, op[0]);
+    if constexpr (KS > 1) read(1, op[1]);
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj) ab[jj] = mfma(op[u & 1][jj][0], op[u & 1][jj][1], ab[jj]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + 2 < KS) read(u + 2, op[u & 1]);
+    }
+  };
+  auto a_blocks_store = [&](const f32x4 (&ab)[3], const float* s_bet) __attribute__((always_inline)) {
 #pragma unroll
     for (int jj = 0; jj < 3; ++jj) {
       const int job = ci + 4 * jj;
       int bw, bj;
       block_of(job, bw, bj);
       const bool real = job < 10;
-      const int slot = real ? job : 0;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < KS; ++u) {
-        const int col = 32 * u + 8 * gq;
-        const bf16x8 aop = *reinterpret_cast<const bf16x8*>(s_ke + (16 * bj + lr) * KP + col);
-        const bf16x8 bop = *reinterpret_cast<const bf16x8*>(s_qv + (slot * 16 + lr) * KP + col);
-        acc = mfma(aop, bop, acc);
-      }
       const f32x4 bt = *reinterpret_cast<const f32x4*>(s_bet + 16 * bj + 4 * gq);
       float out[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sl = 4 * gq + i;
         const bool keep = real && ((bj < bw) || (sl <= lr));
-        out[i] = keep ? acc[i] * bt[i] : 0.f;
+        out[i] = keep ? ab[jj][i] * bt[i] : 0.f;
       }
       st4(s_a + (16 * bw + lr) * TP + 16 * bj + 4 * gq, out);
     }
@@ -997,8 +1052,10 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
           __syncthreads();
           if (!C::stage_o && s >= 1) store_out(opk, s - 1);
           if (s < nchunks) {
-            a_blocks(s_beta);
+            f32x4 ab[3];
+            a_blocks_mma(ab);
             consume_inter(S, acc);
+            a_blocks_store(ab, s_beta);
           }
           __syncthreads();
           if (s + 1 > nchunks) break;
@@ -1007,8 +1064,10 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
           __syncthreads();
           if constexpr (!C::stage_o) store_out(opk, s);
           if (s + 1 < nchunks) {
-            a_blocks(s_beta + kC);
+            f32x4 ab[3];
+            a_blocks_mma(ab);
             consume_inter(S, acc);
+            a_blocks_store(ab, s_beta + kC);
           }
           __syncthreads();
         }
