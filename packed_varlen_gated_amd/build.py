@@ -30,6 +30,11 @@ COMMON_FLAGS = [
     "-Wno-unused-function",
     # keep the compiler away from packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # atomics stay single instructions: the compiler's wave-level rewrite of
+    # a uniform-address atomic broadcasts its result at once, which makes the
+    # issuing wave wait for the atomic where it is issued (the chunk kernels
+    # claim their next work item a step before they use it)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -334,9 +334,12 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 
   // Persistent work-groups: each takes (run, head) items from the plan's
   // queue, a counter the plan kernel resets, in the plan's order (longest
-  // run first, heads of a run together; item = rank * H + h). The next item
-  // is claimed when the current one starts, so the claim's latency hides
-  // behind the item's first loads.
+  // run first, heads of a run together; item = rank * H + h). A work-group
+  // claims its next item one step before the current one ends: the queue is
+  // then served in the order work-groups free up, which is what makes the
+  // longest-first order balance the load (a claim at the item's start pairs
+  // each item with the one claimed after it), and the claim's latency still
+  // hides behind the last step.
   int* s_item = reinterpret_cast<int*>(tile(C::off_item));
   int32_t* const counter = plan + (kState ? 3 : 2);
   const int n_items = (kState ? plan[1] : plan[0]) * H;
@@ -487,32 +490,41 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
         rk[i] = __builtin_amdgcn_rsqf(row_sum16(sk) + kL2NormEps);
       }
     }
-    float cs[4][PCPL], tot[PCPL];
+    // One exponential per gate element, 2^{g log2 e}; the factors are its
+    // products: 2^{c} over the tokens up to and including this one, 2^{T - c}
+    // over the tokens after it, 2^T over the sub-chunk. In-lane over the
+    // lane's 4 tokens, then across the four token groups (the four rows of 16
+    // lanes): row pairs through v_permlane16_swap, pair products through
+    // v_permlane32_swap.
+    float fq[4][PCPL], fk[4][PCPL], tot[PCPL];
 #pragma unroll
     for (int c = 0; c < PCPL; ++c) {
-      float run = 0.f;
+      float e[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        run = fmaf(bf(R.g[i], c), kLog2e, run);
-        cs[i][c] = run;
-      }
-      // prefix over the four token groups of the sub-chunk (the four rows of
-      // 16 lanes): row pairs through v_permlane16_swap, then the pair totals
-      // through v_permlane32_swap
-      const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(run), __float_as_uint(run), false, false);
-      const float pair = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // rows 2m and 2m + 1
-      const float s1 = (tq & 1) ? pair : run;
+      for (int i = 0; i < 4; ++i) e[i] = ex2(bf(R.g[i], c) * kLog2e);
+      const float p1 = e[0] * e[1], p2 = p1 * e[2], row = p2 * e[3];  // in-lane prefix products
+      const float s1 = e[2] * e[3], s0 = e[1] * s1;                  // in-lane suffix products
+      const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(row), __float_as_uint(row), false, false);
+      const float even = __uint_as_float(pr[0]), odd = __uint_as_float(pr[1]);  // rows 2m, 2m + 1
+      const float pair = even * odd;
       const auto pt = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
       const float lo = __uint_as_float(pt[0]), hi = __uint_as_float(pt[1]);  // rows 0-1, rows 2-3
-      const float inc = s1 + (tq >= 2 ? lo : 0.f);
-      const float excl = inc - run;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cs[i][c] += excl;
-      tot[c] = lo + hi;  // the sub-chunk total, in every lane
+      // products over the rows before / after this lane's row
+      const float before = ((tq & 1) ? even : 1.f) * (tq >= 2 ? lo : 1.f);
+      const float after = ((tq & 1) ? 1.f : odd) * (tq < 2 ? hi : 1.f);
+      fq[0][c] = before * e[0];
+      fq[1][c] = before * p1;
+      fq[2][c] = before * p2;
+      fq[3][c] = before * row;
+      fk[0][c] = after * s0;
+      fk[1][c] = after * s1;
+      fk[2][c] = after * e[3];
+      fk[3][c] = after;
+      tot[c] = lo * hi;  // 2^T, the same bits in every lane
     }
     if (tq == 3) {
 #pragma unroll
-      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c + cg) * 4 + sw] = ex2(tot[c]);  // + cg: the table's padding
+      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c + cg) * 4 + sw] = tot[c];  // + cg: the table's padding
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -520,15 +532,11 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       for (int c = 0; c < PCPL; c += 2) {
         if constexpr (kNorm) {
           if constexpr (!kState)
-            X.q[i][c >> 1] = pk2((bf(X.q[i], c) * rq[i]) * ex2(cs[i][c]),
-                                 (bf(X.q[i], c + 1) * rq[i]) * ex2(cs[i][c + 1]));
-          X.k[i][c >> 1] = pk2((bf(X.k[i], c) * rk[i]) * ex2(tot[c] - cs[i][c]),
-                               (bf(X.k[i], c + 1) * rk[i]) * ex2(tot[c + 1] - cs[i][c + 1]));
+            X.q[i][c >> 1] = pk2((bf(X.q[i], c) * rq[i]) * fq[i][c], (bf(X.q[i], c + 1) * rq[i]) * fq[i][c + 1]);
+          X.k[i][c >> 1] = pk2((bf(X.k[i], c) * rk[i]) * fk[i][c], (bf(X.k[i], c + 1) * rk[i]) * fk[i][c + 1]);
         } else {
-          if constexpr (!kState)
-            X.q[i][c >> 1] = pk2(bf(X.q[i], c) * ex2(cs[i][c]), bf(X.q[i], c + 1) * ex2(cs[i][c + 1]));
-          X.k[i][c >> 1] = pk2(bf(X.k[i], c) * ex2(tot[c] - cs[i][c]),
-                               bf(X.k[i], c + 1) * ex2(tot[c + 1] - cs[i][c + 1]));
+          if constexpr (!kState) X.q[i][c >> 1] = pk2(bf(X.q[i], c) * fq[i][c], bf(X.q[i], c + 1) * fq[i][c + 1]);
+          X.k[i][c >> 1] = pk2(bf(X.k[i], c) * fk[i][c], bf(X.k[i], c + 1) * fk[i][c + 1]);
         }
       }
     }
@@ -899,7 +907,9 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   if (producer) {
     for (int item = first_item; item < n_items;) {
       int next = 0;
-      if (tid == 0) next = atomicAdd(counter, 1);
+      auto claim = [&](int s) __attribute__((always_inline)) {  // at step nchunks - 1
+        if (s == nchunks - 1 && tid == 0) next = atomicAdd(counter, 1);
+      };
       begin_item(item);
       Raw<PCPL, PVPL> R;
       RawQK<PCPL> QA, QB;  // q, k of even / odd chunks
@@ -925,6 +935,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       // step, and a load left pending on a rare path would otherwise make
       // every step's first LDS reads wait for the previous step's loads.
       auto step_even = [&](int s) __attribute__((always_inline)) {
+        claim(s);
         load_qk(QB, s + 1);
         if (s < nchunks) produce_a(QA, s_qh, s_kb0, s_decay, s_beta);
         if (beta_wave) bnext2 = load_beta(s + 2);
@@ -938,6 +949,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
         __syncthreads();
       };
       auto step_odd = [&](int s) __attribute__((always_inline)) {  // step s + 1
+        claim(s + 1);
         load_qk(QA, s + 2);
         if (s + 1 < nchunks) produce_a(QB, s_qh, s_kb1, s_decay + DK, s_beta + kC);
         if (beta_wave) bnext = load_beta(s + 3);
