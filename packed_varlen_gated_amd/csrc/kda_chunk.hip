@@ -905,43 +905,53 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // Producers and consumers run separate loops with the same barrier sequence
   // (two per step), so neither role keeps the other's registers live.
   if (producer) {
-    for (int item = first_item; item < n_items;) {
+    Raw<PCPL, PVPL> R;
+    RawQK<PCPL> QA, QB;  // q, k of even / odd chunks
+    const bool beta_wave = w == 0;
+    uint32_t b0 = 0;  // raw beta of an item's first chunk (wave 0)
+    // An item's first chunk: g, q, k and v to registers (R, QA), beta to b0.
+    // For every item but the first, issued in the previous item's last step.
+    auto load_first = [&]() __attribute__((always_inline)) {
+      load_g(R, 0);
+      load_qk(QA, 0);
+      load_v(R, 0);
+      if (beta_wave) b0 = load_beta(0);
+    };
+    int item = first_item;
+    if (item < n_items) {
+      begin_item(item);
+      load_first();
+    }
+    while (item < n_items) {
       int next = 0;
       auto claim = [&](int s) __attribute__((always_inline)) {  // at step nchunks - 1
         if (s == nchunks - 1 && tid == 0) next = atomicAdd(counter, 1);
       };
-      begin_item(item);
-      Raw<PCPL, PVPL> R;
-      RawQK<PCPL> QA, QB;  // q, k of even / odd chunks
-      const bool beta_wave = w == 0;
       uint32_t bnext = 0, bnext2 = 0;  // raw beta of the next chunks (wave 0)
-      load_g(R, 0);
-      load_qk(QA, 0);
-      load_v(R, 0);
       if (beta_wave) {
-        const uint32_t b0 = load_beta(0);
         bnext = load_beta(1);
         s_beta[lane] = __uint_as_float(b0 << 16);
       }
       scan(R, QA);
       load_g(R, 1);
       __syncthreads();
-      // Steps s = 0 .. nchunks (step s prepares chunk s and finishes chunk
-      // s - 1): even steps use LDS buffers 0, odd steps buffers 1; two steps
-      // per iteration (the q, k register sets alternate), the last even step
-      // peeled, so the loop exits only at its bottom. Where a step skips the
-      // use of loaded registers (an item's last chunks) it waits for its
-      // loads instead: the compiler's wait bookkeeping merges the paths of a
-      // step, and a load left pending on a rare path would otherwise make
-      // every step's first LDS reads wait for the previous step's loads.
+      // Steps s = 0 .. nchunks - 1 (step s prepares chunk s and finishes
+      // chunk s - 1): even steps use LDS buffers 0, odd steps buffers 1; two
+      // steps per iteration (the q, k register sets alternate), the last even
+      // step peeled, so the loop exits only at its bottom. Where a step skips
+      // the use of loaded registers (the scan of a chunk past the item) it
+      // waits for its loads instead: the compiler's wait bookkeeping merges
+      // the paths of a step, and a load left pending on a rare path would
+      // otherwise make every step's first LDS reads wait for the previous
+      // step's loads.
       auto step_even = [&](int s) __attribute__((always_inline)) {
         claim(s);
         load_qk(QB, s + 1);
-        if (s < nchunks) produce_a(QA, s_qh, s_kb0, s_decay, s_beta);
+        produce_a(QA, s_qh, s_kb0, s_decay, s_beta);
         if (beta_wave) bnext2 = load_beta(s + 2);
         __syncthreads();
         if (!kState && C::stage_o && s >= 1) store_rows(s - 1);
-        if (s < nchunks) produce_b(R.v); else wait_vm_all();
+        produce_b(R.v);
         load_v(R, s + 1);
         if (beta_wave) s_beta[kC + lane] = __uint_as_float(bnext << 16);
         if (s + 1 < nchunks) scan(R, QB); else wait_vm_all();
@@ -951,11 +961,11 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       auto step_odd = [&](int s) __attribute__((always_inline)) {  // step s + 1
         claim(s + 1);
         load_qk(QA, s + 2);
-        if (s + 1 < nchunks) produce_a(QB, s_qh, s_kb1, s_decay + DK, s_beta + kC);
+        produce_a(QB, s_qh, s_kb1, s_decay + DK, s_beta + kC);
         if (beta_wave) bnext = load_beta(s + 3);
         __syncthreads();
         if (!kState && C::stage_o) store_rows(s);
-        if (s + 1 < nchunks) produce_b(R.v); else wait_vm_all();
+        produce_b(R.v);
         load_v(R, s + 2);
         if (beta_wave) s_beta[lane] = __uint_as_float(bnext2 << 16);
         if (s + 2 < nchunks) scan(R, QA); else wait_vm_all();
@@ -963,16 +973,25 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
         __syncthreads();
       };
       int s = 0;
-      for (; s + 1 <= nchunks; s += 2) {
+      for (; s + 2 <= nchunks; s += 2) {
         step_even(s);
         step_odd(s);
       }
-      if (s <= nchunks) step_even(s);
-      wait_vm_all();
-      // every thread has read this item's number before the item's first barrier
+      if (s < nchunks) step_even(s);
+      // Step nchunks (the consumers finish the last chunk): the claimed item
+      // number goes to LDS (every wave reads it after the barrier; the
+      // consumers read it after this step), the last chunk's outputs are
+      // stored, and the next item's first chunk is loaded, so its latency
+      // overlaps this step and the consumers' end of the item.
       if (tid == 0) *s_item = next;
       __syncthreads();
+      if (!kState && C::stage_o) store_rows(nchunks - 1);
       item = __builtin_amdgcn_readfirstlane(*s_item);
+      if (item < n_items) {
+        begin_item(item);
+        load_first();
+      }
+      __syncthreads();
     }  // item loop
   } else {
     // Run states and decays in the workspace: slot j, head h holds S as the
@@ -1094,7 +1113,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
                 fs[int64_t(16 * dt + 4 * gq + i) * DV + e0 + ecol(et, lr)] = S[dt][et][i];
         }
       }
-      __syncthreads();
+      // written by the producers before the last step's first barrier
       item = __builtin_amdgcn_readfirstlane(*s_item);
     }  // item loop
   }
