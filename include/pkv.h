@@ -81,6 +81,14 @@ typedef enum {
 #define PKV_FLAG_BAD_CU_SEQLENS 4  /* chunk_kda_varlen saw cu[0] != 0, a
                                       decreasing pair or cu[i] > N; the outputs
                                       of the offending segments are undefined */
+#define PKV_FLAG_GATE_RANGE 8      /* a chunked bf16 call met a 16-token
+                                      sub-chunk whose gates sum below
+                                      -120 ln 2 (about -83) on some key
+                                      channel: its factor 2^(-sum log2 e) can
+                                      leave the fp32 / bf16 range, so that
+                                      (segment, head)'s results may be inf,
+                                      NaN or inaccurate; the token-serial
+                                      fp32 path is not limited this way */
 
 /* Bits of the `options` argument of the recurrence's entry points. */
 #define PKV_OPT_QK_L2NORM 1        /* RFC-0026 section 3.3's use_qk_l2norm_in_kernel:
@@ -203,16 +211,19 @@ size_t pkv_chunk_kda_varlen_workspace_size(int64_t N, int32_t H, int32_t Dk, int
  *             q, k, v, g, o, initial_state and final_state must be 16-byte
  *             aligned, beta aligned to its element size.
  * final_state float32 [max_segs, H, Dk, Dv] or NULL (not written).
- * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in.
+ * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS and, on the chunked
+ *             bf16 path, PKV_FLAG_GATE_RANGE are OR-ed in.
  * workspace   device buffer of at least pkv_chunk_kda_varlen_workspace_size()
  *             bytes, 16-byte aligned (NULL allowed when that size is 0);
  *             contents are scratch, overwritten by every call, so calls that
  *             share a workspace must be ordered on one stream. After the
  *             call its int32 words 0 and 1 hold the number of runs and of
  *             runs whose state was saved for the next piece (diagnostics).
- * Supported: Dk, Dv in {32, 64, 128}. Inputs with large positive g or with
- * 16 * max|g| beyond ~60 within a segment may lose accuracy (the chunked
- * factorisation bounds exponents per 16-token sub-chunk).
+ * Supported: Dk, Dv in {32, 64, 128}. The chunked bf16 path bounds exponents
+ * per 16-token sub-chunk: gates whose sum over 16 consecutive tokens of a
+ * segment falls below about -83 on some key channel are reported with
+ * PKV_FLAG_GATE_RANGE; large positive g (outside the recurrence's decay
+ * range) may lose accuracy unreported.
  * Errors: PKV_ERR_INVALID_ARGUMENT for NULL tensors, N < 1, N > INT32_MAX,
  * H < 1, max_segs < 1 (with cu_seqlens), max_segs * H > 2^22, a misaligned
  * tensor or o aliasing an input; PKV_ERR_UNSUPPORTED for other Dk/Dv, dtype or
@@ -272,6 +283,8 @@ pkv_status pkv_chunk_kda_varlen_noalloc(const void* q, const void* k, const void
  *             (one dtype); segment_ids int32 [B, T]; options as for
  *             pkv_chunk_kda_varlen.
  * initial_state, final_state  float32 [B, H, Dk, Dv] or NULL; must not overlap.
+ * flags       int32 [1] or NULL; PKV_FLAG_GATE_RANGE is OR-ed in as for
+ *             pkv_chunk_kda_varlen.
  * workspace   at least pkv_chunk_kda_segment_ids_workspace_size() bytes,
  *             16-byte aligned; scratch, as for pkv_chunk_kda_varlen (the
  *             segment starts found in the ids are kept there).
@@ -309,7 +322,8 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
  *             outputs, all written, none overlapping an input or each other.
  * d_initial_state float32 [max_segs, H, Dk, Dv] or NULL (not written).
  * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in (the
- *             gradients of an invalid slot are then left unwritten).
+ *             gradients of an invalid slot are then left unwritten), and on
+ *             the chunked path PKV_FLAG_GATE_RANGE as in the forward call.
  * The reverse pass recomputes the states (nothing is saved by the forward
  * call). For bf16 with Dk, Dv in {64, 128} it is chunked: the workspace holds
  * the work plan (chunk, piece and summary offsets per slot), the bf16 state

@@ -29,6 +29,7 @@ PKV_F32 = 1
 FLAG_OVERFLOW = 1
 FLAG_LEADING_PAD = 2
 FLAG_BAD_CU_SEQLENS = 4
+FLAG_GATE_RANGE = 8
 OPT_QK_L2NORM = 1
 
 _lib = None

@@ -22,6 +22,14 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf1
 constexpr int32_t kFlagOverflow = 1;
 constexpr int32_t kFlagLeadingPad = 2;
 constexpr int32_t kFlagBadCuSeqlens = 4;
+constexpr int32_t kFlagGateRange = 8;
+// The chunked bf16 paths split each 64-token chunk into 16-token sub-chunks
+// and put 2^{-(sum of a sub-chunk's log2 gates)} on one operand of its
+// diagonal block (the forward's query side, the reverse pass's key side).
+// Below this total (log2 units; 2^-120 as a factor) that operand can leave
+// the fp32 / bf16 range, and the call sets kFlagGateRange.
+constexpr float kGateRangeMinLog2 = -120.f;
+constexpr float kGateRangeMin = 0x1p-120f;  // 2^kGateRangeMinLog2
 
 // Launchers (host side). Each returns the HIP error of its launch(es).
 hipError_t launch_cu_seqlens(const int32_t* seg, int64_t N, int64_t T, int32_t max_segs,

@@ -303,7 +303,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     int32_t H, float scale, const float* __restrict__ initial_state, bf16* __restrict__ o,
     float* __restrict__ final_state, float* __restrict__ run_states,
     float* __restrict__ run_decays, int64_t row_len, const int32_t* __restrict__ seg_ids,
-    const int32_t* __restrict__ n_dev, int32_t lds_zero) {
+    const int32_t* __restrict__ n_dev, int32_t* __restrict__ flags, int32_t lds_zero) {
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
   constexpr int PCPL = C::PCPL, PVPL = C::PVPL, ET = C::ET, DT = C::DT, KS = C::KS;
@@ -473,6 +473,8 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // the cumsums, stay live until the first half; s_T gets 2^T of every
   // sub-chunk (the next half's factors are products of those). The state
   // pass has no q and folds k only.
+  // smallest 2^T the producer's scans met (the gate-range check)
+  float tmin = 1.f;
   auto scan = [&](const Raw<PCPL, PVPL>& R, RawQK<PCPL>& X) __attribute__((always_inline)) {
     // kNorm: 1 / sqrt(|x|^2 + eps) of each token's q and k; the 16 lanes of a
     // row hold the token's Dk channels, PCPL each
@@ -524,7 +526,10 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     }
     if (tq == 3) {
 #pragma unroll
-      for (int c = 0; c < PCPL; ++c) s_T[(ch0 + c + cg) * 4 + sw] = tot[c];  // + cg: the table's padding
+      for (int c = 0; c < PCPL; ++c) {
+        s_T[(ch0 + c + cg) * 4 + sw] = tot[c];  // + cg: the table's padding
+        tmin = fminf(tmin, tot[c]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -993,6 +998,8 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       }
       __syncthreads();
     }  // item loop
+    if (flags != nullptr && tmin < kGateRangeMin)
+      atomicOr(flags, kFlagGateRange);
   } else {
     // Run states and decays in the workspace: slot j, head h holds S as the
     // consumers keep it (consumer ci, tile (dt, et), lane: one f32x4 each)
@@ -1429,14 +1436,14 @@ hipError_t launch_dims(const Launch& a) {
     hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true, kNorm>), dim3(grid), dim3(C::NT), state_bytes,
                        a.stream, qp, kp, vp, gp, bp, a.cu, plan, int32_t(L.runs_max), a.max_segs, a.N,
                        a.H, a.scale, static_cast<const float*>(nullptr), static_cast<bf16*>(nullptr),
-                       static_cast<float*>(nullptr), states, decays, a.row_len, a.seg_ids, a.n_dev, 0);
+                       static_cast<float*>(nullptr), states, decays, a.row_len, a.seg_ids, a.n_dev, a.flags, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false, kNorm>), dim3(grid), dim3(C::NT), C::bytes,
                      a.stream, qp, kp, vp, gp, bp, a.cu, plan, int32_t(L.runs_max), a.max_segs, a.N,
                      a.H, a.scale, a.s0, static_cast<bf16*>(a.o), a.fs, states, decays, a.row_len,
-                     a.seg_ids, a.n_dev, 0);
+                     a.seg_ids, a.n_dev, a.flags, 0);
   return hipGetLastError();
 }
 

@@ -480,17 +480,19 @@ struct ChCfg {
   static constexpr int o_fP = o_fT + 4 * DK * 4;       // fp32 [10][DK]: 2^{T_j + .. + T_{i-1}}, j < i <= 4
   static constexpr int o_db = o_fP + 10 * DK * 4;       // fp32 [4 sub-chunks][NW waves][16]
   static constexpr int o_beta = o_db + 4 * NW * 16 * 4; // fp32 [64]
-  static constexpr int bytes = o_beta + kC * 4;
+  static constexpr int o_dg = o_beta + kC * 4;          // fp32 [NW waves][2][16]: diagonals of dA
+  static constexpr int bytes = o_dg + NW * 32 * 4;
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 16) threads
+__global__ __launch_bounds__(DK * 4, DK == 64 ? (DV == 64 ? 3 : 2) : 1) void kda_bwd_chunk_kernel(  // 64 (DK / 16) threads
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base, int32_t max_segs,
     int32_t max_chunks, int64_t N, int32_t H, float scale, const bf16* __restrict__ Sws,
     const bf16* __restrict__ Lws, bf16* __restrict__ dq, bf16* __restrict__ dk,
-    bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta) {
+    bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta,
+    int32_t* __restrict__ flags) {
   using C = ChCfg<DK, DV>;
   constexpr int NW = C::NW, NT = C::NT;
   // key block w per wave; value blocks split over the waves (at Dv < Dk only the
@@ -510,6 +512,7 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
   float* s_beta = reinterpret_cast<float*>(smem + C::o_beta);
   float* s_fT = reinterpret_cast<float*>(smem + C::o_fT);
   float* s_fP = reinterpret_cast<float*>(smem + C::o_fP);
+  float* s_dg = reinterpret_cast<float*>(smem + C::o_dg);
   // row of 2^{T_j + .. + T_{i-1}} in s_fP
   auto pidx = [](int j, int i) { return i * (i - 1) / 2 + j; };
 
@@ -625,6 +628,8 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
       s_kt[t * RK + d] = bf16(s_beta[t] * to_f32(s_k[t * RK + d]) * ex2(-c));
     }
     s_T[j * DK + d] = c;
+    // 2^{-c} of Kt can leave the fp32 / bf16 range below this total
+    if (c < kGateRangeMinLog2 && flags != nullptr) atomicOr(flags, kFlagGateRange);
   }
   __syncthreads();
   // decay factors of whole sub-chunks, once per chunk
@@ -738,6 +743,27 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
     const s16x4 opAT = pack4(Am);    // A-operand of A^T (rows s, slots t)
     const s16x4 opdA = pack4(dATm);  // A-operand of dA (rows t, slots s)
     const s16x4 opdAT = pack4(dAm);  // A-operand of dA^T (rows s, slots t)
+    // dA_tt as those operands hold it (bf16) for this lane's tokens t = t0 +
+    // 4 g4 + j. The products dA_tt Kt_t (in dq) and dA_tt Qh_t (in u) are the
+    // token's pair with itself: in q dq - k dk they cancel exactly, but only
+    // to bf16 rounding as computed, which swamps a small gate gradient
+    // (strong forgetting); dg takes both sums without them. The diagonal of
+    // a 16x16 result sits in register n - 4 g4 of the lanes with n in
+    // [4 g4, 4 g4 + 3]; they pass it on through the wave's own LDS slots (the
+    // wave's LDS operations complete in order).
+    f32x4 dgq, dgk;
+    {
+      float* dgw = s_dg + 32 * w;
+      const int jd = n - 4 * g4;
+      if (jd >= 0 && jd < 4) {
+        const float xq = jd == 0 ? dATm[0] : jd == 1 ? dATm[1] : jd == 2 ? dATm[2] : dATm[3];
+        const float xk = jd == 0 ? dAm[0] : jd == 1 ? dAm[1] : jd == 2 ? dAm[2] : dAm[3];
+        dgw[n] = __uint_as_float(pk2(xq, 0.f) << 16);  // rounded as pack4 rounds
+        dgw[16 + n] = __uint_as_float(pk2(xk, 0.f) << 16);
+      }
+      dgq = *reinterpret_cast<const f32x4*>(dgw + 4 * g4);
+      dgk = *reinterpret_cast<const f32x4*>(dgw + 16 + 4 * g4);
+    }
 
     // 2^{T_i} Lambda_i in both orientations: used by u and dv, and the update
     // to Lambda before sub-chunk i accumulates onto it
@@ -770,7 +796,8 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
         const s16x8 sb = join(pack4(S[2 * P][dd]), pack4(S[2 * P + 1][dd]));
         acc = mfma32(oa, sb, acc);
       }
-      acc += mfma16(opdA, tr4(tr_ptr(s_kt, RK, t0, 16 * Dblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
+      const s16x4 ktv = tr4(tr_ptr(s_kt, RK, t0, 16 * Dblk, lane));  // Kt_t[d]
+      acc += mfma16(opdA, ktv, f32x4{0.f, 0.f, 0.f, 0.f});
       const f32x4 Et = *reinterpret_cast<const f32x4*>(s_E + d * ES + t0 + 4 * g4);
       const f32x4 qv = unpack4(tr4(tr_ptr(s_q, RK, t0, 16 * Dblk, lane)));
       const f32x4 kv = unpack4(tr4(tr_ptr(s_k, RK, t0, 16 * Dblk, lane)));
@@ -778,7 +805,7 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         dqv[j] = scale * Et[j] * acc[j];
-        x[j] = qv[j] * dqv[j];
+        x[j] = qv[j] * (scale * Et[j] * (acc[j] - dgq[j] * bf2f(ktv[j])));  // exact product
       }
       // u: (2^{T_i} Lambda_i) v + dA^T Qh, then 2^{-c_s}
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -789,14 +816,16 @@ __global__ __launch_bounds__(DK * 4, 1) void kda_bwd_chunk_kernel(  // 64 (DK / 
         const s16x8 lb = join(pack4(L1[2 * P][dd]), pack4(L1[2 * P + 1][dd]));
         acc = mfma32(va, lb, acc);
       }
-      acc += mfma16(opdAT, tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
+      const s16x4 qhv = tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane));  // Qh_t[d]
+      acc += mfma16(opdAT, qhv, f32x4{0.f, 0.f, 0.f, 0.f});
       float dkv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = t0 + 4 * g4 + j;
-        const float u = acc[j] * __builtin_amdgcn_rcpf(Et[j]);
+        const float re = __builtin_amdgcn_rcpf(Et[j]);
+        const float u = acc[j] * re;
         dkv[j] = s_beta[t] * u;
-        x[j] -= kv[j] * dkv[j];
+        x[j] -= kv[j] * (s_beta[t] * ((acc[j] - dgk[j] * bf2f(qhv[j])) * re));
         db[j] = fmaf(kv[j], u, db[j]);
       }
       // dg: suffix sum over the sub-chunk's tokens, plus everything after it
@@ -943,7 +972,7 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
                      dim3(CC::NT), CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
                      int32_t(l.max_chunks), N, H, scale, Sws, Lws, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
-                     static_cast<bf16*>(db));
+                     static_cast<bf16*>(db), flags);
   return hipGetLastError();
 }
 

@@ -234,3 +234,13 @@ def test_backward_workspace(lib):
     assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args(ws=ctypes.c_void_p(0x1080), ws_bytes=need)) == 3
     # a workspace over an input
     assert lib.pkv_chunk_kda_varlen_backward(*_bwd_args(ws=ctypes.c_void_p(0x10000000), ws_bytes=need)) == 1
+
+
+def test_header_flag_and_option_bits_match_the_binding():
+    import packed_varlen_gated_amd as pkv
+    text = open(HEADER).read()
+    bits = dict((n, int(v)) for n, v in re.findall(r"#define PKV_((?:FLAG|OPT)_[A-Z0-9_]+)\s+(\d+)", text))
+    assert bits == {"FLAG_OVERFLOW": 1, "FLAG_LEADING_PAD": 2, "FLAG_BAD_CU_SEQLENS": 4,
+                    "FLAG_GATE_RANGE": 8, "OPT_QK_L2NORM": 1}
+    for n, v in bits.items():
+        assert getattr(pkv, n) == v, n

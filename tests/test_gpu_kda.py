@@ -501,3 +501,57 @@ def test_qk_l2norm_cut_segment_and_ling3_sample():
     ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], cu, use_qk_l2norm=True)
     check_close(f64(o[0]), ro, "bf16", "ling3 o")
     check_close(f64(fs), rfs, "bf16", "ling3 final states")
+
+
+def _gate_case(rng, N, H, Dk, Dv, glo, ghi):
+    q = rng.standard_normal((N, H, Dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((N, H, Dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((N, H, Dv))
+    g = -rng.uniform(glo, ghi, (N, H, Dk))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((N, H))))
+    return [q, k, v, g, beta]
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (128, 128)])
+def test_gate_range_edge_and_flag(Dk, Dv):
+    """RFC-0026 Background recurrence with strong forgetting on the chunked
+    bf16 path. Gates of -4.3 .. -4.7 per token keep every 16-token sub-chunk
+    sum above the path's limit (-83): forward and reverse match the oracle and
+    no flag is set. One key channel of one head at g = -7 (a 16-token sum of
+    -112) sets PKV_FLAG_GATE_RANGE on both passes."""
+    pkv = _pkv()
+    rng = np.random.default_rng(Dk + 11)
+    H = 2
+    lens = [200, 64, 77]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(cu[-1])
+    arrs = _gate_case(rng, N, H, Dk, Dv, 4.3, 4.7)
+    do = rng.standard_normal((N, H, Dv))
+    ts = [torch.from_numpy(a).to(torch.bfloat16) for a in arrs]
+    dot = torch.from_numpy(do).to(torch.bfloat16)
+    dev = device()
+    q, k, v, g, beta = [t.to(dev)[None] for t in ts]
+    cud = torch.from_numpy(cu).to(dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    o, fs = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, flags=flags)
+    gr = pkv.chunk_kda_varlen_backward(q, k, v, g, beta, dot.to(dev)[None], cud, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    x64 = [f64(t) for t in ts]
+    ro, rfs = oracle.chunk_kda_varlen(*x64, cu)
+    check_close(f64(o[0]), ro, "bf16", "o")
+    check_close(f64(fs), rfs, "bf16", "final_state")
+    ref = oracle.chunk_kda_varlen_backward(*x64, f64(dot), cu)
+    for n, got, r in zip(("dq", "dk", "dv", "dg", "dbeta"), gr[:5], ref[:5]):
+        check_close(f64(got[0]), r, "bf16", n)
+    # one channel beyond the limit
+    g2 = g.clone()
+    g2[0, :, 1, 3] = -7.0
+    for backward in (False, True):
+        flags.zero_()
+        if backward:
+            pkv.chunk_kda_varlen_backward(q, k, v, g2, beta, dot.to(dev)[None], cud, flags=flags)
+        else:
+            pkv.chunk_kda_varlen(q, k, v, g2, beta, cud, flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) & pkv.FLAG_GATE_RANGE, ("backward" if backward else "forward")

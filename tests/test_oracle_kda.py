@@ -113,6 +113,26 @@ def test_single_token_segments():
             np.testing.assert_allclose(fs[t, h], beta[t, h] * np.outer(k[t, h], v[t, h]), rtol=1e-13)
 
 
+def test_hard_forgetting_leaves_only_the_current_token():
+    # RFC-0026 Background recurrence with g = -50 on every channel: e^{-50} is
+    # below 2e-22, so every earlier token's weight in S_t vanishes and
+    # o_t = scale beta_t (q_t . k_t) v_t, S_end = beta_last k_last v_last^T, to
+    # fp64 rounding (the strong-forgetting regime the chunked GPU path flags).
+    rng = np.random.default_rng(8)
+    N, H, Dk, Dv = 40, 2, 5, 3
+    q, k, v, _, beta = _rand_inputs(rng, N, H, Dk, Dv)
+    g = np.full((N, H, Dk), -50.0)
+    cu = np.array([0, 17, 40])
+    o, fs = oracle.chunk_kda_varlen(q, k, v, g, beta, cu, scale=0.7)
+    for t in range(N):
+        for h in range(H):
+            np.testing.assert_allclose(o[t, h], 0.7 * beta[t, h] * np.dot(q[t, h], k[t, h]) * v[t, h],
+                                       rtol=1e-12, atol=1e-14)
+    for i, t in enumerate((16, 39)):
+        for h in range(H):
+            np.testing.assert_allclose(fs[i, h], beta[t, h] * np.outer(k[t, h], v[t, h]), rtol=1e-12, atol=1e-14)
+
+
 def test_gate_injection_equivalence():
     # RFC-0026 Alternatives, gate injection: one continuous segment with
     # g = -inf at every document's first token gives the segmented result.
