@@ -27,28 +27,30 @@
 // A work-group runs one (run, head) item at a time: 4 producer waves and 4
 // consumer waves, software-pipelined over chunks (two barriers per chunk step):
 //   first half  P: chunk c: per-channel factors from the sub-chunk totals,
-//                  Q^ = q 2^b and Kbar^T = (beta k 2^{b_C - b})^T to the LDS
-//                  buffers of c's parity, the operand versions of the ten
-//                  A blocks, KE, and 2^{b_C}.
+//                  Q^ = q 2^b, Kbar^T = (beta k 2^{b_C - b})^T and 2^{b_C}
+//                  (the last two to the LDS buffers of c's parity), the
+//                  operand versions of the ten A blocks and KE.
 //               C: chunk c-1: o^T += V^T A^T for its Dv/4 columns, packed;
 //                  S = diag(2^{b_C}) S + Kbar^T V.
-//   second half P: V of chunk c; the in-sub-chunk cumulative gates of chunk
-//                  c+1, their sub-chunk totals (to LDS) and the per-element
-//                  factors q 2^{c} and k 2^{T - c} of chunk c+1 (in the
-//                  registers of its q and k).
+//   second half P: V of chunk c; the gate products of chunk c+1, its
+//                  sub-chunk totals 2^T (to LDS) and the per-element factors
+//                  q 2^{c} and k 2^{T - c} of chunk c+1 (in the registers of
+//                  its q and k).
 //               C: the stores of chunk c-1's outputs; three of the twelve A
 //                  block jobs of chunk c (MFMA), masked, beta-scaled, to LDS;
 //                  o^T = S^T Q^^T.
 // Producer wave w owns 16-token sub-chunk w and all Dk channels; lane
 // 16 tq + cg holds the 4 consecutive tokens 4 tq .. 4 tq + 3 x Dk/16 channels
 // of group cg, so each 16-lane row of a load or an LDS store covers one whole
-// token row (conflict-free LDS writes) and the in-sub-chunk cumsum is an
-// in-lane prefix plus a scan across the four rows (v_permlane16_swap and
-// v_permlane32_swap). The sub-chunk totals go through a small LDS table, and
-// the sub-chunk index is uniform per wave (no divergent stores).
-// Raw inputs of chunk c+1 are loaded at the start of step c. Each
-// single-buffered LDS tile is written in one half and read in the other; Q^,
-// Kbar^T and 2^{b_C}, read a step later, are double-buffered.
+// token row (conflict-free LDS writes) and the in-sub-chunk products are an
+// in-lane prefix / suffix plus a step across the four rows (v_permlane16_swap
+// and v_permlane32_swap). The sub-chunk totals go through a small LDS table,
+// and the sub-chunk index is uniform per wave (no divergent stores).
+// Raw inputs of chunk c+1 are loaded at the start of step c. Every
+// single-buffered LDS tile (Q^, KE, the A-block versions, V, A, the totals)
+// is written in one half and read in the other; Kbar^T, 2^{b_C} and beta,
+// which the consumers read in the next step's first half, are double-buffered
+// by chunk parity.
 // MFMA v_mfma_f32_16x16x32_bf16: A operand lane l holds row l%16 and eight
 // contraction slots of lane group l/16, B likewise for column l%16; the 16x16
 // fp32 result has column l%16 and rows 4(l/16)+i. The contraction index may be
