@@ -478,22 +478,6 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // smallest 2^T the producer's scans met (the gate-range check)
   float tmin = 1.f;
   auto scan = [&](const Raw<PCPL, PVPL>& R, RawQK<PCPL>& X) __attribute__((always_inline)) {
-    // kNorm: 1 / sqrt(|x|^2 + eps) of each token's q and k; the 16 lanes of a
-    // row hold the token's Dk channels, PCPL each
-    float rq[4], rk[4];
-    if constexpr (kNorm) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int c = 0; c < PCPL; ++c) {
-          if constexpr (!kState) sq = fmaf(bf(X.q[i], c), bf(X.q[i], c), sq);
-          sk = fmaf(bf(X.k[i], c), bf(X.k[i], c), sk);
-        }
-        if constexpr (!kState) rq[i] = __builtin_amdgcn_rsqf(row_sum16(sq) + kL2NormEps);
-        rk[i] = __builtin_amdgcn_rsqf(row_sum16(sk) + kL2NormEps);
-      }
-    }
     // One exponential per gate element, 2^{g log2 e}; the factors are its
     // products: 2^{c} over the tokens up to and including this one, 2^{T - c}
     // over the tokens after it, 2^T over the sub-chunk. In-lane over the
@@ -531,6 +515,23 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       for (int c = 0; c < PCPL; ++c) {
         s_T[(ch0 + c + cg) * 4 + sw] = tot[c];  // + cg: the table's padding
         tmin = fminf(tmin, tot[c]);
+      }
+    }
+    // kNorm: 1 / sqrt(|x|^2 + eps) of each token's q and k; the 16 lanes of a
+    // row hold the token's Dk channels, PCPL each (formed after the gate
+    // products, whose temporaries are dead by then)
+    float rq[4], rk[4];
+    if constexpr (kNorm) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int c = 0; c < PCPL; ++c) {
+          if constexpr (!kState) sq = fmaf(bf(X.q[i], c), bf(X.q[i], c), sq);
+          sk = fmaf(bf(X.k[i], c), bf(X.k[i], c), sk);
+        }
+        if constexpr (!kState) rq[i] = __builtin_amdgcn_rsqf(row_sum16(sq) + kL2NormEps);
+        rk[i] = __builtin_amdgcn_rsqf(row_sum16(sk) + kL2NormEps);
       }
     }
 #pragma unroll
