@@ -326,12 +326,15 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
  *             the chunked path PKV_FLAG_GATE_RANGE as in the forward call.
  * The reverse pass recomputes the states (nothing is saved by the forward
  * call). For bf16 with Dk, Dv in {64, 128} it is chunked: the workspace holds
- * the work plan (chunk, piece and summary offsets per slot), the bf16 state
- * and adjoint state (dL/dS from everything after it) at every 64-token chunk
- * boundary, and, for segments long enough to be cut into pieces, fp32 piece
- * summaries (end state and decay product per piece), all written and read
- * within the call (scratch: calls sharing a workspace must be ordered on one
- * stream); see pkv_chunk_kda_varlen_backward_workspace_size() for its size. Every other shape runs token-serially and needs no workspace (size
+ * the work plan (chunk, piece and summary offsets per slot, the pieces in
+ * longest-first order, a work counter), the bf16 state at every 64-token
+ * chunk boundary (the adjoint dL/dS is carried in registers while the
+ * chunks are walked backwards), and, for segments long enough to be cut into
+ * pieces, fp32 piece summaries (end state and decay product per piece and
+ * role), all written and read within the call (scratch: calls sharing a
+ * workspace must be ordered on one stream); see
+ * pkv_chunk_kda_varlen_backward_workspace_size() for its size. Every other
+ * shape runs token-serially and needs no workspace (size
  * 0, NULL allowed): between its two sweeps the dg and dk buffers hold fp32
  * intermediates. Alignment rules as for the forward call, and the workspace
  * must be 256-byte aligned. The arithmetic is fp32 (bf16 tensors are read

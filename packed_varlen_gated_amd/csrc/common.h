@@ -31,6 +31,9 @@ constexpr int32_t kFlagGateRange = 8;
 constexpr float kGateRangeMinLog2 = -120.f;
 constexpr float kGateRangeMin = 0x1p-120f;  // 2^kGateRangeMinLog2
 
+// Compute units of the current device (the persistent grids' size; cached per device).
+int device_cus();
+
 // Launchers (host side). Each returns the HIP error of its launch(es).
 hipError_t launch_cu_seqlens(const int32_t* seg, int64_t N, int64_t T, int32_t max_segs,
                              int32_t* cu, int32_t* token_seg, int32_t* n_segs, int32_t* flags,

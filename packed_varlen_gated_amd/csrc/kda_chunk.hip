@@ -1371,18 +1371,6 @@ PlanLayout plan_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max
   return p;
 }
 
-// Compute units of the current device (the persistent grids' size).
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 // Arguments of one call of the chunk path.
 struct Launch {
@@ -1464,6 +1452,19 @@ hipError_t dispatch(int32_t Dk, int32_t Dv, bool qk_l2norm, const Launch& a) {
 }
 
 }  // namespace
+
+// Compute units of the current device (the persistent grids' size).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 bool kda_chunk_supported(int32_t Dk, int32_t Dv, int32_t dtype) {
   return dtype == 0 && (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);

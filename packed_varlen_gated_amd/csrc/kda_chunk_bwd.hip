@@ -10,22 +10,26 @@
 //
 // Four launches:
 //   plan     one work-group: per segment slot its chunk count and their prefix
-//            sums (global chunk index of each segment's first chunk), and the
-//            cut of long segments into pieces (as in the forward pass).
+//            sums (global chunk index of each segment's first chunk), the cut
+//            of long segments into pieces (as in the forward pass), and the
+//            pieces ranked longest first.
 //   summary  per piece of a cut segment, head and role: the piece walked from a
-//            zero state; its end state and the product of its decays (fp32).
-//   walk     one work-group per (piece, head) and role, the two roles in one grid:
-//            forward, S before every chunk (bf16 in the workspace), starting
-//            from the initial state composed with the earlier pieces' summaries;
-//            adjoint, Lambda after every chunk, walking the chunks backwards from
-//            dL/dfinal_state composed with the later pieces' summaries, then
-//            d initial state = Lambda before the first chunk.
+//            zero state; its end state and the product of its decays (fp32):
 //              S   <- 2^{B} S + sum_t kbar_t v_t^T,     kbar_t = beta_t k_t 2^{B - b_t}
 //              Lam <- 2^{B} Lam + sum_t q'_t do_t^T,    q'_t = scale q_t 2^{b_t}
 //            (b_t the log2 cumulative gate from the chunk start, B its last
-//            value; rows scaled per key channel.)
-//   chunk    one work-group per (chunk, head), independent of the others: from
-//            S_c and Lambda_c it walks the sub-chunks backwards. For sub-chunk i
+//            value; rows scaled per key channel; Lambda walks backwards.)
+//   walk     one work-group per (piece, head): S before every chunk (bf16 in the
+//            workspace), starting from the initial state composed with the
+//            earlier pieces' summaries.
+//   chunk    persistent work-groups over (piece, head) items, longest first:
+//            each walks its piece's chunks backwards, starting from
+//            dL/dfinal_state composed with the later pieces' adjoint summaries,
+//            and carries Lambda (the adjoint after the chunk, fp32 in
+//            registers) from one chunk to the one before it; the segment's
+//            first piece ends with d initial state = Lambda before its first
+//            chunk. Per chunk, from S_c and Lambda it walks the sub-chunks
+//            backwards. For sub-chunk i
 //            with within-sub-chunk cumulative c_t (log2) and total T_i, S_i the
 //            state before it (formed directly from S_c) and Lambda_i the adjoint
 //            after it (carried):
@@ -74,7 +78,7 @@ constexpr int kPlanThreads = 1024;
 constexpr int kCutMin = 128;
 constexpr int kPieceLen = 64;
 constexpr int kMaxPieces = 16;
-constexpr int kTailBlocks = 64;
+constexpr int kRankBins = 2048;  // piece-length bins of the longest-first order
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -167,7 +171,8 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t x, int64_t* s_scan, i
 __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
     const int32_t* __restrict__ cu, int32_t max_segs, int64_t N, int32_t H, int32_t max_chunks,
     int32_t max_pieces, int32_t max_sums, int32_t* __restrict__ base, int32_t* __restrict__ pbase,
-    int32_t* __restrict__ sbase, int32_t* __restrict__ flags) {
+    int32_t* __restrict__ sbase, int32_t* __restrict__ order, int32_t* __restrict__ counter,
+    int32_t* __restrict__ flags) {
   __shared__ int64_t s_scan[kPlanThreads];
   const int tid = threadIdx.x;
   int64_t running = 0, tot;
@@ -212,7 +217,48 @@ __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
   if (tid == 0) {
     pbase[max_segs] = int32_t(run_p < max_pieces ? run_p : max_pieces);
     sbase[max_segs] = int32_t(run_s < max_sums ? run_s : max_sums);
+    *counter = 0;
   }
+  __threadfence_block();
+  __syncthreads();
+  // order[r] = the piece of rank r, longest first (a counting sort over the
+  // pieces' chunk counts, capped at kRankBins - 1; ties in any order: results
+  // do not depend on the order)
+  __shared__ int s_bin[kRankBins];
+  for (int b = tid; b < kRankBins; b += kPlanThreads) s_bin[b] = 0;
+  __syncthreads();
+  const int npieces = pbase[max_segs];
+  auto piece_bin = [&](int pc) {
+    int lo = 0, hi = max_segs - 1;  // the slot: last i with pbase[i] <= pc
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pbase[mid] <= pc) lo = mid; else hi = mid - 1;
+    }
+    const int64_t nn = int64_t(base[lo + 1]) - base[lo];
+    const int64_t jj = pc - pbase[lo], mm = int64_t(pbase[lo + 1]) - pbase[lo];
+    const int64_t len = mm > 0 ? nn * (jj + 1) / mm - nn * jj / mm : 0;
+    return int(len < kRankBins - 1 ? len : kRankBins - 1);
+  };
+  for (int pc = tid; pc < npieces; pc += kPlanThreads) atomicAdd(&s_bin[piece_bin(pc)], 1);
+  __syncthreads();
+  // exclusive prefix over the bins from the longest down; thread t takes the
+  // kRankBins / kPlanThreads bins below kRankBins - 1 - t * that many
+  constexpr int kPer = kRankBins / kPlanThreads;
+  int cnt[kPer], sum = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    cnt[u] = s_bin[kRankBins - 1 - (tid * kPer + u)];
+    sum += cnt[u];
+  }
+  int64_t all;
+  int64_t before = block_excl_scan(sum, s_scan, all);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    s_bin[kRankBins - 1 - (tid * kPer + u)] = int(before);  // the bin's first rank
+    before += cnt[u];
+  }
+  __syncthreads();
+  for (int pc = tid; pc < npieces; pc += kPlanThreads) order[atomicAdd(&s_bin[piece_bin(pc)], 1)] = pc;
 }
 
 // Last index i in [0, n) with tab[i] <= x (tab non-decreasing, tab[0] <= x).
@@ -245,10 +291,10 @@ struct StCfg {
   static constexpr int NY = kC * DV / 8 / NT;          // ... Dv-wide tile
 };
 
-// kSum = false (walk): one work-group per (piece, head, role); the state at the
-// piece's start (S role) or the adjoint at its end (Lambda role) is composed from
-// the summaries of the other pieces, then the piece's chunks are walked and the
-// state before (S) or adjoint after (Lambda) every chunk is stored.
+// kSum = false (walk): one work-group per (piece, head), S role only (the grid
+// holds no adjoint work-groups): the state at the piece's start is composed
+// from the earlier pieces' summaries, then the piece's chunks are walked and
+// the state before every chunk is stored.
 // kSum = true (summary): one work-group per (summary slot, head, role) of a cut
 // segment: the piece walked from a zero state; its end state (S role: after the
 // piece; Lambda role: before it) and the product of its decays are stored.
@@ -259,8 +305,8 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base,
     const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase, int32_t max_segs,
     int32_t units, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
-    const float* __restrict__ dfinal, bf16* __restrict__ Sws, bf16* __restrict__ Lws,
-    float* __restrict__ sumL, float* __restrict__ sumD, float* __restrict__ dinit) {
+    const float* __restrict__ dfinal, bf16* __restrict__ Sws, float* __restrict__ sumL,
+    float* __restrict__ sumD) {
   using C = StCfg<DK, DV>;
   constexpr int EB = DV / 16, NT = C::NT, NX = C::NX, NY = C::NY;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -292,18 +338,7 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
   const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
   const int d_own = 16 * w + n;  // key channel of this lane's X tiles
 
-  if (!kSum && nch == 0) {
-    // empty (or malformed) slot: its d initial state is the final-state cotangent
-    if (adjoint && dinit != nullptr) {
-#pragma unroll
-      for (int E = 0; E < EB; ++E) {
-        const int64_t off = sh + int64_t(d_own) * DV + 16 * E + 4 * g4;
-        *reinterpret_cast<f32x4*>(dinit + off) =
-            dfinal ? *reinterpret_cast<const f32x4*>(dfinal + off) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-    return;
-  }
+  if (!kSum && nch == 0) return;  // empty (or malformed) slot: no state to store
   // summary storage of slot s: L [s][role][h][Dk][Dv], D [s][role][h][Dk]
   auto sumL_at = [&](int s_, bool adj) {
     return sumL + ((int64_t(s_) * 2 + adj) * H + h) * DK * DV + int64_t(d_own) * DV + 4 * g4;
@@ -430,7 +465,7 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
   // Branch-free main loop (one vector-memory counter covers loads and stores, so a
   // conditional store or load here would make the wait for the prefetched inputs wait
   // for the stores too): the prefetch index is clamped, and the last step is peeled.
-  bf16* ws_out = adjoint ? Lws : Sws;
+  bf16* ws_out = Sws;
   if (napply > 0) {
     fetch(chunk_of(0));
     put();
@@ -455,11 +490,6 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
     if (g4 == 0) *sumD_at(s_, adjoint) = Dprod;
     return;
   }
-  if (adjoint && j == 0 && dinit != nullptr) {
-#pragma unroll
-    for (int E = 0; E < EB; ++E)
-      *reinterpret_cast<f32x4*>(dinit + sh + int64_t(d_own) * DV + 16 * E + 4 * g4) = X[E];
-  }
 }
 
 // ---------------------------------------------------------------- chunk pass
@@ -481,18 +511,23 @@ struct ChCfg {
   static constexpr int o_db = o_fP + 10 * DK * 4;       // fp32 [4 sub-chunks][NW waves][16]
   static constexpr int o_beta = o_db + 4 * NW * 16 * 4; // fp32 [64]
   static constexpr int o_dg = o_beta + kC * 4;          // fp32 [NW waves][2][16]: diagonals of dA
-  static constexpr int bytes = o_dg + NW * 32 * 4;
+  static constexpr int o_item = o_dg + NW * 32 * 4;     // int: the next (piece, head) item
+  static constexpr int bytes = o_item + 16;
+  // persistent work-groups per CU: as many as the LDS holds (two at Dk = Dv = 64)
+  static constexpr int WG_PER_CU = bytes <= 80 * 1024 ? 2 : 1;
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(DK * 4, DK == 64 ? (DV == 64 ? 3 : 2) : 1) void kda_bwd_chunk_kernel(  // 64 (DK / 16) threads
+__global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bwd_chunk_kernel(  // 64 (DK / 16) threads
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ base, int32_t max_segs,
-    int32_t max_chunks, int64_t N, int32_t H, float scale, const bf16* __restrict__ Sws,
-    const bf16* __restrict__ Lws, bf16* __restrict__ dq, bf16* __restrict__ dk,
-    bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta,
-    int32_t* __restrict__ flags) {
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase,
+    const int32_t* __restrict__ order, int32_t* __restrict__ counter, int32_t max_segs, int64_t N,
+    int32_t H, float scale, const float* __restrict__ dfinal, const float* __restrict__ sumL,
+    const float* __restrict__ sumD, const bf16* __restrict__ Sws, bf16* __restrict__ dq,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta,
+    float* __restrict__ dinit, int32_t* __restrict__ flags) {
   using C = ChCfg<DK, DV>;
   constexpr int NW = C::NW, NT = C::NT;
   // key block w per wave; value blocks split over the waves (at Dv < Dk only the
@@ -513,394 +548,455 @@ __global__ __launch_bounds__(DK * 4, DK == 64 ? (DV == 64 ? 3 : 2) : 1) void kda
   float* s_fT = reinterpret_cast<float*>(smem + C::o_fT);
   float* s_fP = reinterpret_cast<float*>(smem + C::o_fP);
   float* s_dg = reinterpret_cast<float*>(smem + C::o_dg);
+  int* s_item = reinterpret_cast<int*>(smem + C::o_item);
   // row of 2^{T_j + .. + T_{i-1}} in s_fP
   auto pidx = [](int j, int i) { return i * (i - 1) / 2 + j; };
 
   const int tid = threadIdx.x;
-  const int64_t chunk_blocks = int64_t(max_chunks) * H;
-  if (int64_t(blockIdx.x) >= chunk_blocks) {
-    // positions not covered by any segment get zero gradients
-    int64_t cu_last = cu_at(cu, max_segs, N);
-    cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
-    const int64_t stride = int64_t(kTailBlocks) * NT;
-    const int64_t first = (int64_t(blockIdx.x) - chunk_blocks) * NT + tid;
-    const bf16 z = bf16(0.f);
-    for (int64_t i = first; i < (N - cu_last) * H * DK; i += stride) {
-      dq[cu_last * H * DK + i] = z;
-      dk[cu_last * H * DK + i] = z;
-      dg[cu_last * H * DK + i] = z;
-    }
-    for (int64_t i = first; i < (N - cu_last) * H * DV; i += stride) dv[cu_last * H * DV + i] = z;
-    for (int64_t i = first; i < (N - cu_last) * H; i += stride) dbeta[cu_last * H + i] = z;
-    return;
-  }
-  const int gc = int(blockIdx.x / H), h = int(blockIdx.x % H);
-  if (gc >= base[max_segs]) return;
-  // slot: the last i with base[i] <= gc (empty slots share their base with the next)
-  int lo = 0, hi = max_segs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (base[mid] <= gc) lo = mid; else hi = mid - 1;
-  }
-  const int slot = lo;
-  const int64_t a = cu_at(cu, slot, N) + int64_t(kC) * (gc - base[slot]);
-  const int64_t seg_end = cu_at(cu, slot + 1, N);
-  const int L = int(seg_end - a < kC ? seg_end - a : kC);
-  const int nsub = (L + 15) >> 4;
-  // gradient rows of this chunk's tokens (all heads); stores past token L are dropped
-  const auto r_dq = rsrc(dq + a * H * DK, uint32_t(L) * H * DK * 2);
-  const auto r_dk = rsrc(dk + a * H * DK, uint32_t(L) * H * DK * 2);
-  const auto r_dg = rsrc(dg + a * H * DK, uint32_t(L) * H * DK * 2);
-  const auto r_dv = rsrc(dv + a * H * DV, uint32_t(L) * H * DV * 2);
-
   const int lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
-  const int64_t soff = (int64_t(gc) * H + h) * DK * DV;
   const bool ev_active = EB >= NW || w < EB;  // wave-uniform
   auto eblk = [&](int ee) { return EB >= NW ? w * EBW + ee : w; };
-  // the chunk's Lambda (two orientations) and S_c from the workspace, raw bf16:
-  // issued with the input loads, so their latency overlaps the scan below
-  s16x4 L1r[EB][DBW], L2r[DB][EBW], Sc[EB][DBW];
-
-  // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads, all
-  // issued before the first LDS store
-  {
-    constexpr int NX = kC * DK / 8 / NT, NY = kC * DV / 8 / NT;
-    const s16x8 z8 = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    s16x8 xq[NX], xk[NX], xg[NX], xv[NY], xd[NY];
-#pragma unroll
-    for (int r = 0; r < NX; ++r) {
-      const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
-      const int64_t off = ((a + t) * H + h) * DK + c8;
-      xq[r] = t < L ? *reinterpret_cast<const s16x8*>(q + off) : z8;
-      xk[r] = t < L ? *reinterpret_cast<const s16x8*>(k + off) : z8;
-      xg[r] = t < L ? *reinterpret_cast<const s16x8*>(g + off) : z8;
-    }
-#pragma unroll
-    for (int r = 0; r < NY; ++r) {
-      const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-      const int64_t off = ((a + t) * H + h) * DV + c8;
-      xv[r] = t < L ? *reinterpret_cast<const s16x8*>(v + off) : z8;
-      xd[r] = t < L ? *reinterpret_cast<const s16x8*>(dout + off) : z8;
-    }
-    const bf16 xb = tid < L ? beta[(a + tid) * H + h] : bf16(0.f);
-#pragma unroll
-    for (int dd = 0; dd < DBW; ++dd) {
-      const int d = 16 * (w * DBW + dd) + n;
-#pragma unroll
-      for (int E = 0; E < EB; ++E) {
-        L1r[E][dd] = ld4(Lws + soff + int64_t(d) * DV + 16 * E + 4 * g4);
-        Sc[E][dd] = ld4(Sws + soff + int64_t(d) * DV + 16 * E + 4 * g4);
-      }
-    }
-#pragma unroll
-    for (int D = 0; D < DB; ++D)
-#pragma unroll
-      for (int ee = 0; ee < EBW; ++ee)
-        L2r[D][ee] = ev_active ? ld4(Lws + soff + int64_t(16 * D + n) * DV + 16 * eblk(ee) + 4 * g4)
-                               : s16x4{0, 0, 0, 0};
-#pragma unroll
-    for (int r = 0; r < NX; ++r) {
-      const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
-      *reinterpret_cast<s16x8*>(s_q + t * RK + c8) = xq[r];
-      *reinterpret_cast<s16x8*>(s_k + t * RK + c8) = xk[r];
-      *reinterpret_cast<s16x8*>(s_qh + t * RK + c8) = xg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < NY; ++r) {
-      const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-      *reinterpret_cast<s16x8*>(s_v + t * RV + c8) = xv[r];
-      *reinterpret_cast<s16x8*>(s_do + t * RV + c8) = xd[r];
-    }
-    if (tid < kC) s_beta[tid] = to_f32(xb);
-  }
-  __syncthreads();
-  // per (sub-chunk, channel): 2^{c_t}, Qh over g, Kt, and the sub-chunk total
-  for (int p = tid; p < 4 * DK; p += NT) {
-    const int j = p / DK, d = p % DK;
-    float c = 0.f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int t = 16 * j + u;
-      c += to_f32(s_qh[t * RK + d]) * kLog2e;
-      const float e = ex2(c);
-      s_E[d * ES + t] = e;
-      s_qh[t * RK + d] = bf16(scale * to_f32(s_q[t * RK + d]) * e);
-      s_kt[t * RK + d] = bf16(s_beta[t] * to_f32(s_k[t * RK + d]) * ex2(-c));
-    }
-    s_T[j * DK + d] = c;
-    // 2^{-c} of Kt can leave the fp32 / bf16 range below this total
-    if (c < kGateRangeMinLog2 && flags != nullptr) atomicOr(flags, kFlagGateRange);
-  }
-  __syncthreads();
-  // decay factors of whole sub-chunks, once per chunk
-  if (tid < DK) {
-    const int d = tid;
-    float T[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      T[j] = s_T[j * DK + d];
-      s_fT[j * DK + d] = ex2(T[j]);
-    }
-#pragma unroll
-    for (int i = 1; i <= 4; ++i) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = i - 1; j >= 0; --j) {
-        acc += T[j];
-        s_fP[pidx(j, i) * DK + d] = ex2(acc);
-      }
-    }
-  }
-  __syncthreads();
-
-  // Lambda in the two orientations: L1[E][dd] (rows e, column d = 16 (w DBW + dd) + n)
-  // and L2[D][ee] (rows d = 16 D + 4 g4 + j, column e = 16 (w EBW + ee) + n).
-  f32x4 L1[EB][DBW], L2[DB][EBW];
-#pragma unroll
-  for (int dd = 0; dd < DBW; ++dd)
-#pragma unroll
-    for (int E = 0; E < EB; ++E) L1[E][dd] = unpack4(L1r[E][dd]);
+  const int d_own = 16 * w + n;  // key channel of this lane's L1 tiles (DBW = 1)
   // identity 16x16 operand (either side)
   s16x4 eye;
 #pragma unroll
   for (int j = 0; j < 4; ++j) eye[j] = (4 * g4 + j == n) ? short(0x3F80) : short(0);
-  {
+
+  // Persistent work-groups over (piece, head) items, longest piece first (the
+  // plan's order; item = rank * H + h). A work-group claims its next item when
+  // it starts the current item's last chunk, and walks the piece's chunks from
+  // the last to the first, carrying Lambda (the adjoint after the chunk) in
+  // registers from one chunk to the one before it.
+  const int n_items = pbase[max_segs] * H;
+  if (tid == 0) *s_item = atomicAdd(counter, 1);
+  __syncthreads();
+  int item = __builtin_amdgcn_readfirstlane(*s_item);
+  while (item < n_items) {
+    const int rank = item / H, h = item % H;
+    const int pc = order[rank];
+    const int slot = last_le(pbase, max_segs, pc);
+    const int j = pc - pbase[slot];
+    const int m = pbase[slot + 1] - pbase[slot];
+    const int cbase = base[slot];
+    const int nseg = base[slot + 1] - cbase;
+    const int c0 = int(int64_t(nseg) * j / m), c1 = int(int64_t(nseg) * (j + 1) / m);
+    const int64_t seg_start = nseg > 0 ? cu_at(cu, slot, N) : 0;
+    const int64_t seg_end = nseg > 0 ? cu_at(cu, slot + 1, N) : 0;
+    const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
+    int next = 0;
+
+    // Lambda after the piece: dL/dfinal_state (or 0), composed with the later
+    // pieces' adjoint summaries (Lambda <- D Lambda + L' over pieces m-1 .. j+1),
+    // in both orientations: L1[E][dd] (rows e, column d = 16 (w DBW + dd) + n)
+    // and L2[D][ee] (rows d = 16 D + 4 g4 + i, column e = 16 eblk(ee) + n).
+    f32x4 L1[EB][DBW], L2[DB][EBW];
+#pragma unroll
+    for (int E = 0; E < EB; ++E)
+      L1[E][0] = dfinal ? *reinterpret_cast<const f32x4*>(dfinal + sh + int64_t(d_own) * DV + 16 * E + 4 * g4)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int D = 0; D < DB; ++D)
 #pragma unroll
-      for (int ee = 0; ee < EBW; ++ee) L2[D][ee] = mfma16(L2r[D][ee], eye, f32x4{0.f, 0.f, 0.f, 0.f});
-  }
-
-  // S^T before sub-chunk i, columns of this wave: 2^{sum_{j<i} T_j} S_c^T plus the
-  // sub-chunks before i, each with Kt scaled by 2^{sum_{j<=j'<i} T_j'}.
-  f32x4 S[EB][DBW];
-  auto state_at = [&](int i) {
+      for (int ee = 0; ee < EBW; ++ee) {
 #pragma unroll
-    for (int dd = 0; dd < DBW; ++dd) {
-      const int d = 16 * (w * DBW + dd) + n;
-      const float f = i > 0 ? s_fP[pidx(0, i) * DK + d] : 1.f;
-      // S_c^T unpacked by a product with the identity, then scaled
-#pragma unroll
-      for (int E = 0; E < EB; ++E) S[E][dd] = f * mfma16(eye, Sc[E][dd], f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-    for (int j = 0; j < i; ++j) {
-      s16x4 kb[DBW];
-#pragma unroll
-      for (int dd = 0; dd < DBW; ++dd) {
-        const int d = 16 * (w * DBW + dd) + n;
-        kb[dd] = pack4(s_fP[pidx(j, i) * DK + d] * unpack4(tr4(tr_ptr(s_kt, RK, 16 * j, 16 * (w * DBW + dd), lane))));
+        for (int i = 0; i < 4; ++i)
+          L2[D][ee][i] = (dfinal && ev_active)
+                             ? dfinal[sh + int64_t(16 * D + 4 * g4 + i) * DV + 16 * eblk(ee) + n] : 0.f;
       }
+    for (int t = 0; t < m - 1 - j; ++t) {
+      const int s_ = sbase[slot] + (m - 1 - t);
+      const int64_t ls = ((int64_t(s_) * 2 + 1) * H + h) * DK;  // adjoint role
+      const float* Lp = sumL + ls * DV;
+      const float* Dp = sumD + ls;
+      const float dprod = Dp[d_own];
 #pragma unroll
-      for (int E = 0; E < EB; ++E) {
-        const s16x4 va = tr4(tr_ptr(s_v, RV, 16 * j, 16 * E, lane));
-#pragma unroll
-        for (int dd = 0; dd < DBW; ++dd) S[E][dd] = mfma16(va, kb[dd], S[E][dd]);
-      }
-    }
-  };
-
-  // G_c = sum_e Lambda_c * S_end, per key channel: the running gate gradient
-  float r[DBW];
-  state_at(nsub);
-#pragma unroll
-  for (int dd = 0; dd < DBW; ++dd) {
-    float p = 0.f;
-#pragma unroll
-    for (int E = 0; E < EB; ++E)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p = fmaf(L1[E][dd][j], S[E][dd][j], p);
-    p += __shfl_xor(p, 16, 64);
-    p += __shfl_xor(p, 32, 64);
-    r[dd] = p;
-  }
-
-  for (int i = nsub - 1; i >= 0; --i) {
-    state_at(i);
-    const int t0 = 16 * i;
-    // A, dA (rows t, column s) and dA^T (rows s, column t) of the sub-chunk
-    f32x4 Ac = {0.f, 0.f, 0.f, 0.f}, dA = Ac, dAT = Ac;
-#pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) {
-      const s16x8 qa = ld8(s_qh + (t0 + n) * RK + 32 * kb + 8 * g4);
-      const s16x8 kt = ld8(s_kt + (t0 + n) * RK + 32 * kb + 8 * g4);
-      Ac = mfma32(qa, kt, Ac);
-    }
-#pragma unroll
-    for (int kb = 0; kb < DV / 32; ++kb) {
-      const s16x8 oa = ld8(s_do + (t0 + n) * RV + 32 * kb + 8 * g4);
-      const s16x8 va = ld8(s_v + (t0 + n) * RV + 32 * kb + 8 * g4);
-      dA = mfma32(oa, va, dA);
-      dAT = mfma32(va, oa, dAT);
-    }
-    f32x4 Am, dAm, dATm;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool lower = 4 * g4 + j >= n;  // row index >= column index
-      Am[j] = lower ? Ac[j] : 0.f;
-      dAm[j] = lower ? dA[j] : 0.f;
-      dATm[j] = (4 * g4 + j <= n) ? dAT[j] : 0.f;
-    }
-    const s16x4 opAT = pack4(Am);    // A-operand of A^T (rows s, slots t)
-    const s16x4 opdA = pack4(dATm);  // A-operand of dA (rows t, slots s)
-    const s16x4 opdAT = pack4(dAm);  // A-operand of dA^T (rows s, slots t)
-    // dA_tt as those operands hold it (bf16) for this lane's tokens t = t0 +
-    // 4 g4 + j. The products dA_tt Kt_t (in dq) and dA_tt Qh_t (in u) are the
-    // token's pair with itself: in q dq - k dk they cancel exactly, but only
-    // to bf16 rounding as computed, which swamps a small gate gradient
-    // (strong forgetting); dg takes both sums without them. The diagonal of
-    // a 16x16 result sits in register n - 4 g4 of the lanes with n in
-    // [4 g4, 4 g4 + 3]; they pass it on through the wave's own LDS slots (the
-    // wave's LDS operations complete in order).
-    f32x4 dgq, dgk;
-    {
-      float* dgw = s_dg + 32 * w;
-      const int jd = n - 4 * g4;
-      if (jd >= 0 && jd < 4) {
-        const float xq = jd == 0 ? dATm[0] : jd == 1 ? dATm[1] : jd == 2 ? dATm[2] : dATm[3];
-        const float xk = jd == 0 ? dAm[0] : jd == 1 ? dAm[1] : jd == 2 ? dAm[2] : dAm[3];
-        dgw[n] = __uint_as_float(pk2(xq, 0.f) << 16);  // rounded as pack4 rounds
-        dgw[16 + n] = __uint_as_float(pk2(xk, 0.f) << 16);
-      }
-      dgq = *reinterpret_cast<const f32x4*>(dgw + 4 * g4);
-      dgk = *reinterpret_cast<const f32x4*>(dgw + 16 + 4 * g4);
-    }
-
-    // 2^{T_i} Lambda_i in both orientations: used by u and dv, and the update
-    // to Lambda before sub-chunk i accumulates onto it
-#pragma unroll
-    for (int dd = 0; dd < DBW; ++dd) {
-      const float fT = s_fT[i * DK + 16 * (w * DBW + dd) + n];
-#pragma unroll
-      for (int E = 0; E < EB; ++E) L1[E][dd] *= fT;
-    }
-    if (ev_active) {
+      for (int E = 0; E < EB; ++E)
+        L1[E][0] = dprod * L1[E][0] + *reinterpret_cast<const f32x4*>(Lp + int64_t(d_own) * DV + 16 * E + 4 * g4);
 #pragma unroll
       for (int D = 0; D < DB; ++D) {
-        const f32x4 fr = *reinterpret_cast<const f32x4*>(s_fT + i * DK + 16 * D + 4 * g4);
+        const f32x4 dr = *reinterpret_cast<const f32x4*>(Dp + 16 * D + 4 * g4);
 #pragma unroll
-        for (int ee = 0; ee < EBW; ++ee) L2[D][ee] *= fr;
+        for (int ee = 0; ee < EBW; ++ee)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            L2[D][ee][i] = ev_active ? dr[i] * L2[D][ee][i] + Lp[int64_t(16 * D + 4 * g4 + i) * DV + 16 * eblk(ee) + n]
+                                     : 0.f;
       }
     }
+    if (c1 == c0 && tid == 0) next = atomicAdd(counter, 1);  // empty piece
 
-    float db[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dd = 0; dd < DBW; ++dd) {
-      const int Dblk = w * DBW + dd;
-      const int d = 16 * Dblk + n;
-      // dq: dO S_i^T + dA Kt, then scale 2^{c_t}
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int P = 0; P < EB / 2; ++P) {
-        const s16x8 oa = join(ld4(s_do + (t0 + n) * RV + 32 * P + 4 * g4),
-                              ld4(s_do + (t0 + n) * RV + 32 * P + 16 + 4 * g4));
-        const s16x8 sb = join(pack4(S[2 * P][dd]), pack4(S[2 * P + 1][dd]));
-        acc = mfma32(oa, sb, acc);
-      }
-      const s16x4 ktv = tr4(tr_ptr(s_kt, RK, t0, 16 * Dblk, lane));  // Kt_t[d]
-      acc += mfma16(opdA, ktv, f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 Et = *reinterpret_cast<const f32x4*>(s_E + d * ES + t0 + 4 * g4);
-      const f32x4 qv = unpack4(tr4(tr_ptr(s_q, RK, t0, 16 * Dblk, lane)));
-      const f32x4 kv = unpack4(tr4(tr_ptr(s_k, RK, t0, 16 * Dblk, lane)));
-      float x[4], dqv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dqv[j] = scale * Et[j] * acc[j];
-        x[j] = qv[j] * (scale * Et[j] * (acc[j] - dgq[j] * bf2f(ktv[j])));  // exact product
-      }
-      // u: (2^{T_i} Lambda_i) v + dA^T Qh, then 2^{-c_s}
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int P = 0; P < EB / 2; ++P) {
-        const s16x8 va = join(ld4(s_v + (t0 + n) * RV + 32 * P + 4 * g4),
-                              ld4(s_v + (t0 + n) * RV + 32 * P + 16 + 4 * g4));
-        const s16x8 lb = join(pack4(L1[2 * P][dd]), pack4(L1[2 * P + 1][dd]));
-        acc = mfma32(va, lb, acc);
-      }
-      const s16x4 qhv = tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane));  // Qh_t[d]
-      acc += mfma16(opdAT, qhv, f32x4{0.f, 0.f, 0.f, 0.f});
-      float dkv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t0 + 4 * g4 + j;
-        const float re = __builtin_amdgcn_rcpf(Et[j]);
-        const float u = acc[j] * re;
-        dkv[j] = s_beta[t] * u;
-        x[j] -= kv[j] * (s_beta[t] * ((acc[j] - dgk[j] * bf2f(qhv[j])) * re));
-        db[j] = fmaf(kv[j], u, db[j]);
-      }
-      // dg: suffix sum over the sub-chunk's tokens, plus everything after it
-      float suf[4];
-      suf[3] = x[3];
-      suf[2] = x[2] + suf[3];
-      suf[1] = x[1] + suf[2];
-      suf[0] = x[0] + suf[1];
-      const float tg0 = __shfl(suf[0], n, 64), tg1 = __shfl(suf[0], n + 16, 64);
-      const float tg2 = __shfl(suf[0], n + 32, 64), tg3 = __shfl(suf[0], n + 48, 64);
-      const float after = (g4 < 1 ? tg1 : 0.f) + (g4 < 2 ? tg2 : 0.f) + (g4 < 3 ? tg3 : 0.f) + r[dd];
-      r[dd] += (tg0 + tg1) + (tg2 + tg3);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t off = ((uint32_t(t0 + 4 * g4 + j) * H + h) * DK + d) * 2;
-        st_bf16(r_dq, off, dqv[j]);
-        st_bf16(r_dk, off, dkv[j]);
-        st_bf16(r_dg, off, suf[j] + after);
-      }
-    }
-    // dbeta partials: over this lane's channels, then the 16 lanes of a row group
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float p = db[j];
-      p += __shfl_xor(p, 1, 64);
-      p += __shfl_xor(p, 2, 64);
-      p += __shfl_xor(p, 4, 64);
-      p += __shfl_xor(p, 8, 64);
-      if (n == 0) s_db[(i * NW + w) * 16 + 4 * g4 + j] = p;
-    }
+    for (int c = c1 - 1; c >= c0; --c) {
+      if (c == c0 && tid == 0) next = atomicAdd(counter, 1);
+      const int gc = cbase + c;
+      const int64_t a = seg_start + int64_t(kC) * c;
+      const int L = int(seg_end - a < kC ? seg_end - a : kC);
+      const int nsub = (L + 15) >> 4;
+      // gradient rows of this chunk's tokens (all heads); stores past token L are dropped
+      const auto r_dq = rsrc(dq + a * H * DK, uint32_t(L) * H * DK * 2);
+      const auto r_dk = rsrc(dk + a * H * DK, uint32_t(L) * H * DK * 2);
+      const auto r_dg = rsrc(dg + a * H * DK, uint32_t(L) * H * DK * 2);
+      const auto r_dv = rsrc(dv + a * H * DV, uint32_t(L) * H * DV * 2);
+      const int64_t soff = (int64_t(gc) * H + h) * DK * DV;
+      // S_c from the workspace, raw bf16: issued with the input loads, so its
+      // latency overlaps the scan below
+      s16x4 Sc[EB][DBW];
 
-    // dv: Kt (2^{T_i} Lambda_i) + A^T dO, columns e of this wave
+      // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads,
+      // all issued before the first LDS store
+      // Buffer resources over the chunk's rows of head h (32-bit offsets, rows
+      // past the chunk's end read 0): a 64-bit address per lane and tensor
+      // would be held across the chunk loop.
+      {
+        constexpr int NX = kC * DK / 8 / NT, NY = kC * DV / 8 / NT;
+        const uint32_t rowK = uint32_t(H) * DK * 2, rowV = uint32_t(H) * DV * 2;
+        const int64_t tb = a * H + h;  // token a, head h
+        const uint32_t nK = uint32_t(L - 1) * rowK + DK * 2, nV = uint32_t(L - 1) * rowV + DV * 2;
+        const auto rq = rsrc(q + tb * DK, nK), rk = rsrc(k + tb * DK, nK), rg = rsrc(g + tb * DK, nK);
+        const auto rv = rsrc(v + tb * DV, nV), rd = rsrc(dout + tb * DV, nV);
+        const auto rb = rsrc(beta + tb, uint32_t(L - 1) * H * 2 + 2);
+        const auto rs = rsrc(Sws + soff, DK * DV * 2);
+        auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
+          return __builtin_bit_cast(s16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        };
+        s16x8 xq[NX], xk[NX], xg[NX], xv[NY], xd[NY];
 #pragma unroll
-    for (int ee = 0; ee < EBW; ++ee) {
-      if (!ev_active) break;
-      const int Eblk = eblk(ee);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < NX; ++r) {
+          const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+          const uint32_t off = uint32_t(t) * rowK + c8 * 2;
+          xq[r] = ld16(rq, off);
+          xk[r] = ld16(rk, off);
+          xg[r] = ld16(rg, off);
+        }
 #pragma unroll
-      for (int P = 0; P < DB / 2; ++P) {
-        const int d0 = 32 * P + 4 * g4, d1 = 32 * P + 16 + 4 * g4;
-        const s16x8 ka = join(ld4(s_kt + (t0 + n) * RK + d0), ld4(s_kt + (t0 + n) * RK + d1));
-        const s16x8 lb = join(pack4(L2[2 * P][ee]), pack4(L2[2 * P + 1][ee]));
-        acc = mfma32(ka, lb, acc);
+        for (int r = 0; r < NY; ++r) {
+          const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+          const uint32_t off = uint32_t(t) * rowV + c8 * 2;
+          xv[r] = ld16(rv, off);
+          xd[r] = ld16(rd, off);
+        }
+        const unsigned short xb = __builtin_amdgcn_raw_buffer_load_b16(rb, uint32_t(tid < kC ? tid : kC) * H * 2, 0, 0);
+#pragma unroll
+        for (int E = 0; E < EB; ++E) {
+          typedef int v2 __attribute__((ext_vector_type(2)));
+          Sc[E][0] = __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   rs, uint32_t(d_own * DV + 16 * E + 4 * g4) * 2, 0, 0));
+        }
+        // (every wave is past the previous chunk's LDS reads: its last barrier)
+#pragma unroll
+        for (int r = 0; r < NX; ++r) {
+          const int i = tid + NT * r, t = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+          *reinterpret_cast<s16x8*>(s_q + t * RK + c8) = xq[r];
+          *reinterpret_cast<s16x8*>(s_k + t * RK + c8) = xk[r];
+          *reinterpret_cast<s16x8*>(s_qh + t * RK + c8) = xg[r];
+        }
+#pragma unroll
+        for (int r = 0; r < NY; ++r) {
+          const int i = tid + NT * r, t = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+          *reinterpret_cast<s16x8*>(s_v + t * RV + c8) = xv[r];
+          *reinterpret_cast<s16x8*>(s_do + t * RV + c8) = xd[r];
+        }
+        if (tid < kC) s_beta[tid] = __uint_as_float(uint32_t(xb) << 16);
       }
-      acc += mfma16(opAT, tr4(tr_ptr(s_do, RV, t0, 16 * Eblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
+      __syncthreads();
+      // per (sub-chunk, channel): 2^{c_t}, Qh over g, Kt, and the sub-chunk total
+      for (int p = tid; p < 4 * DK; p += NT) {
+        const int j = p / DK, d = p % DK;
+        float c = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        st_bf16(r_dv, ((uint32_t(t0 + 4 * g4 + j) * H + h) * DV + 16 * Eblk + n) * 2, acc[j]);
-    }
+        for (int u = 0; u < 16; ++u) {
+          const int t = 16 * j + u;
+          c += to_f32(s_qh[t * RK + d]) * kLog2e;
+          const float e = ex2(c);
+          s_E[d * ES + t] = e;
+          s_qh[t * RK + d] = bf16(scale * to_f32(s_q[t * RK + d]) * e);
+          s_kt[t * RK + d] = bf16(s_beta[t] * to_f32(s_k[t * RK + d]) * ex2(-c));
+        }
+        s_T[j * DK + d] = c;
+        // 2^{-c} of Kt can leave the fp32 / bf16 range below this total
+        if (c < kGateRangeMinLog2 && flags != nullptr) atomicOr(flags, kFlagGateRange);
+      }
+      __syncthreads();
+      // decay factors of whole sub-chunks, once per chunk
+      if (tid < DK) {
+        const int d = tid;
+        float T[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          T[j] = s_T[j * DK + d];
+          s_fT[j * DK + d] = ex2(T[j]);
+        }
+#pragma unroll
+        for (int i = 1; i <= 4; ++i) {
+          float acc = 0.f;
+#pragma unroll
+          for (int j = i - 1; j >= 0; --j) {
+            acc += T[j];
+            s_fP[pidx(j, i) * DK + d] = ex2(acc);
+          }
+        }
+      }
+      __syncthreads();
 
-    // Lambda before sub-chunk i: 2^{T_i} Lambda_i + Qh^T dO (every register index static)
-    if (i > 0) {
+      // S^T before sub-chunk i, columns of this wave: 2^{sum_{j<i} T_j} S_c^T plus the
+      // sub-chunks before i, each with Kt scaled by 2^{sum_{j<=j'<i} T_j'}.
+      f32x4 S[EB][DBW];
+      auto state_at = [&](int i) {
+#pragma unroll
+        for (int dd = 0; dd < DBW; ++dd) {
+          const int d = 16 * (w * DBW + dd) + n;
+          const float f = i > 0 ? s_fP[pidx(0, i) * DK + d] : 1.f;
+          // S_c^T unpacked by a product with the identity, then scaled
+#pragma unroll
+          for (int E = 0; E < EB; ++E) S[E][dd] = f * mfma16(eye, Sc[E][dd], f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        for (int j = 0; j < i; ++j) {
+          s16x4 kb[DBW];
+#pragma unroll
+          for (int dd = 0; dd < DBW; ++dd) {
+            const int d = 16 * (w * DBW + dd) + n;
+            kb[dd] = pack4(s_fP[pidx(j, i) * DK + d] * unpack4(tr4(tr_ptr(s_kt, RK, 16 * j, 16 * (w * DBW + dd), lane))));
+          }
+#pragma unroll
+          for (int E = 0; E < EB; ++E) {
+            const s16x4 va = tr4(tr_ptr(s_v, RV, 16 * j, 16 * E, lane));
+#pragma unroll
+            for (int dd = 0; dd < DBW; ++dd) S[E][dd] = mfma16(va, kb[dd], S[E][dd]);
+          }
+        }
+      };
+
+      // G_c = sum_e Lambda_c * S_end, per key channel: the running gate gradient
+      float r[DBW];
+      state_at(nsub);
 #pragma unroll
       for (int dd = 0; dd < DBW; ++dd) {
-        const s16x4 qb = tr4(tr_ptr(s_qh, RK, t0, 16 * (w * DBW + dd), lane));
+        float p = 0.f;
 #pragma unroll
-        for (int E = 0; E < EB; ++E) L1[E][dd] = mfma16(tr4(tr_ptr(s_do, RV, t0, 16 * E, lane)), qb, L1[E][dd]);
+        for (int E = 0; E < EB; ++E)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p = fmaf(L1[E][dd][j], S[E][dd][j], p);
+        p += __shfl_xor(p, 16, 64);
+        p += __shfl_xor(p, 32, 64);
+        r[dd] = p;
       }
+
+      for (int i = nsub - 1; i >= 0; --i) {
+        state_at(i);
+        const int t0 = 16 * i;
+        // A, dA (rows t, column s) and dA^T (rows s, column t) of the sub-chunk
+        f32x4 Ac = {0.f, 0.f, 0.f, 0.f}, dA = Ac, dAT = Ac;
 #pragma unroll
-      for (int ee = 0; ee < EBW; ++ee) {
-        if (!ev_active) break;
-        const s16x4 ob = tr4(tr_ptr(s_do, RV, t0, 16 * eblk(ee), lane));
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          const s16x8 qa = ld8(s_qh + (t0 + n) * RK + 32 * kb + 8 * g4);
+          const s16x8 kt = ld8(s_kt + (t0 + n) * RK + 32 * kb + 8 * g4);
+          Ac = mfma32(qa, kt, Ac);
+        }
 #pragma unroll
-        for (int D = 0; D < DB; ++D) L2[D][ee] = mfma16(tr4(tr_ptr(s_qh, RK, t0, 16 * D, lane)), ob, L2[D][ee]);
+        for (int kb = 0; kb < DV / 32; ++kb) {
+          const s16x8 oa = ld8(s_do + (t0 + n) * RV + 32 * kb + 8 * g4);
+          const s16x8 va = ld8(s_v + (t0 + n) * RV + 32 * kb + 8 * g4);
+          dA = mfma32(oa, va, dA);
+          dAT = mfma32(va, oa, dAT);
+        }
+        f32x4 Am, dAm, dATm;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool lower = 4 * g4 + j >= n;  // row index >= column index
+          Am[j] = lower ? Ac[j] : 0.f;
+          dAm[j] = lower ? dA[j] : 0.f;
+          dATm[j] = (4 * g4 + j <= n) ? dAT[j] : 0.f;
+        }
+        const s16x4 opAT = pack4(Am);    // A-operand of A^T (rows s, slots t)
+        const s16x4 opdA = pack4(dATm);  // A-operand of dA (rows t, slots s)
+        const s16x4 opdAT = pack4(dAm);  // A-operand of dA^T (rows s, slots t)
+        // dA_tt as those operands hold it (bf16) for this lane's tokens t = t0 +
+        // 4 g4 + j. The products dA_tt Kt_t (in dq) and dA_tt Qh_t (in u) are the
+        // token's pair with itself: in q dq - k dk they cancel exactly, but only
+        // to bf16 rounding as computed, which swamps a small gate gradient
+        // (strong forgetting); dg takes both sums without them. The diagonal of
+        // a 16x16 result sits in register n - 4 g4 of the lanes with n in
+        // [4 g4, 4 g4 + 3]; they pass it on through the wave's own LDS slots (the
+        // wave's LDS operations complete in order).
+        f32x4 dgq, dgk;
+        {
+          float* dgw = s_dg + 32 * w;
+          const int jd = n - 4 * g4;
+          if (jd >= 0 && jd < 4) {
+            const float xq = jd == 0 ? dATm[0] : jd == 1 ? dATm[1] : jd == 2 ? dATm[2] : dATm[3];
+            const float xk = jd == 0 ? dAm[0] : jd == 1 ? dAm[1] : jd == 2 ? dAm[2] : dAm[3];
+            dgw[n] = __uint_as_float(pk2(xq, 0.f) << 16);  // rounded as pack4 rounds
+            dgw[16 + n] = __uint_as_float(pk2(xk, 0.f) << 16);
+          }
+          dgq = *reinterpret_cast<const f32x4*>(dgw + 4 * g4);
+          dgk = *reinterpret_cast<const f32x4*>(dgw + 16 + 4 * g4);
+        }
+
+        // 2^{T_i} Lambda_i in both orientations: used by u and dv, and the update
+        // to Lambda before sub-chunk i accumulates onto it
+#pragma unroll
+        for (int dd = 0; dd < DBW; ++dd) {
+          const float fT = s_fT[i * DK + 16 * (w * DBW + dd) + n];
+#pragma unroll
+          for (int E = 0; E < EB; ++E) L1[E][dd] *= fT;
+        }
+        if (ev_active) {
+#pragma unroll
+          for (int D = 0; D < DB; ++D) {
+            const f32x4 fr = *reinterpret_cast<const f32x4*>(s_fT + i * DK + 16 * D + 4 * g4);
+#pragma unroll
+            for (int ee = 0; ee < EBW; ++ee) L2[D][ee] *= fr;
+          }
+        }
+
+        float db[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dd = 0; dd < DBW; ++dd) {
+          const int Dblk = w * DBW + dd;
+          const int d = 16 * Dblk + n;
+          // dq: dO S_i^T + dA Kt, then scale 2^{c_t}
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int P = 0; P < EB / 2; ++P) {
+            const s16x8 oa = join(ld4(s_do + (t0 + n) * RV + 32 * P + 4 * g4),
+                                  ld4(s_do + (t0 + n) * RV + 32 * P + 16 + 4 * g4));
+            const s16x8 sb = join(pack4(S[2 * P][dd]), pack4(S[2 * P + 1][dd]));
+            acc = mfma32(oa, sb, acc);
+          }
+          const s16x4 ktv = tr4(tr_ptr(s_kt, RK, t0, 16 * Dblk, lane));  // Kt_t[d]
+          acc += mfma16(opdA, ktv, f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 Et = *reinterpret_cast<const f32x4*>(s_E + d * ES + t0 + 4 * g4);
+          const f32x4 qv = unpack4(tr4(tr_ptr(s_q, RK, t0, 16 * Dblk, lane)));
+          const f32x4 kv = unpack4(tr4(tr_ptr(s_k, RK, t0, 16 * Dblk, lane)));
+          float x[4], dqv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dqv[j] = scale * Et[j] * acc[j];
+            x[j] = qv[j] * (scale * Et[j] * (acc[j] - dgq[j] * bf2f(ktv[j])));  // exact product
+          }
+          // u: (2^{T_i} Lambda_i) v + dA^T Qh, then 2^{-c_s}
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int P = 0; P < EB / 2; ++P) {
+            const s16x8 va = join(ld4(s_v + (t0 + n) * RV + 32 * P + 4 * g4),
+                                  ld4(s_v + (t0 + n) * RV + 32 * P + 16 + 4 * g4));
+            const s16x8 lb = join(pack4(L1[2 * P][dd]), pack4(L1[2 * P + 1][dd]));
+            acc = mfma32(va, lb, acc);
+          }
+          const s16x4 qhv = tr4(tr_ptr(s_qh, RK, t0, 16 * Dblk, lane));  // Qh_t[d]
+          acc += mfma16(opdAT, qhv, f32x4{0.f, 0.f, 0.f, 0.f});
+          float dkv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = t0 + 4 * g4 + j;
+            const float re = __builtin_amdgcn_rcpf(Et[j]);
+            const float u = acc[j] * re;
+            dkv[j] = s_beta[t] * u;
+            x[j] -= kv[j] * (s_beta[t] * ((acc[j] - dgk[j] * bf2f(qhv[j])) * re));
+            db[j] = fmaf(kv[j], u, db[j]);
+          }
+          // dg: suffix sum over the sub-chunk's tokens, plus everything after it
+          float suf[4];
+          suf[3] = x[3];
+          suf[2] = x[2] + suf[3];
+          suf[1] = x[1] + suf[2];
+          suf[0] = x[0] + suf[1];
+          const float tg0 = __shfl(suf[0], n, 64), tg1 = __shfl(suf[0], n + 16, 64);
+          const float tg2 = __shfl(suf[0], n + 32, 64), tg3 = __shfl(suf[0], n + 48, 64);
+          const float after = (g4 < 1 ? tg1 : 0.f) + (g4 < 2 ? tg2 : 0.f) + (g4 < 3 ? tg3 : 0.f) + r[dd];
+          r[dd] += (tg0 + tg1) + (tg2 + tg3);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t off = ((uint32_t(t0 + 4 * g4 + j) * H + h) * DK + d) * 2;
+            st_bf16(r_dq, off, dqv[j]);
+            st_bf16(r_dk, off, dkv[j]);
+            st_bf16(r_dg, off, suf[j] + after);
+          }
+        }
+        // dbeta partials: over this lane's channels, then the 16 lanes of a row group
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float p = db[j];
+          p += __shfl_xor(p, 1, 64);
+          p += __shfl_xor(p, 2, 64);
+          p += __shfl_xor(p, 4, 64);
+          p += __shfl_xor(p, 8, 64);
+          if (n == 0) s_db[(i * NW + w) * 16 + 4 * g4 + j] = p;
+        }
+
+        // dv: Kt (2^{T_i} Lambda_i) + A^T dO, columns e of this wave
+#pragma unroll
+        for (int ee = 0; ee < EBW; ++ee) {
+          if (!ev_active) break;
+          const int Eblk = eblk(ee);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int P = 0; P < DB / 2; ++P) {
+            const int d0 = 32 * P + 4 * g4, d1 = 32 * P + 16 + 4 * g4;
+            const s16x8 ka = join(ld4(s_kt + (t0 + n) * RK + d0), ld4(s_kt + (t0 + n) * RK + d1));
+            const s16x8 lb = join(pack4(L2[2 * P][ee]), pack4(L2[2 * P + 1][ee]));
+            acc = mfma32(ka, lb, acc);
+          }
+          acc += mfma16(opAT, tr4(tr_ptr(s_do, RV, t0, 16 * Eblk, lane)), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            st_bf16(r_dv, ((uint32_t(t0 + 4 * g4 + j) * H + h) * DV + 16 * Eblk + n) * 2, acc[j]);
+        }
+
+        // Lambda before sub-chunk i: 2^{T_i} Lambda_i + Qh^T dO (every register index
+        // static); after sub-chunk 0 it is Lambda before the chunk, carried to the
+        // previous chunk
+        {
+#pragma unroll
+          for (int dd = 0; dd < DBW; ++dd) {
+            const s16x4 qb = tr4(tr_ptr(s_qh, RK, t0, 16 * (w * DBW + dd), lane));
+#pragma unroll
+            for (int E = 0; E < EB; ++E) L1[E][dd] = mfma16(tr4(tr_ptr(s_do, RV, t0, 16 * E, lane)), qb, L1[E][dd]);
+          }
+#pragma unroll
+          for (int ee = 0; ee < EBW; ++ee) {
+            if (!ev_active) break;
+            const s16x4 ob = tr4(tr_ptr(s_do, RV, t0, 16 * eblk(ee), lane));
+#pragma unroll
+            for (int D = 0; D < DB; ++D) L2[D][ee] = mfma16(tr4(tr_ptr(s_qh, RK, t0, 16 * D, lane)), ob, L2[D][ee]);
+          }
+        }
       }
+
+      __syncthreads();
+      if (tid < L) {
+        const int i = tid >> 4, s = tid & 15;
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) sum += s_db[(i * NW + ww) * 16 + s];
+        dbeta[(a + tid) * H + h] = bf16(sum);
+      }
+    }  // chunk loop
+    // d initial state: Lambda before the segment's first chunk (an empty
+    // segment passes dL/dfinal_state through)
+    if (j == 0 && dinit != nullptr) {
+#pragma unroll
+      for (int E = 0; E < EB; ++E)
+        *reinterpret_cast<f32x4*>(dinit + sh + int64_t(d_own) * DV + 16 * E + 4 * g4) = L1[E][0];
     }
+    if (tid == 0) *s_item = next;
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(*s_item);
+    __syncthreads();  // every wave has read it before it is written again
+  }  // item loop
+
+  // positions not covered by any segment get zero gradients (grid-strided)
+  int64_t cu_last = cu_at(cu, max_segs, N);
+  cu_last = cu_last < 0 ? 0 : (cu_last > N ? N : cu_last);
+  const int64_t stride = int64_t(gridDim.x) * NT;
+  const int64_t first = int64_t(blockIdx.x) * NT + tid;
+  const bf16 z = bf16(0.f);
+  for (int64_t i = first; i < (N - cu_last) * H * DK; i += stride) {
+    dq[cu_last * H * DK + i] = z;
+    dk[cu_last * H * DK + i] = z;
+    dg[cu_last * H * DK + i] = z;
   }
-  __syncthreads();
-  if (tid < L) {
-    const int i = tid >> 4, s = tid & 15;
-    float sum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) sum += s_db[(i * NW + ww) * 16 + s];
-    dbeta[(a + tid) * H + h] = bf16(sum);
-  }
+  for (int64_t i = first; i < (N - cu_last) * H * DV; i += stride) dv[cu_last * H * DV + i] = z;
+  for (int64_t i = first; i < (N - cu_last) * H; i += stride) dbeta[cu_last * H + i] = z;
 }
 
 // Workspace layout of one call (host side).
@@ -908,6 +1004,8 @@ struct BwdLayout {
   int64_t max_chunks, max_sums, max_pieces;
   size_t plan_bytes, state_bytes, sumL_bytes, sumD_bytes, bytes;
 };
+// Plan words: base, pbase, sbase ([max_segs + 1] each), the queue counter, then
+// order[max_pieces].
 BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   BwdLayout l;
@@ -915,11 +1013,11 @@ BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_s
   // pieces of cut segments: m <= ceil(n / kPieceLen) < n / 16 per cut segment (n > kCutMin)
   l.max_sums = l.max_chunks / 16 + 1;
   l.max_pieces = max_segs + l.max_sums;
-  l.plan_bytes = up((size_t(max_segs) + 1) * 4 * 3);
+  l.plan_bytes = up(((size_t(max_segs) + 1) * 3 + 1 + size_t(l.max_pieces)) * 4);
   l.state_bytes = up(size_t(l.max_chunks) * H * Dk * Dv * 2);
   l.sumL_bytes = up(size_t(l.max_sums) * 2 * H * Dk * Dv * 4);
   l.sumD_bytes = up(size_t(l.max_sums) * 2 * H * Dk * 4);
-  l.bytes = l.plan_bytes + 2 * l.state_bytes + l.sumL_bytes + l.sumD_bytes;
+  l.bytes = l.plan_bytes + l.state_bytes + l.sumL_bytes + l.sumD_bytes;
   return l;
 }
 
@@ -949,10 +1047,11 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   int32_t* base = reinterpret_cast<int32_t*>(w);
   int32_t* pbase = base + (max_segs + 1);
   int32_t* sbase = pbase + (max_segs + 1);
+  int32_t* counter = sbase + (max_segs + 1);
+  int32_t* order = counter + 1;
   bf16* Sws = reinterpret_cast<bf16*>(w + l.plan_bytes);
-  bf16* Lws = reinterpret_cast<bf16*>(w + l.plan_bytes + l.state_bytes);
-  float* sumL = reinterpret_cast<float*>(w + l.plan_bytes + 2 * l.state_bytes);
-  float* sumD = reinterpret_cast<float*>(w + l.plan_bytes + 2 * l.state_bytes + l.sumL_bytes);
+  float* sumL = reinterpret_cast<float*>(w + l.plan_bytes + l.state_bytes);
+  float* sumD = reinterpret_cast<float*>(w + l.plan_bytes + l.state_bytes + l.sumL_bytes);
   const bf16* qb = static_cast<const bf16*>(q);
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
@@ -961,18 +1060,21 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   const bf16* ob = static_cast<const bf16*>(dout);
   hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, max_segs, N, H,
                      int32_t(l.max_chunks), int32_t(l.max_pieces), int32_t(l.max_sums), base, pbase,
-                     sbase, flags);
+                     sbase, order, counter, flags);
+  // summaries of the pieces of cut segments, both roles
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, true>), dim3(unsigned(2 * l.max_sums * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, Lws, sumL, sumD, dinit);
-  hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(2 * l.max_pieces * H)),
+                     max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD);
+  // the walk, S role only: the state before every chunk
+  hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(l.max_pieces * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, Lws, sumL, sumD, dinit);
-  hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(l.max_chunks * H + kTailBlocks)),
-                     dim3(CC::NT), CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, max_segs,
-                     int32_t(l.max_chunks), N, H, scale, Sws, Lws, static_cast<bf16*>(dq),
+                     max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD);
+  // the chunks of each (piece, head) walked backwards, Lambda carried
+  hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(device_cus() * CC::WG_PER_CU)), dim3(CC::NT),
+                     CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, order, counter,
+                     max_segs, N, H, scale, dF, sumL, sumD, Sws, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
-                     static_cast<bf16*>(db), flags);
+                     static_cast<bf16*>(db), dinit, flags);
   return hipGetLastError();
 }
 
@@ -983,7 +1085,8 @@ bool kda_chunk_bwd_supported(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32
   if (dtype != 0 || !(Dk == 64 || Dk == 128) || !(Dv == 64 || Dv == 128)) return false;
   if (N < 1 || H < 1 || max_segs < 1) return false;
   const int64_t max_chunks = (N + kC - 1) / kC + max_segs;
-  return max_chunks * H + kTailBlocks < (int64_t(1) << 31) && max_chunks < (int64_t(1) << 31);
+  const int64_t max_pieces = max_segs + max_chunks / 16 + 1;
+  return max_pieces * H < (int64_t(1) << 31) && max_chunks * H < (int64_t(1) << 31);
 }
 
 size_t kda_chunk_bwd_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
