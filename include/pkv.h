@@ -331,7 +331,8 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
  * chunk boundary (the adjoint dL/dS is carried in registers while the
  * chunks are walked backwards), and, for segments long enough to be cut into
  * pieces, fp32 piece summaries (end state and decay product per piece and
- * role), all written and read within the call (scratch: calls sharing a
+ * role), and per (segment slot, head, key channel) an fp32 final-state term of
+ * the gate gradient, all written and read within the call (scratch: calls sharing a
  * workspace must be ordered on one stream); see
  * pkv_chunk_kda_varlen_backward_workspace_size() for its size. Every other
  * shape runs token-serially and needs no workspace (size

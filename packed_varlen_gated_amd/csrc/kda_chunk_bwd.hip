@@ -21,7 +21,9 @@
 //            value; rows scaled per key channel; Lambda walks backwards.)
 //   walk     one work-group per (piece, head): S before every chunk (bf16 in the
 //            workspace), starting from the initial state composed with the
-//            earlier pieces' summaries.
+//            earlier pieces' summaries; when dL/dfinal_state is given, a
+//            segment's last piece walks on to the final state and leaves
+//            sum_e dL/dS_final * S_final per key channel.
 //   chunk    persistent work-groups over (piece, head) items, longest first:
 //            each walks its piece's chunks backwards, starting from
 //            dL/dfinal_state composed with the later pieces' adjoint summaries,
@@ -31,8 +33,7 @@
 //            chunk. Per chunk, from S_c and Lambda it walks the sub-chunks
 //            backwards. For sub-chunk i
 //            with within-sub-chunk cumulative c_t (log2) and total T_i, S_i the
-//            state before it (formed directly from S_c) and Lambda_i the adjoint
-//            after it (carried):
+//            state before it and Lambda_i the adjoint after it (carried):
 //              Qh_t = scale q_t 2^{c_t}, Kt_s = beta_s k_s 2^{-c_s},
 //              A = (Qh Kt^T) masked t >= s, dA = (dO V^T) masked t >= s,
 //              dq_t  = scale 2^{c_t} (S_i do_t + sum_s dA_ts Kt_s)
@@ -40,10 +41,16 @@
 //              dk_s  = beta_s u_s,  dbeta_s = k_s . u_s
 //              dv_s  = (Kt_s 2^{T_i})^T Lambda_i + sum_t A_ts do_t
 //              Lambda_{i-1} = 2^{T_i} Lambda_i + sum_t Qh_t do_t^T.
+//            S_i is never formed: S_i = 2^{T_0 + .. + T_{i-1}} S_c + sum over
+//            j < i of 2^{T_j + .. + T_{i-1}} Kt_j^T V_j, so S_i do_t takes S_c
+//            (bf16, as stored) and the blocks dA_ij = dO_i V_j^T, each scaled
+//            per key channel. The blocks A_ii and dA_ij (j <= i) are computed
+//            once per chunk and shared through LDS.
 //            dg_t is the sum over u >= t in the chunk of (q_u dq_u - k_u dk_u)
 //            plus G_c = sum_e Lambda_c * S_end (S_end the state after the
-//            chunk): the gate gradient at the chunk's first following token,
-//            which stands for all later tokens and the final-state cotangent.
+//            chunk: the next chunk's stored S, or the final state): the gate
+//            gradient at the chunk's first following token, which stands for
+//            all later tokens and the final-state cotangent.
 //
 // MFMA operand conventions (v_mfma_f32_16x16x16_bf16 and _16x16x32_bf16):
 // operand lane l has row (A) or column (B) l%16 and contraction slots of lane
@@ -52,8 +59,7 @@
 // and tiles of two adjacent result blocks feed a 16x16x32 product whose other
 // operand is read with the same contraction-index permutation. Lambda is kept
 // in two orientations (key channels per lane for the products contracting
-// over Dv, value channels per lane for those over Dk); the second one starts
-// from a product with the identity. A 16x16x16 product never accumulates
+// over Dv, value channels per lane for those over Dk). A 16x16x16 product never accumulates
 // straight onto a 16x16x32 result: its own accumulator is added afterwards
 // (taking the first as its C operand gave wrong rows).
 
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
     const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase, int32_t max_segs,
     int32_t units, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
     const float* __restrict__ dfinal, bf16* __restrict__ Sws, float* __restrict__ sumL,
-    float* __restrict__ sumD) {
+    float* __restrict__ sumD, float* __restrict__ gfin) {
   using C = StCfg<DK, DV>;
   constexpr int EB = DV / 16, NT = C::NT, NX = C::NX, NY = C::NY;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -416,8 +422,10 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
   };
 
   // S role: chunks c0 .. c1-1 (a walk stores S before each and skips the last
-  // update); Lambda role: chunks c1-1 .. c0, every update applied
-  const int napply = (adjoint || kSum) ? nch : nch - 1;
+  // update, except in a segment's last piece when dL/dfinal_state is given: there
+  // it reaches the final state); Lambda role: chunks c1-1 .. c0, every update applied
+  const bool fin = !kSum && !adjoint && dfinal != nullptr && j == m - 1;
+  const int napply = (adjoint || kSum || fin) ? nch : nch - 1;
   auto chunk_of = [&](int it) { return adjoint ? c1 - 1 - it : c0 + it; };
   auto step = [&]() {  // the chunk whose inputs are in LDS: scan, then update X
     __syncthreads();
@@ -482,6 +490,19 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
     step();
     if (!kSum && napply < nch) store_state(ws_out, cbase + chunk_of(napply));
   }
+  if (fin) {
+    // the gate gradient at the segment's end: sum_e dL/dS_final * S_final, per key channel
+    float p = 0.f;
+#pragma unroll
+    for (int E = 0; E < EB; ++E) {
+      const f32x4 df = *reinterpret_cast<const f32x4*>(dfinal + sh + int64_t(d_own) * DV + 16 * E + 4 * g4);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) p = fmaf(df[jj], X[E][jj], p);
+    }
+    p += __shfl_xor(p, 16, 64);
+    p += __shfl_xor(p, 32, 64);
+    if (g4 == 0) gfin[(int64_t(slot) * H + h) * DK + d_own] = p;
+  }
   if (kSum) {
     const int s_ = u;
     float* Lp = sumL_at(s_, adjoint);
@@ -497,24 +518,31 @@ template <int DK, int DV>
 struct ChCfg {
   // one wave per 16 key channels: 8 waves at Dk = 128, 4 at Dk = 64
   static constexpr int NW = DK / 16, NT = 64 * NW;
-  static constexpr int RK = DK + 8, RV = DV + 8, ES = kC + 4;
+  static constexpr int RK = DK + 8, RV = DV + 8;
   static constexpr int o_q = 0;                         // bf16 [64][RK] raw q
   static constexpr int o_k = o_q + kC * RK * 2;         // raw k
   static constexpr int o_qh = o_k + kC * RK * 2;        // Qh = scale q 2^{c}
   static constexpr int o_kt = o_qh + kC * RK * 2;       // Kt = beta k 2^{-c}
   static constexpr int o_v = o_kt + kC * RK * 2;        // bf16 [64][RV]
   static constexpr int o_do = o_v + kC * RV * 2;
-  static constexpr int o_E = o_do + kC * RV * 2;        // fp32 [DK][ES]: 2^{c_t}, channel-major
-  static constexpr int o_T = o_E + DK * ES * 4;         // fp32 [4][DK]: sub-chunk totals (log2)
-  static constexpr int o_fT = o_T + 4 * DK * 4;        // fp32 [4][DK]: 2^{T_i}
-  static constexpr int o_fP = o_fT + 4 * DK * 4;       // fp32 [10][DK]: 2^{T_j + .. + T_{i-1}}, j < i <= 4
-  static constexpr int o_db = o_fP + 10 * DK * 4;       // fp32 [4 sub-chunks][NW waves][16]
+  // fp32 [DK][64]: 2^{c_t}, channel-major, the 4-token groups of row d at group
+  // (t / 4) ^ (d % 16) (reads of 16 channels' f32x4 meet no bank twice)
+  static constexpr int o_E = o_do + kC * RV * 2;
+  // fp32 [7][DK]: 2^{T_j + .. + T_{i-1}} for j < i <= 3 at row i (i - 1) / 2 + j, and
+  // 2^{T_3} at row 6; its first word also passes the next item's index at item ends
+  static constexpr int o_fP = o_E + DK * kC * 4;
+  // fp32 [4][DK]: the sub-chunk totals (log2) after the gate scan; in the same words
+  // later, fp32 [4 sub-chunks][NW waves][16]: dbeta partials
+  static constexpr int o_db = o_fP + 7 * DK * 4;
+  static constexpr int o_T = o_db;
   static constexpr int o_beta = o_db + 4 * NW * 16 * 4; // fp32 [64]
-  static constexpr int o_dg = o_beta + kC * 4;          // fp32 [NW waves][2][16]: diagonals of dA
-  static constexpr int o_item = o_dg + NW * 32 * 4;     // int: the next (piece, head) item
-  static constexpr int bytes = o_item + 16;
+  // bf16 [14][16][16] sub-chunk blocks, each stored column-major ([s][t]): the four
+  // masked diagonal blocks of A, then dA (i, j) for j <= i at 4 + i (i + 1) / 2 + j
+  static constexpr int o_blk = o_beta + kC * 4;
+  static constexpr int bytes = o_blk + 14 * 256 * 2;
   // persistent work-groups per CU: as many as the LDS holds (two at Dk = Dv = 64)
   static constexpr int WG_PER_CU = bytes <= 80 * 1024 ? 2 : 1;
+  static_assert(DK != 64 || DV != 64 || WG_PER_CU == 2, "two work-groups per CU at Dk = Dv = 64");
 };
 
 template <int DK, int DV>
@@ -525,7 +553,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
     const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase,
     const int32_t* __restrict__ order, int32_t* __restrict__ counter, int32_t max_segs, int64_t N,
     int32_t H, float scale, const float* __restrict__ dfinal, const float* __restrict__ sumL,
-    const float* __restrict__ sumD, const bf16* __restrict__ Sws, bf16* __restrict__ dq,
+    const float* __restrict__ sumD, const float* __restrict__ gfin, const bf16* __restrict__ Sws, bf16* __restrict__ dq,
     bf16* __restrict__ dk, bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta,
     float* __restrict__ dinit, int32_t* __restrict__ flags) {
   using C = ChCfg<DK, DV>;
@@ -533,7 +561,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
   // key block w per wave; value blocks split over the waves (at Dv < Dk only the
   // first Dv / 16 waves take one)
   constexpr int DB = DK / 16, EB = DV / 16, DBW = 1, EBW = EB >= NW ? EB / NW : 1;
-  constexpr int RK = C::RK, RV = C::RV, ES = C::ES;
+  constexpr int RK = C::RK, RV = C::RV;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* s_q = reinterpret_cast<bf16*>(smem + C::o_q);
   bf16* s_k = reinterpret_cast<bf16*>(smem + C::o_k);
@@ -545,23 +573,18 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
   float* s_T = reinterpret_cast<float*>(smem + C::o_T);
   float* s_db = reinterpret_cast<float*>(smem + C::o_db);
   float* s_beta = reinterpret_cast<float*>(smem + C::o_beta);
-  float* s_fT = reinterpret_cast<float*>(smem + C::o_fT);
   float* s_fP = reinterpret_cast<float*>(smem + C::o_fP);
-  float* s_dg = reinterpret_cast<float*>(smem + C::o_dg);
-  int* s_item = reinterpret_cast<int*>(smem + C::o_item);
-  // row of 2^{T_j + .. + T_{i-1}} in s_fP
-  auto pidx = [](int j, int i) { return i * (i - 1) / 2 + j; };
+  bf16* s_blk = reinterpret_cast<bf16*>(smem + C::o_blk);
+  int* s_item = reinterpret_cast<int*>(smem + C::o_fP);
+  // row of 2^{T_j + .. + T_{i-1}} in s_fP (j < i <= 3, or j = 3, i = 4)
+  auto pidx = [](int j, int i) { return i < 4 ? i * (i - 1) / 2 + j : 6; };
+  auto ft_row = [&](int i) { return pidx(i, i + 1); };  // 2^{T_i}
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
   const bool ev_active = EB >= NW || w < EB;  // wave-uniform
   auto eblk = [&](int ee) { return EB >= NW ? w * EBW + ee : w; };
   const int d_own = 16 * w + n;  // key channel of this lane's L1 tiles (DBW = 1)
-  // identity 16x16 operand (either side)
-  s16x4 eye;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) eye[j] = (4 * g4 + j == n) ? short(0x3F80) : short(0);
-
   // Persistent work-groups over (piece, head) items, longest piece first (the
   // plan's order; item = rank * H + h). A work-group claims its next item when
   // it starts the current item's last chunk, and walks the piece's chunks from
@@ -622,6 +645,32 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
             L2[D][ee][i] = ev_active ? dr[i] * L2[D][ee][i] + Lp[int64_t(16 * D + 4 * g4 + i) * DV + 16 * eblk(ee) + n]
                                      : 0.f;
       }
+    }
+    // G, per key channel: the gate gradient from everything after the chunk being
+    // walked, sum_e Lambda * S_end (Lambda the adjoint after the chunk, S_end the
+    // state after it). S_end of the piece's last chunk is the next piece's first
+    // stored state, or at the segment's end the final state (the walk leaves its
+    // product with dL/dfinal_state); for every other chunk it is the S_c of the
+    // chunk walked before it.
+    auto sdot = [&](const s16x4 (&Sx)[EB][DBW]) {
+      float p = 0.f;
+#pragma unroll
+      for (int E = 0; E < EB; ++E)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) p = fmaf(L1[E][0][jj], bf2f(Sx[E][0][jj]), p);
+      p += __shfl_xor(p, 16, 64);
+      p += __shfl_xor(p, 32, 64);
+      return p;
+    };
+    float r = 0.f;
+    if (c1 > c0 && c1 < nseg) {
+      const bf16* Sn = Sws + (int64_t(cbase + c1) * H + h) * DK * DV + int64_t(d_own) * DV + 4 * g4;
+      s16x4 Sx[EB][DBW];
+#pragma unroll
+      for (int E = 0; E < EB; ++E) Sx[E][0] = ld4(Sn + 16 * E);
+      r = sdot(Sx);
+    } else if (c1 > c0 && gfin != nullptr) {
+      r = gfin[(int64_t(slot) * H + h) * DK + d_own];
     }
     if (c1 == c0 && tid == 0) next = atomicAdd(counter, 1);  // empty piece
 
@@ -707,7 +756,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
           const int t = 16 * j + u;
           c += to_f32(s_qh[t * RK + d]) * kLog2e;
           const float e = ex2(c);
-          s_E[d * ES + t] = e;
+          s_E[d * kC + (((t >> 2) ^ (d & 15)) << 2) + (t & 3)] = e;
           s_qh[t * RK + d] = bf16(scale * to_f32(s_q[t * RK + d]) * e);
           s_kt[t * RK + d] = bf16(s_beta[t] * to_f32(s_k[t * RK + d]) * ex2(-c));
         }
@@ -721,12 +770,9 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
         const int d = tid;
         float T[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          T[j] = s_T[j * DK + d];
-          s_fT[j * DK + d] = ex2(T[j]);
-        }
+        for (int j = 0; j < 4; ++j) T[j] = s_T[j * DK + d];
 #pragma unroll
-        for (int i = 1; i <= 4; ++i) {
+        for (int i = 1; i <= 3; ++i) {
           float acc = 0.f;
 #pragma unroll
           for (int j = i - 1; j >= 0; --j) {
@@ -734,115 +780,62 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
             s_fP[pidx(j, i) * DK + d] = ex2(acc);
           }
         }
+        s_fP[pidx(3, 4) * DK + d] = ex2(T[3]);
+      }
+      // the sub-chunk blocks, each computed by one wave (wave w takes blocks w, w +
+      // NW, ..): A_ii = Qh_i Kt_i^T and dA_ij = dO_i V_j^T for j <= i, rows t and
+      // columns s, the diagonal blocks masked to t >= s
+      for (int b = __builtin_amdgcn_readfirstlane(w); b < 14; b += NW) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        bool diag = true;
+        if (b < 4) {
+#pragma unroll
+          for (int kb = 0; kb < DK / 32; ++kb)
+            acc = mfma32(ld8(s_qh + (16 * b + n) * RK + 32 * kb + 8 * g4),
+                         ld8(s_kt + (16 * b + n) * RK + 32 * kb + 8 * g4), acc);
+        } else {
+          const int x = b - 4, i = x < 1 ? 0 : x < 3 ? 1 : x < 6 ? 2 : 3, jb = x - i * (i + 1) / 2;
+          diag = jb == i;
+#pragma unroll
+          for (int kb = 0; kb < DV / 32; ++kb)
+            acc = mfma32(ld8(s_do + (16 * i + n) * RV + 32 * kb + 8 * g4),
+                         ld8(s_v + (16 * jb + n) * RV + 32 * kb + 8 * g4), acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = (diag && 4 * g4 + j < n) ? 0.f : acc[j];
+        // column-major: element (t, s) at s * 16 + t
+        *reinterpret_cast<s16x4*>(s_blk + b * 256 + n * 16 + 4 * g4) = pack4(acc);
       }
       __syncthreads();
 
-      // S^T before sub-chunk i, columns of this wave: 2^{sum_{j<i} T_j} S_c^T plus the
-      // sub-chunks before i, each with Kt scaled by 2^{sum_{j<=j'<i} T_j'}.
-      f32x4 S[EB][DBW];
-      auto state_at = [&](int i) {
-#pragma unroll
-        for (int dd = 0; dd < DBW; ++dd) {
-          const int d = 16 * (w * DBW + dd) + n;
-          const float f = i > 0 ? s_fP[pidx(0, i) * DK + d] : 1.f;
-          // S_c^T unpacked by a product with the identity, then scaled
-#pragma unroll
-          for (int E = 0; E < EB; ++E) S[E][dd] = f * mfma16(eye, Sc[E][dd], f32x4{0.f, 0.f, 0.f, 0.f});
-        }
-        for (int j = 0; j < i; ++j) {
-          s16x4 kb[DBW];
-#pragma unroll
-          for (int dd = 0; dd < DBW; ++dd) {
-            const int d = 16 * (w * DBW + dd) + n;
-            kb[dd] = pack4(s_fP[pidx(j, i) * DK + d] * unpack4(tr4(tr_ptr(s_kt, RK, 16 * j, 16 * (w * DBW + dd), lane))));
-          }
-#pragma unroll
-          for (int E = 0; E < EB; ++E) {
-            const s16x4 va = tr4(tr_ptr(s_v, RV, 16 * j, 16 * E, lane));
-#pragma unroll
-            for (int dd = 0; dd < DBW; ++dd) S[E][dd] = mfma16(va, kb[dd], S[E][dd]);
-          }
-        }
-      };
-
-      // G_c = sum_e Lambda_c * S_end, per key channel: the running gate gradient
-      float r[DBW];
-      state_at(nsub);
-#pragma unroll
-      for (int dd = 0; dd < DBW; ++dd) {
-        float p = 0.f;
-#pragma unroll
-        for (int E = 0; E < EB; ++E)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p = fmaf(L1[E][dd][j], S[E][dd][j], p);
-        p += __shfl_xor(p, 16, 64);
-        p += __shfl_xor(p, 32, 64);
-        r[dd] = p;
-      }
-
       for (int i = nsub - 1; i >= 0; --i) {
-        state_at(i);
         const int t0 = 16 * i;
-        // A, dA (rows t, column s) and dA^T (rows s, column t) of the sub-chunk
-        f32x4 Ac = {0.f, 0.f, 0.f, 0.f}, dA = Ac, dAT = Ac;
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-          const s16x8 qa = ld8(s_qh + (t0 + n) * RK + 32 * kb + 8 * g4);
-          const s16x8 kt = ld8(s_kt + (t0 + n) * RK + 32 * kb + 8 * g4);
-          Ac = mfma32(qa, kt, Ac);
-        }
-#pragma unroll
-        for (int kb = 0; kb < DV / 32; ++kb) {
-          const s16x8 oa = ld8(s_do + (t0 + n) * RV + 32 * kb + 8 * g4);
-          const s16x8 va = ld8(s_v + (t0 + n) * RV + 32 * kb + 8 * g4);
-          dA = mfma32(oa, va, dA);
-          dAT = mfma32(va, oa, dAT);
-        }
-        f32x4 Am, dAm, dATm;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool lower = 4 * g4 + j >= n;  // row index >= column index
-          Am[j] = lower ? Ac[j] : 0.f;
-          dAm[j] = lower ? dA[j] : 0.f;
-          dATm[j] = (4 * g4 + j <= n) ? dAT[j] : 0.f;
-        }
-        const s16x4 opAT = pack4(Am);    // A-operand of A^T (rows s, slots t)
-        const s16x4 opdA = pack4(dATm);  // A-operand of dA (rows t, slots s)
-        const s16x4 opdAT = pack4(dAm);  // A-operand of dA^T (rows s, slots t)
+        const bf16* blkA = s_blk + i * 256;                          // A_ii
+        const bf16* blkD = s_blk + (4 + i * (i + 1) / 2 + i) * 256;  // dA_ii
+        const s16x4 opAT = ld4(blkA + n * 16 + 4 * g4);              // A-operand of A^T (rows s, slots t)
+        const s16x4 opdAT = ld4(blkD + n * 16 + 4 * g4);             // A-operand of dA^T (rows s, slots t)
+        const s16x4 opdA = tr4(tr_ptr(blkD, 16, 0, 0, lane));        // A-operand of dA (rows t, slots s)
         // dA_tt as those operands hold it (bf16) for this lane's tokens t = t0 +
         // 4 g4 + j. The products dA_tt Kt_t (in dq) and dA_tt Qh_t (in u) are the
         // token's pair with itself: in q dq - k dk they cancel exactly, but only
         // to bf16 rounding as computed, which swamps a small gate gradient
-        // (strong forgetting); dg takes both sums without them. The diagonal of
-        // a 16x16 result sits in register n - 4 g4 of the lanes with n in
-        // [4 g4, 4 g4 + 3]; they pass it on through the wave's own LDS slots (the
-        // wave's LDS operations complete in order).
-        f32x4 dgq, dgk;
-        {
-          float* dgw = s_dg + 32 * w;
-          const int jd = n - 4 * g4;
-          if (jd >= 0 && jd < 4) {
-            const float xq = jd == 0 ? dATm[0] : jd == 1 ? dATm[1] : jd == 2 ? dATm[2] : dATm[3];
-            const float xk = jd == 0 ? dAm[0] : jd == 1 ? dAm[1] : jd == 2 ? dAm[2] : dAm[3];
-            dgw[n] = __uint_as_float(pk2(xq, 0.f) << 16);  // rounded as pack4 rounds
-            dgw[16 + n] = __uint_as_float(pk2(xk, 0.f) << 16);
-          }
-          dgq = *reinterpret_cast<const f32x4*>(dgw + 4 * g4);
-          dgk = *reinterpret_cast<const f32x4*>(dgw + 16 + 4 * g4);
-        }
+        // (strong forgetting); dg takes both sums without them.
+        f32x4 dgs;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dgs[j] = bf2f(reinterpret_cast<const short*>(blkD)[(4 * g4 + j) * 17]);
 
         // 2^{T_i} Lambda_i in both orientations: used by u and dv, and the update
         // to Lambda before sub-chunk i accumulates onto it
 #pragma unroll
         for (int dd = 0; dd < DBW; ++dd) {
-          const float fT = s_fT[i * DK + 16 * (w * DBW + dd) + n];
+          const float fT = s_fP[ft_row(i) * DK + 16 * (w * DBW + dd) + n];
 #pragma unroll
           for (int E = 0; E < EB; ++E) L1[E][dd] *= fT;
         }
         if (ev_active) {
 #pragma unroll
           for (int D = 0; D < DB; ++D) {
-            const f32x4 fr = *reinterpret_cast<const f32x4*>(s_fT + i * DK + 16 * D + 4 * g4);
+            const f32x4 fr = *reinterpret_cast<const f32x4*>(s_fP + ft_row(i) * DK + 16 * D + 4 * g4);
 #pragma unroll
             for (int ee = 0; ee < EBW; ++ee) L2[D][ee] *= fr;
           }
@@ -853,25 +846,33 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
         for (int dd = 0; dd < DBW; ++dd) {
           const int Dblk = w * DBW + dd;
           const int d = 16 * Dblk + n;
-          // dq: dO S_i^T + dA Kt, then scale 2^{c_t}
+          // dq: dO S_i^T + dA Kt, then scale 2^{c_t}, with S_i (the state before
+          // sub-chunk i) = 2^{T_0 + .. + T_{i-1}} S_c plus, per earlier sub-chunk j,
+          // 2^{T_j + .. + T_{i-1}} Kt_j^T V_j: dO S_i^T takes the first term from S_c
+          // (bf16, as stored) and the others as dA_ij Kt_j, each scaled per channel
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int P = 0; P < EB / 2; ++P) {
             const s16x8 oa = join(ld4(s_do + (t0 + n) * RV + 32 * P + 4 * g4),
                                   ld4(s_do + (t0 + n) * RV + 32 * P + 16 + 4 * g4));
-            const s16x8 sb = join(pack4(S[2 * P][dd]), pack4(S[2 * P + 1][dd]));
-            acc = mfma32(oa, sb, acc);
+            acc = mfma32(oa, join(Sc[2 * P][dd], Sc[2 * P + 1][dd]), acc);
+          }
+          if (i > 0) acc *= s_fP[pidx(0, i) * DK + d];
+          for (int j = 0; j < i; ++j) {
+            const s16x4 da = tr4(tr_ptr(s_blk + (4 + i * (i + 1) / 2 + j) * 256, 16, 0, 0, lane));
+            const s16x4 kj = tr4(tr_ptr(s_kt, RK, 16 * j, 16 * Dblk, lane));
+            acc += s_fP[pidx(j, i) * DK + d] * mfma16(da, kj, f32x4{0.f, 0.f, 0.f, 0.f});
           }
           const s16x4 ktv = tr4(tr_ptr(s_kt, RK, t0, 16 * Dblk, lane));  // Kt_t[d]
           acc += mfma16(opdA, ktv, f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 Et = *reinterpret_cast<const f32x4*>(s_E + d * ES + t0 + 4 * g4);
+          const f32x4 Et = *reinterpret_cast<const f32x4*>(s_E + d * kC + (((4 * i + g4) ^ (d & 15)) << 2));
           const f32x4 qv = unpack4(tr4(tr_ptr(s_q, RK, t0, 16 * Dblk, lane)));
           const f32x4 kv = unpack4(tr4(tr_ptr(s_k, RK, t0, 16 * Dblk, lane)));
           float x[4], dqv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             dqv[j] = scale * Et[j] * acc[j];
-            x[j] = qv[j] * (scale * Et[j] * (acc[j] - dgq[j] * bf2f(ktv[j])));  // exact product
+            x[j] = qv[j] * (scale * Et[j] * (acc[j] - dgs[j] * bf2f(ktv[j])));  // exact product
           }
           // u: (2^{T_i} Lambda_i) v + dA^T Qh, then 2^{-c_s}
           acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -891,7 +892,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
             const float re = __builtin_amdgcn_rcpf(Et[j]);
             const float u = acc[j] * re;
             dkv[j] = s_beta[t] * u;
-            x[j] -= kv[j] * (s_beta[t] * ((acc[j] - dgk[j] * bf2f(qhv[j])) * re));
+            x[j] -= kv[j] * (s_beta[t] * ((acc[j] - dgs[j] * bf2f(qhv[j])) * re));
             db[j] = fmaf(kv[j], u, db[j]);
           }
           // dg: suffix sum over the sub-chunk's tokens, plus everything after it
@@ -902,8 +903,8 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
           suf[0] = x[0] + suf[1];
           const float tg0 = __shfl(suf[0], n, 64), tg1 = __shfl(suf[0], n + 16, 64);
           const float tg2 = __shfl(suf[0], n + 32, 64), tg3 = __shfl(suf[0], n + 48, 64);
-          const float after = (g4 < 1 ? tg1 : 0.f) + (g4 < 2 ? tg2 : 0.f) + (g4 < 3 ? tg3 : 0.f) + r[dd];
-          r[dd] += (tg0 + tg1) + (tg2 + tg3);
+          const float after = (g4 < 1 ? tg1 : 0.f) + (g4 < 2 ? tg2 : 0.f) + (g4 < 3 ? tg3 : 0.f) + r;
+          r += (tg0 + tg1) + (tg2 + tg3);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t off = ((uint32_t(t0 + 4 * g4 + j) * H + h) * DK + d) * 2;
@@ -961,6 +962,8 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
           }
         }
       }
+      // G for the chunk before: Lambda before this chunk with S_c, its state after
+      r = sdot(Sc);
 
       __syncthreads();
       if (tid < L) {
@@ -1002,7 +1005,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
 // Workspace layout of one call (host side).
 struct BwdLayout {
   int64_t max_chunks, max_sums, max_pieces;
-  size_t plan_bytes, state_bytes, sumL_bytes, sumD_bytes, bytes;
+  size_t plan_bytes, state_bytes, sumL_bytes, sumD_bytes, gfin_bytes, bytes;
 };
 // Plan words: base, pbase, sbase ([max_segs + 1] each), the queue counter, then
 // order[max_pieces].
@@ -1017,7 +1020,8 @@ BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_s
   l.state_bytes = up(size_t(l.max_chunks) * H * Dk * Dv * 2);
   l.sumL_bytes = up(size_t(l.max_sums) * 2 * H * Dk * Dv * 4);
   l.sumD_bytes = up(size_t(l.max_sums) * 2 * H * Dk * 4);
-  l.bytes = l.plan_bytes + l.state_bytes + l.sumL_bytes + l.sumD_bytes;
+  l.gfin_bytes = up(size_t(max_segs) * H * Dk * 4);
+  l.bytes = l.plan_bytes + l.state_bytes + l.sumL_bytes + l.sumD_bytes + l.gfin_bytes;
   return l;
 }
 
@@ -1052,6 +1056,9 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   bf16* Sws = reinterpret_cast<bf16*>(w + l.plan_bytes);
   float* sumL = reinterpret_cast<float*>(w + l.plan_bytes + l.state_bytes);
   float* sumD = reinterpret_cast<float*>(w + l.plan_bytes + l.state_bytes + l.sumL_bytes);
+  // per (segment, head, key channel): sum_e dL/dS_final * S_final (written only
+  // when dL/dfinal_state is given)
+  float* gfin = reinterpret_cast<float*>(w + l.plan_bytes + l.state_bytes + l.sumL_bytes + l.sumD_bytes);
   const bf16* qb = static_cast<const bf16*>(q);
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
@@ -1064,15 +1071,15 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   // summaries of the pieces of cut segments, both roles
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, true>), dim3(unsigned(2 * l.max_sums * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD);
+                     max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin);
   // the walk, S role only: the state before every chunk
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(l.max_pieces * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD);
+                     max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin);
   // the chunks of each (piece, head) walked backwards, Lambda carried
   hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(device_cus() * CC::WG_PER_CU)), dim3(CC::NT),
                      CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, order, counter,
-                     max_segs, N, H, scale, dF, sumL, sumD, Sws, static_cast<bf16*>(dq),
+                     max_segs, N, H, scale, dF, sumL, sumD, dF ? gfin : nullptr, Sws, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
                      static_cast<bf16*>(db), dinit, flags);
   return hipGetLastError();

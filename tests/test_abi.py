@@ -218,7 +218,8 @@ def test_backward_workspace(lib):
     padded to 256 bytes), one bf16 state of Dk x Dv per (chunk, head), chunks =
     ceil(N / 64) + max_segs, and for the pieces of cut segments, at most
     chunks / 16 + 1 of them, an fp32 Dk x Dv state and Dk decay products per
-    (piece, role, head); other shapes need none."""
+    (piece, role, head), and Dk fp32 final-state gate terms per (slot, head);
+    other shapes need none."""
     size = lib.pkv_chunk_kda_varlen_backward_workspace_size
     up = lambda x: (x + 255) // 256 * 256
     for N, H, Dk, Dv, S in [(65536, 32, 128, 128, 256), (256, 2, 64, 64, 4), (1000, 3, 64, 128, 7),
@@ -226,7 +227,7 @@ def test_backward_workspace(lib):
         chunks = (N + 63) // 64 + S
         sums = chunks // 16 + 1
         expect = (up(4 * (3 * (S + 1) + 1 + S + sums)) + up(chunks * H * Dk * Dv * 2)
-                  + up(sums * 2 * H * Dk * Dv * 4) + up(sums * 2 * H * Dk * 4))
+                  + up(sums * 2 * H * Dk * Dv * 4) + up(sums * 2 * H * Dk * 4) + up(S * H * Dk * 4))
         assert size(N, H, Dk, Dv, S, 0) == expect, (N, H, S)
     assert size(256, 2, 32, 32, 4, 0) == 0 and size(256, 2, 64, 64, 4, 1) == 0
     need = size(256, 2, 64, 64, 4, 0)
