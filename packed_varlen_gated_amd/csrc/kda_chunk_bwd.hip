@@ -748,21 +748,51 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
       }
       __syncthreads();
       // per (sub-chunk, channel): 2^{c_t}, Qh over g, Kt, and the sub-chunk total
-      for (int p = tid; p < 4 * DK; p += NT) {
-        const int j = p / DK, d = p % DK;
-        float c = 0.f;
+      {
+        // thread: sub-chunk j, channels d and d + 1 (one 4-byte word of each bf16 row),
+        // tokens 8 hf .. 8 hf + 7 of the sub-chunk; the halves hf = 0, 1 of a unit sit
+        // in lanes l and l + 32 of one wave
+        static_assert(NT == 4 * DK, "one thread per (sub-chunk, channel pair, half)");
+        const int unit = 32 * w + (lane & 31), hf = lane >> 5;
+        const int j = unit / (DK / 2), d = 2 * (unit % (DK / 2)), tb = 16 * j + 8 * hf;
+        // all reads first (Qh overwrites g in place)
+        uint32_t gv[8], qv[8], kv[8];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int t = 16 * j + u;
-          c += to_f32(s_qh[t * RK + d]) * kLog2e;
-          const float e = ex2(c);
-          s_E[d * kC + (((t >> 2) ^ (d & 15)) << 2) + (t & 3)] = e;
-          s_qh[t * RK + d] = bf16(scale * to_f32(s_q[t * RK + d]) * e);
-          s_kt[t * RK + d] = bf16(s_beta[t] * to_f32(s_k[t * RK + d]) * ex2(-c));
+        for (int u = 0; u < 8; ++u) {
+          const int t = tb + u;
+          gv[u] = *reinterpret_cast<const uint32_t*>(s_qh + t * RK + d);
+          qv[u] = *reinterpret_cast<const uint32_t*>(s_q + t * RK + d);
+          kv[u] = *reinterpret_cast<const uint32_t*>(s_k + t * RK + d);
         }
-        s_T[j * DK + d] = c;
-        // 2^{-c} of Kt can leave the fp32 / bf16 range below this total
-        if (c < kGateRangeMinLog2 && flags != nullptr) atomicOr(flags, kFlagGateRange);
+        auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
+        auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+        // the first half's total starts the second half
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          p0 += lo(gv[u]);
+          p1 += hi(gv[u]);
+        }
+        const float o0 = __shfl_xor(p0, 32, 64), o1 = __shfl_xor(p1, 32, 64);
+        float c0 = hf ? o0 * kLog2e : 0.f, c1 = hf ? o1 * kLog2e : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int t = tb + u;
+          c0 += lo(gv[u]) * kLog2e;
+          c1 += hi(gv[u]) * kLog2e;
+          const float e0 = ex2(c0), e1 = ex2(c1);
+          s_E[d * kC + (((t >> 2) ^ (d & 15)) << 2) + (t & 3)] = e0;
+          s_E[(d + 1) * kC + (((t >> 2) ^ ((d + 1) & 15)) << 2) + (t & 3)] = e1;
+          *reinterpret_cast<uint32_t*>(s_qh + t * RK + d) = pk2(scale * lo(qv[u]) * e0, scale * hi(qv[u]) * e1);
+          const float bt = s_beta[t];
+          *reinterpret_cast<uint32_t*>(s_kt + t * RK + d) = pk2(bt * lo(kv[u]) * ex2(-c0), bt * hi(kv[u]) * ex2(-c1));
+        }
+        if (hf) {
+          s_T[j * DK + d] = c0;
+          s_T[j * DK + d + 1] = c1;
+          // 2^{-c} of Kt can leave the fp32 / bf16 range below this total
+          if ((c0 < kGateRangeMinLog2 || c1 < kGateRangeMinLog2) && flags != nullptr) atomicOr(flags, kFlagGateRange);
+        }
       }
       __syncthreads();
       // decay factors of whole sub-chunks, once per chunk
