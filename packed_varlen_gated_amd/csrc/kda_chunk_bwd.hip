@@ -127,6 +127,21 @@ __device__ __forceinline__ const bf16* tr_ptr(const bf16* tile, int rs, int r0, 
 }
 __device__ __forceinline__ s16x4 ld4(const bf16* p) { return *reinterpret_cast<const s16x4*>(p); }
 __device__ __forceinline__ s16x8 ld8(const bf16* p) { return *reinterpret_cast<const s16x8*>(p); }
+// The value of another lane of the same 16-lane row (DPP control kCtrl).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a row, in every lane: quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror (lane j of an 8-lane half takes lane 7 - j),
+// row_mirror (lane j of the row takes lane 15 - j).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
 
 // Raw buffer resource over [base, base + bytes): accesses at offsets past the end
 // are dropped (stores) or read 0 (loads).
@@ -305,11 +320,12 @@ struct StCfg {
 // segment: the piece walked from a zero state; its end state (S role: after the
 // piece; Lambda role: before it) and the product of its decays are stored.
 template <int DK, int DV, bool kSum>
-__global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 16) threads
+__global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_bwd_state_kernel(  // 64 (DK / 16) threads
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase, int32_t max_segs,
+    const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase,
+    const int32_t* __restrict__ order, int32_t max_segs,
     int32_t units, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
     const float* __restrict__ dfinal, bf16* __restrict__ Sws, float* __restrict__ sumL,
     float* __restrict__ sumD, float* __restrict__ gfin) {
@@ -326,11 +342,13 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
   const int64_t pairs = int64_t(units) * H;
   const bool adjoint = int64_t(blockIdx.x) >= pairs;
   const int64_t idx = adjoint ? int64_t(blockIdx.x) - pairs : int64_t(blockIdx.x);
-  const int u = int(idx / H), h = int(idx % H);
+  const int h = int(idx % H);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
-  // the unit: a summary slot or a piece, its segment slot and piece index j of m
+  // the unit: a summary slot or a piece (the walk takes the pieces longest first, in
+  // the plan's order), its segment slot and piece index j of m
   const int32_t* ubase = kSum ? sbase : pbase;
-  if (u >= ubase[max_segs]) return;
+  if (idx / H >= ubase[max_segs]) return;
+  const int u = kSum ? int(idx / H) : order[idx / H];
   const int slot = last_le(ubase, max_segs, u);
   const int j = u - ubase[slot];
   const int m = pbase[slot + 1] - pbase[slot];
@@ -447,13 +465,19 @@ __global__ __launch_bounds__(DK * 4, 2) void kda_bwd_state_kernel(  // 64 (DK / 
         off += pp < p4 ? x : 0.f;
         B += x;
       }
+      // eight tokens at a time, their reads before the in-place writes over g
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int t = 16 * p4 + u;
-        const float kq = to_f32(s_k[t * C::RX + d]);
-        // forward: kbar = beta k 2^{B - b_t}; adjoint: q' = scale q 2^{b_t}
-        s_x[t * C::RX + d] = adjoint ? bf16(scale * kq * ex2(off + lb[u]))
-                                     : bf16(s_beta[t] * kq * ex2(B - (off + lb[u])));
+      for (int u0 = 0; u0 < 16; u0 += 8) {
+        float kq[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kq[u] = to_f32(s_k[(16 * p4 + u0 + u) * C::RX + d]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int t = 16 * p4 + u0 + u;
+          // forward: kbar = beta k 2^{B - b_t}; adjoint: q' = scale q 2^{b_t}
+          s_x[t * C::RX + d] = adjoint ? bf16(scale * kq[u] * ex2(off + lb[u0 + u]))
+                                       : bf16(s_beta[t] * kq[u] * ex2(B - (off + lb[u0 + u])));
+        }
       }
       if (p4 == 0) s_dec[d] = ex2(B);
     }
@@ -581,7 +605,8 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
   auto ft_row = [&](int i) { return pidx(i, i + 1); };  // 2^{T_i}
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, n = lane & 15, g4 = lane >> 4;
+  const int lane = tid & 63, n = lane & 15, g4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const bool ev_active = EB >= NW || w < EB;  // wave-uniform
   auto eblk = [&](int ee) { return EB >= NW ? w * EBW + ee : w; };
   const int d_own = 16 * w + n;  // key channel of this lane's L1 tiles (DBW = 1)
@@ -815,7 +840,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
       // the sub-chunk blocks, each computed by one wave (wave w takes blocks w, w +
       // NW, ..): A_ii = Qh_i Kt_i^T and dA_ij = dO_i V_j^T for j <= i, rows t and
       // columns s, the diagonal blocks masked to t >= s
-      for (int b = __builtin_amdgcn_readfirstlane(w); b < 14; b += NW) {
+      for (int b = w; b < 14; b += NW) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         bool diag = true;
         if (b < 4) {
@@ -931,10 +956,16 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
           suf[2] = x[2] + suf[3];
           suf[1] = x[1] + suf[2];
           suf[0] = x[0] + suf[1];
-          const float tg0 = __shfl(suf[0], n, 64), tg1 = __shfl(suf[0], n + 16, 64);
-          const float tg2 = __shfl(suf[0], n + 32, 64), tg3 = __shfl(suf[0], n + 48, 64);
-          const float after = (g4 < 1 ? tg1 : 0.f) + (g4 < 2 ? tg2 : 0.f) + (g4 < 3 ? tg3 : 0.f) + r;
-          r += (tg0 + tg1) + (tg2 + tg3);
+          // the four rows' sums at this lane's column: rows 2m, 2m + 1 of the lane's
+          // row pair (v_permlane16_swap), then pair sums of rows 0-1 and 2-3
+          // (v_permlane32_swap)
+          const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(suf[0]), __float_as_uint(suf[0]), false, false);
+          const float ev = __uint_as_float(pr[0]), od = __uint_as_float(pr[1]), pair = ev + od;
+          const auto pt = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+          const float lo = __uint_as_float(pt[0]), hi = __uint_as_float(pt[1]);
+          // rows after this lane's row g4
+          const float after = ((g4 & 1) ? 0.f : od) + ((g4 & 2) ? 0.f : hi) + r;
+          r += lo + hi;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t off = ((uint32_t(t0 + 4 * g4 + j) * H + h) * DK + d) * 2;
@@ -946,11 +977,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
         // dbeta partials: over this lane's channels, then the 16 lanes of a row group
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float p = db[j];
-          p += __shfl_xor(p, 1, 64);
-          p += __shfl_xor(p, 2, 64);
-          p += __shfl_xor(p, 4, 64);
-          p += __shfl_xor(p, 8, 64);
+          const float p = row_sum16(db[j]);
           if (n == 0) s_db[(i * NW + w) * 16 + 4 * g4 + j] = p;
         }
 
@@ -1101,11 +1128,11 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   // summaries of the pieces of cut segments, both roles
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, true>), dim3(unsigned(2 * l.max_sums * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin);
+                     order, max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin);
   // the walk, S role only: the state before every chunk
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(l.max_pieces * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin);
+                     order, max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin);
   // the chunks of each (piece, head) walked backwards, Lambda carried
   hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(device_cus() * CC::WG_PER_CU)), dim3(CC::NT),
                      CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, order, counter,
