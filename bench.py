@@ -12,7 +12,8 @@ Modes used for profiling (no JSON line): --mode kernel (only chunk_kda_varlen,
 for rocprofv3 counters) and --mode copy (a plain device copy of known size,
 the calibration of the HBM byte counters). --mode backward times the reverse
 pass (chunk_kda_varlen_backward) on the same workload and prints its own JSON
-line (not the headline metric).
+line (not the headline metric); the default run also reports it, measured after
+the headline steps, under "legs".
 """
 
 import argparse
@@ -277,27 +278,32 @@ def main():
         log(f"kernel mode: {args.warmup + args.steps} launches of {DOMINANT_KERNEL}")
         return
 
-    if args.mode == "backward":
+    def time_backward(warmup, steps):
+        """One chunk_kda_varlen_backward call per step (seeded do, no state
+        arguments): wall ms per step and each call's seconds by HIP events on
+        the launch stream."""
         gen = torch.Generator(device=dev).manual_seed(2024)
         do = torch.randn(1, N, H, cfg.Dv, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
         bws = torch.empty(max(pkv.chunk_kda_varlen_backward_workspace_size(N, H, cfg.Dk, cfg.Dv, cfg.max_segs,
                                                                           q.dtype), 1),
                           dtype=torch.uint8, device=dev)
         cu_dev = res.cu_seqlens
-        for _ in range(args.warmup):
-            pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_dev, flags=flags, workspace=bws)
+        call = lambda: pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_dev, flags=flags, workspace=bws)
+        for _ in range(warmup):
+            call()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         t0 = time.perf_counter()
         for a_ev, b_ev in evs:
             a_ev.record()
-            pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_dev, flags=flags, workspace=bws)
+            call()
             b_ev.record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        ms = (t1 - t0) * 1000.0 / args.steps
-        calls = [a.elapsed_time(b) / 1000.0 for a, b in evs]
+        return (t1 - t0) * 1000.0 / steps, [a.elapsed_time(b) / 1000.0 for a, b in evs]
+
+    if args.mode == "backward":
+        ms, calls = time_backward(args.warmup, args.steps)
         call_s = sum(calls) / len(calls)
         cp = pct(calls)
         bb = backward_bytes(cfg, cu_host)
@@ -367,13 +373,17 @@ def main():
         return (t1 - t0) * 1000.0 / nsteps, calls, steps
 
     # Extra legs, measured before the headline steps and not part of `value`:
-    # the same workload with the final states toggled, and with q, k
-    # normalised inside the call (each after its own W warm-up steps); and a
-    # plain 1 GiB device copy, the measured bandwidth beside the published
-    # peak. They run first so the headline steps find the GPU at the clocks
-    # of sustained work (clocks rise over the first ~15 ms of work).
+    # a plain 1 GiB device copy (the measured bandwidth beside the published
+    # peak), then the same workload with the final states toggled and with q, k
+    # normalised inside the call (each after its own W warm-up steps). They run
+    # first, the copy first of all, so the headline steps follow compute-bound
+    # calls and find the GPU at the clocks of sustained work (clocks rise over
+    # the first ~15 ms of work, and a memory-bound copy lets them drop). The
+    # reverse pass on the same inputs is timed after the headline steps, so its
+    # heavier load cannot change their clocks.
     legs = {}
     if args.legs:
+        legs["copy_gbs"] = copy_bandwidth(dev)
         for name, kw, with_fs in (("output_final_state_" + ("off" if final_state else "on"),
                                    {"fstate": not final_state}, not final_state),
                                   ("qk_l2norm", {"l2": True}, final_state)):
@@ -387,7 +397,6 @@ def main():
                           "hbm_frac": b / lp["avg"] / 1e9 / HBM_PEAK_GBS}
             log(f"leg {name}: call {lp['avg'] * 1e6:.1f} us avg (median {lp['median'] * 1e6:.1f}); "
                 f"{b / lp['avg'] / 1e9 / HBM_PEAK_GBS:.3f} of HBM peak")
-        legs["copy_gbs"] = copy_bandwidth(dev)
         log(f"device copy of 1 GiB: {legs['copy_gbs']:.0f} GB/s (read + written) against the "
             f"{HBM_PEAK_GBS:.0f} GB/s published peak")
 
@@ -413,6 +422,16 @@ def main():
         f"= {achieved / HBM_PEAK_GBS:.3f} of HBM peak; MFMA {mfma_frac:.4f} of bf16 peak; "
         f"n_segs {n_segs}")
     log("calls in order (us): " + " ".join(f"{x * 1e6:.0f}" for x in kc))
+    if args.legs:
+        # the reverse pass on the same inputs (one chunk_kda_varlen_backward call per step)
+        bm, bc = time_backward(args.warmup, args.steps)
+        bp = pct(bc)
+        bb = backward_bytes(cfg, cu_host)
+        legs["backward"] = {"call_us": {k2: x * 1e6 for k2, x in bp.items()}, "ms_per_step": bm,
+                            "tokens_per_s": N / bp["avg"], "algorithmic_bytes": bb,
+                            "hbm_frac": bb / bp["avg"] / 1e9 / HBM_PEAK_GBS}
+        log(f"leg backward: call {bp['avg'] * 1e6:.1f} us avg (median {bp['median'] * 1e6:.1f}); "
+            f"{bb / bp['avg'] / 1e9 / HBM_PEAK_GBS:.3f} of HBM peak")
 
     cpu = None
     if not args.no_cpu_baseline:
