@@ -19,8 +19,9 @@
 //              Lam <- 2^{B} Lam + sum_t q'_t do_t^T,    q'_t = scale q_t 2^{b_t}
 //            (b_t the log2 cumulative gate from the chunk start, B its last
 //            value; rows scaled per key channel; Lambda walks backwards.)
-//   walk     one work-group per (piece, head): S before every chunk (bf16 in the
-//            workspace), starting from the initial state composed with the
+//   walk     one work-group per (piece, head): S before every chunk (bf16 in
+//            the workspace; not a segment's first when it is zero), starting
+//            from the initial state composed with the
 //            earlier pieces' summaries; when dL/dfinal_state is given, a
 //            segment's last piece walks on to the final state and leaves
 //            sum_e dL/dS_final * S_final per key channel.
@@ -127,10 +128,12 @@ __device__ __forceinline__ const bf16* tr_ptr(const bf16* tile, int rs, int r0, 
 }
 __device__ __forceinline__ s16x4 ld4(const bf16* p) { return *reinterpret_cast<const s16x4*>(p); }
 __device__ __forceinline__ s16x8 ld8(const bf16* p) { return *reinterpret_cast<const s16x8*>(p); }
-// The value of another lane of the same 16-lane row (DPP control kCtrl).
+// The value of another lane of the same 16-lane row (DPP control kCtrl; every lane
+// active: the zero-for-invalid-source setting, which never applies within a row,
+// lets the compiler fold the move into the add that uses it).
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
 }
 // Sum over the 16 lanes of a row, in every lane: quad_perm [1,0,3,2], quad_perm
 // [2,3,0,1], row_half_mirror (lane j of an 8-lane half takes lane 7 - j),
@@ -503,7 +506,9 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
     put();
     fetch(chunk_of(napply > 1 ? 1 : 0));
   }
-  if (!kSum) store_state(ws_out, cbase + chunk_of(0));
+  // (a segment's first state is zero without an initial state: not stored, the
+  // chunk pass takes zeros for it)
+  if (!kSum && (c0 > 0 || initial_state != nullptr)) store_state(ws_out, cbase + chunk_of(0));
   for (int it = 0; it < napply - 1; ++it) {
     step();
     put();
@@ -579,7 +584,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
     int32_t H, float scale, const float* __restrict__ dfinal, const float* __restrict__ sumL,
     const float* __restrict__ sumD, const float* __restrict__ gfin, const bf16* __restrict__ Sws, bf16* __restrict__ dq,
     bf16* __restrict__ dk, bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta,
-    float* __restrict__ dinit, int32_t* __restrict__ flags) {
+    float* __restrict__ dinit, int32_t* __restrict__ flags, int32_t has_init) {
   using C = ChCfg<DK, DV>;
   constexpr int NW = C::NW, NT = C::NT;
   // key block w per wave; value blocks split over the waves (at Dv < Dk only the
@@ -728,7 +733,9 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
         const auto rq = rsrc(q + tb * DK, nK), rk = rsrc(k + tb * DK, nK), rg = rsrc(g + tb * DK, nK);
         const auto rv = rsrc(v + tb * DV, nV), rd = rsrc(dout + tb * DV, nV);
         const auto rb = rsrc(beta + tb, uint32_t(L - 1) * H * 2 + 2);
-        const auto rs = rsrc(Sws + soff, DK * DV * 2);
+        // S_c; the zero state before a segment's first chunk (no initial state) is not
+        // stored: an empty range reads zeros without touching memory
+        const auto rs = rsrc(Sws + soff, (c > 0 || has_init) ? DK * DV * 2 : 0);
         auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
           return __builtin_bit_cast(s16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
         };
@@ -1138,7 +1145,7 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
                      CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, order, counter,
                      max_segs, N, H, scale, dF, sumL, sumD, dF ? gfin : nullptr, Sws, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
-                     static_cast<bf16*>(db), dinit, flags);
+                     static_cast<bf16*>(db), dinit, flags, int32_t(s0 != nullptr));
   return hipGetLastError();
 }
 
