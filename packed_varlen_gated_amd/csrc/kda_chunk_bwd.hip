@@ -716,9 +716,13 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
       const auto r_dg = rsrc(dg + a * H * DK, uint32_t(L) * H * DK * 2);
       const auto r_dv = rsrc(dv + a * H * DV, uint32_t(L) * H * DV * 2);
       const int64_t soff = (int64_t(gc) * H + h) * DK * DV;
-      // S_c from the workspace, raw bf16: issued with the input loads, so its
-      // latency overlaps the scan below
+      // S_c from the workspace, raw bf16 (the zero state before a segment's first
+      // chunk without an initial state is not stored: an empty range reads zeros
+      // without touching memory). Loaded once the chunk's tiles are in LDS: the
+      // tiles' loads then have the work-group's outstanding requests to themselves,
+      // and S_c's latency overlaps the gate scan and the sub-chunk blocks.
       s16x4 Sc[EB][DBW];
+      const auto rs = rsrc(Sws + soff, (c > 0 || has_init) ? DK * DV * 2 : 0);
 
       // ---- load: rows of q, k, g (g into the Qh tile), v and do with 16-byte loads,
       // all issued before the first LDS store
@@ -733,9 +737,6 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
         const auto rq = rsrc(q + tb * DK, nK), rk = rsrc(k + tb * DK, nK), rg = rsrc(g + tb * DK, nK);
         const auto rv = rsrc(v + tb * DV, nV), rd = rsrc(dout + tb * DV, nV);
         const auto rb = rsrc(beta + tb, uint32_t(L - 1) * H * 2 + 2);
-        // S_c; the zero state before a segment's first chunk (no initial state) is not
-        // stored: an empty range reads zeros without touching memory
-        const auto rs = rsrc(Sws + soff, (c > 0 || has_init) ? DK * DV * 2 : 0);
         auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
           return __builtin_bit_cast(s16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
         };
@@ -756,12 +757,6 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
           xd[r] = ld16(rd, off);
         }
         const unsigned short xb = __builtin_amdgcn_raw_buffer_load_b16(rb, uint32_t(tid < kC ? tid : kC) * H * 2, 0, 0);
-#pragma unroll
-        for (int E = 0; E < EB; ++E) {
-          typedef int v2 __attribute__((ext_vector_type(2)));
-          Sc[E][0] = __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                                                   rs, uint32_t(d_own * DV + 16 * E + 4 * g4) * 2, 0, 0));
-        }
         // (every wave is past the previous chunk's LDS reads: its last barrier)
 #pragma unroll
         for (int r = 0; r < NX; ++r) {
@@ -779,6 +774,10 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
         if (tid < kC) s_beta[tid] = __uint_as_float(uint32_t(xb) << 16);
       }
       __syncthreads();
+#pragma unroll
+      for (int E = 0; E < EB; ++E)
+        Sc[E][0] = __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 rs, uint32_t(d_own * DV + 16 * E + 4 * g4) * 2, 0, 0));
       // per (sub-chunk, channel): 2^{c_t}, Qh over g, Kt, and the sub-chunk total
       {
         // thread: sub-chunk j, channels d and d + 1 (one 4-byte word of each bf16 row),
