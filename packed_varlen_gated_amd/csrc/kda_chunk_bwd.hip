@@ -555,7 +555,8 @@ struct ChCfg {
   static constexpr int o_v = o_kt + kC * RK * 2;        // bf16 [64][RV]
   static constexpr int o_do = o_v + kC * RV * 2;
   // fp32 [DK][64]: 2^{c_t}, channel-major, the 4-token groups of row d at group
-  // (t / 4) ^ (d % 16) (reads of 16 channels' f32x4 meet no bank twice)
+  // (t / 4) ^ sigma(d), sigma(d) = (d / 4 % 16) ^ (4 (d % 4)): the f32x4 of 16
+  // consecutive channels, or of 16 channels 4 apart, meet no bank twice
   static constexpr int o_E = o_do + kC * RV * 2;
   // fp32 [7][DK]: 2^{T_j + .. + T_{i-1}} for j < i <= 3 at row i (i - 1) / 2 + j, and
   // 2^{T_3} at row 6; its first word also passes the next item's index at item ends
@@ -608,6 +609,10 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
   // row of 2^{T_j + .. + T_{i-1}} in s_fP (j < i <= 3, or j = 3, i = 4)
   auto pidx = [](int j, int i) { return i < 4 ? i * (i - 1) / 2 + j : 6; };
   auto ft_row = [&](int i) { return pidx(i, i + 1); };  // 2^{T_i}
+  // word of 2^{c_t} at channel d, token t in s_E
+  auto e_off = [](int d, int t) {
+    return d * kC + ((((t >> 2) ^ ((d >> 2) & 15) ^ ((d & 3) << 2))) << 2) + (t & 3);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, n = lane & 15, g4 = lane >> 4;
@@ -780,49 +785,68 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
                                                  rs, uint32_t(d_own * DV + 16 * E + 4 * g4) * 2, 0, 0));
       // per (sub-chunk, channel): 2^{c_t}, Qh over g, Kt, and the sub-chunk total
       {
-        // thread: sub-chunk j, channels d and d + 1 (one 4-byte word of each bf16 row),
-        // tokens 8 hf .. 8 hf + 7 of the sub-chunk; the halves hf = 0, 1 of a unit sit
-        // in lanes l and l + 32 of one wave
-        static_assert(NT == 4 * DK, "one thread per (sub-chunk, channel pair, half)");
-        const int unit = 32 * w + (lane & 31), hf = lane >> 5;
-        const int j = unit / (DK / 2), d = 2 * (unit % (DK / 2)), tb = 16 * j + 8 * hf;
+        // thread: sub-chunk j, channels d .. d + 3 (one 8-byte word of each bf16 row),
+        // tokens 4 qt .. 4 qt + 3 of the sub-chunk; the four quarters qt of a unit sit
+        // in the four 16-lane rows of one wave
+        static_assert(NT == 4 * DK, "one thread per (sub-chunk, channel quad, quarter)");
+        const int qt = g4, unit = 16 * w + n;
+        const int j = unit / (DK / 4), d = 4 * (unit % (DK / 4)), tb = 16 * j + 4 * qt;
         // all reads first (Qh overwrites g in place)
-        uint32_t gv[8], qv[8], kv[8];
+        u32x2 gv[4], qv[4], kv[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 4; ++u) {
           const int t = tb + u;
-          gv[u] = *reinterpret_cast<const uint32_t*>(s_qh + t * RK + d);
-          qv[u] = *reinterpret_cast<const uint32_t*>(s_q + t * RK + d);
-          kv[u] = *reinterpret_cast<const uint32_t*>(s_k + t * RK + d);
+          gv[u] = *reinterpret_cast<const u32x2*>(s_qh + t * RK + d);
+          qv[u] = *reinterpret_cast<const u32x2*>(s_q + t * RK + d);
+          kv[u] = *reinterpret_cast<const u32x2*>(s_k + t * RK + d);
         }
-        auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
-        auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
-        // the first half's total starts the second half
-        float p0 = 0.f, p1 = 0.f;
+        // channel d + ch of a row word pair
+        auto chv = [](u32x2 x, int ch) {
+          const uint32_t wd = x[ch >> 1];
+          return __uint_as_float((ch & 1) ? (wd & 0xffff0000u) : (wd << 16));
+        };
+        // the quarter's gate sum per channel, then the sums of the quarters before it
+        // (the rows of the lane's row pair by v_permlane16_swap, the pair sums by
+        // v_permlane32_swap)
+        float c[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          p0 += lo(gv[u]);
-          p1 += hi(gv[u]);
+        for (int ch = 0; ch < 4; ++ch) {
+          float p = 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) p += chv(gv[u], ch);
+          const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+          const float ev = __uint_as_float(pr[0]), od = __uint_as_float(pr[1]);
+          const float pair = ev + od;
+          const auto pt = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+          c[ch] = (((qt & 1) ? ev : 0.f) + ((qt & 2) ? __uint_as_float(pt[0]) : 0.f)) * kLog2e;
         }
-        const float o0 = __shfl_xor(p0, 32, 64), o1 = __shfl_xor(p1, 32, 64);
-        float c0 = hf ? o0 * kLog2e : 0.f, c1 = hf ? o1 * kLog2e : 0.f;
+        float e[4][4];  // [channel][token]
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 4; ++u) {
           const int t = tb + u;
-          c0 += lo(gv[u]) * kLog2e;
-          c1 += hi(gv[u]) * kLog2e;
-          const float e0 = ex2(c0), e1 = ex2(c1);
-          s_E[d * kC + (((t >> 2) ^ (d & 15)) << 2) + (t & 3)] = e0;
-          s_E[(d + 1) * kC + (((t >> 2) ^ ((d + 1) & 15)) << 2) + (t & 3)] = e1;
-          *reinterpret_cast<uint32_t*>(s_qh + t * RK + d) = pk2(scale * lo(qv[u]) * e0, scale * hi(qv[u]) * e1);
+          float ek[4];
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch) {
+            c[ch] += chv(gv[u], ch) * kLog2e;
+            e[ch][u] = ex2(c[ch]);
+            ek[ch] = ex2(-c[ch]);
+          }
+          *reinterpret_cast<u32x2*>(s_qh + t * RK + d) =
+              u32x2{pk2(scale * chv(qv[u], 0) * e[0][u], scale * chv(qv[u], 1) * e[1][u]),
+                    pk2(scale * chv(qv[u], 2) * e[2][u], scale * chv(qv[u], 3) * e[3][u])};
           const float bt = s_beta[t];
-          *reinterpret_cast<uint32_t*>(s_kt + t * RK + d) = pk2(bt * lo(kv[u]) * ex2(-c0), bt * hi(kv[u]) * ex2(-c1));
+          *reinterpret_cast<u32x2*>(s_kt + t * RK + d) =
+              u32x2{pk2(bt * chv(kv[u], 0) * ek[0], bt * chv(kv[u], 1) * ek[1]),
+                    pk2(bt * chv(kv[u], 2) * ek[2], bt * chv(kv[u], 3) * ek[3])};
         }
-        if (hf) {
-          s_T[j * DK + d] = c0;
-          s_T[j * DK + d + 1] = c1;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch)
+          *reinterpret_cast<f32x4*>(s_E + e_off(d + ch, tb)) = f32x4{e[ch][0], e[ch][1], e[ch][2], e[ch][3]};
+        if (qt == 3) {
+          *reinterpret_cast<f32x4*>(s_T + j * DK + d) = f32x4{c[0], c[1], c[2], c[3]};
           // 2^{-c} of Kt can leave the fp32 / bf16 range below this total
-          if ((c0 < kGateRangeMinLog2 || c1 < kGateRangeMinLog2) && flags != nullptr) atomicOr(flags, kFlagGateRange);
+          const float cm = fminf(fminf(c[0], c[1]), fminf(c[2], c[3]));
+          if (cm < kGateRangeMinLog2 && flags != nullptr) atomicOr(flags, kFlagGateRange);
         }
       }
       __syncthreads();
@@ -926,7 +950,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
           }
           const s16x4 ktv = tr4(tr_ptr(s_kt, RK, t0, 16 * Dblk, lane));  // Kt_t[d]
           acc += mfma16(opdA, ktv, f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 Et = *reinterpret_cast<const f32x4*>(s_E + d * kC + (((4 * i + g4) ^ (d & 15)) << 2));
+          const f32x4 Et = *reinterpret_cast<const f32x4*>(s_E + e_off(d, t0 + 4 * g4));
           const f32x4 qv = unpack4(tr4(tr_ptr(s_q, RK, t0, 16 * Dblk, lane)));
           const f32x4 kv = unpack4(tr4(tr_ptr(s_k, RK, t0, 16 * Dblk, lane)));
           float x[4], dqv[4];
