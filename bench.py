@@ -12,8 +12,11 @@ Modes used for profiling (no JSON line): --mode kernel (only chunk_kda_varlen,
 for rocprofv3 counters) and --mode copy (a plain device copy of known size,
 the calibration of the HBM byte counters). --mode backward times the reverse
 pass (chunk_kda_varlen_backward) on the same workload and prints its own JSON
-line (not the headline metric); the default run also reports it, measured after
-the headline steps, under "legs".
+line (not the headline metric); with --bwd-states the reverse pass reads the
+per-chunk states a forward call saved (chunk_kda_varlen(..., chunk_states=...))
+instead of recomputing them. The default run also reports both, measured after
+the headline steps, under "legs" (backward; backward_saved_states, with the
+saving forward call beside it).
 """
 
 import argparse
@@ -50,6 +53,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="oracle sample size in tokens (0: sized for ~15 s of CPU work)")
     p.add_argument("--mode", choices=["bench", "kernel", "copy", "backward"], default="bench")
+    p.add_argument("--bwd-states", action="store_true",
+                   help="--mode backward: the reverse pass reads the states a forward call saved")
     p.add_argument("--entry", choices=["cu_seqlens", "segment_ids"], default="cu_seqlens",
                    help="segment_ids: the step is one pkv_chunk_kda_segment_ids call on the [B, T] ids "
                         "(no conversion, no phantom slots) instead of the conversion + chunk_kda_varlen")
@@ -278,17 +283,9 @@ def main():
         log(f"kernel mode: {args.warmup + args.steps} launches of {DOMINANT_KERNEL}")
         return
 
-    def time_backward(warmup, steps):
-        """One chunk_kda_varlen_backward call per step (seeded do, no state
-        arguments): wall ms per step and each call's seconds by HIP events on
-        the launch stream."""
-        gen = torch.Generator(device=dev).manual_seed(2024)
-        do = torch.randn(1, N, H, cfg.Dv, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
-        bws = torch.empty(max(pkv.chunk_kda_varlen_backward_workspace_size(N, H, cfg.Dk, cfg.Dv, cfg.max_segs,
-                                                                          q.dtype), 1),
-                          dtype=torch.uint8, device=dev)
-        cu_dev = res.cu_seqlens
-        call = lambda: pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_dev, flags=flags, workspace=bws)
+    def time_calls(call, warmup, steps):
+        """warmup untimed calls, then steps calls: wall ms per call and each
+        call's seconds by HIP events on the launch stream."""
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
@@ -302,11 +299,49 @@ def main():
         t1 = time.perf_counter()
         return (t1 - t0) * 1000.0 / steps, [a.elapsed_time(b) / 1000.0 for a, b in evs]
 
+    chunk_states = None
+
+    def saving_forward():
+        """The forward call that also keeps the state before every chunk."""
+        return pkv.chunk_kda_varlen(q, k, v, g, beta, res.cu_seqlens, output_final_state=False, flags=flags,
+                                    out=o, workspace=ws, chunk_states=chunk_states)
+
+    def time_backward(warmup, steps, with_states=False):
+        """One chunk_kda_varlen_backward call per step (seeded do, no initial
+        or final state), recomputing the states or (with_states) reading the ones
+        a saving forward call left: wall ms per step and each call's seconds."""
+        nonlocal chunk_states
+        gen = torch.Generator(device=dev).manual_seed(2024)
+        do = torch.randn(1, N, H, cfg.Dv, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
+        size_fn = (pkv.chunk_kda_varlen_backward_states_workspace_size if with_states
+                   else pkv.chunk_kda_varlen_backward_workspace_size)
+        bws = torch.empty(max(size_fn(N, H, cfg.Dk, cfg.Dv, cfg.max_segs, q.dtype), 1),
+                          dtype=torch.uint8, device=dev)
+        cu_dev = res.cu_seqlens
+        st = None
+        if with_states:
+            if chunk_states is None:
+                chunk_states = pkv.new_chunk_states(N, H, cfg.Dk, cfg.Dv, cfg.max_segs, dev)
+            saving_forward()
+            st = chunk_states
+        call = lambda: pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_dev, flags=flags, workspace=bws,
+                                                     chunk_states=st)
+        return time_calls(call, warmup, steps)
+
+    def states_read_bytes():
+        """bf16 states the reverse pass reads when they are given: one per chunk
+        but a segment's first (zero without an initial state)."""
+        import numpy as np
+        lens = np.diff(cu_host.astype(np.int64))
+        chunks = int(np.sum((lens + 63) // 64)) - int(np.sum(lens > 0))
+        return chunks * H * cfg.Dk * cfg.Dv * 2
+
     if args.mode == "backward":
-        ms, calls = time_backward(args.warmup, args.steps)
+        ms, calls = time_backward(args.warmup, args.steps, args.bwd_states)
         call_s = sum(calls) / len(calls)
         cp = pct(calls)
-        bb = backward_bytes(cfg, cu_host)
+        # with saved states they are one more input
+        bb = backward_bytes(cfg, cu_host) + (states_read_bytes() if args.bwd_states else 0)
         achieved = bb / call_s / 1e9
         log(f"backward: {call_s * 1e3:.3f} ms per call (median {cp['median'] * 1e3:.3f}, p10 "
             f"{cp['p10'] * 1e3:.3f}, p90 {cp['p90'] * 1e3:.3f}); {achieved:.0f} GB/s = "
@@ -317,7 +352,9 @@ def main():
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
             "config": {"workload": cfg.name, "N": N, "H": H, "Dk": cfg.Dk, "Dv": cfg.Dv,
-                       "max_segs": cfg.max_segs, "n_segs": n_segs, "step": "chunk_kda_varlen_backward"},
+                       "max_segs": cfg.max_segs, "n_segs": n_segs,
+                       "step": "chunk_kda_varlen_backward" + (" (states saved by the forward call)"
+                                                              if args.bwd_states else "")},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "kernel": "chunk_kda_varlen_backward", "kernel_avg_us": call_s * 1e6,
@@ -432,6 +469,24 @@ def main():
                             "hbm_frac": bb / bp["avg"] / 1e9 / HBM_PEAK_GBS}
         log(f"leg backward: call {bp['avg'] * 1e6:.1f} us avg (median {bp['median'] * 1e6:.1f}); "
             f"{bb / bp['avg'] / 1e9 / HBM_PEAK_GBS:.3f} of HBM peak")
+        # the training pair with the states kept by the forward call: that call,
+        # then the reverse pass reading them
+        if pkv.chunk_kda_states_size(N, H, cfg.Dk, cfg.Dv, cfg.max_segs, q.dtype) > 0:
+            sm, sc = time_backward(args.warmup, args.steps, with_states=True)
+            fm, fc = time_calls(saving_forward, args.warmup, args.steps)
+            spp, fpp = pct(sc), pct(fc)
+            sb = bb + states_read_bytes()
+            legs["backward_saved_states"] = {
+                "call_us": {k2: x * 1e6 for k2, x in spp.items()}, "ms_per_step": sm,
+                "tokens_per_s": N / spp["avg"], "algorithmic_bytes": sb,
+                "hbm_frac": sb / spp["avg"] / 1e9 / HBM_PEAK_GBS,
+                "saving_forward_call_us": {k2: x * 1e6 for k2, x in fpp.items()},
+                "pair_us": (spp["avg"] + fpp["avg"]) * 1e6,
+                "pair_us_recomputing": (bp["avg"] + kc_avg_s) * 1e6}
+            log(f"leg backward_saved_states: call {spp['avg'] * 1e6:.1f} us avg (median "
+                f"{spp['median'] * 1e6:.1f}); the saving forward call {fpp['avg'] * 1e6:.1f} us avg; "
+                f"forward + reverse {(spp['avg'] + fpp['avg']) * 1e6:.0f} us against "
+                f"{(bp['avg'] + kc_avg_s) * 1e6:.0f} us recomputing")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -238,6 +238,45 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of the per-chunk state buffer of pkv_chunk_kda_varlen_states and
+ * pkv_chunk_kda_varlen_backward_states: bf16 [ceil(N / 64) + max_segs, H, Dk, Dv]
+ * (max_segs taken as 1 when cu_seqlens will be NULL). 0 when the shape has no
+ * chunked path (dtype other than PKV_BF16, Dk or Dv not in {64, 128}); those
+ * calls then return PKV_ERR_UNSUPPORTED.
+ */
+size_t pkv_chunk_kda_states_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs,
+                                 int32_t dtype);
+
+/*
+ * pkv_chunk_kda_varlen that also keeps, for the reverse pass, the state S before
+ * every 64-token chunk (RFC-0026 Background recurrence; chunks aligned to the
+ * segment starts as in the chunked forward pass). A training step can then run
+ * pkv_chunk_kda_varlen_backward_states, which reads these states instead of
+ * recomputing them from k, g, v and beta.
+ *
+ * Arguments, results and errors are those of pkv_chunk_kda_varlen, plus:
+ * chunk_states  device buffer of at least pkv_chunk_kda_states_size() bytes,
+ *               16-byte aligned, not overlapping any other argument. Chunk c of
+ *               slot i (tokens cu[i] + 64 c ...) is entry b_i + c, where b_i is
+ *               the number of chunks (ceil(length / 64), 0 for empty slots) of
+ *               the slots before i; entry [b_i + c, h] holds head h's S
+ *               (rows d, columns e) as bf16 row-major [Dk][Dv]. The
+ *               zero state before a segment's first chunk is not written when
+ *               initial_state is NULL; entries past the last chunk are left
+ *               alone. Only the bf16 chunked path (Dk, Dv in {64, 128}).
+ * Errors: as pkv_chunk_kda_varlen; PKV_ERR_UNSUPPORTED for a shape without the
+ * chunked path; PKV_ERR_INVALID_ARGUMENT for a missing, small, misaligned or
+ * overlapping chunk_states.
+ */
+pkv_status pkv_chunk_kda_varlen_states(const void* q, const void* k, const void* v, const void* g,
+                                       const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
+                                       int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                       int32_t dtype, int32_t options, const float* initial_state,
+                                       void* o, float* final_state, int32_t* flags, void* workspace,
+                                       size_t workspace_bytes, void* chunk_states,
+                                       size_t chunk_states_bytes, void* stream);
+
+/*
  * pkv_chunk_kda_varlen for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc. Arguments, results and errors are those of pkv_chunk_kda_varlen
@@ -324,8 +363,9 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
  * flags       int32 [1] or NULL; PKV_FLAG_BAD_CU_SEQLENS is OR-ed in (the
  *             gradients of an invalid slot are then left unwritten), and on
  *             the chunked path PKV_FLAG_GATE_RANGE as in the forward call.
- * The reverse pass recomputes the states (nothing is saved by the forward
- * call). For bf16 with Dk, Dv in {64, 128} it is chunked: the workspace holds
+ * This call recomputes the states (pkv_chunk_kda_varlen_backward_states reads
+ * them from the forward call instead). For bf16 with Dk, Dv in {64, 128} it is
+ * chunked: the workspace holds
  * the work plan (chunk, piece and summary offsets per slot, the pieces in
  * longest-first order, a work counter), the bf16 state at every 64-token
  * chunk boundary (the adjoint dL/dS is carried in registers while the
@@ -358,11 +398,40 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
                                          float* d_initial_state, int32_t* flags, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_chunk_kda_varlen_backward with the states the forward call saved
+ * (pkv_chunk_kda_varlen_states on the same q, k, v, g, beta, cu_seqlens,
+ * max_segs, scale and initial_state): the states before every chunk are read
+ * from chunk_states instead of being recomputed, so the call reads k, g, v and
+ * beta once instead of twice and keeps no states of its own. With dfinal_state
+ * given, each segment's last chunk is stepped once more from its saved state to
+ * reach the final state the gate gradient needs.
+ *
+ * Arguments, results and errors are those of pkv_chunk_kda_varlen_backward,
+ * plus chunk_states (at least pkv_chunk_kda_states_size() bytes, 16-byte
+ * aligned, read only, not overlapping an output or the workspace). The
+ * workspace needs pkv_chunk_kda_varlen_backward_states_workspace_size() bytes.
+ * Results equal pkv_chunk_kda_varlen_backward's up to the rounding of the
+ * states (both round them to bf16; the forward and reverse passes sum their
+ * updates in different orders). PKV_ERR_UNSUPPORTED for a shape without the
+ * chunked path.
+ */
+size_t pkv_chunk_kda_varlen_backward_states_workspace_size(int64_t N, int32_t H, int32_t Dk,
+                                                           int32_t Dv, int32_t max_segs,
+                                                           int32_t dtype);
+pkv_status pkv_chunk_kda_varlen_backward_states(
+    const void* q, const void* k, const void* v, const void* g, const void* beta,
+    const int32_t* cu_seqlens, int32_t max_segs, int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+    float scale, int32_t dtype, const float* initial_state, const void* do_,
+    const float* dfinal_state, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+    float* d_initial_state, int32_t* flags, void* workspace, size_t workspace_bytes,
+    const void* chunk_states, size_t chunk_states_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(int32_t status);
 
 /* ABI version of this header (bumped on any signature change). */
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 int32_t pkv_abi_version(void);
 
 #ifdef __cplusplus

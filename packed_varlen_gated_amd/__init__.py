@@ -74,6 +74,17 @@ def _load():
     lib.pkv_chunk_kda_varlen_backward.restype = i32
     lib.pkv_chunk_kda_varlen_backward_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
     lib.pkv_chunk_kda_varlen_backward_workspace_size.restype = sz
+    lib.pkv_chunk_kda_states_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    lib.pkv_chunk_kda_states_size.restype = sz
+    lib.pkv_chunk_kda_varlen_states.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32, i32,
+                                                vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    lib.pkv_chunk_kda_varlen_states.restype = i32
+    lib.pkv_chunk_kda_varlen_backward_states_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    lib.pkv_chunk_kda_varlen_backward_states_workspace_size.restype = sz
+    lib.pkv_chunk_kda_varlen_backward_states.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                                         f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                         vp, vp, sz, vp, sz, vp]
+    lib.pkv_chunk_kda_varlen_backward_states.restype = i32
     lib.pkv_status_string.argtypes = [i32]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_abi_version.argtypes = []
@@ -209,15 +220,30 @@ def chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype):
     return int(_load().pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, _dtype_code(dtype)))
 
 
+def chunk_kda_states_size(N, H, Dk, Dv, max_segs, dtype=torch.bfloat16):
+    """Bytes of the per-chunk state buffer (0 when the shape has no chunked path)."""
+    return int(_load().pkv_chunk_kda_states_size(N, H, Dk, Dv, max_segs, _dtype_code(dtype)))
+
+
+def new_chunk_states(N, H, Dk, Dv, max_segs, device, dtype=torch.bfloat16):
+    """A device buffer for ``chunk_kda_varlen(..., chunk_states=...)``."""
+    n = chunk_kda_states_size(N, H, Dk, Dv, max_segs, dtype)
+    if n == 0:
+        raise PkvError("per-chunk states need the chunked path (bf16, Dk and Dv in {64, 128})")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_state=True,
                      flags=None, out=None, workspace=None, initial_state=None,
-                     use_qk_l2norm_in_kernel=False):
+                     use_qk_l2norm_in_kernel=False, chunk_states=None):
     """Packed KDA forward.
 
     q, k, g: [1, N, H, Dk] (or [B, T, H, Dk], taken as the flattened [1, B*T, H, Dk]);
     v: [..., Dv]; beta: [1, N, H]; cu_seqlens: int32 [max_segs + 1] or None (one segment).
     initial_state: fp32 [max_segs, H, Dk, Dv] or None (each segment starts from its slot's state).
     use_qk_l2norm_in_kernel: q and k are L2-normalised per (token, head) inside the call.
+    chunk_states: None, or a device buffer (``new_chunk_states``) that receives the state before
+    every 64-token chunk, for ``chunk_kda_varlen_backward(..., chunk_states=...)``.
     Returns (o [same leading shape as q, Dv], final_state fp32 [max_segs, H, Dk, Dv] or None).
     """
     lib = _load()
@@ -250,11 +276,16 @@ def chunk_kda_varlen(q, k, v, g, beta, cu_seqlens=None, scale=1.0, output_final_
             raise ValueError(f"initial_state must be [{max_segs}, {H}, {Dk}, {Dv}]")
     need = int(lib.pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, code))
     workspace, ws_bytes = _workspace(workspace, need, dev)
-    _check(lib.pkv_chunk_kda_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                    max_segs, N, H, Dk, Dv, float(scale), code,
-                                    OPT_QK_L2NORM if use_qk_l2norm_in_kernel else 0, _ptr(initial_state),
-                                    _ptr(o), _ptr(fs),
-                                    _ptr(flags), _ptr(workspace), ws_bytes, _stream(dev)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), max_segs, N, H, Dk, Dv,
+            float(scale), code, OPT_QK_L2NORM if use_qk_l2norm_in_kernel else 0, _ptr(initial_state),
+            _ptr(o), _ptr(fs), _ptr(flags), _ptr(workspace), ws_bytes)
+    if chunk_states is None:
+        _check(lib.pkv_chunk_kda_varlen(*args, _stream(dev)))
+    else:
+        _need(chunk_states, "chunk_states", dev, None, None)
+        _check(lib.pkv_chunk_kda_varlen_states(*args, _ptr(chunk_states),
+                                               chunk_states.numel() * chunk_states.element_size(),
+                                               _stream(dev)))
     return o, fs
 
 
@@ -317,15 +348,22 @@ def chunk_kda_varlen_backward_workspace_size(N, H, Dk, Dv, max_segs, dtype):
                                                                     _dtype_code(dtype)))
 
 
+def chunk_kda_varlen_backward_states_workspace_size(N, H, Dk, Dv, max_segs, dtype):
+    return int(_load().pkv_chunk_kda_varlen_backward_states_workspace_size(N, H, Dk, Dv, max_segs,
+                                                                           _dtype_code(dtype)))
+
+
 def chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_seqlens=None, scale=1.0, initial_state=None,
                               dfinal_state=None, output_d_initial_state=None, flags=None,
-                              workspace=None):
+                              workspace=None, chunk_states=None):
     """Reverse pass of ``chunk_kda_varlen`` on the same inputs.
 
     do: dL/do, shaped like the forward output; dfinal_state: fp32 [max_segs, H, Dk, Dv] or None
     (dL/dfinal_state). Returns KdaGrads; d_initial_state is returned when
     ``output_d_initial_state`` is true (default: when initial_state is given). The chunked path
     (bf16, Dk and Dv in {64, 128}) needs a workspace (allocated here when not given).
+    chunk_states: None (the states are recomputed), or the buffer the forward call filled
+    (``chunk_kda_varlen(..., chunk_states=...)`` on the same inputs).
     """
     lib = _load()
     dev = q.device
@@ -360,11 +398,18 @@ def chunk_kda_varlen_backward(q, k, v, g, beta, do, cu_seqlens=None, scale=1.0, 
     dv = torch.empty_like(v)
     dbeta = torch.empty_like(beta)
     dinit = torch.empty(max_segs, H, Dk, Dv, dtype=torch.float32, device=dev) if output_d_initial_state else None
-    need = int(lib.pkv_chunk_kda_varlen_backward_workspace_size(N, H, Dk, Dv, max_segs, code))
+    size_fn = (lib.pkv_chunk_kda_varlen_backward_workspace_size if chunk_states is None
+               else lib.pkv_chunk_kda_varlen_backward_states_workspace_size)
+    need = int(size_fn(N, H, Dk, Dv, max_segs, code))
     workspace, ws_bytes = _workspace(workspace, need, dev)
-    _check(lib.pkv_chunk_kda_varlen_backward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), max_segs, N, H, Dk, Dv,
-        float(scale), code, _ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dinit), _ptr(flags), _ptr(workspace), ws_bytes,
-        _stream(dev)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), max_segs, N, H, Dk, Dv,
+            float(scale), code, _ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dinit), _ptr(flags), _ptr(workspace), ws_bytes)
+    if chunk_states is None:
+        _check(lib.pkv_chunk_kda_varlen_backward(*args, _stream(dev)))
+    else:
+        _need(chunk_states, "chunk_states", dev, None, None)
+        _check(lib.pkv_chunk_kda_varlen_backward_states(*args, _ptr(chunk_states),
+                                                        chunk_states.numel() * chunk_states.element_size(),
+                                                        _stream(dev)))
     return KdaGrads(dq, dk, dv, dg, dbeta, dinit)

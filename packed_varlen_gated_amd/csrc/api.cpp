@@ -163,6 +163,44 @@ pkv_status pkv_chunk_kda_varlen(const void* q, const void* k, const void* v, con
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t pkv_chunk_kda_states_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs,
+                                 int32_t dtype) {
+  return pkv::kda_chunk_states_bytes(N, H, Dk, Dv, dtype, max_segs);
+}
+
+pkv_status pkv_chunk_kda_varlen_states(const void* q, const void* k, const void* v, const void* g,
+                                       const void* beta, const int32_t* cu_seqlens, int32_t max_segs,
+                                       int64_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                       int32_t dtype, int32_t options, const float* initial_state,
+                                       void* o, float* final_state, int32_t* flags, void* workspace,
+                                       size_t workspace_bytes, void* chunk_states,
+                                       size_t chunk_states_bytes, void* stream) {
+  const pkv_status st = check_kda_args(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv, dtype,
+                                       options, initial_state, o, final_state);
+  const bool l2 = (options & PKV_OPT_QK_L2NORM) != 0;
+  if (st != PKV_OK) return st;
+  const size_t states = pkv::kda_chunk_states_bytes(N, H, Dk, Dv, dtype, max_segs);
+  if (!pkv::kda_chunk_supported(Dk, Dv, dtype) || states == 0) return PKV_ERR_UNSUPPORTED;
+  const size_t need = pkv_chunk_kda_varlen_workspace_size(N, H, Dk, Dv, max_segs, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                   reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
+    return PKV_ERR_WORKSPACE;
+  if (chunk_states == nullptr || chunk_states_bytes < states ||
+      reinterpret_cast<uintptr_t>(chunk_states) % 16 != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t es = elem_size(dtype), sb = int64_t(states);
+  const int64_t kb = N * H * Dk * es, vb = N * H * Dv * es;
+  const int64_t fb = int64_t(max_segs) * H * Dk * Dv * 4;
+  const void* others[9] = {q, k, v, g, beta, o, initial_state, final_state, workspace};
+  const int64_t other_bytes[9] = {kb, kb, vb, kb, N * H * es, vb, fb, fb, int64_t(need)};
+  for (int i = 0; i < 9; ++i)
+    if (others[i] != nullptr && overlaps(chunk_states, sb, others[i], other_bytes[i]))
+      return PKV_ERR_INVALID_ARGUMENT;
+  return from_hip(pkv::launch_kda_chunk(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv, scale,
+                                        l2, initial_state, o, final_state, flags, workspace,
+                                        static_cast<hipStream_t>(stream), chunk_states));
+}
+
 pkv_status pkv_chunk_kda_varlen_noalloc(const void* q, const void* k, const void* v,
                                         const void* g, const void* beta,
                                         const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
@@ -186,15 +224,19 @@ pkv_status pkv_chunk_kda_varlen_noalloc(const void* q, const void* k, const void
                                          static_cast<hipStream_t>(stream)));
 }
 
-pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const void* v,
-                                         const void* g, const void* beta,
-                                         const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
-                                         int32_t H, int32_t Dk, int32_t Dv, float scale,
-                                         int32_t dtype, const float* initial_state,
-                                         const void* do_, const float* dfinal_state, void* dq,
-                                         void* dk, void* dv, void* dg, void* dbeta,
-                                         float* d_initial_state, int32_t* flags, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pkv_chunk_kda_varlen_backward, and with with_states its variant that reads the
+// forward call's per-chunk states instead of recomputing them.
+pkv_status kda_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        const int32_t* cu_seqlens, int32_t max_segs, int64_t N, int32_t H,
+                        int32_t Dk, int32_t Dv, float scale, int32_t dtype,
+                        const float* initial_state, const void* do_, const float* dfinal_state,
+                        void* dq, void* dk, void* dv, void* dg, void* dbeta, float* d_initial_state,
+                        int32_t* flags, void* workspace, size_t workspace_bytes, bool with_states,
+                        const void* chunk_states, size_t chunk_states_bytes, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
       do_ == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || dg == nullptr ||
       dbeta == nullptr)
@@ -218,16 +260,23 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
       reinterpret_cast<uintptr_t>(dfinal_state) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(d_initial_state) % 16 != 0)
     return PKV_ERR_INVALID_ARGUMENT;
+  const size_t states = with_states ? pkv::kda_chunk_states_bytes(N, H, Dk, Dv, dtype, max_segs) : 0;
+  if (with_states) {
+    if (states == 0) return PKV_ERR_UNSUPPORTED;
+    if (chunk_states == nullptr || chunk_states_bytes < states ||
+        reinterpret_cast<uintptr_t>(chunk_states) % 16 != 0)
+      return PKV_ERR_INVALID_ARGUMENT;
+  }
   const int64_t kb = N * H * Dk * es, vb = N * H * Dv * es, bb = N * H * es;
   const int64_t sb = int64_t(max_segs) * H * Dk * Dv * 4;
   const int64_t cb = cu_seqlens ? (int64_t(max_segs) + 1) * 4 : 0;
-  const void* ins[8] = {q, k, v, g, beta, do_, initial_state, dfinal_state};
-  const int64_t in_bytes[8] = {kb, kb, vb, kb, bb, vb, sb, sb};
+  const void* ins[9] = {q, k, v, g, beta, do_, initial_state, dfinal_state, chunk_states};
+  const int64_t in_bytes[9] = {kb, kb, vb, kb, bb, vb, sb, sb, int64_t(states)};
   const void* outs[6] = {dq, dk, dv, dg, dbeta, d_initial_state};
   const int64_t out_bytes[6] = {kb, kb, vb, kb, bb, sb};
   for (int i = 0; i < 6; ++i) {
     if (outs[i] == nullptr) continue;
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 9; ++j)
       if (ins[j] != nullptr && overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
         return PKV_ERR_INVALID_ARGUMENT;
     if (cu_seqlens != nullptr && overlaps(outs[i], out_bytes[i], cu_seqlens, cb))
@@ -236,12 +285,12 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
       if (outs[j] != nullptr && overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
         return PKV_ERR_INVALID_ARGUMENT;
   }
-  const size_t need = pkv::kda_chunk_bwd_workspace_bytes(N, H, Dk, Dv, dtype, max_segs);
+  const size_t need = pkv::kda_chunk_bwd_workspace_bytes(N, H, Dk, Dv, dtype, max_segs, with_states);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need ||
         reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return PKV_ERR_WORKSPACE;
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 9; ++i)
       if (ins[i] != nullptr && overlaps(workspace, int64_t(need), ins[i], in_bytes[i]))
         return PKV_ERR_INVALID_ARGUMENT;
     for (int i = 0; i < 6; ++i)
@@ -250,12 +299,50 @@ pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const voi
     return from_hip(pkv::launch_kda_chunk_backward(
         q, k, v, g, beta, do_, cu_seqlens, max_segs, N, H, Dk, Dv, scale, initial_state,
         dfinal_state, dq, dk, dv, dg, dbeta, d_initial_state, flags, workspace,
-        static_cast<hipStream_t>(stream)));
+        static_cast<hipStream_t>(stream), with_states ? chunk_states : nullptr));
   }
   return from_hip(pkv::launch_kda_backward(q, k, v, g, beta, do_, cu_seqlens, max_segs, N, H, Dk,
                                            Dv, scale, dtype, initial_state, dfinal_state, dq, dk,
                                            dv, dg, dbeta, d_initial_state, flags,
                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_chunk_kda_varlen_backward(const void* q, const void* k, const void* v,
+                                         const void* g, const void* beta,
+                                         const int32_t* cu_seqlens, int32_t max_segs, int64_t N,
+                                         int32_t H, int32_t Dk, int32_t Dv, float scale,
+                                         int32_t dtype, const float* initial_state,
+                                         const void* do_, const float* dfinal_state, void* dq,
+                                         void* dk, void* dv, void* dg, void* dbeta,
+                                         float* d_initial_state, int32_t* flags, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return kda_backward(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv, scale, dtype,
+                      initial_state, do_, dfinal_state, dq, dk, dv, dg, dbeta, d_initial_state,
+                      flags, workspace, workspace_bytes, false, nullptr, 0, stream);
+}
+
+pkv_status pkv_chunk_kda_varlen_backward_states(
+    const void* q, const void* k, const void* v, const void* g, const void* beta,
+    const int32_t* cu_seqlens, int32_t max_segs, int64_t N, int32_t H, int32_t Dk, int32_t Dv,
+    float scale, int32_t dtype, const float* initial_state, const void* do_,
+    const float* dfinal_state, void* dq, void* dk, void* dv, void* dg, void* dbeta,
+    float* d_initial_state, int32_t* flags, void* workspace, size_t workspace_bytes,
+    const void* chunk_states, size_t chunk_states_bytes, void* stream) {
+  return kda_backward(q, k, v, g, beta, cu_seqlens, max_segs, N, H, Dk, Dv, scale, dtype,
+                      initial_state, do_, dfinal_state, dq, dk, dv, dg, dbeta, d_initial_state,
+                      flags, workspace, workspace_bytes, true, chunk_states, chunk_states_bytes,
+                      stream);
+}
+
+size_t pkv_chunk_kda_varlen_backward_states_workspace_size(int64_t N, int32_t H, int32_t Dk,
+                                                           int32_t Dv, int32_t max_segs,
+                                                           int32_t dtype) {
+  if (pkv::kda_chunk_states_bytes(N, H, Dk, Dv, dtype, max_segs) == 0) return 0;
+  return pkv::kda_chunk_bwd_workspace_bytes(N, H, Dk, Dv, dtype, max_segs, true);
 }
 
 size_t pkv_chunk_kda_varlen_backward_workspace_size(int64_t N, int32_t H, int32_t Dk, int32_t Dv,

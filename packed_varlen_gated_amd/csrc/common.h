@@ -81,11 +81,14 @@ hipError_t launch_kda_serial_ids(const void* q, const void* k, const void* v, co
                                  bool qk_l2norm, const float* initial_state, void* o,
                                  float* final_state, hipStream_t stream);
 
+// chunk_states: NULL, or where the bf16 state before every 64-token chunk is
+// written (the reverse pass's layout; see kda_chunk_states_bytes).
 hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                             int32_t H, int32_t Dk, int32_t Dv, float scale, bool qk_l2norm,
                             const float* initial_state, void* o, float* final_state,
-                            int32_t* flags, void* workspace, hipStream_t stream);
+                            int32_t* flags, void* workspace, hipStream_t stream,
+                            void* chunk_states = nullptr);
 
 // The same with the workspace in the library's fixed per-GPU scratch array of
 // kNoAllocScratchBytes (for callers that cannot allocate); the caller has
@@ -98,18 +101,24 @@ hipError_t launch_kda_chunk_noalloc(const void* q, const void* k, const void* v,
                                     float* final_state, int32_t* flags, hipStream_t stream);
 
 // Reverse pass of the recurrence, chunked on MFMA (bf16, Dk and Dv in {64, 128}):
-// the work plan and the bf16 states S and Lambda of every chunk in the workspace.
+// the work plan, piece summaries and (unless the caller gives them) the bf16
+// state before every chunk in the workspace.
 bool kda_chunk_bwd_supported(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
                              int32_t max_segs);
 size_t kda_chunk_bwd_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
-                                     int32_t max_segs);
+                                     int32_t max_segs, bool states_given = false);
+// Bytes of the per-chunk states ([ceil(N / 64) + max_segs, H, Dk, Dv] bf16), or 0
+// when the shape has no chunked reverse pass.
+size_t kda_chunk_states_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                              int32_t max_segs);
 hipError_t launch_kda_chunk_backward(const void* q, const void* k, const void* v, const void* g,
                                      const void* beta, const void* dout, const int32_t* cu,
                                      int32_t max_segs, int64_t N, int32_t H, int32_t Dk, int32_t Dv,
                                      float scale, const float* initial_state,
                                      const float* dfinal_state, void* dq, void* dk, void* dv,
                                      void* dg, void* dbeta, float* dinitial_state, int32_t* flags,
-                                     void* workspace, hipStream_t stream);
+                                     void* workspace, hipStream_t stream,
+                                     const void* chunk_states = nullptr);
 
 // Reverse pass of the recurrence, token-serial (every other shape; no workspace).
 hipError_t launch_kda_backward(const void* q, const void* k, const void* v, const void* g,

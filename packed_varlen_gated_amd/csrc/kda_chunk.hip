@@ -152,6 +152,11 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
+// A register of another lane of the same quad (DPP quad_perm kCtrl; every lane active).
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dppu(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), kCtrl, 0xF, 0xF, true));
+}
 // Sum over the 16 lanes of a row, the same bits in every lane (each step adds
 // two equal partial sums in either order): quad_perm [1,0,3,2], quad_perm
 // [2,3,0,1], row_half_mirror (lane j of an 8-lane half takes lane 7 - j),
@@ -297,7 +302,8 @@ __device__ __forceinline__ void wload(uint32_t (&w)[n], __amdgpu_buffer_rsrc_t r
 // last: S from zero over the run and the product of its decays, both to the
 // workspace (no outputs).
 // kNorm: q and k are first L2-normalised per (token, head) over Dk.
-template <int DK, int DV, bool kState, bool kNorm>
+// kSave: the forward pass also writes the state before every chunk to chunk_states.
+template <int DK, int DV, bool kState, bool kNorm, bool kSave>
 __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -305,7 +311,8 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     int32_t H, float scale, const float* __restrict__ initial_state, bf16* __restrict__ o,
     float* __restrict__ final_state, float* __restrict__ run_states,
     float* __restrict__ run_decays, int64_t row_len, const int32_t* __restrict__ seg_ids,
-    const int32_t* __restrict__ n_dev, int32_t* __restrict__ flags, int32_t lds_zero) {
+    const int32_t* __restrict__ n_dev, int32_t* __restrict__ flags, bf16* __restrict__ chunk_states,
+    int32_t lds_zero) {
   using C = Cfg<DK, DV>;
   constexpr int NP = C::NP, NT = C::NT;
   constexpr int PCPL = C::PCPL, PVPL = C::PVPL, ET = C::ET, DT = C::DT, KS = C::KS;
@@ -349,6 +356,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // same barriers), so neither role's loop keeps the other's registers live.
   // The current item's run, set by begin_item in both loops:
   int h = 0, slot = 0, run_idx = 0, sbase = 0, nchunks = 0;
+  int gc0 = 0;  // global index of the run's first chunk (chunks of all slots in slot order)
   bool last = false;
   int64_t start = 0, end = 0;
   auto begin_item = [&](int item) __attribute__((always_inline)) {
@@ -369,6 +377,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       run_idx = e[3];  // runs of the segment before this one
       sbase = e[4];    // their state slots: sbase .. sbase + run_idx - 1
       last = e[5] != 0;
+      gc0 = e[6] + c0;
     }
     // the run: chunks [c0, c1) of the segment, which are aligned to its start
     // (the plan holds well-formed, non-empty segments only)
@@ -683,6 +692,35 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // ---- consumer, second half of step c: o^T = S^T Q^^T for chunk c (S holds
   // the state after chunk c-1 by then); kept in registers until the first
   // half of step c+1 adds V^T A^T. Contraction over Dk in steps of 32.
+  // The state before global chunk gc, bf16, row-major [Dk][Dv] at
+  // chunk_states[gc][h]: the reverse pass's layout. Lane lr of a consumer holds
+  // rows 16 dt + 4 gq .. + 3 of column e0 + ecol(et, lr); the four lanes of a
+  // quad hold four consecutive columns, so a 4 x 4 transpose within the quad
+  // gives each lane one row's four columns (one 8-byte store): swap the
+  // off-diagonal 2 x 2 blocks with lane ^ 2 (quad_perm [2,3,0,1]), then the
+  // halves of each block's rows with lane ^ 1 (quad_perm [1,0,3,2], v_perm_b32).
+  auto save_state = [&](const f32x4 (&S)[DT][ET], int gc) __attribute__((always_inline)) {
+    // one 32-bit base offset per lane plus an immediate per (dt, et)
+    const auto rs = rsrc(chunk_states + (int64_t(gc) * H + h) * DK * DV, DK * DV * 2);
+    const int q4 = lr & 3;
+    const uint32_t lane_off = uint32_t((4 * gq + q4) * DV + e0 + 4 * ET * (lr >> 2)) * 2;
+    const uint32_t sel = (q4 & 1) ? 0x03020706u : 0x05040100u;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const f32x4 x = S[dt][et];
+        uint32_t w0 = pk2(x[0], x[1]), w1 = pk2(x[2], x[3]);
+        const uint32_t got = dppu<0x4E>((q4 & 2) ? w0 : w1);
+        if (q4 & 2) w0 = got; else w1 = got;
+        w0 = __builtin_amdgcn_perm(dppu<0xB1>(w0), w0, sel);
+        w1 = __builtin_amdgcn_perm(dppu<0xB1>(w1), w1, sel);
+        // row 16 dt + 4 gq + q4, columns e0 + 4 ET (lr / 4) + 4 et .. + 3
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(v2i{int(w0), int(w1)}, rs, lane_off,
+                                              (16 * dt * DV + 4 * et) * 2, 0);
+      }
+  };
   auto consume_inter = [&](const f32x4 (&S)[DT][ET], f32x4 (&acc)[4][ET]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -1093,6 +1131,10 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
           __syncthreads();
           if (!C::stage_o && s >= 1) store_out(opk, s - 1);
           if (s < nchunks) {
+            // (the zero state before a segment's first chunk, without an initial
+            // state, is not stored)
+            if constexpr (kSave)
+              if (s > 0 || run_idx > 0 || initial_state != nullptr) save_state(S, gc0 + s);
             f32x4 ab[3];
             a_blocks_mma(ab);
             consume_inter(S, acc);
@@ -1105,6 +1147,7 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
           __syncthreads();
           if constexpr (!C::stage_o) store_out(opk, s);
           if (s + 1 < nchunks) {
+            if constexpr (kSave) save_state(S, gc0 + s + 1);
             f32x4 ab[3];
             a_blocks_mma(ab);
             consume_inter(S, acc);
@@ -1263,24 +1306,27 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   // Runs of each segment, with the state-slot budget enforced in slot order:
   // a segment whose extra runs would not fit stays whole (only on malformed
   // input; the workspace bound covers every well-formed one).
+  // cb: chunks of the slots before slot i (the global index of slot i's first chunk)
   auto pass = [&](auto&& body) {
-    int carry = 0;
+    int carry = 0, ccarry = 0;
     for (int base = 0; base < max_segs; base += kPlanThreads) {
       const int i = base + tid;
       bool bad;
       const int n = i >= max_segs ? 0 : cached ? s_n[i] : chunks(i, bad);
       int m = plan_runs(n);
-      int tile_total;
+      int tile_total, tile_chunks;
       const int sb = carry + block_exclusive_scan(m > 1 ? m - 1 : 0, s_tmp, &tile_total);
+      const int cb = ccarry + block_exclusive_scan(n, s_tmp, &tile_chunks);
       if (m > 1 && sb + m - 1 > states_max) m = 1;
       // a clamped segment's slots stay unused; later segments keep theirs
-      if (m > 0) body(i, n, m, sb);
+      if (m > 0) body(i, n, m, sb, cb);
       carry = carry + tile_total < (1 << 29) ? carry + tile_total : (1 << 29);
+      ccarry += tile_chunks;
     }
   };
   // A segment of n chunks in m runs has n % m runs of q + 1 chunks and the
   // rest of q (q = n / m); its last run is one of the long ones iff n % m > 0.
-  pass([&](int, int n, int m, int) {
+  pass([&](int, int n, int m, int, int) {
     const int q = n / m, nl = n - q * m, last_long = nl > 0;
     atomicAdd(&s_hr[len_bin(q + 1)], nl);
     atomicAdd(&s_hr[len_bin(q)], m - nl);
@@ -1317,7 +1363,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
     plan[2] = 0;   // queue counters of the forward and state passes
     plan[3] = 0;
   }
-  pass([&](int i, int n, int m, int sb) {
+  pass([&](int i, int n, int m, int sb, int cb) {
     // ranks for the segment's long and short runs, reserved in one go each
     const int q = n / m, nl = n - q * m, last_long = nl > 0;
     int rl = atomicAdd(&s_hr[len_bin(q + 1)], nl);
@@ -1334,6 +1380,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
       e[3] = j;
       e[4] = sb;
       e[5] = j + 1 == m;
+      e[6] = cb;
       if (j + 1 < m) {
         int32_t* f = plan + states_word_off + 4 * (lng ? sl++ : ss++);
         f[0] = i;
@@ -1390,22 +1437,23 @@ struct Launch {
   int64_t row_len;        // > 0: ids path, segments map to rows of this length
   const int32_t* seg_ids; // ids path: the [B, T] ids
   hipStream_t stream;
+  void* chunk_states;     // bf16 state before every chunk, or NULL
 };
 
 // The plan, the state pass and the forward pass over segments given by cu
 // (max_segs slots), or, with n_dev, by the first *n_dev + 1 entries of cu that
 // a boundary scan wrote (layout_segs bounds their number; row_len > 0 then
 // maps segments to rows for the initial and final states).
-template <int DK, int DV, bool kNorm>
+template <int DK, int DV, bool kNorm, bool kSave>
 hipError_t launch_dims(const Launch& a) {
   using C = Cfg<DK, DV>;
   constexpr int state_bytes = C::off_qh;  // the state pass uses the small tables, V and Kbar
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, false, kNorm>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, false, kNorm, kSave>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::bytes);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, true, kNorm>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<DK, DV, true, kNorm, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, state_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -1424,23 +1472,26 @@ hipError_t launch_dims(const Launch& a) {
   // persistent grids: as many work-groups as the LDS lets each CU hold
   const unsigned grid = unsigned(device_cus() * C::WG_PER_CU);
   if (L.states_max > 0) {
-    hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true, kNorm>), dim3(grid), dim3(C::NT), state_bytes,
+    hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, true, kNorm, false>), dim3(grid), dim3(C::NT), state_bytes,
                        a.stream, qp, kp, vp, gp, bp, a.cu, plan, int32_t(L.runs_max), a.max_segs, a.N,
                        a.H, a.scale, static_cast<const float*>(nullptr), static_cast<bf16*>(nullptr),
-                       static_cast<float*>(nullptr), states, decays, a.row_len, a.seg_ids, a.n_dev, a.flags, 0);
+                       static_cast<float*>(nullptr), states, decays, a.row_len, a.seg_ids, a.n_dev, a.flags,
+                       static_cast<bf16*>(nullptr), 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false, kNorm>), dim3(grid), dim3(C::NT), C::bytes,
+  hipLaunchKernelGGL((kda_chunk_kernel<DK, DV, false, kNorm, kSave>), dim3(grid), dim3(C::NT), C::bytes,
                      a.stream, qp, kp, vp, gp, bp, a.cu, plan, int32_t(L.runs_max), a.max_segs, a.N,
                      a.H, a.scale, a.s0, static_cast<bf16*>(a.o), a.fs, states, decays, a.row_len,
-                     a.seg_ids, a.n_dev, a.flags, 0);
+                     a.seg_ids, a.n_dev, a.flags, static_cast<bf16*>(a.chunk_states), 0);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t launch_norm(bool qk_l2norm, const Launch& a) {
-  return qk_l2norm ? launch_dims<DK, DV, true>(a) : launch_dims<DK, DV, false>(a);
+  if (a.chunk_states != nullptr)
+    return qk_l2norm ? launch_dims<DK, DV, true, true>(a) : launch_dims<DK, DV, false, true>(a);
+  return qk_l2norm ? launch_dims<DK, DV, true, false>(a) : launch_dims<DK, DV, false, false>(a);
 }
 
 hipError_t dispatch(int32_t Dk, int32_t Dv, bool qk_l2norm, const Launch& a) {
@@ -1498,7 +1549,7 @@ hipError_t launch_kda_chunk_ids(const void* q, const void* k, const void* v, con
   const hipError_t e = launch_segment_bounds(seg, N, T, bounds, n_dev, stream);
   if (e != hipSuccess) return e;
   const Launch a{q, k, v, g, beta, bounds, n_dev, int32_t(N), 0, N, H, scale, initial_state, o,
-                 final_state, flags, ws + ids_bounds_bytes(N), T, seg, stream};
+                 final_state, flags, ws + ids_bounds_bytes(N), T, seg, stream, nullptr};
   return dispatch(Dk, Dv, qk_l2norm, a);
 }
 
@@ -1506,9 +1557,9 @@ hipError_t launch_kda_chunk(const void* q, const void* k, const void* v, const v
                             const void* beta, const int32_t* cu, int32_t max_segs, int64_t N,
                             int32_t H, int32_t Dk, int32_t Dv, float scale, bool qk_l2norm,
                             const float* initial_state, void* o, float* final_state,
-                            int32_t* flags, void* workspace, hipStream_t stream) {
+                            int32_t* flags, void* workspace, hipStream_t stream, void* chunk_states) {
   const Launch a{q, k, v, g, beta, cu, nullptr, max_segs, max_segs, N, H, scale, initial_state, o,
-                 final_state, flags, static_cast<char*>(workspace), 0, nullptr, stream};
+                 final_state, flags, static_cast<char*>(workspace), 0, nullptr, stream, chunk_states};
   return dispatch(Dk, Dv, qk_l2norm, a);
 }
 

@@ -331,7 +331,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
     const int32_t* __restrict__ order, int32_t max_segs,
     int32_t units, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
     const float* __restrict__ dfinal, bf16* __restrict__ Sws, float* __restrict__ sumL,
-    float* __restrict__ sumD, float* __restrict__ gfin) {
+    float* __restrict__ sumD, float* __restrict__ gfin, int32_t from_saved) {
   using C = StCfg<DK, DV>;
   constexpr int EB = DV / 16, NT = C::NT, NX = C::NX, NY = C::NY;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -356,10 +356,17 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
   const int j = u - ubase[slot];
   const int m = pbase[slot + 1] - pbase[slot];
   if (kSum && (adjoint ? j == 0 : j == m - 1)) return;  // summary not needed
+  // With the states saved by the forward call (from_saved), the S role's
+  // summaries are not needed, and the walk only takes a segment's last piece when
+  // dL/dfinal_state is given: from the saved state before its last chunk, that
+  // chunk's update gives the final state.
+  const bool fin = !kSum && !adjoint && dfinal != nullptr && j == m - 1;
+  if (from_saved && (kSum ? !adjoint : !fin)) return;
   const int cbase = base[slot];
   const int64_t nseg = int64_t(base[slot + 1]) - cbase;
-  const int c0 = int(nseg * j / m), c1 = int(nseg * (j + 1) / m);
-  const int nch = c1 - c0;  // chunks of this piece
+  const int cp0 = int(nseg * j / m), c1 = int(nseg * (j + 1) / m);
+  const int c0 = (!kSum && from_saved && c1 > cp0) ? c1 - 1 : cp0;
+  const int nch = c1 - c0;  // chunks of this piece (walked)
   const int64_t start = nch > 0 ? cu_at(cu, slot, N) : 0;
   const int64_t end = nch > 0 ? cu_at(cu, slot + 1, N) : 0;
   const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
@@ -378,6 +385,10 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
   if (kSum) {
 #pragma unroll
     for (int E = 0; E < EB; ++E) X[E] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (from_saved && c0 > 0) {
+    const bf16* Sp = Sws + (int64_t(cbase + c0) * H + h) * DK * DV + int64_t(d_own) * DV + 4 * g4;
+#pragma unroll
+    for (int E = 0; E < EB; ++E) X[E] = unpack4(ld4(Sp + 16 * E));
   } else {
     const float* src = adjoint ? dfinal : initial_state;
 #pragma unroll
@@ -445,7 +456,6 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
   // S role: chunks c0 .. c1-1 (a walk stores S before each and skips the last
   // update, except in a segment's last piece when dL/dfinal_state is given: there
   // it reaches the final state); Lambda role: chunks c1-1 .. c0, every update applied
-  const bool fin = !kSum && !adjoint && dfinal != nullptr && j == m - 1;
   const int napply = (adjoint || kSum || fin) ? nch : nch - 1;
   auto chunk_of = [&](int it) { return adjoint ? c1 - 1 - it : c0 + it; };
   auto step = [&]() {  // the chunk whose inputs are in LDS: scan, then update X
@@ -508,16 +518,16 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
   }
   // (a segment's first state is zero without an initial state: not stored, the
   // chunk pass takes zeros for it)
-  if (!kSum && (c0 > 0 || initial_state != nullptr)) store_state(ws_out, cbase + chunk_of(0));
+  if (!kSum && !from_saved && (c0 > 0 || initial_state != nullptr)) store_state(ws_out, cbase + chunk_of(0));
   for (int it = 0; it < napply - 1; ++it) {
     step();
     put();
     fetch(chunk_of(it + 2 < napply ? it + 2 : napply - 1));
-    if (!kSum) store_state(ws_out, cbase + chunk_of(it + 1));
+    if (!kSum && !from_saved) store_state(ws_out, cbase + chunk_of(it + 1));
   }
   if (napply > 0) {
     step();
-    if (!kSum && napply < nch) store_state(ws_out, cbase + chunk_of(napply));
+    if (!kSum && !from_saved && napply < nch) store_state(ws_out, cbase + chunk_of(napply));
   }
   if (fin) {
     // the gate gradient at the segment's end: sum_e dL/dS_final * S_final, per key channel
@@ -1096,7 +1106,8 @@ struct BwdLayout {
 };
 // Plan words: base, pbase, sbase ([max_segs + 1] each), the queue counter, then
 // order[max_pieces].
-BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs) {
+// own_states: the states live in the workspace (not given by the caller).
+BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs, bool own_states = true) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   BwdLayout l;
   l.max_chunks = (N + kC - 1) / kC + max_segs;
@@ -1104,7 +1115,7 @@ BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_s
   l.max_sums = l.max_chunks / 16 + 1;
   l.max_pieces = max_segs + l.max_sums;
   l.plan_bytes = up(((size_t(max_segs) + 1) * 3 + 1 + size_t(l.max_pieces)) * 4);
-  l.state_bytes = up(size_t(l.max_chunks) * H * Dk * Dv * 2);
+  l.state_bytes = own_states ? up(size_t(l.max_chunks) * H * Dk * Dv * 2) : 0;
   l.sumL_bytes = up(size_t(l.max_sums) * 2 * H * Dk * Dv * 4);
   l.sumD_bytes = up(size_t(l.max_sums) * 2 * H * Dk * 4);
   l.gfin_bytes = up(size_t(max_segs) * H * Dk * 4);
@@ -1117,7 +1128,7 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
                        const void* dout, const int32_t* cu, int32_t max_segs, int64_t N, int32_t H,
                        float scale, const float* s0, const float* dF, void* dq, void* dk, void* dv,
                        void* dg, void* db, float* dinit, int32_t* flags, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, const void* states_in) {
   using SC = StCfg<DK, DV>;
   using CC = ChCfg<DK, DV>;
   static bool attr_set = false;
@@ -1133,14 +1144,18 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const BwdLayout l = bwd_layout(N, H, DK, DV, max_segs);
+  const BwdLayout l = bwd_layout(N, H, DK, DV, max_segs, states_in == nullptr);
+  const int32_t from_saved = states_in != nullptr;
   char* w = static_cast<char*>(ws);
   int32_t* base = reinterpret_cast<int32_t*>(w);
   int32_t* pbase = base + (max_segs + 1);
   int32_t* sbase = pbase + (max_segs + 1);
   int32_t* counter = sbase + (max_segs + 1);
   int32_t* order = counter + 1;
-  bf16* Sws = reinterpret_cast<bf16*>(w + l.plan_bytes);
+  // the bf16 state before every chunk: the caller's (saved by the forward call,
+  // only read here) or the walk's, in the workspace
+  bf16* Sws = from_saved ? const_cast<bf16*>(static_cast<const bf16*>(states_in))
+                         : reinterpret_cast<bf16*>(w + l.plan_bytes);
   float* sumL = reinterpret_cast<float*>(w + l.plan_bytes + l.state_bytes);
   float* sumD = reinterpret_cast<float*>(w + l.plan_bytes + l.state_bytes + l.sumL_bytes);
   // per (segment, head, key channel): sum_e dL/dS_final * S_final (written only
@@ -1158,11 +1173,15 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   // summaries of the pieces of cut segments, both roles
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, true>), dim3(unsigned(2 * l.max_sums * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     order, max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin);
-  // the walk, S role only: the state before every chunk
-  hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(l.max_pieces * H)),
-                     dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     order, max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin);
+                     order, max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
+                     from_saved);
+  // the walk, S role only: the state before every chunk (with saved states, only
+  // the final-state term of the gate gradient, when dL/dfinal_state is given)
+  if (!from_saved || dF != nullptr)
+    hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(l.max_pieces * H)),
+                       dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
+                       order, max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
+                       from_saved);
   // the chunks of each (piece, head) walked backwards, Lambda carried
   hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(device_cus() * CC::WG_PER_CU)), dim3(CC::NT),
                      CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, order, counter,
@@ -1184,9 +1203,15 @@ bool kda_chunk_bwd_supported(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32
 }
 
 size_t kda_chunk_bwd_workspace_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
-                                     int32_t max_segs) {
+                                     int32_t max_segs, bool states_given) {
   if (!kda_chunk_bwd_supported(N, H, Dk, Dv, dtype, max_segs)) return 0;
-  return bwd_layout(N, H, Dk, Dv, max_segs).bytes;
+  return bwd_layout(N, H, Dk, Dv, max_segs, !states_given).bytes;
+}
+
+size_t kda_chunk_states_bytes(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                              int32_t max_segs) {
+  if (!kda_chunk_bwd_supported(N, H, Dk, Dv, dtype, max_segs)) return 0;
+  return size_t((N + kC - 1) / kC + max_segs) * H * Dk * Dv * 2;
 }
 
 hipError_t launch_kda_chunk_backward(const void* q, const void* k, const void* v, const void* g,
@@ -1195,12 +1220,12 @@ hipError_t launch_kda_chunk_backward(const void* q, const void* k, const void* v
                                      float scale, const float* initial_state,
                                      const float* dfinal_state, void* dq, void* dk, void* dv,
                                      void* dg, void* dbeta, float* dinitial_state, int32_t* flags,
-                                     void* workspace, hipStream_t stream) {
+                                     void* workspace, hipStream_t stream, const void* chunk_states) {
 #define PKV_BWD_LAUNCH(DK_, DV_)                                                                  \
   if (Dk == DK_ && Dv == DV_)                                                                     \
     return launch_dims<DK_, DV_>(q, k, v, g, beta, dout, cu, max_segs, N, H, scale, initial_state, \
                                  dfinal_state, dq, dk, dv, dg, dbeta, dinitial_state, flags,       \
-                                 workspace, stream);
+                                 workspace, stream, chunk_states);
   PKV_BWD_LAUNCH(64, 64)
   PKV_BWD_LAUNCH(64, 128)
   PKV_BWD_LAUNCH(128, 64)

@@ -29,13 +29,13 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pkv_abi_version() == 5
+    assert lib.pkv_abi_version() == 6
     for code, name in [(0, b"PKV_OK"), (1, b"PKV_ERR_INVALID_ARGUMENT"), (2, b"PKV_ERR_UNSUPPORTED"),
                        (3, b"PKV_ERR_WORKSPACE"), (4, b"PKV_ERR_HIP"), (99, b"PKV_ERR_UNKNOWN")]:
         assert lib.pkv_status_string(code) == name
@@ -246,3 +246,65 @@ def test_header_flag_and_option_bits_match_the_binding():
                     "FLAG_GATE_RANGE": 8, "OPT_QK_L2NORM": 1}
     for n, v in bits.items():
         assert getattr(pkv, n) == v, n
+
+
+# ---- the forward call that keeps the per-chunk states, and the reverse pass
+# that reads them (argument checks only: nothing here reaches a launch)
+
+def _kda_states_args(states=ctypes.c_void_p(0x7f000000), states_bytes=1 << 24, **kw):
+    a = list(_kda_args(**kw))
+    return tuple(a[:-1] + [states, states_bytes, a[-1]])
+
+
+def _bwd_states_args(states=ctypes.c_void_p(0x7f000000), states_bytes=1 << 24, **kw):
+    a = list(_bwd_args(**kw))
+    return tuple(a[:-1] + [states, states_bytes, a[-1]])
+
+
+def test_chunk_states_size(lib):
+    """bf16 [ceil(N / 64) + max_segs, H, Dk, Dv] on the chunked path, else 0."""
+    size = lib.pkv_chunk_kda_states_size
+    for N, H, Dk, Dv, S in [(65536, 32, 128, 128, 256), (345, 2, 64, 64, 7), (1000, 3, 64, 128, 1),
+                            (64, 1, 128, 64, 1)]:
+        assert size(N, H, Dk, Dv, S, 0) == ((N + 63) // 64 + S) * H * Dk * Dv * 2
+    assert size(256, 2, 32, 32, 4, 0) == 0       # Dk = 32: token-serial path
+    assert size(256, 2, 64, 64, 4, 1) == 0       # fp32
+    # the reverse pass given the states keeps none of its own
+    full = lib.pkv_chunk_kda_varlen_backward_workspace_size
+    lean = lib.pkv_chunk_kda_varlen_backward_states_workspace_size
+    up = lambda x: (x + 255) // 256 * 256
+    for N, H, Dk, Dv, S in [(65536, 32, 128, 128, 256), (1000, 3, 64, 128, 7)]:
+        assert lean(N, H, Dk, Dv, S, 0) == full(N, H, Dk, Dv, S, 0) - up(size(N, H, Dk, Dv, S, 0))
+    assert lean(256, 2, 32, 32, 4, 0) == 0
+
+
+def test_forward_with_states_validation(lib):
+    need = lib.pkv_chunk_kda_states_size(256, 2, 64, 64, 4, 0)
+    ws = lib.pkv_chunk_kda_varlen_workspace_size(256, 2, 64, 64, 4, 0)
+    W = dict(ws=ctypes.c_void_p(0x7e000000), ws_bytes=ws)
+    f = lib.pkv_chunk_kda_varlen_states
+    assert f(*_kda_states_args(states=NUL, **W)) == 1                                  # missing
+    assert f(*_kda_states_args(states_bytes=need - 1, **W)) == 1                       # too small
+    assert f(*_kda_states_args(states=ctypes.c_void_p(0x7f000008), **W)) == 1          # misaligned
+    assert f(*_kda_states_args(states=ctypes.c_void_p(0x60000000), **W)) == 1          # over o
+    assert f(*_kda_states_args(states=ctypes.c_void_p(0x7e000000), **W)) == 1          # over the workspace
+    assert f(*_kda_states_args(Dk=32, Dv=32, **W)) == 2                                # no chunked path
+    assert f(*_kda_states_args(dtype=1, **W)) == 2                                     # fp32
+    assert f(*_kda_states_args()) == 3                                                 # no workspace
+    assert f(*_kda_states_args(q=NUL, **W)) == 1                                       # the forward's own checks
+
+
+def test_backward_with_states_validation(lib):
+    need = lib.pkv_chunk_kda_states_size(256, 2, 64, 64, 4, 0)
+    ws = lib.pkv_chunk_kda_varlen_backward_states_workspace_size(256, 2, 64, 64, 4, 0)
+    W = dict(ws=ctypes.c_void_p(0x7e000000), ws_bytes=ws)
+    f = lib.pkv_chunk_kda_varlen_backward_states
+    assert f(*_bwd_states_args(states=NUL, **W)) == 1
+    assert f(*_bwd_states_args(states_bytes=need - 1, **W)) == 1
+    assert f(*_bwd_states_args(states=ctypes.c_void_p(0x7f000004), **W)) == 1
+    assert f(*_bwd_states_args(states=ctypes.c_void_p(0x60000000), **W)) == 1          # under dq
+    assert f(*_bwd_states_args(Dk=32, Dv=32, **W)) == 2
+    assert f(*_bwd_states_args(dtype=1, **W)) == 2
+    assert f(*_bwd_states_args()) == 3                                                 # no workspace
+    assert f(*_bwd_states_args(ws=ctypes.c_void_p(0x7e000000), ws_bytes=ws - 1)) == 3
+    assert f(*_bwd_states_args(dq=NUL, **W)) == 1

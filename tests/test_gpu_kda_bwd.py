@@ -270,3 +270,92 @@ def test_backward_deterministic(Dk, Dv):
     r2 = _run(ts, cu, 0.5, None, dF)
     for a, b in zip(r1, r2):
         assert torch.equal(a.cpu(), b.cpu())
+
+
+# ---- the forward call that keeps the state before every chunk, and the reverse
+# pass that reads those states instead of recomputing them
+
+def _oracle_prefix_state(ts, cu, i, c, S0):
+    """The oracle's state of segment i after its first 64 c tokens (the state
+    before its chunk c), [H, Dk, Dv]."""
+    q, k, v, g, beta, _ = [f64(t)[0] for t in ts]
+    a = int(cu[i])
+    e = a + 64 * c
+    init = None if S0 is None else S0[i:i + 1]
+    _, fs = oracle.chunk_kda_varlen(q[a:e], k[a:e], v[a:e], g[a:e], beta[a:e], [0, e - a], 1.0, init)
+    return fs[0]
+
+
+def _saved_states_case(ts, cu, scale, S0, dF, what, check_states=True):
+    pkv = _pkv()
+    dev = device()
+    q, k, v, g, beta, do = [t.to(dev) for t in ts]
+    N, H, Dk, Dv = q.shape[1], q.shape[2], q.shape[3], v.shape[3]
+    S = len(cu) - 1
+    cud = torch.from_numpy(np.asarray(cu, dtype=np.int32)).to(dev)
+    s0 = None if S0 is None else torch.from_numpy(S0).float().to(dev)
+    df = None if dF is None else torch.from_numpy(dF).float().to(dev)
+    o0, f0 = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, scale=scale, initial_state=s0)
+    st = pkv.new_chunk_states(N, H, Dk, Dv, S, dev)
+    o1, f1 = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, scale=scale, initial_state=s0, chunk_states=st)
+    torch.cuda.synchronize()
+    # the outputs do not depend on whether the states are kept
+    assert torch.equal(o0, o1) and torch.equal(f0, f1), what
+    if check_states:
+        sv = st.view(torch.bfloat16).view(-1, H, Dk, Dv)
+        nch = [int((cu[i + 1] - cu[i] + 63) // 64) for i in range(S)]
+        b = np.concatenate([[0], np.cumsum(nch)]).astype(np.int64)
+        for i in range(S):
+            for c in range(nch[i]):
+                if c == 0 and S0 is None:
+                    continue  # zero, not stored
+                check_close(f64(sv[b[i] + c]), _oracle_prefix_state(ts, cu, i, c, S0), "bf16",
+                            f"{what} state slot {i} chunk {c}")
+    r = pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cud, scale=scale, initial_state=s0,
+                                      dfinal_state=df, output_d_initial_state=True, chunk_states=st)
+    r0 = pkv.chunk_kda_varlen_backward(q, k, v, g, beta, do, cud, scale=scale, initial_state=s0,
+                                       dfinal_state=df, output_d_initial_state=True)
+    torch.cuda.synchronize()
+    ref = _oracle(ts, cu, scale, S0, dF)
+    _compare(r, ref, "bf16", f"{what} from saved states")
+    # and close to the reverse pass that recomputes the states (both round them to bf16)
+    for name, a_, b_ in zip(["dq", "dk", "dv", "dg", "dbeta", "dinit"], r, r0):
+        a64, b64 = f64(a_), f64(b_)
+        rel = np.linalg.norm(a64 - b64) / max(np.linalg.norm(b64), 1e-30)
+        print(f"    {what} {name}: saved vs recomputed rel-L2 {rel:.2e}", flush=True)
+        assert rel <= 1e-2, (what, name, rel)
+
+
+@pytest.mark.parametrize("Dk,Dv,with_s0,with_dF", [(128, 128, False, True), (64, 64, True, True),
+                                                   (128, 64, True, False), (64, 128, False, False)])
+def test_saved_chunk_states(Dk, Dv, with_s0, with_dF):
+    """pkv_chunk_kda_varlen_states gives o and final states bit-identical to the
+    plain call, every stored state matches the oracle's state at that chunk
+    boundary (layout: entry b_i + c, rows d, columns e), and the reverse pass that
+    reads them matches the oracle's reverse mode and the recomputing pass; ragged
+    segments, single tokens and an empty slot."""
+    print(f"  saved states Dk={Dk} Dv={Dv} s0={with_s0} dF={with_dF}", flush=True)
+    rng = np.random.default_rng(100 + Dk + Dv + 2 * with_s0 + with_dF)
+    N, H = 345, 2
+    cu = np.array(CU_RAGGED, dtype=np.int64)
+    ts = _inputs(rng, N, H, Dk, Dv, torch.bfloat16)
+    S = len(cu) - 1
+    S0 = rng.standard_normal((S, H, Dk, Dv)) * 0.5 if with_s0 else None
+    dF = rng.standard_normal((S, H, Dk, Dv)) * 0.5 if with_dF else None
+    _saved_states_case(ts, cu, Dk ** -0.5, S0, dF, f"{Dk}x{Dv}")
+
+
+@pytest.mark.parametrize("lens,Dk,Dv", [((70, 20000, 33), 64, 64), ((8300,), 128, 128)])
+def test_saved_chunk_states_cut_segments(lens, Dk, Dv):
+    """Documents long enough that the forward pass cuts them into runs (each run
+    after the first starts from a composed state) and the reverse pass into
+    pieces; initial states and a final-state cotangent on every slot."""
+    print(f"  saved states cut lens={lens} Dk={Dk} Dv={Dv}", flush=True)
+    rng = np.random.default_rng(sum(lens) + 3 * Dk)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N, H = int(cu[-1]), 1
+    ts = _inputs(rng, N, H, Dk, Dv, torch.bfloat16, gl=0.0005, gh=0.02)
+    S = len(lens)
+    S0 = rng.standard_normal((S, H, Dk, Dv)) * 0.3
+    dF = rng.standard_normal((S, H, Dk, Dv)) * 0.3
+    _saved_states_case(ts, cu, Dk ** -0.5, S0, dF, f"cut {lens}", check_states=False)
