@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--mode", choices=["bench", "kernel", "copy", "backward"], default="bench")
     p.add_argument("--bwd-states", action="store_true",
                    help="--mode backward: the reverse pass reads the states a forward call saved")
+    p.add_argument("--fwd-states", action="store_true",
+                   help="--mode kernel: the forward call also saves the per-chunk states")
     p.add_argument("--entry", choices=["cu_seqlens", "segment_ids"], default="cu_seqlens",
                    help="segment_ids: the step is one pkv_chunk_kda_segment_ids call on the [B, T] ids "
                         "(no conversion, no phantom slots) instead of the conversion + chunk_kda_varlen")
@@ -276,9 +278,10 @@ def main():
     n_segs = int(res.n_segs.item())
 
     if args.mode == "kernel":
+        kst = pkv.new_chunk_states(N, H, cfg.Dk, cfg.Dv, cfg.max_segs, dev) if args.fwd_states else None
         for _ in range(args.warmup + args.steps):
             pkv.chunk_kda_varlen(q, k, v, g, beta, res.cu_seqlens, output_final_state=final_state,
-                                 flags=flags, out=o, workspace=ws)
+                                 flags=flags, out=o, workspace=ws, chunk_states=kst)
         torch.cuda.synchronize()
         log(f"kernel mode: {args.warmup + args.steps} launches of {DOMINANT_KERNEL}")
         return
