@@ -195,8 +195,8 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t x, int64_t* s_scan, i
 __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
     const int32_t* __restrict__ cu, int32_t max_segs, int64_t N, int32_t H, int32_t max_chunks,
     int32_t max_pieces, int32_t max_sums, int32_t* __restrict__ base, int32_t* __restrict__ pbase,
-    int32_t* __restrict__ sbase, int32_t* __restrict__ order, int32_t* __restrict__ counter,
-    int32_t* __restrict__ flags) {
+    int32_t* __restrict__ sbase, int32_t* __restrict__ order, int32_t* __restrict__ oslot,
+    int32_t* __restrict__ counter, int32_t* __restrict__ flags) {
   __shared__ int64_t s_scan[kPlanThreads];
   const int tid = threadIdx.x;
   int64_t running = 0, tot;
@@ -252,18 +252,21 @@ __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
   for (int b = tid; b < kRankBins; b += kPlanThreads) s_bin[b] = 0;
   __syncthreads();
   const int npieces = pbase[max_segs];
-  auto piece_bin = [&](int pc) {
+  auto piece_slot = [&](int pc) {
     int lo = 0, hi = max_segs - 1;  // the slot: last i with pbase[i] <= pc
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (pbase[mid] <= pc) lo = mid; else hi = mid - 1;
     }
+    return lo;
+  };
+  auto piece_bin = [&](int pc, int lo) {
     const int64_t nn = int64_t(base[lo + 1]) - base[lo];
     const int64_t jj = pc - pbase[lo], mm = int64_t(pbase[lo + 1]) - pbase[lo];
     const int64_t len = mm > 0 ? nn * (jj + 1) / mm - nn * jj / mm : 0;
     return int(len < kRankBins - 1 ? len : kRankBins - 1);
   };
-  for (int pc = tid; pc < npieces; pc += kPlanThreads) atomicAdd(&s_bin[piece_bin(pc)], 1);
+  for (int pc = tid; pc < npieces; pc += kPlanThreads) atomicAdd(&s_bin[piece_bin(pc, piece_slot(pc))], 1);
   __syncthreads();
   // exclusive prefix over the bins from the longest down; thread t takes the
   // kRankBins / kPlanThreads bins below kRankBins - 1 - t * that many
@@ -282,7 +285,13 @@ __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
     before += cnt[u];
   }
   __syncthreads();
-  for (int pc = tid; pc < npieces; pc += kPlanThreads) order[atomicAdd(&s_bin[piece_bin(pc)], 1)] = pc;
+  // oslot[r]: the slot of piece order[r], so the passes need no search per item
+  for (int pc = tid; pc < npieces; pc += kPlanThreads) {
+    const int sl = piece_slot(pc);
+    const int r = atomicAdd(&s_bin[piece_bin(pc, sl)], 1);
+    order[r] = pc;
+    oslot[r] = sl;
+  }
 }
 
 // Last index i in [0, n) with tab[i] <= x (tab non-decreasing, tab[0] <= x).
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base,
     const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase,
-    const int32_t* __restrict__ order, int32_t max_segs,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ oslot, int32_t max_segs,
     int32_t units, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
     const float* __restrict__ dfinal, bf16* __restrict__ Sws, float* __restrict__ sumL,
     float* __restrict__ sumD, float* __restrict__ gfin, int32_t from_saved) {
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
   const int32_t* ubase = kSum ? sbase : pbase;
   if (idx / H >= ubase[max_segs]) return;
   const int u = kSum ? int(idx / H) : order[idx / H];
-  const int slot = last_le(ubase, max_segs, u);
+  const int slot = kSum ? last_le(ubase, max_segs, u) : oslot[idx / H];
   const int j = u - ubase[slot];
   const int m = pbase[slot + 1] - pbase[slot];
   if (kSum && (adjoint ? j == 0 : j == m - 1)) return;  // summary not needed
@@ -591,7 +600,8 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base,
     const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase,
-    const int32_t* __restrict__ order, int32_t* __restrict__ counter, int32_t max_segs, int64_t N,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ oslot, int32_t* __restrict__ counter,
+    int32_t max_segs, int64_t N,
     int32_t H, float scale, const float* __restrict__ dfinal, const float* __restrict__ sumL,
     const float* __restrict__ sumD, const float* __restrict__ gfin, const bf16* __restrict__ Sws, bf16* __restrict__ dq,
     bf16* __restrict__ dk, bf16* __restrict__ dv, bf16* __restrict__ dg, bf16* __restrict__ dbeta,
@@ -642,7 +652,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
   while (item < n_items) {
     const int rank = item / H, h = item % H;
     const int pc = order[rank];
-    const int slot = last_le(pbase, max_segs, pc);
+    const int slot = oslot[rank];
     const int j = pc - pbase[slot];
     const int m = pbase[slot + 1] - pbase[slot];
     const int cbase = base[slot];
@@ -1105,7 +1115,7 @@ struct BwdLayout {
   size_t plan_bytes, state_bytes, sumL_bytes, sumD_bytes, gfin_bytes, bytes;
 };
 // Plan words: base, pbase, sbase ([max_segs + 1] each), the queue counter, then
-// order[max_pieces].
+// order[max_pieces] and oslot[max_pieces] (the slot of each ranked piece).
 // own_states: the states live in the workspace (not given by the caller).
 BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs, bool own_states = true) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -1114,7 +1124,7 @@ BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_s
   // pieces of cut segments: m <= ceil(n / kPieceLen) < n / 16 per cut segment (n > kCutMin)
   l.max_sums = l.max_chunks / 16 + 1;
   l.max_pieces = max_segs + l.max_sums;
-  l.plan_bytes = up(((size_t(max_segs) + 1) * 3 + 1 + size_t(l.max_pieces)) * 4);
+  l.plan_bytes = up(((size_t(max_segs) + 1) * 3 + 1 + 2 * size_t(l.max_pieces)) * 4);
   l.state_bytes = own_states ? up(size_t(l.max_chunks) * H * Dk * Dv * 2) : 0;
   l.sumL_bytes = up(size_t(l.max_sums) * 2 * H * Dk * Dv * 4);
   l.sumD_bytes = up(size_t(l.max_sums) * 2 * H * Dk * 4);
@@ -1152,6 +1162,7 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   int32_t* sbase = pbase + (max_segs + 1);
   int32_t* counter = sbase + (max_segs + 1);
   int32_t* order = counter + 1;
+  int32_t* oslot = order + l.max_pieces;
   // the bf16 state before every chunk: the caller's (saved by the forward call,
   // only read here) or the walk's, in the workspace
   bf16* Sws = from_saved ? const_cast<bf16*>(static_cast<const bf16*>(states_in))
@@ -1169,22 +1180,22 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   const bf16* ob = static_cast<const bf16*>(dout);
   hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, max_segs, N, H,
                      int32_t(l.max_chunks), int32_t(l.max_pieces), int32_t(l.max_sums), base, pbase,
-                     sbase, order, counter, flags);
+                     sbase, order, oslot, counter, flags);
   // summaries of the pieces of cut segments, both roles
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, true>), dim3(unsigned(2 * l.max_sums * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     order, max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
+                     order, oslot, max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
                      from_saved);
   // the walk, S role only: the state before every chunk (with saved states, only
   // the final-state term of the gate gradient, when dL/dfinal_state is given)
   if (!from_saved || dF != nullptr)
     hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(l.max_pieces * H)),
                        dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                       order, max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
+                       order, oslot, max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
                        from_saved);
   // the chunks of each (piece, head) walked backwards, Lambda carried
   hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(device_cus() * CC::WG_PER_CU)), dim3(CC::NT),
-                     CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, order, counter,
+                     CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, order, oslot, counter,
                      max_segs, N, H, scale, dF, sumL, sumD, dF ? gfin : nullptr, Sws, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
                      static_cast<bf16*>(db), dinit, flags, int32_t(s0 != nullptr));
