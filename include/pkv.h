@@ -367,7 +367,7 @@ pkv_status pkv_chunk_kda_segment_ids(const void* q, const void* k, const void* v
  * them from the forward call instead). For bf16 with Dk, Dv in {64, 128} it is
  * chunked: the workspace holds
  * the work plan (chunk, piece and summary offsets per slot, the pieces in
- * longest-first order with their slots, a work counter), the bf16 state at every 64-token
+ * longest-first order with a record of each, a work counter), the bf16 state at every 64-token
  * chunk boundary (the adjoint dL/dS is carried in registers while the
  * chunks are walked backwards), and, for segments long enough to be cut into
  * pieces, fp32 piece summaries (end state and decay product per piece and

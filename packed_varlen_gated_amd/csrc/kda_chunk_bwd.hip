@@ -86,6 +86,11 @@ constexpr int kCutMin = 128;
 constexpr int kPieceLen = 64;
 constexpr int kMaxPieces = 16;
 constexpr int kRankBins = 2048;  // piece-length bins of the longest-first order
+// The plan's record of the piece of each rank: its slot, its index j of the
+// slot's m pieces, the slot's first global chunk and chunk count, the segment's
+// token bounds (0, 0 when it has no chunk) and its first summary slot.
+constexpr int kRecWords = 8;
+enum { kRecSlot, kRecPiece, kRecPieces, kRecChunk0, kRecChunks, kRecStart, kRecEnd, kRecSum0 };
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -195,8 +200,8 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t x, int64_t* s_scan, i
 __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
     const int32_t* __restrict__ cu, int32_t max_segs, int64_t N, int32_t H, int32_t max_chunks,
     int32_t max_pieces, int32_t max_sums, int32_t* __restrict__ base, int32_t* __restrict__ pbase,
-    int32_t* __restrict__ sbase, int32_t* __restrict__ order, int32_t* __restrict__ oslot,
-    int32_t* __restrict__ counter, int32_t* __restrict__ flags) {
+    int32_t* __restrict__ sbase, int32_t* __restrict__ irec, int32_t* __restrict__ counter,
+    int32_t* __restrict__ flags) {
   __shared__ int64_t s_scan[kPlanThreads];
   const int tid = threadIdx.x;
   int64_t running = 0, tot;
@@ -245,9 +250,9 @@ __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
   }
   __threadfence_block();
   __syncthreads();
-  // order[r] = the piece of rank r, longest first (a counting sort over the
-  // pieces' chunk counts, capped at kRankBins - 1; ties in any order: results
-  // do not depend on the order)
+  // rank r = the r-th piece, longest first (a counting sort over the pieces'
+  // chunk counts, capped at kRankBins - 1; ties in any order: results do not
+  // depend on the order)
   __shared__ int s_bin[kRankBins];
   for (int b = tid; b < kRankBins; b += kPlanThreads) s_bin[b] = 0;
   __syncthreads();
@@ -285,12 +290,21 @@ __global__ __launch_bounds__(kPlanThreads) void kda_bwd_plan_kernel(
     before += cnt[u];
   }
   __syncthreads();
-  // oslot[r]: the slot of piece order[r], so the passes need no search per item
+  // irec[r]: what a pass needs of the piece of rank r, in one record (the passes
+  // read it with one load instead of chains of dependent ones)
   for (int pc = tid; pc < npieces; pc += kPlanThreads) {
     const int sl = piece_slot(pc);
     const int r = atomicAdd(&s_bin[piece_bin(pc, sl)], 1);
-    order[r] = pc;
-    oslot[r] = sl;
+    int32_t* e = irec + kRecWords * int64_t(r);
+    const int n = base[sl + 1] - base[sl];
+    e[kRecSlot] = sl;
+    e[kRecPiece] = pc - pbase[sl];
+    e[kRecPieces] = pbase[sl + 1] - pbase[sl];
+    e[kRecChunk0] = base[sl];
+    e[kRecChunks] = n;
+    e[kRecStart] = n > 0 ? int32_t(cu_at(cu, sl, N)) : 0;
+    e[kRecEnd] = n > 0 ? int32_t(cu_at(cu, sl + 1, N)) : 0;
+    e[kRecSum0] = sbase[sl];
   }
 }
 
@@ -337,7 +351,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base,
     const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase,
-    const int32_t* __restrict__ order, const int32_t* __restrict__ oslot, int32_t max_segs,
+    const int32_t* __restrict__ irec, int32_t max_segs,
     int32_t units, int64_t N, int32_t H, float scale, const float* __restrict__ initial_state,
     const float* __restrict__ dfinal, bf16* __restrict__ Sws, float* __restrict__ sumL,
     float* __restrict__ sumD, float* __restrict__ gfin, int32_t from_saved) {
@@ -360,10 +374,11 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
   // the plan's order), its segment slot and piece index j of m
   const int32_t* ubase = kSum ? sbase : pbase;
   if (idx / H >= ubase[max_segs]) return;
-  const int u = kSum ? int(idx / H) : order[idx / H];
-  const int slot = kSum ? last_le(ubase, max_segs, u) : oslot[idx / H];
-  const int j = u - ubase[slot];
-  const int m = pbase[slot + 1] - pbase[slot];
+  const int32_t* rec = irec + kRecWords * (idx / H);  // (the walk's piece)
+  const int u = kSum ? int(idx / H) : 0;
+  const int slot = kSum ? last_le(ubase, max_segs, u) : rec[kRecSlot];
+  const int j = kSum ? u - ubase[slot] : rec[kRecPiece];
+  const int m = kSum ? pbase[slot + 1] - pbase[slot] : rec[kRecPieces];
   if (kSum && (adjoint ? j == 0 : j == m - 1)) return;  // summary not needed
   // With the states saved by the forward call (from_saved), the S role's
   // summaries are not needed, and the walk only takes a segment's last piece when
@@ -371,13 +386,13 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
   // chunk's update gives the final state.
   const bool fin = !kSum && !adjoint && dfinal != nullptr && j == m - 1;
   if (from_saved && (kSum ? !adjoint : !fin)) return;
-  const int cbase = base[slot];
-  const int64_t nseg = int64_t(base[slot + 1]) - cbase;
+  const int cbase = kSum ? base[slot] : rec[kRecChunk0];
+  const int64_t nseg = kSum ? int64_t(base[slot + 1]) - cbase : rec[kRecChunks];
   const int cp0 = int(nseg * j / m), c1 = int(nseg * (j + 1) / m);
   const int c0 = (!kSum && from_saved && c1 > cp0) ? c1 - 1 : cp0;
   const int nch = c1 - c0;  // chunks of this piece (walked)
-  const int64_t start = nch > 0 ? cu_at(cu, slot, N) : 0;
-  const int64_t end = nch > 0 ? cu_at(cu, slot + 1, N) : 0;
+  const int64_t start = nch > 0 ? (kSum ? cu_at(cu, slot, N) : rec[kRecStart]) : 0;
+  const int64_t end = nch > 0 ? (kSum ? cu_at(cu, slot + 1, N) : rec[kRecEnd]) : 0;
   const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
   const int d_own = 16 * w + n;  // key channel of this lane's X tiles
 
@@ -410,7 +425,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 128) ? 2 : 4) void kda_b
       const int nj = adjoint ? m - 1 - j : j;
       for (int t = 0; t < nj; ++t) {
         const int jj = adjoint ? m - 1 - t : t;
-        const int s_ = sbase[slot] + jj;
+        const int s_ = rec[kRecSum0] + jj;  // (the walk only: summaries start from zero)
         const float dprod = *sumD_at(s_, adjoint);
         const float* Lp = sumL_at(s_, adjoint);
 #pragma unroll
@@ -600,7 +615,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ base,
     const int32_t* __restrict__ pbase, const int32_t* __restrict__ sbase,
-    const int32_t* __restrict__ order, const int32_t* __restrict__ oslot, int32_t* __restrict__ counter,
+    const int32_t* __restrict__ irec, int32_t* __restrict__ counter,
     int32_t max_segs, int64_t N,
     int32_t H, float scale, const float* __restrict__ dfinal, const float* __restrict__ sumL,
     const float* __restrict__ sumD, const float* __restrict__ gfin, const bf16* __restrict__ Sws, bf16* __restrict__ dq,
@@ -651,15 +666,13 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
   int item = __builtin_amdgcn_readfirstlane(*s_item);
   while (item < n_items) {
     const int rank = item / H, h = item % H;
-    const int pc = order[rank];
-    const int slot = oslot[rank];
-    const int j = pc - pbase[slot];
-    const int m = pbase[slot + 1] - pbase[slot];
-    const int cbase = base[slot];
-    const int nseg = base[slot + 1] - cbase;
+    // the plan's record of the piece (one uniform load)
+    const int32_t* rec = irec + kRecWords * rank;
+    const int slot = rec[kRecSlot], j = rec[kRecPiece], m = rec[kRecPieces];
+    const int cbase = rec[kRecChunk0], nseg = rec[kRecChunks];
     const int c0 = int(int64_t(nseg) * j / m), c1 = int(int64_t(nseg) * (j + 1) / m);
-    const int64_t seg_start = nseg > 0 ? cu_at(cu, slot, N) : 0;
-    const int64_t seg_end = nseg > 0 ? cu_at(cu, slot + 1, N) : 0;
+    const int64_t seg_start = rec[kRecStart], seg_end = rec[kRecEnd];
+    const int sum0 = rec[kRecSum0];
     const int64_t sh = (int64_t(slot) * H + h) * DK * DV;
     int next = 0;
 
@@ -682,7 +695,7 @@ __global__ __launch_bounds__(DK * 4, (DK == 64 && DV == 64) ? 2 : 1) void kda_bw
                              ? dfinal[sh + int64_t(16 * D + 4 * g4 + i) * DV + 16 * eblk(ee) + n] : 0.f;
       }
     for (int t = 0; t < m - 1 - j; ++t) {
-      const int s_ = sbase[slot] + (m - 1 - t);
+      const int s_ = sum0 + (m - 1 - t);
       const int64_t ls = ((int64_t(s_) * 2 + 1) * H + h) * DK;  // adjoint role
       const float* Lp = sumL + ls * DV;
       const float* Dp = sumD + ls;
@@ -1115,7 +1128,7 @@ struct BwdLayout {
   size_t plan_bytes, state_bytes, sumL_bytes, sumD_bytes, gfin_bytes, bytes;
 };
 // Plan words: base, pbase, sbase ([max_segs + 1] each), the queue counter, then
-// order[max_pieces] and oslot[max_pieces] (the slot of each ranked piece).
+// irec[max_pieces][kRecWords] (the record of each ranked piece).
 // own_states: the states live in the workspace (not given by the caller).
 BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_segs, bool own_states = true) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -1124,7 +1137,7 @@ BwdLayout bwd_layout(int64_t N, int32_t H, int32_t Dk, int32_t Dv, int32_t max_s
   // pieces of cut segments: m <= ceil(n / kPieceLen) < n / 16 per cut segment (n > kCutMin)
   l.max_sums = l.max_chunks / 16 + 1;
   l.max_pieces = max_segs + l.max_sums;
-  l.plan_bytes = up(((size_t(max_segs) + 1) * 3 + 1 + 2 * size_t(l.max_pieces)) * 4);
+  l.plan_bytes = up(((size_t(max_segs) + 1) * 3 + 1 + kRecWords * size_t(l.max_pieces)) * 4);
   l.state_bytes = own_states ? up(size_t(l.max_chunks) * H * Dk * Dv * 2) : 0;
   l.sumL_bytes = up(size_t(l.max_sums) * 2 * H * Dk * Dv * 4);
   l.sumD_bytes = up(size_t(l.max_sums) * 2 * H * Dk * 4);
@@ -1161,8 +1174,7 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   int32_t* pbase = base + (max_segs + 1);
   int32_t* sbase = pbase + (max_segs + 1);
   int32_t* counter = sbase + (max_segs + 1);
-  int32_t* order = counter + 1;
-  int32_t* oslot = order + l.max_pieces;
+  int32_t* irec = counter + 1;
   // the bf16 state before every chunk: the caller's (saved by the forward call,
   // only read here) or the walk's, in the workspace
   bf16* Sws = from_saved ? const_cast<bf16*>(static_cast<const bf16*>(states_in))
@@ -1180,22 +1192,22 @@ hipError_t launch_dims(const void* q, const void* k, const void* v, const void* 
   const bf16* ob = static_cast<const bf16*>(dout);
   hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, max_segs, N, H,
                      int32_t(l.max_chunks), int32_t(l.max_pieces), int32_t(l.max_sums), base, pbase,
-                     sbase, order, oslot, counter, flags);
+                     sbase, irec, counter, flags);
   // summaries of the pieces of cut segments, both roles
   hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, true>), dim3(unsigned(2 * l.max_sums * H)),
                      dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                     order, oslot, max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
+                     irec, max_segs, int32_t(l.max_sums), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
                      from_saved);
   // the walk, S role only: the state before every chunk (with saved states, only
   // the final-state term of the gate gradient, when dL/dfinal_state is given)
   if (!from_saved || dF != nullptr)
     hipLaunchKernelGGL((kda_bwd_state_kernel<DK, DV, false>), dim3(unsigned(l.max_pieces * H)),
                        dim3(SC::NT), SC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase,
-                       order, oslot, max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
+                       irec, max_segs, int32_t(l.max_pieces), N, H, scale, s0, dF, Sws, sumL, sumD, gfin,
                        from_saved);
   // the chunks of each (piece, head) walked backwards, Lambda carried
   hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV>), dim3(unsigned(device_cus() * CC::WG_PER_CU)), dim3(CC::NT),
-                     CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, order, oslot, counter,
+                     CC::bytes, stream, qb, kb, vb, gb, bb, ob, cu, base, pbase, sbase, irec, counter,
                      max_segs, N, H, scale, dF, sumL, sumD, dF ? gfin : nullptr, Sws, static_cast<bf16*>(dq),
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), static_cast<bf16*>(dg),
                      static_cast<bf16*>(db), dinit, flags, int32_t(s0 != nullptr));

@@ -214,8 +214,8 @@ def test_backward_entry_validation(lib, kw, code):
 def test_backward_workspace(lib):
     """The chunked reverse pass (bf16, Dk and Dv in {64, 128}) keeps its plan
     (chunk, piece and summary offsets: 3 (max_segs + 1) int32, a work counter
-    and the longest-first order of the pieces with each one's slot, twice
-    max_segs + summaries int32, padded to 256 bytes), one bf16 state of Dk x Dv per (chunk, head), chunks =
+    and an 8-int32 record of each piece in longest-first order, for max_segs +
+    summaries pieces, padded to 256 bytes), one bf16 state of Dk x Dv per (chunk, head), chunks =
     ceil(N / 64) + max_segs, and for the pieces of cut segments, at most
     chunks / 16 + 1 of them, an fp32 Dk x Dv state and Dk decay products per
     (piece, role, head), and Dk fp32 final-state gate terms per (slot, head);
@@ -226,7 +226,7 @@ def test_backward_workspace(lib):
                             (131072, 32, 128, 64, 8)]:
         chunks = (N + 63) // 64 + S
         sums = chunks // 16 + 1
-        expect = (up(4 * (3 * (S + 1) + 1 + 2 * (S + sums))) + up(chunks * H * Dk * Dv * 2)
+        expect = (up(4 * (3 * (S + 1) + 1 + 8 * (S + sums))) + up(chunks * H * Dk * Dv * 2)
                   + up(sums * 2 * H * Dk * Dv * 4) + up(sums * 2 * H * Dk * 4) + up(S * H * Dk * 4))
         assert size(N, H, Dk, Dv, S, 0) == expect, (N, H, S)
     assert size(256, 2, 32, 32, 4, 0) == 0 and size(256, 2, 64, 64, 4, 1) == 0
