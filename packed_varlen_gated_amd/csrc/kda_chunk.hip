@@ -82,6 +82,10 @@ constexpr int kCutMin = 128;      // chunks: segments of at most this many are n
 constexpr int kRunLen = 64;       // chunks: target length of the runs of a cut segment
 constexpr int kMaxRuns = 16;      // runs per segment
 constexpr int kPlanHeader = 64;   // int32 words before the run table
+constexpr int kGroupN = 4;        // chunks: segments of at most this many may share an item
+constexpr int kGroupWin = 12;     // chunks: window of the global chunk order a group's segments start in
+constexpr int kGroupMax = kGroupWin + kGroupN - 1;  // chunks of a group, at most
+static_assert(kGroupMax <= 64, "a group's chunk table is one word per lane");
 constexpr int kPlanCache = 8192;  // segment slots whose chunk counts the plan keeps in LDS
 
 // A blocks (row sub-chunk w, column sub-chunk j), j <= w, in this order (the
@@ -359,6 +363,13 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   int gc0 = 0;  // global index of the run's first chunk (chunks of all slots in slot order)
   bool last = false;
   int64_t start = 0, end = 0;
+  // A group of short segments (whole, in consecutive slots) is one item: its
+  // chunks follow each other in token order. Lane c of ctab corrects chunk c's
+  // place: chunk c starts 64 c - (ctab >> 8) tokens after start, is at most
+  // 64 - (ctab & 127) tokens long, and starts a segment of the group when bit 7
+  // is set. The table is zero for an ordinary item (and past chunk 63), so
+  // the addressing has no branch.
+  uint32_t ctab = 0;
   auto begin_item = [&](int item) __attribute__((always_inline)) {
     const int rank = item / H;
     h = item % H;
@@ -378,6 +389,26 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
       sbase = e[4];    // their state slots: sbase .. sbase + run_idx - 1
       last = e[5] != 0;
       gc0 = e[6] + c0;
+      const int ns = e[7];  // > 0: slots slot .. slot + ns - 1 form a group
+      ctab = 0;
+      if (ns > 0) {
+        start = cu[slot];
+        end = cu[slot + ns];
+        nchunks = c1;
+        int64_t a0 = start;
+        int c = 0;
+        for (int j = 1; j <= ns; ++j) {
+          const int64_t a1 = cu[slot + j];
+          for (int64_t p = a0; p < a1; p += kC, ++c) {
+            const uint32_t L = uint32_t(a1 - p < kC ? a1 - p : kC);
+            if (lane == c)
+              ctab = (uint32_t(int64_t(c) * kC - (p - start)) << 8) | (p == a0 && c > 0 ? 128u : 0u) |
+                     (uint32_t(kC) - L);
+          }
+          a0 = a1;
+        }
+        return;
+      }
     }
     // the run: chunks [c0, c1) of the segment, which are aligned to its start
     // (the plan holds well-formed, non-empty segments only)
@@ -398,9 +429,18 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   const uint32_t rowK = uint32_t(H) * DK * 2;  // bytes between tokens (q, k, g)
   const uint32_t rowV = uint32_t(H) * DV * 2;
   const uint32_t rowB = uint32_t(H) * 2;
-  auto chunk_len = [&](int c) __attribute__((always_inline)) {
-    const int64_t rem = end - (start + int64_t(c) * kC);
-    return int(rem < kC ? rem : kC);
+  // chunk c's first token and length (segments, and so items, are below 2^31 tokens)
+  struct CPos {
+    int64_t p0;
+    int len;
+  };
+  auto chunk_pos = [&](int c) __attribute__((always_inline)) {
+    const uint32_t w = uint32_t(__builtin_amdgcn_readlane(int(ctab), c & 63));
+    CPos r;
+    r.p0 = start + int64_t(c) * kC - int64_t(w >> 8);
+    const int rem = int(end - r.p0), cap = kC - int(w & 127u);
+    r.len = rem < cap ? rem : cap;
+    return r;
   };
 
   // ---------------------------------------------------------------- roles
@@ -439,8 +479,9 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   };
   auto src_of = [&](int c) __attribute__((always_inline)) {
     const bool live = c < nchunks;
-    const int64_t p0 = start + int64_t(live ? c : 0) * kC;
-    const int Lc = live ? chunk_len(c) : 1;
+    const CPos cp = chunk_pos(live ? c : 0);
+    const int64_t p0 = cp.p0;
+    const int Lc = live ? cp.len : 1;
     Src r;
     r.tokbase = p0 * H + h;
     r.nK = live ? uint32_t(Lc - 1) * rowK + DK * 2 : 0u;
@@ -699,6 +740,12 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // gives each lane one row's four columns (one 8-byte store): swap the
   // off-diagonal 2 x 2 blocks with lane ^ 2 (quad_perm [2,3,0,1]), then the
   // halves of each block's rows with lane ^ 1 (quad_perm [1,0,3,2], v_perm_b32).
+  auto zero_state = [&](f32x4 (&S)[DT][ET]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int et = 0; et < ET; ++et) S[dt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
   auto save_state = [&](const f32x4 (&S)[DT][ET], int gc) __attribute__((always_inline)) {
     // one 32-bit base offset per lane plus an immediate per (dt, et)
     const auto rs = rsrc(chunk_states + (int64_t(gc) * H + h) * DK * DV, DK * DV * 2);
@@ -834,8 +881,9 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // the stage, whole rows per store (producer w: the rows of sub-chunk w, 16
   // lanes per 256-byte row); rows past the chunk end are dropped by the range.
   auto store_rows = [&](int c) __attribute__((always_inline)) {
-    const int64_t p0 = start + int64_t(c) * kC;
-    const int Lc = chunk_len(c);
+    const CPos cp = chunk_pos(c);
+    const int64_t p0 = cp.p0;
+    const int Lc = cp.len;
     const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -849,8 +897,9 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
   // packed in the first half. Issuing the stores here keeps them off the first
   // half, where the producers' loads fill the vector memory queue.
   auto store_out = [&](const uint32_t (&opk)[4][2 * ET], int c) __attribute__((always_inline)) {
-    const int64_t p0 = start + int64_t(c) * kC;
-    const int Lc = chunk_len(c);
+    const CPos cp = chunk_pos(c);
+    const int64_t p0 = cp.p0;
+    const int Lc = cp.len;
     const auto ro = rsrc(o + (p0 * H + h) * DV, uint32_t(Lc - 1) * rowV + DV * 2);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -1054,6 +1103,8 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     };
     for (int item = first_item; item < n_items;) {
       begin_item(item);
+      // bit c: chunk c > 0 starts a segment of the group (none in an ordinary item)
+      const uint64_t fresh_mask = __builtin_amdgcn_ballot_w64((ctab & 128u) != 0);
       f32x4 S[DT][ET];  // state rows [0, DK), columns [e0, e0 + EW)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -1131,10 +1182,12 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
           __syncthreads();
           if (!C::stage_o && s >= 1) store_out(opk, s - 1);
           if (s < nchunks) {
-            // (the zero state before a segment's first chunk, without an initial
-            // state, is not stored)
+            // a grouped segment after the first starts from zero (the zero state
+            // before a segment's first chunk, without an initial state, is not stored)
+            const bool fresh = s == 0 || ((fresh_mask >> (s & 63)) & 1);
+            if (fresh && s > 0) zero_state(S);
             if constexpr (kSave)
-              if (s > 0 || run_idx > 0 || initial_state != nullptr) save_state(S, gc0 + s);
+              if (!fresh || run_idx > 0 || initial_state != nullptr) save_state(S, gc0 + s);
             f32x4 ab[3];
             a_blocks_mma(ab);
             consume_inter(S, acc);
@@ -1147,7 +1200,10 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
           __syncthreads();
           if constexpr (!C::stage_o) store_out(opk, s);
           if (s + 1 < nchunks) {
-            if constexpr (kSave) save_state(S, gc0 + s + 1);
+            const bool fresh = (fresh_mask >> ((s + 1) & 63)) & 1;
+            if (fresh) zero_state(S);
+            if constexpr (kSave)
+              if (!fresh) save_state(S, gc0 + s + 1);
             f32x4 ab[3];
             a_blocks_mma(ab);
             consume_inter(S, acc);
@@ -1223,9 +1279,15 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 //    cut (and with it the rounding of the composed states) never depends on
 //    the other segments of the launch; empty and malformed segments have no
 //    run (malformed ones set PKV_FLAG_BAD_CU_SEQLENS here);
-// 2. runs are ranked longest first through a histogram of run lengths (ties in
-//    any order: results do not depend on the order), and so are the runs that
-//    are not last in their segment, which the state pass takes.
+// 2. in a call without initial and final states, short segments (at most
+//    kGroupN chunks) in consecutive slots whose first chunks fall in one window
+//    of kGroupWin chunks of the global chunk order form one item (a group):
+//    its chunks run back to back, each segment from the zero state, so a
+//    short document no longer pays a pipeline fill and drain of its own; the
+//    outputs are those of the segments run as items of their own;
+// 3. items are ranked longest first through a histogram of their lengths (ties
+//    in any order: results do not depend on the order), and so are the runs
+//    that are not last in their segment, which the state pass takes.
 // The state slots of a segment's first m - 1 runs are consecutive from sbase
 // (exclusive prefix of m - 1 over the segments, computed tile by tile).
 // Chunk counts are below 2^26 (N <= INT32_MAX), so all per-segment arithmetic
@@ -1270,7 +1332,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
                                                                 const int32_t* __restrict__ seg_ids,
                                                                 int32_t max_segs_arg, int32_t N,
                                                                 int32_t states_max,
-                                                                int32_t runs_max,
+                                                                int32_t runs_max, int32_t group,
                                                                 int32_t* __restrict__ plan,
                                                                 int32_t* __restrict__ flags) {
   __shared__ int s_hr[kHistBins];  // main runs per length bin, then next free rank
@@ -1302,6 +1364,35 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   }
   if (any_bad && flags != nullptr) atomicOr(flags, kFlagBadCuSeqlens);
   __syncthreads();
+  auto nchunks_of = [&](int i) -> int {
+    bool bad;
+    return cached ? s_n[i] : chunks(i, bad);
+  };
+  // Groups (only when group != 0): short segments (1..kGroupN chunks, one run
+  // each) in consecutive slots, with no empty slot between them, whose first
+  // chunks fall in the same window of kGroupWin chunks of the global chunk
+  // order, share one item. The grouping only changes which work-group runs a
+  // segment and when: each segment still starts from the zero state. Returns
+  // 0 for a member that is not its group's first slot, else the number of
+  // slots in the group (1: the segment alone); *tot gets the group's chunks.
+  auto group_span = [&](int i, int n, int cb, int* tot) -> int {
+    *tot = n;
+    if (!group || n > kGroupN) return 1;
+    const int win = cb / kGroupWin;
+    if (i > 0) {
+      const int np = nchunks_of(i - 1);
+      if (np >= 1 && np <= kGroupN && (cb - np) / kGroupWin == win) return 0;
+    }
+    int j = i + 1, c = cb + n;
+    while (j < max_segs && c / kGroupWin == win) {
+      const int nj = nchunks_of(j);
+      if (nj < 1 || nj > kGroupN) break;
+      *tot += nj;
+      c += nj;
+      ++j;
+    }
+    return j - i;
+  };
 
   // Runs of each segment, with the state-slot budget enforced in slot order:
   // a segment whose extra runs would not fit stays whole (only on malformed
@@ -1326,7 +1417,14 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   };
   // A segment of n chunks in m runs has n % m runs of q + 1 chunks and the
   // rest of q (q = n / m); its last run is one of the long ones iff n % m > 0.
-  pass([&](int, int n, int m, int, int) {
+  pass([&](int i, int n, int m, int, int cb) {
+    int tot = n;
+    const int gs = m == 1 ? group_span(i, n, cb, &tot) : 1;
+    if (gs == 0) return;
+    if (gs > 1) {
+      atomicAdd(&s_hr[len_bin(tot)], 1);
+      return;
+    }
     const int q = n / m, nl = n - q * m, last_long = nl > 0;
     atomicAdd(&s_hr[len_bin(q + 1)], nl);
     atomicAdd(&s_hr[len_bin(q)], m - nl);
@@ -1364,6 +1462,21 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
     plan[3] = 0;
   }
   pass([&](int i, int n, int m, int sb, int cb) {
+    int tot = n;
+    const int gs = m == 1 ? group_span(i, n, cb, &tot) : 1;
+    if (gs == 0) return;
+    if (gs > 1) {  // slots i .. i + gs - 1, chunks 0 .. tot - 1 of the group
+      int32_t* e = plan + kPlanHeader + 8 * atomicAdd(&s_hr[len_bin(tot)], 1);
+      e[0] = i;
+      e[1] = 0;
+      e[2] = tot;
+      e[3] = 0;
+      e[4] = sb;
+      e[5] = 1;
+      e[6] = cb;
+      e[7] = gs;
+      return;
+    }
     // ranks for the segment's long and short runs, reserved in one go each
     const int q = n / m, nl = n - q * m, last_long = nl > 0;
     int rl = atomicAdd(&s_hr[len_bin(q + 1)], nl);
@@ -1381,6 +1494,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
       e[4] = sb;
       e[5] = j + 1 == m;
       e[6] = cb;
+      e[7] = 0;
       if (j + 1 < m) {
         int32_t* f = plan + states_word_off + 4 * (lng ? sl++ : ss++);
         f[0] = i;
@@ -1463,7 +1577,8 @@ hipError_t launch_dims(const Launch& a) {
   float* states = reinterpret_cast<float*>(a.ws + L.off_L);
   float* decays = reinterpret_cast<float*>(a.ws + L.off_D);
   hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, a.stream, a.cu, a.n_dev, a.seg_ids,
-                     a.max_segs, int32_t(a.N), int32_t(L.states_max), int32_t(L.runs_max), plan, a.flags);
+                     a.max_segs, int32_t(a.N), int32_t(L.states_max), int32_t(L.runs_max),
+                     int32_t(a.s0 == nullptr && a.fs == nullptr), plan, a.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const auto qp = static_cast<const bf16*>(a.q), kp = static_cast<const bf16*>(a.k);

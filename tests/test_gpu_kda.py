@@ -374,6 +374,83 @@ def test_packed_equals_each_document_alone_long_context():
     assert cut >= 3  # the invariant is tested where cuts happen
 
 
+def _plan_items(lens, grouped):
+    """Items of the forward plan for segments of these token counts (slot order):
+    a segment of n chunks is _runs_of(n) runs; when grouped (a call without
+    initial and final states), short segments (1..4 chunks) in consecutive slots
+    whose first chunks fall in the same 12-chunk window of the global chunk order
+    share one item."""
+    n = [-(-int(L) // 64) for L in lens]
+    cb = np.concatenate([[0], np.cumsum(n)])
+    items, span = 0, 0
+    for i, ni in enumerate(n):
+        if ni == 0:
+            continue
+        short = grouped and ni <= 4
+        if short and i > 0 and 1 <= n[i - 1] <= 4 and cb[i - 1] // 12 == cb[i] // 12:
+            span += ni
+            assert span <= 15
+            continue
+        span = ni
+        items += _runs_of(ni)
+    return items
+
+
+def _group_lens(rng):
+    """Short documents of 1..300 tokens (1..5 chunks) with exact multiples of 64,
+    single tokens, empty slots and a document cut into runs among them."""
+    lens = list(rng.integers(1, 301, 70))
+    lens[3:9] = [64, 1, 128, 0, 65, 256]
+    lens[20:23] = [9000, 0, 320]   # 141 chunks (3 runs), an empty slot, 5 chunks
+    lens[40:44] = [1, 1, 1, 63]
+    return lens
+
+
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_grouped_short_documents(Dk, Dv):
+    """Without initial and final states, short documents share an item and each
+    starts from the zero state inside it: the outputs, and the states kept
+    before every chunk, are bit-identical to those of the call that runs every
+    document as its own item (the same call with final states), and the outputs
+    match the oracle; the plan holds the expected number of items."""
+    pkv = _pkv()
+    rng = np.random.default_rng(Dk + 3 * Dv)
+    lens = _group_lens(rng)
+    slots = len(lens) + 3
+    real = np.concatenate([[0], np.cumsum(lens)])
+    cu = np.concatenate([real, [real[-1]] * (slots + 1 - len(real))]).astype(np.int64)
+    N, H = int(real[-1]) + 5, 2
+    print(f"  grouped Dk={Dk} Dv={Dv}: N {N}, {slots} slots, items {_plan_items(lens, True)} "
+          f"grouped / {_plan_items(lens, False)}", flush=True)
+    ts = _small_case(rng, N, H, Dk, Dv, torch.bfloat16, None)
+    q, k, v, g, beta = [t.to(device())[None] for t in ts]
+    cud = torch.from_numpy(cu.astype(np.int32)).to(device())
+    ws = torch.empty(pkv.chunk_kda_varlen_workspace_size(N, H, Dk, Dv, slots, torch.bfloat16),
+                     dtype=torch.uint8, device=device())
+    nst = pkv.chunk_kda_states_size(N, H, Dk, Dv, slots)
+    st_g = torch.zeros(nst, dtype=torch.uint8, device=device())
+    st_u = torch.zeros(nst, dtype=torch.uint8, device=device())
+    o_g, none = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, output_final_state=False, workspace=ws)
+    torch.cuda.synchronize()
+    items_g = ws[:8].view(torch.int32).cpu().tolist()[0]
+    o_u, fs = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, workspace=ws)
+    torch.cuda.synchronize()
+    items_u = ws[:8].view(torch.int32).cpu().tolist()[0]
+    assert none is None
+    assert (items_g, items_u) == (_plan_items(lens, True), _plan_items(lens, False))
+    assert items_g < items_u
+    assert torch.equal(o_g, o_u)
+    o_gs, _ = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, output_final_state=False, chunk_states=st_g)
+    o_us, _ = pkv.chunk_kda_varlen(q, k, v, g, beta, cud, chunk_states=st_u)
+    torch.cuda.synchronize()
+    assert torch.equal(o_gs, o_g) and torch.equal(o_us, o_g)
+    assert torch.equal(st_g, st_u)
+    assert torch.count_nonzero(st_g).item() > 0
+    ro, rfs = oracle.chunk_kda_varlen(*[f64(t) for t in ts], cu)
+    check_close(f64(o_g[0]), ro, "bf16", "o")
+    check_close(f64(fs), rfs, "bf16", "final states")
+
+
 # RFC-0026 section 3.3's initial_state, one per segment slot: every segment
 # starts from its slot's state; empty slots keep it as their final state.
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
