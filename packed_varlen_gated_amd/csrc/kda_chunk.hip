@@ -423,6 +423,10 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
     if (end < start) end = start;
     nchunks = int((end - start + kC - 1) / kC);
   };
+  // A state pass with nothing to do ends before touching the queue (its
+  // work-groups would otherwise line up on the counter's atomic).
+  if constexpr (kState)
+    if (n_items == 0) return;
   if (tid == 0) *s_item = atomicAdd(counter, 1);
   __syncthreads();
   const int first_item = __builtin_amdgcn_readfirstlane(*s_item);
