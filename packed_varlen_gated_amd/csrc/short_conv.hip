@@ -10,7 +10,10 @@
 // mask of the tile is computed once into LDS as one bit per (token, tap); each
 // thread then streams its VEC contiguous channels (16-byte vectors) down the
 // tile, keeping the previous Kc-1 input vectors in registers, so every input
-// element is read once plus a Kc-1 token halo per tile.
+// element is read once plus a Kc-1 token halo per tile. A full tile is read in
+// batches of kBatch tokens whose loads are issued one batch ahead of the
+// arithmetic (a register double buffer), so each wave keeps kBatch vector
+// loads in flight instead of one.
 
 #include "common.h"
 
@@ -19,11 +22,41 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTokens = 32;
+constexpr int kBatch = 8;
+static_assert(kTokens % kBatch == 0, "a full tile is whole batches");
 
 template <typename T, int VEC>
 struct Vec {
   T v[VEC];
 };
+
+// One output token: y = sum_k [mask bit k] w_k x[t-k] over the VEC channels,
+// in fp32 with tap 0 first; then the history moves one token on.
+template <typename T, int VEC, int KC>
+__device__ __forceinline__ void conv_token(const Vec<T, VEC>& in, uint32_t m, const float (&wr)[VEC][KC],
+                                           float (&hist)[KC > 1 ? KC - 1 : 1][VEC], T* dst) {
+  float cur[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) cur[c] = to_f32(in.v[c]);
+  Vec<T, VEC> out;
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) {
+    float acc = (m & 1u) ? wr[c][0] * cur[c] : 0.f;
+#pragma unroll
+    for (int k = 1; k < KC; ++k)
+      if ((m >> k) & 1u) acc = fmaf(wr[c][k], hist[k - 1][c], acc);
+    out.v[c] = from_f32<T>(acc);
+  }
+  *reinterpret_cast<Vec<T, VEC>*>(dst) = out;
+#pragma unroll
+  for (int j = KC - 2; j >= 1; --j)
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) hist[j][c] = hist[j - 1][c];
+  if (KC > 1) {
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) hist[0][c] = cur[c];
+  }
+}
 
 template <typename T, int VEC, int KC>
 __global__ __launch_bounds__(kThreads) void short_conv_kernel(
@@ -76,31 +109,29 @@ __global__ __launch_bounds__(kThreads) void short_conv_kernel(
   }
 
   const int nt = (T_len - t0) < kTokens ? int(T_len - t0) : kTokens;
+  if (nt == kTokens) {
+    Vec<T, VEC> buf[2][kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) buf[0][i] = *reinterpret_cast<const Vec<T, VEC>*>(xrow + (t0 + i) * F);
+#pragma unroll
+    for (int bb = 0; bb < kTokens / kBatch; ++bb) {
+      if (bb + 1 < kTokens / kBatch) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          buf[(bb + 1) & 1][i] =
+              *reinterpret_cast<const Vec<T, VEC>*>(xrow + (t0 + (bb + 1) * kBatch + i) * F);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int ti = bb * kBatch + i;
+        conv_token<T, VEC, KC>(buf[bb & 1][i], s_mask[ti], wr, hist, yrow + (t0 + ti) * F);
+      }
+    }
+    return;
+  }
   for (int i = 0; i < nt; ++i) {
-    const int64_t t = t0 + i;
-    const Vec<T, VEC> in = *reinterpret_cast<const Vec<T, VEC>*>(xrow + t * F);
-    const uint32_t m = s_mask[i];
-    float cur[VEC];
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) cur[c] = to_f32(in.v[c]);
-    Vec<T, VEC> out;
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-      float acc = (m & 1u) ? wr[c][0] * cur[c] : 0.f;
-#pragma unroll
-      for (int k = 1; k < KC; ++k)
-        if ((m >> k) & 1u) acc = fmaf(wr[c][k], hist[k - 1][c], acc);
-      out.v[c] = from_f32<T>(acc);
-    }
-    *reinterpret_cast<Vec<T, VEC>*>(yrow + t * F) = out;
-#pragma unroll
-    for (int j = KC - 2; j >= 1; --j)
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) hist[j][c] = hist[j - 1][c];
-    if (KC > 1) {
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) hist[0][c] = cur[c];
-    }
+    const Vec<T, VEC> in = *reinterpret_cast<const Vec<T, VEC>*>(xrow + (t0 + i) * F);
+    conv_token<T, VEC, KC>(in, s_mask[i], wr, hist, yrow + (t0 + i) * F);
   }
 }
 
