@@ -76,7 +76,7 @@ constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 f
 // Work plan (built on the device by kda_plan_kernel; see there). How a
 // segment is cut depends on its own chunk count and these constants only, so
 // a segment's results never depend on the other segments of the launch.
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 1024;
 constexpr int kHistBins = 2048;   // run-length bins of the longest-first order
 constexpr int kCutMin = 128;      // chunks: segments of at most this many are never cut
 constexpr int kRunLen = 64;       // chunks: target length of the runs of a cut segment
@@ -1295,7 +1295,8 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 // The state slots of a segment's first m - 1 runs are consecutive from sbase
 // (exclusive prefix of m - 1 over the segments, computed tile by tile).
 // Chunk counts are below 2^26 (N <= INT32_MAX), so all per-segment arithmetic
-// is 32-bit; the work-group is small because the work is tiny and serial.
+// is 32-bit. One work-group of 1024 threads: a call of up to 1024 slots is a
+// single tile, so each pass over the slots takes one block scan.
 __device__ __forceinline__ int plan_runs(int n) {
   if (n <= 0) return 0;
   if (n <= kCutMin) return 1;
@@ -1306,27 +1307,32 @@ __device__ __forceinline__ int plan_runs(int n) {
 __device__ __forceinline__ int run_begin(int n, int m, int j) { return int(uint32_t(n * j) / uint32_t(m)); }
 __device__ __forceinline__ int len_bin(int len) { return len < kHistBins - 1 ? len : kHistBins - 1; }
 
-// Exclusive prefix over the work-group (kPlanThreads threads); *total gets the sum.
-__device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
+// Two exclusive prefixes over the work-group at once (the barriers of one);
+// *tx and *ty get the sums.
+__device__ void block_exclusive_scan2(int x, int y, int2* s_tmp2, int* ex, int* ey, int* tx, int* ty) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int inc = x;
+  int ix = x, iy = y;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += y;
+    const int ux = __shfl_up(ix, d, 64), uy = __shfl_up(iy, d, 64);
+    if (lane >= d) { ix += ux; iy += uy; }
   }
-  if (lane == 63) s_tmp[wv] = inc;
+  if (lane == 63) s_tmp2[wv] = make_int2(ix, iy);
   __syncthreads();
-  int before = 0, all = 0;
+  int bx = 0, by = 0, ax = 0, ay = 0;
 #pragma unroll
   for (int i = 0; i < kPlanThreads / 64; ++i) {
-    const int t = s_tmp[i];
-    before += i < wv ? t : 0;
-    all += t;
+    const int2 t = s_tmp2[i];
+    bx += i < wv ? t.x : 0;
+    by += i < wv ? t.y : 0;
+    ax += t.x;
+    ay += t.y;
   }
   __syncthreads();
-  *total = all;
-  return before + inc - x;
+  *tx = ax;
+  *ty = ay;
+  *ex = bx + ix - x;
+  *ey = by + iy - y;
 }
 
 // seg_ids (segments from a [B, T] id scan): a segment whose first id is 0 is
@@ -1341,7 +1347,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
                                                                 int32_t* __restrict__ flags) {
   __shared__ int s_hr[kHistBins];  // main runs per length bin, then next free rank
   __shared__ int s_hs[kHistBins];  // state runs likewise
-  __shared__ int s_tmp[kPlanThreads / 64];
+  __shared__ int2 s_tmp2[kPlanThreads / 64];
   __shared__ int s_n[kPlanCache];  // chunk counts, when max_segs <= kPlanCache
   const int tid = threadIdx.x;
   // segment slots: the caller's count, or the one a boundary scan left on the device
@@ -1409,9 +1415,10 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
       bool bad;
       const int n = i >= max_segs ? 0 : cached ? s_n[i] : chunks(i, bad);
       int m = plan_runs(n);
-      int tile_total, tile_chunks;
-      const int sb = carry + block_exclusive_scan(m > 1 ? m - 1 : 0, s_tmp, &tile_total);
-      const int cb = ccarry + block_exclusive_scan(n, s_tmp, &tile_chunks);
+      int tile_total, tile_chunks, esb, ecb;
+      block_exclusive_scan2(m > 1 ? m - 1 : 0, n, s_tmp2, &esb, &ecb, &tile_total, &tile_chunks);
+      const int sb = carry + esb;
+      const int cb = ccarry + ecb;
       if (m > 1 && sb + m - 1 > states_max) m = 1;
       // a clamped segment's slots stay unused; later segments keep theirs
       if (m > 0) body(i, n, m, sb, cb);
@@ -1447,9 +1454,8 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
     sr += cr[u];
     ss += cs[u];
   }
-  int tr, ts;
-  int er = block_exclusive_scan(sr, s_tmp, &tr);
-  int es = block_exclusive_scan(ss, s_tmp, &ts);
+  int tr, ts, er, es;
+  block_exclusive_scan2(sr, ss, s_tmp2, &er, &es, &tr, &ts);
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int b = kHistBins - 1 - (tid * kPer + u);
