@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
   const uint32_t T32 = uint32_t(T);
   const uint32_t step = uint32_t(4 * kThreads) % T32;
   int running = 0;  // boundaries before the tile
+  int first_id = 0;  // seg[0], kept from thread 0's first load for the leading-pad flag
   for (int64_t base = 0; base < N; base += kTilePos) {
     // A. boundary bits of each group. The id before group m is the last id
     // of group m - 1: lane - 1's (a shuffle), for lane 0 the wave before's
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
       for (int j = 0; j < kGroupsPerThread; ++j) s_edge[j * kWaves + wid] = xs[j][3];
     }
     const int before_tile = (tid == 0 && base > 0) ? seg[base - 1] : 0;
+    if (base == 0) first_id = xs[0][0];
     __syncthreads();
     int tile_nz = -1;  // last non-zero position in the tile, tile-relative
 #pragma unroll
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void cu_seqlens_kernel(
     if (flags_out != nullptr) {
       int32_t f = 0;
       if (n > max_segs) f |= kFlagOverflow;
-      if (seg[0] == 0 && e_last > 0) f |= kFlagLeadingPad;
+      if (first_id == 0 && e_last > 0) f |= kFlagLeadingPad;
       *flags_out = f;
     }
   }
