@@ -76,7 +76,8 @@ constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 f
 // Work plan (built on the device by kda_plan_kernel; see there). How a
 // segment is cut depends on its own chunk count and these constants only, so
 // a segment's results never depend on the other segments of the launch.
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 1024;  // plan work-group for calls of more than kPlanSmall slots
+constexpr int kPlanSmall = 256;     // and for calls of at most this many slots (fewer waves to synchronise)
 constexpr int kHistBins = 2048;   // run-length bins of the longest-first order
 constexpr int kCutMin = 128;      // chunks: segments of at most this many are never cut
 constexpr int kRunLen = 64;       // chunks: target length of the runs of a cut segment
@@ -1295,8 +1296,9 @@ __global__ __launch_bounds__(512, (DK == 64 && DV == 64) ? 4 : 1) void kda_chunk
 // The state slots of a segment's first m - 1 runs are consecutive from sbase
 // (exclusive prefix of m - 1 over the segments, computed tile by tile).
 // Chunk counts are below 2^26 (N <= INT32_MAX), so all per-segment arithmetic
-// is 32-bit. One work-group of 1024 threads: a call of up to 1024 slots is a
-// single tile, so each pass over the slots takes one block scan.
+// is 32-bit. One work-group of kPlanSmall threads for up to kPlanSmall slots,
+// else of kPlanThreads: a call of up to 1024 slots is a single tile, so each
+// pass over the slots takes one block scan.
 __device__ __forceinline__ int plan_runs(int n) {
   if (n <= 0) return 0;
   if (n <= kCutMin) return 1;
@@ -1309,6 +1311,7 @@ __device__ __forceinline__ int len_bin(int len) { return len < kHistBins - 1 ? l
 
 // Two exclusive prefixes over the work-group at once (the barriers of one);
 // *tx and *ty get the sums.
+template <int NT>
 __device__ void block_exclusive_scan2(int x, int y, int2* s_tmp2, int* ex, int* ey, int* tx, int* ty) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int ix = x, iy = y;
@@ -1321,7 +1324,7 @@ __device__ void block_exclusive_scan2(int x, int y, int2* s_tmp2, int* ex, int* 
   __syncthreads();
   int bx = 0, by = 0, ax = 0, ay = 0;
 #pragma unroll
-  for (int i = 0; i < kPlanThreads / 64; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const int2 t = s_tmp2[i];
     bx += i < wv ? t.x : 0;
     by += i < wv ? t.y : 0;
@@ -1337,7 +1340,8 @@ __device__ void block_exclusive_scan2(int x, int y, int2* s_tmp2, int* ex, int* 
 
 // seg_ids (segments from a [B, T] id scan): a segment whose first id is 0 is
 // padding and gets no run (its tokens leave the state alone and output 0).
-__global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* __restrict__ cu,
+template <int NT>
+__global__ __launch_bounds__(NT) void kda_plan_kernel(const int32_t* __restrict__ cu,
                                                                 const int32_t* __restrict__ n_dev,
                                                                 const int32_t* __restrict__ seg_ids,
                                                                 int32_t max_segs_arg, int32_t N,
@@ -1347,14 +1351,14 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
                                                                 int32_t* __restrict__ flags) {
   __shared__ int s_hr[kHistBins];  // main runs per length bin, then next free rank
   __shared__ int s_hs[kHistBins];  // state runs likewise
-  __shared__ int2 s_tmp2[kPlanThreads / 64];
+  __shared__ int2 s_tmp2[NT / 64];
   __shared__ int s_n[kPlanCache];  // chunk counts, when max_segs <= kPlanCache
   const int tid = threadIdx.x;
   // segment slots: the caller's count, or the one a boundary scan left on the device
   const int max_segs = n_dev != nullptr ? *n_dev : max_segs_arg;
   const int states_word_off = kPlanHeader + 8 * runs_max;
   const bool cached = max_segs <= kPlanCache;
-  for (int i = tid; i < kHistBins; i += kPlanThreads) s_hr[i] = s_hs[i] = 0;
+  for (int i = tid; i < kHistBins; i += NT) s_hr[i] = s_hs[i] = 0;
   __syncthreads();
   // chunks of segment i; malformed and padding ones count 0, malformed ones are flagged
   auto chunks = [&](int i, bool& bad) -> int {
@@ -1366,7 +1370,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
     return int((uint32_t(e - a) + kC - 1) / kC);
   };
   bool any_bad = false;
-  for (int i = tid; i < max_segs; i += kPlanThreads) {
+  for (int i = tid; i < max_segs; i += NT) {
     bool bad;
     const int n = chunks(i, bad);
     if (cached) s_n[i] = n;
@@ -1410,13 +1414,13 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   // cb: chunks of the slots before slot i (the global index of slot i's first chunk)
   auto pass = [&](auto&& body) {
     int carry = 0, ccarry = 0;
-    for (int base = 0; base < max_segs; base += kPlanThreads) {
+    for (int base = 0; base < max_segs; base += NT) {
       const int i = base + tid;
       bool bad;
       const int n = i >= max_segs ? 0 : cached ? s_n[i] : chunks(i, bad);
       int m = plan_runs(n);
       int tile_total, tile_chunks, esb, ecb;
-      block_exclusive_scan2(m > 1 ? m - 1 : 0, n, s_tmp2, &esb, &ecb, &tile_total, &tile_chunks);
+      block_exclusive_scan2<NT>(m > 1 ? m - 1 : 0, n, s_tmp2, &esb, &ecb, &tile_total, &tile_chunks);
       const int sb = carry + esb;
       const int cb = ccarry + ecb;
       if (m > 1 && sb + m - 1 > states_max) m = 1;
@@ -1444,7 +1448,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
   });
   __syncthreads();
   // bins to first ranks, longest first (suffix sums), consecutive bins per thread
-  constexpr int kPer = kHistBins / kPlanThreads;
+  constexpr int kPer = kHistBins / NT;
   int cr[kPer], cs[kPer], sr = 0, ss = 0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
@@ -1455,7 +1459,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_plan_kernel(const int32_t* _
     ss += cs[u];
   }
   int tr, ts, er, es;
-  block_exclusive_scan2(sr, ss, s_tmp2, &er, &es, &tr, &ts);
+  block_exclusive_scan2<NT>(sr, ss, s_tmp2, &er, &es, &tr, &ts);
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int b = kHistBins - 1 - (tid * kPer + u);
@@ -1586,9 +1590,14 @@ hipError_t launch_dims(const Launch& a) {
   int32_t* plan = reinterpret_cast<int32_t*>(a.ws);
   float* states = reinterpret_cast<float*>(a.ws + L.off_L);
   float* decays = reinterpret_cast<float*>(a.ws + L.off_D);
-  hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(kPlanThreads), 0, a.stream, a.cu, a.n_dev, a.seg_ids,
-                     a.max_segs, int32_t(a.N), int32_t(L.states_max), int32_t(L.runs_max),
-                     int32_t(a.s0 == nullptr && a.fs == nullptr), plan, a.flags);
+  if (a.max_segs <= kPlanSmall)
+    hipLaunchKernelGGL(kda_plan_kernel<kPlanSmall>, dim3(1), dim3(kPlanSmall), 0, a.stream, a.cu, a.n_dev,
+                       a.seg_ids, a.max_segs, int32_t(a.N), int32_t(L.states_max), int32_t(L.runs_max),
+                       int32_t(a.s0 == nullptr && a.fs == nullptr), plan, a.flags);
+  else
+    hipLaunchKernelGGL(kda_plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), 0, a.stream, a.cu, a.n_dev,
+                       a.seg_ids, a.max_segs, int32_t(a.N), int32_t(L.states_max), int32_t(L.runs_max),
+                       int32_t(a.s0 == nullptr && a.fs == nullptr), plan, a.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const auto qp = static_cast<const bf16*>(a.q), kp = static_cast<const bf16*>(a.k);
